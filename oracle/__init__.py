@@ -1,0 +1,351 @@
+"""CPU oracle of the single-GPU MoE layer (test infrastructure only).
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg may import
+this package. It wraps the plain C oracle in ``moe_oracle.c`` (built with gcc,
+no GPU code, nothing shared with the HIP library) with numpy marshalling.
+
+bf16 arrays travel as ``np.uint16`` bit patterns, fp32 arrays as ``np.float32``.
+Route tables are route-major [k, S] (route r = 0 is the largest gate).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Dict, Optional, Sequence
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "moe_oracle.c")
+LIB = os.path.join(HERE, "libmoe_oracle.so")
+
+DT_F32 = 0
+DT_BF16 = 1
+
+_c_i32p = np.ctypeslib.ndpointer(dtype=np.int32, flags="C_CONTIGUOUS")
+_c_i64p = np.ctypeslib.ndpointer(dtype=np.int64, flags="C_CONTIGUOUS")
+_c_f32p = np.ctypeslib.ndpointer(dtype=np.float32, flags="C_CONTIGUOUS")
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (no fused multiply-add, fp64 accumulation as written)."""
+    if force or not os.path.exists(LIB):
+        tmp = LIB + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp",
+                               "-std=c99", "-D_GNU_SOURCE", "-Wall", "-shared", "-fPIC",
+                               SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, LIB)
+    return LIB
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB):
+            build()
+        L = ctypes.CDLL(LIB)
+        vp, i32, i64, d = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_double
+        L.oracle_f64_to_bf16.argtypes = [d]; L.oracle_f64_to_bf16.restype = ctypes.c_uint16
+        L.oracle_act.argtypes = [ctypes.c_int, d]; L.oracle_act.restype = d
+        L.oracle_act_grad.argtypes = [ctypes.c_int, d]; L.oracle_act_grad.restype = d
+        L.oracle_gate_logits.argtypes = [i32, i32, i32, ctypes.c_int, vp, _c_f32p, _c_f32p]
+        L.oracle_gate_logits.restype = None
+        L.oracle_softmax_topk.argtypes = [i32, i32, i32, _c_f32p, _c_i32p, _c_f32p]
+        L.oracle_softmax_topk.restype = ctypes.c_int
+        L.oracle_locations.argtypes = [i32, i32, i32, _c_i32p, _c_i32p, _c_i32p]
+        L.oracle_locations.restype = None
+        L.oracle_capacity.argtypes = [i32, i32, i32, d, _c_i32p]
+        L.oracle_capacity.restype = i32
+        L.oracle_route.argtypes = [i32, i32, i32, d, _c_f32p, _c_i32p, _c_f32p, _c_i32p, _c_i32p,
+                                   _c_i32p, vp]
+        L.oracle_route.restype = i32
+        L.oracle_encode.argtypes = [i32, i32, i32, i32, i32, ctypes.c_int, vp, _c_i32p, _c_i32p, vp]
+        L.oracle_encode.restype = None
+        L.oracle_expert_rows.argtypes = [i32, i32, i32, i32, ctypes.c_int, ctypes.c_int, vp, vp, vp,
+                                         vp, vp, i64, _c_i64p, vp, vp, vp]
+        L.oracle_expert_rows.restype = None
+        L.oracle_decode.argtypes = [i32, i32, i32, i32, i32, ctypes.c_int, vp, _c_f32p, _c_i32p,
+                                    _c_i32p, i64, vp, vp]
+        L.oracle_decode.restype = None
+        L.oracle_backward_rows.argtypes = [i32, i32, i32, i32, i32, ctypes.c_int, ctypes.c_int, vp,
+                                           vp, vp, vp, _c_f32p, vp, i64, _c_i64p, _c_i32p, vp, vp, vp]
+        L.oracle_backward_rows.restype = None
+        L.oracle_weight_grads.argtypes = [i32, i32, ctypes.c_int, i64, vp, vp, vp, vp, _c_f32p,
+                                          _c_f32p, _c_f32p, _c_f32p]
+        L.oracle_weight_grads.restype = None
+        L.oracle_dgates.argtypes = [i32, i32, ctypes.c_int, i64, _c_i32p, vp, vp, _c_f32p]
+        L.oracle_dgates.restype = None
+        L.oracle_dx.argtypes = [i32, i32, ctypes.c_int, vp, i64, _c_i64p, vp]
+        L.oracle_dx.restype = None
+        _lib = L
+    return _lib
+
+
+# ------------------------------------------------------------------ helpers
+
+def elem_dtype(dtype: int):
+    return np.float32 if dtype == DT_F32 else np.uint16
+
+
+def _ptr(a: Optional[np.ndarray]):
+    if a is None:
+        return None
+    assert a.flags["C_CONTIGUOUS"], "oracle arrays must be C-contiguous"
+    return a.ctypes.data
+
+
+def _check(a: np.ndarray, dtype: int, shape=None) -> np.ndarray:
+    a = np.ascontiguousarray(a)
+    assert a.dtype == elem_dtype(dtype), (a.dtype, dtype)
+    if shape is not None:
+        assert a.shape == tuple(shape), (a.shape, shape)
+    return a
+
+
+def bf16_to_f32(a: np.ndarray) -> np.ndarray:
+    """Exact widening of bf16 bit patterns to fp32."""
+    return (a.astype(np.uint32) << 16).view(np.float32)
+
+
+def to_f64(a: np.ndarray, dtype: int) -> np.ndarray:
+    return a.astype(np.float64) if dtype == DT_F32 else bf16_to_f32(a).astype(np.float64)
+
+
+def f64_to_bf16(v: float) -> int:
+    return int(lib().oracle_f64_to_bf16(float(v)))
+
+
+def act(a: int, v: float) -> float:
+    return lib().oracle_act(a, float(v))
+
+
+def act_grad(a: int, v: float) -> float:
+    return lib().oracle_act_grad(a, float(v))
+
+
+# ------------------------------------------------------------------ gating
+
+def gate_logits(x: np.ndarray, Wg: np.ndarray, dtype: int) -> np.ndarray:
+    S, M = x.shape
+    E = Wg.shape[1]
+    x = _check(x, dtype)
+    Wg = np.ascontiguousarray(Wg, dtype=np.float32)
+    out = np.empty((S, E), np.float32)
+    lib().oracle_gate_logits(S, M, E, dtype, _ptr(x), Wg, out)
+    return out
+
+
+def softmax_topk(logits: np.ndarray, k: int):
+    logits = np.ascontiguousarray(logits, dtype=np.float32)
+    S, E = logits.shape
+    idx = np.empty((k, S), np.int32)
+    gates = np.empty((k, S), np.float32)
+    if lib().oracle_softmax_topk(S, E, k, logits, idx, gates) != 0:
+        raise ValueError("non-finite logit")
+    return idx, gates
+
+
+def locations(idx: np.ndarray, E: int):
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    k, S = idx.shape
+    loc = np.empty((k, S), np.int32)
+    needed = np.empty((E,), np.int32)
+    lib().oracle_locations(S, E, k, idx, loc, needed)
+    return loc, needed
+
+
+def capacity(S: int, E: int, k: int, f: float, needed: np.ndarray) -> int:
+    return int(lib().oracle_capacity(S, E, k, float(f), np.ascontiguousarray(needed, dtype=np.int32)))
+
+
+def route(logits: np.ndarray, k: int, f: float, with_slots: bool = True) -> Dict[str, np.ndarray]:
+    """Softmax top-k, locations, capacity, fill and the slot -> route map."""
+    logits = np.ascontiguousarray(logits, dtype=np.float32)
+    S, E = logits.shape
+    idx = np.empty((k, S), np.int32)
+    gates = np.empty((k, S), np.float32)
+    loc = np.empty((k, S), np.int32)
+    needed = np.empty((E,), np.int32)
+    fill = np.empty((E,), np.int32)
+    # slot_route needs C, which is only known afterwards: route twice (cheap).
+    C = lib().oracle_route(S, E, k, float(f), logits, idx, gates, loc, needed, fill, None)
+    if C < 0:
+        raise ValueError("non-finite logit")
+    out = dict(idx=idx, gates=gates, loc=loc, needed=needed, fill=fill, C=int(C))
+    if with_slots:
+        slot = np.empty((E * C,), np.int32)
+        lib().oracle_route(S, E, k, float(f), logits, idx, gates, loc, needed, fill, _ptr(slot))
+        out["slot_route"] = slot
+    return out
+
+
+# ------------------------------------------------------------------ encode / FFN / decode
+
+def encode(x: np.ndarray, rt: Dict, E: int, dtype: int) -> np.ndarray:
+    x = _check(x, dtype)
+    S, M = x.shape
+    k = rt["idx"].shape[0]
+    C = rt["C"]
+    buf = np.empty((E * C, M), elem_dtype(dtype))
+    lib().oracle_encode(S, M, E, k, C, dtype, _ptr(x), rt["idx"], rt["loc"], _ptr(buf))
+    return buf
+
+
+def expert_rows(buf, W1, b1, W2, b2, rows: Sequence[int], C: int, act_kind: int, dtype: int,
+                want_pre: bool = False, want_h: bool = False):
+    """Expert FFN for the listed buffer rows (row = e*C + j). Returns (pre, h, y), compact."""
+    buf = _check(buf, dtype)
+    W1 = _check(W1, dtype)
+    W2 = _check(W2, dtype)
+    E, H, M = W1.shape
+    b1 = None if b1 is None else _check(b1, dtype, (E, H))
+    b2 = None if b2 is None else _check(b2, dtype, (E, M))
+    rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    n = rows.shape[0]
+    et = elem_dtype(dtype)
+    pre = np.empty((n, H), et) if want_pre else None
+    h = np.empty((n, H), et) if want_h else None
+    y = np.empty((n, M), et)
+    lib().oracle_expert_rows(M, H, E, C, dtype, act_kind, _ptr(buf), _ptr(W1), _ptr(b1), _ptr(W2),
+                             _ptr(b2), n, rows, _ptr(pre), _ptr(h), _ptr(y))
+    return pre, h, y
+
+
+def filled_rows(rt: Dict) -> np.ndarray:
+    """Buffer rows e*C + j with j < fill[e], in expert order."""
+    C = rt["C"]
+    return np.concatenate([e * C + np.arange(f, dtype=np.int64) for e, f in enumerate(rt["fill"])]
+                          or [np.zeros(0, np.int64)]).astype(np.int64)
+
+
+def decode(y: np.ndarray, rt: Dict, E: int, dtype: int, tokens: Optional[Sequence[int]] = None) -> np.ndarray:
+    """Gate-weighted combine; y is the [E*C, M] expert output (only kept rows are read)."""
+    y = _check(y, dtype)
+    M = y.shape[1]
+    k, S = rt["idx"].shape
+    C = rt["C"]
+    if tokens is None:
+        n, tok = S, None
+    else:
+        tok = np.ascontiguousarray(np.asarray(tokens, dtype=np.int64))
+        n = tok.shape[0]
+    out = np.empty((n, M), elem_dtype(dtype))
+    lib().oracle_decode(S, M, E, k, C, dtype, _ptr(y), rt["gates"], rt["idx"], rt["loc"], n,
+                        _ptr(tok), _ptr(out))
+    return out
+
+
+def layer_forward(inp: Dict[str, np.ndarray], k: int, f: float, act_kind: int, dtype: int,
+                  logits: Optional[np.ndarray] = None) -> Dict:
+    """The whole forward for small shapes: returns route tables, buf, pre, h, y (full E*C rows,
+    padding rows of pre/h/y left zero) and out."""
+    x = inp["x"]
+    if logits is None:
+        logits = inp["logits"] if "logits" in inp else gate_logits(x, inp["Wg"], dtype)
+    E = inp["W1"].shape[0]
+    rt = route(logits, k, f)
+    buf = encode(x, rt, E, dtype)
+    rows = filled_rows(rt)
+    pre_r, h_r, y_r = expert_rows(buf, inp["W1"], inp.get("b1"), inp["W2"], inp.get("b2"), rows,
+                                  rt["C"], act_kind, dtype, want_pre=True, want_h=True)
+    H = inp["W1"].shape[1]
+    M = x.shape[1]
+    et = elem_dtype(dtype)
+    pre = np.zeros((E * rt["C"], H), et); pre[rows] = pre_r
+    h = np.zeros((E * rt["C"], H), et); h[rows] = h_r
+    y = np.zeros((E * rt["C"], M), et); y[rows] = y_r
+    out = decode(y, rt, E, dtype)
+    return dict(logits=logits, route=rt, buf=buf, pre=pre, h=h, y=y, out=out, rows=rows)
+
+
+# ------------------------------------------------------------------ backward
+
+def backward_rows(fw: Dict, inp: Dict, rows: np.ndarray, act_kind: int, dtype: int,
+                  want_dy=True, want_dpre=True, want_dbuf=True):
+    """Per-row backward (dy, dpre, dbuf) for kept buffer rows, compact outputs."""
+    rt = fw["route"]
+    C = rt["C"]
+    k, S = rt["idx"].shape
+    W1, W2 = inp["W1"], inp["W2"]
+    E, H, M = W1.shape
+    rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    routes = np.ascontiguousarray(rt["slot_route"][rows].astype(np.int32))
+    assert (routes >= 0).all(), "backward rows must be filled rows"
+    n = rows.shape[0]
+    et = elem_dtype(dtype)
+    dy = np.empty((n, M), et) if want_dy else None
+    dpre = np.empty((n, H), et) if want_dpre else None
+    dbuf = np.empty((n, M), et) if want_dbuf else None
+    b1 = inp.get("b1")
+    lib().oracle_backward_rows(S, M, H, E, C, dtype, act_kind, _ptr(fw["buf"]), _ptr(W1), _ptr(b1),
+                               _ptr(W2), rt["gates"].reshape(-1).copy(), _ptr(_check(inp["dout"], dtype)),
+                               n, rows, routes, _ptr(dy), _ptr(dpre), _ptr(dbuf))
+    return routes, dy, dpre, dbuf
+
+
+def weight_grads(dy, hv, dpre, bufrows, dtype: int):
+    n, M = dy.shape
+    H = hv.shape[1]
+    dW1 = np.empty((H, M), np.float32); db1 = np.empty((H,), np.float32)
+    dW2 = np.empty((M, H), np.float32); db2 = np.empty((M,), np.float32)
+    lib().oracle_weight_grads(M, H, dtype, n, _ptr(np.ascontiguousarray(dy)), _ptr(np.ascontiguousarray(hv)),
+                              _ptr(np.ascontiguousarray(dpre)), _ptr(np.ascontiguousarray(bufrows)),
+                              dW1, db1, dW2, db2)
+    return dW1, db1, dW2, db2
+
+
+def dgates(routes: np.ndarray, dout: np.ndarray, yrows: np.ndarray, S: int, dtype: int) -> np.ndarray:
+    routes = np.ascontiguousarray(routes, dtype=np.int32)
+    n = routes.shape[0]
+    M = dout.shape[1]
+    dg = np.empty((n,), np.float32)
+    lib().oracle_dgates(S, M, dtype, n, routes, _ptr(_check(dout, dtype)),
+                        _ptr(np.ascontiguousarray(yrows)), dg)
+    return dg
+
+
+def dx_tokens(routes: np.ndarray, dbufrows: np.ndarray, tokens: Sequence[int], S: int, k: int,
+              dtype: int) -> np.ndarray:
+    """dx of the listed tokens from the dbuf rows of kept routes (routes[i] = r*S + s)."""
+    routes = np.asarray(routes, dtype=np.int64)
+    tok = np.asarray(tokens, dtype=np.int64)
+    pos = {int(t): i for i, t in enumerate(tok)}
+    table = np.full((tok.shape[0], k), -1, np.int64)
+    for i, q in enumerate(routes):
+        t = pos.get(int(q % S))
+        if t is not None:
+            table[t, int(q // S)] = i
+    M = dbufrows.shape[1]
+    out = np.empty((tok.shape[0], M), elem_dtype(dtype))
+    lib().oracle_dx(M, k, dtype, _ptr(np.ascontiguousarray(dbufrows)), tok.shape[0],
+                    np.ascontiguousarray(table), _ptr(out))
+    return out
+
+
+def layer_backward(fw: Dict, inp: Dict, act_kind: int, dtype: int) -> Dict[str, np.ndarray]:
+    """The whole backward for small shapes: dx, dW1, db1, dW2, db2 (fp32) and dgates [k,S]
+    (0 for dropped routes)."""
+    rt = fw["route"]
+    C = rt["C"]
+    k, S = rt["idx"].shape
+    E, H, M = inp["W1"].shape
+    rows = fw["rows"]
+    routes, dy, dpre, dbuf = backward_rows(fw, inp, rows, act_kind, dtype)
+    dW1 = np.zeros((E, H, M), np.float32); db1 = np.zeros((E, H), np.float32)
+    dW2 = np.zeros((E, M, H), np.float32); db2 = np.zeros((E, M), np.float32)
+    start = 0
+    for e in range(E):
+        n = int(rt["fill"][e])
+        sl = slice(start, start + n)
+        dW1[e], db1[e], dW2[e], db2[e] = weight_grads(dy[sl], fw["h"][rows[sl]], dpre[sl],
+                                                      fw["buf"][rows[sl]], dtype)
+        start += n
+    dg = np.zeros((k * S,), np.float32)
+    dg[routes] = dgates(routes, inp["dout"], fw["y"][rows], S, dtype)
+    dx = dx_tokens(routes, dbuf, np.arange(S), S, k, dtype)
+    return dict(dx=dx, dW1=dW1, db1=db1, dW2=dW2, db2=db2, dgates=dg.reshape(k, S),
+                dy=dy, dpre=dpre, dbuf=dbuf, routes=routes)

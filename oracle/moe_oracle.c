@@ -1,0 +1,440 @@
+/*
+ * CPU oracle for the single-GPU MoE layer: softmax top-k gating, capacity-bounded
+ * slot assignment, index-based encode, per-expert FFN, gate-weighted decode, and
+ * the backward of encode/FFN/decode.
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing in the product path may link, load or call
+ * this file; only the tests, the smoke check and the benchmark's CPU-baseline leg
+ * do. It is written to be read against the pages, not to be fast: plain loops,
+ * one accumulator per output, fp64 accumulation, no blocking and no reordering.
+ * It shares no code, header, table or constant with the HIP library.
+ *
+ * Build: gcc -O2 -ffp-contract=off -fopenmp -shared -fPIC (the contraction flag
+ * keeps every multiply and add separately rounded, as written).
+ *
+ * Sources (pages as printed; sections named on the page):
+ *  - Tutel catalogue page (diedong.com), "key configuration" table and FAQ:
+ *    gate_type {'type':'top','k':..,'capacity_factor':..}; capacity_factor > 0
+ *    is a fixed factor, 0 is max(needed volumes), < 0 is min(-X, max needed);
+ *    experts {'type':'ffn', hidden size per expert, has_fc1_bias/has_fc2_bias
+ *    (default True)}.
+ *  - MoE training blog (DeepSpeed-MoE vs Tutel), part 3 section 3.5 "fast
+ *    encode/decode and dynamic capacity factor": encode maps T x M plus the
+ *    gate's token-to-expert table into E x C x M, decode maps back; the dense
+ *    form is an einsum over a one-hot [T,E,C] mask; kernels K0/K1/K2 are the
+ *    combine-forward/encode-backward, encode-forward/combine-backward and the
+ *    cross term. Part 1 section 1.4 (third layer, kernels): top-k + cumsum +
+ *    scatter with a dense mapping table instead of one-hot einsum.
+ *  - DeepSpeed PR #8195 (page of PR #8174), section 1: per-route index,
+ *    location and gate values come from the top-k columns, as int32; section 2:
+ *    the flat [e*c, m] dispatch buffer; section 3: dispatch and combine by
+ *    index, combine accumulated in fp32.
+ *
+ * Readings where the pages are silent (each one is listed with its reason in the
+ * design notes of the repository):
+ *  - top-k orders experts by logit, larger first, and among equal logits the
+ *    lower expert index first (+0 and -0 are equal); route r = 0 is the largest;
+ *  - the softmax is computed in fp64 over all E logits and rounded once to fp32;
+ *    gates are the probabilities of the selected experts, not renormalised;
+ *  - locations count earlier routes to the same expert in route-major, then
+ *    token order; a route is kept iff its location < C; the location of a
+ *    dropped route is its raw rank;
+ *  - C = ceil(k*S*|f|/E) for f > 0; max needed for f = 0; the smaller of the
+ *    two for f < 0; never below 1;
+ *  - encode copies token rows (no gate scaling); padding rows are +0;
+ *  - FFN: pre = buf . W1[e]^T + b1[e] (W1 is [E,H,M]), h = act(pre) rounded to
+ *    the data type, y = h . W2[e]^T + b2[e] (W2 is [E,M,H]) rounded to the data
+ *    type; GELU is the exact erf form;
+ *  - decode accumulates gate * y in fp32 in route order from +0 with separate
+ *    multiply and add, then rounds to the data type; dropped routes add nothing;
+ *  - backward: dy = g * dout (rounded to the data type), dgate = <dout, y>,
+ *    dh = dy . W2[e], dpre = dh * act'(pre) rounded, dbuf = dpre . W1[e]
+ *    rounded, dx = sum of dbuf over kept routes rounded; weight and bias
+ *    gradients are fp32 sums over the expert's filled rows.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define DT_F32 0
+#define DT_BF16 1
+#define ACT_RELU 0
+#define ACT_GELU 1
+
+/* ------------------------------------------------------------------ scalars */
+
+static float bits_to_f32(uint32_t u) { float f; memcpy(&f, &u, 4); return f; }
+static uint32_t f32_to_bits(float f) { uint32_t u; memcpy(&u, &f, 4); return u; }
+
+/* bf16 is the upper half of an IEEE binary32. */
+static double bf16_value(uint16_t b) { return (double)bits_to_f32((uint32_t)b << 16); }
+
+/* binary32 -> bf16, round to nearest, ties to even (finite inputs). */
+static uint16_t f32_to_bf16(float f) {
+    uint32_t u = f32_to_bits(f);
+    uint32_t lsb = (u >> 16) & 1u;
+    return (uint16_t)((u + 0x7FFFu + lsb) >> 16);
+}
+
+/* binary64 -> bf16 with a single rounding to nearest-even: first round to a
+ * binary32 by round-to-odd (exact whenever representable, otherwise the
+ * truncated value with its last bit set), which has more than two extra bits
+ * over bf16, so the second rounding cannot double-round. */
+static uint16_t f64_to_bf16(double v) {
+    float f = (float)v;
+    if ((double)f != v) {
+        uint32_t u = f32_to_bits(f);
+        if (fabs((double)f) > fabs(v)) u -= 1u; /* step back toward zero */
+        u |= 1u;
+        f = bits_to_f32(u);
+    }
+    return f32_to_bf16(f);
+}
+
+static double load_elem(const void *p, int dtype, int64_t i) {
+    if (dtype == DT_F32) return (double)((const float *)p)[i];
+    return bf16_value(((const uint16_t *)p)[i]);
+}
+
+/* Store v rounded once to the data type. */
+static void store_elem(void *p, int dtype, int64_t i, double v) {
+    if (dtype == DT_F32) ((float *)p)[i] = (float)v;
+    else ((uint16_t *)p)[i] = f64_to_bf16(v);
+}
+
+/* The value the data type holds after storing v. */
+static double round_to_dtype(double v, int dtype) {
+    if (dtype == DT_F32) return (double)(float)v;
+    return bf16_value(f64_to_bf16(v));
+}
+
+static double act_f(int act, double v) {
+    if (act == ACT_RELU) return v > 0.0 ? v : 0.0;
+    return 0.5 * v * (1.0 + erf(v / sqrt(2.0)));
+}
+
+static double act_grad(int act, double v) {
+    if (act == ACT_RELU) return v > 0.0 ? 1.0 : 0.0;
+    const double pdf = exp(-0.5 * v * v) / sqrt(2.0 * M_PI);
+    return 0.5 * (1.0 + erf(v / sqrt(2.0))) + v * pdf;
+}
+
+/* Exposed for the tests: the scalar roundings above. */
+uint16_t oracle_f64_to_bf16(double v) { return f64_to_bf16(v); }
+double oracle_act(int act, double v) { return act_f(act, v); }
+double oracle_act_grad(int act, double v) { return act_grad(act, v); }
+
+/* ------------------------------------------------------------------ gating */
+
+/* Gate projection: logit[s][e] = fp32( sum_m x[s][m] * Wg[m][e] ), the sum in
+ * fp64 over m in order. x is [S,M] in the data type, Wg is [M,E] fp32. */
+void oracle_gate_logits(int32_t S, int32_t M, int32_t E, int dtype, const void *x,
+                        const float *Wg, float *logits) {
+    for (int64_t s = 0; s < S; ++s)
+        for (int32_t e = 0; e < E; ++e) {
+            double acc = 0.0;
+            for (int32_t m = 0; m < M; ++m)
+                acc += load_elem(x, dtype, s * M + m) * (double)Wg[(int64_t)m * E + e];
+            logits[s * E + e] = (float)acc;
+        }
+}
+
+/* Order of two experts of one token: larger logit first, equal logits (+0 and
+ * -0 included) by lower index first. */
+typedef struct { float v; int32_t e; } cand_t;
+static int cand_cmp(const void *a, const void *b) {
+    const cand_t *x = (const cand_t *)a, *y = (const cand_t *)b;
+    if (x->v > y->v) return -1;
+    if (x->v < y->v) return 1;
+    return (x->e < y->e) ? -1 : (x->e > y->e);
+}
+
+/* Softmax over each token's E logits and the k largest as (expert, prob),
+ * route-major outputs idx[r][s], gates[r][s]. Returns 0, or -1 on a
+ * non-finite logit (finite logits are a precondition). */
+int oracle_softmax_topk(int32_t S, int32_t E, int32_t k, const float *logits,
+                        int32_t *idx, float *gates) {
+    cand_t *c = (cand_t *)malloc(sizeof(cand_t) * (size_t)E);
+    for (int64_t s = 0; s < S; ++s) {
+        const float *l = logits + s * E;
+        double mx = -INFINITY;
+        for (int32_t e = 0; e < E; ++e) {
+            if (!isfinite(l[e])) { free(c); return -1; }
+            if ((double)l[e] > mx) mx = (double)l[e];
+        }
+        double sum = 0.0;
+        for (int32_t e = 0; e < E; ++e) sum += exp((double)l[e] - mx);
+        for (int32_t e = 0; e < E; ++e) { c[e].v = l[e]; c[e].e = e; }
+        qsort(c, (size_t)E, sizeof(cand_t), cand_cmp); /* full sort: the comparator is total */
+        for (int32_t r = 0; r < k; ++r) {
+            idx[(int64_t)r * S + s] = c[r].e;
+            gates[(int64_t)r * S + s] = (float)(exp((double)c[r].v - mx) / sum);
+        }
+    }
+    free(c);
+    return 0;
+}
+
+/* Location of every route: the number of earlier routes (route-major, then
+ * token order) that chose the same expert. needed[e] = routes to e. */
+void oracle_locations(int32_t S, int32_t E, int32_t k, const int32_t *idx, int32_t *loc,
+                      int32_t *needed) {
+    for (int32_t e = 0; e < E; ++e) needed[e] = 0;
+    for (int32_t r = 0; r < k; ++r)
+        for (int64_t s = 0; s < S; ++s) {
+            const int32_t e = idx[(int64_t)r * S + s];
+            loc[(int64_t)r * S + s] = needed[e];
+            needed[e] += 1;
+        }
+}
+
+/* Capacity from capacity_factor f: f > 0 fixed factor, f == 0 max needed,
+ * f < 0 the smaller of the |f| factor and max needed; at least 1. */
+int32_t oracle_capacity(int32_t S, int32_t E, int32_t k, double f, const int32_t *needed) {
+    int32_t max_needed = 0;
+    for (int32_t e = 0; e < E; ++e)
+        if (needed[e] > max_needed) max_needed = needed[e];
+    const double by_factor = ceil(((double)k * (double)S * fabs(f)) / (double)E);
+    int64_t c;
+    if (f > 0) c = (int64_t)by_factor;
+    else if (f == 0) c = max_needed;
+    else c = (int64_t)by_factor < max_needed ? (int64_t)by_factor : max_needed;
+    if (c < 1) c = 1;
+    return (int32_t)c;
+}
+
+/* The whole routing step. fill[e] = min(needed[e], C). slot_route (may be NULL,
+ * else E*C entries) gets r*S+s at row e*C+loc for every kept route and -1 on
+ * padding rows. Returns C, or -1 on non-finite logits. */
+int32_t oracle_route(int32_t S, int32_t E, int32_t k, double f, const float *logits,
+                     int32_t *idx, float *gates, int32_t *loc, int32_t *needed,
+                     int32_t *fill, int32_t *slot_route) {
+    if (oracle_softmax_topk(S, E, k, logits, idx, gates) != 0) return -1;
+    oracle_locations(S, E, k, idx, loc, needed);
+    const int32_t C = oracle_capacity(S, E, k, f, needed);
+    for (int32_t e = 0; e < E; ++e) fill[e] = needed[e] < C ? needed[e] : C;
+    if (slot_route) {
+        for (int64_t i = 0; i < (int64_t)E * C; ++i) slot_route[i] = -1;
+        for (int32_t r = 0; r < k; ++r)
+            for (int64_t s = 0; s < S; ++s) {
+                const int64_t q = (int64_t)r * S + s;
+                if (loc[q] < C) slot_route[(int64_t)idx[q] * C + loc[q]] = (int32_t)q;
+            }
+    }
+    return C;
+}
+
+/* ------------------------------------------------------------------ encode */
+
+/* buf[e*C + loc] = x[s] for every kept route (a copy of the bits), every other
+ * row of the [E*C, M] buffer = +0. */
+void oracle_encode(int32_t S, int32_t M, int32_t E, int32_t k, int32_t C, int dtype,
+                   const void *x, const int32_t *idx, const int32_t *loc, void *buf) {
+    const size_t eb = dtype == DT_F32 ? 4 : 2;
+    memset(buf, 0, eb * (size_t)E * (size_t)C * (size_t)M);
+    for (int32_t r = 0; r < k; ++r)
+        for (int64_t s = 0; s < S; ++s) {
+            const int64_t q = (int64_t)r * S + s;
+            if (loc[q] >= C) continue;
+            const int64_t row = (int64_t)idx[q] * C + loc[q];
+            memcpy((char *)buf + row * M * eb, (const char *)x + s * M * eb, (size_t)M * eb);
+        }
+}
+
+/* -------------------------------------------------------------- expert FFN */
+
+/* One buffer row `row` = e*C + j through expert e:
+ *   pre[h] = sum_m buf[row][m] * W1[e][h][m] + b1[e][h]   (fp64)
+ *   hv[h]  = act(pre[h]) rounded to the data type
+ *   y[m]   = sum_h hv[h] * W2[e][m][h] + b2[e][m]          (fp64)
+ * pre_exact (H doubles) gets the unrounded pre-activation. */
+static void ffn_row(int32_t M, int32_t H, int32_t C, int dtype, int act, const void *buf,
+                    const void *W1, const void *b1, const void *W2, const void *b2,
+                    int64_t row, double *pre_exact, double *hv, double *yv) {
+    const int64_t e = row / C;
+    for (int32_t h = 0; h < H; ++h) {
+        double acc = 0.0;
+        for (int32_t m = 0; m < M; ++m)
+            acc += load_elem(buf, dtype, row * M + m) * load_elem(W1, dtype, (e * H + h) * M + m);
+        if (b1) acc += load_elem(b1, dtype, e * H + h);
+        pre_exact[h] = acc;
+        hv[h] = round_to_dtype(act_f(act, acc), dtype);
+    }
+    for (int32_t m = 0; m < M; ++m) {
+        double acc = 0.0;
+        for (int32_t h = 0; h < H; ++h)
+            acc += hv[h] * load_elem(W2, dtype, (e * M + m) * H + h);
+        if (b2) acc += load_elem(b2, dtype, e * M + m);
+        yv[m] = acc;
+    }
+}
+
+/* Forward through the experts for nrows buffer rows (rows[i] = e*C + j).
+ * Outputs are compact, one row per listed row, in the data type:
+ * pre_out [nrows,H] (may be NULL), h_out [nrows,H] (may be NULL), y_out [nrows,M]. */
+void oracle_expert_rows(int32_t M, int32_t H, int32_t E, int32_t C, int dtype, int act,
+                        const void *buf, const void *W1, const void *b1, const void *W2,
+                        const void *b2, int64_t nrows, const int64_t *rows, void *pre_out,
+                        void *h_out, void *y_out) {
+    (void)E;
+#pragma omp parallel
+    {
+        double *pre = (double *)malloc(sizeof(double) * (size_t)H);
+        double *hv = (double *)malloc(sizeof(double) * (size_t)H);
+        double *yv = (double *)malloc(sizeof(double) * (size_t)M);
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t i = 0; i < nrows; ++i) {
+            ffn_row(M, H, C, dtype, act, buf, W1, b1, W2, b2, rows[i], pre, hv, yv);
+            for (int32_t h = 0; h < H; ++h) {
+                if (pre_out) store_elem(pre_out, dtype, i * H + h, pre[h]);
+                if (h_out) store_elem(h_out, dtype, i * H + h, hv[h]);
+            }
+            for (int32_t m = 0; m < M; ++m) store_elem(y_out, dtype, i * M + m, yv[m]);
+        }
+        free(pre); free(hv); free(yv);
+    }
+}
+
+/* ------------------------------------------------------------------ decode */
+
+/* out[s][m] = sum over kept routes r (in route order) of gates[r][s] * y[slot][m],
+ * fp32 from +0 with separate multiply and add, then rounded to the data type.
+ * y is the [E*C, M] expert output. tokens (may be NULL = all S) lists the
+ * ntok tokens to produce; out is compact [ntok, M]. */
+void oracle_decode(int32_t S, int32_t M, int32_t E, int32_t k, int32_t C, int dtype,
+                   const void *y, const float *gates, const int32_t *idx, const int32_t *loc,
+                   int64_t ntok, const int64_t *tokens, void *out) {
+    (void)E;
+    for (int64_t i = 0; i < ntok; ++i) {
+        const int64_t s = tokens ? tokens[i] : i;
+        for (int32_t m = 0; m < M; ++m) {
+            float acc = 0.0f;
+            for (int32_t r = 0; r < k; ++r) {
+                const int64_t q = (int64_t)r * S + s;
+                if (loc[q] >= C) continue;
+                const int64_t row = (int64_t)idx[q] * C + loc[q];
+                const float prod = gates[q] * (float)load_elem(y, dtype, row * M + m);
+                acc = acc + prod;
+            }
+            store_elem(out, dtype, i * M + m, (double)acc);
+        }
+    }
+}
+
+/* ---------------------------------------------------------------- backward */
+
+/* Backward of one kept buffer row `row` = e*C + j that holds route q = r*S+s:
+ *   dy[m]   = gates[q] * dout[s][m], rounded to the data type
+ *   dh[h]   = sum_m dy[m] * W2[e][m][h]                      (fp64)
+ *   dpre[h] = dh[h] * act'(pre_exact[h]), rounded
+ *   dbuf[m] = sum_h dpre[h] * W1[e][h][m], rounded
+ * Outputs (compact, rows in the data type) may each be NULL. */
+void oracle_backward_rows(int32_t S, int32_t M, int32_t H, int32_t E, int32_t C, int dtype,
+                          int act, const void *buf, const void *W1, const void *b1,
+                          const void *W2, const float *gates, const void *dout,
+                          int64_t nrows, const int64_t *rows, const int32_t *routes,
+                          void *dy_out, void *dpre_out, void *dbuf_out) {
+    (void)E; (void)S;
+#pragma omp parallel
+    {
+        double *pre = (double *)malloc(sizeof(double) * (size_t)H);
+        double *dy = (double *)malloc(sizeof(double) * (size_t)M);
+        double *dpre = (double *)malloc(sizeof(double) * (size_t)H);
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t i = 0; i < nrows; ++i) {
+            const int64_t row = rows[i], e = row / C;
+            const int64_t q = routes[i], s = q % S;
+            for (int32_t h = 0; h < H; ++h) {
+                double acc = 0.0;
+                for (int32_t m = 0; m < M; ++m)
+                    acc += load_elem(buf, dtype, row * M + m) * load_elem(W1, dtype, (e * H + h) * M + m);
+                if (b1) acc += load_elem(b1, dtype, e * H + h);
+                pre[h] = acc;
+            }
+            for (int32_t m = 0; m < M; ++m) {
+                dy[m] = round_to_dtype((double)gates[q] * load_elem(dout, dtype, s * M + m), dtype);
+                if (dy_out) store_elem(dy_out, dtype, i * M + m, dy[m]);
+            }
+            for (int32_t h = 0; h < H; ++h) {
+                double acc = 0.0;
+                for (int32_t m = 0; m < M; ++m)
+                    acc += dy[m] * load_elem(W2, dtype, (e * M + m) * H + h);
+                dpre[h] = round_to_dtype(acc * act_grad(act, pre[h]), dtype);
+                if (dpre_out) store_elem(dpre_out, dtype, i * H + h, dpre[h]);
+            }
+            if (dbuf_out)
+                for (int32_t m = 0; m < M; ++m) {
+                    double acc = 0.0;
+                    for (int32_t h = 0; h < H; ++h)
+                        acc += dpre[h] * load_elem(W1, dtype, (e * H + h) * M + m);
+                    store_elem(dbuf_out, dtype, i * M + m, acc);
+                }
+        }
+        free(pre); free(dy); free(dpre);
+    }
+}
+
+/* Weight and bias gradients of expert e from its n filled rows (in row order):
+ *   dW2[m][h] = sum_j dy[j][m] * hv[j][h]      db2[m] = sum_j dy[j][m]
+ *   dW1[h][m] = sum_j dpre[j][h] * buf[j][m]   db1[h] = sum_j dpre[j][h]
+ * dy, hv, dpre, bufrows are compact [n, *] arrays in the data type; outputs are
+ * fp32 [M,H], [M], [H,M], [H] for this expert. */
+void oracle_weight_grads(int32_t M, int32_t H, int dtype, int64_t n, const void *dy,
+                         const void *hv, const void *dpre, const void *bufrows, float *dW1,
+                         float *db1, float *dW2, float *db2) {
+#pragma omp parallel for schedule(static)
+    for (int32_t m = 0; m < M; ++m) {
+        for (int32_t h = 0; h < H; ++h) {
+            double acc = 0.0;
+            for (int64_t j = 0; j < n; ++j)
+                acc += load_elem(dy, dtype, j * M + m) * load_elem(hv, dtype, j * H + h);
+            dW2[(int64_t)m * H + h] = (float)acc;
+        }
+        double acc = 0.0;
+        for (int64_t j = 0; j < n; ++j) acc += load_elem(dy, dtype, j * M + m);
+        db2[m] = (float)acc;
+    }
+#pragma omp parallel for schedule(static)
+    for (int32_t h = 0; h < H; ++h) {
+        for (int32_t m = 0; m < M; ++m) {
+            double acc = 0.0;
+            for (int64_t j = 0; j < n; ++j)
+                acc += load_elem(dpre, dtype, j * H + h) * load_elem(bufrows, dtype, j * M + m);
+            dW1[(int64_t)h * M + m] = (float)acc;
+        }
+        double acc = 0.0;
+        for (int64_t j = 0; j < n; ++j) acc += load_elem(dpre, dtype, j * H + h);
+        db1[h] = (float)acc;
+    }
+}
+
+/* dgate of route q: sum_m dout[s][m] * y[slot][m] in fp64, rounded to fp32.
+ * yrows holds the kept routes' expert-output rows, compact [n, M]. */
+void oracle_dgates(int32_t S, int32_t M, int dtype, int64_t n, const int32_t *routes,
+                   const void *dout, const void *yrows, float *dg) {
+    for (int64_t i = 0; i < n; ++i) {
+        const int64_t s = routes[i] % S;
+        double acc = 0.0;
+        for (int32_t m = 0; m < M; ++m)
+            acc += load_elem(dout, dtype, s * M + m) * load_elem(yrows, dtype, i * M + m);
+        dg[i] = (float)acc;
+    }
+}
+
+/* dx[s][m] = sum over the token's kept routes of dbuf[slot][m] in route order
+ * (fp64), rounded to the data type. dbufrows [n, M] holds dbuf rows; for token
+ * t, route_rows[t*k + r] is the dbuf row of its route r, or -1 when that route
+ * was dropped. dx is [ntok, M]. */
+void oracle_dx(int32_t M, int32_t k, int dtype, const void *dbufrows, int64_t ntok,
+               const int64_t *route_rows, void *dx) {
+    for (int64_t t = 0; t < ntok; ++t)
+        for (int32_t m = 0; m < M; ++m) {
+            double acc = 0.0;
+            for (int32_t r = 0; r < k; ++r) {
+                const int64_t i = route_rows[t * k + r];
+                if (i >= 0) acc += load_elem(dbufrows, dtype, i * M + m);
+            }
+            store_elem(dx, dtype, t * M + m, acc);
+        }
+}

@@ -1,0 +1,387 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix (no GPU).
+
+Each test ties one oracle function to something other than itself: a hand-derived
+value from the pages' statements, a closed form, a library routine on a special
+case, an invariant, or brute force on tiny inputs. The pages print no worked
+numeric example for this path, so there are no printed values to pin to.
+"""
+from __future__ import annotations
+
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import oracle
+import workloads as W
+from tests.helpers import (bf16_bits_of_f32, dense_combine, dense_dispatch, f32_of, np_of, onehot_mask,
+                           to_dtype_bits)
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---------------------------------------------------------------- scalar roundings
+
+def test_bf16_rounding_single_rounding_and_ties():
+    # ties go to even: 1 + 2^-8 is halfway between 1 and 1 + 2^-7
+    assert oracle.f64_to_bf16(1.0 + 2 ** -8) == 0x3F80
+    assert oracle.f64_to_bf16(1.0 + 3 * 2 ** -8) == 0x3F82
+    # just above the tie by less than half an fp32 ulp: a double rounding through fp32
+    # would land on the tie and go down; a single rounding goes up.
+    assert oracle.f64_to_bf16(1.0 + 2 ** -8 + 2 ** -30) == 0x3F81
+    assert oracle.f64_to_bf16(-(1.0 + 2 ** -8 + 2 ** -30)) == 0xBF81
+    # on fp32-representable values it equals torch's fp32 -> bf16 conversion
+    rng = np.random.default_rng(0)
+    v = (rng.standard_normal(20000) * np.exp(rng.uniform(-20, 20, 20000))).astype(np.float32)
+    want = bf16_bits_of_f32(v)
+    got = np.array([oracle.f64_to_bf16(float(a)) for a in v], np.uint16)
+    assert np.array_equal(got, want)
+
+
+def test_activation_matches_library():
+    v = np.linspace(-6, 6, 241)
+    t = torch.from_numpy(v).requires_grad_(True)
+    g = torch.nn.functional.gelu(t)  # exact erf form
+    (dg,) = torch.autograd.grad(g.sum(), t)
+    for i, a in enumerate(v):
+        assert oracle.act(W.ACT_GELU, a) == pytest.approx(float(g[i]), abs=1e-15)
+        assert oracle.act_grad(W.ACT_GELU, a) == pytest.approx(float(dg[i]), abs=1e-14)
+        assert oracle.act(W.ACT_RELU, a) == max(a, 0.0)
+        assert oracle.act_grad(W.ACT_RELU, a) == (1.0 if a > 0 else 0.0)
+
+
+# ---------------------------------------------------------------- gate projection
+
+def test_gate_logits_exact_products_and_fp32_rounding():
+    # bf16 x times fp32 Wg: each product is exact in fp64; the sum of few terms is too.
+    rng = np.random.default_rng(1)
+    x32 = rng.standard_normal((5, 16)).astype(np.float32)
+    x = bf16_bits_of_f32(x32)
+    Wg = (rng.standard_normal((16, 3)) * 0.02).astype(np.float32)
+    got = oracle.gate_logits(x, Wg, W.DT_BF16)
+    want = (f32_of(x).astype(np.float64) @ Wg.astype(np.float64)).astype(np.float32)
+    assert np.array_equal(got, want)
+
+
+# ---------------------------------------------------------------- capacity
+
+def test_capacity_golden_cases():
+    with open(os.path.join(GOLDEN, "capacity_cases.json")) as fh:
+        cases = json.load(fh)["cases"]
+    for c in cases:
+        if "needed" in c:
+            needed = np.array(c["needed"], np.int32)
+        else:
+            needed = np.zeros(c["E"], np.int32)
+            needed[0] = c["needed_hot"]
+        assert oracle.capacity(c["S"], c["E"], c["k"], c["f"], needed) == c["C"], c["why"]
+
+
+@pytest.mark.parametrize("w", W.WORKLOADS, ids=lambda w: w.name)
+def test_capacity_bound_of_workloads(w):
+    # f > 0: the bound is the capacity itself; f <= 0: the capacity never exceeds it.
+    needed = np.full(w.E, w.S, np.int32)  # the largest any expert can need
+    C = oracle.capacity(w.S, w.E, w.k, w.capacity_factor, needed)
+    assert C == W.capacity_bound(w)
+    if w.capacity_factor > 0:
+        assert C == math.ceil(w.k * w.S * w.capacity_factor / w.E)
+
+
+def test_capacity_closed_forms_of_named_workloads():
+    assert W.capacity_bound(W.TINY_F32) == 64
+    assert W.capacity_bound(W.GATED_BF16) == 1280
+    assert W.capacity_bound(W.FINE_BF16) == 2304
+    assert W.capacity_bound(W.LARGE_BF16) == 4096
+
+
+# ---------------------------------------------------------------- softmax top-k
+
+def _brute_topk(logits: np.ndarray, k: int):
+    """Brute force: lexicographic sort by (-logit, expert) and fp64 softmax (scipy)."""
+    S, E = logits.shape
+    idx = np.empty((k, S), np.int32)
+    gates = np.empty((k, S), np.float32)
+    p = scipy.special.softmax(logits.astype(np.float64), axis=1)
+    for s in range(S):
+        order = np.lexsort((np.arange(E), -logits[s].astype(np.float64)))
+        idx[:, s] = order[:k]
+        gates[:, s] = p[s, order[:k]].astype(np.float32)
+    return idx, gates, p
+
+
+@pytest.mark.parametrize("E,k", [(4, 1), (8, 2), (16, 3), (64, 6), (128, 8), (5, 5), (1, 1)])
+def test_topk_against_brute_force_with_ties(E, k):
+    rng = np.random.default_rng(E * 10 + k)
+    S = 300
+    logits = rng.standard_normal((S, E)).astype(np.float32)
+    # inject exact ties, +0/-0 pairs and an all-equal token
+    logits[0, :] = 0.5
+    if E > 1:
+        logits[1, :] = 0.0
+        logits[1, ::2] = -0.0
+        logits[2, E - 1] = logits[2, 0]
+        logits[3, :] = np.float32(-1.0)
+        logits[3, E // 2] = np.float32(2.0)
+    for s in range(4, S, 7):  # quantised rows: many ties
+        logits[s] = np.round(logits[s] * 2) / 2
+    idx, gates = oracle.softmax_topk(logits, k)
+    bidx, bgates, p = _brute_topk(logits, k)
+    assert np.array_equal(idx, bidx)
+    # fp64 softmax rounded once to fp32: equal up to one fp32 ulp (exp/sum libm differences)
+    assert np.allclose(gates, bgates, rtol=2.5e-7, atol=0)
+    # invariants: distinct experts, non-increasing gates, probabilities sum to one
+    for s in range(S):
+        assert len(set(idx[:, s].tolist())) == k
+    assert (np.diff(gates, axis=0) <= 0).all()
+    assert np.allclose(p.sum(axis=1), 1.0, atol=1e-12)
+    # all-equal token: lowest indices first, each prob 1/E
+    assert idx[:, 0].tolist() == list(range(k))
+    assert np.allclose(gates[:, 0], 1.0 / E, rtol=1e-7)
+
+
+def test_topk_rejects_non_finite():
+    logits = np.zeros((2, 4), np.float32)
+    logits[1, 2] = np.nan
+    with pytest.raises(ValueError):
+        oracle.softmax_topk(logits, 1)
+
+
+# ---------------------------------------------------------------- locations
+
+def test_locations_brute_force_tiny():
+    rng = np.random.default_rng(3)
+    for (S, E, k) in [(9, 3, 2), (17, 4, 3), (1, 2, 2), (12, 5, 1)]:
+        logits = rng.standard_normal((S, E)).astype(np.float32)
+        idx, _ = oracle.softmax_topk(logits, k)
+        loc, needed = oracle.locations(idx, E)
+        routes = [(r, s) for r in range(k) for s in range(S)]  # route-major, then token
+        for i, (r, s) in enumerate(routes):
+            earlier = sum(1 for (r2, s2) in routes[:i] if idx[r2, s2] == idx[r, s])
+            assert loc[r, s] == earlier
+        assert needed.tolist() == [int((idx == e).sum()) for e in range(E)]
+
+
+@pytest.mark.parametrize("w", [W.TINY_F32, W.FINE_BF16.replace(S=2048)], ids=lambda w: w.name)
+def test_route_invariants(w):
+    inp = W.make_inputs(w, seed=1)
+    rt = oracle.route(np_of(inp["logits"]), w.k, w.capacity_factor)
+    k, S = rt["idx"].shape
+    C = rt["C"]
+    assert rt["needed"].sum() == k * S
+    for e in range(w.E):
+        locs = np.sort(rt["loc"][rt["idx"] == e])
+        assert np.array_equal(locs, np.arange(rt["needed"][e]))
+        assert rt["fill"][e] == min(rt["needed"][e], C)
+    kept = rt["loc"] < C
+    assert kept.sum() == rt["fill"].sum()
+    # slot_route is a bijection from kept routes onto filled rows, -1 on padding
+    slot = rt["slot_route"].reshape(w.E, C)
+    for e in range(w.E):
+        assert (slot[e, :rt["fill"][e]] >= 0).all() and (slot[e, rt["fill"][e]:] == -1).all()
+    q = slot[slot >= 0]
+    assert len(np.unique(q)) == kept.sum()
+    assert kept.reshape(-1)[q].all()
+    r, s = q // S, q % S
+    assert np.array_equal(rt["idx"][r, s] * C + rt["loc"][r, s], np.nonzero(slot.reshape(-1) >= 0)[0])
+
+
+def test_factor_zero_keeps_every_route():
+    w = W.DSPR_BF16.replace(S=1024, M=64, H=64)
+    inp = W.make_inputs(w, seed=2)
+    rt = oracle.route(np_of(inp["logits"]), w.k, 0.0)
+    assert rt["C"] == rt["needed"].max()
+    assert (rt["loc"] < rt["C"]).all()
+    assert rt["fill"].sum() == w.k * w.S
+
+
+def test_negative_factor_drops_on_hot_experts():
+    w = W.FINE_BF16.replace(S=4096)
+    inp = W.make_inputs(w, seed=0)
+    rt = oracle.route(np_of(inp["logits"]), w.k, w.capacity_factor)
+    bound = math.ceil(w.k * w.S * 1.5 / w.E)
+    assert rt["C"] == min(bound, rt["needed"].max())
+    assert rt["needed"].max() > bound  # the Zipf skew overloads expert 0
+    dropped = (rt["loc"] >= rt["C"]).sum()
+    assert dropped == (rt["needed"] - rt["fill"]).sum() > 0
+
+
+# ---------------------------------------------------------------- encode / decode == dense einsum
+
+DENSE_CASES = [(k, f) for k in (1, 2, 3) for f in (1.0, 0.5, 0.0, -0.5, -1.0)]
+
+
+@pytest.mark.parametrize("dtype", [W.DT_F32, W.DT_BF16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("k,f", DENSE_CASES)
+def test_index_path_equals_dense_einsum(dtype, k, f):
+    S, M, E = 40, 16, 4
+    rng = np.random.default_rng(100 * k + int(10 * f) + dtype)
+    logits = rng.standard_normal((S, E)).astype(np.float32)
+    x = to_dtype_bits(rng.standard_normal((S, M)).astype(np.float32), dtype)
+    rt = oracle.route(logits, k, f)
+    C = rt["C"]
+    buf = oracle.encode(x, rt, E, dtype)
+    mask = onehot_mask(rt["idx"], rt["loc"], E, C)
+    dense_buf = dense_dispatch(f32_of(x), mask).reshape(E * C, M)
+    assert np.array_equal(f32_of(buf), dense_buf)
+    # padding rows are +0 bit patterns
+    pad = np.ones(E * C, bool)
+    pad[oracle.filled_rows(rt)] = False
+    assert (buf[pad].view(np.uint16 if dtype == W.DT_BF16 else np.uint32) == 0).all()
+    # combine: per-route dense form equals the index decode exactly
+    y = to_dtype_bits(rng.standard_normal((E * C, M)).astype(np.float32), dtype)
+    out = oracle.decode(y, rt, E, dtype)
+    dense_out = dense_combine(f32_of(y).reshape(E, C, M), mask, rt["gates"])
+    assert np.array_equal(out, to_dtype_bits(dense_out, dtype))
+
+
+@pytest.mark.parametrize("S,E,k", [(1, 3, 2), (7, 1, 1), (13, 4, 4), (0, 4, 1)])
+def test_index_path_edge_cases(S, E, k):
+    M = 8
+    rng = np.random.default_rng(S + E + k)
+    logits = rng.standard_normal((S, E)).astype(np.float32)
+    x = rng.standard_normal((S, M)).astype(np.float32)
+    rt = oracle.route(logits, k, 0.0 if S else 1.0)
+    C = rt["C"]
+    buf = oracle.encode(x, rt, E, W.DT_F32)
+    mask = onehot_mask(rt["idx"], rt["loc"], E, C)
+    assert np.array_equal(buf, dense_dispatch(x, mask).reshape(E * C, M))
+    y = rng.standard_normal((E * C, M)).astype(np.float32)
+    out = oracle.decode(y, rt, E, W.DT_F32)
+    assert np.array_equal(out, dense_combine(y.reshape(E, C, M), mask, rt["gates"]))
+    if k == E and S:
+        # every expert chosen by every token: gates are the full softmax, summing to one
+        assert np.allclose(rt["gates"].astype(np.float64).sum(axis=0), 1.0, atol=1e-6)
+
+
+# ---------------------------------------------------------------- expert FFN
+
+def _torch_mlp(x64, W1, b1, W2, b2, act):
+    pre = x64 @ W1.T + (b1 if b1 is not None else 0)
+    h = torch.nn.functional.gelu(pre) if act == W.ACT_GELU else torch.relu(pre)
+    return h @ W2.T + (b2 if b2 is not None else 0)
+
+
+@pytest.mark.parametrize("act", [W.ACT_GELU, W.ACT_RELU], ids=["gelu", "relu"])
+def test_single_expert_top1_is_dense_mlp(act):
+    # E=1, k=1, f=0: every gate is 1 and C = S, so the layer is a dense MLP.
+    w = W.Workload("mlp", S=33, M=32, E=1, k=1, H=48, capacity_factor=0.0, dtype=W.DT_F32, act=act)
+    inp = {k_: np_of(v) for k_, v in W.make_inputs(w, seed=4).items()}
+    fw = oracle.layer_forward(inp, w.k, w.capacity_factor, act, W.DT_F32)
+    assert fw["route"]["C"] == w.S and np.all(fw["route"]["gates"] == 1.0)
+    t = {k_: torch.from_numpy(v).double() for k_, v in inp.items()}
+    ref = _torch_mlp(t["x"], t["W1"][0], t["b1"][0], t["W2"][0], t["b2"][0], act).numpy()
+    # h is rounded to fp32 before fc2, y rounded to fp32: relative error ~ 1e-7
+    assert np.allclose(fw["out"], ref, rtol=2e-6, atol=1e-7)
+
+
+def test_identical_experts_closed_form():
+    # All experts share weights and nothing is dropped (f = 0): out[s] = (sum_r g_r) * MLP(x[s]).
+    # With k = E the gates sum to one and out = MLP(x).
+    S, M, E, H = 24, 16, 3, 32
+    rng = np.random.default_rng(5)
+    W1 = np.repeat((rng.standard_normal((1, H, M)) * 0.2).astype(np.float32), E, 0)
+    W2 = np.repeat((rng.standard_normal((1, M, H)) * 0.2).astype(np.float32), E, 0)
+    b1 = np.repeat((rng.standard_normal((1, H)) * 0.2).astype(np.float32), E, 0)
+    b2 = np.repeat((rng.standard_normal((1, M)) * 0.2).astype(np.float32), E, 0)
+    x = rng.standard_normal((S, M)).astype(np.float32)
+    logits = rng.standard_normal((S, E)).astype(np.float32)
+    ref = _torch_mlp(torch.from_numpy(x).double(), torch.from_numpy(W1[0]).double(),
+                     torch.from_numpy(b1[0]).double(), torch.from_numpy(W2[0]).double(),
+                     torch.from_numpy(b2[0]).double(), W.ACT_GELU).numpy()
+    for k in (1, 2, 3):
+        inp = dict(x=x, W1=W1, W2=W2, b1=b1, b2=b2)
+        fw = oracle.layer_forward(inp, k, 0.0, W.ACT_GELU, W.DT_F32, logits=logits)
+        gsum = fw["route"]["gates"].astype(np.float64).sum(axis=0)
+        assert np.allclose(fw["out"], gsum[:, None] * ref, rtol=1e-5, atol=1e-6)
+        if k == E:
+            assert np.allclose(fw["out"], ref, rtol=1e-5, atol=1e-6)
+
+
+def test_bf16_ffn_within_rounding_of_fp64_mlp():
+    w = W.Workload("mlp16", S=20, M=64, E=1, k=1, H=64, capacity_factor=0.0)
+    inp = {k_: np_of(v) for k_, v in W.make_inputs(w, seed=6).items()}
+    fw = oracle.layer_forward(inp, 1, 0.0, W.ACT_GELU, W.DT_BF16)
+    t = {k_: torch.from_numpy(f32_of(v)).double() for k_, v in inp.items() if k_ != "logits"}
+    ref = _torch_mlp(t["x"], t["W1"][0], t["b1"][0], t["W2"][0], t["b2"][0], W.ACT_GELU).numpy()
+    got = f32_of(fw["out"]).astype(np.float64)
+    rms = np.sqrt((ref ** 2).mean())
+    assert np.abs(got - ref).max() / rms < 2e-2  # bf16 h and y: ~2^-8 relative each
+
+
+# ---------------------------------------------------------------- backward
+
+def _dense_layer_torch(x, logits_route, W1, b1, W2, b2, act, E, C, idx, loc, gates):
+    """Dense (one-hot) formulation in fp64 torch: dispatch einsum, per-expert MLP by bmm,
+    per-route gate-weighted combine einsum."""
+    k, S = idx.shape
+    mask = torch.from_numpy(onehot_mask(idx, loc, E, C)).double()  # [k,S,E,C]
+    buf = torch.einsum("sec,sm->ecm", mask.sum(0), x)
+    pre = torch.bmm(buf, W1.transpose(1, 2).contiguous()) + b1[:, None, :]
+    h = torch.nn.functional.gelu(pre) if act == W.ACT_GELU else torch.relu(pre)
+    y = torch.bmm(h, W2.transpose(1, 2).contiguous()) + b2[:, None, :]
+    out = torch.zeros(S, x.shape[1], dtype=torch.float64)
+    for r in range(k):
+        out = out + torch.einsum("sec,ecm->sm", gates[r][:, None, None] * mask[r], y)
+    return out
+
+
+@pytest.mark.parametrize("act,k,f", [(W.ACT_GELU, 2, 0.0), (W.ACT_GELU, 3, -0.5), (W.ACT_RELU, 2, 0.75)])
+def test_backward_matches_autograd_of_dense_layer(act, k, f):
+    S, M, E, H = 16, 8, 3, 10
+    rng = np.random.default_rng(7 + k)
+    x = rng.standard_normal((S, M)).astype(np.float32)
+    logits = rng.standard_normal((S, E)).astype(np.float32)
+    W1 = (rng.standard_normal((E, H, M)) * 0.3).astype(np.float32)
+    W2 = (rng.standard_normal((E, M, H)) * 0.3).astype(np.float32)
+    b1 = (rng.standard_normal((E, H)) * 0.3).astype(np.float32)
+    b2 = (rng.standard_normal((E, M)) * 0.3).astype(np.float32)
+    dout = rng.standard_normal((S, M)).astype(np.float32)
+    inp = dict(x=x, W1=W1, W2=W2, b1=b1, b2=b2, dout=dout)
+    fw = oracle.layer_forward(inp, k, f, act, W.DT_F32, logits=logits)
+    bw = oracle.layer_backward(fw, inp, act, W.DT_F32)
+    rt = fw["route"]
+    tt = {n: torch.from_numpy(v).double().requires_grad_(True) for n, v in inp.items() if n != "dout"}
+    g = torch.from_numpy(rt["gates"]).double().requires_grad_(True)
+    out = _dense_layer_torch(tt["x"], logits, tt["W1"], tt["b1"], tt["W2"], tt["b2"], act, E, rt["C"],
+                             rt["idx"], rt["loc"], g)
+    assert np.allclose(fw["out"], out.detach().numpy(), rtol=1e-5, atol=1e-6)
+    grads = torch.autograd.grad((out * torch.from_numpy(dout).double()).sum(),
+                                [tt["x"], tt["W1"], tt["b1"], tt["W2"], tt["b2"], g])
+    names = ["dx", "dW1", "db1", "dW2", "db2", "dgates"]
+    for n, ref in zip(names, grads):
+        ref = ref.numpy()
+        got = bw[n].astype(np.float64)
+        scale = max(np.abs(ref).max(), 1e-30)
+        assert np.abs(got - ref).max() / scale < 2e-6, n
+    # dropped routes get no gate gradient
+    assert (bw["dgates"][rt["loc"] >= rt["C"]] == 0).all()
+
+
+def test_encode_decode_adjoint_identities():
+    # <encode(x), B> = <x, K0(B)> and <decode(y, g), D> = <y, K1'(D, g)>, the K0/K1 duality.
+    S, M, E, k = 30, 8, 4, 2
+    rng = np.random.default_rng(11)
+    logits = rng.standard_normal((S, E)).astype(np.float32)
+    rt = oracle.route(logits, k, 0.75)
+    C = rt["C"]
+    x = rng.standard_normal((S, M)).astype(np.float32)
+    B = rng.standard_normal((E * C, M)).astype(np.float32)
+    rows = oracle.filled_rows(rt)
+    routes = rt["slot_route"][rows]
+    lhs = (oracle.encode(x, rt, E, W.DT_F32).astype(np.float64) * B).sum()
+    K0B = oracle.dx_tokens(routes, B[rows], np.arange(S), S, k, W.DT_F32).astype(np.float64)
+    assert lhs == pytest.approx((x.astype(np.float64) * K0B).sum(), rel=1e-6)
+    y = rng.standard_normal((E * C, M)).astype(np.float32)
+    D = rng.standard_normal((S, M)).astype(np.float32)
+    lhs2 = (oracle.decode(y, rt, E, W.DT_F32).astype(np.float64) * D).sum()
+    # K1'(D, g): row slot of route (r, s) gets g[r][s] * D[s]
+    K1D = np.zeros((E * C, M))
+    for q in routes:
+        r, s = divmod(int(q), S)
+        K1D[rt["idx"][r, s] * C + rt["loc"][r, s]] = rt["gates"][r, s] * D[s].astype(np.float64)
+    assert lhs2 == pytest.approx((y.astype(np.float64) * K1D).sum(), rel=1e-6)
