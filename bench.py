@@ -1,0 +1,236 @@
+"""Benchmark of the single-GPU MoE layer on MI355X.
+
+One step = one pass of the whole layer over one batch of synthetic input that is
+already resident in HBM: for the default workload (S=4096 tokens, M=1024, E=8
+experts, top-2, H=4096, bf16, logits projected from x by an fp32 gate matrix,
+capacity_factor 1.25) that is gate projection -> route -> encode -> fc1 -> fc2
+-> decode; workloads with a backward add the backward of decode, FFN and
+encode. The timed region is exactly --steps calls of the fused C-ABI entry
+points, bracketed by synchronisations.
+
+A second timed loop records HIP events around each stage on the stream the
+library launches on, to report each stage against its roofline (bytes or flops
+the method must move or compute per launch, over the stage's average time).
+The CPU oracle is timed on a bounded sample of the same workload as a baseline.
+
+Prints one JSON line on stdout; diagnostics go to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/sec on 1 MI355X; encode/decode HBM GB/s; FFN MFMA util"
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+MFMA_BF16_PEAK_TFS = 2500.0  # dense bf16 MFMA
+FP32_VECTOR_PEAK_TFS = 157.3
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="gated_bf16_S4096_M1024_E8_k2_H4096",
+                    help="workload name (see workloads.py); default: the S=4096 gate-projected bf16 layer")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle FFN sample")
+    return ap.parse_args()
+
+
+def algorithmic(w, C, kept):
+    """Bytes (or flops) each stage must move (or compute), per launch."""
+    b = w.elem_bytes
+    S, M, E, k, H = w.S, w.M, w.E, w.k, w.H
+    st = {
+        "route": ("bytes", 4 * S * E + 12 * k * S + 4 * kept + 8 * E),
+        "encode": ("bytes", S * M * b + E * C * M * b + 8 * k * S),
+        "fc1": ("flops", 2 * M * H * kept),
+        "fc2": ("flops", 2 * M * H * kept),
+        "decode": ("bytes", kept * M * b + S * M * b + 12 * k * S),
+    }
+    if w.logits == "gate":
+        st["gate"] = ("bytes", S * M * b + 4 * M * E + 4 * S * E)
+    if w.backward:
+        # dy/dgates: read dout and kept y rows, write kept dy rows; dx: read kept dbuf rows, write dx;
+        # GEMMs: dh, dW2, dbuf, dW1 (2*M*H*kept flops each)
+        st["backward"] = ("flops", 8 * M * H * kept)
+    return st
+
+
+def roofline_of(kind, amount, ms, dtype_bf16=True):
+    if kind == "bytes":
+        ach = amount / (ms * 1e-3) / 1e9
+        return dict(bound="hbm", achieved=round(ach, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(ach / HBM_PEAK_GBS, 4))
+    ach = amount / (ms * 1e-3) / 1e12
+    peak = MFMA_BF16_PEAK_TFS if dtype_bf16 else FP32_VECTOR_PEAK_TFS
+    return dict(bound="mfma" if dtype_bf16 else "alu", achieved=round(ach, 2), peak=peak, unit="TFLOP/s",
+                frac=round(ach / peak, 4))
+
+
+def cpu_baseline(w, inp, C_gpu, budget_s):
+    """Time the CPU oracle on a bounded sample of the workload; returns the cpu_baseline object."""
+    import numpy as np
+    import oracle
+    from tests.helpers import np_of
+    ni = {k: np_of(v) for k, v in inp.items()}
+    t = {}
+    t0 = time.perf_counter()
+    if w.logits == "gate":
+        logits = oracle.gate_logits(ni["x"], ni["Wg"], w.dtype)
+    else:
+        logits = ni["logits"]
+    t["gate"] = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    rt = oracle.route(logits, w.k, w.capacity_factor, with_slots=False)
+    t["route"] = time.perf_counter() - t0
+    assert rt["C"] == C_gpu, (rt["C"], C_gpu)
+    t0 = time.perf_counter()
+    buf = oracle.encode(ni["x"], rt, w.E, w.dtype)
+    t["encode"] = time.perf_counter() - t0
+    rows = oracle.filled_rows(rt)
+    kept = len(rows)
+    # FFN on an evenly strided sample of the filled rows, sized to about budget_s
+    probe = rows[:: max(1, kept // 16)][:16]
+    t0 = time.perf_counter()
+    oracle.expert_rows(buf, ni["W1"], ni.get("b1"), ni["W2"], ni.get("b2"), probe, rt["C"], w.act, w.dtype)
+    per_row = (time.perf_counter() - t0) / max(1, len(probe))
+    n = int(min(kept, max(16, budget_s / max(per_row, 1e-9))))
+    sample = rows[:: max(1, kept // n)][:n]
+    t0 = time.perf_counter()
+    _, _, ys = oracle.expert_rows(buf, ni["W1"], ni.get("b1"), ni["W2"], ni.get("b2"), sample, rt["C"], w.act,
+                                  w.dtype)
+    t_sample = time.perf_counter() - t0
+    t["ffn"] = t_sample / len(sample) * kept
+    y = np.zeros((w.E * rt["C"], w.M), ys.dtype)  # decode's cost does not depend on the values
+    y[sample] = ys
+    t0 = time.perf_counter()
+    oracle.decode(y, rt, w.E, w.dtype)
+    t["decode"] = time.perf_counter() - t0
+    total = sum(t.values())
+    return dict(value=round(w.S / total, 2), unit="tokens/s", cores=oracle.num_threads(), kind="oracle",
+                sample=(f"gate/route/encode/decode on all {w.S} tokens; expert FFN on {len(sample)} of the {kept} "
+                        f"filled rows (evenly strided, {t_sample:.1f}s), scaled linearly to all filled rows; "
+                        f"forward only"),
+                seconds={k: round(v, 3) for k, v in t.items()})
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU's share of the layer: --gpus {args.gpus} is not supported "
+              "(this build has no multi-GPU path; run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import combine_softmax_top_amd as moe
+    import workloads as W
+
+    w = W.BY_NAME[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"[bench] workload {w.name}: generating inputs on the GPU")
+    inp = W.make_inputs(w, seed=0, device=dev)
+    s = moe.Shape.of(w)
+    gate = w.logits == "gate"
+    bufs = moe.alloc_forward(s, dev, training=w.backward, gate_projection=gate)
+    grads = moe.alloc_backward(s, dev) if w.backward else None
+    x, W1, W2, b1, b2 = inp["x"], inp["W1"], inp["W2"], inp.get("b1"), inp.get("b2")
+    logits_in, Wg = (None, inp["Wg"]) if gate else (inp["logits"], None)
+
+    def step():
+        moe.layer_forward(s, x, W1, b1, W2, b2, logits=logits_in, Wg=Wg, bufs=bufs)
+        if w.backward:
+            moe.layer_backward(s, bufs, inp["dout"], W1, W2, grads=grads)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] warmup done ({args.warmup} steps); timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / max(1, args.steps)
+    value = w.S * args.steps / elapsed
+
+    C = int(bufs["capacity"].item())
+    kept = int(bufs["fill"].sum().item())
+    log(f"[bench] {ms_per_step:.4f} ms/step, {value:.4g} tokens/s; C={C}, kept={kept}")
+
+    # ---- per-stage HIP-event timing on the library's stream
+    stream = torch.cuda.current_stream()
+    names = (["gate"] if gate else []) + ["route", "encode", "fc1", "fc2", "decode"] + (
+        ["backward"] if w.backward else [])
+    ev = {n: [] for n in names}
+    lg = bufs["logits"] if gate else logits_in
+    b = bufs
+
+    def stage(name, fn):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        ev[name].append((e0, e1))
+
+    for it in range(args.warmup + args.steps):
+        timed = it >= args.warmup
+        run = stage if timed else (lambda n, f: f())
+        if gate:
+            run("gate", lambda: moe.moe_gate_project(s, x, Wg, lg))
+        run("route", lambda: moe.moe_route(s, lg, b["idx"], b["loc"], b["gates"], b["needed"], b["fill"],
+                                           b["capacity"], b["slot_route"], b["ws"]))
+        run("encode", lambda: moe.moe_encode(s, x, b["idx"], b["loc"], b["fill"], b["capacity"], b["buf"]))
+        run("fc1", lambda: moe.moe_expert_fc1(s, b["buf"], W1, b1, b["fill"], b["capacity"], b["pre"], b["h"]))
+        run("fc2", lambda: moe.moe_expert_fc2(s, b["h"], W2, b2, b["fill"], b["capacity"], b["y"]))
+        run("decode", lambda: moe.moe_decode(s, b["y"], b["gates"], b["idx"], b["loc"], b["capacity"], b["out"]))
+        if w.backward:
+            run("backward", lambda: moe.layer_backward(s, b, inp["dout"], W1, W2, grads=grads))
+    torch.cuda.synchronize()
+    alg = algorithmic(w, C, kept)
+    stages = {}
+    for n in names:
+        ms = sum(e0.elapsed_time(e1) for e0, e1 in ev[n]) / len(ev[n])
+        kind, amount = alg[n]
+        r = roofline_of(kind, amount, ms, w.dtype == W.DT_BF16)
+        r["ms"] = round(ms, 5)
+        r["algorithmic_" + kind] = amount
+        stages[n] = r
+        log(f"[bench] stage {n:9s} {ms:9.4f} ms  {r['achieved']:10.2f} {r['unit']}  ({100 * r['frac']:.1f}% of peak)")
+    dominant = max((n for n in names if n != "backward"), key=lambda n: stages[n]["ms"])
+    d = stages[dominant]
+    roofline = dict(kernel=dominant, bound=d["bound"], achieved=d["achieved"], peak=d["peak"], unit=d["unit"],
+                    frac=d["frac"], traffic=None)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a bounded sample")
+        cpu = cpu_baseline(w, inp, C, args.cpu_seconds)
+        log(f"[bench] cpu baseline {cpu['value']} tokens/s on {cpu['cores']} threads: {cpu['sample']}")
+
+    line = dict(
+        metric=METRIC, value=round(value, 1), unit="tokens/s", n_gpus=1, steps=args.steps, warmup=args.warmup,
+        ms_per_step=round(ms_per_step, 5), higher_is_better=True, scaling="weak", vs_baseline=None,
+        dtype="bf16" if w.dtype == W.DT_BF16 else "f32", data="synthetic",
+        config=dict(workload=w.name, S=w.S, M=w.M, E=w.E, k=w.k, H=w.H, capacity_factor=w.capacity_factor,
+                    act="gelu" if w.act == W.ACT_GELU else "relu", biases=[w.has_fc1_bias, w.has_fc2_bias],
+                    logits=w.logits, backward=w.backward, C=C, kept_routes=kept, parallelism="single-gpu"),
+        roofline=roofline, stages=stages, cpu_baseline=cpu,
+    )
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,249 @@
+"""Python binding of the gfx950 MoE layer library (``libmoe.so``, C ABI in include/moe.h).
+
+Argument marshalling only: every step of the layer runs in the library's HIP
+kernels. PyTorch supplies device memory and the stream. Each function has the
+name of the C entry point it calls, takes torch tensors (or None for NULL), and
+raises ``MoeError`` on a non-OK status. Nothing here computes any part of the
+layer; if the library is missing, importing this package fails.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+from typing import Dict, Optional
+
+import torch  # loads the HIP runtime that libmoe.so then binds to
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmoe.so")
+
+MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP = 0, -1, -2, -3, -4
+MOE_DT_F32, MOE_DT_BF16 = 0, 1
+MOE_ACT_RELU, MOE_ACT_GELU = 0, 1
+
+STATUS_NAMES = {0: "MOE_OK", -1: "MOE_EINVAL", -2: "MOE_EUNSUPPORTED", -3: "MOE_EWORKSPACE", -4: "MOE_EHIP"}
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+class moe_shape(ctypes.Structure):
+    _fields_ = [("S", ctypes.c_int32), ("M", ctypes.c_int32), ("E", ctypes.c_int32), ("k", ctypes.c_int32),
+                ("H", ctypes.c_int32), ("capacity_factor", ctypes.c_double), ("dtype", ctypes.c_int32),
+                ("act", ctypes.c_int32), ("has_fc1_bias", ctypes.c_int32), ("has_fc2_bias", ctypes.c_int32)]
+
+
+@dataclasses.dataclass(frozen=True)
+class Shape:
+    S: int
+    M: int
+    E: int
+    k: int
+    H: int
+    capacity_factor: float
+    dtype: int = MOE_DT_BF16
+    act: int = MOE_ACT_GELU
+    has_fc1_bias: bool = True
+    has_fc2_bias: bool = True
+
+    def c(self) -> moe_shape:
+        return moe_shape(self.S, self.M, self.E, self.k, self.H, float(self.capacity_factor), self.dtype, self.act,
+                         int(bool(self.has_fc1_bias)), int(bool(self.has_fc2_bias)))
+
+    @property
+    def torch_dtype(self) -> torch.dtype:
+        return torch.float32 if self.dtype == MOE_DT_F32 else torch.bfloat16
+
+    @staticmethod
+    def of(w) -> "Shape":
+        """From any object with the layer's fields (e.g. a workload description)."""
+        return Shape(w.S, w.M, w.E, w.k, w.H, w.capacity_factor, w.dtype, w.act, w.has_fc1_bias, w.has_fc2_bias)
+
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m combine_softmax_top_amd.build` "
+                      "(or __graft_entry__.build()); there is no fallback path")
+_lib = ctypes.CDLL(LIB_PATH)
+
+_P = ctypes.c_void_p
+_SP = ctypes.POINTER(moe_shape)
+_SIGS = {
+    "moe_validate": [_SP],
+    "moe_capacity_bound": [_SP, ctypes.POINTER(ctypes.c_int32)],
+    "moe_workspace_size": [_SP, ctypes.POINTER(ctypes.c_size_t)],
+    "moe_gate_project": [_SP, _P, _P, _P, _P],
+    "moe_route": [_SP, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
+    "moe_encode": [_SP, _P, _P, _P, _P, _P, _P, _P],
+    "moe_expert_ffn": [_SP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
+    "moe_expert_fc1": [_SP, _P, _P, _P, _P, _P, _P, _P, _P],
+    "moe_expert_fc2": [_SP, _P, _P, _P, _P, _P, _P, _P],
+    "moe_decode": [_SP, _P, _P, _P, _P, _P, _P, _P],
+    "moe_layer_forward": [_SP] + [_P] * 21 + [ctypes.c_size_t, _P],
+    "moe_layer_backward": [_SP] + [_P] * 22,
+}
+for _name, _args in _SIGS.items():
+    _fn = getattr(_lib, _name)
+    _fn.argtypes = _args
+    _fn.restype = ctypes.c_int
+_lib.moe_last_error.argtypes = []
+_lib.moe_last_error.restype = ctypes.c_char_p
+
+EXPORTED = sorted(list(_SIGS) + ["moe_last_error"])
+
+
+def moe_last_error() -> str:
+    return _lib.moe_last_error().decode()
+
+
+def _check(status: int) -> None:
+    if status != MOE_OK:
+        raise MoeError(status, moe_last_error())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to the MoE library must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+def moe_validate(shape: Shape) -> int:
+    return _lib.moe_validate(ctypes.byref(shape.c()))
+
+
+def moe_capacity_bound(shape: Shape) -> int:
+    c = ctypes.c_int32()
+    _check(_lib.moe_capacity_bound(ctypes.byref(shape.c()), ctypes.byref(c)))
+    return c.value
+
+
+def moe_workspace_size(shape: Shape) -> int:
+    n = ctypes.c_size_t()
+    _check(_lib.moe_workspace_size(ctypes.byref(shape.c()), ctypes.byref(n)))
+    return n.value
+
+
+def moe_gate_project(shape: Shape, x, Wg, logits, stream=None) -> None:
+    _check(_lib.moe_gate_project(ctypes.byref(shape.c()), _ptr(x), _ptr(Wg), _ptr(logits), _stream(stream)))
+
+
+def moe_route(shape: Shape, logits, idx, loc, gates, needed, fill, capacity, slot_route, ws, stream=None) -> None:
+    _check(_lib.moe_route(ctypes.byref(shape.c()), _ptr(logits), _ptr(idx), _ptr(loc), _ptr(gates), _ptr(needed),
+                          _ptr(fill), _ptr(capacity), _ptr(slot_route), _ptr(ws),
+                          0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def moe_encode(shape: Shape, x, idx, loc, fill, capacity, buf, stream=None) -> None:
+    _check(_lib.moe_encode(ctypes.byref(shape.c()), _ptr(x), _ptr(idx), _ptr(loc), _ptr(fill), _ptr(capacity),
+                           _ptr(buf), _stream(stream)))
+
+
+def moe_expert_ffn(shape: Shape, buf, W1, b1, W2, b2, fill, capacity, pre, h, y, stream=None) -> None:
+    _check(_lib.moe_expert_ffn(ctypes.byref(shape.c()), _ptr(buf), _ptr(W1), _ptr(b1), _ptr(W2), _ptr(b2),
+                               _ptr(fill), _ptr(capacity), _ptr(pre), _ptr(h), _ptr(y), _stream(stream)))
+
+
+def moe_expert_fc1(shape: Shape, buf, W1, b1, fill, capacity, pre, h, stream=None) -> None:
+    _check(_lib.moe_expert_fc1(ctypes.byref(shape.c()), _ptr(buf), _ptr(W1), _ptr(b1), _ptr(fill), _ptr(capacity),
+                               _ptr(pre), _ptr(h), _stream(stream)))
+
+
+def moe_expert_fc2(shape: Shape, h, W2, b2, fill, capacity, y, stream=None) -> None:
+    _check(_lib.moe_expert_fc2(ctypes.byref(shape.c()), _ptr(h), _ptr(W2), _ptr(b2), _ptr(fill), _ptr(capacity),
+                               _ptr(y), _stream(stream)))
+
+
+def moe_decode(shape: Shape, y, gates, idx, loc, capacity, out, stream=None) -> None:
+    _check(_lib.moe_decode(ctypes.byref(shape.c()), _ptr(y), _ptr(gates), _ptr(idx), _ptr(loc), _ptr(capacity),
+                           _ptr(out), _stream(stream)))
+
+
+def moe_layer_forward(shape: Shape, x, logits_in, Wg, logits_out, W1, b1, W2, b2, idx, loc, gates, needed, fill,
+                      capacity, slot_route, buf, pre, h, y, out, ws, stream=None) -> None:
+    _check(_lib.moe_layer_forward(
+        ctypes.byref(shape.c()), _ptr(x), _ptr(logits_in), _ptr(Wg), _ptr(logits_out), _ptr(W1), _ptr(b1), _ptr(W2),
+        _ptr(b2), _ptr(idx), _ptr(loc), _ptr(gates), _ptr(needed), _ptr(fill), _ptr(capacity), _ptr(slot_route),
+        _ptr(buf), _ptr(pre), _ptr(h), _ptr(y), _ptr(out), _ptr(ws),
+        0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def moe_layer_backward(shape: Shape, dout, buf, pre, h, y, gates, idx, loc, fill, capacity, W1, W2, dy, dpre, dbuf,
+                       dx, dW1, db1, dW2, db2, dgates, stream=None) -> None:
+    _check(_lib.moe_layer_backward(
+        ctypes.byref(shape.c()), _ptr(dout), _ptr(buf), _ptr(pre), _ptr(h), _ptr(y), _ptr(gates), _ptr(idx),
+        _ptr(loc), _ptr(fill), _ptr(capacity), _ptr(W1), _ptr(W2), _ptr(dy), _ptr(dpre), _ptr(dbuf), _ptr(dx),
+        _ptr(dW1), _ptr(db1), _ptr(dW2), _ptr(db2), _ptr(dgates), _stream(stream)))
+
+
+# ---------------------------------------------------------------- buffers
+
+def alloc_forward(shape: Shape, device="cuda", training: bool = False,
+                  gate_projection: bool = False) -> Dict[str, torch.Tensor]:
+    """Allocate every output and scratch buffer the forward writes, sized with the host
+    capacity bound (torch.empty: contents undefined until the library writes them)."""
+    S, M, E, k, H = shape.S, shape.M, shape.E, shape.k, shape.H
+    cmax = moe_capacity_bound(shape)
+    dt = shape.torch_dtype
+    i32 = dict(dtype=torch.int32, device=device)
+    bufs = dict(
+        idx=torch.empty(k, S, **i32), loc=torch.empty(k, S, **i32),
+        gates=torch.empty(k, S, dtype=torch.float32, device=device),
+        needed=torch.empty(E, **i32), fill=torch.empty(E, **i32), capacity=torch.empty(1, **i32),
+        slot_route=torch.empty(E * cmax, **i32),
+        buf=torch.empty(E * cmax, M, dtype=dt, device=device),
+        h=torch.empty(E * cmax, H, dtype=dt, device=device),
+        y=torch.empty(E * cmax, M, dtype=dt, device=device),
+        out=torch.empty(S, M, dtype=dt, device=device),
+        ws=torch.empty(max(1, moe_workspace_size(shape)), dtype=torch.uint8, device=device),
+    )
+    bufs["pre"] = torch.empty(E * cmax, H, dtype=dt, device=device) if training else None
+    bufs["logits"] = torch.empty(S, E, dtype=torch.float32, device=device) if gate_projection else None
+    return bufs
+
+
+def layer_forward(shape: Shape, x, W1, b1, W2, b2, logits=None, Wg=None, bufs=None, training=False, stream=None):
+    """Run the fused forward into ``bufs`` (allocated if None) and return them."""
+    if bufs is None:
+        bufs = alloc_forward(shape, x.device, training=training, gate_projection=Wg is not None)
+    moe_layer_forward(shape, x, logits, Wg, bufs["logits"] if Wg is not None else None, W1, b1, W2, b2,
+                      bufs["idx"], bufs["loc"], bufs["gates"], bufs["needed"], bufs["fill"], bufs["capacity"],
+                      bufs["slot_route"], bufs["buf"], bufs["pre"], bufs["h"], bufs["y"], bufs["out"], bufs["ws"],
+                      stream)
+    return bufs
+
+
+def alloc_backward(shape: Shape, device="cuda") -> Dict[str, torch.Tensor]:
+    S, M, E, k, H = shape.S, shape.M, shape.E, shape.k, shape.H
+    cmax = moe_capacity_bound(shape)
+    dt = shape.torch_dtype
+    f32 = dict(dtype=torch.float32, device=device)
+    dyb = torch.empty(E * cmax, M, dtype=dt, device=device)
+    return dict(
+        dy=dyb, dbuf=dyb,  # dbuf reuses dy's memory (allowed by the ABI)
+        dpre=torch.empty(E * cmax, H, dtype=dt, device=device),
+        dx=torch.empty(S, M, dtype=dt, device=device),
+        dW1=torch.empty(E, H, M, **f32), dW2=torch.empty(E, M, H, **f32),
+        db1=torch.empty(E, H, **f32) if shape.has_fc1_bias else None,
+        db2=torch.empty(E, M, **f32) if shape.has_fc2_bias else None,
+        dgates=torch.empty(k, S, **f32),
+    )
+
+
+def layer_backward(shape: Shape, fw: Dict[str, torch.Tensor], dout, W1, W2, grads=None, stream=None):
+    if grads is None:
+        grads = alloc_backward(shape, dout.device)
+    moe_layer_backward(shape, dout, fw["buf"], fw["pre"], fw["h"], fw["y"], fw["gates"], fw["idx"], fw["loc"],
+                       fw["fill"], fw["capacity"], W1, W2, grads["dy"], grads["dpre"], grads["dbuf"], grads["dx"],
+                       grads["dW1"], grads["db1"], grads["dW2"], grads["db2"], grads["dgates"], stream)
+    return grads

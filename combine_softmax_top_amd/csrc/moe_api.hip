@@ -1,0 +1,261 @@
+// The C ABI (include/moe.h): argument checks on the host, then launches on the
+// caller's stream. Nothing here allocates or synchronises.
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "moe_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+moe_status fail(moe_status st, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+moe_status fail(moe_status st, const char *fmt, ...) {
+    char msg[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(msg, sizeof msg, fmt, ap);
+    va_end(ap);
+    g_last_error = msg;
+    return st;
+}
+
+moe_status hip_fail(hipError_t e, const char *where) {
+    return fail(MOE_EHIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+#define MOE_REQUIRE(cond, ...)                         \
+    do {                                               \
+        if (!(cond)) return fail(MOE_EINVAL, __VA_ARGS__); \
+    } while (0)
+
+int64_t by_factor(const moe_shape &s) {
+    // ceil(k * S * |f| / E), the capacity a factor of |f| gives
+    return static_cast<int64_t>(std::ceil((static_cast<double>(s.k) * static_cast<double>(s.S) *
+                                           std::fabs(s.capacity_factor)) / static_cast<double>(s.E)));
+}
+
+int64_t cap_bound(const moe_shape &s) {
+    int64_t c;
+    if (s.capacity_factor > 0) c = by_factor(s);
+    else if (s.capacity_factor == 0) c = s.S;
+    else c = std::min<int64_t>(by_factor(s), s.S);
+    return c < 1 ? 1 : c;
+}
+
+int32_t num_tiles(const moe_shape &s) { return (s.S + moe::kRouteTile - 1) / moe::kRouteTile; }
+
+size_t ws_bytes_needed(const moe_shape &s) {
+    const size_t n = static_cast<size_t>(s.E) * s.k * num_tiles(s);
+    return ((n * sizeof(int32_t)) + 255) & ~static_cast<size_t>(255);
+}
+
+moe_status check_shape(const moe_shape *sp) {
+    if (sp == nullptr) return fail(MOE_EINVAL, "shape is NULL");
+    const moe_shape &s = *sp;
+    if (s.S < 0 || s.M <= 0 || s.E <= 0 || s.H <= 0 || s.k <= 0)
+        return fail(MOE_EINVAL, "sizes must be positive (S >= 0): S=%d M=%d E=%d k=%d H=%d", s.S, s.M, s.E, s.k, s.H);
+    if (s.k > s.E) return fail(MOE_EINVAL, "k=%d exceeds E=%d", s.k, s.E);
+    if (!std::isfinite(s.capacity_factor)) return fail(MOE_EINVAL, "capacity_factor is not finite");
+    if (s.dtype != MOE_DT_F32 && s.dtype != MOE_DT_BF16) return fail(MOE_EINVAL, "unknown dtype %d", s.dtype);
+    if (s.act != MOE_ACT_RELU && s.act != MOE_ACT_GELU) return fail(MOE_EINVAL, "unknown activation %d", s.act);
+    if (s.k > moe::kMaxK) return fail(MOE_EUNSUPPORTED, "k=%d above the supported %d", s.k, moe::kMaxK);
+    if (s.E > moe::kMaxE) return fail(MOE_EUNSUPPORTED, "E=%d above the supported %d", s.E, moe::kMaxE);
+    if (s.M % 64 != 0 || s.H % 64 != 0)
+        return fail(MOE_EUNSUPPORTED, "M=%d and H=%d must be multiples of 64", s.M, s.H);
+    if (static_cast<int64_t>(s.S) * s.k >= (int64_t(1) << 31))
+        return fail(MOE_EUNSUPPORTED, "S*k=%lld routes exceed int32 indices", (long long)s.S * s.k);
+    const int64_t rows = static_cast<int64_t>(s.E) * cap_bound(s);
+    if (rows >= (int64_t(1) << 31))
+        return fail(MOE_EUNSUPPORTED, "E*C bound %lld rows exceeds int32 slot indices", (long long)rows);
+    if (cap_bound(s) / 128 >= 65535) return fail(MOE_EUNSUPPORTED, "capacity bound too large for the GEMM grid");
+    return MOE_OK;
+}
+
+hipStream_t as_stream(void *p) { return reinterpret_cast<hipStream_t>(p); }
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_validate(const moe_shape *shape) { return check_shape(shape); }
+
+moe_status moe_capacity_bound(const moe_shape *shape, int32_t *cmax_host) {
+    moe_status st = check_shape(shape);
+    if (st != MOE_OK) return st;
+    MOE_REQUIRE(cmax_host != nullptr, "cmax_host is NULL");
+    *cmax_host = static_cast<int32_t>(cap_bound(*shape));
+    return MOE_OK;
+}
+
+moe_status moe_workspace_size(const moe_shape *shape, size_t *bytes_host) {
+    moe_status st = check_shape(shape);
+    if (st != MOE_OK) return st;
+    MOE_REQUIRE(bytes_host != nullptr, "bytes_host is NULL");
+    *bytes_host = ws_bytes_needed(*shape);
+    return MOE_OK;
+}
+
+moe_status moe_gate_project(const moe_shape *shape, const void *x, const float *Wg, float *logits, void *stream) {
+    moe_status st = check_shape(shape);
+    if (st != MOE_OK) return st;
+    const moe_shape &s = *shape;
+    if (s.S > 0) MOE_REQUIRE(x && Wg && logits, "x, Wg and logits must be non-NULL");
+    hipError_t e = moe::launch_gate_project(s, x, Wg, logits, as_stream(stream));
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "gate projection");
+}
+
+moe_status moe_route(const moe_shape *shape, const float *logits, int32_t *idx, int32_t *loc, float *gates,
+                     int32_t *needed, int32_t *fill, int32_t *capacity, int32_t *slot_route, void *ws,
+                     size_t ws_bytes, void *stream) {
+    moe_status st = check_shape(shape);
+    if (st != MOE_OK) return st;
+    const moe_shape &s = *shape;
+    MOE_REQUIRE(needed && fill && capacity, "needed, fill and capacity must be non-NULL");
+    if (s.S > 0) MOE_REQUIRE(logits && idx && loc && gates, "logits, idx, loc and gates must be non-NULL");
+    const size_t need = ws_bytes_needed(s);
+    if (need > 0 && (ws == nullptr || ws_bytes < need))
+        return fail(MOE_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws == nullptr ? 0 : ws_bytes);
+    moe::RouteWs w{static_cast<int32_t *>(ws), num_tiles(s)};
+    hipError_t e = moe::launch_route(s, logits, idx, loc, gates, needed, fill, capacity, slot_route, w, by_factor(s),
+                                     as_stream(stream));
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "route");
+}
+
+moe_status moe_encode(const moe_shape *shape, const void *x, const int32_t *idx, const int32_t *loc,
+                      const int32_t *fill, const int32_t *capacity, void *buf, void *stream) {
+    moe_status st = check_shape(shape);
+    if (st != MOE_OK) return st;
+    const moe_shape &s = *shape;
+    MOE_REQUIRE(fill && capacity && buf, "fill, capacity and buf must be non-NULL");
+    if (s.S > 0) MOE_REQUIRE(x && idx && loc, "x, idx and loc must be non-NULL");
+    hipError_t e = moe::launch_encode(s, x, idx, loc, fill, capacity, buf, static_cast<int32_t>(cap_bound(s)),
+                                      as_stream(stream));
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "encode");
+}
+
+moe_status moe_expert_ffn(const moe_shape *shape, const void *buf, const void *W1, const void *b1, const void *W2,
+                          const void *b2, const int32_t *fill, const int32_t *capacity, void *pre, void *h, void *y,
+                          void *stream) {
+    moe_status st = check_shape(shape);
+    if (st != MOE_OK) return st;
+    const moe_shape &s = *shape;
+    MOE_REQUIRE(buf && W1 && W2 && fill && capacity && h && y, "buf, W1, W2, fill, capacity, h and y must be non-NULL");
+    MOE_REQUIRE((b1 != nullptr) == (s.has_fc1_bias != 0), "b1 must be given iff has_fc1_bias");
+    MOE_REQUIRE((b2 != nullptr) == (s.has_fc2_bias != 0), "b2 must be given iff has_fc2_bias");
+    const int32_t cmax = static_cast<int32_t>(cap_bound(s));
+    hipError_t e = moe::launch_fc1(s, buf, W1, b1, fill, capacity, pre, h, cmax, as_stream(stream));
+    if (e != hipSuccess) return hip_fail(e, "expert fc1");
+    e = moe::launch_fc2(s, h, W2, b2, fill, capacity, y, cmax, as_stream(stream));
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "expert fc2");
+}
+
+moe_status moe_expert_fc1(const moe_shape *shape, const void *buf, const void *W1, const void *b1,
+                          const int32_t *fill, const int32_t *capacity, void *pre, void *h, void *stream) {
+    moe_status st = check_shape(shape);
+    if (st != MOE_OK) return st;
+    const moe_shape &s = *shape;
+    MOE_REQUIRE(buf && W1 && fill && capacity && h, "buf, W1, fill, capacity and h must be non-NULL");
+    MOE_REQUIRE((b1 != nullptr) == (s.has_fc1_bias != 0), "b1 must be given iff has_fc1_bias");
+    hipError_t e = moe::launch_fc1(s, buf, W1, b1, fill, capacity, pre, h, static_cast<int32_t>(cap_bound(s)),
+                                   as_stream(stream));
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "expert fc1");
+}
+
+moe_status moe_expert_fc2(const moe_shape *shape, const void *h, const void *W2, const void *b2,
+                          const int32_t *fill, const int32_t *capacity, void *y, void *stream) {
+    moe_status st = check_shape(shape);
+    if (st != MOE_OK) return st;
+    const moe_shape &s = *shape;
+    MOE_REQUIRE(h && W2 && fill && capacity && y, "h, W2, fill, capacity and y must be non-NULL");
+    MOE_REQUIRE((b2 != nullptr) == (s.has_fc2_bias != 0), "b2 must be given iff has_fc2_bias");
+    hipError_t e = moe::launch_fc2(s, h, W2, b2, fill, capacity, y, static_cast<int32_t>(cap_bound(s)),
+                                   as_stream(stream));
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "expert fc2");
+}
+
+moe_status moe_decode(const moe_shape *shape, const void *y, const float *gates, const int32_t *idx,
+                      const int32_t *loc, const int32_t *capacity, void *out, void *stream) {
+    moe_status st = check_shape(shape);
+    if (st != MOE_OK) return st;
+    const moe_shape &s = *shape;
+    MOE_REQUIRE(capacity != nullptr, "capacity is NULL");
+    if (s.S > 0) MOE_REQUIRE(y && gates && idx && loc && out, "y, gates, idx, loc and out must be non-NULL");
+    hipError_t e = moe::launch_decode(s, y, gates, idx, loc, capacity, out, false, as_stream(stream));
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "decode");
+}
+
+moe_status moe_layer_forward(const moe_shape *shape, const void *x, const float *logits_in, const float *Wg,
+                             float *logits_out, const void *W1, const void *b1, const void *W2, const void *b2,
+                             int32_t *idx, int32_t *loc, float *gates, int32_t *needed, int32_t *fill,
+                             int32_t *capacity, int32_t *slot_route, void *buf, void *pre, void *h, void *y,
+                             void *out, void *ws, size_t ws_bytes, void *stream) {
+    moe_status st = check_shape(shape);
+    if (st != MOE_OK) return st;
+    const moe_shape &s = *shape;
+    // with no token, empty logits may arrive as NULL
+    MOE_REQUIRE(!(logits_in != nullptr && Wg != nullptr), "exactly one of logits_in and Wg must be given");
+    MOE_REQUIRE(s.S == 0 || logits_in != nullptr || Wg != nullptr, "exactly one of logits_in and Wg must be given");
+    MOE_REQUIRE(Wg == nullptr || logits_out != nullptr || s.S == 0, "logits_out is required with Wg");
+    MOE_REQUIRE(needed && fill && capacity && buf && W1 && W2 && h && y,
+                "needed, fill, capacity, buf, W1, W2, h and y must be non-NULL");
+    if (s.S > 0) MOE_REQUIRE(x && idx && loc && gates && out, "x, idx, loc, gates and out must be non-NULL");
+    MOE_REQUIRE((b1 != nullptr) == (s.has_fc1_bias != 0), "b1 must be given iff has_fc1_bias");
+    MOE_REQUIRE((b2 != nullptr) == (s.has_fc2_bias != 0), "b2 must be given iff has_fc2_bias");
+    const size_t need = ws_bytes_needed(s);
+    if (need > 0 && (ws == nullptr || ws_bytes < need))
+        return fail(MOE_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws == nullptr ? 0 : ws_bytes);
+    hipStream_t strm = as_stream(stream);
+    const int32_t cmax = static_cast<int32_t>(cap_bound(s));
+    const float *logits = logits_in;
+    hipError_t e;
+    if (Wg != nullptr && s.S > 0) {
+        if ((e = moe::launch_gate_project(s, x, Wg, logits_out, strm)) != hipSuccess) return hip_fail(e, "gate projection");
+        logits = logits_out;
+    }
+    moe::RouteWs w{static_cast<int32_t *>(ws), num_tiles(s)};
+    if ((e = moe::launch_route(s, logits, idx, loc, gates, needed, fill, capacity, slot_route, w, by_factor(s), strm)) !=
+        hipSuccess)
+        return hip_fail(e, "route");
+    if ((e = moe::launch_encode(s, x, idx, loc, fill, capacity, buf, cmax, strm)) != hipSuccess)
+        return hip_fail(e, "encode");
+    if ((e = moe::launch_fc1(s, buf, W1, b1, fill, capacity, pre, h, cmax, strm)) != hipSuccess)
+        return hip_fail(e, "expert fc1");
+    if ((e = moe::launch_fc2(s, h, W2, b2, fill, capacity, y, cmax, strm)) != hipSuccess)
+        return hip_fail(e, "expert fc2");
+    if ((e = moe::launch_decode(s, y, gates, idx, loc, capacity, out, false, strm)) != hipSuccess)
+        return hip_fail(e, "decode");
+    return MOE_OK;
+}
+
+moe_status moe_layer_backward(const moe_shape *shape, const void *dout, const void *buf, const void *pre,
+                              const void *h, const void *y, const float *gates, const int32_t *idx,
+                              const int32_t *loc, const int32_t *fill, const int32_t *capacity, const void *W1,
+                              const void *W2, void *dy, void *dpre, void *dbuf, void *dx, float *dW1, float *db1,
+                              float *dW2, float *db2, float *dgates, void *stream) {
+    moe_status st = check_shape(shape);
+    if (st != MOE_OK) return st;
+    const moe_shape &s = *shape;
+    MOE_REQUIRE(buf && pre && h && y && fill && capacity && W1 && W2 && dy && dpre && dbuf && dW1 && dW2,
+                "buf, pre, h, y, fill, capacity, W1, W2, dy, dpre, dbuf, dW1 and dW2 must be non-NULL");
+    if (s.S > 0) MOE_REQUIRE(dout && gates && idx && loc && dx && dgates, "dout, gates, idx, loc, dx and dgates must be non-NULL");
+    hipStream_t strm = as_stream(stream);
+    const int32_t cmax = static_cast<int32_t>(cap_bound(s));
+    hipError_t e;
+    if ((e = moe::launch_decode_bwd(s, dout, y, gates, idx, loc, capacity, dy, dgates, strm)) != hipSuccess)
+        return hip_fail(e, "decode backward");
+    if ((e = moe::launch_expert_ffn_bwd(s, buf, pre, h, W1, W2, fill, capacity, dy, dpre, dbuf, dW1, db1, dW2, db2,
+                                        cmax, strm)) != hipSuccess)
+        return hip_fail(e, "expert ffn backward");
+    if ((e = moe::launch_decode(s, dbuf, nullptr, idx, loc, capacity, dx, true, strm)) != hipSuccess)
+        return hip_fail(e, "encode backward");
+    return MOE_OK;
+}
+
+const char *moe_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

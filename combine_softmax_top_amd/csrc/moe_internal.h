@@ -1,0 +1,90 @@
+// Internal declarations of the gfx950 MoE library: device helpers shared by the
+// kernels and the host launchers that the C ABI (moe_api.hip) calls.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+constexpr int kWave = 64;          // CDNA wavefront
+constexpr int kRouteTile = 64;     // tokens per routing tile: one wavefront, one lane per token
+constexpr int kMaxK = 32;
+constexpr int kMaxE = 512;
+
+typedef uint16_t bf16_t;           // bf16 bit pattern
+
+// ------------------------------------------------------------- device helpers
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t b) {
+    return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Round to nearest even (finite values), the rounding of every bf16 store.
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return static_cast<bf16_t>(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+}
+
+// GELU in its exact erf form and its derivative, fp32.
+__device__ __forceinline__ float gelu_f(float v) {
+    return 0.5f * v * (1.0f + erff(v * 0.70710678118654752f));
+}
+__device__ __forceinline__ float gelu_grad_f(float v) {
+    const float cdf = 0.5f * (1.0f + erff(v * 0.70710678118654752f));
+    const float pdf = 0.39894228040143268f * __expf(-0.5f * v * v);
+    return cdf + v * pdf;
+}
+
+template <int ACT>
+__device__ __forceinline__ float act_f(float v) {
+    if constexpr (ACT == MOE_ACT_RELU) return v > 0.f ? v : 0.f;
+    else return gelu_f(v);
+}
+template <int ACT>
+__device__ __forceinline__ float act_grad_f(float v) {
+    if constexpr (ACT == MOE_ACT_RELU) return v > 0.f ? 1.f : 0.f;
+    else return gelu_grad_f(v);
+}
+
+// ------------------------------------------------------------- host launchers
+// Each returns hipSuccess or the launch error; arguments were validated by the
+// caller. `cap` and `fill` are device pointers written by the routing step.
+
+struct RouteWs {
+    int32_t *counts;  // [E][k][nblk] per-tile route counts, scanned in place to offsets
+    int32_t nblk;
+};
+
+hipError_t launch_gate_project(const moe_shape &s, const void *x, const float *Wg, float *logits,
+                               hipStream_t st);
+hipError_t launch_route(const moe_shape &s, const float *logits, int32_t *idx, int32_t *loc,
+                        float *gates, int32_t *needed, int32_t *fill, int32_t *cap, int32_t *slot_route,
+                        RouteWs ws, int64_t cap_by_factor, hipStream_t st);
+hipError_t launch_encode(const moe_shape &s, const void *x, const int32_t *idx, const int32_t *loc,
+                         const int32_t *fill, const int32_t *cap, void *buf, int32_t cmax,
+                         hipStream_t st);
+// Gate-weighted combine (unit_gates = false) or plain gather-sum (gates ignored).
+hipError_t launch_decode(const moe_shape &s, const void *y, const float *gates, const int32_t *idx,
+                         const int32_t *loc, const int32_t *cap, void *out, bool unit_gates,
+                         hipStream_t st);
+hipError_t launch_decode_bwd(const moe_shape &s, const void *dout, const void *y, const float *gates,
+                             const int32_t *idx, const int32_t *loc, const int32_t *cap, void *dy,
+                             float *dgates, hipStream_t st);
+hipError_t launch_fc1(const moe_shape &s, const void *buf, const void *W1, const void *b1, const int32_t *fill,
+                      const int32_t *cap, void *pre, void *h, int32_t cmax, hipStream_t st);
+hipError_t launch_fc2(const moe_shape &s, const void *h, const void *W2, const void *b2, const int32_t *fill,
+                      const int32_t *cap, void *y, int32_t cmax, hipStream_t st);
+hipError_t launch_expert_ffn_bwd(const moe_shape &s, const void *buf, const void *pre, const void *h,
+                                 const void *W1, const void *W2, const int32_t *fill,
+                                 const int32_t *cap, void *dy, void *dpre, void *dbuf, float *dW1,
+                                 float *db1, float *dW2, float *db2, int32_t cmax, hipStream_t st);
+
+}  // namespace moe

@@ -1,0 +1,204 @@
+/*
+ * moe.h — C ABI of the single-GPU Mixture-of-Experts layer for MI355X (gfx950).
+ *
+ * The layer, as the Tutel and DeepSpeed-MoE pages describe it:
+ *   1. gate: per token, softmax over E gate logits and the k largest experts
+ *      (Tutel catalogue page, "key configuration": gate_type
+ *      {'type': 'top', 'k': ..., 'capacity_factor': ...});
+ *   2. capacity-bounded slots: each route's location is the count of earlier
+ *      routes to the same expert; capacity C follows capacity_factor (catalogue
+ *      page FAQ: positive = fixed factor X, 0 = max needed volume, negative =
+ *      min(-X, max needed); MoE training blog, part 3 section 3.5, "dynamic
+ *      capacity factor"); routes at or beyond C are dropped;
+ *   3. fast encode: tokens are copied into a flat [E*C, M] expert buffer by
+ *      index (blog part 3 section 3.5 "fast encode/decode"; DeepSpeed PR #8195
+ *      sections 2 and 3);
+ *   4. expert FFN: fc1 + bias, activation, fc2 + bias per expert (catalogue
+ *      page: experts {'type': 'ffn', hidden size per expert, has_fc1_bias,
+ *      has_fc2_bias}, biases default on);
+ *   5. fast decode: out[s] = sum of gate * expert output over the token's kept
+ *      routes, accumulated in fp32 (DeepSpeed PR #8195 section 3).
+ * The backward covers decode (gate-weighted scatter of dout and the gate
+ * gradient, kernels K1/K2 of blog part 3 section 3.5), the expert FFN (data
+ * and fp32 weight/bias gradients) and encode (gather-sum, kernel K0).
+ *
+ * Conventions shared by every call:
+ *  - Pointers named *_host are host memory; every other pointer is device
+ *    memory allocated and owned by the caller. The library allocates nothing
+ *    and keeps no state between calls; calls on different streams may overlap.
+ *  - `stream` is a hipStream_t (NULL = the null stream). Device work is only
+ *    enqueued; no call waits for the device.
+ *  - Data-type tensors (x, W1, b1, W2, b2, buf, pre, h, y, out, dout, dx, dy,
+ *    dpre, dbuf) are fp32 or bf16 as moe_shape.dtype says. logits, Wg, gates,
+ *    dgates and the weight/bias gradients are fp32. Index tables are int32.
+ *  - Route tables are route-major [k, S]: entry r*S + s is route r of token s,
+ *    r = 0 the largest gate.
+ *  - The capacity C is computed on the device and written to capacity[0];
+ *    later calls read it there. Row e*C + j of a flat [E*C, *] buffer is slot j
+ *    of expert e. Buffers sized with the host bound cmax (moe_capacity_bound)
+ *    always hold E*C rows.
+ *  - Errors: arguments are checked before anything is enqueued; a failing
+ *    check returns MOE_EINVAL, MOE_EUNSUPPORTED or MOE_EWORKSPACE and enqueues
+ *    nothing. A failed launch returns MOE_EHIP. moe_last_error() gives the
+ *    message of the last failure on the calling thread. Device faults surface
+ *    at the caller's next synchronisation.
+ *  - Preconditions not checked: logits are finite; device buffers have the
+ *    sizes stated below; buffers that are written do not overlap inputs
+ *    unless a call says so.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_status {
+    MOE_OK = 0,
+    MOE_EINVAL = -1,       /* bad argument: null pointer, size out of range */
+    MOE_EUNSUPPORTED = -2, /* valid layer, but outside what the kernels support */
+    MOE_EWORKSPACE = -3,   /* workspace smaller than moe_workspace_size() */
+    MOE_EHIP = -4          /* a HIP runtime call or launch failed */
+} moe_status;
+
+enum { MOE_DT_F32 = 0, MOE_DT_BF16 = 1 };
+enum { MOE_ACT_RELU = 0, MOE_ACT_GELU = 1 };
+
+/* The layer's sizes and options (Tutel catalogue page, "key configuration":
+ * model_dim = M, number of experts = E, gate k and capacity_factor,
+ * hidden_size_per_expert = H, has_fc1_bias / has_fc2_bias).
+ * Supported: S >= 0; 1 <= k <= min(E, 32); E <= 512; M and H multiples of 64;
+ * dtype MOE_DT_F32 or MOE_DT_BF16; act MOE_ACT_RELU (max(0,v)) or
+ * MOE_ACT_GELU (0.5 v (1 + erf(v / sqrt 2))); capacity_factor finite. */
+typedef struct moe_shape {
+    int32_t S;   /* tokens */
+    int32_t M;   /* model dim */
+    int32_t E;   /* experts */
+    int32_t k;   /* experts per token */
+    int32_t H;   /* hidden size per expert */
+    double capacity_factor;
+    int32_t dtype;
+    int32_t act;
+    int32_t has_fc1_bias;
+    int32_t has_fc2_bias;
+} moe_shape;
+
+/* Checks a shape on the host (no GPU needed). */
+moe_status moe_validate(const moe_shape *shape);
+
+/* Host upper bound of C (no GPU needed): for capacity_factor f > 0 the capacity
+ * itself, ceil(k*S*f/E); for f == 0, S; for f < 0, min(ceil(k*S*|f|/E), S);
+ * never below 1. Size every [E*C, *] buffer with E * (*cmax_host) rows. */
+moe_status moe_capacity_bound(const moe_shape *shape, int32_t *cmax_host);
+
+/* Bytes of device workspace moe_route / moe_layer_forward need (no GPU needed). */
+moe_status moe_workspace_size(const moe_shape *shape, size_t *bytes_host);
+
+/* Gate projection: logits[s][e] = fp32(sum_m x[s][m] * Wg[m][e]), the sum
+ * accumulated in fp64 so that the fp32 logits do not depend on summation order
+ * in practice (routing decisions are taken on them).
+ * x [S, M] data type, Wg [M, E] fp32 row-major, logits [S, E] fp32. */
+moe_status moe_gate_project(const moe_shape *shape, const void *x, const float *Wg, float *logits,
+                            void *stream);
+
+/* Routing (Tutel catalogue page FAQ on k and capacity_factor; DeepSpeed PR
+ * #8195 section 1: per-route index, location and gate from the top-k, int32):
+ *   idx[r][s]   expert of route r of token s: experts ordered by logit, larger
+ *               first, equal logits (+0 == -0) by lower index first;
+ *   gates[r][s] softmax probability of that expert over all E logits (computed
+ *               in fp64, rounded to fp32), not renormalised;
+ *   loc[r][s]   number of earlier routes, in route-major then token order, to
+ *               the same expert; the route is kept iff loc < C;
+ *   needed[e]   routes to expert e;  capacity[0] = C;  fill[e] = min(needed, C);
+ *   slot_route  (may be NULL) [E * cmax]: row e*C + loc gets r*S + s for every
+ *               kept route; rows at or beyond fill[e] are not written.
+ * logits [S, E] fp32; idx, loc [k, S] int32; gates [k, S] fp32; needed, fill [E]
+ * int32; capacity [1] int32; ws: moe_workspace_size() bytes. */
+moe_status moe_route(const moe_shape *shape, const float *logits, int32_t *idx, int32_t *loc,
+                     float *gates, int32_t *needed, int32_t *fill, int32_t *capacity,
+                     int32_t *slot_route, void *ws, size_t ws_bytes, void *stream);
+
+/* Fast encode (blog part 3 section 3.5, "Encode"; DeepSpeed PR #8195 section 2,
+ * the flat [e*c, m] buffer): buf[idx*C + loc] = x[s] (a bit copy) for every kept
+ * route; every other row e*C + j with j < C is set to +0.
+ * x [S, M]; buf [E * cmax, M]; the first E*C rows are written. */
+moe_status moe_encode(const moe_shape *shape, const void *x, const int32_t *idx, const int32_t *loc,
+                      const int32_t *fill, const int32_t *capacity, void *buf, void *stream);
+
+/* Expert FFN (Tutel catalogue page, experts 'ffn'; blog part 3 section 3.5,
+ * expert batch matrix multiply on the per-expert [E, C, M] layout), for the
+ * filled rows j < fill[e] of each expert e:
+ *   pre = buf[e*C+j] . W1[e]^T + b1[e]   (fp32 accumulation)
+ *   h   = act(pre)                        stored in the data type
+ *   y   = h . W2[e]^T + b2[e]             (fp32 accumulation), stored
+ * W1 [E, H, M], b1 [E, H] (NULL iff !has_fc1_bias), W2 [E, M, H], b2 [E, M]
+ * (NULL iff !has_fc2_bias); buf, y [E*cmax, M]; h, pre [E*cmax, H]; pre may be
+ * NULL (it is needed by moe_layer_backward). Rows at or beyond fill[e] of
+ * pre, h and y are not written. */
+moe_status moe_expert_ffn(const moe_shape *shape, const void *buf, const void *W1, const void *b1,
+                          const void *W2, const void *b2, const int32_t *fill,
+                          const int32_t *capacity, void *pre, void *h, void *y, void *stream);
+
+/* The two halves of moe_expert_ffn, for callers that schedule or time them
+ * separately (same definitions, same row rules):
+ *   moe_expert_fc1: pre = buf . W1[e]^T + b1[e]; h = act(pre)   (pre may be NULL)
+ *   moe_expert_fc2: y = h . W2[e]^T + b2[e]                       */
+moe_status moe_expert_fc1(const moe_shape *shape, const void *buf, const void *W1, const void *b1,
+                          const int32_t *fill, const int32_t *capacity, void *pre, void *h, void *stream);
+moe_status moe_expert_fc2(const moe_shape *shape, const void *h, const void *W2, const void *b2,
+                          const int32_t *fill, const int32_t *capacity, void *y, void *stream);
+
+/* Fast decode (blog part 3 section 3.5, "Decode"; DeepSpeed PR #8195 section 3,
+ * combine accumulated in fp32): out[s] = sum over kept routes r = 0..k-1, in
+ * order, of gates[r][s] * y[idx*C + loc], accumulated in fp32 from +0 with
+ * separately rounded multiply and add, then stored in the data type. A token
+ * whose routes were all dropped gets 0. y [E*cmax, M]; out [S, M]. */
+moe_status moe_decode(const moe_shape *shape, const void *y, const float *gates, const int32_t *idx,
+                      const int32_t *loc, const int32_t *capacity, void *out, void *stream);
+
+/* The whole forward: [gate projection] -> route -> encode -> expert FFN ->
+ * decode, on one stream, without a host synchronisation. Exactly one of
+ * logits_in (given logits [S,E]) and Wg ([M,E], projected from x) is non-NULL;
+ * with Wg, logits_out [S,E] receives the logits (it may be NULL only when
+ * logits_in is given). Route outputs, buf, pre, h and y are kept for the
+ * backward; pre may be NULL for inference. Sizes as in the calls above. */
+moe_status moe_layer_forward(const moe_shape *shape, const void *x, const float *logits_in,
+                             const float *Wg, float *logits_out, const void *W1, const void *b1,
+                             const void *W2, const void *b2, int32_t *idx, int32_t *loc,
+                             float *gates, int32_t *needed, int32_t *fill, int32_t *capacity,
+                             int32_t *slot_route, void *buf, void *pre, void *h, void *y, void *out,
+                             void *ws, size_t ws_bytes, void *stream);
+
+/* The backward of decode, expert FFN and encode for upstream gradient dout
+ * [S, M] (blog part 3 section 3.5: K1 is combine-backward, K2 the cross term,
+ * K0 encode-backward), given the forward's saved tensors (buf, pre, h, y and
+ * the route tables):
+ *   dy[slot]     = gates[r][s] * dout[s]            (rows of kept routes only)
+ *   dgates[r][s] = <dout[s], y[slot]> in fp32, 0 for dropped routes
+ *   dpre = (dy . W2[e]) * act'(pre), stored;   dbuf = dpre . W1[e], stored
+ *   dW2[e] = sum_j dy_j^T h_j, db2[e] = sum_j dy_j,
+ *   dW1[e] = sum_j dpre_j^T buf_j, db1[e] = sum_j dpre_j   (fp32, over j < fill[e])
+ *   dx[s] = sum over kept routes of dbuf[slot] (fp32 accumulation), stored;
+ *           0 for a token whose routes were all dropped.
+ * dy, dbuf [E*cmax, M] and dpre [E*cmax, H] are caller scratch; dy and dbuf
+ * may be the same buffer. dW1 [E,H,M], dW2 [E,M,H] fp32; db1 [E,H], db2 [E,M]
+ * fp32 or NULL (not computed); dgates [k,S] fp32; dx [S,M]. Gradients are
+ * overwritten, not accumulated. pre must come from the forward. */
+moe_status moe_layer_backward(const moe_shape *shape, const void *dout, const void *buf,
+                              const void *pre, const void *h, const void *y, const float *gates,
+                              const int32_t *idx, const int32_t *loc, const int32_t *fill,
+                              const int32_t *capacity, const void *W1, const void *W2, void *dy,
+                              void *dpre, void *dbuf, void *dx, float *dW1, float *db1, float *dW2,
+                              float *db2, float *dgates, void *stream);
+
+/* Message of the last failing call on this thread ("" if none). */
+const char *moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H_ */

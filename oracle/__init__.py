@@ -49,6 +49,7 @@ def lib():
             build()
         L = ctypes.CDLL(LIB)
         vp, i32, i64, d = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_double
+        L.oracle_num_threads.argtypes = []; L.oracle_num_threads.restype = ctypes.c_int
         L.oracle_f64_to_bf16.argtypes = [d]; L.oracle_f64_to_bf16.restype = ctypes.c_uint16
         L.oracle_act.argtypes = [ctypes.c_int, d]; L.oracle_act.restype = d
         L.oracle_act_grad.argtypes = [ctypes.c_int, d]; L.oracle_act_grad.restype = d
@@ -74,6 +75,9 @@ def lib():
         L.oracle_backward_rows.argtypes = [i32, i32, i32, i32, i32, ctypes.c_int, ctypes.c_int, vp,
                                            vp, vp, vp, _c_f32p, vp, i64, _c_i64p, _c_i32p, vp, vp, vp]
         L.oracle_backward_rows.restype = None
+        L.oracle_backward_cols.argtypes = [i32, i32, i32, i32, ctypes.c_int, ctypes.c_int, vp, vp, vp, vp,
+                                           _c_f32p, vp, i64, _c_i64p, _c_i32p, i32, _c_i32p, vp, vp, vp]
+        L.oracle_backward_cols.restype = None
         L.oracle_weight_grads.argtypes = [i32, i32, ctypes.c_int, i64, vp, vp, vp, vp, _c_f32p,
                                           _c_f32p, _c_f32p, _c_f32p]
         L.oracle_weight_grads.restype = None
@@ -113,6 +117,10 @@ def bf16_to_f32(a: np.ndarray) -> np.ndarray:
 
 def to_f64(a: np.ndarray, dtype: int) -> np.ndarray:
     return a.astype(np.float64) if dtype == DT_F32 else bf16_to_f32(a).astype(np.float64)
+
+
+def num_threads() -> int:
+    return int(lib().oracle_num_threads())
 
 
 def f64_to_bf16(v: float) -> int:
@@ -285,6 +293,28 @@ def backward_rows(fw: Dict, inp: Dict, rows: np.ndarray, act_kind: int, dtype: i
                                _ptr(W2), rt["gates"].reshape(-1).copy(), _ptr(_check(inp["dout"], dtype)),
                                n, rows, routes, _ptr(dy), _ptr(dpre), _ptr(dbuf))
     return routes, dy, dpre, dbuf
+
+
+def backward_cols(rt: Dict, buf: np.ndarray, inp: Dict, rows, hcols, act_kind: int, dtype: int):
+    """dy rows, h columns and dpre columns of the listed kept rows (selected hidden columns)."""
+    C = rt["C"]
+    k, S = rt["idx"].shape
+    W1, W2 = _check(inp["W1"], dtype), _check(inp["W2"], dtype)
+    E, H, M = W1.shape
+    rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    routes = np.ascontiguousarray(rt["slot_route"][rows].astype(np.int32))
+    assert (routes >= 0).all()
+    hcols = np.ascontiguousarray(np.asarray(hcols, dtype=np.int32))
+    n, nc = rows.shape[0], hcols.shape[0]
+    et = elem_dtype(dtype)
+    dy = np.empty((n, M), et)
+    hv = np.empty((n, nc), et)
+    dpre = np.empty((n, nc), et)
+    lib().oracle_backward_cols(S, M, H, C, dtype, act_kind, _ptr(_check(buf, dtype)), _ptr(W1),
+                               _ptr(inp.get("b1")), _ptr(W2), rt["gates"].reshape(-1).copy(),
+                               _ptr(_check(inp["dout"], dtype)), n, rows, routes, nc, hcols, _ptr(dy), _ptr(hv),
+                               _ptr(dpre))
+    return routes, dy, hv, dpre
 
 
 def weight_grads(dy, hv, dpre, bufrows, dtype: int):

@@ -56,6 +56,9 @@
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 #define DT_F32 0
 #define DT_BF16 1
@@ -118,6 +121,15 @@ static double act_grad(int act, double v) {
     if (act == ACT_RELU) return v > 0.0 ? 1.0 : 0.0;
     const double pdf = exp(-0.5 * v * v) / sqrt(2.0 * M_PI);
     return 0.5 * (1.0 + erf(v / sqrt(2.0))) + v * pdf;
+}
+
+/* Threads the OpenMP loops below use (1 without OpenMP). */
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
 }
 
 /* Exposed for the tests: the scalar roundings above. */
@@ -372,6 +384,43 @@ void oracle_backward_rows(int32_t S, int32_t M, int32_t H, int32_t E, int32_t C,
                 }
         }
         free(pre); free(dy); free(dpre);
+    }
+}
+
+/* The same backward quantities for selected hidden columns only, for sampling
+ * the weight gradients of large layers. For each listed kept row (rows[i] =
+ * e*C + j holding route routes[i]) and each hidden column hcols[c]:
+ *   hv[i][c]   = act(pre) rounded,  dpre[i][c] = (dy . W2[e][:, h]) * act'(pre) rounded,
+ * and the full dy row dy[i][:] = gates * dout[s] rounded. Every element follows
+ * the same definitions as ffn_row / oracle_backward_rows. */
+void oracle_backward_cols(int32_t S, int32_t M, int32_t H, int32_t C, int dtype, int act, const void *buf,
+                          const void *W1, const void *b1, const void *W2, const float *gates,
+                          const void *dout, int64_t nrows, const int64_t *rows, const int32_t *routes,
+                          int32_t ncols, const int32_t *hcols, void *dy_out, void *hv_out, void *dpre_out) {
+#pragma omp parallel
+    {
+        double *dy = (double *)malloc(sizeof(double) * (size_t)M);
+#pragma omp for schedule(dynamic, 4)
+        for (int64_t i = 0; i < nrows; ++i) {
+            const int64_t row = rows[i], e = row / C;
+            const int64_t q = routes[i], s = q % S;
+            for (int32_t m = 0; m < M; ++m) {
+                dy[m] = round_to_dtype((double)gates[q] * load_elem(dout, dtype, s * M + m), dtype);
+                store_elem(dy_out, dtype, i * M + m, dy[m]);
+            }
+            for (int32_t c = 0; c < ncols; ++c) {
+                const int64_t h = hcols[c];
+                double pre = 0.0;
+                for (int32_t m = 0; m < M; ++m)
+                    pre += load_elem(buf, dtype, row * M + m) * load_elem(W1, dtype, (e * H + h) * M + m);
+                if (b1) pre += load_elem(b1, dtype, e * H + h);
+                store_elem(hv_out, dtype, i * ncols + c, act_f(act, pre));
+                double dh = 0.0;
+                for (int32_t m = 0; m < M; ++m) dh += dy[m] * load_elem(W2, dtype, (e * M + m) * H + h);
+                store_elem(dpre_out, dtype, i * ncols + c, dh * act_grad(act, pre));
+            }
+        }
+        free(dy);
     }
 }
 

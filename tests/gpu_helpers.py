@@ -1,0 +1,117 @@
+"""Helpers of the GPU parity tests: moving arrays between numpy (oracle side) and
+torch device tensors (HIP side), running the library's entry points, and the
+tolerance rules.
+
+Tolerances: routing indices, locations, needed, fill, C, slot map and the
+encode buffer are compared bit for bit; gates within one fp32 ulp (both sides
+compute the softmax in fp64 and round once; only the fp64 summation order
+differs); decode given the same expert output bit for bit. The FFN output and
+the layer output are compared in fp32 with max |got - want| <= 1e-4 for fp32
+data, or max |got - want| / RMS(want) <= 2e-2 for bf16 data; bf16
+intermediates and gradients use the same rule plus one bf16 ulp of every
+rounded value they are made of (see check_close).
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict
+
+import numpy as np
+import torch
+
+import workloads as W
+from tests.helpers import f32_of, np_of
+
+TOL_F32_ABS = 1e-4
+TOL_BF16_REL_RMS = 2e-2
+
+
+def dev(a: np.ndarray, device="cuda") -> torch.Tensor:
+    """numpy -> device tensor (uint16 arrays become bf16 bit patterns)."""
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(device)
+    return torch.from_numpy(a).to(device)
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    return np_of(t)
+
+
+def inputs_np(inp: Dict[str, torch.Tensor]) -> Dict[str, np.ndarray]:
+    return {k: np_of(v) for k, v in inp.items()}
+
+
+def check_close(got: np.ndarray, want: np.ndarray, dtype: int, what: str, mag: np.ndarray = None) -> float:
+    """The tolerance rule; returns the error measure.
+
+    fp32 data: max |got - want| <= 1e-4. bf16 data: max |got - want| <= 2e-2 RMS(want)
+    (the rule for the FFN output y and the layer output). For bf16 tensors that are
+    rounded to bf16 again downstream, or are sums of such rounded terms (h, pre, dpre,
+    dx), pass mag: each element may also differ by one bf16 ulp of every rounded
+    value it is made of, |got - want| <= 2e-2 RMS(want) + 2^-7 mag, with mag = |want|
+    (+ the magnitudes of the rounded terms summed into it).
+    """
+    g = f32_of(got).astype(np.float64)
+    w = f32_of(want).astype(np.float64)
+    assert g.shape == w.shape, (what, g.shape, w.shape)
+    if g.size == 0:
+        return 0.0
+    assert np.isfinite(g).all(), f"{what}: non-finite values"
+    d = np.abs(g - w)
+    diff = d.max()
+    if dtype == W.DT_F32:
+        assert diff <= TOL_F32_ABS, f"{what}: max abs err {diff:.3e} > {TOL_F32_ABS}"
+        return float(diff)
+    rms = math.sqrt((w ** 2).mean())
+    if mag is None:
+        rel = diff / rms if rms > 0 else diff
+        i = np.unravel_index(np.argmax(d), d.shape)
+        assert rel <= TOL_BF16_REL_RMS, (f"{what}: max err / rms = {rel:.3e} > {TOL_BF16_REL_RMS} (rms {rms:.3e}; "
+                                         f"at {i}: got {g[i]:.6e} want {w[i]:.6e})")
+        return float(rel)
+    bound = TOL_BF16_REL_RMS * rms + 2.0 ** -7 * np.asarray(mag, np.float64)
+    ratio = d / np.maximum(bound, 1e-300)
+    i = np.unravel_index(np.argmax(ratio), d.shape)
+    assert ratio[i] <= 1.0, (f"{what}: |err| {d[i]:.3e} exceeds 2e-2*rms + 2^-7*mag = {bound[i]:.3e} at {i} "
+                             f"(got {g[i]:.6e} want {w[i]:.6e}, rms {rms:.3e})")
+    return float(ratio[i])
+
+
+def check_gates(got: np.ndarray, want: np.ndarray, what="gates"):
+    ulp = np.spacing(np.abs(want).astype(np.float32))
+    bad = np.abs(got.astype(np.float64) - want.astype(np.float64)) > ulp
+    assert not bad.any(), f"{what}: {bad.sum()} values differ by more than one ulp"
+
+
+def shape_of(w: W.Workload):
+    import combine_softmax_top_amd as moe
+    return moe.Shape.of(w)
+
+
+def gpu_route(w: W.Workload, logits: np.ndarray) -> Dict[str, np.ndarray]:
+    """moe_route on the given fp32 logits; returns host arrays (slot map cut to E*C)."""
+    import combine_softmax_top_amd as moe
+    s = shape_of(w)
+    b = moe.alloc_forward(s)
+    lg = dev(np.ascontiguousarray(logits, dtype=np.float32))
+    moe.moe_route(s, lg, b["idx"], b["loc"], b["gates"], b["needed"], b["fill"], b["capacity"], b["slot_route"],
+                  b["ws"])
+    torch.cuda.synchronize()
+    C = int(b["capacity"].item())
+    return dict(idx=host(b["idx"]), loc=host(b["loc"]), gates=host(b["gates"]), needed=host(b["needed"]),
+                fill=host(b["fill"]), C=C, slot_route=host(b["slot_route"][: w.E * C]))
+
+
+def compare_route(g: Dict, o: Dict, E: int):
+    assert g["C"] == o["C"], (g["C"], o["C"])
+    for k in ("idx", "loc", "needed", "fill"):
+        assert np.array_equal(g[k], o[k]), k
+    check_gates(g["gates"], o["gates"])
+    # slot map: rows below fill are defined; compare those
+    C = o["C"]
+    so = o["slot_route"].reshape(E, C)
+    sg = g["slot_route"].reshape(E, C)
+    for e in range(E):
+        f = int(o["fill"][e])
+        assert np.array_equal(sg[e, :f], so[e, :f]), f"slot_route expert {e}"

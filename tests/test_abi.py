@@ -1,0 +1,96 @@
+"""The C ABI without a GPU: the library loads, exports every entry point the
+header declares, and its host-side checks behave as documented (nothing here
+launches a kernel)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def moe():
+    import combine_softmax_top_amd as m
+    return m
+
+
+def _declared():
+    with open(os.path.join(ROOT, "include", "moe.h")) as fh:
+        text = fh.read()
+    return sorted(set(re.findall(r"^\s*(?:moe_status|const char \*)\s*(moe_\w+)\s*\(", text, re.M)))
+
+
+def test_every_declared_symbol_is_exported(moe):
+    names = _declared()
+    assert len(names) == 13, names
+    lib = ctypes.CDLL(moe.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert names == moe.EXPORTED
+
+
+def test_shape_struct_layout_matches_header(moe):
+    # int32 S, M, E, k, H; (4 bytes padding); double; int32 x4
+    assert ctypes.sizeof(moe.moe_shape) == 48
+    assert moe.moe_shape.capacity_factor.offset == 24
+
+
+@pytest.mark.parametrize("w", W.WORKLOADS, ids=lambda w: w.name)
+def test_capacity_bound_and_workspace(moe, w):
+    s = moe.Shape.of(w)
+    assert moe.moe_validate(s) == moe.MOE_OK
+    assert moe.moe_capacity_bound(s) == W.capacity_bound(w)
+    tiles = (w.S + 63) // 64
+    assert moe.moe_workspace_size(s) >= 4 * w.E * w.k * tiles
+
+
+def test_validation_errors(moe):
+    ok = moe.Shape(S=64, M=64, E=4, k=2, H=64, capacity_factor=1.0)
+    assert moe.moe_validate(ok) == moe.MOE_OK
+    bad = [
+        (dict(k=5), moe.MOE_EINVAL),            # k > E
+        (dict(k=0), moe.MOE_EINVAL),
+        (dict(S=-1), moe.MOE_EINVAL),
+        (dict(M=0), moe.MOE_EINVAL),
+        (dict(dtype=7), moe.MOE_EINVAL),
+        (dict(act=9), moe.MOE_EINVAL),
+        (dict(capacity_factor=float("nan")), moe.MOE_EINVAL),
+        (dict(M=96), moe.MOE_EUNSUPPORTED),      # not a multiple of 64
+        (dict(H=100), moe.MOE_EUNSUPPORTED),
+        (dict(E=600, k=2), moe.MOE_EUNSUPPORTED),
+        (dict(E=64, k=33), moe.MOE_EUNSUPPORTED),
+    ]
+    import dataclasses
+    for change, want in bad:
+        s = dataclasses.replace(ok, **change)
+        assert moe.moe_validate(s) == want, change
+        assert moe.moe_last_error() != ""
+    lib = ctypes.CDLL(moe.LIB_PATH)
+    lib.moe_validate.argtypes = [ctypes.c_void_p]
+    assert lib.moe_validate(None) == moe.MOE_EINVAL
+
+
+def test_entry_points_reject_before_enqueueing(moe):
+    # Every failing check returns before any HIP call, so these run without a GPU.
+    s = moe.Shape(S=64, M=64, E=4, k=2, H=64, capacity_factor=1.0)
+    c = s.c()
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: checks fail first
+    lib = moe._lib
+    st = lib.moe_route(ctypes.byref(c), None, fake, fake, fake, fake, fake, fake, None, fake, 16, None)
+    assert st == moe.MOE_EINVAL  # logits NULL
+    st = lib.moe_route(ctypes.byref(c), fake, fake, fake, fake, fake, fake, fake, None, fake, 1, None)
+    assert st == moe.MOE_EWORKSPACE and "workspace" in moe.moe_last_error()
+    st = lib.moe_expert_ffn(ctypes.byref(c), fake, fake, None, fake, fake, fake, fake, None, fake, fake, None)
+    assert st == moe.MOE_EINVAL and "b1" in moe.moe_last_error()  # biases on, b1 missing
+    st = lib.moe_layer_forward(ctypes.byref(c), fake, fake, fake, fake, *([fake] * 17), 1 << 20, None)
+    assert st == moe.MOE_EINVAL  # both logits and Wg given
+    st = lib.moe_layer_backward(ctypes.byref(c), *([None] * 22))
+    assert st == moe.MOE_EINVAL
+    with pytest.raises(moe.MoeError):
+        moe._check(lib.moe_decode(ctypes.byref(c), None, None, None, None, None, None, None))

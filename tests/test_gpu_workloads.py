@@ -1,0 +1,143 @@
+"""GPU parity at the five workloads' full sizes, in the launch configuration the
+benchmark times (the fused C-ABI calls).
+
+Routing (and the gate projection) and the encode buffer are compared in full,
+bit for bit. GEMM-dependent outputs are compared on seeded samples that the
+oracle computes one by one from the original inputs: every expert's first and
+last filled rows plus random rows of h and y, a random set of tokens of the
+layer output, and, for the workload with a backward, random gate gradients,
+random tokens of dx, and the weight/bias gradients of three experts (hottest,
+median, coldest) on random hidden columns.
+"""
+from __future__ import annotations
+
+import time
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from tests.gpu_helpers import check_close, compare_route, host
+from tests.helpers import f32_of
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+@pytest.mark.parametrize("w", W.WORKLOADS, ids=lambda w: w.name)
+def test_full_size_workload(w):
+    import combine_softmax_top_amd as moe
+    t0 = time.time()
+    rng = np.random.default_rng(1234)
+    inp = W.make_inputs(w, seed=0, device="cuda")
+    s = moe.Shape.of(w)
+    gate = w.logits == "gate"
+    b = moe.layer_forward(s, inp["x"], inp["W1"], inp.get("b1"), inp["W2"], inp.get("b2"),
+                          logits=None if gate else inp["logits"], Wg=inp.get("Wg"), training=w.backward)
+    gr = moe.layer_backward(s, b, inp["dout"], inp["W1"], inp["W2"]) if w.backward else None
+    torch.cuda.synchronize()
+    _say(f"[{w.name}] GPU forward{'+backward' if w.backward else ''} done in {time.time() - t0:.1f}s")
+    ni = {k: host(v) for k, v in inp.items()}
+    C = int(b["capacity"].item())
+
+    # ---- gate projection and routing, in full
+    if gate:
+        logits = oracle.gate_logits(ni["x"], ni["Wg"], w.dtype)
+        assert np.array_equal(host(b["logits"]), logits), "gate projection"
+    else:
+        logits = ni["logits"]
+    rt = oracle.route(logits, w.k, w.capacity_factor)
+    g = dict(idx=host(b["idx"]), loc=host(b["loc"]), gates=host(b["gates"]), needed=host(b["needed"]),
+             fill=host(b["fill"]), C=C, slot_route=host(b["slot_route"][: w.E * C]))
+    compare_route(g, rt, w.E)
+    kept = int(rt["fill"].sum())
+    _say(f"[{w.name}] route bit-exact: C={C}, kept {kept} of {w.k * w.S} routes")
+
+    # ---- encode, in full
+    obuf = oracle.encode(ni["x"], rt, w.E, w.dtype)
+    gbuf = host(b["buf"][: w.E * C])
+    assert np.array_equal(gbuf.view(np.uint8), obuf.view(np.uint8)), "encode buffer"
+    del gbuf
+    _say(f"[{w.name}] encode buffer bit-exact ({obuf.nbytes / 2**20:.0f} MiB)")
+
+    # ---- expert FFN on sampled rows
+    fill = rt["fill"]
+    rows = []
+    for e in range(w.E):
+        if fill[e] > 0:
+            rows += [e * C, e * C + int(fill[e]) - 1]
+    filled = oracle.filled_rows(rt)
+    rows += rng.choice(filled, size=min(len(filled), 64), replace=False).tolist()
+    rows = np.unique(np.asarray(rows, np.int64))
+    # tokens of the layer output, and the rows their kept routes read
+    ntok = min(w.S, 96)
+    toks = np.sort(rng.choice(w.S, size=ntok, replace=False))
+    tok_rows = []
+    for r in range(w.k):
+        for t in toks:
+            if rt["loc"][r, t] < C:
+                tok_rows.append(rt["idx"][r, t] * C + rt["loc"][r, t])
+    all_rows = np.unique(np.concatenate([rows, np.asarray(tok_rows, np.int64)]))
+    t1 = time.time()
+    _, h_o, y_o = oracle.expert_rows(obuf, ni["W1"], ni.get("b1"), ni["W2"], ni.get("b2"), all_rows, C, w.act,
+                                     w.dtype, want_h=True)
+    _say(f"[{w.name}] oracle FFN on {len(all_rows)} rows in {time.time() - t1:.1f}s")
+    gy = host(b["y"][torch.from_numpy(all_rows).cuda()])
+    gh = host(b["h"][torch.from_numpy(all_rows).cuda()])
+    check_close(gh, h_o, w.dtype, "h rows", mag=np.abs(f32_of(h_o)))
+    check_close(gy, y_o, w.dtype, "y rows")
+    y_full = np.zeros((w.E * C, w.M), y_o.dtype)
+    y_full[all_rows] = y_o
+    out_o = oracle.decode(y_full, rt, w.E, w.dtype, tokens=toks)
+    check_close(host(b["out"][torch.from_numpy(toks).cuda()]), out_o, w.dtype, "out tokens")
+    _say(f"[{w.name}] FFN rows and {ntok} output tokens within tolerance")
+
+    if not w.backward:
+        return
+
+    # ---- backward: dgates on sampled kept routes, dx on sampled tokens, weight grads of 3 experts
+    dout = ni["dout"]
+    slot = rt["slot_route"]
+    kept_rows = all_rows[slot[all_rows] >= 0]
+    routes = slot[kept_rows]
+    dg_o = oracle.dgates(routes, dout, y_full[kept_rows], w.S, w.dtype)
+    dg_g = host(gr["dgates"]).reshape(-1)[routes]
+    check_close(dg_g, dg_o, w.dtype, "dgates (sampled)")
+    dx_toks = toks[:8]
+    dx_rows = np.asarray([rt["idx"][r, t] * C + rt["loc"][r, t] for r in range(w.k) for t in dx_toks
+                          if rt["loc"][r, t] < C], np.int64)
+    fw = dict(route=rt, buf=obuf)
+    q, _, _, dbuf_o = oracle.backward_rows(fw, ni, dx_rows, w.act, w.dtype, want_dy=False, want_dpre=False)
+    dx_o = oracle.dx_tokens(q, dbuf_o, dx_toks, w.S, w.k, w.dtype)
+    terms = np.zeros(dx_o.shape)
+    for i, qq in enumerate(q):
+        terms[list(dx_toks).index(int(qq) % w.S)] += np.abs(f32_of(dbuf_o[i]))
+    check_close(host(gr["dx"][torch.from_numpy(dx_toks).cuda()]), dx_o, w.dtype, "dx (sampled)",
+                mag=np.abs(f32_of(dx_o)) + terms)
+    _say(f"[{w.name}] dgates on {len(routes)} routes and dx on {len(dx_toks)} tokens within tolerance")
+    order = np.argsort(fill)
+    experts = sorted({int(order[-1]), int(order[len(order) // 2]), int(order[0])})
+    hcols = np.sort(rng.choice(w.H, size=4, replace=False)).astype(np.int32)
+    gW1, gW2 = gr["dW1"], gr["dW2"]
+    for e in experts:
+        erows = e * C + np.arange(int(fill[e]), dtype=np.int64)
+        if len(erows) == 0:
+            assert (host(gW1[e]) == 0).all() and (host(gW2[e]) == 0).all()
+            continue
+        t1 = time.time()
+        _, dy_o, hv_o, dpre_o = oracle.backward_cols(rt, obuf, ni, erows, hcols, w.act, w.dtype)
+        dW1_o, db1_o, dW2_o, db2_o = oracle.weight_grads(dy_o, hv_o, dpre_o, obuf[erows], w.dtype)
+        hc = torch.from_numpy(hcols.astype(np.int64)).cuda()
+        check_close(host(gW1[e][hc]), dW1_o, w.dtype, f"dW1[{e}] (columns {hcols.tolist()})")
+        check_close(host(gW2[e][:, hc]), dW2_o, w.dtype, f"dW2[{e}] (columns {hcols.tolist()})")
+        if w.has_fc1_bias:
+            check_close(host(gr["db1"][e][hc]), db1_o, w.dtype, f"db1[{e}]")
+        if w.has_fc2_bias:
+            check_close(host(gr["db2"][e]), db2_o, w.dtype, f"db2[{e}]")
+        _say(f"[{w.name}] expert {e} ({len(erows)} rows) weight gradients within tolerance "
+             f"({time.time() - t1:.1f}s)")

@@ -385,3 +385,17 @@ def test_encode_decode_adjoint_identities():
         r, s = divmod(int(q), S)
         K1D[rt["idx"][r, s] * C + rt["loc"][r, s]] = rt["gates"][r, s] * D[s].astype(np.float64)
     assert lhs2 == pytest.approx((y.astype(np.float64) * K1D).sum(), rel=1e-6)
+
+
+def test_backward_columns_equal_backward_rows():
+    # the column-subset helper used to sample large layers computes the same elements
+    w = W.Workload("cols", S=96, M=64, E=3, k=2, H=64, capacity_factor=0.0, backward=True)
+    inp = {k_: np_of(v) for k_, v in W.make_inputs(w, seed=9).items()}
+    fw = oracle.layer_forward(inp, w.k, w.capacity_factor, w.act, w.dtype)
+    rows = fw["rows"]
+    _, dy, dpre, _ = oracle.backward_rows(fw, inp, rows, w.act, w.dtype)
+    cols = np.arange(w.H, dtype=np.int32)[::3]
+    _, dy2, hv2, dpre2 = oracle.backward_cols(fw["route"], fw["buf"], inp, rows, cols, w.act, w.dtype)
+    assert np.array_equal(dy, dy2)
+    assert np.array_equal(dpre[:, cols], dpre2)
+    assert np.array_equal(fw["h"][rows][:, cols], hv2)
