@@ -89,7 +89,7 @@ def test_full_size_workload(w):
     _say(f"[{w.name}] oracle FFN on {len(all_rows)} rows in {time.time() - t1:.1f}s")
     gy = host(b["y"][torch.from_numpy(all_rows).cuda()])
     gh = host(b["h"][torch.from_numpy(all_rows).cuda()])
-    check_close(gh, h_o, w.dtype, "h rows", mag=np.abs(f32_of(h_o)))
+    check_close(gh, h_o, w.dtype, "h rows")
     check_close(gy, y_o, w.dtype, "y rows")
     y_full = np.zeros((w.E * C, w.M), y_o.dtype)
     y_full[all_rows] = y_o
