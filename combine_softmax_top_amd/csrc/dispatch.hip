@@ -9,6 +9,8 @@
 //  - the gate projection x . Wg with fp64 accumulation.
 // Rows are moved as uint4 (8 bf16 or 4 fp32). Grids are sized to fill the
 // chip and loop over tokens/rows (grid-stride), reading C from the device.
+#include <algorithm>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -219,44 +221,109 @@ __global__ __launch_bounds__(kThreads) void decode_bwd_kernel(const uint4 *__res
 
 // ---------------------------------------------------------------- gate projection
 
-// logits[s][e] = fp32(sum_m x[s][m] * Wg[m][e]) with an fp64 accumulator: the
-// products of a bf16 or fp32 input and an fp32 weight are exact in fp64, so
-// the result rounds to the same fp32 value whatever the summation order,
-// except when the fp64 sum lies within a few fp64 ulps of an fp32 rounding
-// boundary.
+// logits[s][e] = fp32(sum_m x[s][m] * Wg[m][e]): one thread per output, an fp64
+// accumulator updated in increasing m. Each product of a bf16/fp32 input and an
+// fp32 weight is exact in fp64, so fma(x, w, acc) rounds exactly like acc + x*w
+// and the fp32 logit is the fp64 sequential sum rounded once. A block covers TT
+// tokens and all E experts (IPT experts per thread when E > 256). Per chunk of
+// MC rows of Wg, the block first copies the chunk of Wg and its TT rows of x
+// into LDS with all loads in flight at once (the chains are short, so load
+// latency, not arithmetic, bounds this kernel), then runs the chains from LDS.
+constexpr int GP_W_FLOATS = 8192;  // Wg rows of one chunk: 32 KiB
+constexpr int GP_X_BYTES = 32768;  // the block's x rows of one chunk: 32 KiB
+constexpr int GP_MAX_TT = 16;
+constexpr int GP_UNROLL = 8;       // 16-byte loads in flight per thread
+
 template <bool BF16>
 __global__ __launch_bounds__(kThreads) void gate_project_kernel(const void *__restrict__ xv,
                                                                 const float *__restrict__ Wg,
-                                                                float *__restrict__ logits, int S, int M, int E) {
-    const int lane = threadIdx.x & (kWave - 1);
-    const int64_t nw = num_waves();
-    constexpr int EB = 8;
-    for (int64_t s = global_wave(); s < S; s += nw) {
-        for (int e0 = 0; e0 < E; e0 += EB) {
-            double acc[EB];
+                                                                float *__restrict__ logits, int S, int M, int E,
+                                                                int TT, int MC) {
+    __shared__ float4 ws[GP_W_FLOATS / 4];
+    // row t of the x chunk starts at xs[t * xstride]; the one-vector pad puts
+    // consecutive tokens' vectors on different banks
+    __shared__ uint4 xs[GP_X_BYTES / 16 + GP_MAX_TT];
+    constexpr int EPV = BF16 ? 8 : 4;  // x elements per 16-byte vector
+    const int tid = threadIdx.x, nt = blockDim.x;
+    const int64_t s0 = static_cast<int64_t>(blockIdx.x) * TT;
+    const int ntok = static_cast<int>(min<int64_t>(TT, S - s0));
+    const int items = TT * E;
+    const int xstride = MC / EPV + 1;
+    const uint4 *xg = reinterpret_cast<const uint4 *>(xv);  // row s, vector v at xg[s * (M / EPV) + v]
+    const float4 *wg = reinterpret_cast<const float4 *>(Wg);
+    const float *wsf = reinterpret_cast<const float *>(ws);
+    constexpr int IPT = kMaxE / 256;
+    double acc[IPT];
+    int tok[IPT], ex[IPT];
 #pragma unroll
-            for (int i = 0; i < EB; ++i) acc[i] = 0.0;
-            for (int m = lane; m < M; m += kWave) {
-                const double xm = BF16 ? static_cast<double>(bf16_to_f32(static_cast<const bf16_t *>(xv)[s * M + m]))
-                                       : static_cast<double>(static_cast<const float *>(xv)[s * M + m]);
-                const float *w = Wg + static_cast<int64_t>(m) * E + e0;
+    for (int j = 0; j < IPT; ++j) {
+        acc[j] = 0.0;
+        const int it = tid + j * nt;
+        tok[j] = it < items ? it / E : -1;
+        ex[j] = it < items ? it - (it / E) * E : 0;
+        if (tok[j] >= ntok) tok[j] = -1;
+    }
+    for (int m0 = 0; m0 < M; m0 += MC) {
+        const int mc = min(MC, M - m0);
+        const int nv = mc / EPV;
+        __syncthreads();
+        // Wg rows m0 .. m0+mc-1 are mc*E contiguous floats (a multiple of 8)
+        const int nw = mc * E / 4;
+        const float4 *wsrc = wg + static_cast<int64_t>(m0) * E / 4;
+        // loads are unconditional (index clamped to the last element) so that the
+        // staging registers stay registers; only the LDS stores are guarded
+        for (int i0 = tid; i0 < nw; i0 += GP_UNROLL * nt) {
+            float4 r[GP_UNROLL];
 #pragma unroll
-                for (int i = 0; i < EB; ++i)
-                    if (e0 + i < E) acc[i] = fma(xm, static_cast<double>(w[i]), acc[i]);
+            for (int u = 0; u < GP_UNROLL; ++u) r[u] = wsrc[min(i0 + u * nt, nw - 1)];
+#pragma unroll
+            for (int u = 0; u < GP_UNROLL; ++u)
+                if (i0 + u * nt < nw) ws[i0 + u * nt] = r[u];
+        }
+        const int nx = ntok * nv;
+        for (int i0 = tid; i0 < nx; i0 += GP_UNROLL * nt) {
+            uint4 r[GP_UNROLL];
+            int dst[GP_UNROLL];
+#pragma unroll
+            for (int u = 0; u < GP_UNROLL; ++u) {
+                const int i = min(i0 + u * nt, nx - 1);
+                const int t = i / nv, v = i - t * nv;
+                r[u] = xg[(s0 + t) * (M / EPV) + m0 / EPV + v];
+                dst[u] = t * xstride + v;
             }
 #pragma unroll
-            for (int i = 0; i < EB; ++i) {
+            for (int u = 0; u < GP_UNROLL; ++u)
+                if (i0 + u * nt < nx) xs[dst[u]] = r[u];
+        }
+        __syncthreads();
 #pragma unroll
-                for (int off = 32; off > 0; off >>= 1) acc[i] += __shfl_xor(acc[i], off, kWave);
-            }
-            if (lane < EB && e0 + lane < E) {
-                double a = acc[0];
+        for (int j = 0; j < IPT; ++j) {
+            if (tok[j] < 0) continue;
+            const uint4 *xr = xs + tok[j] * xstride;
+            const float *wcol = wsf + ex[j];
+#pragma unroll 2
+            for (int v = 0; v < nv; ++v) {
+                const uint4 u = xr[v];
+                const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+                float xf[EPV];
 #pragma unroll
-                for (int i = 1; i < EB; ++i) a = lane == i ? acc[i] : a;
-                logits[s * E + e0 + lane] = static_cast<float>(a);
+                for (int q = 0; q < 4; ++q) {
+                    if (BF16) {
+                        xf[2 * q] = __uint_as_float(w4[q] << 16);
+                        xf[2 * q + 1] = __uint_as_float(w4[q] & 0xFFFF0000u);
+                    } else {
+                        xf[q] = __uint_as_float(w4[q]);
+                    }
+                }
+#pragma unroll
+                for (int q = 0; q < EPV; ++q)
+                    acc[j] = fma(static_cast<double>(xf[q]), static_cast<double>(wcol[(v * EPV + q) * E]), acc[j]);
             }
         }
     }
+#pragma unroll
+    for (int j = 0; j < IPT; ++j)
+        if (tok[j] >= 0) logits[(s0 + tok[j]) * E + ex[j]] = static_cast<float>(acc[j]);
 }
 
 int grid_for(int64_t waves) {
@@ -269,12 +336,21 @@ int grid_for(int64_t waves) {
 
 hipError_t launch_gate_project(const moe_shape &s, const void *x, const float *Wg, float *logits, hipStream_t st) {
     if (s.S == 0) return hipSuccess;
-    const int grid = grid_for(s.S);
+    // tokens per block: up to 256 outputs per block, at most 16 tokens so that
+    // small-E layers still spread over many workgroups
+    const int TT = s.E >= 256 ? 1 : std::min(GP_MAX_TT, 256 / s.E);
+    const int threads = s.E > 256 ? 256 : std::max(64, ((TT * s.E + 63) / 64) * 64);
+    const int esz = s.dtype == MOE_DT_BF16 ? 2 : 4;
+    // chunk rows: Wg chunk and x chunk each fit their LDS area; a multiple of 8
+    // (>= 16 for E <= 512), so every chunk is whole 16-byte vectors
+    const int MC = std::min(GP_W_FLOATS / s.E, GP_X_BYTES / (esz * TT)) & ~7;
+    const int grid = (s.S + TT - 1) / TT;
     if (s.dtype == MOE_DT_BF16)
-        hipLaunchKernelGGL(gate_project_kernel<true>, dim3(grid), dim3(kThreads), 0, st, x, Wg, logits, s.S, s.M, s.E);
+        hipLaunchKernelGGL(gate_project_kernel<true>, dim3(grid), dim3(threads), 0, st, x, Wg, logits, s.S, s.M, s.E,
+                           TT, MC);
     else
-        hipLaunchKernelGGL(gate_project_kernel<false>, dim3(grid), dim3(kThreads), 0, st, x, Wg, logits, s.S, s.M,
-                           s.E);
+        hipLaunchKernelGGL(gate_project_kernel<false>, dim3(grid), dim3(threads), 0, st, x, Wg, logits, s.S, s.M,
+                           s.E, TT, MC);
     return hipGetLastError();
 }
 

@@ -24,6 +24,8 @@
 // written to LDS. Results are staged through LDS so that bias, activation and
 // stores run on 16-byte row chunks. Row tiles past fill[e] exit at once.
 // fp32 (MOE_DT_F32) uses a plain LDS-tiled SIMT kernel with the same maths.
+#include <cstdlib>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -242,6 +244,386 @@ __global__ __launch_bounds__(NT) void rows_gemm_bf16(const bf16_t *__restrict__ 
     }
 }
 
+// ------------------------------------------------------------------ rows-grouped bf16 GEMM, large tiles
+
+// Forward products (A and B both k-contiguous) with BM x BN tiles (128 or 256
+// each), NTH/64 wavefronts in a 2 x (NTH/128) grid, a two-stage LDS ring of
+// 64-wide K steps filled by direct global->LDS 16-byte loads (no register
+// staging), persistent workgroups walking an XCD-aware tile order. A
+// wavefront's load writes 64 consecutive 16-byte LDS slots (8 rows of 64 k);
+// each lane fetches the global chunk that belongs at its slot under the row
+// XOR swizzle, so fragment reads are free of bank conflicts. Rows past the
+// valid range are clamped to the last valid row: they only feed output rows
+// or columns that are never stored.
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// 16-byte chunk slot of logical chunk c of row r in a tile whose rows hold KB
+// bf16 (KB/8 chunks). The LDS serves 16 lanes of a 16-byte read per cycle over
+// 64 four-byte banks (256 bytes, 16 chunk slots); row r starts at slot
+// (r * KB/8) mod 16, so rows r and r + 16/(KB/8) start on the same slot. XOR-ing
+// the chunk index with (r / (16/(KB/8))) mod (KB/8) spreads the 16 consecutive
+// rows a fragment read touches (same logical chunk) over all 16 slots.
+template <int KB>
+__device__ __forceinline__ int swz_chunk(int row, int c) {
+    constexpr int CPR = KB / 8, RPB = 16 / CPR;
+    return c ^ ((row / RPB) & (CPR - 1));
+}
+
+template <int R, int KB, int NW>
+__device__ __forceinline__ void dma_tile(const bf16_t *base, int64_t ld, int rows_valid, int k0, bf16_t *lds,
+                                         int wave, int lane) {
+    constexpr int CPR = KB / 8;          // chunks per row
+    constexpr int RPI = 64 / CPR;        // rows per wavefront instruction
+    static_assert(R % (NW * RPI) == 0, "tile rows must split evenly over the wavefronts");
+#pragma unroll
+    for (int j = 0; j < R / (NW * RPI); ++j) {
+        const int rb = (j * NW + wave) * RPI;
+        const int row = rb + lane / CPR;
+        const int kc = swz_chunk<KB>(row, lane % CPR);  // the logical chunk stored at slot lane % CPR
+        const int src_row = row < rows_valid ? row : rows_valid - 1;
+        __builtin_amdgcn_global_load_lds(base + static_cast<int64_t>(src_row) * ld + k0 + kc * 8,
+                                         (lds_void_t *)(lds + rb * KB), 16, 0, 0);
+    }
+}
+
+// s_waitcnt with only the vector-memory counter constrained (vmcnt <= N).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Workgroup barrier that leaves direct-to-LDS loads in flight. __syncthreads()
+// is a release/acquire fence plus s_barrier, and the fence makes the compiler
+// wait for every outstanding vector-memory operation (vmcnt(0)), which would
+// drain the loads of later ring stages at every K step. Here each wavefront
+// waits for its own loads of the stage about to be read (wait_vmcnt) before
+// the barrier; the memory clobber keeps the compiler from moving LDS accesses
+// across it. LDS reads of the stage being recycled have completed before the
+// barrier because their fragments were consumed by MFMAs.
+__device__ __forceinline__ void barrier_keep_loads() { asm volatile("s_barrier" ::: "memory"); }
+// The same after this wavefront's outstanding LDS reads have completed, for a
+// barrier after which other wavefronts overwrite the LDS just read.
+__device__ __forceinline__ void barrier_keep_loads_lds() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Fragments of one 16-wide k slice (kk) of the LDS tiles. The MFMA operands
+// are swapped: the weight (output-feature) fragment is the 32-row operand and
+// the token fragment the 32-column one, so lane l ends up holding, for each
+// 32x32 block, token (l % 32) and features 8q + 4(l / 32) + r at accumulator
+// register 4q + r: four consecutive features per q, stored as one 8-byte chunk.
+template <int TM, int TN, int KB>
+__device__ __forceinline__ void frag_load(const bf16_t *sA, const bf16_t *sB, int kk, bf16x8 (&ax)[TM],
+                                          bf16x8 (&bx)[TN], int wr0, int wc0, int lane) {
+    const int chunk = kk * 2 + (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+        const int row = wr0 + i * 32 + (lane & 31);
+        ax[i] = *reinterpret_cast<const bf16x8 *>(sA + row * KB + (swz_chunk<KB>(row, chunk) << 3));
+    }
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+        const int col = wc0 + j * 32 + (lane & 31);
+        bx[j] = *reinterpret_cast<const bf16x8 *>(sB + col * KB + (swz_chunk<KB>(col, chunk) << 3));
+    }
+}
+
+template <int TM, int TN>
+__device__ __forceinline__ void mfma_slice(const bf16x8 (&ax)[TM], const bf16x8 (&bx)[TN], f32x16 (&acc)[TM][TN]) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bx[j], ax[i], acc[i][j], 0, 0, 0);
+}
+
+// Instruction order of one slice: its MFMAs interleaved one-to-one with the
+// fragment reads of the following slice, then the remaining MFMAs.
+template <int TM, int TN>
+__device__ __forceinline__ void slice_schedule() {
+    constexpr int FR = TM + TN, MF = TM * TN;
+    static_assert(MF >= FR, "a slice needs at least as many MFMAs as fragment reads");
+#pragma unroll
+    for (int f = 0; f < FR; ++f) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, MF - FR, 0);
+}
+
+__device__ __forceinline__ void load4_bf16(const bf16_t *p, float *f) {
+    const uint2 u = *reinterpret_cast<const uint2 *>(p);
+    f[0] = __uint_as_float(u.x << 16);
+    f[1] = __uint_as_float(u.x & 0xFFFF0000u);
+    f[2] = __uint_as_float(u.y << 16);
+    f[3] = __uint_as_float(u.y & 0xFFFF0000u);
+}
+__device__ __forceinline__ void store4_bf16(bf16_t *p, const float *f) {
+    *reinterpret_cast<uint2 *>(p) = make_uint2(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]));
+}
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// 16-byte chunk slot of chunk c of row r in the epilogue tile (CH chunks per
+// row, a power of two): XOR with the row spreads the 32 rows that one
+// fragment store touches over the chunk slots, and a row read stays a
+// permutation of the row's chunks.
+template <int CH>
+__device__ __forceinline__ int epi_swz(int r, int c) {
+    return c ^ (r & (CH - 1));
+}
+
+constexpr int kBigKB = 64;  // k per ring stage of the large-tile GEMM
+// LDS of the large-tile GEMM: two ring stages, the tile prefix table
+// (kMaxE + 1 ints, padded to 16 bytes), then the tile's BN bias values.
+constexpr int kBigPrefixBytes = ((kMaxE + 1) * 4 + 15) / 16 * 16;
+template <int BM, int BN>
+constexpr int big_lds_bytes() {
+    return 2 * (BM + BN) * kBigKB * 2 + kBigPrefixBytes + BN * 2;
+}
+
+// Tile schedule of a persistent rows-grouped GEMM. Expert e has
+// rt_e = ceil(fill[e] / BM) row tiles and nx column tiles; tiles are numbered
+// expert by expert, and inside an expert in groups of GM row tiles walked
+// column by column, so that a window of consecutive tiles shares few A row
+// tiles and few B column tiles. Workgroups are dispatched to the 8 XCDs round
+// robin (workgroup b on XCD b % 8), so XCD x takes the x-th eighth of the tile
+// numbers and its workgroups walk that range together: the tiles in flight on
+// one XCD share their operands in that XCD's L2.
+constexpr int kXcds = 8;
+constexpr int kGroupM = 4;
+
+struct TileSched {
+    int T;        // total tiles
+    int first;    // first tile of this workgroup
+    int stride;   // workgroups on this XCD
+    int end;      // end of this XCD's range
+};
+
+// prefix[e] = sum over e' < e of row tiles (LDS, E + 1 entries); returns the schedule.
+template <int NTH>
+__device__ __forceinline__ TileSched make_sched(const int32_t *fill, int E, int BMv, int nx, int *prefix) {
+    __shared__ int wsum[NTH / 64];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    int base = 0;
+    for (int e0 = 0; e0 < E; e0 += NTH) {
+        const int e = e0 + tid;
+        const int rt = e < E ? (fill[e] + BMv - 1) / BMv : 0;
+        int inc = rt;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int o = __shfl_up(inc, off, 64);
+            if (lane >= off) inc += o;
+        }
+        if (lane == 63) wsum[w] = inc;
+        __syncthreads();
+        int before = 0, total = 0;
+#pragma unroll
+        for (int q = 0; q < NTH / 64; ++q) {
+            before += q < w ? wsum[q] : 0;
+            total += wsum[q];
+        }
+        if (e < E) prefix[e] = base + before + inc - rt;
+        base += total;
+        __syncthreads();
+    }
+    if (tid == 0) prefix[E] = base;
+    __syncthreads();
+    TileSched sc;
+    sc.T = base * nx;
+    const int x = blockIdx.x % kXcds, nb = gridDim.x / kXcds;  // gridDim.x is a multiple of 8
+    const int per = (sc.T + kXcds - 1) / kXcds;
+    const int start = min(sc.T, x * per);
+    sc.end = min(sc.T, start + per);
+    sc.first = start + static_cast<int>(blockIdx.x) / kXcds;
+    sc.stride = nb;
+    return sc;
+}
+
+// tile number -> (expert, row tile, column tile)
+__device__ __forceinline__ void decode_tile(int L, const int *prefix, int E, int nx, int &e, int &rtile, int &ctile) {
+    const int r = L / nx;  // global row-tile index
+    int lo = 0, hi = E - 1;
+    while (lo < hi) {  // last e with prefix[e] <= r
+        const int mid = (lo + hi + 1) >> 1;
+        if (prefix[mid] <= r) lo = mid;
+        else hi = mid - 1;
+    }
+    e = lo;
+    const int rt_e = prefix[e + 1] - prefix[e];
+    const int u = L - prefix[e] * nx;  // tile within the expert
+    const int g = u / (kGroupM * nx);
+    const int gm = min(kGroupM, rt_e - g * kGroupM);
+    const int within = u - g * kGroupM * nx;
+    rtile = g * kGroupM + within % gm;
+    ctile = within / gm;
+}
+
+// K loop ("ping-pong"): two LDS stages of 64 k. The workgroup barrier of stage
+// t sits before its last 16-wide slice: by then every wavefront has read all of
+// stage t's fragments (waited with lgkmcnt(0)) and has waited for its own loads
+// of stage t+1; after it, the loads of stage t+2 go into stage t's buffer and
+// the first fragments of stage t+1 are read while the last slice of stage t
+// multiplies. The barrier does not wait for vector memory (barrier_keep_loads),
+// so a stage's loads have one full stage of MFMA work to land.
+template <int BM, int BN, int NTH, int EPI, int ACT>
+__global__ __launch_bounds__(NTH, 1) void rows_gemm_big(const bf16_t *__restrict__ A, const bf16_t *__restrict__ B,
+                                                      bf16_t *__restrict__ D, int N, int K, int E,
+                                                      const int32_t *__restrict__ fill,
+                                                      const int32_t *__restrict__ cap,
+                                                      const bf16_t *__restrict__ bias, bf16_t *__restrict__ pre_out) {
+    extern __shared__ __align__(16) bf16_t lds[];
+    constexpr int KB = kBigKB, S = KB / 16;
+    // NW wavefronts in 2 rows x NW/2 columns, each owning a (BM/2) x (BN/(NW/2)) block
+    constexpr int NW = NTH / 64, WGC = NW / 2;
+    constexpr int TM = BM / 64, TN = BN / (32 * WGC);
+    static_assert(TN >= 1 && BN % (32 * WGC) == 0, "wavefront columns must be whole 32-wide blocks");
+    constexpr int STAGE = (BM + BN) * KB;
+    constexpr int LPS = (BM + BN) * KB / 8 / NTH;  // direct-load instructions per stage per thread
+    static_assert(BM * BN <= 2 * STAGE, "the epilogue tile must fit in the ring");
+    static_assert(BM * (BN / 8) % NTH == 0, "epilogue chunks must split evenly over the threads");
+    int *prefix = reinterpret_cast<int *>(lds + 2 * STAGE);
+    bf16_t *sbias = lds + 2 * STAGE + kBigPrefixBytes / 2;
+    const int nx = (N + BN - 1) / BN;
+    const TileSched sc = make_sched<NTH>(fill, E, BM, nx, prefix);
+    const int C = *cap;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wr0 = (wave / WGC) * (BM / 2), wc0 = (wave % WGC) * (BN / WGC);
+    const int nk = K / KB;
+    for (int L = sc.first; L < sc.end; L += sc.stride) {
+        int g, rtile, ctile;
+        decode_tile(L, prefix, E, nx, g, rtile, ctile);
+        const int row0 = rtile * BM, col0 = ctile * BN;
+        const int rows_valid = min(BM, fill[g] - row0);
+        const int cols_valid = min(BN, N - col0);
+        const int64_t grow0 = static_cast<int64_t>(g) * C + row0;
+        const bf16_t *Ab = A + grow0 * K;
+        const bf16_t *Bb = B + static_cast<int64_t>(g) * N * K + static_cast<int64_t>(col0) * K;
+
+        f32x16 acc[TM][TN];
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+        // The previous tile's LDS reads (epilogue) are complete in every
+        // wavefront; its global stores may still be in flight.
+        barrier_keep_loads_lds();
+        // The tile's BN bias values go to LDS by one direct load of wavefront 0,
+        // issued before the ring's loads: vector-memory loads complete in order,
+        // so the stage waits below (which count only the newest loads) cover it.
+        // Columns past the matrix read the last valid chunk and are never used.
+        if (bias != nullptr && wave == 0 && lane < BN / 8) {
+            const int c = min(lane * 8, cols_valid - 8);
+            __builtin_amdgcn_global_load_lds(bias + static_cast<int64_t>(g) * N + col0 + c, (lds_void_t *)sbias, 16,
+                                             0, 0);
+        }
+        dma_tile<BM, KB, NW>(Ab, K, rows_valid, 0, lds, wave, lane);
+        dma_tile<BN, KB, NW>(Bb, K, cols_valid, 0, lds + BM * KB, wave, lane);
+        if (nk > 1) {
+            dma_tile<BM, KB, NW>(Ab, K, rows_valid, KB, lds + STAGE, wave, lane);
+            dma_tile<BN, KB, NW>(Bb, K, cols_valid, KB, lds + STAGE + BM * KB, wave, lane);
+            wait_vmcnt<LPS>();
+        } else {
+            wait_vmcnt<0>();
+        }
+        barrier_keep_loads();
+        bf16x8 fa[2][TM], fb[2][TN];
+        frag_load<TM, TN, KB>(lds, lds + BM * KB, 0, fa[0], fb[0], wr0, wc0, lane);
+        for (int t = 0; t < nk; ++t) {
+            const bf16_t *scur = lds + (t & 1) * STAGE;
+#pragma unroll
+            for (int kk = 0; kk < S - 1; ++kk) {
+                frag_load<TM, TN, KB>(scur, scur + BM * KB, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1], wr0, wc0,
+                                      lane);
+                mfma_slice<TM, TN>(fa[kk & 1], fb[kk & 1], acc);
+                slice_schedule<TM, TN>();
+            }
+            // At the last step this also runs, uniformly: there is no load to wait
+            // for, and the fragments read from the other buffer are not used.
+            wait_vmcnt<0>();  // this wavefront's loads of stage t+1 have landed
+            barrier_keep_loads_lds();
+            if (t + 2 < nk) {
+                bf16_t *sn = lds + (t & 1) * STAGE;
+                dma_tile<BM, KB, NW>(Ab, K, rows_valid, (t + 2) * KB, sn, wave, lane);
+                dma_tile<BN, KB, NW>(Bb, K, cols_valid, (t + 2) * KB, sn + BM * KB, wave, lane);
+            }
+            const bf16_t *snext = lds + ((t + 1) & 1) * STAGE;
+            frag_load<TM, TN, KB>(snext, snext + BM * KB, 0, fa[S & 1], fb[S & 1], wr0, wc0, lane);
+            mfma_slice<TM, TN>(fa[(S - 1) & 1], fb[(S - 1) & 1], acc);
+            slice_schedule<TM, TN>();
+        }
+
+        // Epilogue through LDS. Per 32x32 block, lane l owns token row (l % 32)
+        // and, for q = 0..3, features 8q + 4(l / 32) .. +3: written (bias added,
+        // activation applied, rounded to bf16) into the free ring as a row-major
+        // BM x BN tile whose 16-byte chunks are XOR-swizzled by row, then read
+        // back a row at a time so that every global store is whole 16-byte
+        // chunks of contiguous rows (full cache lines), not 32 rows x 16 bytes.
+        // fc1 with a pre-activation output makes two passes (pre, then h).
+        barrier_keep_loads_lds();  // every wavefront is done with the ring
+        constexpr int NPASS = EPI == EPI_FC1 ? 2 : 1;
+#pragma unroll
+        for (int pass = 0; pass < NPASS; ++pass) {
+            // fc1: pass 0 = pre-activation (only when requested), pass 1 = h
+            if (NPASS == 2 && pass == 0 && pre_out == nullptr) continue;
+            const bool act = EPI == EPI_FC1 && pass == NPASS - 1;
+            bf16_t *dst = (NPASS == 2 && pass == 0) ? pre_out : D;
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+                const int trow = wr0 + i * 32 + (lane & 31);
+#pragma unroll
+                for (int j = 0; j < TN; ++j) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int tcol = wc0 + j * 32 + 8 * q + 4 * (lane >> 5);
+                        f32x2 lo = {acc[i][j][4 * q], acc[i][j][4 * q + 1]};
+                        f32x2 hi = {acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+                        if (bias != nullptr) {
+                            const uint2 u2 = *reinterpret_cast<const uint2 *>(sbias + tcol);
+                            lo[0] += __uint_as_float(u2.x << 16);
+                            lo[1] += __uint_as_float(u2.x & 0xFFFF0000u);
+                            hi[0] += __uint_as_float(u2.y << 16);
+                            hi[1] += __uint_as_float(u2.y & 0xFFFF0000u);
+                        }
+                        if (act) {
+                            lo[0] = act_fast<ACT>(lo[0]);
+                            lo[1] = act_fast<ACT>(lo[1]);
+                            hi[0] = act_fast<ACT>(hi[0]);
+                            hi[1] = act_fast<ACT>(hi[1]);
+                        }
+                        const bf16x2 plo = __builtin_convertvector(lo, bf16x2);
+                        const bf16x2 phi = __builtin_convertvector(hi, bf16x2);
+                        uint2 w;
+                        w.x = *reinterpret_cast<const uint32_t *>(&plo);
+                        w.y = *reinterpret_cast<const uint32_t *>(&phi);
+                        const int c = tcol >> 3;
+                        *reinterpret_cast<uint2 *>(lds + trow * BN + (epi_swz<BN / 8>(trow, c) << 3) +
+                                                   ((lane >> 5) << 2)) = w;
+                    }
+                }
+            }
+            barrier_keep_loads_lds();
+            constexpr int CH = BN / 8;
+#pragma unroll 4
+            for (int u = 0; u < BM * CH / NTH; ++u) {
+                const int idx = tid + u * NTH, r = idx / CH, c = idx % CH;
+                const uint4 v = *reinterpret_cast<const uint4 *>(lds + r * BN + (epi_swz<CH>(r, c) << 3));
+                if (r < rows_valid && c * 8 < cols_valid)
+                    *reinterpret_cast<uint4 *>(dst + (grow0 + r) * N + col0 + c * 8) = v;
+            }
+            if (pass + 1 < NPASS) barrier_keep_loads_lds();  // the tile is read before the next pass rewrites it
+        }
+        // The next tile's barrier (below the loop head) orders these LDS reads
+        // before its loads refill the ring; the global stores drain meanwhile.
+    }
+    wait_vmcnt<0>();  // no direct-to-LDS write may land after the workgroup's LDS is released
+}
+
 // ------------------------------------------------------------------ K-grouped bf16 GEMM (weight gradients)
 
 __global__ __launch_bounds__(NT) void kgroup_gemm_bf16(const bf16_t *__restrict__ A, const bf16_t *__restrict__ B,
@@ -415,6 +797,74 @@ hipError_t rows_launch(int act, const void *A, const void *B, void *D, int N, in
     return hipGetLastError();
 }
 
+// Workgroups that fit on the device at once (a multiple of the XCD count).
+static int resident_blocks(int per_cu) {
+    static int cus[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    if (cus[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cus[dev] = n;
+    }
+    return ((cus[dev] * per_cu + kXcds - 1) / kXcds) * kXcds;
+}
+
+template <int BM, int BN, int NTH, int EPI>
+hipError_t big_launch(int act, const void *A, const void *B, void *D, int N, int K, int E, const int32_t *fill,
+                      const int32_t *cap, const void *bias, void *pre_out, hipStream_t st) {
+    constexpr int lds = big_lds_bytes<BM, BN>();
+    constexpr int per_cu = (160 * 1024) / lds >= 2 ? 2 : 1;
+    const dim3 grid(resident_blocks(per_cu));
+    auto a = static_cast<const bf16_t *>(A);
+    auto b = static_cast<const bf16_t *>(B);
+    auto d = static_cast<bf16_t *>(D);
+    auto bi = static_cast<const bf16_t *>(bias);
+    auto po = static_cast<bf16_t *>(pre_out);
+    if (act == MOE_ACT_GELU) {
+        auto k = rows_gemm_big<BM, BN, NTH, EPI, MOE_ACT_GELU>;
+        static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(k),
+                                                           hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+        if (attr != hipSuccess) return attr;
+        hipLaunchKernelGGL(k, grid, dim3(NTH), lds, st, a, b, d, N, K, E, fill, cap, bi, po);
+    } else {
+        auto k = rows_gemm_big<BM, BN, NTH, EPI, MOE_ACT_RELU>;
+        static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(k),
+                                                           hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+        if (attr != hipSuccess) return attr;
+        hipLaunchKernelGGL(k, grid, dim3(NTH), lds, st, a, b, d, N, K, E, fill, cap, bi, po);
+    }
+    return hipGetLastError();
+}
+
+// Forward-product tile configuration. 256 x 256 tiles (eight wavefronts, one
+// workgroup per CU) halve the operand traffic per flop of 128 x 128 tiles (four
+// wavefronts, two workgroups per CU), and win on every measured shape except
+// short-K products: with K <= 1024 a tile's fixed cost (prologue loads and the
+// epilogue) is a large share of its time, and two independent workgroups per
+// CU overlap one's epilogue with the other's MFMAs. MOE_GEMM_CFG overrides the
+// choice for tuning (1 = 256 x 256, 2 = 256 x 128, 3 = 128 x 128).
+static int gemm_cfg_override() {
+    static const int v = [] {
+        const char *e = getenv("MOE_GEMM_CFG");
+        return e ? atoi(e) : 0;
+    }();
+    return v;
+}
+
+template <int EPI>
+hipError_t fwd_launch(int act, const void *A, const void *B, void *D, int N, int K, int cmax, int E,
+                      const int32_t *fill, const int32_t *cap, const void *bias, void *pre_out, hipStream_t st) {
+    (void)cmax;
+    int cfg = gemm_cfg_override();
+    if (cfg < 1 || cfg > 3) cfg = K <= 1024 ? 3 : 1;
+    switch (cfg) {
+    case 1: return big_launch<256, 256, 512, EPI>(act, A, B, D, N, K, E, fill, cap, bias, pre_out, st);
+    case 2: return big_launch<256, 128, 256, EPI>(act, A, B, D, N, K, E, fill, cap, bias, pre_out, st);
+    default: return big_launch<128, 128, 256, EPI>(act, A, B, D, N, K, E, fill, cap, bias, pre_out, st);
+    }
+}
+
 hipError_t kgroup_launch(const void *A, const void *B, float *D, int Mo, int No, int E, const int32_t *fill,
                          const int32_t *cap, float *colsum, hipStream_t st) {
     const dim3 grid((No + BN - 1) / BN, (Mo + BM - 1) / BM, E);
@@ -429,7 +879,7 @@ hipError_t launch_fc1(const moe_shape &s, const void *buf, const void *W1, const
                       const int32_t *cap, void *pre, void *h, int32_t cmax, hipStream_t st) {
     const int M = s.M, H = s.H, E = s.E;
     if (s.dtype == MOE_DT_BF16)
-        return rows_launch<true, EPI_FC1>(s.act, buf, W1, h, H, M, cmax, E, fill, cap, b1, nullptr, pre, st);
+        return fwd_launch<EPI_FC1>(s.act, buf, W1, h, H, M, cmax, E, fill, cap, b1, pre, st);
     SimtArgs a{};
     a.A = static_cast<const float *>(buf); a.a_si = M; a.a_sk = 1; a.a_gfix = 0; a.a_gcap = M;
     a.B = static_cast<const float *>(W1); a.b_sn = M; a.b_sk = 1; a.b_gfix = static_cast<int64_t>(H) * M; a.b_gcap = 0;
@@ -443,7 +893,7 @@ hipError_t launch_fc2(const moe_shape &s, const void *h, const void *W2, const v
                       const int32_t *cap, void *y, int32_t cmax, hipStream_t st) {
     const int M = s.M, H = s.H, E = s.E;
     if (s.dtype == MOE_DT_BF16)
-        return rows_launch<true, EPI_FC2>(s.act, h, W2, y, M, H, cmax, E, fill, cap, b2, nullptr, nullptr, st);
+        return fwd_launch<EPI_FC2>(s.act, h, W2, y, M, H, cmax, E, fill, cap, b2, nullptr, st);
     SimtArgs b{};
     b.A = static_cast<const float *>(h); b.a_si = H; b.a_sk = 1; b.a_gfix = 0; b.a_gcap = H;
     b.B = static_cast<const float *>(W2); b.b_sn = H; b.b_sk = 1; b.b_gfix = static_cast<int64_t>(M) * H; b.b_gcap = 0;

@@ -33,6 +33,13 @@ moe_status hip_fail(hipError_t e, const char *where) {
         if (!(cond)) return fail(MOE_EINVAL, __VA_ARGS__); \
     } while (0)
 
+// The kernels move rows in 16-byte vectors; NULL counts as aligned.
+template <class... P>
+bool aligned16(P... p) {
+    return (((reinterpret_cast<uintptr_t>(p) & 15u) == 0) && ...);
+}
+#define MOE_REQUIRE_ALIGNED(...) MOE_REQUIRE(aligned16(__VA_ARGS__), "device buffers must be 16-byte aligned")
+
 int64_t by_factor(const moe_shape &s) {
     // ceil(k * S * |f| / E), the capacity a factor of |f| gives
     return static_cast<int64_t>(std::ceil((static_cast<double>(s.k) * static_cast<double>(s.S) *
@@ -105,6 +112,7 @@ moe_status moe_gate_project(const moe_shape *shape, const void *x, const float *
     if (st != MOE_OK) return st;
     const moe_shape &s = *shape;
     if (s.S > 0) MOE_REQUIRE(x && Wg && logits, "x, Wg and logits must be non-NULL");
+    MOE_REQUIRE_ALIGNED(x, Wg, logits);
     hipError_t e = moe::launch_gate_project(s, x, Wg, logits, as_stream(stream));
     return e == hipSuccess ? MOE_OK : hip_fail(e, "gate projection");
 }
@@ -120,6 +128,7 @@ moe_status moe_route(const moe_shape *shape, const float *logits, int32_t *idx, 
     const size_t need = ws_bytes_needed(s);
     if (need > 0 && (ws == nullptr || ws_bytes < need))
         return fail(MOE_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws == nullptr ? 0 : ws_bytes);
+    MOE_REQUIRE_ALIGNED(logits, idx, loc, gates, needed, fill, capacity, slot_route, ws);
     moe::RouteWs w{static_cast<int32_t *>(ws), num_tiles(s)};
     hipError_t e = moe::launch_route(s, logits, idx, loc, gates, needed, fill, capacity, slot_route, w, by_factor(s),
                                      as_stream(stream));
@@ -133,6 +142,7 @@ moe_status moe_encode(const moe_shape *shape, const void *x, const int32_t *idx,
     const moe_shape &s = *shape;
     MOE_REQUIRE(fill && capacity && buf, "fill, capacity and buf must be non-NULL");
     if (s.S > 0) MOE_REQUIRE(x && idx && loc, "x, idx and loc must be non-NULL");
+    MOE_REQUIRE_ALIGNED(x, idx, loc, fill, capacity, buf);
     hipError_t e = moe::launch_encode(s, x, idx, loc, fill, capacity, buf, static_cast<int32_t>(cap_bound(s)),
                                       as_stream(stream));
     return e == hipSuccess ? MOE_OK : hip_fail(e, "encode");
@@ -147,6 +157,7 @@ moe_status moe_expert_ffn(const moe_shape *shape, const void *buf, const void *W
     MOE_REQUIRE(buf && W1 && W2 && fill && capacity && h && y, "buf, W1, W2, fill, capacity, h and y must be non-NULL");
     MOE_REQUIRE((b1 != nullptr) == (s.has_fc1_bias != 0), "b1 must be given iff has_fc1_bias");
     MOE_REQUIRE((b2 != nullptr) == (s.has_fc2_bias != 0), "b2 must be given iff has_fc2_bias");
+    MOE_REQUIRE_ALIGNED(buf, W1, b1, W2, b2, fill, capacity, pre, h, y);
     const int32_t cmax = static_cast<int32_t>(cap_bound(s));
     hipError_t e = moe::launch_fc1(s, buf, W1, b1, fill, capacity, pre, h, cmax, as_stream(stream));
     if (e != hipSuccess) return hip_fail(e, "expert fc1");
@@ -161,6 +172,7 @@ moe_status moe_expert_fc1(const moe_shape *shape, const void *buf, const void *W
     const moe_shape &s = *shape;
     MOE_REQUIRE(buf && W1 && fill && capacity && h, "buf, W1, fill, capacity and h must be non-NULL");
     MOE_REQUIRE((b1 != nullptr) == (s.has_fc1_bias != 0), "b1 must be given iff has_fc1_bias");
+    MOE_REQUIRE_ALIGNED(buf, W1, b1, fill, capacity, pre, h);
     hipError_t e = moe::launch_fc1(s, buf, W1, b1, fill, capacity, pre, h, static_cast<int32_t>(cap_bound(s)),
                                    as_stream(stream));
     return e == hipSuccess ? MOE_OK : hip_fail(e, "expert fc1");
@@ -173,6 +185,7 @@ moe_status moe_expert_fc2(const moe_shape *shape, const void *h, const void *W2,
     const moe_shape &s = *shape;
     MOE_REQUIRE(h && W2 && fill && capacity && y, "h, W2, fill, capacity and y must be non-NULL");
     MOE_REQUIRE((b2 != nullptr) == (s.has_fc2_bias != 0), "b2 must be given iff has_fc2_bias");
+    MOE_REQUIRE_ALIGNED(h, W2, b2, fill, capacity, y);
     hipError_t e = moe::launch_fc2(s, h, W2, b2, fill, capacity, y, static_cast<int32_t>(cap_bound(s)),
                                    as_stream(stream));
     return e == hipSuccess ? MOE_OK : hip_fail(e, "expert fc2");
@@ -185,6 +198,7 @@ moe_status moe_decode(const moe_shape *shape, const void *y, const float *gates,
     const moe_shape &s = *shape;
     MOE_REQUIRE(capacity != nullptr, "capacity is NULL");
     if (s.S > 0) MOE_REQUIRE(y && gates && idx && loc && out, "y, gates, idx, loc and out must be non-NULL");
+    MOE_REQUIRE_ALIGNED(y, gates, idx, loc, capacity, out);
     hipError_t e = moe::launch_decode(s, y, gates, idx, loc, capacity, out, false, as_stream(stream));
     return e == hipSuccess ? MOE_OK : hip_fail(e, "decode");
 }
@@ -209,6 +223,8 @@ moe_status moe_layer_forward(const moe_shape *shape, const void *x, const float 
     const size_t need = ws_bytes_needed(s);
     if (need > 0 && (ws == nullptr || ws_bytes < need))
         return fail(MOE_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws == nullptr ? 0 : ws_bytes);
+    MOE_REQUIRE_ALIGNED(x, logits_in, Wg, logits_out, W1, b1, W2, b2, idx, loc, gates, needed, fill, capacity,
+                        slot_route, buf, pre, h, y, out, ws);
     hipStream_t strm = as_stream(stream);
     const int32_t cmax = static_cast<int32_t>(cap_bound(s));
     const float *logits = logits_in;
@@ -243,6 +259,8 @@ moe_status moe_layer_backward(const moe_shape *shape, const void *dout, const vo
     MOE_REQUIRE(buf && pre && h && y && fill && capacity && W1 && W2 && dy && dpre && dbuf && dW1 && dW2,
                 "buf, pre, h, y, fill, capacity, W1, W2, dy, dpre, dbuf, dW1 and dW2 must be non-NULL");
     if (s.S > 0) MOE_REQUIRE(dout && gates && idx && loc && dx && dgates, "dout, gates, idx, loc, dx and dgates must be non-NULL");
+    MOE_REQUIRE_ALIGNED(dout, buf, pre, h, y, gates, idx, loc, fill, capacity, W1, W2, dy, dpre, dbuf, dx, dW1, db1,
+                        dW2, db2, dgates);
     hipStream_t strm = as_stream(stream);
     const int32_t cmax = static_cast<int32_t>(cap_bound(s));
     hipError_t e;

@@ -43,6 +43,31 @@ __device__ __forceinline__ float gelu_grad_f(float v) {
     return cdf + v * pdf;
 }
 
+// erf by Abramowitz & Stegun, Handbook of Mathematical Functions, formula
+// 7.1.26: erf(x) = 1 - t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) exp(-x^2),
+// t = 1 / (1 + p x) for x >= 0, odd extension; absolute error <= 1.5e-7.
+// Used by the GEMM epilogue, where it costs about half the instructions of erff.
+__device__ __forceinline__ float erf_as(float x) {
+    const float ax = fabsf(x);
+    const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, ax, 1.0f));
+    float y = fmaf(1.061405429f, t, -1.453152027f);
+    y = fmaf(y, t, 1.421413741f);
+    y = fmaf(y, t, -0.284496736f);
+    y = fmaf(y, t, 0.254829592f);
+    y *= t;
+    const float r = 1.0f - y * __expf(-ax * ax);
+    return copysignf(r, x);
+}
+__device__ __forceinline__ float gelu_fast(float v) {
+    return 0.5f * v * (1.0f + erf_as(v * 0.70710678118654752f));
+}
+
+template <int ACT>
+__device__ __forceinline__ float act_fast(float v) {
+    if constexpr (ACT == MOE_ACT_RELU) return v > 0.f ? v : 0.f;
+    else return gelu_fast(v);
+}
+
 template <int ACT>
 __device__ __forceinline__ float act_f(float v) {
     if constexpr (ACT == MOE_ACT_RELU) return v > 0.f ? v : 0.f;

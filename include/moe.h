@@ -28,6 +28,8 @@
  *    and keeps no state between calls; calls on different streams may overlap.
  *  - `stream` is a hipStream_t (NULL = the null stream). Device work is only
  *    enqueued; no call waits for the device.
+ *  - Every device pointer is 16-byte aligned (checked: MOE_EINVAL); the
+ *    kernels move rows as 16-byte vectors.
  *  - Data-type tensors (x, W1, b1, W2, b2, buf, pre, h, y, out, dout, dx, dy,
  *    dpre, dbuf) are fp32 or bf16 as moe_shape.dtype says. logits, Wg, gates,
  *    dgates and the weight/bias gradients are fp32. Index tables are int32.

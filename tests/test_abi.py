@@ -94,3 +94,8 @@ def test_entry_points_reject_before_enqueueing(moe):
     assert st == moe.MOE_EINVAL
     with pytest.raises(moe.MoeError):
         moe._check(lib.moe_decode(ctypes.byref(c), None, None, None, None, None, None, None))
+    odd = ctypes.c_void_p(0x1008)  # 8-byte aligned only
+    st = lib.moe_encode(ctypes.byref(c), odd, fake, fake, fake, fake, fake, None)
+    assert st == moe.MOE_EINVAL and "aligned" in moe.moe_last_error()
+    st = lib.moe_expert_fc2(ctypes.byref(c), fake, fake, fake, fake, fake, odd, None)
+    assert st == moe.MOE_EINVAL and "aligned" in moe.moe_last_error()

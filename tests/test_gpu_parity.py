@@ -27,6 +27,9 @@ MID = [
                act=W.ACT_RELU),
     W.Workload("mid_f32_gelu_S333_E6_k2", S=333, M=128, E=6, k=2, H=192, capacity_factor=0.5, dtype=W.DT_F32),
     W.Workload("mid_relu_bf16_S257_E5_k5", S=257, M=64, E=5, k=5, H=64, capacity_factor=0.0, act=W.ACT_RELU),
+    # K > 1024 in both products, so the forward GEMMs take their large-tile
+    # configuration; ragged row tiles and a partial last column tile (1152, 1088)
+    W.Workload("mid_bigtile_S600_M1088_E4_k2_H1152", S=600, M=1088, E=4, k=2, H=1152, capacity_factor=1.0),
 ]
 
 
@@ -87,15 +90,30 @@ def test_route_empty_input():
     assert g["C"] == 1 and (g["needed"] == 0).all() and (g["fill"] == 0).all()
 
 
-def test_gate_projection_bit_exact():
+# Gate projection shapes: one chunk and several chunks of Wg rows, ragged token
+# blocks, E above 256 (two outputs per thread), E not a power of two, both dtypes.
+GATE_CASES = [
+    MID[3],
+    W.GATED_BF16.replace(S=1024),
+    W.Workload("gp_bf16_S33_M3072_E8", S=33, M=3072, E=8, k=2, H=64, capacity_factor=1.0, logits="gate"),
+    W.Workload("gp_f32_S50_M2048_E3", S=50, M=2048, E=3, k=1, H=64, capacity_factor=1.0, dtype=W.DT_F32,
+               logits="gate"),
+    W.Workload("gp_f32_S45_M192_E300", S=45, M=192, E=300, k=3, H=64, capacity_factor=1.0, dtype=W.DT_F32,
+               logits="gate"),
+    W.Workload("gp_bf16_S37_M128_E512", S=37, M=128, E=512, k=2, H=64, capacity_factor=1.0, logits="gate"),
+    W.Workload("gp_bf16_S5_M64_E200", S=5, M=64, E=200, k=4, H=64, capacity_factor=1.0, logits="gate"),
+]
+
+
+@pytest.mark.parametrize("w", GATE_CASES, ids=lambda w: w.name)
+def test_gate_projection_bit_exact(w):
     import combine_softmax_top_amd as moe
-    for w in (MID[3], W.GATED_BF16.replace(S=1024)):
-        inp = W.make_inputs(w, seed=3)
-        o = oracle.gate_logits(host(inp["x"]), host(inp["Wg"]), w.dtype)
-        logits = torch.empty(w.S, w.E, dtype=torch.float32, device="cuda")
-        moe.moe_gate_project(shape_of(w), inp["x"].cuda(), inp["Wg"].cuda(), logits)
-        torch.cuda.synchronize()
-        assert np.array_equal(host(logits), o)
+    inp = W.make_inputs(w, seed=3)
+    o = oracle.gate_logits(host(inp["x"]), host(inp["Wg"]), w.dtype)
+    logits = torch.empty(w.S, w.E, dtype=torch.float32, device="cuda")
+    moe.moe_gate_project(shape_of(w), inp["x"].cuda(), inp["Wg"].cuda(), logits)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(logits), o)
 
 
 # ------------------------------------------------------------------ stage by stage
