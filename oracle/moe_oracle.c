@@ -139,16 +139,35 @@ double oracle_act_grad(int act, double v) { return act_grad(act, v); }
 
 /* ------------------------------------------------------------------ gating */
 
-/* Gate projection: logit[s][e] = fp32( sum_m x[s][m] * Wg[m][e] ), the sum in
- * fp64 over m in order. x is [S,M] in the data type, Wg is [M,E] fp32. */
+/* Gate projection: logit[s][e] = fp32( sum_m x[s][m] * Wg[m][e] ). x is [S,M]
+ * in the data type, Wg is [M,E] fp32; every product is exact in fp64. The pages
+ * leave the summation order open; the reading taken here: m is cut into
+ * consecutive chunks of L = 64 * ceil(M / 4096) (so there are at most 64; the
+ * last may be shorter), each chunk is summed in fp64 from 0 in increasing m,
+ * and the chunk sums are combined level by level, neighbours 2i and 2i+1
+ * added (left + right), an unpaired last sum carried up unchanged; the root
+ * is rounded once to fp32. */
+enum { GATE_MAX_CHUNKS = 64 };
+static int32_t gate_chunk_len(int32_t M) { return 64 * ((M + 4095) / 4096); }
+
 void oracle_gate_logits(int32_t S, int32_t M, int32_t E, int dtype, const void *x,
                         const float *Wg, float *logits) {
+    const int32_t L = gate_chunk_len(M);
+    const int32_t n = (M + L - 1) / L;
     for (int64_t s = 0; s < S; ++s)
         for (int32_t e = 0; e < E; ++e) {
-            double acc = 0.0;
-            for (int32_t m = 0; m < M; ++m)
-                acc += load_elem(x, dtype, s * M + m) * (double)Wg[(int64_t)m * E + e];
-            logits[s * E + e] = (float)acc;
+            double part[GATE_MAX_CHUNKS];
+            for (int32_t c = 0; c < n; ++c) {
+                double acc = 0.0;
+                for (int32_t m = c * L; m < M && m < (c + 1) * L; ++m)
+                    acc += load_elem(x, dtype, s * M + m) * (double)Wg[(int64_t)m * E + e];
+                part[c] = acc;
+            }
+            for (int32_t cnt = n; cnt > 1; cnt = (cnt + 1) / 2) {
+                for (int32_t i = 0; i < cnt / 2; ++i) part[i] = part[2 * i] + part[2 * i + 1];
+                if (cnt % 2) part[cnt / 2] = part[cnt - 1];
+            }
+            logits[s * E + e] = (float)part[0];
         }
 }
 

@@ -57,6 +57,65 @@ def test_activation_matches_library():
 
 # ---------------------------------------------------------------- gate projection
 
+def _gate_case(x_vals, w_vals):
+    """One token, one expert: x (exactly representable in bf16) and the Wg column."""
+    x = bf16_bits_of_f32(np.asarray(x_vals, np.float32)[None, :])
+    Wg = np.asarray(w_vals, np.float32)[:, None]
+    return x, Wg
+
+
+def test_gate_logits_summation_order_is_chunked_tree():
+    # Reading of the unspecified summation order: chunks of 64 products summed
+    # in order in fp64, chunk sums combined pairwise (left + right, an odd one
+    # carried up). Products: +2^30 at m = 0, 2^-23 at m = 64..126 (63 terms),
+    # -2^30 at m = 128; all others 0. Chunk sums: 2^30, 63 * 2^-23 (exact),
+    # -2^30.
+    #   chunked tree ((c0 + c1) + c2): 63 * 2^-23 is 31.5 ulps of 2^30 (ulp
+    #     2^-22), a tie rounded to even: 2^30 + 2^-17; minus 2^30 gives 2^-17.
+    #   one sequential sum: each 2^-23 is half an ulp of 2^30 and rounds away
+    #     (to even), giving 0; chunks of 128 behave the same.
+    #   right-leaning tree (c0 + (c1 + c2)): 2^30 - 63 * 2^-23 is exact (ulp
+    #     2^-23 below 2^30), giving 63 * 2^-23.
+    M = 192
+    xv = np.zeros(M, np.float32)
+    wv = np.zeros(M, np.float32)
+    xv[0], wv[0] = 2.0 ** 15, 2.0 ** 15
+    xv[64:127], wv[64:127] = 2.0 ** -8, 2.0 ** -15
+    xv[128], wv[128] = -(2.0 ** 15), 2.0 ** 15
+    x, Wg = _gate_case(xv, wv)
+    got = oracle.gate_logits(x, Wg, W.DT_BF16)[0, 0]
+    assert got == np.float32(2.0 ** -17)
+
+
+def test_gate_logits_one_hot_weights_select_inputs():
+    # Wg[m][e] = 1 iff m == e: every logit is one input element, whatever the order.
+    rng = np.random.default_rng(7)
+    S, M, E = 6, 4160, 5  # M > 4096: chunks of 128, 33 of them, the last one short
+    x = bf16_bits_of_f32(rng.standard_normal((S, M)).astype(np.float32))
+    Wg = np.zeros((M, E), np.float32)
+    for e in range(E):
+        Wg[e * 997, e] = 1.0
+    got = oracle.gate_logits(x, Wg, W.DT_BF16)
+    assert np.array_equal(got, f32_of(x)[:, [e * 997 for e in range(E)]])
+
+
+def test_gate_logits_within_error_bound_of_exact_sum():
+    # The fp64 tree sum differs from the exact sum by far less than half an fp32
+    # ulp of typical logits, so the fp32 result is the exact sum rounded, except
+    # (rarely) next to a rounding boundary: allow one fp32 ulp.
+    import math
+    rng = np.random.default_rng(11)
+    S, M, E = 4, 1024, 3
+    x = bf16_bits_of_f32(rng.standard_normal((S, M)).astype(np.float32))
+    Wg = (rng.standard_normal((M, E)) * 0.02).astype(np.float32)
+    got = oracle.gate_logits(x, Wg, W.DT_BF16)
+    xf = f32_of(x).astype(np.float64)
+    for s in range(S):
+        for e in range(E):
+            exact = np.float32(math.fsum(xf[s] * Wg[:, e].astype(np.float64)))
+            assert abs(int(got[s, e].view(np.int32)) - int(exact.view(np.int32))) <= 1
+
+
 def test_gate_logits_exact_products_and_fp32_rounding():
     # bf16 x times fp32 Wg: each product is exact in fp64; the sum of few terms is too.
     rng = np.random.default_rng(1)
