@@ -221,109 +221,221 @@ __global__ __launch_bounds__(kThreads) void decode_bwd_kernel(const uint4 *__res
 
 // ---------------------------------------------------------------- gate projection
 
-// logits[s][e] = fp32(sum_m x[s][m] * Wg[m][e]): one thread per output, an fp64
-// accumulator updated in increasing m. Each product of a bf16/fp32 input and an
-// fp32 weight is exact in fp64, so fma(x, w, acc) rounds exactly like acc + x*w
-// and the fp32 logit is the fp64 sequential sum rounded once. A block covers TT
-// tokens and all E experts (IPT experts per thread when E > 256). Per chunk of
-// MC rows of Wg, the block first copies the chunk of Wg and its TT rows of x
-// into LDS with all loads in flight at once (the chains are short, so load
-// latency, not arithmetic, bounds this kernel), then runs the chains from LDS.
-constexpr int GP_W_FLOATS = 8192;  // Wg rows of one chunk: 32 KiB
-constexpr int GP_X_BYTES = 32768;  // the block's x rows of one chunk: 32 KiB
-constexpr int GP_MAX_TT = 16;
-constexpr int GP_UNROLL = 8;       // 16-byte loads in flight per thread
+// logits[s][e] = fp32(sum_m x[s][m] * Wg[m][e]), the sum in fp64 in a fixed
+// order: m is cut into n chunks of L = 64 * ceil(M / 4096) (n <= 64, the last
+// may be shorter), each chunk is summed from 0 in increasing m, and the chunk
+// sums are combined level by level, neighbours 2i and 2i+1 added, an unpaired
+// last sum carried up; the root is rounded once to fp32. Each product of a
+// bf16/fp32 input and an fp32 weight is exact in fp64, so fma(x, w, acc)
+// rounds exactly like acc + x*w.
+//
+// A block takes a tile of TT tokens and ET experts. It stages in LDS the
+// tile's x rows and the Wg columns of its experts, every load in flight at
+// once, both cut into the summation chunks with a 16-byte pad per chunk so
+// that lanes on different chunks read different banks. Lane (c, e, u) then
+// runs the L-long chains of chunk c, expert e for tokens u, u + TS, ... (TPL of
+// them, TS = 256 / (G * ET)) from LDS. The G = pow2ceil(n) lanes of a
+// (token, expert) are consecutive, so the tree runs on shuffles: at stride s,
+// lane c (a multiple of 2s) adds lane c + s when c + s < n -- the element at
+// lane j * 2^l of level l exists iff j * 2^l < n, which is the level-by-level
+// pairing above. Lanes c >= n hold empty chains that are never added.
+// Division by a run-time invariant d >= 1 for 0 <= x < 2^31 (Granlund and
+// Montgomery, "Division by invariant integers using multiplication", 1994):
+// with s = ceil(log2 d) and m = floor(2^32 (2^s - d) / d) + 1,
+// x / d = (mulhi(x, m) + x) >> s.
+struct FastDiv {
+    uint32_t d, m, s;
+    __host__ static FastDiv make(uint32_t dv) {
+        FastDiv f{dv, 0u, 0u};
+        while ((1ull << f.s) < dv) ++f.s;
+        f.m = static_cast<uint32_t>(((1ull << 32) * ((1ull << f.s) - dv)) / dv + 1);
+        return f;
+    }
+    __device__ __forceinline__ int div(int x) const {
+        const uint32_t hi = __umulhi(static_cast<uint32_t>(x), m);
+        return static_cast<int>((static_cast<uint64_t>(hi) + static_cast<uint32_t>(x)) >> s);
+    }
+};
 
-template <bool BF16>
+struct GateTile {
+    FastDiv dne, dvpr, dvpc, dL, dLE4;  // by experts in the tile, x vectors per row / per chunk,
+                                        // chunk length, float4s per chunk of all experts
+    int L, n, G;     // chunk length, chunk count, lanes per (token, expert)
+    int ET, TS, TPL; // experts per block, token lanes, tokens per lane
+    int wpitch;      // floats per Wg chunk in LDS: L * ET + 4
+    int xpitch;      // bytes per x chunk in LDS: L * esz + 16
+    size_t lds;      // bytes
+};
+
+constexpr int kGateLdsMax = 160 * 1024;
+
+__host__ GateTile gate_tile(int S, int M, int E, int esz) {
+    GateTile t{};
+    t.L = 64 * ((M + 4095) / 4096);
+    t.n = (M + t.L - 1) / t.L;
+    t.G = 1;
+    while (t.G < t.n) t.G <<= 1;
+    t.ET = std::min(E, 256 / t.G);
+    t.wpitch = t.L * t.ET + 4;
+    while (t.ET > 1 && static_cast<size_t>(t.n) * (t.L * t.ET + 4) * 4 > 64 * 1024) {
+        --t.ET;
+        t.wpitch = t.L * t.ET + 4;
+    }
+    t.TS = 256 / (t.G * t.ET);
+    t.xpitch = t.L * esz + 16;
+    const size_t wbytes = static_cast<size_t>(t.n) * t.wpitch * 4;
+    const size_t xrow = static_cast<size_t>(t.n) * t.xpitch;
+    // tokens per lane: up to 8 while the LDS tiles fit and the grid keeps at
+    // least two blocks per CU (512) along the tokens
+    t.TPL = 1;
+    while (t.TPL < 8 && wbytes + xrow * t.TS * (t.TPL * 2) <= static_cast<size_t>(kGateLdsMax) &&
+           (S + t.TS * t.TPL * 2 - 1) / (t.TS * t.TPL * 2) >= 512)
+        t.TPL *= 2;
+    t.lds = wbytes + xrow * t.TS * t.TPL;
+    t.dne = FastDiv::make(static_cast<uint32_t>(t.ET));
+    t.dvpr = FastDiv::make(static_cast<uint32_t>(M / (16 / esz)));
+    t.dvpc = FastDiv::make(static_cast<uint32_t>(t.L / (16 / esz)));
+    t.dL = FastDiv::make(static_cast<uint32_t>(t.L));
+    t.dLE4 = FastDiv::make(static_cast<uint32_t>(t.L * E / 4));
+    return t;
+}
+
+template <bool BF16, int TPL>
 __global__ __launch_bounds__(kThreads) void gate_project_kernel(const void *__restrict__ xv,
                                                                 const float *__restrict__ Wg,
                                                                 float *__restrict__ logits, int S, int M, int E,
-                                                                int TT, int MC) {
-    __shared__ float4 ws[GP_W_FLOATS / 4];
-    // row t of the x chunk starts at xs[t * xstride]; the one-vector pad puts
-    // consecutive tokens' vectors on different banks
-    __shared__ uint4 xs[GP_X_BYTES / 16 + GP_MAX_TT];
-    constexpr int EPV = BF16 ? 8 : 4;  // x elements per 16-byte vector
-    const int tid = threadIdx.x, nt = blockDim.x;
+                                                                GateTile tl) {
+    extern __shared__ __align__(16) unsigned char gsm[];
+    constexpr int ESZ = BF16 ? 2 : 4;
+    constexpr int EPV = 16 / ESZ;  // x elements per 16-byte vector
+    const int L = tl.L, n = tl.n, G = tl.G, ET = tl.ET, TS = tl.TS;
+    const int TT = TS * TPL;
+    float *wl = reinterpret_cast<float *>(gsm);
+    unsigned char *xl = gsm + static_cast<size_t>(n) * tl.wpitch * 4;
+    const int tid = threadIdx.x;
     const int64_t s0 = static_cast<int64_t>(blockIdx.x) * TT;
-    const int ntok = static_cast<int>(min<int64_t>(TT, S - s0));
-    const int items = TT * E;
-    const int xstride = MC / EPV + 1;
-    const uint4 *xg = reinterpret_cast<const uint4 *>(xv);  // row s, vector v at xg[s * (M / EPV) + v]
-    const float4 *wg = reinterpret_cast<const float4 *>(Wg);
-    const float *wsf = reinterpret_cast<const float *>(ws);
-    constexpr int IPT = kMaxE / 256;
-    double acc[IPT];
-    int tok[IPT], ex[IPT];
+    const int e0 = blockIdx.y * ET;
+    const int ne = min(ET, E - e0);
+    const int nt = static_cast<int>(min<int64_t>(TT, S - s0));
+
+    // stage Wg[m][e0 .. e0+ne) at wl[c * wpitch + (m - c*L) * ET + (e - e0)]
+    // (the tile's last expert block may hold ne < ET experts: its divisor is
+    // ne, not the one precomputed for ET)
+    if (ET == E) {
+        // every expert: Wg is M*E contiguous floats; a chunk's L*E of them are
+        // contiguous in LDS too (L*E is a multiple of 4)
+        const int total4 = M * E / 4;
+        const float4 *w4 = reinterpret_cast<const float4 *>(Wg);
+        for (int i0 = tid; i0 < total4; i0 += 8 * kThreads) {
+            float4 r[8];
+            int dst[8];
 #pragma unroll
-    for (int j = 0; j < IPT; ++j) {
-        acc[j] = 0.0;
-        const int it = tid + j * nt;
-        tok[j] = it < items ? it / E : -1;
-        ex[j] = it < items ? it - (it / E) * E : 0;
-        if (tok[j] >= ntok) tok[j] = -1;
-    }
-    for (int m0 = 0; m0 < M; m0 += MC) {
-        const int mc = min(MC, M - m0);
-        const int nv = mc / EPV;
-        __syncthreads();
-        // Wg rows m0 .. m0+mc-1 are mc*E contiguous floats (a multiple of 8)
-        const int nw = mc * E / 4;
-        const float4 *wsrc = wg + static_cast<int64_t>(m0) * E / 4;
-        // loads are unconditional (index clamped to the last element) so that the
-        // staging registers stay registers; only the LDS stores are guarded
-        for (int i0 = tid; i0 < nw; i0 += GP_UNROLL * nt) {
-            float4 r[GP_UNROLL];
-#pragma unroll
-            for (int u = 0; u < GP_UNROLL; ++u) r[u] = wsrc[min(i0 + u * nt, nw - 1)];
-#pragma unroll
-            for (int u = 0; u < GP_UNROLL; ++u)
-                if (i0 + u * nt < nw) ws[i0 + u * nt] = r[u];
-        }
-        const int nx = ntok * nv;
-        for (int i0 = tid; i0 < nx; i0 += GP_UNROLL * nt) {
-            uint4 r[GP_UNROLL];
-            int dst[GP_UNROLL];
-#pragma unroll
-            for (int u = 0; u < GP_UNROLL; ++u) {
-                const int i = min(i0 + u * nt, nx - 1);
-                const int t = i / nv, v = i - t * nv;
-                r[u] = xg[(s0 + t) * (M / EPV) + m0 / EPV + v];
-                dst[u] = t * xstride + v;
+            for (int u = 0; u < 8; ++u) {
+                const int i = min(i0 + u * kThreads, total4 - 1);
+                const int c = tl.dLE4.div(i);
+                r[u] = w4[i];
+                dst[u] = c * tl.wpitch + (i - c * (L * E / 4)) * 4;
             }
 #pragma unroll
-            for (int u = 0; u < GP_UNROLL; ++u)
-                if (i0 + u * nt < nx) xs[dst[u]] = r[u];
+            for (int u = 0; u < 8; ++u)
+                if (i0 + u * kThreads < total4) *reinterpret_cast<float4 *>(wl + dst[u]) = r[u];
         }
-        __syncthreads();
+    } else {
+        const FastDiv dne = ne == ET ? tl.dne : FastDiv{static_cast<uint32_t>(ne), 0u, 0u};
+        const bool fast = ne == ET;
+        const int total = M * ne;
+        for (int i0 = tid; i0 < total; i0 += 8 * kThreads) {
+            float r[8];
+            int dst[8];
 #pragma unroll
-        for (int j = 0; j < IPT; ++j) {
-            if (tok[j] < 0) continue;
-            const uint4 *xr = xs + tok[j] * xstride;
-            const float *wcol = wsf + ex[j];
-#pragma unroll 2
-            for (int v = 0; v < nv; ++v) {
-                const uint4 u = xr[v];
-                const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
-                float xf[EPV];
+            for (int u = 0; u < 8; ++u) {
+                const int i = min(i0 + u * kThreads, total - 1);
+                const int m = fast ? dne.div(i) : i / ne, e = i - m * ne, c = tl.dL.div(m);
+                r[u] = Wg[static_cast<int64_t>(m) * E + e0 + e];
+                dst[u] = c * tl.wpitch + (m - c * L) * ET + e;
+            }
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    if (BF16) {
-                        xf[2 * q] = __uint_as_float(w4[q] << 16);
-                        xf[2 * q + 1] = __uint_as_float(w4[q] & 0xFFFF0000u);
-                    } else {
-                        xf[q] = __uint_as_float(w4[q]);
-                    }
+            for (int u = 0; u < 8; ++u)
+                if (i0 + u * kThreads < total) wl[dst[u]] = r[u];
+        }
+    }
+    // stage x rows s0 .. s0+nt, 16-byte vectors, at xl[(t * n + c) * xpitch + (m - c*L) * ESZ]
+    {
+        const int vpr = M / EPV;  // vectors per row
+        const int vpc = L / EPV;  // vectors per chunk
+        const int total = nt * vpr;
+        const uint4 *xg = reinterpret_cast<const uint4 *>(xv);
+        for (int i0 = tid; i0 < total; i0 += 8 * kThreads) {
+            uint4 r[8];
+            int dst[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int i = min(i0 + u * kThreads, total - 1);
+                const int t = tl.dvpr.div(i), v = i - t * vpr, c = tl.dvpc.div(v);
+                r[u] = xg[(s0 + t) * vpr + v];
+                dst[u] = (t * n + c) * tl.xpitch + (v - c * vpc) * 16;
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (i0 + u * kThreads < total) *reinterpret_cast<uint4 *>(xl + dst[u]) = r[u];
+        }
+    }
+    __syncthreads();
+
+    const int c = tid & (G - 1);
+    const int el = (tid / G) % ET;
+    const int u = tid / (G * ET);
+    const bool live = u < TS && el < ne;
+    const int m0 = c * L, len = max(0, min(M, m0 + L) - m0);
+    double acc[TPL];
+#pragma unroll
+    for (int j = 0; j < TPL; ++j) acc[j] = 0.0;
+    if (live) {
+        const float *wc = wl + c * tl.wpitch + el;
+        const unsigned char *xc[TPL];
+#pragma unroll
+        for (int j = 0; j < TPL; ++j) {
+            const int t = min(u + j * TS, nt - 1);  // tokens past the tile re-read the last one, never stored
+            xc[j] = xl + static_cast<size_t>(t * n + c) * tl.xpitch;
+        }
+        for (int i = 0; i < len; i += EPV) {
+            // all reads of the step first, then the TPL independent chains
+            // interleaved (each chain still takes its products in increasing m)
+            double w[EPV];
+#pragma unroll
+            for (int q = 0; q < EPV; ++q) w[q] = static_cast<double>(wc[(i + q) * ET]);
+            uint4 xv4[TPL];
+#pragma unroll
+            for (int j = 0; j < TPL; ++j) xv4[j] = *reinterpret_cast<const uint4 *>(xc[j] + i * ESZ);
+#pragma unroll
+            for (int q = 0; q < EPV; ++q) {
+#pragma unroll
+                for (int j = 0; j < TPL; ++j) {
+                    const uint32_t word = q / (EPV / 4) == 0 ? xv4[j].x
+                                        : q / (EPV / 4) == 1 ? xv4[j].y
+                                        : q / (EPV / 4) == 2 ? xv4[j].z : xv4[j].w;
+                    float xf;
+                    if (BF16) xf = __uint_as_float((q & 1) ? (word & 0xFFFF0000u) : (word << 16));
+                    else xf = __uint_as_float(word);
+                    acc[j] = fma(static_cast<double>(xf), w[q], acc[j]);
                 }
-#pragma unroll
-                for (int q = 0; q < EPV; ++q)
-                    acc[j] = fma(static_cast<double>(xf[q]), static_cast<double>(wcol[(v * EPV + q) * E]), acc[j]);
             }
         }
     }
+    for (int st = 1; st < G; st <<= 1) {
 #pragma unroll
-    for (int j = 0; j < IPT; ++j)
-        if (tok[j] >= 0) logits[(s0 + tok[j]) * E + ex[j]] = static_cast<float>(acc[j]);
+        for (int j = 0; j < TPL; ++j) {
+            const double o = __shfl_down(acc[j], st, 64);
+            if ((c & (2 * st - 1)) == 0 && c + st < n) acc[j] += o;
+        }
+    }
+    if (live && c == 0) {
+#pragma unroll
+        for (int j = 0; j < TPL; ++j) {
+            const int t = u + j * TS;
+            if (t < nt) logits[(s0 + t) * E + e0 + el] = static_cast<float>(acc[j]);
+        }
+    }
 }
 
 int grid_for(int64_t waves) {
@@ -334,24 +446,40 @@ int grid_for(int64_t waves) {
 
 }  // namespace
 
+template <bool BF16, int TPL>
+static hipError_t gate_launch(const moe_shape &s, const void *x, const float *Wg, float *logits, const GateTile &t,
+                              hipStream_t st) {
+    auto k = gate_project_kernel<BF16, TPL>;
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(k),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, kGateLdsMax);
+    if (attr != hipSuccess) return attr;
+    const int TT = t.TS * TPL;
+    const dim3 grid((s.S + TT - 1) / TT, (s.E + t.ET - 1) / t.ET);
+    hipLaunchKernelGGL(k, grid, dim3(kThreads), t.lds, st, x, Wg, logits, s.S, s.M, s.E, t);
+    return hipGetLastError();
+}
+
+template <bool BF16>
+static hipError_t gate_dispatch(const moe_shape &s, const void *x, const float *Wg, float *logits, hipStream_t st) {
+    const GateTile t = gate_tile(s.S, s.M, s.E, BF16 ? 2 : 4);
+    if (t.lds > static_cast<size_t>(kGateLdsMax)) return hipErrorInvalidValue;
+    switch (t.TPL) {
+    case 8: return gate_launch<BF16, 8>(s, x, Wg, logits, t, st);
+    case 4: return gate_launch<BF16, 4>(s, x, Wg, logits, t, st);
+    case 2: return gate_launch<BF16, 2>(s, x, Wg, logits, t, st);
+    default: return gate_launch<BF16, 1>(s, x, Wg, logits, t, st);
+    }
+}
+
+bool gate_supported(int M, int E, int dtype) {
+    // the token count only lowers tokens per lane, never below the one-token tile checked here
+    return gate_tile(0, M, E, dtype == MOE_DT_BF16 ? 2 : 4).lds <= static_cast<size_t>(kGateLdsMax);
+}
+
 hipError_t launch_gate_project(const moe_shape &s, const void *x, const float *Wg, float *logits, hipStream_t st) {
     if (s.S == 0) return hipSuccess;
-    // tokens per block: up to 256 outputs per block, at most 16 tokens so that
-    // small-E layers still spread over many workgroups
-    const int TT = s.E >= 256 ? 1 : std::min(GP_MAX_TT, 256 / s.E);
-    const int threads = s.E > 256 ? 256 : std::max(64, ((TT * s.E + 63) / 64) * 64);
-    const int esz = s.dtype == MOE_DT_BF16 ? 2 : 4;
-    // chunk rows: Wg chunk and x chunk each fit their LDS area; a multiple of 8
-    // (>= 16 for E <= 512), so every chunk is whole 16-byte vectors
-    const int MC = std::min(GP_W_FLOATS / s.E, GP_X_BYTES / (esz * TT)) & ~7;
-    const int grid = (s.S + TT - 1) / TT;
-    if (s.dtype == MOE_DT_BF16)
-        hipLaunchKernelGGL(gate_project_kernel<true>, dim3(grid), dim3(threads), 0, st, x, Wg, logits, s.S, s.M, s.E,
-                           TT, MC);
-    else
-        hipLaunchKernelGGL(gate_project_kernel<false>, dim3(grid), dim3(threads), 0, st, x, Wg, logits, s.S, s.M,
-                           s.E, TT, MC);
-    return hipGetLastError();
+    return s.dtype == MOE_DT_BF16 ? gate_dispatch<true>(s, x, Wg, logits, st)
+                                  : gate_dispatch<false>(s, x, Wg, logits, st);
 }
 
 hipError_t launch_encode(const moe_shape &s, const void *x, const int32_t *idx, const int32_t *loc,

@@ -113,6 +113,8 @@ moe_status moe_gate_project(const moe_shape *shape, const void *x, const float *
     const moe_shape &s = *shape;
     if (s.S > 0) MOE_REQUIRE(x && Wg && logits, "x, Wg and logits must be non-NULL");
     MOE_REQUIRE_ALIGNED(x, Wg, logits);
+    if (!moe::gate_supported(s.M, s.E, s.dtype))
+        return fail(MOE_EUNSUPPORTED, "gate projection tiles for M=%d, E=%d do not fit in LDS", s.M, s.E);
     hipError_t e = moe::launch_gate_project(s, x, Wg, logits, as_stream(stream));
     return e == hipSuccess ? MOE_OK : hip_fail(e, "gate projection");
 }
@@ -225,6 +227,8 @@ moe_status moe_layer_forward(const moe_shape *shape, const void *x, const float 
         return fail(MOE_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws == nullptr ? 0 : ws_bytes);
     MOE_REQUIRE_ALIGNED(x, logits_in, Wg, logits_out, W1, b1, W2, b2, idx, loc, gates, needed, fill, capacity,
                         slot_route, buf, pre, h, y, out, ws);
+    if (Wg != nullptr && !moe::gate_supported(s.M, s.E, s.dtype))
+        return fail(MOE_EUNSUPPORTED, "gate projection tiles for M=%d, E=%d do not fit in LDS", s.M, s.E);
     hipStream_t strm = as_stream(stream);
     const int32_t cmax = static_cast<int32_t>(cap_bound(s));
     const float *logits = logits_in;

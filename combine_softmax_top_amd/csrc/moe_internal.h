@@ -90,6 +90,8 @@ struct RouteWs {
 
 hipError_t launch_gate_project(const moe_shape &s, const void *x, const float *Wg, float *logits,
                                hipStream_t st);
+// Whether the gate projection's LDS tiles fit for this model dim / expert count.
+bool gate_supported(int M, int E, int dtype);
 hipError_t launch_route(const moe_shape &s, const float *logits, int32_t *idx, int32_t *loc,
                         float *gates, int32_t *needed, int32_t *fill, int32_t *cap, int32_t *slot_route,
                         RouteWs ws, int64_t cap_by_factor, hipStream_t st);

@@ -99,10 +99,16 @@ moe_status moe_capacity_bound(const moe_shape *shape, int32_t *cmax_host);
 /* Bytes of device workspace moe_route / moe_layer_forward need (no GPU needed). */
 moe_status moe_workspace_size(const moe_shape *shape, size_t *bytes_host);
 
-/* Gate projection: logits[s][e] = fp32(sum_m x[s][m] * Wg[m][e]), the sum
- * accumulated in fp64 so that the fp32 logits do not depend on summation order
- * in practice (routing decisions are taken on them).
- * x [S, M] data type, Wg [M, E] fp32 row-major, logits [S, E] fp32. */
+/* Gate projection (Tutel catalogue page, "key configuration": the top-k gate
+ * scores each token against E experts): logits[s][e] = fp32(sum_m x[s][m] *
+ * Wg[m][e]). The products are exact in fp64 and are summed in fp64 in a fixed
+ * order, so the logits (on which routing decisions are taken) are reproducible
+ * bit for bit: m is cut into chunks of 64 * ceil(M / 4096), each chunk summed in
+ * increasing m, the chunk sums combined pairwise level by level (neighbours
+ * added, an unpaired last one carried up), the result rounded once to fp32.
+ * x [S, M] data type, Wg [M, E] fp32 row-major, logits [S, E] fp32.
+ * Supported for M <= 12288 with bf16 x and M <= 7680 with fp32 x (the LDS tiles
+ * must fit; MOE_EUNSUPPORTED otherwise, also from moe_layer_forward with Wg). */
 moe_status moe_gate_project(const moe_shape *shape, const void *x, const float *Wg, float *logits,
                             void *stream);
 

@@ -90,8 +90,9 @@ def test_route_empty_input():
     assert g["C"] == 1 and (g["needed"] == 0).all() and (g["fill"] == 0).all()
 
 
-# Gate projection shapes: one chunk and several chunks of Wg rows, ragged token
-# blocks, E above 256 (two outputs per thread), E not a power of two, both dtypes.
+# Gate projection shapes: one summation chunk (M = 64) up to 48 chunks and the
+# 128-wide chunks of M > 4096, chunk counts that are not powers of two, ragged
+# token groups, E from 3 to 512, both dtypes.
 GATE_CASES = [
     MID[3],
     W.GATED_BF16.replace(S=1024),
@@ -102,6 +103,8 @@ GATE_CASES = [
                logits="gate"),
     W.Workload("gp_bf16_S37_M128_E512", S=37, M=128, E=512, k=2, H=64, capacity_factor=1.0, logits="gate"),
     W.Workload("gp_bf16_S5_M64_E200", S=5, M=64, E=200, k=4, H=64, capacity_factor=1.0, logits="gate"),
+    # M > 4096: chunks of 128, 33 of them, the last one 64 long
+    W.Workload("gp_bf16_S19_M4160_E4", S=19, M=4160, E=4, k=2, H=64, capacity_factor=1.0, logits="gate"),
 ]
 
 
