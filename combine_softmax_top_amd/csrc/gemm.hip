@@ -282,8 +282,64 @@ __device__ __forceinline__ void dma_tile(const bf16_t *base, int64_t ld, int row
         const int row = rb + lane / CPR;
         const int kc = swz_chunk<KB>(row, lane % CPR);  // the logical chunk stored at slot lane % CPR
         const int src_row = row < rows_valid ? row : rows_valid - 1;
-        __builtin_amdgcn_global_load_lds(base + static_cast<int64_t>(src_row) * ld + k0 + kc * 8,
-                                         (lds_void_t *)(lds + rb * KB), 16, 0, 0);
+        // uniform base + 32-bit lane offset (a tile spans well under 2^31 elements)
+        const uint32_t off = static_cast<uint32_t>(src_row * static_cast<int>(ld) + kc * 8);
+        __builtin_amdgcn_global_load_lds(base + k0 + off, (lds_void_t *)(lds + rb * KB), 16, 0, 0);
+    }
+}
+
+// A B tile stored n-contiguous in memory (B[k][n], as the weights are read by
+// the backward data products): KB rows of k, each BN values of n. It lands in
+// LDS as [KB][BN] with 16-byte chunk c of row k at slot c ^ 4(k mod 4). The
+// transposing fragment reads below take a 4 (k) x 16 (n) block per 16 lanes;
+// with this swizzle the 32 lanes of a half-wave touch each of the 64 banks once.
+template <int BN, int KB, int NW>
+__device__ __forceinline__ void dma_tile_mn(const bf16_t *base, int64_t ld, int cols_valid, int k0, bf16_t *lds,
+                                            int wave, int lane) {
+    constexpr int CPR = BN / 8;   // chunks per k row
+    constexpr int RPI = 64 / CPR; // k rows per wavefront instruction
+    static_assert(CPR >= 16 && KB % (NW * RPI) == 0, "n-contiguous tile shape");
+#pragma unroll
+    for (int j = 0; j < KB / (NW * RPI); ++j) {
+        const int rb = (j * NW + wave) * RPI;
+        const int row = rb + lane / CPR;
+        const int c = min((lane % CPR) ^ (4 * (row & 3)), cols_valid / 8 - 1);  // chunk stored at this slot
+        const uint32_t off = static_cast<uint32_t>(row * static_cast<int>(ld) + c * 8);
+        __builtin_amdgcn_global_load_lds(base + static_cast<int64_t>(k0) * ld + off, (lds_void_t *)(lds + rb * BN),
+                                         16, 0, 0);
+    }
+}
+
+typedef short v4s16 __attribute__((ext_vector_type(4)));
+typedef short v8s16 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) v4s16 lds_v4s16_t;
+
+// Weight fragments (the 32-row MFMA operand) of k slice kk from an n-contiguous
+// tile. ds_read_b64_tr_b16 gives lane i of each 16-lane group, for q = 0..3,
+// element (i mod 4) of the 8 bytes read by lane 4q + i/4 of the group; when
+// that lane addresses (k0 + q', n0 + 4 (lane mod 4)) for q' = lane / 4, lane i
+// receives column n0 + i at rows k0 .. k0+3. Two reads (k0 and k0 + 4) make the
+// eight k values of the operand: lane l holds n = l mod 32 of the block and
+// k = 8 (l / 32) .. +7 of the slice.
+// The lane's offset (elements) in the tile for block j at kk = 0: k mod 4 is
+// the same for every slice and both halves, so the other reads add constants.
+template <int BN>
+__device__ __forceinline__ int frag_b_mn_offset(int j, int wc0, int lane) {
+    const int g = lane >> 4, i = lane & 15;
+    const int k = (g >> 1) * 8 + (i >> 2);
+    const int n = wc0 + j * 32 + (g & 1) * 16 + 4 * (i & 3);
+    return k * BN + (((n >> 3) ^ (4 * (k & 3))) << 3) + (n & 7);
+}
+
+template <int TN, int BN>
+__device__ __forceinline__ void frag_b_mn(const bf16_t *sB, int kk, bf16x8 (&bx)[TN], int wc0, int lane) {
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+        const bf16_t *p = sB + frag_b_mn_offset<BN>(j, wc0, lane) + kk * 16 * BN;
+        const v4s16 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s16_t *)p);
+        const v4s16 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s16_t *)(p + 4 * BN));
+        const v8s16 w = __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7);
+        bx[j] = __builtin_bit_cast(bf16x8, w);
     }
 }
 
@@ -313,7 +369,7 @@ __device__ __forceinline__ void barrier_keep_loads_lds() {
 // the token fragment the 32-column one, so lane l ends up holding, for each
 // 32x32 block, token (l % 32) and features 8q + 4(l / 32) + r at accumulator
 // register 4q + r: four consecutive features per q, stored as one 8-byte chunk.
-template <int TM, int TN, int KB>
+template <int TM, int TN, int KB, bool BMN = false, int BN = 0>
 __device__ __forceinline__ void frag_load(const bf16_t *sA, const bf16_t *sB, int kk, bf16x8 (&ax)[TM],
                                           bf16x8 (&bx)[TN], int wr0, int wc0, int lane) {
     const int chunk = kk * 2 + (lane >> 5);
@@ -322,10 +378,14 @@ __device__ __forceinline__ void frag_load(const bf16_t *sA, const bf16_t *sB, in
         const int row = wr0 + i * 32 + (lane & 31);
         ax[i] = *reinterpret_cast<const bf16x8 *>(sA + row * KB + (swz_chunk<KB>(row, chunk) << 3));
     }
+    if constexpr (BMN) {
+        frag_b_mn<TN, BN>(sB, kk, bx, wc0, lane);
+    } else {
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-        const int col = wc0 + j * 32 + (lane & 31);
-        bx[j] = *reinterpret_cast<const bf16x8 *>(sB + col * KB + (swz_chunk<KB>(col, chunk) << 3));
+        for (int j = 0; j < TN; ++j) {
+            const int col = wc0 + j * 32 + (lane & 31);
+            bx[j] = *reinterpret_cast<const bf16x8 *>(sB + col * KB + (swz_chunk<KB>(col, chunk) << 3));
+        }
     }
 }
 
@@ -468,12 +528,19 @@ __device__ __forceinline__ void decode_tile(int L, const int *prefix, int E, int
 // the first fragments of stage t+1 are read while the last slice of stage t
 // multiplies. The barrier does not wait for vector memory (barrier_keep_loads),
 // so a stage's loads have one full stage of MFMA work to land.
-template <int BM, int BN, int NTH, int EPI, int ACT>
+//
+// B is read k-contiguous (B[e][n][k], the forward weights) or, with BMN,
+// n-contiguous (B[e][k][n], the weights as the backward data products read
+// them). Epilogues: fc1 (bias, optional pre-activation output, activation),
+// fc2 (bias), plain, and the activation gradient (D = acc * act'(aux), aux the
+// saved pre-activation, staged through LDS so that the product is rounded once).
+template <int BM, int BN, int NTH, int EPI, int ACT, bool BMN>
 __global__ __launch_bounds__(NTH, 1) void rows_gemm_big(const bf16_t *__restrict__ A, const bf16_t *__restrict__ B,
                                                       bf16_t *__restrict__ D, int N, int K, int E,
                                                       const int32_t *__restrict__ fill,
                                                       const int32_t *__restrict__ cap,
-                                                      const bf16_t *__restrict__ bias, bf16_t *__restrict__ pre_out) {
+                                                      const bf16_t *__restrict__ bias, bf16_t *__restrict__ pre_out,
+                                                      const bf16_t *__restrict__ aux) {
     extern __shared__ __align__(16) bf16_t lds[];
     constexpr int KB = kBigKB, S = KB / 16;
     // NW wavefronts in 2 rows x NW/2 columns, each owning a (BM/2) x (BN/(NW/2)) block
@@ -500,7 +567,12 @@ __global__ __launch_bounds__(NTH, 1) void rows_gemm_big(const bf16_t *__restrict
         const int cols_valid = min(BN, N - col0);
         const int64_t grow0 = static_cast<int64_t>(g) * C + row0;
         const bf16_t *Ab = A + grow0 * K;
-        const bf16_t *Bb = B + static_cast<int64_t>(g) * N * K + static_cast<int64_t>(col0) * K;
+        const bf16_t *Bb = BMN ? B + static_cast<int64_t>(g) * K * N + col0
+                               : B + static_cast<int64_t>(g) * N * K + static_cast<int64_t>(col0) * K;
+        auto load_b = [&](int k0, bf16_t *dst) {
+            if constexpr (BMN) dma_tile_mn<BN, KB, NW>(Bb, N, cols_valid, k0, dst, wave, lane);
+            else dma_tile<BN, KB, NW>(Bb, K, cols_valid, k0, dst, wave, lane);
+        };
 
         f32x16 acc[TM][TN];
 #pragma unroll
@@ -523,23 +595,23 @@ __global__ __launch_bounds__(NTH, 1) void rows_gemm_big(const bf16_t *__restrict
                                              0, 0);
         }
         dma_tile<BM, KB, NW>(Ab, K, rows_valid, 0, lds, wave, lane);
-        dma_tile<BN, KB, NW>(Bb, K, cols_valid, 0, lds + BM * KB, wave, lane);
+        load_b(0, lds + BM * KB);
         if (nk > 1) {
             dma_tile<BM, KB, NW>(Ab, K, rows_valid, KB, lds + STAGE, wave, lane);
-            dma_tile<BN, KB, NW>(Bb, K, cols_valid, KB, lds + STAGE + BM * KB, wave, lane);
+            load_b(KB, lds + STAGE + BM * KB);
             wait_vmcnt<LPS>();
         } else {
             wait_vmcnt<0>();
         }
         barrier_keep_loads();
         bf16x8 fa[2][TM], fb[2][TN];
-        frag_load<TM, TN, KB>(lds, lds + BM * KB, 0, fa[0], fb[0], wr0, wc0, lane);
+        frag_load<TM, TN, KB, BMN, BN>(lds, lds + BM * KB, 0, fa[0], fb[0], wr0, wc0, lane);
         for (int t = 0; t < nk; ++t) {
             const bf16_t *scur = lds + (t & 1) * STAGE;
 #pragma unroll
             for (int kk = 0; kk < S - 1; ++kk) {
-                frag_load<TM, TN, KB>(scur, scur + BM * KB, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1], wr0, wc0,
-                                      lane);
+                frag_load<TM, TN, KB, BMN, BN>(scur, scur + BM * KB, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1],
+                                               wr0, wc0, lane);
                 mfma_slice<TM, TN>(fa[kk & 1], fb[kk & 1], acc);
                 slice_schedule<TM, TN>();
             }
@@ -550,10 +622,10 @@ __global__ __launch_bounds__(NTH, 1) void rows_gemm_big(const bf16_t *__restrict
             if (t + 2 < nk) {
                 bf16_t *sn = lds + (t & 1) * STAGE;
                 dma_tile<BM, KB, NW>(Ab, K, rows_valid, (t + 2) * KB, sn, wave, lane);
-                dma_tile<BN, KB, NW>(Bb, K, cols_valid, (t + 2) * KB, sn + BM * KB, wave, lane);
+                load_b((t + 2) * KB, sn + BM * KB);
             }
             const bf16_t *snext = lds + ((t + 1) & 1) * STAGE;
-            frag_load<TM, TN, KB>(snext, snext + BM * KB, 0, fa[S & 1], fb[S & 1], wr0, wc0, lane);
+            frag_load<TM, TN, KB, BMN, BN>(snext, snext + BM * KB, 0, fa[S & 1], fb[S & 1], wr0, wc0, lane);
             mfma_slice<TM, TN>(fa[(S - 1) & 1], fb[(S - 1) & 1], acc);
             slice_schedule<TM, TN>();
         }
@@ -566,6 +638,23 @@ __global__ __launch_bounds__(NTH, 1) void rows_gemm_big(const bf16_t *__restrict
         // chunks of contiguous rows (full cache lines), not 32 rows x 16 bytes.
         // fc1 with a pre-activation output makes two passes (pre, then h).
         barrier_keep_loads_lds();  // every wavefront is done with the ring
+        if constexpr (EPI == EPI_DACT) {
+            // the tile's saved pre-activations, in the epilogue tile's layout
+            constexpr int CH = BN / 8, RPI = 64 / CH;
+            static_assert(BM % (NW * RPI) == 0, "pre-activation tile rows must split over the wavefronts");
+#pragma unroll
+            for (int j = 0; j < BM / (NW * RPI); ++j) {
+                const int rb = (j * NW + wave) * RPI;
+                const int r = rb + lane / CH;
+                const int c = min(epi_swz<CH>(r, lane % CH), cols_valid / 8 - 1);  // chunk stored at this slot
+                const int rr = min(r, rows_valid - 1);
+                const uint32_t off = static_cast<uint32_t>(rr * N + c * 8);
+                __builtin_amdgcn_global_load_lds(aux + grow0 * N + col0 + off, (lds_void_t *)(lds + rb * BN), 16, 0,
+                                                 0);
+            }
+            wait_vmcnt<0>();
+            barrier_keep_loads();
+        }
         constexpr int NPASS = EPI == EPI_FC1 ? 2 : 1;
 #pragma unroll
         for (int pass = 0; pass < NPASS; ++pass) {
@@ -596,15 +685,26 @@ __global__ __launch_bounds__(NTH, 1) void rows_gemm_big(const bf16_t *__restrict
                             hi[0] = act_fast<ACT>(hi[0]);
                             hi[1] = act_fast<ACT>(hi[1]);
                         }
+                        const int c = tcol >> 3;
+                        uint2 *slot = reinterpret_cast<uint2 *>(lds + trow * BN + (epi_swz<BN / 8>(trow, c) << 3) +
+                                                                ((lane >> 5) << 2));
+                        if constexpr (EPI == EPI_DACT) {
+                            const uint2 p = *slot;  // the pre-activations of these four outputs
+                            lo[0] *= act_grad_fast<ACT>(__uint_as_float(p.x << 16));
+                            lo[1] *= act_grad_fast<ACT>(__uint_as_float(p.x & 0xFFFF0000u));
+                            hi[0] *= act_grad_fast<ACT>(__uint_as_float(p.y << 16));
+                            hi[1] *= act_grad_fast<ACT>(__uint_as_float(p.y & 0xFFFF0000u));
+                        }
                         const bf16x2 plo = __builtin_convertvector(lo, bf16x2);
                         const bf16x2 phi = __builtin_convertvector(hi, bf16x2);
                         uint2 w;
                         w.x = *reinterpret_cast<const uint32_t *>(&plo);
                         w.y = *reinterpret_cast<const uint32_t *>(&phi);
-                        const int c = tcol >> 3;
-                        *reinterpret_cast<uint2 *>(lds + trow * BN + (epi_swz<BN / 8>(trow, c) << 3) +
-                                                   ((lane >> 5) << 2)) = w;
+                        *slot = w;
                     }
+                    // one 32 x 32 block at a time: keeps the activation math of
+                    // different blocks from being interleaved (register pressure)
+                    __builtin_amdgcn_sched_barrier(0);
                 }
             }
             barrier_keep_loads_lds();
@@ -620,6 +720,187 @@ __global__ __launch_bounds__(NTH, 1) void rows_gemm_big(const bf16_t *__restrict
         }
         // The next tile's barrier (below the loop head) orders these LDS reads
         // before its loads refill the ring; the global stores drain meanwhile.
+    }
+    wait_vmcnt<0>();  // no direct-to-LDS write may land after the workgroup's LDS is released
+}
+
+// ------------------------------------------------------------------ weight gradients, large tiles
+
+// D[e][p][q] = sum over the filled rows r < fill[e] of X[e*C + r][p] * Y[e*C + r][q]
+// (fp32), and with colsum also colsum[e][p] = sum_r X[e*C + r][p]: the weight
+// and bias gradients of one expert layer (X = the layer's output gradient, Y =
+// its input). Both operands are read n-contiguous, so their tiles land in LDS
+// as [64 rows][BM or BN] in the transposed swizzle and every MFMA operand comes
+// from transposing reads. Loads are raw-buffer direct loads whose range ends at
+// the expert's last filled row: rows past it read as zero, so the last, partial
+// K step needs no masking. Same ping-pong K loop as the row-grouped kernel;
+// persistent workgroups over the E * ceil(P/BM) * ceil(Q/BN) tiles, in
+// XCD-contiguous ranges. The bias gradient is summed from the X fragments of
+// the first column tile.
+template <int BN, int KB, int NW>
+__device__ __forceinline__ void buf_tile_mn(__amdgpu_buffer_rsrc_t rs, int ld, int cols_valid, int k0, bf16_t *lds,
+                                            int wave, int lane) {
+    constexpr int CPR = BN / 8;   // chunks per k row
+    constexpr int RPI = 64 / CPR; // k rows per wavefront instruction
+    static_assert(CPR >= 16 && KB % (NW * RPI) == 0, "n-contiguous tile shape");
+#pragma unroll
+    for (int j = 0; j < KB / (NW * RPI); ++j) {
+        const int rb = (j * NW + wave) * RPI;
+        const int row = rb + lane / CPR;
+        const int c = min((lane % CPR) ^ (4 * (row & 3)), cols_valid / 8 - 1);  // chunk stored at this slot
+        const int voff = ((k0 + row) * ld + c * 8) * 2;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t *)(lds + rb * BN), 16, voff, 0, 0, 0);
+    }
+}
+
+// Raw buffer over [base, base + bytes): loads past the end return zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const bf16_t *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t *>(base), 0, static_cast<int>(bytes), 0x00020000);
+}
+
+template <int BM, int BN, int NTH>
+__global__ __launch_bounds__(NTH, 1) void kgrad_gemm_big(const bf16_t *__restrict__ X, const bf16_t *__restrict__ Y,
+                                                       float *__restrict__ D, int P, int Q, int E,
+                                                       const int32_t *__restrict__ fill,
+                                                       const int32_t *__restrict__ cap,
+                                                       float *__restrict__ colsum) {
+    extern __shared__ __align__(16) bf16_t lds[];
+    constexpr int KB = kBigKB, S = KB / 16;
+    constexpr int NW = NTH / 64, WGC = NW / 2;
+    constexpr int TM = BM / 64, TN = BN / (32 * WGC);
+    static_assert(TN >= 1 && BN % (32 * WGC) == 0, "wavefront columns must be whole 32-wide blocks");
+    constexpr int STAGE = (BM + BN) * KB;
+    const int tp = (P + BM - 1) / BM, tq = (Q + BN - 1) / BN;
+    const int per_e = tp * tq;
+    const int T = E * per_e;
+    const int x = blockIdx.x % kXcds, nb = gridDim.x / kXcds;
+    const int per = (T + kXcds - 1) / kXcds;
+    const int start = min(T, x * per), end = min(T, start + per);
+    const int C = *cap;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wr0 = (wave / WGC) * (BM / 2), wc0 = (wave % WGC) * (BN / WGC);
+    for (int L = start + static_cast<int>(blockIdx.x) / kXcds; L < end; L += nb) {
+        const int e = L / per_e, u = L - e * per_e;
+        const int grp = u / (kGroupM * tq);
+        const int gm = min(kGroupM, tp - grp * kGroupM);
+        const int within = u - grp * kGroupM * tq;
+        const int pt = grp * kGroupM + within % gm, qt = within / gm;
+        const int p0 = pt * BM, q0 = qt * BN;
+        const int pv = min(BM, P - p0), qv = min(BN, Q - q0);
+        const int rows = fill[e];
+        const int nk = (rows + KB - 1) / KB;
+        const int64_t r0 = static_cast<int64_t>(e) * C;
+        const __amdgpu_buffer_rsrc_t rx = raw_rsrc(X + r0 * P + p0, static_cast<uint32_t>((rows * P - p0) * 2));
+        const __amdgpu_buffer_rsrc_t ry = raw_rsrc(Y + r0 * Q + q0, static_cast<uint32_t>((rows * Q - q0) * 2));
+        const bool col_sums = colsum != nullptr && qt == 0 && (wave % WGC) == 0;
+
+        f32x16 acc[TM][TN];
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+        float csum[TM];
+#pragma unroll
+        for (int i = 0; i < TM; ++i) csum[i] = 0.f;
+
+        barrier_keep_loads_lds();  // the previous tile's LDS reads are complete in every wavefront
+        if (nk > 0) {
+            buf_tile_mn<BM, KB, NW>(rx, P, pv, 0, lds, wave, lane);
+            buf_tile_mn<BN, KB, NW>(ry, Q, qv, 0, lds + BM * KB, wave, lane);
+            if (nk > 1) {
+                buf_tile_mn<BM, KB, NW>(rx, P, pv, KB, lds + STAGE, wave, lane);
+                buf_tile_mn<BN, KB, NW>(ry, Q, qv, KB, lds + STAGE + BM * KB, wave, lane);
+                wait_vmcnt<(BM + BN) * KB / 8 / NTH>();
+            } else {
+                wait_vmcnt<0>();
+            }
+            barrier_keep_loads();
+            bf16x8 fx[2][TM], fy[2][TN];
+            frag_b_mn<TM, BM>(lds, 0, fx[0], wr0, lane);
+            frag_b_mn<TN, BN>(lds + BM * KB, 0, fy[0], wc0, lane);
+            auto colsum_add = [&](const bf16x8 (&f)[TM]) {
+                if (!col_sums) return;
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+#pragma unroll
+                    for (int v = 0; v < 8; ++v) csum[i] += static_cast<float>(f[i][v]);
+            };
+            for (int t = 0; t < nk; ++t) {
+                const bf16_t *scur = lds + (t & 1) * STAGE;
+#pragma unroll
+                for (int kk = 0; kk < S - 1; ++kk) {
+                    const int nx = (kk + 1) & 1;
+                    frag_b_mn<TM, BM>(scur, kk + 1, fx[nx], wr0, lane);
+                    frag_b_mn<TN, BN>(scur + BM * KB, kk + 1, fy[nx], wc0, lane);
+                    mfma_slice<TM, TN>(fx[kk & 1], fy[kk & 1], acc);
+                    slice_schedule<TM, TN>();
+                    colsum_add(fx[kk & 1]);
+                }
+                wait_vmcnt<0>();  // this wavefront's loads of stage t+1 have landed
+                barrier_keep_loads_lds();
+                if (t + 2 < nk) {
+                    bf16_t *sn = lds + (t & 1) * STAGE;
+                    buf_tile_mn<BM, KB, NW>(rx, P, pv, (t + 2) * KB, sn, wave, lane);
+                    buf_tile_mn<BN, KB, NW>(ry, Q, qv, (t + 2) * KB, sn + BM * KB, wave, lane);
+                }
+                const bf16_t *snext = lds + ((t + 1) & 1) * STAGE;
+                frag_b_mn<TM, BM>(snext, 0, fx[S & 1], wr0, lane);
+                frag_b_mn<TN, BN>(snext + BM * KB, 0, fy[S & 1], wc0, lane);
+                mfma_slice<TM, TN>(fx[(S - 1) & 1], fy[(S - 1) & 1], acc);
+                slice_schedule<TM, TN>();
+                colsum_add(fx[(S - 1) & 1]);
+            }
+        }
+        // Output through LDS, in two halves of BM/2 rows (the fp32 tile is twice
+        // the ring): the wavefronts owning the half write their accumulators as
+        // a row-major [BM/2][BN] fp32 tile, 16-byte chunk c of row r at slot
+        // c ^ (r mod CH), and every thread then stores whole rows. Lane l holds,
+        // per 32 x 32 block, p = wr0 + 32 i + (l mod 32) and q = wc0 + 32 j +
+        // 8 q' + 4 (l / 32) .. +3 (one chunk).
+        float *De = D + static_cast<int64_t>(e) * P * Q;
+        float *tile = reinterpret_cast<float *>(lds);
+        constexpr int CH = BN / 4;  // 16-byte chunks per fp32 row
+        static_assert((BM / 2) * BN * 4 <= 2 * STAGE * 2, "half the fp32 tile must fit in the ring");
+        static_assert((BM / 2) * CH % NTH == 0, "output chunks must split evenly over the threads");
+        barrier_keep_loads_lds();  // every wavefront is done with the ring
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            if (wr0 / (BM / 2) == half) {
+#pragma unroll
+                for (int i = 0; i < TM; ++i) {
+                    const int r = wr0 - half * (BM / 2) + i * 32 + (lane & 31);
+#pragma unroll
+                    for (int j = 0; j < TN; ++j)
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const int c = (wc0 + j * 32 + 8 * q + 4 * (lane >> 5)) >> 2;
+                            *reinterpret_cast<float4 *>(tile + r * BN + ((c ^ (r & (CH - 1))) << 2)) =
+                                make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                                            acc[i][j][4 * q + 3]);
+                        }
+                }
+            }
+            barrier_keep_loads_lds();
+#pragma unroll 4
+            for (int u = 0; u < (BM / 2) * CH / NTH; ++u) {
+                const int idx = tid + u * NTH, r = idx / CH, c = idx % CH;
+                const float4 v = *reinterpret_cast<const float4 *>(tile + r * BN + ((c ^ (r & (CH - 1))) << 2));
+                const int p = half * (BM / 2) + r;
+                if (p < pv && c * 4 < qv)
+                    *reinterpret_cast<float4 *>(De + static_cast<int64_t>(p0 + p) * Q + q0 + c * 4) = v;
+            }
+            if (half == 0) barrier_keep_loads_lds();  // read before the second half overwrites it
+        }
+        if (col_sums) {
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+                const float v = csum[i] + __shfl_down(csum[i], 32, 64);  // k 0-7 and 8-15 of each slice
+                const int p = wr0 + i * 32 + lane;
+                if (lane < 32 && p < pv) colsum[static_cast<int64_t>(e) * P + p0 + p] = v;
+            }
+        }
     }
     wait_vmcnt<0>();  // no direct-to-LDS write may land after the workgroup's LDS is released
 }
@@ -810,9 +1091,10 @@ static int resident_blocks(int per_cu) {
     return ((cus[dev] * per_cu + kXcds - 1) / kXcds) * kXcds;
 }
 
-template <int BM, int BN, int NTH, int EPI>
+template <int BM, int BN, int NTH, int EPI, bool BMN = false>
 hipError_t big_launch(int act, const void *A, const void *B, void *D, int N, int K, int E, const int32_t *fill,
-                      const int32_t *cap, const void *bias, void *pre_out, hipStream_t st) {
+                      const int32_t *cap, const void *bias, void *pre_out, hipStream_t st,
+                      const void *aux = nullptr) {
     constexpr int lds = big_lds_bytes<BM, BN>();
     constexpr int per_cu = (160 * 1024) / lds >= 2 ? 2 : 1;
     const dim3 grid(resident_blocks(per_cu));
@@ -821,18 +1103,19 @@ hipError_t big_launch(int act, const void *A, const void *B, void *D, int N, int
     auto d = static_cast<bf16_t *>(D);
     auto bi = static_cast<const bf16_t *>(bias);
     auto po = static_cast<bf16_t *>(pre_out);
+    auto ax = static_cast<const bf16_t *>(aux);
     if (act == MOE_ACT_GELU) {
-        auto k = rows_gemm_big<BM, BN, NTH, EPI, MOE_ACT_GELU>;
+        auto k = rows_gemm_big<BM, BN, NTH, EPI, MOE_ACT_GELU, BMN>;
         static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(k),
                                                            hipFuncAttributeMaxDynamicSharedMemorySize, lds);
         if (attr != hipSuccess) return attr;
-        hipLaunchKernelGGL(k, grid, dim3(NTH), lds, st, a, b, d, N, K, E, fill, cap, bi, po);
+        hipLaunchKernelGGL(k, grid, dim3(NTH), lds, st, a, b, d, N, K, E, fill, cap, bi, po, ax);
     } else {
-        auto k = rows_gemm_big<BM, BN, NTH, EPI, MOE_ACT_RELU>;
+        auto k = rows_gemm_big<BM, BN, NTH, EPI, MOE_ACT_RELU, BMN>;
         static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(k),
                                                            hipFuncAttributeMaxDynamicSharedMemorySize, lds);
         if (attr != hipSuccess) return attr;
-        hipLaunchKernelGGL(k, grid, dim3(NTH), lds, st, a, b, d, N, K, E, fill, cap, bi, po);
+        hipLaunchKernelGGL(k, grid, dim3(NTH), lds, st, a, b, d, N, K, E, fill, cap, bi, po, ax);
     }
     return hipGetLastError();
 }
@@ -852,6 +1135,20 @@ static int gemm_cfg_override() {
     return v;
 }
 
+// Backward data products, weights read n-contiguous: same tile choice as the
+// forward products.
+template <int EPI>
+hipError_t bwd_data_launch(int act, const void *A, const void *B, void *D, int N, int K, int E, const int32_t *fill,
+                           const int32_t *cap, const void *aux, hipStream_t st) {
+    int cfg = gemm_cfg_override();
+    if (cfg < 1 || cfg > 3) cfg = K <= 1024 ? 3 : 1;
+    switch (cfg) {
+    case 1: return big_launch<256, 256, 512, EPI, true>(act, A, B, D, N, K, E, fill, cap, nullptr, nullptr, st, aux);
+    case 2: return big_launch<256, 128, 256, EPI, true>(act, A, B, D, N, K, E, fill, cap, nullptr, nullptr, st, aux);
+    default: return big_launch<128, 128, 256, EPI, true>(act, A, B, D, N, K, E, fill, cap, nullptr, nullptr, st, aux);
+    }
+}
+
 template <int EPI>
 hipError_t fwd_launch(int act, const void *A, const void *B, void *D, int N, int K, int cmax, int E,
                       const int32_t *fill, const int32_t *cap, const void *bias, void *pre_out, hipStream_t st) {
@@ -865,8 +1162,22 @@ hipError_t fwd_launch(int act, const void *A, const void *B, void *D, int N, int
     }
 }
 
+// Weight gradients: the large-tile kernel when one expert's rows of either
+// operand span less than 2 GiB (its raw-buffer offsets are 32-bit), else the
+// register-staged kernel below.
 hipError_t kgroup_launch(const void *A, const void *B, float *D, int Mo, int No, int E, const int32_t *fill,
-                         const int32_t *cap, float *colsum, hipStream_t st) {
+                         const int32_t *cap, float *colsum, int32_t cmax, hipStream_t st) {
+    // the last K step reads up to 63 rows past the expert's fill (they read as zero)
+    if (static_cast<int64_t>(cmax + 64) * std::max(Mo, No) * 2 < (int64_t(1) << 31)) {
+        constexpr int lds = 2 * (256 + 256) * kBigKB * 2;
+        auto k = kgrad_gemm_big<256, 256, 512>;
+        static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(k),
+                                                           hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+        if (attr != hipSuccess) return attr;
+        hipLaunchKernelGGL(k, dim3(resident_blocks(1)), dim3(512), lds, st, static_cast<const bf16_t *>(A),
+                           static_cast<const bf16_t *>(B), D, Mo, No, E, fill, cap, colsum);
+        return hipGetLastError();
+    }
     const dim3 grid((No + BN - 1) / BN, (Mo + BM - 1) / BM, E);
     hipLaunchKernelGGL(kgroup_gemm_bf16, grid, dim3(NT), 0, st, static_cast<const bf16_t *>(A),
                        static_cast<const bf16_t *>(B), D, Mo, No, fill, cap, colsum);
@@ -911,17 +1222,15 @@ hipError_t launch_expert_ffn_bwd(const moe_shape &s, const void *buf, const void
     hipError_t err;
     if (s.dtype == MOE_DT_BF16) {
         // dpre = (dy . W2[e]) * act'(pre): A = dy [rows][M], B = W2[e] read as [K=M][N=H]
-        if ((err = rows_launch<false, EPI_DACT>(s.act, dy, W2, dpre, H, M, cmax, E, fill, cap, nullptr, pre, nullptr,
-                                                st)) != hipSuccess)
+        if ((err = bwd_data_launch<EPI_DACT>(s.act, dy, W2, dpre, H, M, E, fill, cap, pre, st)) != hipSuccess)
             return err;
         // dW2[e] = dy^T h (+ db2 = column sums of dy)
-        if ((err = kgroup_launch(dy, h, dW2, M, H, E, fill, cap, db2, st)) != hipSuccess) return err;
+        if ((err = kgroup_launch(dy, h, dW2, M, H, E, fill, cap, db2, cmax, st)) != hipSuccess) return err;
         // dbuf = dpre . W1[e]: B = W1[e] read as [K=H][N=M]   (dbuf may alias dy: dy is consumed above)
-        if ((err = rows_launch<false, EPI_PLAIN>(s.act, dpre, W1, dbuf, M, H, cmax, E, fill, cap, nullptr, nullptr,
-                                                 nullptr, st)) != hipSuccess)
+        if ((err = bwd_data_launch<EPI_PLAIN>(s.act, dpre, W1, dbuf, M, H, E, fill, cap, nullptr, st)) != hipSuccess)
             return err;
         // dW1[e] = dpre^T buf (+ db1 = column sums of dpre)
-        return kgroup_launch(dpre, buf, dW1, H, M, E, fill, cap, db1, st);
+        return kgroup_launch(dpre, buf, dW1, H, M, E, fill, cap, db1, cmax, st);
     }
     SimtArgs a{};  // dpre = (dy . W2) * act'(pre); B(n=h, kk=m) = W2[e][m][h]
     a.A = static_cast<const float *>(dy); a.a_si = M; a.a_sk = 1; a.a_gfix = 0; a.a_gcap = M;

@@ -47,7 +47,8 @@ __device__ __forceinline__ float gelu_grad_f(float v) {
 // 7.1.26: erf(x) = 1 - t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) exp(-x^2),
 // t = 1 / (1 + p x) for x >= 0, odd extension; absolute error <= 1.5e-7.
 // Used by the GEMM epilogue, where it costs about half the instructions of erff.
-__device__ __forceinline__ float erf_as(float x) {
+// *ex receives exp(-x^2), which the formula computes anyway.
+__device__ __forceinline__ float erf_as(float x, float *ex = nullptr) {
     const float ax = fabsf(x);
     const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, ax, 1.0f));
     float y = fmaf(1.061405429f, t, -1.453152027f);
@@ -55,17 +56,32 @@ __device__ __forceinline__ float erf_as(float x) {
     y = fmaf(y, t, -0.284496736f);
     y = fmaf(y, t, 0.254829592f);
     y *= t;
-    const float r = 1.0f - y * __expf(-ax * ax);
+    const float e = __expf(-ax * ax);
+    if (ex != nullptr) *ex = e;
+    const float r = 1.0f - y * e;
     return copysignf(r, x);
 }
 __device__ __forceinline__ float gelu_fast(float v) {
     return 0.5f * v * (1.0f + erf_as(v * 0.70710678118654752f));
+}
+// d/dv of 0.5 v (1 + erf(v / sqrt 2)) = Phi(v) + v phi(v), phi(v) = exp(-v^2/2) / sqrt(2 pi);
+// exp(-v^2/2) is the exp(-x^2) of erf_as at x = v / sqrt 2.
+__device__ __forceinline__ float gelu_grad_fast(float v) {
+    float e;
+    const float erf = erf_as(v * 0.70710678118654752f, &e);
+    return fmaf(v * 0.39894228040143268f, e, 0.5f * (1.0f + erf));
 }
 
 template <int ACT>
 __device__ __forceinline__ float act_fast(float v) {
     if constexpr (ACT == MOE_ACT_RELU) return v > 0.f ? v : 0.f;
     else return gelu_fast(v);
+}
+
+template <int ACT>
+__device__ __forceinline__ float act_grad_fast(float v) {
+    if constexpr (ACT == MOE_ACT_RELU) return v > 0.f ? 1.f : 0.f;
+    else return gelu_grad_fast(v);
 }
 
 template <int ACT>

@@ -260,6 +260,10 @@ BWD = [
                backward=True),
     W.Workload("bwd_f32_relu_S130_E3_k3", S=130, M=64, E=3, k=3, H=64, capacity_factor=0.0, dtype=W.DT_F32,
                act=W.ACT_RELU, backward=True),
+    # K > 1024 in both backward data products (the large-tile configuration,
+    # weights read n-contiguous), ragged row tiles, partial last column tiles
+    W.Workload("bwd_bigtile_S300_M1088_E4_k2_H1152", S=300, M=1088, E=4, k=2, H=1152, capacity_factor=1.0,
+               backward=True),
 ]
 
 
