@@ -39,8 +39,10 @@ def log(*a):
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    # a step of the default workload is ~0.25 ms: 1000 timed steps keep the GPU at
+    # its steady clocks for about a quarter second (20 steps measured the ramp)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="gated_bf16_S4096_M1024_E8_k2_H4096",
                     help="workload name (see workloads.py); default: the S=4096 gate-projected bf16 layer")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -177,32 +179,61 @@ def main():
     lg = bufs["logits"] if gate else logits_in
     b = bufs
 
-    def stage(name, fn):
+    # Each stage is timed over a batch of back-to-back launches between two events.
+    # bf16 matmuls enqueued ahead of the first event keep the GPU busy while the
+    # host enqueues the batch, so the events bracket kernel time, not host gaps.
+    # Every stage is idempotent (same inputs, same outputs).
+    fa = torch.randn(4096, 4096, device="cuda", dtype=torch.bfloat16)
+    fb = torch.randn(4096, 4096, device="cuda", dtype=torch.bfloat16)
+    torch.mm(fa, fb)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    for _ in range(4):
+        torch.mm(fa, fb)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    filler_ms = max(c0.elapsed_time(c1) / 4, 1e-3)
+
+    def stage_batch(name, fn, reps):
+        t0 = time.perf_counter()
+        fn()
+        torch.cuda.synchronize()
+        host_ms = (time.perf_counter() - t0) * 1e3  # bounds one call's host time
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
+        for _ in range(min(200, int((2.0 * host_ms * reps + 0.5) / filler_ms) + 1)):
+            torch.mm(fa, fb)
         e0.record(stream)
-        fn()
+        for _ in range(reps):
+            fn()
         e1.record(stream)
-        ev[name].append((e0, e1))
+        ev[name].append((e0, e1, reps))
 
-    for it in range(args.warmup + args.steps):
-        timed = it >= args.warmup
-        run = stage if timed else (lambda n, f: f())
-        if gate:
-            run("gate", lambda: moe.moe_gate_project(s, x, Wg, lg))
-        run("route", lambda: moe.moe_route(s, lg, b["idx"], b["loc"], b["gates"], b["needed"], b["fill"],
-                                           b["capacity"], b["slot_route"], b["ws"]))
-        run("encode", lambda: moe.moe_encode(s, x, b["idx"], b["loc"], b["fill"], b["capacity"], b["buf"]))
-        run("fc1", lambda: moe.moe_expert_fc1(s, b["buf"], W1, b1, b["fill"], b["capacity"], b["pre"], b["h"]))
-        run("fc2", lambda: moe.moe_expert_fc2(s, b["h"], W2, b2, b["fill"], b["capacity"], b["y"]))
-        run("decode", lambda: moe.moe_decode(s, b["y"], b["gates"], b["idx"], b["loc"], b["capacity"], b["out"]))
-        if w.backward:
-            run("backward", lambda: moe.layer_backward(s, b, inp["dout"], W1, W2, grads=grads))
+    stage_fns = []
+    if gate:
+        stage_fns.append(("gate", lambda: moe.moe_gate_project(s, x, Wg, lg)))
+    stage_fns += [
+        ("route", lambda: moe.moe_route(s, lg, b["idx"], b["loc"], b["gates"], b["needed"], b["fill"],
+                                        b["capacity"], b["slot_route"], b["ws"])),
+        ("encode", lambda: moe.moe_encode(s, x, b["idx"], b["loc"], b["fill"], b["capacity"], b["buf"])),
+        ("fc1", lambda: moe.moe_expert_fc1(s, b["buf"], W1, b1, b["fill"], b["capacity"], b["pre"], b["h"])),
+        ("fc2", lambda: moe.moe_expert_fc2(s, b["h"], W2, b2, b["fill"], b["capacity"], b["y"])),
+        ("decode", lambda: moe.moe_decode(s, b["y"], b["gates"], b["idx"], b["loc"], b["capacity"], b["out"])),
+    ]
+    if w.backward:
+        stage_fns.append(("backward", lambda: moe.layer_backward(s, b, inp["dout"], W1, W2, grads=grads)))
+    reps = max(1, min(50, args.steps))
+    rounds = max(1, min(10, args.steps // reps))
+    for rd in range(rounds):
+        for name, fn in stage_fns:
+            stage_batch(name, fn, reps)
+        torch.cuda.synchronize()
+        log(f"[bench] stage timing round {rd + 1}/{rounds} done ({reps} launches per stage)")
     torch.cuda.synchronize()
     alg = algorithmic(w, C, kept)
     stages = {}
     for n in names:
-        ms = sum(e0.elapsed_time(e1) for e0, e1 in ev[n]) / len(ev[n])
+        ms = sum(e0.elapsed_time(e1) for e0, e1, r in ev[n]) / sum(r for _, _, r in ev[n])
         kind, amount = alg[n]
         r = roofline_of(kind, amount, ms, w.dtype == W.DT_BF16)
         r["ms"] = round(ms, 5)
