@@ -20,6 +20,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import re
 import sys
 import time
 
@@ -47,7 +48,53 @@ def parse():
                     help="workload name (see workloads.py); default: the S=4096 gate-projected bf16 layer")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle FFN sample")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run 3 plain device copies of MIB MiB each (the reference kernel that scales the "
+                         "FETCH_SIZE / WRITE_SIZE counters) and exit")
     return ap.parse_args()
+
+
+# HBM traffic of the dominant kernel comes from two counter runs (FETCH_SIZE, then
+# WRITE_SIZE) recorded in profiles/traffic_<stage>_<workload>.md together with the
+# sha256 of the kernel sources they were taken on; it is reported only while those
+# sources are unchanged.
+TRAFFIC_SOURCES = ("combine_softmax_top_amd/csrc/gemm.hip", "combine_softmax_top_amd/csrc/moe_internal.h")
+
+
+def sources_sha256():
+    import hashlib
+    h = hashlib.sha256()
+    for rel in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(stage, workload):
+    """Bytes per launch from the committed counter summary, or None if absent or stale."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{stage}_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            m = re.match(r"^- ([a-z_0-9]+): `?([^`\s]+)`?", line.strip())
+            if m:
+                fields[m.group(1)] = m.group(2)
+    if fields.get("sources_sha256") != sources_sha256() or "traffic_bytes_per_launch" not in fields:
+        return None
+    return int(fields["traffic_bytes_per_launch"])
+
+
+def copy_calibration(mib):
+    import torch
+    a = torch.ones(mib * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps(dict(copy_bytes_read=a.numel() * 4, copy_bytes_written=a.numel() * 4, launches=3)))
 
 
 def algorithmic(w, C, kept):
@@ -134,6 +181,9 @@ def main():
         print(f"bench.py measures one GPU's share of the layer: --gpus {args.gpus} is not supported "
               "(this build has no multi-GPU path; run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     import torch
     import combine_softmax_top_amd as moe
     import workloads as W
@@ -243,7 +293,7 @@ def main():
     dominant = max((n for n in names if n != "backward"), key=lambda n: stages[n]["ms"])
     d = stages[dominant]
     roofline = dict(kernel=dominant, bound=d["bound"], achieved=d["achieved"], peak=d["peak"], unit=d["unit"],
-                    frac=d["frac"], traffic=None)
+                    frac=d["frac"], traffic=recorded_traffic(dominant, w.name))
 
     cpu = None
     if not args.no_cpu_baseline:
