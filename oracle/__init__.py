@@ -26,6 +26,7 @@ DT_BF16 = 1
 _c_i32p = np.ctypeslib.ndpointer(dtype=np.int32, flags="C_CONTIGUOUS")
 _c_i64p = np.ctypeslib.ndpointer(dtype=np.int64, flags="C_CONTIGUOUS")
 _c_f32p = np.ctypeslib.ndpointer(dtype=np.float32, flags="C_CONTIGUOUS")
+_c_f64p = np.ctypeslib.ndpointer(dtype=np.float64, flags="C_CONTIGUOUS")
 
 
 def build(force: bool = True) -> str:
@@ -83,8 +84,12 @@ def lib():
         L.oracle_weight_grads.restype = None
         L.oracle_dgates.argtypes = [i32, i32, ctypes.c_int, i64, _c_i32p, vp, vp, _c_f32p]
         L.oracle_dgates.restype = None
-        L.oracle_dx.argtypes = [i32, i32, ctypes.c_int, vp, i64, _c_i64p, vp]
+        L.oracle_dx.argtypes = [i32, i32, ctypes.c_int, vp, i64, _c_i64p, i32, vp, vp, vp]
         L.oracle_dx.restype = None
+        L.oracle_gate_backward.argtypes = [i32, i32, i32, d, _c_f32p, _c_i32p, _c_f32p, vp, _c_f64p, _c_f64p]
+        L.oracle_gate_backward.restype = None
+        L.oracle_gate_weight_grad.argtypes = [i32, i32, i32, ctypes.c_int, vp, _c_f64p, _c_f64p]
+        L.oracle_gate_weight_grad.restype = None
         _lib = L
     return _lib
 
@@ -339,8 +344,9 @@ def dgates(routes: np.ndarray, dout: np.ndarray, yrows: np.ndarray, S: int, dtyp
 
 
 def dx_tokens(routes: np.ndarray, dbufrows: np.ndarray, tokens: Sequence[int], S: int, k: int,
-              dtype: int) -> np.ndarray:
-    """dx of the listed tokens from the dbuf rows of kept routes (routes[i] = r*S + s)."""
+              dtype: int, dlogits: Optional[np.ndarray] = None, Wg: Optional[np.ndarray] = None) -> np.ndarray:
+    """dx of the listed tokens from the dbuf rows of kept routes (routes[i] = r*S + s), plus
+    dlogits[token] . Wg^T when the gate projection's gradient (fp64 dlogits [S,E]) is given."""
     routes = np.asarray(routes, dtype=np.int64)
     tok = np.asarray(tokens, dtype=np.int64)
     pos = {int(t): i for i, t in enumerate(tok)}
@@ -351,14 +357,52 @@ def dx_tokens(routes: np.ndarray, dbufrows: np.ndarray, tokens: Sequence[int], S
             table[t, int(q // S)] = i
     M = dbufrows.shape[1]
     out = np.empty((tok.shape[0], M), elem_dtype(dtype))
+    E, dl, wg = 0, None, None
+    if dlogits is not None:
+        E = dlogits.shape[1]
+        dl = np.ascontiguousarray(np.asarray(dlogits, np.float64)[tok])
+        wg = np.ascontiguousarray(Wg, dtype=np.float32)
+        assert wg.shape == (M, E)
     lib().oracle_dx(M, k, dtype, _ptr(np.ascontiguousarray(dbufrows)), tok.shape[0],
-                    np.ascontiguousarray(table), _ptr(out))
+                    np.ascontiguousarray(table), E, _ptr(dl), _ptr(wg), _ptr(out))
     return out
 
 
-def layer_backward(fw: Dict, inp: Dict, act_kind: int, dtype: int) -> Dict[str, np.ndarray]:
+# ------------------------------------------------------------------ gate backward
+
+def gate_backward(logits: np.ndarray, idx: np.ndarray, dgates: np.ndarray, needed: Optional[np.ndarray],
+                  alpha: float):
+    """dlogits (fp64 [S,E]) through the softmax, and the auxiliary load-balance loss (fp64)."""
+    logits = np.ascontiguousarray(logits, dtype=np.float32)
+    S, E = logits.shape
+    k = idx.shape[0]
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    dgates = np.ascontiguousarray(dgates, dtype=np.float32)
+    assert idx.shape == (k, S) and dgates.shape == (k, S)
+    nd = None if needed is None else np.ascontiguousarray(needed, dtype=np.int32)
+    dl = np.empty((S, E), np.float64)
+    aux = np.zeros((1,), np.float64)
+    lib().oracle_gate_backward(S, E, k, float(alpha), logits, idx, dgates, _ptr(nd), dl, aux)
+    return dl, float(aux[0])
+
+
+def gate_weight_grad(x: np.ndarray, dlogits: np.ndarray, dtype: int) -> np.ndarray:
+    """dWg = x^T . dlogits (fp64 [M,E])."""
+    x = _check(x, dtype)
+    S, M = x.shape
+    dl = np.ascontiguousarray(dlogits, dtype=np.float64)
+    E = dl.shape[1]
+    out = np.empty((M, E), np.float64)
+    lib().oracle_gate_weight_grad(S, M, E, dtype, _ptr(x), dl, out)
+    return out
+
+
+def layer_backward(fw: Dict, inp: Dict, act_kind: int, dtype: int, aux_coef: Optional[float] = None
+                   ) -> Dict[str, np.ndarray]:
     """The whole backward for small shapes: dx, dW1, db1, dW2, db2 (fp32) and dgates [k,S]
-    (0 for dropped routes)."""
+    (0 for dropped routes). With aux_coef given, also the gate backward: dlogits (fp64) and
+    aux_loss from the forward's logits, and, when the logits were projected (inp has Wg),
+    dWg (fp64) and the gate projection's share of dx."""
     rt = fw["route"]
     C = rt["C"]
     k, S = rt["idx"].shape
@@ -376,6 +420,16 @@ def layer_backward(fw: Dict, inp: Dict, act_kind: int, dtype: int) -> Dict[str, 
         start += n
     dg = np.zeros((k * S,), np.float32)
     dg[routes] = dgates(routes, inp["dout"], fw["y"][rows], S, dtype)
-    dx = dx_tokens(routes, dbuf, np.arange(S), S, k, dtype)
-    return dict(dx=dx, dW1=dW1, db1=db1, dW2=dW2, db2=db2, dgates=dg.reshape(k, S),
-                dy=dy, dpre=dpre, dbuf=dbuf, routes=routes)
+    dg = dg.reshape(k, S)
+    out = dict(dW1=dW1, db1=db1, dW2=dW2, db2=db2, dgates=dg, dy=dy, dpre=dpre, dbuf=dbuf, routes=routes)
+    dl = Wg = None
+    if aux_coef is not None:
+        dl, out["aux_loss"] = gate_backward(fw["logits"], rt["idx"], dg, rt["needed"], aux_coef)
+        out["dlogits"] = dl
+        if "Wg" in inp:
+            Wg = inp["Wg"]
+            out["dWg"] = gate_weight_grad(inp["x"], dl, dtype)
+        else:
+            dl = None
+    out["dx"] = dx_tokens(routes, dbuf, np.arange(S), S, k, dtype, dlogits=dl, Wg=Wg)
+    return out

@@ -50,7 +50,19 @@
  *  - backward: dy = g * dout (rounded to the data type), dgate = <dout, y>,
  *    dh = dy . W2[e], dpre = dh * act'(pre) rounded, dbuf = dpre . W1[e]
  *    rounded, dx = sum of dbuf over kept routes rounded; weight and bias
- *    gradients are fp32 sums over the expert's filled rows.
+ *    gradients are fp32 sums over the expert's filled rows;
+ *  - gate backward: the gates are softmax probabilities p of the logits, so
+ *    the gradient reaching p is dgates at each route's expert (all k routes as
+ *    given; the layer passes 0 for dropped ones) plus the gradient of an
+ *    auxiliary load-balance loss. The MoE training blog (part 2 section 2.1,
+ *    training settings) fixes only its coefficient, 0.01; its form here is the
+ *    usual product of routed fraction and mean probability,
+ *      l_aux = alpha * E * sum_e f_e * P_e,  f_e = needed[e] / (k S),
+ *      P_e = (1/S) sum_s p[s][e],
+ *    with the counts f taken as constants (they come from an argmax). Then
+ *    dlogits = p * (g - <p, g>) per token (the softmax Jacobian), dWg = x^T .
+ *    dlogits, and the input gradient dx gains dlogits . Wg^T before its one
+ *    rounding. All of it in fp64.
  */
 #include <math.h>
 #include <stdint.h>
@@ -495,7 +507,8 @@ void oracle_dgates(int32_t S, int32_t M, int dtype, int64_t n, const int32_t *ro
  * t, route_rows[t*k + r] is the dbuf row of its route r, or -1 when that route
  * was dropped. dx is [ntok, M]. */
 void oracle_dx(int32_t M, int32_t k, int dtype, const void *dbufrows, int64_t ntok,
-               const int64_t *route_rows, void *dx) {
+               const int64_t *route_rows, int32_t E, const double *dlog_rows, const float *Wg,
+               void *dx) {
     for (int64_t t = 0; t < ntok; ++t)
         for (int32_t m = 0; m < M; ++m) {
             double acc = 0.0;
@@ -503,6 +516,56 @@ void oracle_dx(int32_t M, int32_t k, int dtype, const void *dbufrows, int64_t nt
                 const int64_t i = route_rows[t * k + r];
                 if (i >= 0) acc += load_elem(dbufrows, dtype, i * M + m);
             }
+            if (dlog_rows != NULL) /* the gate projection's share: dlogits[t] . Wg[m]^T */
+                for (int32_t e = 0; e < E; ++e) acc += dlog_rows[t * E + e] * (double)Wg[(int64_t)m * E + e];
             store_elem(dx, dtype, t * M + m, acc);
+        }
+}
+
+/* ------------------------------------------------------------------ gate backward */
+
+/* Gradient of the logits (fp64, [S,E]) and the auxiliary loss (reading in the
+ * header): p = softmax(logits[s]) in fp64; g[e] = sum of dgates[r][s] over the
+ * routes r with idx[r][s] == e, plus alpha * E * f_e / S when needed is given
+ * (needed == NULL: no auxiliary term, aux_loss = 0); dlogits[s][e] =
+ * p[e] * (g[e] - sum_j p[j] g[j]). */
+void oracle_gate_backward(int32_t S, int32_t E, int32_t k, double alpha, const float *logits,
+                          const int32_t *idx, const float *dgates, const int32_t *needed,
+                          double *dlogits, double *aux_loss) {
+    double *p = (double *)malloc(sizeof(double) * (size_t)E);
+    double *g = (double *)malloc(sizeof(double) * (size_t)E);
+    double *colsum = (double *)calloc((size_t)E, sizeof(double));
+    for (int64_t s = 0; s < S; ++s) {
+        const float *l = logits + s * E;
+        double mx = -INFINITY, sum = 0.0;
+        for (int32_t e = 0; e < E; ++e)
+            if ((double)l[e] > mx) mx = (double)l[e];
+        for (int32_t e = 0; e < E; ++e) { p[e] = exp((double)l[e] - mx); sum += p[e]; }
+        for (int32_t e = 0; e < E; ++e) p[e] /= sum;
+        for (int32_t e = 0; e < E; ++e) {
+            g[e] = needed ? alpha * (double)E * ((double)needed[e] / ((double)k * (double)S)) / (double)S : 0.0;
+            colsum[e] += p[e];
+        }
+        for (int32_t r = 0; r < k; ++r) g[idx[(int64_t)r * S + s]] += (double)dgates[(int64_t)r * S + s];
+        double dot = 0.0;
+        for (int32_t e = 0; e < E; ++e) dot += p[e] * g[e];
+        for (int32_t e = 0; e < E; ++e) dlogits[s * E + e] = p[e] * (g[e] - dot);
+    }
+    double loss = 0.0;
+    if (needed != NULL && S > 0)
+        for (int32_t e = 0; e < E; ++e)
+            loss += ((double)needed[e] / ((double)k * (double)S)) * (colsum[e] / (double)S);
+    *aux_loss = alpha * (double)E * loss;
+    free(p); free(g); free(colsum);
+}
+
+/* dWg[m][e] = sum_s x[s][m] * dlogits[s][e] (fp64, [M,E]), s in increasing order. */
+void oracle_gate_weight_grad(int32_t S, int32_t M, int32_t E, int dtype, const void *x,
+                             const double *dlogits, double *dWg) {
+    for (int32_t m = 0; m < M; ++m)
+        for (int32_t e = 0; e < E; ++e) {
+            double acc = 0.0;
+            for (int64_t s = 0; s < S; ++s) acc += load_elem(x, dtype, s * M + m) * dlogits[s * E + e];
+            dWg[(int64_t)m * E + e] = acc;
         }
 }

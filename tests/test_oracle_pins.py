@@ -458,3 +458,174 @@ def test_backward_columns_equal_backward_rows():
     assert np.array_equal(dy, dy2)
     assert np.array_equal(dpre[:, cols], dpre2)
     assert np.array_equal(fw["h"][rows][:, cols], hv2)
+
+
+# ---------------------------------------------------------------- gate backward
+
+def _aux_loss_torch(p, needed, k, alpha):
+    """Load-balance loss as a function of the probabilities: alpha * E * sum_e f_e * mean_s p[s, e],
+    f_e = needed[e] / (k S) held constant."""
+    S, E = p.shape
+    f = torch.from_numpy(np.asarray(needed, np.float64)) / (k * S)
+    return alpha * E * (f * p.mean(dim=0)).sum()
+
+
+def _gate_loss_torch(logits64, idx, dgates, needed, k, alpha):
+    """Scalar whose gradient the gate backward computes: sum over routes of dgates * p at the
+    route's expert, plus the auxiliary loss."""
+    p = torch.softmax(logits64, dim=1)
+    sel = p.gather(1, torch.from_numpy(idx.T.astype(np.int64)))  # [S, k]
+    loss = (sel * torch.from_numpy(dgates.T.astype(np.float64))).sum()
+    if needed is not None:
+        loss = loss + _aux_loss_torch(p, needed, k, alpha)
+    return loss
+
+
+@pytest.mark.parametrize("S,E,k,alpha", [(7, 5, 2, 0.01), (9, 8, 1, 0.0), (6, 3, 3, 0.3), (11, 64, 4, 0.01)])
+def test_gate_backward_matches_autograd_of_softmax_and_aux_loss(S, E, k, alpha):
+    rng = np.random.default_rng(100 + S)
+    logits = (rng.standard_normal((S, E)) * 2).astype(np.float32)
+    idx, _ = oracle.softmax_topk(logits, k)
+    _, needed = oracle.locations(idx, E)
+    dgates = rng.standard_normal((k, S)).astype(np.float32)
+    dl, aux = oracle.gate_backward(logits, idx, dgates, needed, alpha)
+    lt = torch.from_numpy(logits.astype(np.float64)).requires_grad_(True)
+    loss = _gate_loss_torch(lt, idx, dgates, needed, k, alpha)
+    (ref,) = torch.autograd.grad(loss, lt)
+    ref = ref.numpy()
+    assert np.abs(dl - ref).max() <= 1e-13 * max(np.abs(ref).max(), 1.0)
+    p = torch.softmax(torch.from_numpy(logits.astype(np.float64)), 1)
+    assert aux == pytest.approx(float(_aux_loss_torch(p, needed, k, alpha)), rel=1e-13, abs=1e-300)
+
+
+def test_gate_backward_central_differences():
+    # a derivative the oracle does not compute analytically: central differences of the scalar
+    S, E, k, alpha = 5, 6, 2, 0.05
+    rng = np.random.default_rng(3)
+    logits = rng.standard_normal((S, E)).astype(np.float32)
+    idx, _ = oracle.softmax_topk(logits, k)
+    _, needed = oracle.locations(idx, E)
+    dgates = rng.standard_normal((k, S)).astype(np.float32)
+    dl, _ = oracle.gate_backward(logits, idx, dgates, needed, alpha)
+
+    def loss(l64):
+        z = np.exp(l64 - l64.max(axis=1, keepdims=True))
+        p = z / z.sum(axis=1, keepdims=True)
+        v = sum(float(dgates[r, s]) * p[s, idx[r, s]] for r in range(k) for s in range(S))
+        f = needed / (k * S)
+        return v + alpha * E * float((f * p.mean(axis=0)).sum())
+
+    base = logits.astype(np.float64)
+    h = 1e-5
+    for s in range(S):
+        for e in range(E):
+            a, b = base.copy(), base.copy()
+            a[s, e] += h
+            b[s, e] -= h
+            fd = (loss(a) - loss(b)) / (2 * h)
+            assert dl[s, e] == pytest.approx(fd, abs=1e-9)
+
+
+def test_gate_backward_invariants_and_closed_forms():
+    S, E, k = 8, 4, 2
+    rng = np.random.default_rng(5)
+    logits = rng.standard_normal((S, E)).astype(np.float32)
+    idx, _ = oracle.softmax_topk(logits, k)
+    _, needed = oracle.locations(idx, E)
+    dgates = rng.standard_normal((k, S)).astype(np.float32)
+    dl, _ = oracle.gate_backward(logits, idx, dgates, needed, 0.01)
+    # softmax is invariant to adding a constant to a token's logits: each row sums to 0
+    assert np.abs(dl.sum(axis=1)).max() <= 1e-15 * np.abs(dl).max() * E
+    # only the routed entries carry upstream gradient: with alpha = 0 and dgates at one route,
+    # dlogits = dg * p_i * (onehot_i - p)
+    one = np.zeros_like(dgates)
+    one[0, 3] = 2.5
+    dl1, aux0 = oracle.gate_backward(logits, idx, one, needed, 0.0)
+    p = scipy.special.softmax(logits.astype(np.float64), axis=1)
+    i = idx[0, 3]
+    want = np.zeros((S, E))
+    want[3] = 2.5 * p[3, i] * ((np.arange(E) == i) - p[3])
+    assert np.abs(dl1 - want).max() <= 1e-15
+    assert aux0 == 0.0
+    # balanced routing at uniform probabilities: l_aux = alpha exactly, and no gradient at all
+    flat = np.zeros((S, E), np.float32)
+    fidx = np.array([[(2 * s) % E for s in range(S)], [(2 * s + 1) % E for s in range(S)]], np.int32)
+    _, fneed = oracle.locations(fidx, E)
+    assert (fneed == k * S // E).all()
+    dlf, auxf = oracle.gate_backward(flat, fidx, np.zeros((k, S), np.float32), fneed, 0.01)
+    assert auxf == pytest.approx(0.01, rel=1e-15)
+    assert np.abs(dlf).max() <= 1e-18
+    # every route on one expert with (almost) all the probability: l_aux -> alpha * E
+    peaked = np.full((S, E), -60.0, np.float32)
+    peaked[:, 1] = 60.0
+    pidx = np.full((1, S), 1, np.int32)
+    _, pneed = oracle.locations(pidx, E)
+    _, auxp = oracle.gate_backward(peaked, pidx, np.zeros((1, S), np.float32), pneed, 0.01)
+    assert auxp == pytest.approx(0.01 * E, rel=1e-12)
+    # no token: no loss
+    _, aux_e = oracle.gate_backward(np.zeros((0, E), np.float32), np.zeros((k, 0), np.int32),
+                                    np.zeros((k, 0), np.float32), np.zeros(E, np.int32), 0.01)
+    assert aux_e == 0.0
+
+
+@pytest.mark.parametrize("dtype", [W.DT_F32, W.DT_BF16])
+def test_gate_projection_gradients_match_autograd(dtype):
+    # x . Wg exact in fp32 (small integers times multiples of 2^-6), so the oracle's fp32 logits
+    # equal the fp64 ones and autograd of the fp64 composite pins dWg and dx's gate share tightly
+    S, M, E, k, alpha = 12, 16, 5, 2, 0.01
+    rng = np.random.default_rng(21)
+    x32 = rng.integers(-4, 5, (S, M)).astype(np.float32)
+    Wg = (rng.integers(-64, 65, (M, E)) / 64.0).astype(np.float32)
+    x = to_dtype_bits(x32, dtype)
+    logits = oracle.gate_logits(x, Wg, dtype)
+    assert np.array_equal(logits, (x32.astype(np.float64) @ Wg.astype(np.float64)).astype(np.float32))
+    idx, _ = oracle.softmax_topk(logits, k)
+    _, needed = oracle.locations(idx, E)
+    dgates = rng.standard_normal((k, S)).astype(np.float32)
+    dl, _ = oracle.gate_backward(logits, idx, dgates, needed, alpha)
+    dWg = oracle.gate_weight_grad(x, dl, dtype)
+    no_routes = np.zeros((0,), np.int64)
+    dx = oracle.dx_tokens(no_routes, np.zeros((0, M), oracle.elem_dtype(dtype)), np.arange(S), S, k, dtype,
+                          dlogits=dl, Wg=Wg)
+    xt = torch.from_numpy(x32.astype(np.float64)).requires_grad_(True)
+    wt = torch.from_numpy(Wg.astype(np.float64)).requires_grad_(True)
+    loss = _gate_loss_torch(xt @ wt, idx, dgates, needed, k, alpha)
+    rx, rw = (t.numpy() for t in torch.autograd.grad(loss, [xt, wt]))
+    assert np.abs(dWg - rw).max() <= 1e-13 * max(np.abs(rw).max(), 1.0)
+    # dx is stored once in the data type: within half an ulp of the fp64 gradient
+    got = f32_of(dx).astype(np.float64)
+    ulp = np.spacing(np.abs(rx).astype(np.float32)).astype(np.float64)
+    if dtype == W.DT_BF16:
+        ulp = ulp * 2 ** 16  # bf16 keeps 16 fewer fraction bits than fp32
+    assert (np.abs(got - rx) <= 0.5 * ulp + 1e-12 * np.abs(rx).max()).all()
+
+
+def test_layer_backward_with_gate_matches_autograd():
+    # the whole training backward: gates from softmax(x . Wg) and the auxiliary loss
+    S, M, E, k, H, f, act, alpha = 16, 8, 3, 2, 10, 0.75, W.ACT_GELU, 0.01
+    rng = np.random.default_rng(31)
+    x = rng.standard_normal((S, M)).astype(np.float32)
+    Wg = rng.standard_normal((M, E)).astype(np.float32)
+    W1 = (rng.standard_normal((E, H, M)) * 0.3).astype(np.float32)
+    W2 = (rng.standard_normal((E, M, H)) * 0.3).astype(np.float32)
+    b1 = (rng.standard_normal((E, H)) * 0.3).astype(np.float32)
+    b2 = (rng.standard_normal((E, M)) * 0.3).astype(np.float32)
+    dout = rng.standard_normal((S, M)).astype(np.float32)
+    inp = dict(x=x, Wg=Wg, W1=W1, W2=W2, b1=b1, b2=b2, dout=dout)
+    fw = oracle.layer_forward(inp, k, f, act, W.DT_F32)
+    bw = oracle.layer_backward(fw, inp, act, W.DT_F32, aux_coef=alpha)
+    rt = fw["route"]
+    assert (rt["loc"] >= rt["C"]).any(), "the case should drop routes"
+    tt = {n: torch.from_numpy(v).double().requires_grad_(True) for n, v in inp.items() if n != "dout"}
+    logits64 = tt["x"] @ tt["Wg"]
+    p = torch.softmax(logits64, 1)
+    gates = p.gather(1, torch.from_numpy(rt["idx"].T.astype(np.int64))).T  # [k, S]
+    out = _dense_layer_torch(tt["x"], None, tt["W1"], tt["b1"], tt["W2"], tt["b2"], act, E, rt["C"],
+                             rt["idx"], rt["loc"], gates)
+    loss = (out * torch.from_numpy(dout).double()).sum() + _aux_loss_torch(p, rt["needed"], k, alpha)
+    grads = torch.autograd.grad(loss, [tt["x"], tt["Wg"], logits64])
+    for n, ref in zip(["dx", "dWg", "dlogits"], grads):
+        ref = ref.numpy()
+        got = bw[n].astype(np.float64)
+        assert np.abs(got - ref).max() / max(np.abs(ref).max(), 1e-30) < 2e-6, n
+    assert bw["aux_loss"] == pytest.approx(float(_aux_loss_torch(p.detach(), rt["needed"], k, alpha)), rel=1e-6)
