@@ -4,8 +4,9 @@ One step = one pass of the whole layer over one batch of synthetic input that is
 already resident in HBM: for the default workload (S=4096 tokens, M=1024, E=8
 experts, top-2, H=4096, bf16, logits projected from x by an fp32 gate matrix,
 capacity_factor 1.25) that is gate projection -> route -> encode -> fc1 -> fc2
--> decode; workloads with a backward add the backward of decode, FFN and
-encode. The timed region is exactly --steps calls of the fused C-ABI entry
+-> decode; workloads with a backward add the backward of decode, FFN, encode
+and the gate (dlogits through the softmax, the 0.01 load-balance loss, and for
+a projected gate dWg and the projection's share of dx). The timed region is exactly --steps calls of the fused C-ABI entry
 points, bracketed by synchronisations.
 
 A second timed loop records HIP events around each stage on the stream the
@@ -114,6 +115,11 @@ def algorithmic(w, C, kept):
         # dy/dgates: read dout and kept y rows, write kept dy rows; dx: read kept dbuf rows, write dx;
         # GEMMs: dh, dW2, dbuf, dW1 (2*M*H*kept flops each)
         st["backward"] = ("flops", 8 * M * H * kept)
+        # gate backward: read logits, idx, dgates, needed; write dlogits
+        st["gate_bwd"] = ("bytes", 8 * S * E + 8 * k * S + 4 * E)
+        if w.logits == "gate":
+            # dWg = x^T dlogits: read x and dlogits, write dWg
+            st["gate_wgrad"] = ("bytes", S * M * b + 4 * S * E + 4 * M * E)
     return st
 
 
@@ -196,14 +202,20 @@ def main():
     s = moe.Shape.of(w)
     gate = w.logits == "gate"
     bufs = moe.alloc_forward(s, dev, training=w.backward, gate_projection=gate)
-    grads = moe.alloc_backward(s, dev) if w.backward else None
+    grads = moe.alloc_backward(s, dev, gate=True, gate_projection=gate) if w.backward else None
     x, W1, W2, b1, b2 = inp["x"], inp["W1"], inp["W2"], inp.get("b1"), inp.get("b2")
     logits_in, Wg = (None, inp["Wg"]) if gate else (inp["logits"], None)
+    # the training step's backward includes the gate: dlogits, the load-balance loss, and with a
+    # projected gate dWg and dx's gate share
+    logits_bwd = bufs["logits"] if gate else logits_in
+
+    def backward():
+        moe.layer_backward(s, bufs, inp["dout"], W1, W2, grads=grads, logits=logits_bwd, x=x, Wg=Wg)
 
     def step():
         moe.layer_forward(s, x, W1, b1, W2, b2, logits=logits_in, Wg=Wg, bufs=bufs)
         if w.backward:
-            moe.layer_backward(s, bufs, inp["dout"], W1, W2, grads=grads)
+            backward()
 
     for _ in range(args.warmup):
         step()
@@ -224,7 +236,7 @@ def main():
     # ---- per-stage HIP-event timing on the library's stream
     stream = torch.cuda.current_stream()
     names = (["gate"] if gate else []) + ["route", "encode", "fc1", "fc2", "decode"] + (
-        ["backward"] if w.backward else [])
+        ["backward", "gate_bwd"] + (["gate_wgrad"] if gate else []) if w.backward else [])
     ev = {n: [] for n in names}
     lg = bufs["logits"] if gate else logits_in
     b = bufs
@@ -271,7 +283,13 @@ def main():
         ("decode", lambda: moe.moe_decode(s, b["y"], b["gates"], b["idx"], b["loc"], b["capacity"], b["out"])),
     ]
     if w.backward:
-        stage_fns.append(("backward", lambda: moe.layer_backward(s, b, inp["dout"], W1, W2, grads=grads)))
+        stage_fns.append(("backward", backward))
+        stage_fns.append(("gate_bwd", lambda: moe.moe_gate_backward(s, lg, b["idx"], grads["dgates"], b["needed"],
+                                                                    moe.AUX_COEF, grads["dlogits"],
+                                                                    grads["aux_loss"], b["ws"])))
+        if gate:
+            stage_fns.append(("gate_wgrad", lambda: moe.moe_gate_weight_grad(s, x, grads["dlogits"], grads["dWg"],
+                                                                             b["ws"])))
     reps = max(1, min(50, args.steps))
     rounds = max(1, min(10, args.steps // reps))
     for rd in range(rounds):
@@ -307,7 +325,8 @@ def main():
         dtype="bf16" if w.dtype == W.DT_BF16 else "f32", data="synthetic",
         config=dict(workload=w.name, S=w.S, M=w.M, E=w.E, k=w.k, H=w.H, capacity_factor=w.capacity_factor,
                     act="gelu" if w.act == W.ACT_GELU else "relu", biases=[w.has_fc1_bias, w.has_fc2_bias],
-                    logits=w.logits, backward=w.backward, C=C, kept_routes=kept, parallelism="single-gpu"),
+                    logits=w.logits, backward=w.backward, C=C, kept_routes=kept, parallelism="single-gpu",
+                    aux_coef=moe.AUX_COEF if w.backward else None),
         roofline=roofline, stages=stages, cpu_baseline=cpu,
     )
     print(json.dumps(line), flush=True)

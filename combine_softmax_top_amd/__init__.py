@@ -83,8 +83,13 @@ _SIGS = {
     "moe_expert_fc2": [_SP, _P, _P, _P, _P, _P, _P, _P],
     "moe_decode": [_SP, _P, _P, _P, _P, _P, _P, _P],
     "moe_layer_forward": [_SP] + [_P] * 21 + [ctypes.c_size_t, _P],
-    "moe_layer_backward": [_SP] + [_P] * 22,
+    "moe_gate_backward": [_SP, _P, _P, _P, _P, ctypes.c_double, _P, _P, _P, ctypes.c_size_t, _P],
+    "moe_gate_weight_grad": [_SP, _P, _P, _P, _P, ctypes.c_size_t, _P],
+    "moe_layer_backward": [_SP] + [_P] * 23 + [ctypes.c_double] + [_P] * 6 + [ctypes.c_size_t, _P],
 }
+
+# coefficient of the auxiliary load-balance loss in the MoE training blog's runs
+AUX_COEF = 0.01
 for _name, _args in _SIGS.items():
     _fn = getattr(_lib, _name)
     _fn.argtypes = _args
@@ -169,6 +174,21 @@ def moe_decode(shape: Shape, y, gates, idx, loc, capacity, out, stream=None) -> 
                            _ptr(out), _stream(stream)))
 
 
+def _ws_args(ws):
+    return _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size()
+
+
+def moe_gate_backward(shape: Shape, logits, idx, dgates, needed, aux_coef, dlogits, aux_loss, ws,
+                      stream=None) -> None:
+    _check(_lib.moe_gate_backward(ctypes.byref(shape.c()), _ptr(logits), _ptr(idx), _ptr(dgates), _ptr(needed),
+                                  float(aux_coef), _ptr(dlogits), _ptr(aux_loss), *_ws_args(ws), _stream(stream)))
+
+
+def moe_gate_weight_grad(shape: Shape, x, dlogits, dWg, ws, stream=None) -> None:
+    _check(_lib.moe_gate_weight_grad(ctypes.byref(shape.c()), _ptr(x), _ptr(dlogits), _ptr(dWg), *_ws_args(ws),
+                                     _stream(stream)))
+
+
 def moe_layer_forward(shape: Shape, x, logits_in, Wg, logits_out, W1, b1, W2, b2, idx, loc, gates, needed, fill,
                       capacity, slot_route, buf, pre, h, y, out, ws, stream=None) -> None:
     _check(_lib.moe_layer_forward(
@@ -179,11 +199,13 @@ def moe_layer_forward(shape: Shape, x, logits_in, Wg, logits_out, W1, b1, W2, b2
 
 
 def moe_layer_backward(shape: Shape, dout, buf, pre, h, y, gates, idx, loc, fill, capacity, W1, W2, dy, dpre, dbuf,
-                       dx, dW1, db1, dW2, db2, dgates, stream=None) -> None:
+                       dx, dW1, db1, dW2, db2, dgates, logits=None, needed=None, aux_coef=0.0, x=None, Wg=None,
+                       dlogits=None, dWg=None, aux_loss=None, ws=None, stream=None) -> None:
     _check(_lib.moe_layer_backward(
         ctypes.byref(shape.c()), _ptr(dout), _ptr(buf), _ptr(pre), _ptr(h), _ptr(y), _ptr(gates), _ptr(idx),
         _ptr(loc), _ptr(fill), _ptr(capacity), _ptr(W1), _ptr(W2), _ptr(dy), _ptr(dpre), _ptr(dbuf), _ptr(dx),
-        _ptr(dW1), _ptr(db1), _ptr(dW2), _ptr(db2), _ptr(dgates), _stream(stream)))
+        _ptr(dW1), _ptr(db1), _ptr(dW2), _ptr(db2), _ptr(dgates), _ptr(logits), _ptr(needed), float(aux_coef),
+        _ptr(x), _ptr(Wg), _ptr(dlogits), _ptr(dWg), _ptr(aux_loss), *_ws_args(ws), _stream(stream)))
 
 
 # ---------------------------------------------------------------- buffers
@@ -223,13 +245,18 @@ def layer_forward(shape: Shape, x, W1, b1, W2, b2, logits=None, Wg=None, bufs=No
     return bufs
 
 
-def alloc_backward(shape: Shape, device="cuda") -> Dict[str, torch.Tensor]:
+def alloc_backward(shape: Shape, device="cuda", gate: bool = False,
+                   gate_projection: bool = False) -> Dict[str, torch.Tensor]:
+    """Gradient buffers; gate adds dlogits and aux_loss, gate_projection also dWg."""
     S, M, E, k, H = shape.S, shape.M, shape.E, shape.k, shape.H
     cmax = moe_capacity_bound(shape)
     dt = shape.torch_dtype
     f32 = dict(dtype=torch.float32, device=device)
     dyb = torch.empty(E * cmax, M, dtype=dt, device=device)
     return dict(
+        dlogits=torch.empty(S, E, **f32) if gate or gate_projection else None,
+        aux_loss=torch.empty(1, **f32) if gate or gate_projection else None,
+        dWg=torch.empty(M, E, **f32) if gate_projection else None,
         dy=dyb, dbuf=dyb,  # dbuf reuses dy's memory (allowed by the ABI)
         dpre=torch.empty(E * cmax, H, dtype=dt, device=device),
         dx=torch.empty(S, M, dtype=dt, device=device),
@@ -240,10 +267,20 @@ def alloc_backward(shape: Shape, device="cuda") -> Dict[str, torch.Tensor]:
     )
 
 
-def layer_backward(shape: Shape, fw: Dict[str, torch.Tensor], dout, W1, W2, grads=None, stream=None):
+def layer_backward(shape: Shape, fw: Dict[str, torch.Tensor], dout, W1, W2, grads=None, logits=None, x=None,
+                   Wg=None, aux_coef=AUX_COEF, stream=None):
+    """The fused backward into ``grads`` (allocated if None). With ``logits`` (the forward's;
+    ``fw["logits"]`` for a projected gate) it includes the gate backward and the auxiliary
+    load-balance loss of coefficient ``aux_coef``; with ``Wg`` and ``x`` also dWg and the gate
+    projection's share of dx."""
     if grads is None:
-        grads = alloc_backward(shape, dout.device)
+        grads = alloc_backward(shape, dout.device, gate=logits is not None, gate_projection=Wg is not None)
+    gate = logits is not None
     moe_layer_backward(shape, dout, fw["buf"], fw["pre"], fw["h"], fw["y"], fw["gates"], fw["idx"], fw["loc"],
                        fw["fill"], fw["capacity"], W1, W2, grads["dy"], grads["dpre"], grads["dbuf"], grads["dx"],
-                       grads["dW1"], grads["db1"], grads["dW2"], grads["db2"], grads["dgates"], stream)
+                       grads["dW1"], grads["db1"], grads["dW2"], grads["db2"], grads["dgates"],
+                       logits=logits, needed=fw["needed"] if gate else None, aux_coef=aux_coef if gate else 0.0,
+                       x=x if Wg is not None else None, Wg=Wg,
+                       dlogits=grads["dlogits"] if gate else None, dWg=grads["dWg"] if Wg is not None else None,
+                       aux_loss=grads["aux_loss"] if gate else None, ws=fw["ws"] if gate else None, stream=stream)
     return grads

@@ -56,9 +56,19 @@ int64_t cap_bound(const moe_shape &s) {
 
 int32_t num_tiles(const moe_shape &s) { return (s.S + moe::kRouteTile - 1) / moe::kRouteTile; }
 
+// One workspace serves routing (per-tile route counts) and the gate backward
+// (auxiliary-loss partials and dWg slice partials); they are never live together.
 size_t ws_bytes_needed(const moe_shape &s) {
     const size_t n = static_cast<size_t>(s.E) * s.k * num_tiles(s);
-    return ((n * sizeof(int32_t)) + 255) & ~static_cast<size_t>(255);
+    const size_t route = ((n * sizeof(int32_t)) + 255) & ~static_cast<size_t>(255);
+    return std::max(route, moe::gate_grad_ws_bytes(s.S, s.M, s.E));
+}
+
+moe_status check_ws(const moe_shape &s, const void *ws, size_t ws_bytes) {
+    const size_t need = ws_bytes_needed(s);
+    if (need > 0 && (ws == nullptr || ws_bytes < need))
+        return fail(MOE_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws == nullptr ? 0 : ws_bytes);
+    return MOE_OK;
 }
 
 moe_status check_shape(const moe_shape *sp) {
@@ -127,9 +137,7 @@ moe_status moe_route(const moe_shape *shape, const float *logits, int32_t *idx, 
     const moe_shape &s = *shape;
     MOE_REQUIRE(needed && fill && capacity, "needed, fill and capacity must be non-NULL");
     if (s.S > 0) MOE_REQUIRE(logits && idx && loc && gates, "logits, idx, loc and gates must be non-NULL");
-    const size_t need = ws_bytes_needed(s);
-    if (need > 0 && (ws == nullptr || ws_bytes < need))
-        return fail(MOE_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws == nullptr ? 0 : ws_bytes);
+    if ((st = check_ws(s, ws, ws_bytes)) != MOE_OK) return st;
     MOE_REQUIRE_ALIGNED(logits, idx, loc, gates, needed, fill, capacity, slot_route, ws);
     moe::RouteWs w{static_cast<int32_t *>(ws), num_tiles(s)};
     hipError_t e = moe::launch_route(s, logits, idx, loc, gates, needed, fill, capacity, slot_route, w, by_factor(s),
@@ -205,6 +213,35 @@ moe_status moe_decode(const moe_shape *shape, const void *y, const float *gates,
     return e == hipSuccess ? MOE_OK : hip_fail(e, "decode");
 }
 
+moe_status moe_gate_backward(const moe_shape *shape, const float *logits, const int32_t *idx, const float *dgates,
+                             const int32_t *needed, double aux_coef, float *dlogits, float *aux_loss, void *ws,
+                             size_t ws_bytes, void *stream) {
+    moe_status st = check_shape(shape);
+    if (st != MOE_OK) return st;
+    const moe_shape &s = *shape;
+    MOE_REQUIRE(std::isfinite(aux_coef), "aux_coef is not finite");
+    MOE_REQUIRE(needed != nullptr || aux_coef == 0.0, "needed is required when aux_coef != 0");
+    if (s.S > 0) MOE_REQUIRE(logits && idx && dgates && dlogits, "logits, idx, dgates and dlogits must be non-NULL");
+    if ((st = check_ws(s, ws, ws_bytes)) != MOE_OK) return st;
+    MOE_REQUIRE_ALIGNED(logits, idx, dgates, needed, dlogits, aux_loss, ws);
+    hipError_t e = moe::launch_gate_backward(s, logits, idx, dgates, needed, aux_coef, dlogits, aux_loss, ws,
+                                             as_stream(stream));
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "gate backward");
+}
+
+moe_status moe_gate_weight_grad(const moe_shape *shape, const void *x, const float *dlogits, float *dWg, void *ws,
+                                size_t ws_bytes, void *stream) {
+    moe_status st = check_shape(shape);
+    if (st != MOE_OK) return st;
+    const moe_shape &s = *shape;
+    MOE_REQUIRE(dWg != nullptr, "dWg is NULL");
+    if (s.S > 0) MOE_REQUIRE(x && dlogits, "x and dlogits must be non-NULL");
+    if ((st = check_ws(s, ws, ws_bytes)) != MOE_OK) return st;
+    MOE_REQUIRE_ALIGNED(x, dlogits, dWg, ws);
+    hipError_t e = moe::launch_gate_weight_grad(s, x, dlogits, dWg, ws, as_stream(stream));
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "gate weight gradient");
+}
+
 moe_status moe_layer_forward(const moe_shape *shape, const void *x, const float *logits_in, const float *Wg,
                              float *logits_out, const void *W1, const void *b1, const void *W2, const void *b2,
                              int32_t *idx, int32_t *loc, float *gates, int32_t *needed, int32_t *fill,
@@ -222,9 +259,7 @@ moe_status moe_layer_forward(const moe_shape *shape, const void *x, const float 
     if (s.S > 0) MOE_REQUIRE(x && idx && loc && gates && out, "x, idx, loc, gates and out must be non-NULL");
     MOE_REQUIRE((b1 != nullptr) == (s.has_fc1_bias != 0), "b1 must be given iff has_fc1_bias");
     MOE_REQUIRE((b2 != nullptr) == (s.has_fc2_bias != 0), "b2 must be given iff has_fc2_bias");
-    const size_t need = ws_bytes_needed(s);
-    if (need > 0 && (ws == nullptr || ws_bytes < need))
-        return fail(MOE_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws == nullptr ? 0 : ws_bytes);
+    if ((st = check_ws(s, ws, ws_bytes)) != MOE_OK) return st;
     MOE_REQUIRE_ALIGNED(x, logits_in, Wg, logits_out, W1, b1, W2, b2, idx, loc, gates, needed, fill, capacity,
                         slot_route, buf, pre, h, y, out, ws);
     if (Wg != nullptr && !moe::gate_supported(s.M, s.E, s.dtype))
@@ -256,25 +291,49 @@ moe_status moe_layer_backward(const moe_shape *shape, const void *dout, const vo
                               const void *h, const void *y, const float *gates, const int32_t *idx,
                               const int32_t *loc, const int32_t *fill, const int32_t *capacity, const void *W1,
                               const void *W2, void *dy, void *dpre, void *dbuf, void *dx, float *dW1, float *db1,
-                              float *dW2, float *db2, float *dgates, void *stream) {
+                              float *dW2, float *db2, float *dgates, const float *logits, const int32_t *needed,
+                              double aux_coef, const void *x, const float *Wg, float *dlogits, float *dWg,
+                              float *aux_loss, void *ws, size_t ws_bytes, void *stream) {
     moe_status st = check_shape(shape);
     if (st != MOE_OK) return st;
     const moe_shape &s = *shape;
     MOE_REQUIRE(buf && pre && h && y && fill && capacity && W1 && W2 && dy && dpre && dbuf && dW1 && dW2,
                 "buf, pre, h, y, fill, capacity, W1, W2, dy, dpre, dbuf, dW1 and dW2 must be non-NULL");
     if (s.S > 0) MOE_REQUIRE(dout && gates && idx && loc && dx && dgates, "dout, gates, idx, loc, dx and dgates must be non-NULL");
+    // the gate backward runs when any of its inputs or outputs is given
+    const bool gate = logits != nullptr || dlogits != nullptr || dWg != nullptr || aux_loss != nullptr;
+    if (gate) {
+        MOE_REQUIRE(std::isfinite(aux_coef), "aux_coef is not finite");
+        MOE_REQUIRE(needed != nullptr || aux_coef == 0.0, "needed is required when aux_coef != 0");
+        if (s.S > 0) MOE_REQUIRE(logits && dlogits, "the gate backward needs logits and dlogits");
+        MOE_REQUIRE((Wg != nullptr) == (dWg != nullptr), "Wg and dWg go together");
+        if (s.S > 0 && Wg != nullptr) MOE_REQUIRE(x != nullptr, "x is required with Wg");
+        if ((st = check_ws(s, ws, ws_bytes)) != MOE_OK) return st;
+    } else {
+        MOE_REQUIRE(Wg == nullptr, "Wg needs the gate backward (logits, dlogits, dWg)");
+    }
     MOE_REQUIRE_ALIGNED(dout, buf, pre, h, y, gates, idx, loc, fill, capacity, W1, W2, dy, dpre, dbuf, dx, dW1, db1,
-                        dW2, db2, dgates);
+                        dW2, db2, dgates, logits, needed, x, Wg, dlogits, dWg, aux_loss, ws);
     hipStream_t strm = as_stream(stream);
     const int32_t cmax = static_cast<int32_t>(cap_bound(s));
     hipError_t e;
     if ((e = moe::launch_decode_bwd(s, dout, y, gates, idx, loc, capacity, dy, dgates, strm)) != hipSuccess)
         return hip_fail(e, "decode backward");
+    if (gate) {
+        if ((e = moe::launch_gate_backward(s, logits, idx, dgates, needed, aux_coef, dlogits, aux_loss, ws, strm)) !=
+            hipSuccess)
+            return hip_fail(e, "gate backward");
+        if (Wg != nullptr && (e = moe::launch_gate_weight_grad(s, x, dlogits, dWg, ws, strm)) != hipSuccess)
+            return hip_fail(e, "gate weight gradient");
+    }
     if ((e = moe::launch_expert_ffn_bwd(s, buf, pre, h, W1, W2, fill, capacity, dy, dpre, dbuf, dW1, db1, dW2, db2,
                                         cmax, strm)) != hipSuccess)
         return hip_fail(e, "expert ffn backward");
-    if ((e = moe::launch_decode(s, dbuf, nullptr, idx, loc, capacity, dx, true, strm)) != hipSuccess)
-        return hip_fail(e, "encode backward");
+    if (gate && Wg != nullptr)
+        e = moe::launch_gate_dx(s, dbuf, idx, loc, capacity, dlogits, Wg, dx, strm);
+    else
+        e = moe::launch_decode(s, dbuf, nullptr, idx, loc, capacity, dx, true, strm);
+    if (e != hipSuccess) return hip_fail(e, "encode backward");
     return MOE_OK;
 }
 

@@ -125,6 +125,16 @@ hipError_t launch_fc1(const moe_shape &s, const void *buf, const void *W1, const
                       const int32_t *cap, void *pre, void *h, int32_t cmax, hipStream_t st);
 hipError_t launch_fc2(const moe_shape &s, const void *h, const void *W2, const void *b2, const int32_t *fill,
                       const int32_t *cap, void *y, int32_t cmax, hipStream_t st);
+// Gate backward: dlogits (and, with needed, the auxiliary-loss partials in ws
+// and aux_loss if non-NULL); dWg = x^T dlogits; dx = kept dbuf rows + dlogits Wg^T.
+size_t gate_grad_ws_bytes(int S, int M, int E);
+hipError_t launch_gate_backward(const moe_shape &s, const float *logits, const int32_t *idx, const float *dgates,
+                                const int32_t *needed, double aux_coef, float *dlogits, float *aux_loss, void *ws,
+                                hipStream_t st);
+hipError_t launch_gate_weight_grad(const moe_shape &s, const void *x, const float *dlogits, float *dWg, void *ws,
+                                   hipStream_t st);
+hipError_t launch_gate_dx(const moe_shape &s, const void *dbuf, const int32_t *idx, const int32_t *loc,
+                          const int32_t *cap, const float *dlogits, const float *Wg, void *dx, hipStream_t st);
 hipError_t launch_expert_ffn_bwd(const moe_shape &s, const void *buf, const void *pre, const void *h,
                                  const void *W1, const void *W2, const int32_t *fill,
                                  const int32_t *cap, void *dy, void *dpre, void *dbuf, float *dW1,

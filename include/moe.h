@@ -20,7 +20,9 @@
  *      routes, accumulated in fp32 (DeepSpeed PR #8195 section 3).
  * The backward covers decode (gate-weighted scatter of dout and the gate
  * gradient, kernels K1/K2 of blog part 3 section 3.5), the expert FFN (data
- * and fp32 weight/bias gradients) and encode (gather-sum, kernel K0).
+ * and fp32 weight/bias gradients), encode (gather-sum, kernel K0) and the
+ * gate itself: the softmax's gradient, the auxiliary load-balance loss (blog
+ * part 2 section 2.1) and the gate projection's weight and input gradients.
  *
  * Conventions shared by every call:
  *  - Pointers named *_host are host memory; every other pointer is device
@@ -32,7 +34,8 @@
  *    kernels move rows as 16-byte vectors.
  *  - Data-type tensors (x, W1, b1, W2, b2, buf, pre, h, y, out, dout, dx, dy,
  *    dpre, dbuf) are fp32 or bf16 as moe_shape.dtype says. logits, Wg, gates,
- *    dgates and the weight/bias gradients are fp32. Index tables are int32.
+ *    dgates, dlogits, the auxiliary loss and the weight/bias gradients are
+ *    fp32. Index tables are int32.
  *  - Route tables are route-major [k, S]: entry r*S + s is route r of token s,
  *    r = 0 the largest gate.
  *  - The capacity C is computed on the device and written to capacity[0];
@@ -96,7 +99,10 @@ moe_status moe_validate(const moe_shape *shape);
  * never below 1. Size every [E*C, *] buffer with E * (*cmax_host) rows. */
 moe_status moe_capacity_bound(const moe_shape *shape, int32_t *cmax_host);
 
-/* Bytes of device workspace moe_route / moe_layer_forward need (no GPU needed). */
+/* Bytes of device workspace moe_route, moe_layer_forward, the gate backward
+ * calls and moe_layer_backward (with the gate backward) need (no GPU needed).
+ * One buffer of this size serves all of them on one stream; calls that may run
+ * at the same time need workspaces of their own. */
 moe_status moe_workspace_size(const moe_shape *shape, size_t *bytes_host);
 
 /* Gate projection (Tutel catalogue page, "key configuration": the top-k gate
@@ -167,6 +173,35 @@ moe_status moe_expert_fc2(const moe_shape *shape, const void *h, const void *W2,
 moe_status moe_decode(const moe_shape *shape, const void *y, const float *gates, const int32_t *idx,
                       const int32_t *loc, const int32_t *capacity, void *out, void *stream);
 
+/* Gate backward (the softmax gate is trained: MoE training blog, part 2 section
+ * 2.1, training with top-1 gating and an auxiliary load-balance loss of
+ * coefficient 0.01; DeepSpeed PR #8195, forward + backward step times). The
+ * gates are unrenormalised softmax probabilities p of the logits (moe_route),
+ * so with
+ *   g[s][e] = sum of dgates[r][s] over the routes r with idx[r][s] == e
+ *             + aux_coef * E * f_e / S,      f_e = needed[e] / (k S),
+ *   dlogits[s][e] = p[s][e] * (g[s][e] - sum_j p[s][j] g[s][j])     (fp32)
+ * and aux_loss[0] = aux_coef * E * sum_e f_e * (1/S) sum_s p[s][e] (fp32; 0
+ * when S == 0): the load-balance loss in its usual routed-fraction times
+ * mean-probability form, f held constant (it comes from an argmax). Every
+ * route's dgates is used as given (moe_layer_backward passes 0 for dropped
+ * routes). needed may be NULL only when aux_coef == 0 (no auxiliary term);
+ * aux_loss may be NULL (not computed). logits [S,E] fp32 (the forward's);
+ * idx [k,S] int32; dgates [k,S] fp32; needed [E] int32; dlogits [S,E] fp32;
+ * ws: moe_workspace_size() bytes. Reductions run in a fixed order: results are
+ * reproducible run to run. */
+moe_status moe_gate_backward(const moe_shape *shape, const float *logits, const int32_t *idx,
+                             const float *dgates, const int32_t *needed, double aux_coef,
+                             float *dlogits, float *aux_loss, void *ws, size_t ws_bytes, void *stream);
+
+/* Gradient of the gate projection's weights (logits = x . Wg, moe_gate_project):
+ * dWg[m][e] = sum_s x[s][m] * dlogits[s][e], fp32 accumulation in a fixed
+ * order, overwritten (all zeros when S == 0). x [S,M] data type; dlogits [S,E]
+ * fp32; dWg [M,E] fp32; ws: moe_workspace_size() bytes. The projection's share
+ * of dx, dlogits . Wg^T, is added inside moe_layer_backward. */
+moe_status moe_gate_weight_grad(const moe_shape *shape, const void *x, const float *dlogits, float *dWg,
+                                void *ws, size_t ws_bytes, void *stream);
+
 /* The whole forward: [gate projection] -> route -> encode -> expert FFN ->
  * decode, on one stream, without a host synchronisation. Exactly one of
  * logits_in (given logits [S,E]) and Wg ([M,E], projected from x) is non-NULL;
@@ -194,13 +229,23 @@ moe_status moe_layer_forward(const moe_shape *shape, const void *x, const float 
  * dy, dbuf [E*cmax, M] and dpre [E*cmax, H] are caller scratch; dy and dbuf
  * may be the same buffer. dW1 [E,H,M], dW2 [E,M,H] fp32; db1 [E,H], db2 [E,M]
  * fp32 or NULL (not computed); dgates [k,S] fp32; dx [S,M]. Gradients are
- * overwritten, not accumulated. pre must come from the forward. */
+ * overwritten, not accumulated. pre must come from the forward.
+ * Gate backward (moe_gate_backward, moe_gate_weight_grad), run when any of
+ * logits, dlogits, dWg, aux_loss is non-NULL (all NULL: none of it, and Wg,
+ * x, needed, ws are not read): from the forward's logits, needed and
+ * aux_coef, dlogits and aux_loss (may be NULL) as in moe_gate_backward, from
+ * the dgates just computed. With Wg (the projected gate; dWg then required,
+ * x too), dWg = x^T . dlogits and dx[s] gains dlogits[s] . Wg^T, added in fp32
+ * before dx's single rounding to the data type. ws: moe_workspace_size() bytes
+ * (only with the gate backward). */
 moe_status moe_layer_backward(const moe_shape *shape, const void *dout, const void *buf,
                               const void *pre, const void *h, const void *y, const float *gates,
                               const int32_t *idx, const int32_t *loc, const int32_t *fill,
                               const int32_t *capacity, const void *W1, const void *W2, void *dy,
                               void *dpre, void *dbuf, void *dx, float *dW1, float *db1, float *dW2,
-                              float *db2, float *dgates, void *stream);
+                              float *db2, float *dgates, const float *logits, const int32_t *needed,
+                              double aux_coef, const void *x, const float *Wg, float *dlogits,
+                              float *dWg, float *aux_loss, void *ws, size_t ws_bytes, void *stream);
 
 /* Message of the last failing call on this thread ("" if none). */
 const char *moe_last_error(void);

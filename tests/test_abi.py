@@ -26,9 +26,13 @@ def _declared():
     return sorted(set(re.findall(r"^\s*(?:moe_status|const char \*)\s*(moe_\w+)\s*\(", text, re.M)))
 
 
+def odd_ptr():
+    return ctypes.c_void_p(0x1008)  # 8-byte aligned only, never dereferenced
+
+
 def test_every_declared_symbol_is_exported(moe):
     names = _declared()
-    assert len(names) == 13, names
+    assert len(names) == 15, names
     lib = ctypes.CDLL(moe.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -90,11 +94,30 @@ def test_entry_points_reject_before_enqueueing(moe):
     assert st == moe.MOE_EINVAL and "b1" in moe.moe_last_error()  # biases on, b1 missing
     st = lib.moe_layer_forward(ctypes.byref(c), fake, fake, fake, fake, *([fake] * 17), 1 << 20, None)
     assert st == moe.MOE_EINVAL  # both logits and Wg given
-    st = lib.moe_layer_backward(ctypes.byref(c), *([None] * 22))
+    st = lib.moe_layer_backward(ctypes.byref(c), *([None] * 23), 0.0, *([None] * 6), 0, None)
     assert st == moe.MOE_EINVAL
+    # gate backward argument checks
+    st = lib.moe_gate_backward(ctypes.byref(c), fake, fake, fake, None, 0.01, fake, None, fake, 1 << 20, None)
+    assert st == moe.MOE_EINVAL and "needed" in moe.moe_last_error()  # aux term without needed
+    st = lib.moe_gate_backward(ctypes.byref(c), fake, fake, fake, fake, float("nan"), fake, None, fake, 1 << 20, None)
+    assert st == moe.MOE_EINVAL and "aux_coef" in moe.moe_last_error()
+    st = lib.moe_gate_backward(ctypes.byref(c), fake, fake, fake, fake, 0.01, fake, fake, fake, 0, None)
+    assert st == moe.MOE_EWORKSPACE
+    st = lib.moe_gate_weight_grad(ctypes.byref(c), None, fake, fake, fake, 1 << 20, None)
+    assert st == moe.MOE_EINVAL  # x NULL with S > 0
+    st = lib.moe_gate_weight_grad(ctypes.byref(c), fake, fake, odd_ptr(), fake, 1 << 20, None)
+    assert st == moe.MOE_EINVAL and "aligned" in moe.moe_last_error()
+    # layer backward: Wg without dWg, and the gate backward without logits
+    full = [fake] * 21
+    st = lib.moe_layer_backward(ctypes.byref(c), *full[:21], fake, None, 0.0, fake, fake, fake, None, None,
+                                fake, 1 << 20, None)
+    assert st == moe.MOE_EINVAL and "dWg" in moe.moe_last_error()
+    st = lib.moe_layer_backward(ctypes.byref(c), *full[:21], None, None, 0.0, None, None, fake, None, None,
+                                None, 0, None)
+    assert st == moe.MOE_EINVAL and "logits" in moe.moe_last_error()
     with pytest.raises(moe.MoeError):
         moe._check(lib.moe_decode(ctypes.byref(c), None, None, None, None, None, None, None))
-    odd = ctypes.c_void_p(0x1008)  # 8-byte aligned only
+    odd = odd_ptr()
     st = lib.moe_encode(ctypes.byref(c), odd, fake, fake, fake, fake, fake, None)
     assert st == moe.MOE_EINVAL and "aligned" in moe.moe_last_error()
     st = lib.moe_expert_fc2(ctypes.byref(c), fake, fake, fake, fake, fake, odd, None)

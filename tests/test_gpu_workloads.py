@@ -1,13 +1,17 @@
-"""GPU parity at the five workloads' full sizes, in the launch configuration the
+"""GPU parity at the named workloads' full sizes, in the launch configuration the
 benchmark times (the fused C-ABI calls).
 
 Routing (and the gate projection) and the encode buffer are compared in full,
 bit for bit. GEMM-dependent outputs are compared on seeded samples that the
 oracle computes one by one from the original inputs: every expert's first and
 last filled rows plus random rows of h and y, a random set of tokens of the
-layer output, and, for the workload with a backward, random gate gradients,
+layer output, and, for the workloads with a backward, random gate gradients,
 random tokens of dx, and the weight/bias gradients of three experts (hottest,
-median, coldest) on random hidden columns.
+median, coldest) on random hidden columns. The gate backward: the auxiliary
+loss in full; dlogits on the sampled tokens (the oracle's dgates of their
+routes upstream); with a projected gate (small enough for the oracle to run
+every expert row) dgates, dlogits and dWg in full and dx's gate share on the
+sampled tokens.
 """
 from __future__ import annotations
 
@@ -19,7 +23,7 @@ import torch
 
 import oracle
 import workloads as W
-from tests.gpu_helpers import check_close, compare_route, host
+from tests.gpu_helpers import check_close, check_dlogits, check_dwg, compare_route, dgates_err, host
 from tests.helpers import f32_of
 
 pytestmark = pytest.mark.gpu
@@ -39,7 +43,10 @@ def test_full_size_workload(w):
     gate = w.logits == "gate"
     b = moe.layer_forward(s, inp["x"], inp["W1"], inp.get("b1"), inp["W2"], inp.get("b2"),
                           logits=None if gate else inp["logits"], Wg=inp.get("Wg"), training=w.backward)
-    gr = moe.layer_backward(s, b, inp["dout"], inp["W1"], inp["W2"]) if w.backward else None
+    gr = None
+    if w.backward:
+        gr = moe.layer_backward(s, b, inp["dout"], inp["W1"], inp["W2"],
+                                logits=b["logits"] if gate else inp["logits"], x=inp["x"], Wg=inp.get("Wg"))
     torch.cuda.synchronize()
     _say(f"[{w.name}] GPU forward{'+backward' if w.backward else ''} done in {time.time() - t0:.1f}s")
     ni = {k: host(v) for k, v in inp.items()}
@@ -73,6 +80,8 @@ def test_full_size_workload(w):
             rows += [e * C, e * C + int(fill[e]) - 1]
     filled = oracle.filled_rows(rt)
     rows += rng.choice(filled, size=min(len(filled), 64), replace=False).tolist()
+    if gate and w.backward:
+        rows += filled.tolist()  # every kept route's dgates feeds dWg
     rows = np.unique(np.asarray(rows, np.int64))
     # tokens of the layer output, and the rows their kept routes read
     ntok = min(w.S, 96)
@@ -107,18 +116,49 @@ def test_full_size_workload(w):
     routes = slot[kept_rows]
     dg_o = oracle.dgates(routes, dout, y_full[kept_rows], w.S, w.dtype)
     dg_g = host(gr["dgates"]).reshape(-1)[routes]
-    check_close(dg_g, dg_o, w.dtype, "dgates (sampled)")
+    check_close(dg_g, dg_o, w.dtype, "dgates (sampled)" if not gate else "dgates (all kept routes)")
+    # gate backward: the oracle's dgates upstream (0 where not computed), its dlogits compared on
+    # tokens whose kept routes all have them
+    dg_full = np.zeros((w.k * w.S,), np.float32)
+    dg_full[routes] = dg_o
+    dg_full = dg_full.reshape(w.k, w.S)
+    dg_err = np.zeros((w.k * w.S,))
+    dg_err[routes] = dgates_err(dg_o, w.dtype)  # the two sides' dgates agree within this
+    dg_err = dg_err.reshape(w.k, w.S)
+    dl_o, aux_o = oracle.gate_backward(logits, rt["idx"], dg_full, rt["needed"], moe.AUX_COEF)
+    aux_g = float(host(gr["aux_loss"])[0])
+    assert abs(aux_g - aux_o) <= 1e-5 * abs(aux_o) + 1e-12, ("aux_loss", aux_g, aux_o)
+    have = np.zeros(w.S, bool)
+    have[np.unique(routes % w.S)] = True
+    for r in range(w.k):
+        have &= (rt["loc"][r] >= C) | np.isin(r * w.S + np.arange(w.S), routes)
+    dl_toks = np.nonzero(have)[0]
+    assert len(dl_toks) >= min(w.S, 64), len(dl_toks)
+    dl_err = check_dlogits(host(gr["dlogits"])[dl_toks], dl_o[dl_toks], logits[dl_toks], rt["idx"][:, dl_toks],
+                           dg_full[:, dl_toks], rt["needed"], w.k, w.S, moe.AUX_COEF, dg_err=dg_err[:, dl_toks])
+    _say(f"[{w.name}] aux loss {aux_g:.6g} and dlogits on {len(dl_toks)} tokens within tolerance")
+    if gate:
+        assert len(dl_toks) == w.S
+        check_dwg(host(gr["dWg"]), oracle.gate_weight_grad(ni["x"], dl_o, w.dtype), ni["x"], dl_o, w.dtype,
+                  dl_err=dl_err)
+        _say(f"[{w.name}] dWg [{w.M}, {w.E}] within tolerance")
     dx_toks = toks[:8]
     dx_rows = np.asarray([rt["idx"][r, t] * C + rt["loc"][r, t] for r in range(w.k) for t in dx_toks
                           if rt["loc"][r, t] < C], np.int64)
     fw = dict(route=rt, buf=obuf)
     q, _, _, dbuf_o = oracle.backward_rows(fw, ni, dx_rows, w.act, w.dtype, want_dy=False, want_dpre=False)
-    dx_o = oracle.dx_tokens(q, dbuf_o, dx_toks, w.S, w.k, w.dtype)
+    dx_o = oracle.dx_tokens(q, dbuf_o, dx_toks, w.S, w.k, w.dtype, dlogits=dl_o if gate else None,
+                            Wg=ni.get("Wg"))
     terms = np.zeros(dx_o.shape)
     for i, qq in enumerate(q):
         terms[list(dx_toks).index(int(qq) % w.S)] += np.abs(f32_of(dbuf_o[i]))
+    extra = None
+    if gate:
+        wga = np.abs(ni["Wg"].astype(np.float64))
+        terms += np.abs(dl_o[dx_toks]) @ wga.T
+        extra = dl_err[dx_toks] @ wga.T
     check_close(host(gr["dx"][torch.from_numpy(dx_toks).cuda()]), dx_o, w.dtype, "dx (sampled)",
-                mag=np.abs(f32_of(dx_o)) + terms)
+                mag=np.abs(f32_of(dx_o)) + terms, extra=extra)
     _say(f"[{w.name}] dgates on {len(routes)} routes and dx on {len(dx_toks)} tokens within tolerance")
     order = np.argsort(fill)
     experts = sorted({int(order[-1]), int(order[len(order) // 2]), int(order[0])})

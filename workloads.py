@@ -1,4 +1,4 @@
-"""Seeded synthetic inputs for the single-GPU MoE layer, and the five workloads.
+"""Seeded synthetic inputs for the single-GPU MoE layer, and the named workloads.
 
 This module holds no arithmetic of the method: it only draws inputs. Both the
 HIP path (through its tests and the benchmark) and the CPU oracle read the same
@@ -7,9 +7,10 @@ tensors drawn here, so the two sides always see identical bits.
 Recipe (the pages' workloads are trained models on datasets, so seeded random
 tensors of the same shapes stand in for them):
   * every tensor has its own torch generator, seeded with seed*1000 + tensor id
-    (x=1, logits=2, Wg=3, W1=4, b1=5, W2=6, b2=7, dout=8);
+    (x=1, logits=2, Wg=3, W1=4, b1=5, W2=6, b2=7, dout=8, dgates=9; dgates is
+    an upstream gate gradient [k,S] for tests of the gate backward on its own);
   * x ~ N(0,1); logits ~ N(0,1) fp32; Wg, W1, b1, W2, b2 ~ N(0, 0.02) (0.02 is
-    the standard deviation); dout ~ N(0,1);
+    the standard deviation); dout ~ N(0,1); dgates ~ N(0,1) fp32;
   * draws are fp32, then rounded to bf16 (round to nearest even) when the
     workload's dtype is bf16; logits, Wg and gates stay fp32;
   * the skewed workloads add a per-expert bias b_e = 2 (e+1)^-1.1 to every
@@ -34,7 +35,7 @@ DT_BF16 = 1
 ACT_RELU = 0
 ACT_GELU = 1
 
-TENSOR_IDS = {"x": 1, "logits": 2, "Wg": 3, "W1": 4, "b1": 5, "W2": 6, "b2": 7, "dout": 8}
+TENSOR_IDS = {"x": 1, "logits": 2, "Wg": 3, "W1": 4, "b1": 5, "W2": 6, "b2": 7, "dout": 8, "dgates": 9}
 
 
 @dataclasses.dataclass(frozen=True)
@@ -65,11 +66,13 @@ class Workload:
         return 4 if self.dtype == DT_F32 else 2
 
 
-# The five workloads, smallest first.
+# The workloads, smallest first.
 TINY_F32 = Workload("tiny_f32_S256_M64_E4_k1_H128", S=256, M=64, E=4, k=1, H=128,
                     capacity_factor=1.0, dtype=DT_F32, act=ACT_RELU)
 GATED_BF16 = Workload("gated_bf16_S4096_M1024_E8_k2_H4096", S=4096, M=1024, E=8, k=2, H=4096,
                       capacity_factor=1.25, logits="gate")
+# the same layer trained: forward + backward, gate backward and load-balance loss included
+GATED_TRAIN_BF16 = GATED_BF16.replace(name="gated_train_bf16_S4096_M1024_E8_k2_H4096", backward=True)
 DSPR_BF16 = Workload("dspr_bf16_S8192_M2048_E16_k3_H8192", S=8192, M=2048, E=16, k=3, H=8192,
                      capacity_factor=0.0)
 FINE_BF16 = Workload("fine_bf16_S16384_M2048_E64_k6_H1408", S=16384, M=2048, E=64, k=6, H=1408,
@@ -77,7 +80,7 @@ FINE_BF16 = Workload("fine_bf16_S16384_M2048_E64_k6_H1408", S=16384, M=2048, E=6
 LARGE_BF16 = Workload("large_bf16_S32768_M4096_E128_k8_H1536", S=32768, M=4096, E=128, k=8, H=1536,
                       capacity_factor=-2.0, logits="zipf", backward=True)
 
-WORKLOADS = [TINY_F32, GATED_BF16, DSPR_BF16, FINE_BF16, LARGE_BF16]
+WORKLOADS = [TINY_F32, GATED_BF16, GATED_TRAIN_BF16, DSPR_BF16, FINE_BF16, LARGE_BF16]
 BY_NAME = {w.name: w for w in WORKLOADS}
 
 
