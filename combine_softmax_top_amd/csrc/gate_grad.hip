@@ -11,11 +11,11 @@
 //    partial per block; aux_finish_kernel adds the partials in a fixed order:
 //    l_aux = alpha * E / (k S^2) * sum_s q_s.
 //  - gate_wgrad_kernel: dWg[m][e] = sum_s x[s][m] dlogits[s][e]. A block owns
-//    64*VM columns of x, ET experts and one slice of the tokens; its four
-//    wavefronts take interleaved 16-token runs of each 64-token chunk (the
-//    chunk's dlogits staged in LDS), then add their sums in wavefront order.
-//    With more than one slice, each writes a partial [M, E] and
-//    wgrad_reduce_kernel adds them in slice order.
+//    64*VM columns of x, ET experts and one slice of the tokens; wavefront w
+//    takes tokens 16w .. 16w+15 of each 64-token chunk (the chunk's dlogits
+//    staged in LDS), then the four add their sums in wavefront order. With
+//    more than one slice, each writes a partial [M, E] and wgrad_reduce_kernel
+//    adds them in a fixed order.
 //  - gate_dx_kernel: dx[s] = sum of the kept dbuf rows (route order, fp32) +
 //    dlogits[s] . Wg^T, rounded once to the data type: the encode backward with
 //    the gate projection's share fused in. A block takes 32 tokens x 256
@@ -44,19 +44,35 @@ __device__ __forceinline__ float group_sum_f32(float v) {
     return v;
 }
 
+// Value of lane r of the calling lane's group of G lanes.
+template <int G, class T>
+__device__ __forceinline__ T group_bcast(T v, int r) {
+    if constexpr (G == 64) {
+        if constexpr (sizeof(T) == 4 && !__is_same(T, int)) return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), r));
+        else return __builtin_amdgcn_readlane(v, r);
+    } else {
+        return __shfl(v, r, G);
+    }
+}
+
 // Block = 256 threads, tokens [blockIdx.x * 64, +64); G lanes per token, expert
-// e = lane_in_group + G * j for j < EPL. caux = alpha * E / (k S^2) (0: no
-// auxiliary term; needed may then be NULL). partial[blockIdx.x] = sum of q_s.
-template <int G, int EPL>
+// e = lane_in_group + G * j for j < EPL. Group grp takes tokens grp, grp +
+// groups, ... of the tile, B at a time, and runs every step of the B tokens
+// side by side (all loads first, then each cross-lane reduction stage for all B
+// tokens), so that B independent shuffles or loads are in flight where one
+// token alone would wait on each. caux = alpha * E / (k S^2) (0: no auxiliary
+// term; needed may then be NULL). partial[blockIdx.x] = sum of q_s over the tile.
+template <int G, int EPL, int B>
 __global__ __launch_bounds__(256) void gate_bwd_kernel(const float *__restrict__ logits,
                                                        const int32_t *__restrict__ idx,
                                                        const float *__restrict__ dgates,
                                                        const int32_t *__restrict__ needed, float caux, int S,
                                                        int E, int k, float *__restrict__ dlogits,
                                                        double *__restrict__ partial) {
-    __shared__ double wsum[256 / G];
-    const int tid = threadIdx.x, gl = tid % G, grp = tid / G;
     constexpr int groups = 256 / G;
+    constexpr int NT = (kGbTile + groups - 1) / groups;  // tile tokens per group (the last may be absent)
+    __shared__ double wsum[groups];
+    const int tid = threadIdx.x, gl = tid % G, grp = tid / G;
     float nd[EPL];
 #pragma unroll
     for (int j = 0; j < EPL; ++j) {
@@ -64,64 +80,103 @@ __global__ __launch_bounds__(256) void gate_bwd_kernel(const float *__restrict__
         nd[j] = (needed != nullptr && e < E) ? static_cast<float>(needed[e]) : 0.f;
     }
     double qsum = 0.0;  // this group's tokens, in token order
-    for (int t = grp; t < kGbTile; t += groups) {
-        const int s = blockIdx.x * kGbTile + t;
-        if (s >= S) break;  // uniform across the G lanes of a group
-        const float *row = logits + static_cast<int64_t>(s) * E;
-        float v[EPL];
+    for (int i0 = 0; i0 < NT; i0 += B) {
+        float v[B][EPL], p[B][EPL], g[B][EPL], mx[B], sm[B], dot[B], q[B];
+        int re[B];
+        float rdg[B];
+        bool ok[B];
+        int srow[B];
 #pragma unroll
-        for (int j = 0; j < EPL; ++j) {
-            const int e = gl + G * j;
-            v[j] = e < E ? row[e] : -INFINITY;
+        for (int b = 0; b < B; ++b) {
+            const int t = grp + groups * (i0 + b);
+            const int s = blockIdx.x * kGbTile + t;
+            ok[b] = i0 + b < NT && t < kGbTile && s < S;  // uniform across the G lanes of a group
+            srow[b] = ok[b] ? s : 0;  // absent tokens compute on row 0 and store nothing
+            const float *row = logits + static_cast<int64_t>(srow[b]) * E;
+#pragma unroll
+            for (int j = 0; j < EPL; ++j) {
+                const int e = gl + G * j;
+                v[b][j] = e < E ? row[e] : -INFINITY;
+            }
+            // route r's (expert, dgate) is read by lane r of the group (k <= E <= G * EPL, and G >= k)
+            re[b] = -1;
+            rdg[b] = 0.f;
+            if (gl < k) {
+                const int64_t qi = static_cast<int64_t>(gl) * S + srow[b];
+                re[b] = idx[qi];
+                rdg[b] = dgates[qi];
+            }
         }
-        float mx = v[0];
 #pragma unroll
-        for (int j = 1; j < EPL; ++j) mx = fmaxf(mx, v[j]);
-        mx = group_max_f32<G>(mx);
-        float p[EPL], sum = 0.f;
+        for (int b = 0; b < B; ++b) {
+            mx[b] = v[b][0];
 #pragma unroll
-        for (int j = 0; j < EPL; ++j) {
-            p[j] = gl + G * j < E ? expf(v[j] - mx) : 0.f;
-            sum += p[j];
+            for (int j = 1; j < EPL; ++j) mx[b] = fmaxf(mx[b], v[b][j]);
         }
-        sum = group_sum_f32<G>(sum);
-        const float inv = 1.0f / sum;
-        float g[EPL];
 #pragma unroll
-        for (int j = 0; j < EPL; ++j) {
-            p[j] *= inv;
-            g[j] = caux * nd[j];
+        for (int off = G / 2; off > 0; off >>= 1)
+#pragma unroll
+            for (int b = 0; b < B; ++b) mx[b] = fmaxf(mx[b], __shfl_xor(mx[b], off, G));
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+            sm[b] = 0.f;
+#pragma unroll
+            for (int j = 0; j < EPL; ++j) {
+                p[b][j] = gl + G * j < E ? expf(v[b][j] - mx[b]) : 0.f;
+                sm[b] += p[b][j];
+            }
         }
-        // route r's (expert, dgate) is read by lane r of the group (k <= E <= G * EPL, and G >= k)
-        int my_e = -1;
-        float my_dg = 0.f;
-        if (gl < k) {
-            const int64_t q = static_cast<int64_t>(gl) * S + s;
-            my_e = idx[q];
-            my_dg = dgates[q];
+#pragma unroll
+        for (int off = G / 2; off > 0; off >>= 1)
+#pragma unroll
+            for (int b = 0; b < B; ++b) sm[b] += __shfl_xor(sm[b], off, G);
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+            const float inv = 1.0f / sm[b];
+#pragma unroll
+            for (int j = 0; j < EPL; ++j) {
+                p[b][j] *= inv;
+                g[b][j] = caux * nd[j];
+            }
         }
         for (int r = 0; r < k; ++r) {
-            const int er = __shfl(my_e, r, G);
-            const float dgr = __shfl(my_dg, r, G);
 #pragma unroll
-            for (int j = 0; j < EPL; ++j)
-                if (er == gl + G * j) g[j] += dgr;
-        }
-        float dot = 0.f, q = 0.f;
+            for (int b = 0; b < B; ++b) {
+                const int er = group_bcast<G>(re[b], r);
+                const float dgr = group_bcast<G>(rdg[b], r);
 #pragma unroll
-        for (int j = 0; j < EPL; ++j) {
-            dot += p[j] * g[j];
-            q += nd[j] * p[j];
+                for (int j = 0; j < EPL; ++j)
+                    if (er == gl + G * j) g[b][j] += dgr;
+            }
         }
-        dot = group_sum_f32<G>(dot);
-        q = group_sum_f32<G>(q);
-        float *drow = dlogits + static_cast<int64_t>(s) * E;
 #pragma unroll
-        for (int j = 0; j < EPL; ++j) {
-            const int e = gl + G * j;
-            if (e < E) drow[e] = p[j] * (g[j] - dot);
+        for (int b = 0; b < B; ++b) {
+            dot[b] = 0.f;
+            q[b] = 0.f;
+#pragma unroll
+            for (int j = 0; j < EPL; ++j) {
+                dot[b] += p[b][j] * g[b][j];
+                q[b] += nd[j] * p[b][j];
+            }
         }
-        qsum += static_cast<double>(q);
+#pragma unroll
+        for (int off = G / 2; off > 0; off >>= 1)
+#pragma unroll
+            for (int b = 0; b < B; ++b) {
+                dot[b] += __shfl_xor(dot[b], off, G);
+                q[b] += __shfl_xor(q[b], off, G);
+            }
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+            if (!ok[b]) continue;
+            float *drow = dlogits + static_cast<int64_t>(srow[b]) * E;
+#pragma unroll
+            for (int j = 0; j < EPL; ++j) {
+                const int e = gl + G * j;
+                if (e < E) drow[e] = p[b][j] * (g[b][j] - dot[b]);
+            }
+            qsum += static_cast<double>(q[b]);
+        }
     }
     if (partial == nullptr) return;
     if (gl == 0) wsum[grp] = qsum;
@@ -205,20 +260,30 @@ __global__ __launch_bounds__(256) void gate_wgrad_kernel(const void *__restrict_
             sdl[i] = (t < n && e0 + j < E) ? dlogits[static_cast<int64_t>(c0 + t) * E + e0 + j] : 0.f;
         }
         __syncthreads();
+        // wavefront w takes tokens 16w .. 16w+15 of the chunk, XB rows of x in flight at a time
+        constexpr int XB = VM * ET <= 32 ? 16 : 8;
         const int tb = wave * (kWgChunk / 4), te = min(n, tb + kWgChunk / 4);
-        for (int t = tb; t < te; ++t) {
-            float xv[VM];
-            load_x<BF16, VM>(x, static_cast<int64_t>(c0 + t) * M + m0, xv);
-            const float4 *d4 = reinterpret_cast<const float4 *>(sdl + t * ET);
+        for (int t0 = tb; t0 < te; t0 += XB) {
+            float xv[XB][VM];
 #pragma unroll
-            for (int j4 = 0; j4 < ET / 4; ++j4) {
-                const float4 d = d4[j4];
+            for (int u = 0; u < XB; ++u) {
+                const int t = min(t0 + u, te - 1);  // clamped: a repeated row is loaded, not used
+                load_x<BF16, VM>(x, static_cast<int64_t>(c0 + t) * M + m0, xv[u]);
+            }
 #pragma unroll
-                for (int v = 0; v < VM; ++v) {
-                    acc[v][4 * j4 + 0] = fmaf(xv[v], d.x, acc[v][4 * j4 + 0]);
-                    acc[v][4 * j4 + 1] = fmaf(xv[v], d.y, acc[v][4 * j4 + 1]);
-                    acc[v][4 * j4 + 2] = fmaf(xv[v], d.z, acc[v][4 * j4 + 2]);
-                    acc[v][4 * j4 + 3] = fmaf(xv[v], d.w, acc[v][4 * j4 + 3]);
+            for (int u = 0; u < XB; ++u) {
+                if (t0 + u >= te) break;
+                const float4 *d4 = reinterpret_cast<const float4 *>(sdl + (t0 + u) * ET);
+#pragma unroll
+                for (int j4 = 0; j4 < ET / 4; ++j4) {
+                    const float4 d = d4[j4];
+#pragma unroll
+                    for (int v = 0; v < VM; ++v) {
+                        acc[v][4 * j4 + 0] = fmaf(xv[u][v], d.x, acc[v][4 * j4 + 0]);
+                        acc[v][4 * j4 + 1] = fmaf(xv[u][v], d.y, acc[v][4 * j4 + 1]);
+                        acc[v][4 * j4 + 2] = fmaf(xv[u][v], d.z, acc[v][4 * j4 + 2]);
+                        acc[v][4 * j4 + 3] = fmaf(xv[u][v], d.w, acc[v][4 * j4 + 3]);
+                    }
                 }
             }
         }
@@ -245,15 +310,30 @@ __global__ __launch_bounds__(256) void gate_wgrad_kernel(const void *__restrict_
         }
 }
 
-// dWg[i] = sum over slices sp = 0..n-1 of partial[sp][i], in slice order.
+// dWg[i] = sum over the n slice partials partial[sp][i]. A block takes 64
+// consecutive outputs; wavefront w adds slices w, w + 4, w + 8, ... (8 loads
+// in flight), then wavefront 0 adds the four sums in wavefront order: a fixed
+// order for a given n.
 __global__ __launch_bounds__(256) void wgrad_reduce_kernel(const float *__restrict__ partial, int64_t count, int n,
                                                            float *__restrict__ dWg) {
-    for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < count;
-         i += static_cast<int64_t>(gridDim.x) * 256) {
-        float a = 0.f;
-        for (int sp = 0; sp < n; ++sp) a += partial[sp * count + i];
-        dWg[i] = a;
+    __shared__ float sh[3][64];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * 64 + lane;
+    const bool in = i < count;
+    float a = 0.f;
+    for (int sp0 = wave; sp0 < n; sp0 += 32) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int sp = sp0 + 4 * u;
+            v[u] = (in && sp < n) ? partial[sp * count + i] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) a += v[u];
     }
+    if (wave > 0) sh[wave - 1][lane] = a;
+    __syncthreads();
+    if (wave == 0 && in) dWg[i] = ((a + sh[0][lane]) + sh[1][lane]) + sh[2][lane];
 }
 
 // ------------------------------------------------------------- dx with the gate share
@@ -366,8 +446,11 @@ template <int G, int EPL>
 hipError_t gb_launch(const float *logits, const int32_t *idx, const float *dgates, const int32_t *needed, float caux,
                      int S, int E, int k, float *dlogits, double *partial, hipStream_t st) {
     const int nblk = (S + kGbTile - 1) / kGbTile;
-    hipLaunchKernelGGL((gate_bwd_kernel<G, EPL>), dim3(nblk), dim3(256), 0, st, logits, idx, dgates, needed, caux, S,
-                       E, k, dlogits, partial);
+    // rows in flight per group: all of the group's tile tokens, at most 32 logits per lane
+    constexpr int NT = (kGbTile + 256 / G - 1) / (256 / G);
+    constexpr int B = NT < 32 / EPL ? NT : 32 / EPL;
+    hipLaunchKernelGGL((gate_bwd_kernel<G, EPL, B>), dim3(nblk), dim3(256), 0, st, logits, idx, dgates, needed, caux,
+                       S, E, k, dlogits, partial);
     return hipGetLastError();
 }
 
@@ -472,8 +555,8 @@ hipError_t launch_gate_weight_grad(const moe_shape &s, const void *x, const floa
     }
     if (p.nsplit != 1) {  // several slices to add, or no token: dWg = 0
         const int64_t count = static_cast<int64_t>(M) * E;
-        const int blocks = static_cast<int>(std::min<int64_t>((count + 255) / 256, 4096));
-        hipLaunchKernelGGL(wgrad_reduce_kernel, dim3(blocks), dim3(256), 0, st, out, count, p.nsplit, dWg);
+        hipLaunchKernelGGL(wgrad_reduce_kernel, dim3(static_cast<unsigned>((count + 63) / 64)), dim3(256), 0, st, out,
+                           count, p.nsplit, dWg);
         err = hipGetLastError();
     }
     return err;
