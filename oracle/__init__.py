@@ -71,7 +71,7 @@ def lib():
                                          vp, vp, i64, _c_i64p, vp, vp, vp]
         L.oracle_expert_rows.restype = None
         L.oracle_decode.argtypes = [i32, i32, i32, i32, i32, ctypes.c_int, vp, _c_f32p, _c_i32p,
-                                    _c_i32p, i64, vp, vp]
+                                    _c_i32p, i64, vp, vp, vp]
         L.oracle_decode.restype = None
         L.oracle_backward_rows.argtypes = [i32, i32, i32, i32, i32, ctypes.c_int, ctypes.c_int, vp,
                                            vp, vp, vp, _c_f32p, vp, i64, _c_i64p, _c_i32p, vp, vp, vp]
@@ -235,8 +235,10 @@ def filled_rows(rt: Dict) -> np.ndarray:
                           or [np.zeros(0, np.int64)]).astype(np.int64)
 
 
-def decode(y: np.ndarray, rt: Dict, E: int, dtype: int, tokens: Optional[Sequence[int]] = None) -> np.ndarray:
-    """Gate-weighted combine; y is the [E*C, M] expert output (only kept rows are read)."""
+def decode(y: np.ndarray, rt: Dict, E: int, dtype: int, tokens: Optional[Sequence[int]] = None,
+           yres: Optional[np.ndarray] = None) -> np.ndarray:
+    """Gate-weighted combine; y is the [E*C, M] expert output (only kept rows are read).
+    yres: the Residual-MoE dense branch's output [S, M] (only the listed tokens' rows are read)."""
     y = _check(y, dtype)
     M = y.shape[1]
     k, S = rt["idx"].shape
@@ -247,15 +249,27 @@ def decode(y: np.ndarray, rt: Dict, E: int, dtype: int, tokens: Optional[Sequenc
         tok = np.ascontiguousarray(np.asarray(tokens, dtype=np.int64))
         n = tok.shape[0]
     out = np.empty((n, M), elem_dtype(dtype))
+    yr = None if yres is None else _check(yres, dtype, (S, M))
     lib().oracle_decode(S, M, E, k, C, dtype, _ptr(y), rt["gates"], rt["idx"], rt["loc"], n,
-                        _ptr(tok), _ptr(out))
+                        _ptr(tok), _ptr(yr), _ptr(out))
     return out
+
+
+def residual_mlp(x: np.ndarray, W1r, b1r, W2r, b2r, act_kind: int, dtype: int, tokens=None):
+    """Residual-MoE's dense branch: the FFN of the experts' form, with its own weights
+    (W1r [H, M], W2r [M, H]), over the listed tokens (all by default). Returns (h, y) compact."""
+    S = x.shape[0]
+    tok = np.arange(S, dtype=np.int64) if tokens is None else np.asarray(tokens, np.int64)
+    _, h, y = expert_rows(x, W1r[None], None if b1r is None else b1r[None], W2r[None],
+                          None if b2r is None else b2r[None], tok, S, act_kind, dtype, want_h=True)
+    return h, y
 
 
 def layer_forward(inp: Dict[str, np.ndarray], k: int, f: float, act_kind: int, dtype: int,
                   logits: Optional[np.ndarray] = None) -> Dict:
     """The whole forward for small shapes: returns route tables, buf, pre, h, y (full E*C rows,
-    padding rows of pre/h/y left zero) and out."""
+    padding rows of pre/h/y left zero) and out. With the Residual-MoE weights in inp (W1r, W2r,
+    and b1r/b2r when the biases are on) also h_r, y_r and out = MoE output + y_r."""
     x = inp["x"]
     if logits is None:
         logits = inp["logits"] if "logits" in inp else gate_logits(x, inp["Wg"], dtype)
@@ -271,8 +285,12 @@ def layer_forward(inp: Dict[str, np.ndarray], k: int, f: float, act_kind: int, d
     pre = np.zeros((E * rt["C"], H), et); pre[rows] = pre_r
     h = np.zeros((E * rt["C"], H), et); h[rows] = h_r
     y = np.zeros((E * rt["C"], M), et); y[rows] = y_r
-    out = decode(y, rt, E, dtype)
-    return dict(logits=logits, route=rt, buf=buf, pre=pre, h=h, y=y, out=out, rows=rows)
+    res = {}
+    if "W1r" in inp:
+        res["h_r"], res["y_r"] = residual_mlp(x, inp["W1r"], inp.get("b1r"), inp["W2r"], inp.get("b2r"), act_kind,
+                                              dtype)
+    out = decode(y, rt, E, dtype, yres=res.get("y_r"))
+    return dict(logits=logits, route=rt, buf=buf, pre=pre, h=h, y=y, out=out, rows=rows, **res)
 
 
 # ------------------------------------------------------------------ backward

@@ -47,6 +47,11 @@
  *    type; GELU is the exact erf form;
  *  - decode accumulates gate * y in fp32 in route order from +0 with separate
  *    multiply and add, then rounds to the data type; dropped routes add nothing;
+ *  - Residual-MoE: the dense branch is an FFN of the same form over every
+ *    token (its own W1r, b1r, W2r, b2r), its output y_r rounded to the data
+ *    type like an expert's, and decode adds y_r[s] in fp32 after the routes;
+ *    the MoE branch is gate-weighted as usual (the pages say only that the two
+ *    outputs are added);
  *  - backward: dy = g * dout (rounded to the data type), dgate = <dout, y>,
  *    dh = dy . W2[e], dpre = dh * act'(pre) rounded, dbuf = dpre . W1[e]
  *    rounded, dx = sum of dbuf over kept routes rounded; weight and bias
@@ -344,10 +349,14 @@ void oracle_expert_rows(int32_t M, int32_t H, int32_t E, int32_t C, int dtype, i
 /* out[s][m] = sum over kept routes r (in route order) of gates[r][s] * y[slot][m],
  * fp32 from +0 with separate multiply and add, then rounded to the data type.
  * y is the [E*C, M] expert output. tokens (may be NULL = all S) lists the
- * ntok tokens to produce; out is compact [ntok, M]. */
+ * ntok tokens to produce; out is compact [ntok, M].
+ * Residual-MoE (MoE training blog, part 1 section 1.2: every token also passes
+ * through one fixed dense MLP, and the two branches' outputs are added): with
+ * yres (the dense MLP's output [S, M] in the data type, indexed by token) the
+ * fp32 sum gains yres[s][m] after the routes, before the one rounding. */
 void oracle_decode(int32_t S, int32_t M, int32_t E, int32_t k, int32_t C, int dtype,
                    const void *y, const float *gates, const int32_t *idx, const int32_t *loc,
-                   int64_t ntok, const int64_t *tokens, void *out) {
+                   int64_t ntok, const int64_t *tokens, const void *yres, void *out) {
     (void)E;
     for (int64_t i = 0; i < ntok; ++i) {
         const int64_t s = tokens ? tokens[i] : i;
@@ -360,6 +369,7 @@ void oracle_decode(int32_t S, int32_t M, int32_t E, int32_t k, int32_t C, int dt
                 const float prod = gates[q] * (float)load_elem(y, dtype, row * M + m);
                 acc = acc + prod;
             }
+            if (yres != NULL) acc = acc + (float)load_elem(yres, dtype, s * M + m);
             store_elem(out, dtype, i * M + m, (double)acc);
         }
     }

@@ -629,3 +629,59 @@ def test_layer_backward_with_gate_matches_autograd():
         got = bw[n].astype(np.float64)
         assert np.abs(got - ref).max() / max(np.abs(ref).max(), 1e-30) < 2e-6, n
     assert bw["aux_loss"] == pytest.approx(float(_aux_loss_torch(p.detach(), rt["needed"], k, alpha)), rel=1e-6)
+
+
+# ---------------------------------------------------------------- Residual-MoE
+
+def _res_inputs(S, M, E, H, dtype, seed):
+    w = W.Workload("res", S=S, M=M, E=E, k=1, H=H, capacity_factor=1.0, dtype=dtype, residual=True)
+    return {k_: np_of(v) for k_, v in W.make_inputs(w, seed=seed).items()}
+
+
+@pytest.mark.parametrize("act", [W.ACT_GELU, W.ACT_RELU])
+def test_residual_single_expert_is_sum_of_two_mlps(act):
+    # E = 1, k = 1, f = 0: every token's gate is softmax over one logit = 1 and nothing drops, so
+    # the layer is MLP_expert(x) + MLP_dense(x), each rounded to fp32 once, then their sum once
+    S, M, H = 40, 16, 24
+    inp = _res_inputs(S, M, 1, H, W.DT_F32, 3)
+    fw = oracle.layer_forward(inp, 1, 0.0, act, W.DT_F32)
+    x64 = torch.from_numpy(inp["x"]).double()
+    e = _torch_mlp(x64, *(torch.from_numpy(inp[n][0]).double() for n in ("W1", "b1", "W2", "b2")), act)
+    r = _torch_mlp(x64, *(torch.from_numpy(inp[n]).double() for n in ("W1r", "b1r", "W2r", "b2r")), act)
+    want = (e + r).numpy()
+    got = fw["out"].astype(np.float64)
+    assert np.abs(got - want).max() <= 4 * np.spacing(np.abs(want).astype(np.float32)).max()
+    assert np.abs(fw["y_r"].astype(np.float64) - r.numpy()).max() <= 2e-6 * np.abs(r.numpy()).max()
+
+
+def test_residual_branch_is_the_whole_output_of_dropped_tokens():
+    # ties send every token to the same experts; capacity keeps a few, and a token whose routes
+    # are all dropped gets exactly the dense branch's output (0 + y_r rounds to y_r)
+    S, M, E, H = 64, 16, 4, 16
+    for dtype in (W.DT_F32, W.DT_BF16):
+        inp = _res_inputs(S, M, E, H, dtype, 5)
+        logits = np.zeros((S, E), np.float32)
+        fw = oracle.layer_forward(inp, 1, 0.25, W.ACT_GELU, dtype, logits=logits)
+        rt = fw["route"]
+        dropped = np.nonzero(rt["loc"][0] >= rt["C"])[0]
+        assert len(dropped) == S - rt["C"] > 0
+        assert np.array_equal(fw["out"][dropped], fw["y_r"][dropped])
+        # kept tokens: the MoE branch is there too
+        kept = np.nonzero(rt["loc"][0] < rt["C"])[0]
+        assert not np.array_equal(fw["out"][kept], fw["y_r"][kept])
+
+
+def test_residual_branch_ignores_routing():
+    # the dense branch sees every token the same way whatever the gate does
+    S, M, E, H = 48, 16, 4, 32
+    inp = _res_inputs(S, M, E, H, W.DT_BF16, 9)
+    a = oracle.layer_forward(inp, 1, 1.0, W.ACT_GELU, W.DT_BF16,
+                             logits=np.random.default_rng(1).standard_normal((S, E)).astype(np.float32))
+    b = oracle.layer_forward(inp, 1, 0.5, W.ACT_GELU, W.DT_BF16,
+                             logits=np.random.default_rng(2).standard_normal((S, E)).astype(np.float32))
+    assert np.array_equal(a["y_r"], b["y_r"])
+    x64 = torch.from_numpy(f32_of(inp["x"])).double()
+    r = _torch_mlp(x64, *(torch.from_numpy(f32_of(inp[n])).double() for n in ("W1r", "b1r", "W2r", "b2r")),
+                   W.ACT_GELU).numpy()
+    # h_r and y_r are bf16: within a few bf16 ulps of the fp64 MLP
+    assert np.abs(f32_of(a["y_r"]) - r).max() <= 2 ** -6 * np.abs(r).max()

@@ -7,10 +7,12 @@ tensors drawn here, so the two sides always see identical bits.
 Recipe (the pages' workloads are trained models on datasets, so seeded random
 tensors of the same shapes stand in for them):
   * every tensor has its own torch generator, seeded with seed*1000 + tensor id
-    (x=1, logits=2, Wg=3, W1=4, b1=5, W2=6, b2=7, dout=8, dgates=9; dgates is
-    an upstream gate gradient [k,S] for tests of the gate backward on its own);
-  * x ~ N(0,1); logits ~ N(0,1) fp32; Wg, W1, b1, W2, b2 ~ N(0, 0.02) (0.02 is
-    the standard deviation); dout ~ N(0,1); dgates ~ N(0,1) fp32;
+    (x=1, logits=2, Wg=3, W1=4, b1=5, W2=6, b2=7, dout=8, dgates=9, W1r=10,
+    b1r=11, W2r=12, b2r=13; dgates is an upstream gate gradient [k,S] for tests
+    of the gate backward on its own; W1r..b2r are the Residual-MoE dense MLP);
+  * x ~ N(0,1); logits ~ N(0,1) fp32; Wg, W1, b1, W2, b2, W1r, b1r, W2r, b2r ~
+    N(0, 0.02) (0.02 is the standard deviation); dout ~ N(0,1); dgates ~ N(0,1)
+    fp32;
   * draws are fp32, then rounded to bf16 (round to nearest even) when the
     workload's dtype is bf16; logits, Wg and gates stay fp32;
   * the skewed workloads add a per-expert bias b_e = 2 (e+1)^-1.1 to every
@@ -35,7 +37,8 @@ DT_BF16 = 1
 ACT_RELU = 0
 ACT_GELU = 1
 
-TENSOR_IDS = {"x": 1, "logits": 2, "Wg": 3, "W1": 4, "b1": 5, "W2": 6, "b2": 7, "dout": 8, "dgates": 9}
+TENSOR_IDS = {"x": 1, "logits": 2, "Wg": 3, "W1": 4, "b1": 5, "W2": 6, "b2": 7, "dout": 8, "dgates": 9,
+              "W1r": 10, "b1r": 11, "W2r": 12, "b2r": 13}
 
 
 @dataclasses.dataclass(frozen=True)
@@ -53,6 +56,7 @@ class Workload:
     has_fc2_bias: bool = True
     logits: str = "normal"  # "normal" | "gate" (x @ Wg) | "zipf" (normal + Zipf(1.1) bias x2)
     backward: bool = False
+    residual: bool = False  # Residual-MoE: a dense MLP branch added to the MoE output
 
     def replace(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
@@ -73,6 +77,10 @@ GATED_BF16 = Workload("gated_bf16_S4096_M1024_E8_k2_H4096", S=4096, M=1024, E=8,
                       capacity_factor=1.25, logits="gate")
 # the same layer trained: forward + backward, gate backward and load-balance loss included
 GATED_TRAIN_BF16 = GATED_BF16.replace(name="gated_train_bf16_S4096_M1024_E8_k2_H4096", backward=True)
+# Residual-MoE at the same size: top-1 expert plus the dense MLP branch (the MoE training
+# blog's PR-MoE layers use top-1 gating with the residual branch)
+RESIDUAL_BF16 = Workload("residual_bf16_S4096_M1024_E8_k1_H4096", S=4096, M=1024, E=8, k=1, H=4096,
+                         capacity_factor=1.25, logits="gate", residual=True)
 DSPR_BF16 = Workload("dspr_bf16_S8192_M2048_E16_k3_H8192", S=8192, M=2048, E=16, k=3, H=8192,
                      capacity_factor=0.0)
 FINE_BF16 = Workload("fine_bf16_S16384_M2048_E64_k6_H1408", S=16384, M=2048, E=64, k=6, H=1408,
@@ -80,7 +88,7 @@ FINE_BF16 = Workload("fine_bf16_S16384_M2048_E64_k6_H1408", S=16384, M=2048, E=6
 LARGE_BF16 = Workload("large_bf16_S32768_M4096_E128_k8_H1536", S=32768, M=4096, E=128, k=8, H=1536,
                       capacity_factor=-2.0, logits="zipf", backward=True)
 
-WORKLOADS = [TINY_F32, GATED_BF16, GATED_TRAIN_BF16, DSPR_BF16, FINE_BF16, LARGE_BF16]
+WORKLOADS = [TINY_F32, GATED_BF16, GATED_TRAIN_BF16, RESIDUAL_BF16, DSPR_BF16, FINE_BF16, LARGE_BF16]
 BY_NAME = {w.name: w for w in WORKLOADS}
 
 
@@ -109,7 +117,9 @@ def make_inputs(w: Workload, seed: int = 0, device="cpu", with_dout: Optional[bo
 
     Returns a dict with x [S,M], W1 [E,H,M], W2 [E,M,H], b1 [E,H] / b2 [E,M]
     (absent when the bias is off), and either logits [S,E] fp32 or Wg [M,E]
-    fp32 (gate-projected workloads), plus dout [S,M] when a backward is asked.
+    fp32 (gate-projected workloads), the dense branch W1r [H,M], W2r [M,H],
+    b1r [H], b2r [M] for Residual-MoE workloads, plus dout [S,M] when a
+    backward is asked.
     """
     dt = w.torch_dtype
     out: Dict[str, torch.Tensor] = {}
@@ -127,6 +137,13 @@ def make_inputs(w: Workload, seed: int = 0, device="cpu", with_dout: Optional[bo
         out["b1"] = normal((w.E, w.H), seed, "b1", 0.02, device=device).to(dt)
     if w.has_fc2_bias:
         out["b2"] = normal((w.E, w.M), seed, "b2", 0.02, device=device).to(dt)
+    if w.residual:
+        out["W1r"] = normal((w.H, w.M), seed, "W1r", 0.02, device=device).to(dt)
+        out["W2r"] = normal((w.M, w.H), seed, "W2r", 0.02, device=device).to(dt)
+        if w.has_fc1_bias:
+            out["b1r"] = normal((w.H,), seed, "b1r", 0.02, device=device).to(dt)
+        if w.has_fc2_bias:
+            out["b2r"] = normal((w.M,), seed, "b2r", 0.02, device=device).to(dt)
     if with_dout if with_dout is not None else w.backward:
         out["dout"] = normal((w.S, w.M), seed, "dout", device=device).to(dt)
     return out
