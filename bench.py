@@ -4,7 +4,8 @@ One step = one pass of the whole layer over one batch of synthetic input that is
 already resident in HBM: for the default workload (S=4096 tokens, M=1024, E=8
 experts, top-2, H=4096, bf16, logits projected from x by an fp32 gate matrix,
 capacity_factor 1.25) that is gate projection -> route -> encode -> fc1 -> fc2
--> decode; workloads with a backward add the backward of decode, FFN, encode
+-> decode (Residual-MoE workloads add the dense MLP branch over all tokens,
+summed into decode); workloads with a backward add the backward of decode, FFN, encode
 and the gate (dlogits through the softmax, the 0.01 load-balance loss, and for
 a projected gate dWg and the projection's share of dx). The timed region is exactly --steps calls of the fused C-ABI entry
 points, bracketed by synchronisations.
@@ -107,8 +108,11 @@ def algorithmic(w, C, kept):
         "encode": ("bytes", S * M * b + E * C * M * b + 8 * k * S),
         "fc1": ("flops", 2 * M * H * kept),
         "fc2": ("flops", 2 * M * H * kept),
-        "decode": ("bytes", kept * M * b + S * M * b + 12 * k * S),
+        "decode": ("bytes", kept * M * b + S * M * b + 12 * k * S + (S * M * b if w.residual else 0)),
     }
+    if w.residual:
+        # the dense branch: fc1 and fc2 over all S tokens
+        st["res_ffn"] = ("flops", 4 * M * H * S)
     if w.logits == "gate":
         st["gate"] = ("bytes", S * M * b + 4 * M * E + 4 * S * E)
     if w.backward:
@@ -201,7 +205,8 @@ def main():
     inp = W.make_inputs(w, seed=0, device=dev)
     s = moe.Shape.of(w)
     gate = w.logits == "gate"
-    bufs = moe.alloc_forward(s, dev, training=w.backward, gate_projection=gate)
+    bufs = moe.alloc_forward(s, dev, training=w.backward, gate_projection=gate, residual=w.residual)
+    res = {n: inp.get(n) for n in ("W1r", "b1r", "W2r", "b2r")} if w.residual else None
     grads = moe.alloc_backward(s, dev, gate=True, gate_projection=gate) if w.backward else None
     x, W1, W2, b1, b2 = inp["x"], inp["W1"], inp["W2"], inp.get("b1"), inp.get("b2")
     logits_in, Wg = (None, inp["Wg"]) if gate else (inp["logits"], None)
@@ -213,7 +218,7 @@ def main():
         moe.layer_backward(s, bufs, inp["dout"], W1, W2, grads=grads, logits=logits_bwd, x=x, Wg=Wg)
 
     def step():
-        moe.layer_forward(s, x, W1, b1, W2, b2, logits=logits_in, Wg=Wg, bufs=bufs)
+        moe.layer_forward(s, x, W1, b1, W2, b2, logits=logits_in, Wg=Wg, bufs=bufs, residual=res)
         if w.backward:
             backward()
 
@@ -235,7 +240,8 @@ def main():
 
     # ---- per-stage HIP-event timing on the library's stream
     stream = torch.cuda.current_stream()
-    names = (["gate"] if gate else []) + ["route", "encode", "fc1", "fc2", "decode"] + (
+    names = (["gate"] if gate else []) + ["route", "encode", "fc1", "fc2"] + (["res_ffn"] if w.residual else []) + [
+        "decode"] + (
         ["backward", "gate_bwd"] + (["gate_wgrad"] if gate else []) if w.backward else [])
     ev = {n: [] for n in names}
     lg = bufs["logits"] if gate else logits_in
@@ -280,8 +286,15 @@ def main():
         ("encode", lambda: moe.moe_encode(s, x, b["idx"], b["loc"], b["fill"], b["capacity"], b["buf"])),
         ("fc1", lambda: moe.moe_expert_fc1(s, b["buf"], W1, b1, b["fill"], b["capacity"], b["pre"], b["h"])),
         ("fc2", lambda: moe.moe_expert_fc2(s, b["h"], W2, b2, b["fill"], b["capacity"], b["y"])),
-        ("decode", lambda: moe.moe_decode(s, b["y"], b["gates"], b["idx"], b["loc"], b["capacity"], b["out"])),
     ]
+    if w.residual:
+        stage_fns.append(("res_ffn", lambda: moe.moe_residual_ffn(s, x, res["W1r"], res["b1r"], res["W2r"], res["b2r"],
+                                                                  b["h_r"], b["y_r"], b["ws"])))
+        stage_fns.append(("decode", lambda: moe.moe_decode_residual(s, b["y"], b["gates"], b["idx"], b["loc"],
+                                                                    b["capacity"], b["y_r"], b["out"])))
+    else:
+        stage_fns.append(("decode", lambda: moe.moe_decode(s, b["y"], b["gates"], b["idx"], b["loc"], b["capacity"],
+                                                           b["out"])))
     if w.backward:
         stage_fns.append(("backward", backward))
         stage_fns.append(("gate_bwd", lambda: moe.moe_gate_backward(s, lg, b["idx"], grads["dgates"], b["needed"],
@@ -308,7 +321,8 @@ def main():
         r["algorithmic_" + kind] = amount
         stages[n] = r
         log(f"[bench] stage {n:9s} {ms:9.4f} ms  {r['achieved']:10.2f} {r['unit']}  ({100 * r['frac']:.1f}% of peak)")
-    dominant = max((n for n in names if n != "backward"), key=lambda n: stages[n]["ms"])
+    # one-kernel stages only (the fused backward and the dense branch are several launches)
+    dominant = max((n for n in names if n not in ("backward", "res_ffn")), key=lambda n: stages[n]["ms"])
     d = stages[dominant]
     roofline = dict(kernel=dominant, bound=d["bound"], achieved=d["achieved"], peak=d["peak"], unit=d["unit"],
                     frac=d["frac"], traffic=recorded_traffic(dominant, w.name))
@@ -326,7 +340,7 @@ def main():
         config=dict(workload=w.name, S=w.S, M=w.M, E=w.E, k=w.k, H=w.H, capacity_factor=w.capacity_factor,
                     act="gelu" if w.act == W.ACT_GELU else "relu", biases=[w.has_fc1_bias, w.has_fc2_bias],
                     logits=w.logits, backward=w.backward, C=C, kept_routes=kept, parallelism="single-gpu",
-                    aux_coef=moe.AUX_COEF if w.backward else None),
+                    aux_coef=moe.AUX_COEF if w.backward else None, residual=w.residual),
         roofline=roofline, stages=stages, cpu_baseline=cpu,
     )
     print(json.dumps(line), flush=True)

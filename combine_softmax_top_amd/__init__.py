@@ -83,6 +83,9 @@ _SIGS = {
     "moe_expert_fc2": [_SP, _P, _P, _P, _P, _P, _P, _P],
     "moe_decode": [_SP, _P, _P, _P, _P, _P, _P, _P],
     "moe_layer_forward": [_SP] + [_P] * 21 + [ctypes.c_size_t, _P],
+    "moe_residual_ffn": [_SP] + [_P] * 8 + [ctypes.c_size_t, _P],
+    "moe_decode_residual": [_SP] + [_P] * 8,
+    "moe_residual_layer_forward": [_SP] + [_P] * 27 + [ctypes.c_size_t, _P],
     "moe_gate_backward": [_SP, _P, _P, _P, _P, ctypes.c_double, _P, _P, _P, ctypes.c_size_t, _P],
     "moe_gate_weight_grad": [_SP, _P, _P, _P, _P, ctypes.c_size_t, _P],
     "moe_layer_backward": [_SP] + [_P] * 23 + [ctypes.c_double] + [_P] * 6 + [ctypes.c_size_t, _P],
@@ -178,6 +181,26 @@ def _ws_args(ws):
     return _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size()
 
 
+def moe_residual_ffn(shape: Shape, x, W1r, b1r, W2r, b2r, h_r, y_r, ws, stream=None) -> None:
+    _check(_lib.moe_residual_ffn(ctypes.byref(shape.c()), _ptr(x), _ptr(W1r), _ptr(b1r), _ptr(W2r), _ptr(b2r),
+                                 _ptr(h_r), _ptr(y_r), *_ws_args(ws), _stream(stream)))
+
+
+def moe_decode_residual(shape: Shape, y, gates, idx, loc, capacity, y_r, out, stream=None) -> None:
+    _check(_lib.moe_decode_residual(ctypes.byref(shape.c()), _ptr(y), _ptr(gates), _ptr(idx), _ptr(loc),
+                                    _ptr(capacity), _ptr(y_r), _ptr(out), _stream(stream)))
+
+
+def moe_residual_layer_forward(shape: Shape, x, logits_in, Wg, logits_out, W1, b1, W2, b2, W1r, b1r, W2r, b2r,
+                               idx, loc, gates, needed, fill, capacity, slot_route, buf, pre, h, y, h_r, y_r, out, ws,
+                               stream=None) -> None:
+    _check(_lib.moe_residual_layer_forward(
+        ctypes.byref(shape.c()), _ptr(x), _ptr(logits_in), _ptr(Wg), _ptr(logits_out), _ptr(W1), _ptr(b1), _ptr(W2),
+        _ptr(b2), _ptr(W1r), _ptr(b1r), _ptr(W2r), _ptr(b2r), _ptr(idx), _ptr(loc), _ptr(gates), _ptr(needed),
+        _ptr(fill), _ptr(capacity), _ptr(slot_route), _ptr(buf), _ptr(pre), _ptr(h), _ptr(y), _ptr(h_r), _ptr(y_r),
+        _ptr(out), *_ws_args(ws), _stream(stream)))
+
+
 def moe_gate_backward(shape: Shape, logits, idx, dgates, needed, aux_coef, dlogits, aux_loss, ws,
                       stream=None) -> None:
     _check(_lib.moe_gate_backward(ctypes.byref(shape.c()), _ptr(logits), _ptr(idx), _ptr(dgates), _ptr(needed),
@@ -211,9 +234,10 @@ def moe_layer_backward(shape: Shape, dout, buf, pre, h, y, gates, idx, loc, fill
 # ---------------------------------------------------------------- buffers
 
 def alloc_forward(shape: Shape, device="cuda", training: bool = False,
-                  gate_projection: bool = False) -> Dict[str, torch.Tensor]:
+                  gate_projection: bool = False, residual: bool = False) -> Dict[str, torch.Tensor]:
     """Allocate every output and scratch buffer the forward writes, sized with the host
-    capacity bound (torch.empty: contents undefined until the library writes them)."""
+    capacity bound (torch.empty: contents undefined until the library writes them);
+    residual adds the dense branch's h_r [S, H] and y_r [S, M]."""
     S, M, E, k, H = shape.S, shape.M, shape.E, shape.k, shape.H
     cmax = moe_capacity_bound(shape)
     dt = shape.torch_dtype
@@ -231,17 +255,30 @@ def alloc_forward(shape: Shape, device="cuda", training: bool = False,
     )
     bufs["pre"] = torch.empty(E * cmax, H, dtype=dt, device=device) if training else None
     bufs["logits"] = torch.empty(S, E, dtype=torch.float32, device=device) if gate_projection else None
+    bufs["h_r"] = torch.empty(S, H, dtype=dt, device=device) if residual else None
+    bufs["y_r"] = torch.empty(S, M, dtype=dt, device=device) if residual else None
     return bufs
 
 
-def layer_forward(shape: Shape, x, W1, b1, W2, b2, logits=None, Wg=None, bufs=None, training=False, stream=None):
-    """Run the fused forward into ``bufs`` (allocated if None) and return them."""
+def layer_forward(shape: Shape, x, W1, b1, W2, b2, logits=None, Wg=None, bufs=None, training=False,
+                  residual=None, stream=None):
+    """Run the fused forward into ``bufs`` (allocated if None) and return them. ``residual``:
+    the Residual-MoE dense branch's weights as a dict W1r, b1r, W2r, b2r (biases may be None)."""
     if bufs is None:
-        bufs = alloc_forward(shape, x.device, training=training, gate_projection=Wg is not None)
-    moe_layer_forward(shape, x, logits, Wg, bufs["logits"] if Wg is not None else None, W1, b1, W2, b2,
-                      bufs["idx"], bufs["loc"], bufs["gates"], bufs["needed"], bufs["fill"], bufs["capacity"],
-                      bufs["slot_route"], bufs["buf"], bufs["pre"], bufs["h"], bufs["y"], bufs["out"], bufs["ws"],
-                      stream)
+        bufs = alloc_forward(shape, x.device, training=training, gate_projection=Wg is not None,
+                             residual=residual is not None)
+    lo = bufs["logits"] if Wg is not None else None
+    if residual is None:
+        moe_layer_forward(shape, x, logits, Wg, lo, W1, b1, W2, b2,
+                          bufs["idx"], bufs["loc"], bufs["gates"], bufs["needed"], bufs["fill"], bufs["capacity"],
+                          bufs["slot_route"], bufs["buf"], bufs["pre"], bufs["h"], bufs["y"], bufs["out"], bufs["ws"],
+                          stream)
+    else:
+        moe_residual_layer_forward(shape, x, logits, Wg, lo, W1, b1, W2, b2, residual["W1r"], residual.get("b1r"),
+                                   residual["W2r"], residual.get("b2r"), bufs["idx"], bufs["loc"], bufs["gates"],
+                                   bufs["needed"], bufs["fill"], bufs["capacity"], bufs["slot_route"], bufs["buf"],
+                                   bufs["pre"], bufs["h"], bufs["y"], bufs["h_r"], bufs["y_r"], bufs["out"],
+                                   bufs["ws"], stream)
     return bufs
 
 

@@ -121,13 +121,15 @@ struct Vec<false> {  // 4 fp32 in a uint4
 
 // out[s] = sum over kept routes r (in order) of g_r * rows[slot_r], fp32 from +0,
 // multiply and add separately rounded. UNIT: g_r = 1 and the multiply is
-// skipped (encode backward: dx = sum of dbuf rows).
-template <bool BF16, bool UNIT>
+// skipped (encode backward: dx = sum of dbuf rows). RES: Residual-MoE, the
+// dense branch's row yres[s] is added after the routes, before the rounding.
+template <bool BF16, bool UNIT, bool RES>
 __global__ __launch_bounds__(kThreads) void gather_sum_kernel(const uint4 *__restrict__ rows,
                                                               const float *__restrict__ gates,
                                                               const int32_t *__restrict__ idx,
                                                               const int32_t *__restrict__ loc,
                                                               const int32_t *__restrict__ cap,
+                                                              const uint4 *__restrict__ yres,
                                                               uint4 *__restrict__ out, int S, int k, int V) {
 #pragma clang fp contract(off)
     using VT = Vec<BF16>;
@@ -164,6 +166,12 @@ __global__ __launch_bounds__(kThreads) void gather_sum_kernel(const uint4 *__res
 #pragma unroll
                     for (int i = 0; i < N; ++i) acc[i] = UNIT ? acc[i] + f[i] : acc[i] + gr[u] * f[i];
                 }
+            }
+            if constexpr (RES) {
+                float f[N];
+                VT::unpack(yres[s * V + v], f);
+#pragma unroll
+                for (int i = 0; i < N; ++i) acc[i] = acc[i] + f[i];
             }
             out[s * V + v] = VT::pack(acc);
         }
@@ -492,30 +500,61 @@ hipError_t launch_encode(const moe_shape &s, const void *x, const int32_t *idx, 
     return hipGetLastError();
 }
 
+template <bool BF16>
+static void decode_dispatch(bool unit, bool res, int grid, hipStream_t st, const uint4 *Y, const float *gates,
+                            const int32_t *idx, const int32_t *loc, const int32_t *cap, const uint4 *R, uint4 *O, int S,
+                            int k, int V) {
+    if (unit)
+        hipLaunchKernelGGL((gather_sum_kernel<BF16, true, false>), dim3(grid), dim3(kThreads), 0, st, Y, gates, idx,
+                           loc, cap, R, O, S, k, V);
+    else if (res)
+        hipLaunchKernelGGL((gather_sum_kernel<BF16, false, true>), dim3(grid), dim3(kThreads), 0, st, Y, gates, idx,
+                           loc, cap, R, O, S, k, V);
+    else
+        hipLaunchKernelGGL((gather_sum_kernel<BF16, false, false>), dim3(grid), dim3(kThreads), 0, st, Y, gates, idx,
+                           loc, cap, R, O, S, k, V);
+}
+
 hipError_t launch_decode(const moe_shape &s, const void *y, const float *gates, const int32_t *idx,
-                         const int32_t *loc, const int32_t *cap, void *out, bool unit_gates, hipStream_t st) {
+                         const int32_t *loc, const int32_t *cap, void *out, bool unit_gates, hipStream_t st,
+                         const void *yres) {
     if (s.S == 0) return hipSuccess;
     const int eb = s.dtype == MOE_DT_BF16 ? 2 : 4;
     const int V = s.M * eb / 16;
     const int grid = grid_for(s.S);
     auto Y = static_cast<const uint4 *>(y);
+    auto R = static_cast<const uint4 *>(yres);
     auto O = static_cast<uint4 *>(out);
-    if (s.dtype == MOE_DT_BF16) {
-        if (unit_gates)
-            hipLaunchKernelGGL((gather_sum_kernel<true, true>), dim3(grid), dim3(kThreads), 0, st, Y, gates, idx, loc,
-                               cap, O, s.S, s.k, V);
-        else
-            hipLaunchKernelGGL((gather_sum_kernel<true, false>), dim3(grid), dim3(kThreads), 0, st, Y, gates, idx, loc,
-                               cap, O, s.S, s.k, V);
-    } else {
-        if (unit_gates)
-            hipLaunchKernelGGL((gather_sum_kernel<false, true>), dim3(grid), dim3(kThreads), 0, st, Y, gates, idx, loc,
-                               cap, O, s.S, s.k, V);
-        else
-            hipLaunchKernelGGL((gather_sum_kernel<false, false>), dim3(grid), dim3(kThreads), 0, st, Y, gates, idx,
-                               loc, cap, O, s.S, s.k, V);
-    }
+    const bool res = yres != nullptr;
+    if (s.dtype == MOE_DT_BF16)
+        decode_dispatch<true>(unit_gates, res, grid, st, Y, gates, idx, loc, cap, R, O, s.S, s.k, V);
+    else
+        decode_dispatch<false>(unit_gates, res, grid, st, Y, gates, idx, loc, cap, R, O, s.S, s.k, V);
     return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- Residual-MoE dense branch
+
+// The grouped GEMMs read an expert's row count and the capacity from device
+// memory; the dense branch is one "expert" whose rows are all S tokens.
+__global__ void set_dense_rows_kernel(int32_t *rows, int S) {
+    if (threadIdx.x == 0) {
+        rows[0] = S;  // fill[0]
+        rows[1] = S;  // capacity
+    }
+}
+
+hipError_t launch_residual_ffn(const moe_shape &s, const void *x, const void *W1r, const void *b1r, const void *W2r,
+                               const void *b2r, void *h_r, void *y_r, int32_t *dense_rows, hipStream_t st) {
+    if (s.S == 0) return hipSuccess;
+    hipLaunchKernelGGL(set_dense_rows_kernel, dim3(1), dim3(64), 0, st, dense_rows, s.S);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    moe_shape d = s;
+    d.E = 1;
+    if ((err = launch_fc1(d, x, W1r, b1r, dense_rows, dense_rows + 1, nullptr, h_r, s.S, st)) != hipSuccess)
+        return err;
+    return launch_fc2(d, h_r, W2r, b2r, dense_rows, dense_rows + 1, y_r, s.S, st);
 }
 
 hipError_t launch_decode_bwd(const moe_shape &s, const void *dout, const void *y, const float *gates,

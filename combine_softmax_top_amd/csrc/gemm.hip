@@ -26,6 +26,8 @@
 // fp32 (MOE_DT_F32) uses a plain LDS-tiled SIMT kernel with the same maths.
 #include <cstdlib>
 
+#include <algorithm>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -1122,10 +1124,15 @@ hipError_t big_launch(int act, const void *A, const void *B, void *D, int N, int
 
 // Forward-product tile configuration. 256 x 256 tiles (eight wavefronts, one
 // workgroup per CU) halve the operand traffic per flop of 128 x 128 tiles (four
-// wavefronts, two workgroups per CU), and win on every measured shape except
-// short-K products: with K <= 1024 a tile's fixed cost (prologue loads and the
-// epilogue) is a large share of its time, and two independent workgroups per
-// CU overlap one's epilogue with the other's MFMAs. MOE_GEMM_CFG overrides the
+// wavefronts, two workgroups per CU), and win where there are enough of them:
+// short-K products (K <= 1024) lose, because a tile's fixed cost (prologue
+// loads and the epilogue) is a large share of its time and two independent
+// workgroups per CU overlap one's epilogue with the other's MFMAs; and so do
+// products with fewer than 128 large tiles (half the CUs), where 128 x 128
+// tiles keep four times as many workgroups busy (measured: top-1 fc2 at S=4096,
+// M=1024, E=8, H=4096, 64 large tiles, 86 -> 55 us; the top-2 layer's 128 large
+// tiles still favour 256 x 256, 96 vs 105 us). rows_hint bounds the filled rows
+// over all experts (k*S, or S for a dense product). MOE_GEMM_CFG overrides the
 // choice for tuning (1 = 256 x 256, 2 = 256 x 128, 3 = 128 x 128).
 static int gemm_cfg_override() {
     static const int v = [] {
@@ -1135,13 +1142,18 @@ static int gemm_cfg_override() {
     return v;
 }
 
+static int default_cfg(int N, int K, int64_t rows_hint) {
+    const int64_t big_tiles = ((rows_hint + 255) / 256) * ((N + 255) / 256);
+    return (K <= 1024 || big_tiles < 128) ? 3 : 1;
+}
+
 // Backward data products, weights read n-contiguous: same tile choice as the
 // forward products.
 template <int EPI>
 hipError_t bwd_data_launch(int act, const void *A, const void *B, void *D, int N, int K, int E, const int32_t *fill,
-                           const int32_t *cap, const void *aux, hipStream_t st) {
+                           const int32_t *cap, const void *aux, int64_t rows_hint, hipStream_t st) {
     int cfg = gemm_cfg_override();
-    if (cfg < 1 || cfg > 3) cfg = K <= 1024 ? 3 : 1;
+    if (cfg < 1 || cfg > 3) cfg = default_cfg(N, K, rows_hint);
     switch (cfg) {
     case 1: return big_launch<256, 256, 512, EPI, true>(act, A, B, D, N, K, E, fill, cap, nullptr, nullptr, st, aux);
     case 2: return big_launch<256, 128, 256, EPI, true>(act, A, B, D, N, K, E, fill, cap, nullptr, nullptr, st, aux);
@@ -1150,11 +1162,10 @@ hipError_t bwd_data_launch(int act, const void *A, const void *B, void *D, int N
 }
 
 template <int EPI>
-hipError_t fwd_launch(int act, const void *A, const void *B, void *D, int N, int K, int cmax, int E,
+hipError_t fwd_launch(int act, const void *A, const void *B, void *D, int N, int K, int64_t rows_hint, int E,
                       const int32_t *fill, const int32_t *cap, const void *bias, void *pre_out, hipStream_t st) {
-    (void)cmax;
     int cfg = gemm_cfg_override();
-    if (cfg < 1 || cfg > 3) cfg = K <= 1024 ? 3 : 1;
+    if (cfg < 1 || cfg > 3) cfg = default_cfg(N, K, rows_hint);
     switch (cfg) {
     case 1: return big_launch<256, 256, 512, EPI>(act, A, B, D, N, K, E, fill, cap, bias, pre_out, st);
     case 2: return big_launch<256, 128, 256, EPI>(act, A, B, D, N, K, E, fill, cap, bias, pre_out, st);
@@ -1186,11 +1197,16 @@ hipError_t kgroup_launch(const void *A, const void *B, float *D, int Mo, int No,
 
 }  // namespace
 
+// Upper bound of the filled rows over all experts: every route kept, at most E*cmax.
+static int64_t rows_hint(const moe_shape &s, int32_t cmax) {
+    return std::min<int64_t>(static_cast<int64_t>(s.k) * s.S, static_cast<int64_t>(s.E) * cmax);
+}
+
 hipError_t launch_fc1(const moe_shape &s, const void *buf, const void *W1, const void *b1, const int32_t *fill,
                       const int32_t *cap, void *pre, void *h, int32_t cmax, hipStream_t st) {
     const int M = s.M, H = s.H, E = s.E;
     if (s.dtype == MOE_DT_BF16)
-        return fwd_launch<EPI_FC1>(s.act, buf, W1, h, H, M, cmax, E, fill, cap, b1, pre, st);
+        return fwd_launch<EPI_FC1>(s.act, buf, W1, h, H, M, rows_hint(s, cmax), E, fill, cap, b1, pre, st);
     SimtArgs a{};
     a.A = static_cast<const float *>(buf); a.a_si = M; a.a_sk = 1; a.a_gfix = 0; a.a_gcap = M;
     a.B = static_cast<const float *>(W1); a.b_sn = M; a.b_sk = 1; a.b_gfix = static_cast<int64_t>(H) * M; a.b_gcap = 0;
@@ -1204,7 +1220,7 @@ hipError_t launch_fc2(const moe_shape &s, const void *h, const void *W2, const v
                       const int32_t *cap, void *y, int32_t cmax, hipStream_t st) {
     const int M = s.M, H = s.H, E = s.E;
     if (s.dtype == MOE_DT_BF16)
-        return fwd_launch<EPI_FC2>(s.act, h, W2, y, M, H, cmax, E, fill, cap, b2, nullptr, st);
+        return fwd_launch<EPI_FC2>(s.act, h, W2, y, M, H, rows_hint(s, cmax), E, fill, cap, b2, nullptr, st);
     SimtArgs b{};
     b.A = static_cast<const float *>(h); b.a_si = H; b.a_sk = 1; b.a_gfix = 0; b.a_gcap = H;
     b.B = static_cast<const float *>(W2); b.b_sn = H; b.b_sk = 1; b.b_gfix = static_cast<int64_t>(M) * H; b.b_gcap = 0;
@@ -1222,12 +1238,14 @@ hipError_t launch_expert_ffn_bwd(const moe_shape &s, const void *buf, const void
     hipError_t err;
     if (s.dtype == MOE_DT_BF16) {
         // dpre = (dy . W2[e]) * act'(pre): A = dy [rows][M], B = W2[e] read as [K=M][N=H]
-        if ((err = bwd_data_launch<EPI_DACT>(s.act, dy, W2, dpre, H, M, E, fill, cap, pre, st)) != hipSuccess)
+        if ((err = bwd_data_launch<EPI_DACT>(s.act, dy, W2, dpre, H, M, E, fill, cap, pre, rows_hint(s, cmax), st)) !=
+            hipSuccess)
             return err;
         // dW2[e] = dy^T h (+ db2 = column sums of dy)
         if ((err = kgroup_launch(dy, h, dW2, M, H, E, fill, cap, db2, cmax, st)) != hipSuccess) return err;
         // dbuf = dpre . W1[e]: B = W1[e] read as [K=H][N=M]   (dbuf may alias dy: dy is consumed above)
-        if ((err = bwd_data_launch<EPI_PLAIN>(s.act, dpre, W1, dbuf, M, H, E, fill, cap, nullptr, st)) != hipSuccess)
+        if ((err = bwd_data_launch<EPI_PLAIN>(s.act, dpre, W1, dbuf, M, H, E, fill, cap, nullptr, rows_hint(s, cmax),
+                                              st)) != hipSuccess)
             return err;
         // dW1[e] = dpre^T buf (+ db1 = column sums of dpre)
         return kgroup_launch(dpre, buf, dW1, H, M, E, fill, cap, db1, cmax, st);

@@ -242,11 +242,51 @@ moe_status moe_gate_weight_grad(const moe_shape *shape, const void *x, const flo
     return e == hipSuccess ? MOE_OK : hip_fail(e, "gate weight gradient");
 }
 
-moe_status moe_layer_forward(const moe_shape *shape, const void *x, const float *logits_in, const float *Wg,
-                             float *logits_out, const void *W1, const void *b1, const void *W2, const void *b2,
-                             int32_t *idx, int32_t *loc, float *gates, int32_t *needed, int32_t *fill,
-                             int32_t *capacity, int32_t *slot_route, void *buf, void *pre, void *h, void *y,
-                             void *out, void *ws, size_t ws_bytes, void *stream) {
+moe_status moe_residual_ffn(const moe_shape *shape, const void *x, const void *W1r, const void *b1r,
+                            const void *W2r, const void *b2r, void *h_r, void *y_r, void *ws, size_t ws_bytes,
+                            void *stream) {
+    moe_status st = check_shape(shape);
+    if (st != MOE_OK) return st;
+    const moe_shape &s = *shape;
+    MOE_REQUIRE(W1r && W2r, "W1r and W2r must be non-NULL");
+    if (s.S > 0) MOE_REQUIRE(x && h_r && y_r, "x, h_r and y_r must be non-NULL");
+    MOE_REQUIRE((b1r != nullptr) == (s.has_fc1_bias != 0), "b1r must be given iff has_fc1_bias");
+    MOE_REQUIRE((b2r != nullptr) == (s.has_fc2_bias != 0), "b2r must be given iff has_fc2_bias");
+    if (s.S / 128 >= 65535) return fail(MOE_EUNSUPPORTED, "S=%d too large for the dense branch's GEMM grid", s.S);
+    if ((st = check_ws(s, ws, ws_bytes)) != MOE_OK) return st;
+    MOE_REQUIRE_ALIGNED(x, W1r, b1r, W2r, b2r, h_r, y_r, ws);
+    hipError_t e = moe::launch_residual_ffn(s, x, W1r, b1r, W2r, b2r, h_r, y_r, static_cast<int32_t *>(ws),
+                                            as_stream(stream));
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "residual dense branch");
+}
+
+moe_status moe_decode_residual(const moe_shape *shape, const void *y, const float *gates, const int32_t *idx,
+                               const int32_t *loc, const int32_t *capacity, const void *y_r, void *out,
+                               void *stream) {
+    moe_status st = check_shape(shape);
+    if (st != MOE_OK) return st;
+    const moe_shape &s = *shape;
+    MOE_REQUIRE(capacity != nullptr, "capacity is NULL");
+    if (s.S > 0) MOE_REQUIRE(y && gates && idx && loc && y_r && out, "y, gates, idx, loc, y_r and out must be non-NULL");
+    MOE_REQUIRE_ALIGNED(y, gates, idx, loc, capacity, y_r, out);
+    hipError_t e = moe::launch_decode(s, y, gates, idx, loc, capacity, out, false, as_stream(stream), y_r);
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "decode");
+}
+
+}  // extern "C"
+
+namespace {
+
+struct Residual {
+    const void *W1r, *b1r, *W2r, *b2r;
+    void *h_r, *y_r;
+};
+
+moe_status layer_forward_impl(const moe_shape *shape, const void *x, const float *logits_in, const float *Wg,
+                              float *logits_out, const void *W1, const void *b1, const void *W2, const void *b2,
+                              int32_t *idx, int32_t *loc, float *gates, int32_t *needed, int32_t *fill,
+                              int32_t *capacity, int32_t *slot_route, void *buf, void *pre, void *h, void *y,
+                              void *out, void *ws, size_t ws_bytes, const Residual *res, void *stream) {
     moe_status st = check_shape(shape);
     if (st != MOE_OK) return st;
     const moe_shape &s = *shape;
@@ -259,6 +299,15 @@ moe_status moe_layer_forward(const moe_shape *shape, const void *x, const float 
     if (s.S > 0) MOE_REQUIRE(x && idx && loc && gates && out, "x, idx, loc, gates and out must be non-NULL");
     MOE_REQUIRE((b1 != nullptr) == (s.has_fc1_bias != 0), "b1 must be given iff has_fc1_bias");
     MOE_REQUIRE((b2 != nullptr) == (s.has_fc2_bias != 0), "b2 must be given iff has_fc2_bias");
+    if (res != nullptr) {
+        MOE_REQUIRE(res->W1r && res->W2r, "W1r and W2r must be non-NULL");
+        if (s.S > 0) MOE_REQUIRE(res->h_r && res->y_r, "h_r and y_r must be non-NULL");
+        MOE_REQUIRE((res->b1r != nullptr) == (s.has_fc1_bias != 0), "b1r must be given iff has_fc1_bias");
+        MOE_REQUIRE((res->b2r != nullptr) == (s.has_fc2_bias != 0), "b2r must be given iff has_fc2_bias");
+        if (s.S / 128 >= 65535)
+            return fail(MOE_EUNSUPPORTED, "S=%d too large for the dense branch's GEMM grid", s.S);
+        MOE_REQUIRE_ALIGNED(res->W1r, res->b1r, res->W2r, res->b2r, res->h_r, res->y_r);
+    }
     if ((st = check_ws(s, ws, ws_bytes)) != MOE_OK) return st;
     MOE_REQUIRE_ALIGNED(x, logits_in, Wg, logits_out, W1, b1, W2, b2, idx, loc, gates, needed, fill, capacity,
                         slot_route, buf, pre, h, y, out, ws);
@@ -282,9 +331,40 @@ moe_status moe_layer_forward(const moe_shape *shape, const void *x, const float 
         return hip_fail(e, "expert fc1");
     if ((e = moe::launch_fc2(s, h, W2, b2, fill, capacity, y, cmax, strm)) != hipSuccess)
         return hip_fail(e, "expert fc2");
-    if ((e = moe::launch_decode(s, y, gates, idx, loc, capacity, out, false, strm)) != hipSuccess)
+    // the dense branch uses the workspace after routing is done with it
+    if (res != nullptr &&
+        (e = moe::launch_residual_ffn(s, x, res->W1r, res->b1r, res->W2r, res->b2r, res->h_r, res->y_r,
+                                      static_cast<int32_t *>(ws), strm)) != hipSuccess)
+        return hip_fail(e, "residual dense branch");
+    if ((e = moe::launch_decode(s, y, gates, idx, loc, capacity, out, false, strm,
+                                res != nullptr ? res->y_r : nullptr)) != hipSuccess)
         return hip_fail(e, "decode");
     return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_layer_forward(const moe_shape *shape, const void *x, const float *logits_in, const float *Wg,
+                             float *logits_out, const void *W1, const void *b1, const void *W2, const void *b2,
+                             int32_t *idx, int32_t *loc, float *gates, int32_t *needed, int32_t *fill,
+                             int32_t *capacity, int32_t *slot_route, void *buf, void *pre, void *h, void *y,
+                             void *out, void *ws, size_t ws_bytes, void *stream) {
+    return layer_forward_impl(shape, x, logits_in, Wg, logits_out, W1, b1, W2, b2, idx, loc, gates, needed, fill,
+                              capacity, slot_route, buf, pre, h, y, out, ws, ws_bytes, nullptr, stream);
+}
+
+moe_status moe_residual_layer_forward(const moe_shape *shape, const void *x, const float *logits_in,
+                                      const float *Wg, float *logits_out, const void *W1, const void *b1,
+                                      const void *W2, const void *b2, const void *W1r, const void *b1r,
+                                      const void *W2r, const void *b2r, int32_t *idx, int32_t *loc, float *gates,
+                                      int32_t *needed, int32_t *fill, int32_t *capacity, int32_t *slot_route,
+                                      void *buf, void *pre, void *h, void *y, void *h_r, void *y_r, void *out,
+                                      void *ws, size_t ws_bytes, void *stream) {
+    const Residual res{W1r, b1r, W2r, b2r, h_r, y_r};
+    return layer_forward_impl(shape, x, logits_in, Wg, logits_out, W1, b1, W2, b2, idx, loc, gates, needed, fill,
+                              capacity, slot_route, buf, pre, h, y, out, ws, ws_bytes, &res, stream);
 }
 
 moe_status moe_layer_backward(const moe_shape *shape, const void *dout, const void *buf, const void *pre,

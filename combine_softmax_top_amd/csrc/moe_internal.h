@@ -114,10 +114,16 @@ hipError_t launch_route(const moe_shape &s, const float *logits, int32_t *idx, i
 hipError_t launch_encode(const moe_shape &s, const void *x, const int32_t *idx, const int32_t *loc,
                          const int32_t *fill, const int32_t *cap, void *buf, int32_t cmax,
                          hipStream_t st);
-// Gate-weighted combine (unit_gates = false) or plain gather-sum (gates ignored).
+// Gate-weighted combine (unit_gates = false) or plain gather-sum (gates ignored);
+// yres (gate-weighted combine only): Residual-MoE's dense-branch rows, added before the rounding.
 hipError_t launch_decode(const moe_shape &s, const void *y, const float *gates, const int32_t *idx,
                          const int32_t *loc, const int32_t *cap, void *out, bool unit_gates,
-                         hipStream_t st);
+                         hipStream_t st, const void *yres = nullptr);
+// Residual-MoE dense branch: h_r = act(x W1r^T + b1r), y_r = h_r W2r^T + b2r over all S
+// tokens; dense_rows is 2 int32 of device scratch (the branch's row count and "capacity").
+hipError_t launch_residual_ffn(const moe_shape &s, const void *x, const void *W1r, const void *b1r,
+                               const void *W2r, const void *b2r, void *h_r, void *y_r, int32_t *dense_rows,
+                               hipStream_t st);
 hipError_t launch_decode_bwd(const moe_shape &s, const void *dout, const void *y, const float *gates,
                              const int32_t *idx, const int32_t *loc, const int32_t *cap, void *dy,
                              float *dgates, hipStream_t st);

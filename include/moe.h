@@ -33,7 +33,8 @@
  *  - Every device pointer is 16-byte aligned (checked: MOE_EINVAL); the
  *    kernels move rows as 16-byte vectors.
  *  - Data-type tensors (x, W1, b1, W2, b2, buf, pre, h, y, out, dout, dx, dy,
- *    dpre, dbuf) are fp32 or bf16 as moe_shape.dtype says. logits, Wg, gates,
+ *    dpre, dbuf, and Residual-MoE's W1r, b1r, W2r, b2r, h_r, y_r) are fp32 or
+ *    bf16 as moe_shape.dtype says. logits, Wg, gates,
  *    dgates, dlogits, the auxiliary loss and the weight/bias gradients are
  *    fp32. Index tables are int32.
  *  - Route tables are route-major [k, S]: entry r*S + s is route r of token s,
@@ -173,6 +174,27 @@ moe_status moe_expert_fc2(const moe_shape *shape, const void *h, const void *W2,
 moe_status moe_decode(const moe_shape *shape, const void *y, const float *gates, const int32_t *idx,
                       const int32_t *loc, const int32_t *capacity, void *out, void *stream);
 
+/* Residual-MoE (MoE training blog, part 1 section 1.2, the residual half of
+ * PR-MoE): every token also passes through one fixed dense MLP, and its output
+ * is added to the MoE output. The dense branch has the experts' form with its
+ * own weights over all S tokens:
+ *   h_r = act(x . W1r^T + b1r)   stored in the data type
+ *   y_r = h_r . W2r^T + b2r       (fp32 accumulation), stored
+ * W1r [H, M], b1r [H] (NULL iff !has_fc1_bias), W2r [M, H], b2r [M] (NULL iff
+ * !has_fc2_bias); x, y_r [S, M]; h_r [S, H]; ws: moe_workspace_size() bytes (8
+ * bytes of it hold the branch's row count for the grouped GEMMs). Supported
+ * for S < 128 * 65535. */
+moe_status moe_residual_ffn(const moe_shape *shape, const void *x, const void *W1r, const void *b1r,
+                            const void *W2r, const void *b2r, void *h_r, void *y_r, void *ws,
+                            size_t ws_bytes, void *stream);
+
+/* moe_decode with the Residual-MoE add fused in: the fp32 sum over the kept
+ * routes (as in moe_decode) gains y_r[s] after the last route, then is rounded
+ * once to the data type. A token whose routes were all dropped gets y_r[s]. */
+moe_status moe_decode_residual(const moe_shape *shape, const void *y, const float *gates,
+                               const int32_t *idx, const int32_t *loc, const int32_t *capacity,
+                               const void *y_r, void *out, void *stream);
+
 /* Gate backward (the softmax gate is trained: MoE training blog, part 2 section
  * 2.1, training with top-1 gating and an auxiliary load-balance loss of
  * coefficient 0.01; DeepSpeed PR #8195, forward + backward step times). The
@@ -214,6 +236,18 @@ moe_status moe_layer_forward(const moe_shape *shape, const void *x, const float 
                              float *gates, int32_t *needed, int32_t *fill, int32_t *capacity,
                              int32_t *slot_route, void *buf, void *pre, void *h, void *y, void *out,
                              void *ws, size_t ws_bytes, void *stream);
+
+/* moe_layer_forward of a Residual-MoE layer: the same steps, plus the dense
+ * branch (moe_residual_ffn: W1r, b1r, W2r, b2r -> h_r, y_r) before decode,
+ * and decode as moe_decode_residual. Forward only. */
+moe_status moe_residual_layer_forward(const moe_shape *shape, const void *x, const float *logits_in,
+                                      const float *Wg, float *logits_out, const void *W1, const void *b1,
+                                      const void *W2, const void *b2, const void *W1r, const void *b1r,
+                                      const void *W2r, const void *b2r, int32_t *idx, int32_t *loc,
+                                      float *gates, int32_t *needed, int32_t *fill, int32_t *capacity,
+                                      int32_t *slot_route, void *buf, void *pre, void *h, void *y,
+                                      void *h_r, void *y_r, void *out, void *ws, size_t ws_bytes,
+                                      void *stream);
 
 /* The backward of decode, expert FFN and encode for upstream gradient dout
  * [S, M] (blog part 3 section 3.5: K1 is combine-backward, K2 the cross term,

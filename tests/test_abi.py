@@ -32,11 +32,25 @@ def odd_ptr():
 
 def test_every_declared_symbol_is_exported(moe):
     names = _declared()
-    assert len(names) == 15, names
+    assert len(names) == 18, names
     lib = ctypes.CDLL(moe.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
     assert names == moe.EXPORTED
+
+
+def test_binding_arity_matches_header(moe):
+    # every prototype's parameter count equals the argument count the binding declares
+    with open(os.path.join(ROOT, "include", "moe.h")) as fh:
+        text = fh.read()
+    protos = re.findall(r"^\s*(?:moe_status|const char \*)\s*(moe_\w+)\s*\(([^;]*?)\);", text, re.M | re.S)
+    assert len(protos) == len(_declared())
+    for name, params in protos:
+        n = 0 if params.strip() in ("", "void") else params.count(",") + 1
+        if name == "moe_last_error":
+            assert n == 0
+            continue
+        assert n == len(moe._SIGS[name]), (name, n, len(moe._SIGS[name]))
 
 
 def test_shape_struct_layout_matches_header(moe):

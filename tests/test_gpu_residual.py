@@ -1,0 +1,102 @@
+"""GPU parity of Residual-MoE (a dense MLP branch every token passes through, added to
+the MoE output in the decode's fp32 sum) against the CPU oracle: the dense branch on
+its own, the residual decode bit for bit given the same inputs, and the fused layer."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from tests.gpu_helpers import check_close, dev, host, inputs_np, shape_of
+
+pytestmark = pytest.mark.gpu
+
+# (S, M, H, dtype, act, biases)
+FFN_CASES = [
+    (1, 64, 64, W.DT_BF16, W.ACT_GELU, True), (300, 256, 384, W.DT_BF16, W.ACT_GELU, True),
+    (1000, 1088, 1152, W.DT_BF16, W.ACT_GELU, True), (517, 128, 192, W.DT_BF16, W.ACT_RELU, False),
+    (200, 64, 128, W.DT_F32, W.ACT_GELU, True), (0, 64, 64, W.DT_BF16, W.ACT_GELU, True),
+]
+
+
+@pytest.mark.parametrize("S,M,H,dtype,act,bias", FFN_CASES, ids=lambda v: str(v))
+def test_residual_ffn_matches_oracle(S, M, H, dtype, act, bias):
+    import combine_softmax_top_amd as moe
+    print(f"[residual ffn] S={S} M={M} H={H} dtype={dtype} act={act} bias={bias}", flush=True)
+    w = W.Workload("res", S=S, M=M, E=2, k=1, H=H, capacity_factor=1.0, dtype=dtype, act=act, has_fc1_bias=bias,
+                   has_fc2_bias=bias, residual=True)
+    inp = W.make_inputs(w, seed=0)
+    s = shape_of(w)
+    d = {k_: v.cuda() for k_, v in inp.items()}
+    ws = torch.empty(max(1, moe.moe_workspace_size(s)), dtype=torch.uint8, device="cuda")
+    h_r = torch.empty(S, H, dtype=w.torch_dtype, device="cuda")
+    y_r = torch.empty(S, M, dtype=w.torch_dtype, device="cuda")
+    moe.moe_residual_ffn(s, d["x"], d["W1r"], d.get("b1r"), d["W2r"], d.get("b2r"), h_r, y_r, ws)
+    torch.cuda.synchronize()
+    ni = inputs_np(inp)
+    h_o, y_o = oracle.residual_mlp(ni["x"], ni["W1r"], ni.get("b1r"), ni["W2r"], ni.get("b2r"), act, dtype)
+    check_close(host(h_r), h_o, dtype, "h_r")
+    check_close(host(y_r), y_o, dtype, "y_r")
+
+
+@pytest.mark.parametrize("dtype", [W.DT_BF16, W.DT_F32])
+@pytest.mark.parametrize("S,E,k,f", [(1000, 8, 1, 1.25), (777, 16, 2, 0.5), (64, 4, 1, 0.25)])
+def test_decode_residual_bit_exact(S, E, k, f, dtype):
+    # given the same expert outputs and dense-branch rows, the fp32 sum and its one rounding match exactly
+    import combine_softmax_top_amd as moe
+    M = 192
+    w = W.Workload("dres", S=S, M=M, E=E, k=k, H=64, capacity_factor=f, dtype=dtype)
+    logits = W.normal((S, E), 1, "logits").numpy()
+    rt = oracle.route(logits, k, f)
+    C = rt["C"]
+    tdt = w.torch_dtype
+    y = W.normal((E * C, M), 1, "W1").to(tdt)
+    yr = W.normal((S, M), 1, "W2").to(tdt)
+    want = oracle.decode(host(y), rt, E, dtype, yres=host(yr))
+    s = shape_of(w)
+    out = torch.empty(S, M, dtype=tdt, device="cuda")
+    moe.moe_decode_residual(s, y.cuda(), dev(rt["gates"]), dev(rt["idx"]), dev(rt["loc"]),
+                            torch.tensor([C], dtype=torch.int32, device="cuda"), yr.cuda(), out)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(out).view(np.uint8), want.view(np.uint8))
+
+
+RES = [
+    W.Workload("res_gate_S500_E8_k1", S=500, M=256, E=8, k=1, H=384, capacity_factor=1.25, logits="gate",
+               residual=True),
+    W.Workload("res_drops_S300_E4_k1", S=300, M=128, E=4, k=1, H=128, capacity_factor=0.5, residual=True),
+    W.Workload("res_k2_relu_nobias_S257_E6", S=257, M=64, E=6, k=2, H=192, capacity_factor=1.0, act=W.ACT_RELU,
+               has_fc1_bias=False, has_fc2_bias=False, residual=True),
+    W.Workload("res_f32_S200_E4_k1", S=200, M=64, E=4, k=1, H=128, capacity_factor=1.0, dtype=W.DT_F32,
+               residual=True),
+    W.Workload("res_bigtile_S600_M1088_E4_k1_H1152", S=600, M=1088, E=4, k=1, H=1152, capacity_factor=1.0,
+               residual=True),
+]
+
+
+@pytest.mark.parametrize("w", RES, ids=lambda w: w.name)
+def test_residual_layer_forward_matches_oracle(w):
+    import combine_softmax_top_amd as moe
+    print(f"[residual layer] {w.name}", flush=True)
+    inp = W.make_inputs(w, seed=0)
+    s = shape_of(w)
+    d = {k_: v.cuda() for k_, v in inp.items()}
+    res = {n: d.get(n) for n in ("W1r", "b1r", "W2r", "b2r")}
+    b = moe.layer_forward(s, d["x"], d["W1"], d.get("b1"), d["W2"], d.get("b2"), logits=d.get("logits"),
+                          Wg=d.get("Wg"), residual=res)
+    torch.cuda.synchronize()
+    ni = inputs_np(inp)
+    fw = oracle.layer_forward(ni, w.k, w.capacity_factor, w.act, w.dtype)
+    rt = fw["route"]
+    assert int(b["capacity"].item()) == rt["C"]
+    assert np.array_equal(host(b["idx"]), rt["idx"]) and np.array_equal(host(b["loc"]), rt["loc"])
+    check_close(host(b["y_r"]), fw["y_r"], w.dtype, "y_r")
+    check_close(host(b["out"]), fw["out"], w.dtype, "out")
+    # given the GPU's own expert outputs and dense rows, the residual decode is exact
+    want = oracle.decode(host(b["y"][: w.E * rt["C"]]), rt, w.E, w.dtype, yres=host(b["y_r"]))
+    assert np.array_equal(host(b["out"]).view(np.uint8), want.view(np.uint8))
+    dropped = np.nonzero((rt["loc"] >= rt["C"]).all(axis=0))[0]
+    if len(dropped):
+        assert np.array_equal(host(b["out"])[dropped].view(np.uint8), host(b["y_r"])[dropped].view(np.uint8))

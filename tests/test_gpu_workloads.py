@@ -7,7 +7,8 @@ oracle computes one by one from the original inputs: every expert's first and
 last filled rows plus random rows of h and y, a random set of tokens of the
 layer output, and, for the workloads with a backward, random gate gradients,
 random tokens of dx, and the weight/bias gradients of three experts (hottest,
-median, coldest) on random hidden columns. The gate backward: the auxiliary
+median, coldest) on random hidden columns. Residual-MoE: the dense branch's
+output on the sampled tokens, and the layer output with it. The gate backward: the auxiliary
 loss in full; dlogits on the sampled tokens (the oracle's dgates of their
 routes upstream); with a projected gate (small enough for the oracle to run
 every expert row) dgates, dlogits and dWg in full and dx's gate share on the
@@ -41,8 +42,10 @@ def test_full_size_workload(w):
     inp = W.make_inputs(w, seed=0, device="cuda")
     s = moe.Shape.of(w)
     gate = w.logits == "gate"
+    res = {n: inp.get(n) for n in ("W1r", "b1r", "W2r", "b2r")} if w.residual else None
     b = moe.layer_forward(s, inp["x"], inp["W1"], inp.get("b1"), inp["W2"], inp.get("b2"),
-                          logits=None if gate else inp["logits"], Wg=inp.get("Wg"), training=w.backward)
+                          logits=None if gate else inp["logits"], Wg=inp.get("Wg"), training=w.backward,
+                          residual=res)
     gr = None
     if w.backward:
         gr = moe.layer_backward(s, b, inp["dout"], inp["W1"], inp["W2"],
@@ -102,7 +105,14 @@ def test_full_size_workload(w):
     check_close(gy, y_o, w.dtype, "y rows")
     y_full = np.zeros((w.E * C, w.M), y_o.dtype)
     y_full[all_rows] = y_o
-    out_o = oracle.decode(y_full, rt, w.E, w.dtype, tokens=toks)
+    yres = None
+    if w.residual:
+        _, yr_o = oracle.residual_mlp(ni["x"], ni["W1r"], ni.get("b1r"), ni["W2r"], ni.get("b2r"), w.act, w.dtype,
+                                      tokens=toks)
+        check_close(host(b["y_r"][torch.from_numpy(toks).cuda()]), yr_o, w.dtype, "y_r tokens")
+        yres = np.zeros((w.S, w.M), yr_o.dtype)
+        yres[toks] = yr_o
+    out_o = oracle.decode(y_full, rt, w.E, w.dtype, tokens=toks, yres=yres)
     check_close(host(b["out"][torch.from_numpy(toks).cuda()]), out_o, w.dtype, "out tokens")
     _say(f"[{w.name}] FFN rows and {ntok} output tokens within tolerance")
 
