@@ -86,6 +86,16 @@ def lib():
         L.oracle_dgates.restype = None
         L.oracle_dx.argtypes = [i32, i32, ctypes.c_int, vp, i64, _c_i64p, i32, vp, vp, vp]
         L.oracle_dx.restype = None
+        u8p = np.ctypeslib.ndpointer(dtype=np.uint8, flags="C_CONTIGUOUS")
+        L.oracle_e4m3_value.argtypes = [ctypes.c_int]; L.oracle_e4m3_value.restype = d
+        L.oracle_e2m1_value.argtypes = [ctypes.c_int]; L.oracle_e2m1_value.restype = d
+        L.oracle_mx_quantize.argtypes = [ctypes.c_int, i64, i32, ctypes.c_int, vp, u8p, u8p]
+        L.oracle_mx_quantize.restype = None
+        L.oracle_mx_dequantize.argtypes = [ctypes.c_int, i64, i32, u8p, u8p, _c_f64p]
+        L.oracle_mx_dequantize.restype = None
+        L.oracle_expert_rows_mx.argtypes = [i32, i32, i32, ctypes.c_int, ctypes.c_int, u8p, u8p, u8p, u8p, vp, u8p,
+                                            u8p, vp, i64, _c_i64p, vp, vp, vp]
+        L.oracle_expert_rows_mx.restype = None
         L.oracle_gate_backward.argtypes = [i32, i32, i32, d, _c_f32p, _c_i32p, _c_f32p, vp, _c_f64p, _c_f64p]
         L.oracle_gate_backward.restype = None
         L.oracle_gate_weight_grad.argtypes = [i32, i32, i32, ctypes.c_int, vp, _c_f64p, _c_f64p]
@@ -451,3 +461,64 @@ def layer_backward(fw: Dict, inp: Dict, act_kind: int, dtype: int, aux_coef: Opt
             dl = None
     out["dx"] = dx_tokens(routes, dbuf, np.arange(S), S, k, dtype, dlogits=dl, Wg=Wg)
     return out
+
+
+# ------------------------------------------------------------------ MX (microscaling) experts
+
+MX_FP8 = 0  # MXFP8: E4M3 elements, one byte each
+MX_FP4 = 1  # MXFP4: E2M1 elements, two per byte (even index in the low nibble)
+
+
+def e4m3_value(code: int) -> float:
+    return lib().oracle_e4m3_value(int(code))
+
+
+def e2m1_value(code: int) -> float:
+    return lib().oracle_e2m1_value(int(code))
+
+
+def mx_row_bytes(K: int, fmt: int) -> int:
+    return K if fmt == MX_FP8 else K // 2
+
+
+def mx_quantize(a: np.ndarray, fmt: int, dtype: int):
+    """MX quantisation along the last dimension (a multiple of 32) of a data-type array:
+    returns (codes uint8 [..., row bytes], scales uint8 [..., K/32])."""
+    a = _check(a, dtype)
+    K = a.shape[-1]
+    assert K % 32 == 0
+    rows = int(np.prod(a.shape[:-1], dtype=np.int64))
+    codes = np.zeros(a.shape[:-1] + (mx_row_bytes(K, fmt),), np.uint8)
+    scales = np.zeros(a.shape[:-1] + (K // 32,), np.uint8)
+    lib().oracle_mx_quantize(fmt, rows, K, dtype, _ptr(a), codes, scales)
+    return codes, scales
+
+
+def mx_dequantize(codes: np.ndarray, scales: np.ndarray, fmt: int) -> np.ndarray:
+    K = scales.shape[-1] * 32
+    rows = int(np.prod(scales.shape[:-1], dtype=np.int64))
+    out = np.empty(scales.shape[:-1] + (K,), np.float64)
+    lib().oracle_mx_dequantize(fmt, rows, K, np.ascontiguousarray(codes), np.ascontiguousarray(scales), out)
+    return out
+
+
+def expert_rows_mx(bufq, W1q, b1, W2q, b2, rows: Sequence[int], C: int, act_kind: int, wfmt: int,
+                   want_hq: bool = False):
+    """MX expert FFN for the listed buffer rows: bufq = (codes, scales) MXFP8 [E*C, M];
+    W1q = (codes, scales) [E, H, M] and W2q [E, M, H] in format wfmt; biases bf16 or None.
+    Returns (h codes, h scales) when asked and y (bf16, compact [n, M])."""
+    bc, bs = (np.ascontiguousarray(t) for t in bufq)
+    w1c, w1s = (np.ascontiguousarray(t) for t in W1q)
+    w2c, w2s = (np.ascontiguousarray(t) for t in W2q)
+    E, H = w1s.shape[0], w1s.shape[1]
+    M = w2s.shape[1]
+    rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    n = rows.shape[0]
+    hc = np.empty((n, H), np.uint8) if want_hq else None
+    hs = np.empty((n, H // 32), np.uint8) if want_hq else None
+    y = np.empty((n, M), np.uint16)
+    b1 = None if b1 is None else _check(b1, DT_BF16, (E, H))
+    b2 = None if b2 is None else _check(b2, DT_BF16, (E, M))
+    lib().oracle_expert_rows_mx(M, H, C, act_kind, wfmt, bc, bs, w1c, w1s, _ptr(b1), w2c, w2s, _ptr(b2), n, rows,
+                                _ptr(hc), _ptr(hs), _ptr(y))
+    return ((hc, hs) if want_hq else None), y

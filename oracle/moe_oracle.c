@@ -579,3 +579,143 @@ void oracle_gate_weight_grad(int32_t S, int32_t M, int32_t E, int dtype, const v
             dWg[(int64_t)m * E + e] = acc;
         }
 }
+
+/* ------------------------------------------------------------------ MX (microscaling) experts */
+
+/* Low-precision experts (Tutel catalogue page: FP8 / MXFP4 / block-wise FP8
+ * quantised inference). Format: OCP Microscaling (MX) v1.0 -- blocks of 32
+ * consecutive values along the reduction dimension share one E8M0 scale
+ * X = 2^(b - 127); each value is an element P with value X * P.
+ *   fmt 0: MXFP8, E4M3 elements (bias 7, 3 mantissa bits, max normal 448,
+ *          subnormals, S.1111.111 is NaN and never produced), one byte each;
+ *   fmt 1: MXFP4, E2M1 elements (bias 1, 1 mantissa bit, values 0, 0.5, 1,
+ *          1.5, 2, 3, 4, 6), two per byte, the even index in the low nibble.
+ * Quantisation of a block (the MX specification's algorithm): amax = max |v|;
+ * shared exponent e = floor(log2 amax) - emax_elem (8 for E4M3, 2 for E2M1),
+ * clamped to [-127, 127], e = -127 for an all-zero block; each element is
+ * v / 2^e rounded to the nearest element value, ties to the even code, with
+ * magnitudes beyond the largest normal clamped to it; the sign bit is the
+ * input's (so -0 stays -0). */
+static const double kE2M1[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+
+double oracle_e4m3_value(int code) {
+    const int s = (code >> 7) & 1, e = (code >> 3) & 15, m = code & 7;
+    double v;
+    if (e == 15 && m == 7) return NAN;
+    if (e == 0) v = ldexp((double)m / 8.0, -6);
+    else v = ldexp(1.0 + (double)m / 8.0, e - 7);
+    return s ? -v : v;
+}
+
+double oracle_e2m1_value(int code) {
+    const double v = kE2M1[code & 7];
+    return (code & 8) ? -v : v;
+}
+
+/* Nearest element code of |q| (q >= 0), ties to the even code, saturating. */
+static int nearest_code(double q, int fmt) {
+    const int ncodes = fmt == 0 ? 127 : 8;  /* E4M3: codes 0..126 are the finite magnitudes */
+    int best = 0;
+    double bd = INFINITY;
+    for (int c = 0; c < ncodes; ++c) {
+        const double v = fmt == 0 ? oracle_e4m3_value(c) : kE2M1[c];
+        const double d = fabs(v - q);
+        if (d < bd || (d == bd && (c & 1) == 0)) { bd = d; best = c; }
+    }
+    return best;
+}
+
+/* One row of K values (fp64) -> codes (row layout of the format) and K/32 scale bytes. */
+static void mx_quantize_row(const double *v, int32_t K, int fmt, uint8_t *codes, uint8_t *scales) {
+    const int emax = fmt == 0 ? 8 : 2;
+    for (int32_t b = 0; b < K / 32; ++b) {
+        double amax = 0.0;
+        for (int i = 0; i < 32; ++i) amax = fmax(amax, fabs(v[32 * b + i]));
+        int e = -127;
+        if (amax > 0.0) {
+            e = ilogb(amax) - emax;  /* floor(log2 amax) for finite nonzero amax */
+            if (e < -127) e = -127;
+            if (e > 127) e = 127;
+        }
+        scales[b] = (uint8_t)(e + 127);
+        for (int i = 0; i < 32; ++i) {
+            const int32_t k = 32 * b + i;
+            const double x = v[k];
+            const int c = nearest_code(ldexp(fabs(x), -e), fmt) | (signbit(x) ? (fmt == 0 ? 0x80 : 0x8) : 0);
+            if (fmt == 0) codes[k] = (uint8_t)c;
+            else if (k % 2 == 0) codes[k / 2] = (uint8_t)c;
+            else codes[k / 2] |= (uint8_t)(c << 4);
+        }
+    }
+}
+
+static int64_t mx_row_bytes(int32_t K, int fmt) { return fmt == 0 ? K : K / 2; }
+
+static double mx_value(const uint8_t *codes, const uint8_t *scales, int32_t K, int fmt, int64_t row, int32_t k) {
+    const double x = ldexp(1.0, (int)scales[row * (K / 32) + k / 32] - 127);
+    if (fmt == 0) return x * oracle_e4m3_value(codes[row * K + k]);
+    const uint8_t byte = codes[row * (K / 2) + k / 2];
+    return x * oracle_e2m1_value((k & 1) ? (byte >> 4) : (byte & 15));
+}
+
+/* Quantise a row-major [rows, K] matrix of the data type (K a multiple of 32). */
+void oracle_mx_quantize(int fmt, int64_t rows, int32_t K, int dtype, const void *src, uint8_t *codes,
+                        uint8_t *scales) {
+    double *v = (double *)malloc(sizeof(double) * (size_t)K);
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int32_t k = 0; k < K; ++k) v[k] = load_elem(src, dtype, r * K + k);
+        mx_quantize_row(v, K, fmt, codes + r * mx_row_bytes(K, fmt), scales + r * (K / 32));
+    }
+    free(v);
+}
+
+/* Exact values of an MX matrix, fp64 [rows, K]. */
+void oracle_mx_dequantize(int fmt, int64_t rows, int32_t K, const uint8_t *codes, const uint8_t *scales,
+                          double *out) {
+    for (int64_t r = 0; r < rows; ++r)
+        for (int32_t k = 0; k < K; ++k) out[r * K + k] = mx_value(codes, scales, K, fmt, r, k);
+}
+
+/* Expert FFN on MX operands, for the listed buffer rows (row = e*C + j):
+ *   pre = sum_m buf[row][m] W1[e][h][m] + b1[e][h]   (MX values, fp64 sums)
+ *   h   = act(pre), rounded to fp32 (the precision the quantisation decision
+ *         is taken in), then quantised to MXFP8 in blocks of 32 along H
+ *   y   = sum_h hq[h] W2[e][m][h] + b2[e][m], rounded to bf16
+ * buf is MXFP8 ([E*C, M] codes, [E*C, M/32] scales); W1 [E*H, M] and W2 [E*M, H]
+ * in weight format wfmt; biases bf16 (may be NULL). Outputs compact per listed
+ * row: h codes [n, H], h scales [n, H/32] (either may be NULL), y bf16 [n, M]. */
+void oracle_expert_rows_mx(int32_t M, int32_t H, int32_t C, int act, int wfmt, const uint8_t *buf_codes,
+                           const uint8_t *buf_scales, const uint8_t *w1_codes, const uint8_t *w1_scales,
+                           const void *b1, const uint8_t *w2_codes, const uint8_t *w2_scales, const void *b2,
+                           int64_t nrows, const int64_t *rows, uint8_t *h_codes, uint8_t *h_scales, void *y_out) {
+#pragma omp parallel
+    {
+        double *xv = (double *)malloc(sizeof(double) * (size_t)M);
+        double *hv = (double *)malloc(sizeof(double) * (size_t)H);
+        uint8_t *hc = (uint8_t *)malloc((size_t)H);
+        uint8_t *hs = (uint8_t *)malloc((size_t)(H / 32));
+#pragma omp for schedule(dynamic, 4)
+        for (int64_t i = 0; i < nrows; ++i) {
+            const int64_t row = rows[i];
+            const int64_t e = row / C;
+            for (int32_t m = 0; m < M; ++m) xv[m] = mx_value(buf_codes, buf_scales, M, 0, row, m);
+            for (int32_t h = 0; h < H; ++h) {
+                double acc = 0.0;
+                for (int32_t m = 0; m < M; ++m) acc += xv[m] * mx_value(w1_codes, w1_scales, M, wfmt, e * H + h, m);
+                if (b1) acc += load_elem(b1, DT_BF16, e * H + h);
+                hv[h] = (double)(float)act_f(act, acc);
+            }
+            mx_quantize_row(hv, H, 0, hc, hs);
+            if (h_codes) memcpy(h_codes + i * H, hc, (size_t)H);
+            if (h_scales) memcpy(h_scales + i * (H / 32), hs, (size_t)(H / 32));
+            for (int32_t h = 0; h < H; ++h) hv[h] = mx_value(hc, hs, H, 0, 0, h);
+            for (int32_t m = 0; m < M; ++m) {
+                double acc = 0.0;
+                for (int32_t h = 0; h < H; ++h) acc += hv[h] * mx_value(w2_codes, w2_scales, H, wfmt, e * M + m, h);
+                if (b2) acc += load_elem(b2, DT_BF16, e * M + m);
+                store_elem(y_out, DT_BF16, i * M + m, acc);
+            }
+        }
+        free(xv); free(hv); free(hc); free(hs);
+    }
+}

@@ -685,3 +685,135 @@ def test_residual_branch_ignores_routing():
                    W.ACT_GELU).numpy()
     # h_r and y_r are bf16: within a few bf16 ulps of the fp64 MLP
     assert np.abs(f32_of(a["y_r"]) - r).max() <= 2 ** -6 * np.abs(r).max()
+
+
+# ---------------------------------------------------------------- MX (microscaling) experts
+
+def test_e4m3_decode_matches_torch():
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = np.array([oracle.e4m3_value(c) for c in range(256)])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan) and nan.sum() == 2  # S.1111.111 only
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+
+
+def test_e2m1_values_from_the_element_formula():
+    # E2M1: sign, 2 exponent bits (bias 1), 1 mantissa bit; exponent 0 is subnormal (m/2)
+    for c in range(16):
+        s, e, m = c >> 3, (c >> 1) & 3, c & 1
+        v = (m / 2.0) if e == 0 else 2.0 ** (e - 1) * (1 + m / 2.0)
+        assert oracle.e2m1_value(c) == (-v if s else v)
+        assert math.copysign(1.0, oracle.e2m1_value(c)) == (-1.0 if s else 1.0)
+
+
+def _mx_elem_values(fmt):
+    if fmt == oracle.MX_FP8:
+        return np.array([oracle.e4m3_value(c) for c in range(127)])  # finite magnitudes, by code
+    return np.array([oracle.e2m1_value(c) for c in range(8)])
+
+
+def _mx_codes_of(codes, fmt, K):
+    if fmt == oracle.MX_FP8:
+        return codes.astype(np.int64)
+    lo, hi = (codes & 15).astype(np.int64), (codes >> 4).astype(np.int64)
+    return np.stack([lo, hi], axis=-1).reshape(codes.shape[:-1] + (K,))
+
+
+@pytest.mark.parametrize("fmt", [oracle.MX_FP8, oracle.MX_FP4])
+@pytest.mark.parametrize("dtype", [W.DT_F32, W.DT_BF16])
+def test_mx_quantize_against_brute_force(fmt, dtype):
+    rng = np.random.default_rng(40 + fmt)
+    rows, K = 24, 128
+    a = rng.standard_normal((rows, K)) * np.exp(rng.uniform(-12, 12, (rows, 1)))
+    a[0, :32] = 0.0                      # an all-zero block
+    a[1, :32] = 0.0; a[1, 5] = -0.0      # and one with a negative zero
+    a[2, 32:64] = 2.0 ** 5               # amax a power of two
+    a[3, :32] = 1.9 * 2.0 ** 3           # saturating block (v / X = 1.9 * 2^emax)
+    a = to_dtype_bits(a.astype(np.float32), dtype)
+    v = f32_of(a).astype(np.float64)
+    codes, scales = oracle.mx_quantize(a, fmt, dtype)
+    emax = 8 if fmt == oracle.MX_FP8 else 2
+    mags = _mx_elem_values(fmt)
+    cds = _mx_codes_of(codes, fmt, K)
+    sign_bit = 0x80 if fmt == oracle.MX_FP8 else 0x8
+    for r in range(rows):
+        for b in range(K // 32):
+            blk = v[r, 32 * b:32 * b + 32]
+            amax = np.abs(blk).max()
+            e = (np.frexp(amax)[1] - 1 - emax) if amax > 0 else -127
+            assert int(scales[r, b]) == e + 127, (r, b)
+            q = np.abs(blk) / 2.0 ** e
+            d = np.abs(mags[None, :] - q[:, None])
+            best = d.min(axis=1)
+            for i in range(32):
+                c = int(cds[r, 32 * b + i])
+                mag = c & (sign_bit - 1)
+                assert d[i, mag] == best[i], (r, b, i)  # nearest (saturating: only finite codes exist)
+                ties = np.nonzero(d[i] == best[i])[0]
+                if len(ties) > 1:
+                    assert mag % 2 == 0  # ties to the even code
+                assert bool(c & sign_bit) == bool(np.signbit(blk[i]))
+    # dequantised values: X * element
+    deq = oracle.mx_dequantize(codes, scales, fmt)
+    assert deq[0, :32].tolist() == [0.0] * 32 and np.signbit(deq[1, 5])
+    assert np.all(np.abs(deq[3, :32]) == (448.0 * 2 ** -5 if fmt == oracle.MX_FP8 else 6.0 * 2 ** 1))
+
+
+def test_mx_fp8_elements_match_torch_cast():
+    # where no saturation is needed, the element codes equal torch's round-to-nearest fp32 -> e4m3 cast
+    rng = np.random.default_rng(44)
+    a = (rng.standard_normal((16, 256)) * 3).astype(np.float32)
+    codes, scales = oracle.mx_quantize(a, oracle.MX_FP8, W.DT_F32)
+    X = np.repeat(2.0 ** (scales.astype(np.float64) - 127), 32, axis=1)
+    q = (a / X).astype(np.float32)
+    ok = np.abs(q) <= 448
+    ref = torch.from_numpy(q).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert ok.mean() > 0.9 and np.array_equal(codes[ok], ref[ok])
+
+
+def _representable(rng, shape, fmt):
+    """Values whose MX quantisation is exact: per 32-block, a random element set times 2^s with the
+    block's largest magnitude in the format's top binade (so the shared scale is 2^s exactly)."""
+    if fmt == oracle.MX_FP8:
+        pool = np.arange(-14, 15, dtype=np.float64)  # 32 v is representable for |v| <= 14; amax >= 8
+        top = np.array([8.0, 9.0, 10.0, 12.0, 14.0])
+    else:
+        pool = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6, -0.5, -1, -1.5, -2, -3, -4, -6], np.float64)
+        top = np.array([4.0, 6.0, -4.0, -6.0])
+    v = rng.choice(pool, size=shape)
+    blocks = v.reshape(-1, 32)
+    blocks[:, 0] = rng.choice(top, size=blocks.shape[0])
+    scale = 2.0 ** rng.integers(-3, 3, size=(blocks.shape[0], 1))
+    return (blocks * scale).reshape(shape)
+
+
+@pytest.mark.parametrize("wfmt", [oracle.MX_FP8, oracle.MX_FP4])
+def test_mx_ffn_on_exact_operands_matches_torch(wfmt):
+    # operands that quantise exactly: fc1's pre-activation is the exact product sum, h is
+    # act(pre) rounded to fp32 and MX-quantised, and y = deq(hq) . W2^T + b2 rounded to bf16
+    rng = np.random.default_rng(50 + wfmt)
+    E, C, M, H = 2, 3, 64, 96
+    x = _representable(rng, (E * C, M), oracle.MX_FP8)
+    W1 = _representable(rng, (E, H, M), wfmt)
+    W2 = _representable(rng, (E, M, H), wfmt)
+    b1 = bf16_bits_of_f32(rng.standard_normal((E, H)).astype(np.float32))
+    b2 = bf16_bits_of_f32(rng.standard_normal((E, M)).astype(np.float32))
+    bufq = oracle.mx_quantize(x.astype(np.float32), oracle.MX_FP8, W.DT_F32)
+    W1q = oracle.mx_quantize(W1.astype(np.float32), wfmt, W.DT_F32)
+    W2q = oracle.mx_quantize(W2.astype(np.float32), wfmt, W.DT_F32)
+    assert np.array_equal(oracle.mx_dequantize(*bufq, oracle.MX_FP8), x)
+    assert np.array_equal(oracle.mx_dequantize(*W1q, wfmt), W1)
+    rows = np.arange(E * C)
+    hq, y = oracle.expert_rows_mx(bufq, W1q, b1, W2q, b2, rows, C, W.ACT_GELU, wfmt, want_hq=True)
+    for r in rows:
+        e = r // C
+        pre = torch.from_numpy(x[r]) @ torch.from_numpy(W1[e]).T + torch.from_numpy(f32_of(b1[e]).astype(np.float64))
+        h32 = torch.nn.functional.gelu(pre).to(torch.float32).numpy()
+        hc, hs = oracle.mx_quantize(h32[None], oracle.MX_FP8, W.DT_F32)
+        assert np.array_equal(hc[0], hq[0][r]) and np.array_equal(hs[0], hq[1][r])
+        hd = oracle.mx_dequantize(hc, hs, oracle.MX_FP8)[0]
+        yr = torch.from_numpy(hd) @ torch.from_numpy(W2[e]).T + torch.from_numpy(f32_of(b2[e]).astype(np.float64))
+        assert np.array_equal(y[r], bf16_bits_of_f32(yr.numpy().astype(np.float32))) or \
+            np.abs(f32_of(y[r]) - yr.numpy()).max() <= 2 ** -8 * np.abs(yr.numpy()).max()
