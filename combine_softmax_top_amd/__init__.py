@@ -21,6 +21,7 @@ LIB_PATH = os.path.join(HERE, "libmoe.so")
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP = 0, -1, -2, -3, -4
 MOE_DT_F32, MOE_DT_BF16 = 0, 1
 MOE_ACT_RELU, MOE_ACT_GELU = 0, 1
+MOE_MX_FP8, MOE_MX_FP4 = 0, 1
 
 STATUS_NAMES = {0: "MOE_OK", -1: "MOE_EINVAL", -2: "MOE_EUNSUPPORTED", -3: "MOE_EWORKSPACE", -4: "MOE_EHIP"}
 
@@ -83,6 +84,12 @@ _SIGS = {
     "moe_expert_fc2": [_SP, _P, _P, _P, _P, _P, _P, _P],
     "moe_decode": [_SP, _P, _P, _P, _P, _P, _P, _P],
     "moe_layer_forward": [_SP] + [_P] * 21 + [ctypes.c_size_t, _P],
+    "moe_mx_quantize": [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _P, _P, _P, _P],
+    "moe_encode_mx": [_SP] + [_P] * 8,
+    "moe_expert_ffn_mx": [_SP, ctypes.c_int32] + [_P] * 14,
+    "moe_layer_forward_mx": [_SP, ctypes.c_int32] + [_P] * 24 + [ctypes.c_size_t, _P],
+    "moe_expert_fc1_mx": [_SP, ctypes.c_int32] + [_P] * 10,
+    "moe_expert_fc2_mx": [_SP, ctypes.c_int32] + [_P] * 9,
     "moe_residual_ffn": [_SP] + [_P] * 8 + [ctypes.c_size_t, _P],
     "moe_decode_residual": [_SP] + [_P] * 8,
     "moe_residual_layer_forward": [_SP] + [_P] * 27 + [ctypes.c_size_t, _P],
@@ -179,6 +186,80 @@ def moe_decode(shape: Shape, y, gates, idx, loc, capacity, out, stream=None) -> 
 
 def _ws_args(ws):
     return _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size()
+
+
+def moe_mx_quantize(fmt: int, src, codes, scales, dtype: int = None, stream=None) -> None:
+    """MX-quantise the rows of ``src`` ([..., K], fp32 or bf16) into codes / scales (uint8)."""
+    K = src.shape[-1]
+    rows = src.numel() // K if K else 0
+    if dtype is None:
+        dtype = MOE_DT_F32 if src.dtype == torch.float32 else MOE_DT_BF16
+    _check(_lib.moe_mx_quantize(fmt, rows, K, dtype, _ptr(src), _ptr(codes), _ptr(scales), _stream(stream)))
+
+
+def mx_alloc(shape_rows_k, fmt: int, device="cuda"):
+    """Empty (codes, scales) for an MX matrix of the given [..., K] shape."""
+    *lead, K = shape_rows_k
+    cb = K if fmt == MOE_MX_FP8 else K // 2
+    return (torch.empty(*lead, cb, dtype=torch.uint8, device=device),
+            torch.empty(*lead, K // 32, dtype=torch.uint8, device=device))
+
+
+def mx_quantize_weights(W, fmt: int):
+    """(codes, scales) of a weight tensor quantised along its last (input) dimension."""
+    codes, scales = mx_alloc(tuple(W.shape), fmt, W.device)
+    moe_mx_quantize(fmt, W, codes, scales)
+    return codes, scales
+
+
+def moe_encode_mx(shape: Shape, x, idx, loc, fill, capacity, buf_codes, buf_scales, stream=None) -> None:
+    _check(_lib.moe_encode_mx(ctypes.byref(shape.c()), _ptr(x), _ptr(idx), _ptr(loc), _ptr(fill), _ptr(capacity),
+                              _ptr(buf_codes), _ptr(buf_scales), _stream(stream)))
+
+
+def moe_expert_ffn_mx(shape: Shape, wfmt: int, buf_codes, buf_scales, W1q, b1, W2q, b2, fill, capacity, h_codes,
+                      h_scales, y, stream=None) -> None:
+    _check(_lib.moe_expert_ffn_mx(ctypes.byref(shape.c()), wfmt, _ptr(buf_codes), _ptr(buf_scales), _ptr(W1q[0]),
+                                  _ptr(W1q[1]), _ptr(b1), _ptr(W2q[0]), _ptr(W2q[1]), _ptr(b2), _ptr(fill),
+                                  _ptr(capacity), _ptr(h_codes), _ptr(h_scales), _ptr(y), _stream(stream)))
+
+
+def moe_expert_fc1_mx(shape: Shape, wfmt: int, buf_codes, buf_scales, W1q, b1, fill, capacity, h_codes, h_scales,
+                      stream=None) -> None:
+    _check(_lib.moe_expert_fc1_mx(ctypes.byref(shape.c()), wfmt, _ptr(buf_codes), _ptr(buf_scales), _ptr(W1q[0]),
+                                  _ptr(W1q[1]), _ptr(b1), _ptr(fill), _ptr(capacity), _ptr(h_codes), _ptr(h_scales),
+                                  _stream(stream)))
+
+
+def moe_expert_fc2_mx(shape: Shape, wfmt: int, h_codes, h_scales, W2q, b2, fill, capacity, y, stream=None) -> None:
+    _check(_lib.moe_expert_fc2_mx(ctypes.byref(shape.c()), wfmt, _ptr(h_codes), _ptr(h_scales), _ptr(W2q[0]),
+                                  _ptr(W2q[1]), _ptr(b2), _ptr(fill), _ptr(capacity), _ptr(y), _stream(stream)))
+
+
+def alloc_forward_mx(shape: Shape, device="cuda", gate_projection: bool = False) -> Dict[str, torch.Tensor]:
+    """Buffers of the MX forward: the bf16 forward's route tables, out, y and workspace, with
+    the expert buffer and h as MXFP8 codes and scales."""
+    b = alloc_forward(shape, device, gate_projection=gate_projection)
+    cmax = moe_capacity_bound(shape)
+    S, M, E, H = shape.S, shape.M, shape.E, shape.H
+    b["buf_codes"], b["buf_scales"] = mx_alloc((E * cmax, M), MOE_MX_FP8, device)
+    b["h_codes"], b["h_scales"] = mx_alloc((E * cmax, H), MOE_MX_FP8, device)
+    del b["buf"], b["h"]
+    return b
+
+
+def layer_forward_mx(shape: Shape, wfmt: int, x, W1q, b1, W2q, b2, logits=None, Wg=None, bufs=None, stream=None):
+    """The fused MX forward (W1q, W2q = (codes, scales) from mx_quantize_weights)."""
+    if bufs is None:
+        bufs = alloc_forward_mx(shape, x.device, gate_projection=Wg is not None)
+    lo = bufs["logits"] if Wg is not None else None
+    _check(_lib.moe_layer_forward_mx(
+        ctypes.byref(shape.c()), wfmt, _ptr(x), _ptr(logits), _ptr(Wg), _ptr(lo), _ptr(W1q[0]), _ptr(W1q[1]),
+        _ptr(b1), _ptr(W2q[0]), _ptr(W2q[1]), _ptr(b2), _ptr(bufs["idx"]), _ptr(bufs["loc"]), _ptr(bufs["gates"]),
+        _ptr(bufs["needed"]), _ptr(bufs["fill"]), _ptr(bufs["capacity"]), _ptr(bufs["slot_route"]),
+        _ptr(bufs["buf_codes"]), _ptr(bufs["buf_scales"]), _ptr(bufs["h_codes"]), _ptr(bufs["h_scales"]),
+        _ptr(bufs["y"]), _ptr(bufs["out"]), *_ws_args(bufs["ws"]), _stream(stream)))
+    return bufs
 
 
 def moe_residual_ffn(shape: Shape, x, W1r, b1r, W2r, b2r, h_r, y_r, ws, stream=None) -> None:

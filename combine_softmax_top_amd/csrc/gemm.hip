@@ -726,6 +726,284 @@ __global__ __launch_bounds__(NTH, 1) void rows_gemm_big(const bf16_t *__restrict
     wait_vmcnt<0>();  // no direct-to-LDS write may land after the workgroup's LDS is released
 }
 
+// ------------------------------------------------------------------ rows-grouped MX GEMM (MXFP8 / MXFP4)
+
+// The expert FFN on MX operands (OCP microscaling: 32-value blocks along K share
+// an E8M0 scale) with gfx950's scaled MFMA v_mfma_scale_f32_32x32x64_f8f6f4:
+// A = the tokens (MXFP8), B = the weights (MXFP8 or MXFP4), both k-contiguous
+// codes with per-row scale bytes [rows][K/32]. Same persistent, XCD-aware tile
+// walk and ping-pong ring of direct loads as the bf16 kernel; a ring stage
+// holds 128 k (128 bytes per token row, 128 or 64 per weight row) and feeds two
+// 64-wide MFMA slices. Operand layout of the scaled MFMA (checked on the GPU):
+// lane l holds row l % 32; with 8-bit elements lane half h = l / 32 holds the
+// slice's bytes [16h, 16h+16) and [32+16h, 32+16h+16) (two 16-byte LDS reads),
+// with 4-bit elements bytes [16h, 16h+16) (32 values); the scale of k-block h of
+// the slice comes from lane half h. Each lane loads, one stage ahead, the four
+// scale bytes of a stage for each of its rows (one dword) and picks byte
+// 2 * slice + h. The hardware's fp8 accumulation drops low-order bits of products
+// far below the largest one in a group of eight (about 1e-4 of the sum of
+// magnitudes), so results match an exact sum within that, not bit for bit.
+// Epilogues: fc1 adds the bias, applies the activation and quantises h to MXFP8
+// per (token, 32 features): the two lanes l, l ^ 32 holding a token's 32
+// features of a block exchange their amax, codes and scales go through LDS to
+// whole-row stores; fc2 adds the bias and stores bf16 as the bf16 kernel does.
+typedef int mx_v8i __attribute__((ext_vector_type(8)));
+
+constexpr int kMxStageK = 128;  // k per ring stage
+
+// Bytes of the LDS region shared by the two ring stages and the epilogue tile
+// (bf16 y of fc2, or fc1's h codes and scales), then the tile prefix and bias.
+template <int BM, int BN, int WFMT, int EPI>
+constexpr int mx_region_bytes() {
+    constexpr int ring = 2 * (BM * kMxStageK + BN * (WFMT == kMxFp8 ? kMxStageK : kMxStageK / 2));
+    constexpr int epi = EPI == EPI_FC1 ? BM * BN + BM * BN / 32 : BM * BN * 2;
+    return ring > epi ? ring : epi;
+}
+template <int BM, int BN, int WFMT, int EPI>
+constexpr int mx_lds_bytes() {
+    return mx_region_bytes<BM, BN, WFMT, EPI>() + kBigPrefixBytes + BN * 2;
+}
+
+// MFMA operand of one row (the lane's) for slice s from an LDS tile of rows of
+// RB bytes (CPR = RB / 16 chunks, swizzled by swz_chunk on bf16 units).
+template <int RB, bool FP4>
+__device__ __forceinline__ mx_v8i mx_frag(const bf16_t *tile, int row, int s, int h) {
+    constexpr int KBU = RB / 2;  // row length in bf16 units
+    const bf16_t *base = tile + row * KBU;
+    mx_v8i v;
+    if constexpr (FP4) {
+        const uint4 a = *reinterpret_cast<const uint4 *>(base + (swz_chunk<KBU>(row, 2 * s + h) << 3));
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+        v[4] = 0; v[5] = 0; v[6] = 0; v[7] = 0;
+    } else {
+        const uint4 a = *reinterpret_cast<const uint4 *>(base + (swz_chunk<KBU>(row, 4 * s + h) << 3));
+        const uint4 b = *reinterpret_cast<const uint4 *>(base + (swz_chunk<KBU>(row, 4 * s + 2 + h) << 3));
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    }
+    return v;
+}
+
+template <int BM, int BN, int NTH, int EPI, int ACT, int WFMT>
+__global__ __launch_bounds__(NTH, 1) void rows_gemm_mx(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
+                                                     const uint8_t *__restrict__ B, const uint8_t *__restrict__ Bs,
+                                                     void *__restrict__ D, uint8_t *__restrict__ Dsc, int N, int K,
+                                                     int E, const int32_t *__restrict__ fill,
+                                                     const int32_t *__restrict__ cap,
+                                                     const bf16_t *__restrict__ bias) {
+    extern __shared__ __align__(16) bf16_t lds[];
+    constexpr bool FP4 = WFMT == kMxFp4;
+    constexpr int RA = kMxStageK, RBW = FP4 ? kMxStageK / 2 : kMxStageK;  // bytes per row per stage
+    constexpr int KA = RA / 2, KW = RBW / 2;                              // ... in bf16 units
+    constexpr int NW = NTH / 64, WGC = NW / 2;
+    constexpr int TM = BM / 64, TN = BN / (32 * WGC);
+    static_assert(TN >= 1 && BN % (32 * WGC) == 0, "wavefront columns must be whole 32-wide blocks");
+    constexpr int STAGE = BM * KA + BN * KW;  // bf16 units
+    constexpr int REGION = mx_region_bytes<BM, BN, WFMT, EPI>() / 2;
+    int *prefix = reinterpret_cast<int *>(lds + REGION);
+    bf16_t *sbias = lds + REGION + kBigPrefixBytes / 2;
+    const int nx = (N + BN - 1) / BN;
+    const TileSched sc = make_sched<NTH>(fill, E, BM, nx, prefix);
+    const int C = *cap;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5;
+    const int wr0 = (wave / WGC) * (BM / 2), wc0 = (wave % WGC) * (BN / WGC);
+    const int nk = K / kMxStageK, KS = K / 32;  // stages, scale bytes per row
+    const int ldA = K / 2, ldB = FP4 ? K / 4 : K / 2;   // row length in bf16 units
+    constexpr int WCODE = FP4 ? 4 : 0;                  // scaled-MFMA operand formats: 4 = E2M1, 0 = E4M3
+    for (int L = sc.first; L < sc.end; L += sc.stride) {
+        int g, rtile, ctile;
+        decode_tile(L, prefix, E, nx, g, rtile, ctile);
+        const int row0 = rtile * BM, col0 = ctile * BN;
+        const int rows_valid = min(BM, fill[g] - row0);
+        const int cols_valid = min(BN, N - col0);
+        const int64_t grow0 = static_cast<int64_t>(g) * C + row0;
+        const bf16_t *Ab = reinterpret_cast<const bf16_t *>(A + grow0 * K);
+        const int64_t wrow0 = static_cast<int64_t>(g) * N + col0;  // first weight row of the tile
+        const bf16_t *Bb = reinterpret_cast<const bf16_t *>(B + wrow0 * (FP4 ? K / 2 : K));
+        // the lane's scale rows (clamped into the valid range; clamped rows are never stored)
+        const uint32_t *sa_row[TM];
+        const uint32_t *sb_row[TN];
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const int r = min(wr0 + i * 32 + (lane & 31), rows_valid - 1);
+            sa_row[i] = reinterpret_cast<const uint32_t *>(As + (grow0 + r) * KS);
+        }
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int c = min(wc0 + j * 32 + (lane & 31), cols_valid - 1);
+            sb_row[j] = reinterpret_cast<const uint32_t *>(Bs + (wrow0 + c) * KS);
+        }
+
+        f32x16 acc[TM][TN];
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+        barrier_keep_loads_lds();  // the previous tile's epilogue reads of LDS are complete
+        if (bias != nullptr && wave == 0 && lane < BN / 8) {
+            const int c = min(lane * 8, cols_valid - 8);
+            __builtin_amdgcn_global_load_lds(bias + wrow0 + c, (lds_void_t *)sbias, 16, 0, 0);
+        }
+        // stage 0's scales, then the ring's first two stages (loads complete in order)
+        uint32_t sa_cur[TM], sb_cur[TN], sa_nxt[TM], sb_nxt[TN];
+#pragma unroll
+        for (int i = 0; i < TM; ++i) sa_cur[i] = sa_row[i][0];
+#pragma unroll
+        for (int j = 0; j < TN; ++j) sb_cur[j] = sb_row[j][0];
+        dma_tile<BM, KA, NW>(Ab, ldA, rows_valid, 0, lds, wave, lane);
+        dma_tile<BN, KW, NW>(Bb, ldB, cols_valid, 0, lds + BM * KA, wave, lane);
+        if (nk > 1) {
+            dma_tile<BM, KA, NW>(Ab, ldA, rows_valid, KA, lds + STAGE, wave, lane);
+            dma_tile<BN, KW, NW>(Bb, ldB, cols_valid, KW, lds + STAGE + BM * KA, wave, lane);
+            wait_vmcnt<(BM * KA + BN * KW) / 8 / NTH>();
+        } else {
+            wait_vmcnt<0>();
+        }
+        barrier_keep_loads();
+        for (int t = 0; t < nk; ++t) {
+            const bf16_t *scur = lds + (t & 1) * STAGE;
+            if (t + 1 < nk) {  // next stage's scales, one dword (four blocks) per row
+#pragma unroll
+                for (int i = 0; i < TM; ++i) sa_nxt[i] = sa_row[i][t + 1];
+#pragma unroll
+                for (int j = 0; j < TN; ++j) sb_nxt[j] = sb_row[j][t + 1];
+            }
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                mx_v8i fa[TM], fb[TN];
+#pragma unroll
+                for (int i = 0; i < TM; ++i) fa[i] = mx_frag<RA, false>(scur, wr0 + i * 32 + (lane & 31), s, h);
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+                    fb[j] = mx_frag<RBW, FP4>(scur + BM * KA, wc0 + j * 32 + (lane & 31), s, h);
+                const int sh = 8 * (2 * s + h);
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+#pragma unroll
+                    for (int j = 0; j < TN; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                            fb[j], fa[i], acc[i][j], WCODE, 0, 0, static_cast<int>((sb_cur[j] >> sh) & 0xFFu), 0,
+                            static_cast<int>((sa_cur[i] >> sh) & 0xFFu));
+            }
+            wait_vmcnt<0>();  // stage t+1's ring loads and scales have landed
+            barrier_keep_loads_lds();
+            if (t + 2 < nk) {
+                bf16_t *sn = lds + (t & 1) * STAGE;
+                dma_tile<BM, KA, NW>(Ab, ldA, rows_valid, (t + 2) * KA, sn, wave, lane);
+                dma_tile<BN, KW, NW>(Bb, ldB, cols_valid, (t + 2) * KW, sn + BM * KA, wave, lane);
+            }
+#pragma unroll
+            for (int i = 0; i < TM; ++i) sa_cur[i] = sa_nxt[i];
+#pragma unroll
+            for (int j = 0; j < TN; ++j) sb_cur[j] = sb_nxt[j];
+        }
+        wait_vmcnt<0>();
+        barrier_keep_loads_lds();  // every wavefront is done with the ring
+
+        if constexpr (EPI == EPI_FC1) {
+            // h = act(acc + b1) quantised to MXFP8 per (token, 32-feature block); codes staged as a
+            // row-major BM x BN byte tile (16-byte chunks XOR-swizzled by row), scales as [BM][BN/32]
+            constexpr int CH = BN / 16;
+            uint8_t *scodes = reinterpret_cast<uint8_t *>(lds);
+            uint8_t *sscale = scodes + BM * BN;
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+                const int trow = wr0 + i * 32 + (lane & 31);
+#pragma unroll
+                for (int j = 0; j < TN; ++j) {
+                    float v[16];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int tcol = wc0 + j * 32 + 8 * q + 4 * h;
+                        float b4[4] = {0.f, 0.f, 0.f, 0.f};
+                        if (bias != nullptr) {
+                            const uint2 u2 = *reinterpret_cast<const uint2 *>(sbias + tcol);
+                            b4[0] = __uint_as_float(u2.x << 16);
+                            b4[1] = __uint_as_float(u2.x & 0xFFFF0000u);
+                            b4[2] = __uint_as_float(u2.y << 16);
+                            b4[3] = __uint_as_float(u2.y & 0xFFFF0000u);
+                        }
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) v[4 * q + r] = act_fast<ACT>(acc[i][j][4 * q + r] + b4[r]);
+                    }
+                    float amax = 0.f;
+#pragma unroll
+                    for (int u = 0; u < 16; ++u) amax = fmaxf(amax, fabsf(v[u]));
+                    amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+                    const int e = mx_shared_exp(amax, 8);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const uint32_t lo = mx_fp8x2(ldexpf(v[4 * q], -e), ldexpf(v[4 * q + 1], -e));
+                        const uint32_t hi = mx_fp8x2(ldexpf(v[4 * q + 2], -e), ldexpf(v[4 * q + 3], -e));
+                        const int tcol = wc0 + j * 32 + 8 * q + 4 * h;
+                        *reinterpret_cast<uint32_t *>(scodes + trow * BN + (epi_swz<CH>(trow, tcol >> 4) << 4) +
+                                                      (tcol & 15)) = lo | (hi << 16);
+                    }
+                    if (h == 0) sscale[trow * (BN / 32) + (wc0 + j * 32) / 32] = static_cast<uint8_t>(e + 127);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+            barrier_keep_loads_lds();
+            uint8_t *Dc = static_cast<uint8_t *>(D);
+#pragma unroll 4
+            for (int u = 0; u < BM * CH / NTH; ++u) {
+                const int idx = tid + u * NTH, r = idx / CH, c = idx % CH;
+                const uint4 v = *reinterpret_cast<const uint4 *>(scodes + r * BN + (epi_swz<CH>(r, c) << 4));
+                if (r < rows_valid && c * 16 < cols_valid)
+                    *reinterpret_cast<uint4 *>(Dc + (grow0 + r) * N + col0 + c * 16) = v;
+            }
+            for (int idx = tid; idx < BM * (BN / 128); idx += NTH) {  // four scale bytes (128 features) per store
+                const int r = idx / (BN / 128), c = idx % (BN / 128);
+                if (r < rows_valid && c * 128 < cols_valid)
+                    *reinterpret_cast<uint32_t *>(Dsc + (grow0 + r) * (N / 32) + col0 / 32 + c * 4) =
+                        *reinterpret_cast<const uint32_t *>(sscale + r * (BN / 32) + c * 4);
+            }
+        } else {
+            // y = acc + b2, bf16, staged like the bf16 kernel's epilogue
+            constexpr int CH = BN / 8;
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+                const int trow = wr0 + i * 32 + (lane & 31);
+#pragma unroll
+                for (int j = 0; j < TN; ++j) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int tcol = wc0 + j * 32 + 8 * q + 4 * h;
+                        f32x2 lo = {acc[i][j][4 * q], acc[i][j][4 * q + 1]};
+                        f32x2 hi = {acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+                        if (bias != nullptr) {
+                            const uint2 u2 = *reinterpret_cast<const uint2 *>(sbias + tcol);
+                            lo[0] += __uint_as_float(u2.x << 16);
+                            lo[1] += __uint_as_float(u2.x & 0xFFFF0000u);
+                            hi[0] += __uint_as_float(u2.y << 16);
+                            hi[1] += __uint_as_float(u2.y & 0xFFFF0000u);
+                        }
+                        const bf16x2 plo = __builtin_convertvector(lo, bf16x2);
+                        const bf16x2 phi = __builtin_convertvector(hi, bf16x2);
+                        uint2 w;
+                        w.x = *reinterpret_cast<const uint32_t *>(&plo);
+                        w.y = *reinterpret_cast<const uint32_t *>(&phi);
+                        *reinterpret_cast<uint2 *>(lds + trow * BN + (epi_swz<CH>(trow, tcol >> 3) << 3) + (4 * h)) = w;
+                    }
+                }
+            }
+            barrier_keep_loads_lds();
+            bf16_t *Dy = static_cast<bf16_t *>(D);
+#pragma unroll 4
+            for (int u = 0; u < BM * CH / NTH; ++u) {
+                const int idx = tid + u * NTH, r = idx / CH, c = idx % CH;
+                const uint4 v = *reinterpret_cast<const uint4 *>(lds + r * BN + (epi_swz<CH>(r, c) << 3));
+                if (r < rows_valid && c * 8 < cols_valid)
+                    *reinterpret_cast<uint4 *>(Dy + (grow0 + r) * N + col0 + c * 8) = v;
+            }
+        }
+    }
+    wait_vmcnt<0>();
+}
+
 // ------------------------------------------------------------------ weight gradients, large tiles
 
 // D[e][p][q] = sum over the filled rows r < fill[e] of X[e*C + r][p] * Y[e*C + r][q]
@@ -1228,6 +1506,79 @@ hipError_t launch_fc2(const moe_shape &s, const void *h, const void *W2, const v
     b.N = M; b.K = H; b.kgrouped = 0; b.fill = fill; b.cap = cap;
     b.bias = static_cast<const float *>(b2);
     return simt_launch<EPI_FC2>(b, s.act, cmax, E, st);
+}
+
+template <int BM, int BN, int NTH, int EPI, int WFMT>
+hipError_t mx_launch(int act, const uint8_t *A, const uint8_t *As, const uint8_t *B, const uint8_t *Bs, void *D,
+                     uint8_t *Dsc, int N, int K, int E, const int32_t *fill, const int32_t *cap, const void *bias,
+                     hipStream_t st) {
+    constexpr int lds = mx_lds_bytes<BM, BN, WFMT, EPI>();
+    constexpr int per_cu = (160 * 1024) / lds >= 2 ? 2 : 1;
+    const dim3 grid(resident_blocks(per_cu));
+    auto bi = static_cast<const bf16_t *>(bias);
+    if (act == MOE_ACT_GELU) {
+        auto k = rows_gemm_mx<BM, BN, NTH, EPI, MOE_ACT_GELU, WFMT>;
+        static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(k),
+                                                           hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+        if (attr != hipSuccess) return attr;
+        hipLaunchKernelGGL(k, grid, dim3(NTH), lds, st, A, As, B, Bs, D, Dsc, N, K, E, fill, cap, bi);
+    } else {
+        auto k = rows_gemm_mx<BM, BN, NTH, EPI, MOE_ACT_RELU, WFMT>;
+        static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(k),
+                                                           hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+        if (attr != hipSuccess) return attr;
+        hipLaunchKernelGGL(k, grid, dim3(NTH), lds, st, A, As, B, Bs, D, Dsc, N, K, E, fill, cap, bi);
+    }
+    return hipGetLastError();
+}
+
+template <int EPI, int WFMT>
+hipError_t mx_product(int act, const uint8_t *A, const uint8_t *As, const uint8_t *B, const uint8_t *Bs, void *D,
+                      uint8_t *Dsc, int N, int K, int E, const int32_t *fill, const int32_t *cap, const void *bias,
+                      int64_t rows_hint, hipStream_t st) {
+    // 128 x 128 tiles by default: with 8-bit operands a tile moves half the LDS bytes per
+    // flop of a bf16 one, and the 256 x 256 layout runs out of registers (MOE_GEMM_CFG
+    // selects the others for measurement)
+    (void)rows_hint;
+    const int cfg = gemm_cfg_override();
+    switch (cfg) {
+    case 1: return mx_launch<256, 256, 512, EPI, WFMT>(act, A, As, B, Bs, D, Dsc, N, K, E, fill, cap, bias, st);
+    case 2: return mx_launch<256, 128, 256, EPI, WFMT>(act, A, As, B, Bs, D, Dsc, N, K, E, fill, cap, bias, st);
+    default: return mx_launch<128, 128, 256, EPI, WFMT>(act, A, As, B, Bs, D, Dsc, N, K, E, fill, cap, bias, st);
+    }
+}
+
+hipError_t launch_fc1_mx(const moe_shape &s, int wfmt, const uint8_t *buf_codes, const uint8_t *buf_scales,
+                         const uint8_t *w1_codes, const uint8_t *w1_scales, const void *b1, const int32_t *fill,
+                         const int32_t *cap, uint8_t *h_codes, uint8_t *h_scales, int32_t cmax, hipStream_t st) {
+    const int64_t rh = rows_hint(s, cmax);
+    if (wfmt == kMxFp8)
+        return mx_product<EPI_FC1, kMxFp8>(s.act, buf_codes, buf_scales, w1_codes, w1_scales, h_codes, h_scales, s.H,
+                                           s.M, s.E, fill, cap, b1, rh, st);
+    return mx_product<EPI_FC1, kMxFp4>(s.act, buf_codes, buf_scales, w1_codes, w1_scales, h_codes, h_scales, s.H, s.M,
+                                       s.E, fill, cap, b1, rh, st);
+}
+
+hipError_t launch_fc2_mx(const moe_shape &s, int wfmt, const uint8_t *h_codes, const uint8_t *h_scales,
+                         const uint8_t *w2_codes, const uint8_t *w2_scales, const void *b2, const int32_t *fill,
+                         const int32_t *cap, void *y, int32_t cmax, hipStream_t st) {
+    const int64_t rh = rows_hint(s, cmax);
+    if (wfmt == kMxFp8)
+        return mx_product<EPI_FC2, kMxFp8>(s.act, h_codes, h_scales, w2_codes, w2_scales, y, nullptr, s.M, s.H, s.E,
+                                           fill, cap, b2, rh, st);
+    return mx_product<EPI_FC2, kMxFp4>(s.act, h_codes, h_scales, w2_codes, w2_scales, y, nullptr, s.M, s.H, s.E, fill,
+                                       cap, b2, rh, st);
+}
+
+hipError_t launch_expert_ffn_mx(const moe_shape &s, int wfmt, const uint8_t *buf_codes, const uint8_t *buf_scales,
+                                const uint8_t *w1_codes, const uint8_t *w1_scales, const void *b1,
+                                const uint8_t *w2_codes, const uint8_t *w2_scales, const void *b2,
+                                const int32_t *fill, const int32_t *cap, uint8_t *h_codes, uint8_t *h_scales, void *y,
+                                int32_t cmax, hipStream_t st) {
+    hipError_t err = launch_fc1_mx(s, wfmt, buf_codes, buf_scales, w1_codes, w1_scales, b1, fill, cap, h_codes,
+                                   h_scales, cmax, st);
+    if (err != hipSuccess) return err;
+    return launch_fc2_mx(s, wfmt, h_codes, h_scales, w2_codes, w2_scales, b2, fill, cap, y, cmax, st);
 }
 
 hipError_t launch_expert_ffn_bwd(const moe_shape &s, const void *buf, const void *pre, const void *h, const void *W1,

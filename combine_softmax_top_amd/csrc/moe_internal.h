@@ -95,6 +95,36 @@ __device__ __forceinline__ float act_grad_f(float v) {
     else return gelu_grad_f(v);
 }
 
+// ------------------------------------------------------------- MX (OCP microscaling) elements
+// Blocks of 32 values along the reduction dimension share an E8M0 scale 2^(b - 127);
+// MXFP8 elements are E4M3 (max 448), MXFP4 elements E2M1 (max 6), two per byte (even
+// index in the low nibble). A block's shared exponent is floor(log2 amax) - emax_elem
+// (8 for E4M3, 2 for E2M1), clamped to [-127, 127], and -127 for an all-zero block.
+constexpr int kMxFp8 = 0, kMxFp4 = 1;
+
+__device__ __forceinline__ int mx_shared_exp(float amax, int emax) {
+    if (!(amax > 0.f)) return -127;
+    int ex;
+    (void)frexpf(amax, &ex);  // amax = f * 2^ex, f in [0.5, 1)
+    const int e = ex - 1 - emax;
+    return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+// Two values (already divided by the block scale) -> two E4M3 codes in the low 16
+// bits: the conversion rounds to nearest even; values beyond 448 are clamped first
+// (the conversion itself would give NaN above 464). The sign of zero is kept.
+__device__ __forceinline__ uint32_t mx_fp8x2(float a, float b) {
+    a = fminf(fmaxf(a, -448.f), 448.f);
+    b = fminf(fmaxf(b, -448.f), 448.f);
+    return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false)) & 0xFFFFu;
+}
+// One value (already divided by the block scale) -> E2M1 code: nearest of 0, 0.5, 1,
+// 1.5, 2, 3, 4, 6, ties to the even code, saturating at 6, sign bit 8.
+__device__ __forceinline__ uint32_t mx_fp4(float q) {
+    const float a = fabsf(q);
+    const uint32_t c = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) + (a > 2.5f) + (a >= 3.5f) + (a > 5.0f);
+    return c | (signbit(q) ? 8u : 0u);
+}
+
 // ------------------------------------------------------------- host launchers
 // Each returns hipSuccess or the launch error; arguments were validated by the
 // caller. `cap` and `fill` are device pointers written by the routing step.
@@ -141,6 +171,24 @@ hipError_t launch_gate_weight_grad(const moe_shape &s, const void *x, const floa
                                    hipStream_t st);
 hipError_t launch_gate_dx(const moe_shape &s, const void *dbuf, const int32_t *idx, const int32_t *loc,
                           const int32_t *cap, const float *dlogits, const float *Wg, void *dx, hipStream_t st);
+// MX: quantise a row-major [rows, K] matrix (K a multiple of 32) of the data type;
+// encode with the token rows quantised to MXFP8; the expert FFN on MX operands.
+hipError_t launch_mx_quantize(int fmt, int64_t rows, int32_t K, int dtype, const void *src, uint8_t *codes,
+                              uint8_t *scales, hipStream_t st);
+hipError_t launch_encode_mx(const moe_shape &s, const void *x, const int32_t *idx, const int32_t *loc,
+                            const int32_t *fill, const int32_t *cap, uint8_t *buf_codes, uint8_t *buf_scales,
+                            int32_t cmax, hipStream_t st);
+hipError_t launch_fc1_mx(const moe_shape &s, int wfmt, const uint8_t *buf_codes, const uint8_t *buf_scales,
+                         const uint8_t *w1_codes, const uint8_t *w1_scales, const void *b1, const int32_t *fill,
+                         const int32_t *cap, uint8_t *h_codes, uint8_t *h_scales, int32_t cmax, hipStream_t st);
+hipError_t launch_fc2_mx(const moe_shape &s, int wfmt, const uint8_t *h_codes, const uint8_t *h_scales,
+                         const uint8_t *w2_codes, const uint8_t *w2_scales, const void *b2, const int32_t *fill,
+                         const int32_t *cap, void *y, int32_t cmax, hipStream_t st);
+hipError_t launch_expert_ffn_mx(const moe_shape &s, int wfmt, const uint8_t *buf_codes, const uint8_t *buf_scales,
+                                const uint8_t *w1_codes, const uint8_t *w1_scales, const void *b1,
+                                const uint8_t *w2_codes, const uint8_t *w2_scales, const void *b2,
+                                const int32_t *fill, const int32_t *cap, uint8_t *h_codes, uint8_t *h_scales, void *y,
+                                int32_t cmax, hipStream_t st);
 hipError_t launch_expert_ffn_bwd(const moe_shape &s, const void *buf, const void *pre, const void *h,
                                  const void *W1, const void *W2, const int32_t *fill,
                                  const int32_t *cap, void *dy, void *dpre, void *dbuf, float *dW1,

@@ -72,6 +72,7 @@ typedef enum moe_status {
 
 enum { MOE_DT_F32 = 0, MOE_DT_BF16 = 1 };
 enum { MOE_ACT_RELU = 0, MOE_ACT_GELU = 1 };
+enum { MOE_MX_FP8 = 0, MOE_MX_FP4 = 1 };
 
 /* The layer's sizes and options (Tutel catalogue page, "key configuration":
  * model_dim = M, number of experts = E, gate k and capacity_factor,
@@ -173,6 +174,69 @@ moe_status moe_expert_fc2(const moe_shape *shape, const void *h, const void *W2,
  * whose routes were all dropped gets 0. y [E*cmax, M]; out [S, M]. */
 moe_status moe_decode(const moe_shape *shape, const void *y, const float *gates, const int32_t *idx,
                       const int32_t *loc, const int32_t *capacity, void *out, void *stream);
+
+/* MX low-precision experts (Tutel catalogue page and its project summaries:
+ * FP8 / MXFP4 / block-wise FP8 quantised inference). Format: OCP Microscaling
+ * (MX) -- 32 consecutive values along a row share one E8M0 scale byte b
+ * (2^(b - 127)); elements are E4M3 (MOE_MX_FP8: one byte each, max 448) or
+ * E2M1 (MOE_MX_FP4: two per byte, the even index in the low nibble, max 6).
+ * Quantisation: e = floor(log2 max|v|) - (8 for E4M3, 2 for E2M1), clamped to
+ * [-127, 127] (-127 for an all-zero block); elements = v / 2^e rounded to
+ * nearest, ties to the even code, saturating, the sign kept (also of zero).
+ *
+ * moe_mx_quantize: a row-major [rows, K] matrix of dtype (fp32 or bf16), K a
+ * multiple of 32 -> codes [rows, K] (fp8) or [rows, K/2] (fp4) bytes and
+ * scales [rows, K/32] bytes. For the experts' weights: W1 [E*H, M] and W2
+ * [E*M, H] rows, quantised along their input dimension. */
+moe_status moe_mx_quantize(int32_t fmt, int64_t rows, int32_t K, int32_t dtype, const void *src,
+                           void *codes, void *scales, void *stream);
+
+/* moe_encode with the token rows quantised to MXFP8 on the way: buf_codes
+ * [E*cmax, M] and buf_scales [E*cmax, M/32] bytes, the rows of moe_encode (a
+ * token row quantised once, copied to each kept slot; padding rows are zero
+ * codes with scale byte 0). bf16 x; M a multiple of 128. */
+moe_status moe_encode_mx(const moe_shape *shape, const void *x, const int32_t *idx, const int32_t *loc,
+                         const int32_t *fill, const int32_t *capacity, void *buf_codes, void *buf_scales,
+                         void *stream);
+
+/* Expert FFN on MX operands with gfx950's scaled MFMA, for the filled rows
+ * j < fill[e] (padding rows are not written):
+ *   pre = buf . W1[e]^T + b1[e]  (products of the MX values, fp32 accumulation)
+ *   h   = act(pre) in fp32, quantised to MXFP8 along H: h_codes [E*cmax, H],
+ *         h_scales [E*cmax, H/32]
+ *   y   = h . W2[e]^T + b2[e]    (fp32 accumulation), stored bf16 [E*cmax, M]
+ * W1 codes/scales from moe_mx_quantize of [E*H, M], W2 of [E*M, H], in format
+ * wfmt (the tokens and h are always MXFP8); b1 [E, H], b2 [E, M] bf16 (NULL
+ * iff the bias is off). dtype must be bf16; M and H multiples of 128. The
+ * hardware's fp8 accumulation drops low-order bits of products far below the
+ * largest in groups of eight (about 1e-4 of the sum of magnitudes). */
+moe_status moe_expert_ffn_mx(const moe_shape *shape, int32_t wfmt, const void *buf_codes,
+                             const void *buf_scales, const void *W1_codes, const void *W1_scales,
+                             const void *b1, const void *W2_codes, const void *W2_scales, const void *b2,
+                             const int32_t *fill, const int32_t *capacity, void *h_codes, void *h_scales,
+                             void *y, void *stream);
+
+/* The two halves of moe_expert_ffn_mx (same definitions and row rules):
+ *   moe_expert_fc1_mx: h = MXFP8(act(buf . W1[e]^T + b1[e]))
+ *   moe_expert_fc2_mx: y = h . W2[e]^T + b2[e]                 */
+moe_status moe_expert_fc1_mx(const moe_shape *shape, int32_t wfmt, const void *buf_codes,
+                             const void *buf_scales, const void *W1_codes, const void *W1_scales,
+                             const void *b1, const int32_t *fill, const int32_t *capacity, void *h_codes,
+                             void *h_scales, void *stream);
+moe_status moe_expert_fc2_mx(const moe_shape *shape, int32_t wfmt, const void *h_codes, const void *h_scales,
+                             const void *W2_codes, const void *W2_scales, const void *b2,
+                             const int32_t *fill, const int32_t *capacity, void *y, void *stream);
+
+/* The whole forward with MX experts: [gate projection] -> route ->
+ * moe_encode_mx -> moe_expert_ffn_mx -> moe_decode (bf16 out), arguments as
+ * in moe_layer_forward and the two calls above. */
+moe_status moe_layer_forward_mx(const moe_shape *shape, int32_t wfmt, const void *x, const float *logits_in,
+                                const float *Wg, float *logits_out, const void *W1_codes,
+                                const void *W1_scales, const void *b1, const void *W2_codes,
+                                const void *W2_scales, const void *b2, int32_t *idx, int32_t *loc,
+                                float *gates, int32_t *needed, int32_t *fill, int32_t *capacity,
+                                int32_t *slot_route, void *buf_codes, void *buf_scales, void *h_codes,
+                                void *h_scales, void *y, void *out, void *ws, size_t ws_bytes, void *stream);
 
 /* Residual-MoE (MoE training blog, part 1 section 1.2, the residual half of
  * PR-MoE): every token also passes through one fixed dense MLP, and its output
