@@ -32,6 +32,7 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE-layer tokens/sec on 1 MI355X; encode/decode HBM GB/s; FFN MFMA util"
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 MFMA_BF16_PEAK_TFS = 2500.0  # dense bf16 MFMA
+MFMA_FP8_PEAK_TFS = 5000.0   # dense fp8 MFMA (MX experts: the token operand is always MXFP8)
 FP32_VECTOR_PEAK_TFS = 157.3
 
 
@@ -105,7 +106,8 @@ def algorithmic(w, C, kept):
     S, M, E, k, H = w.S, w.M, w.E, w.k, w.H
     st = {
         "route": ("bytes", 4 * S * E + 12 * k * S + 4 * kept + 8 * E),
-        "encode": ("bytes", S * M * b + E * C * M * b + 8 * k * S),
+        # MX encode writes one code byte per value plus a scale byte per 32
+        "encode": ("bytes", S * M * b + (E * C * M * 33 // 32 if w.mx else E * C * M * b) + 8 * k * S),
         "fc1": ("flops", 2 * M * H * kept),
         "fc2": ("flops", 2 * M * H * kept),
         "decode": ("bytes", kept * M * b + S * M * b + 12 * k * S + (S * M * b if w.residual else 0)),
@@ -127,13 +129,13 @@ def algorithmic(w, C, kept):
     return st
 
 
-def roofline_of(kind, amount, ms, dtype_bf16=True):
+def roofline_of(kind, amount, ms, dtype_bf16=True, mx=False):
     if kind == "bytes":
         ach = amount / (ms * 1e-3) / 1e9
         return dict(bound="hbm", achieved=round(ach, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(ach / HBM_PEAK_GBS, 4))
     ach = amount / (ms * 1e-3) / 1e12
-    peak = MFMA_BF16_PEAK_TFS if dtype_bf16 else FP32_VECTOR_PEAK_TFS
+    peak = MFMA_FP8_PEAK_TFS if mx else (MFMA_BF16_PEAK_TFS if dtype_bf16 else FP32_VECTOR_PEAK_TFS)
     return dict(bound="mfma" if dtype_bf16 else "alu", achieved=round(ach, 2), peak=peak, unit="TFLOP/s",
                 frac=round(ach / peak, 4))
 
@@ -160,16 +162,31 @@ def cpu_baseline(w, inp, C_gpu, budget_s):
     t["encode"] = time.perf_counter() - t0
     rows = oracle.filled_rows(rt)
     kept = len(rows)
+    if w.mx:
+        # MX experts: the token rows are quantised in the encode (timed with it), the weights offline
+        wf = oracle.MX_FP8 if w.mx == "mxfp8" else oracle.MX_FP4
+        t0 = time.perf_counter()
+        bufq = oracle.mx_quantize(buf, oracle.MX_FP8, w.dtype)
+        t["encode"] += time.perf_counter() - t0
+        W1q = oracle.mx_quantize(ni["W1"], wf, w.dtype)
+        W2q = oracle.mx_quantize(ni["W2"], wf, w.dtype)
+
+        def ffn(rs):
+            return None, None, oracle.expert_rows_mx(bufq, W1q, ni.get("b1"), W2q, ni.get("b2"), rs, rt["C"], w.act,
+                                                     wf)[1]
+    else:
+        def ffn(rs):
+            return oracle.expert_rows(buf, ni["W1"], ni.get("b1"), ni["W2"], ni.get("b2"), rs, rt["C"], w.act,
+                                      w.dtype)
     # FFN on an evenly strided sample of the filled rows, sized to about budget_s
     probe = rows[:: max(1, kept // 16)][:16]
     t0 = time.perf_counter()
-    oracle.expert_rows(buf, ni["W1"], ni.get("b1"), ni["W2"], ni.get("b2"), probe, rt["C"], w.act, w.dtype)
+    ffn(probe)
     per_row = (time.perf_counter() - t0) / max(1, len(probe))
     n = int(min(kept, max(16, budget_s / max(per_row, 1e-9))))
     sample = rows[:: max(1, kept // n)][:n]
     t0 = time.perf_counter()
-    _, _, ys = oracle.expert_rows(buf, ni["W1"], ni.get("b1"), ni["W2"], ni.get("b2"), sample, rt["C"], w.act,
-                                  w.dtype)
+    _, _, ys = ffn(sample)
     t_sample = time.perf_counter() - t0
     t["ffn"] = t_sample / len(sample) * kept
     y = np.zeros((w.E * rt["C"], w.M), ys.dtype)  # decode's cost does not depend on the values
@@ -205,7 +222,11 @@ def main():
     inp = W.make_inputs(w, seed=0, device=dev)
     s = moe.Shape.of(w)
     gate = w.logits == "gate"
-    bufs = moe.alloc_forward(s, dev, training=w.backward, gate_projection=gate, residual=w.residual)
+    mxf = {"mxfp8": moe.MOE_MX_FP8, "mxfp4": moe.MOE_MX_FP4}.get(w.mx)
+    if mxf is not None:
+        bufs = moe.alloc_forward_mx(s, dev, gate_projection=gate)
+    else:
+        bufs = moe.alloc_forward(s, dev, training=w.backward, gate_projection=gate, residual=w.residual)
     res = {n: inp.get(n) for n in ("W1r", "b1r", "W2r", "b2r")} if w.residual else None
     grads = moe.alloc_backward(s, dev, gate=True, gate_projection=gate) if w.backward else None
     x, W1, W2, b1, b2 = inp["x"], inp["W1"], inp["W2"], inp.get("b1"), inp.get("b2")
@@ -217,7 +238,16 @@ def main():
     def backward():
         moe.layer_backward(s, bufs, inp["dout"], W1, W2, grads=grads, logits=logits_bwd, x=x, Wg=Wg)
 
+    if mxf is not None:
+        # MX experts: the weights are quantised once, outside the timed region (offline)
+        W1q = moe.mx_quantize_weights(W1, mxf)
+        W2q = moe.mx_quantize_weights(W2, mxf)
+        torch.cuda.synchronize()
+
     def step():
+        if mxf is not None:
+            moe.layer_forward_mx(s, mxf, x, W1q, b1, W2q, b2, logits=logits_in, Wg=Wg, bufs=bufs)
+            return
         moe.layer_forward(s, x, W1, b1, W2, b2, logits=logits_in, Wg=Wg, bufs=bufs, residual=res)
         if w.backward:
             backward()
@@ -280,13 +310,23 @@ def main():
     stage_fns = []
     if gate:
         stage_fns.append(("gate", lambda: moe.moe_gate_project(s, x, Wg, lg)))
-    stage_fns += [
-        ("route", lambda: moe.moe_route(s, lg, b["idx"], b["loc"], b["gates"], b["needed"], b["fill"],
-                                        b["capacity"], b["slot_route"], b["ws"])),
-        ("encode", lambda: moe.moe_encode(s, x, b["idx"], b["loc"], b["fill"], b["capacity"], b["buf"])),
-        ("fc1", lambda: moe.moe_expert_fc1(s, b["buf"], W1, b1, b["fill"], b["capacity"], b["pre"], b["h"])),
-        ("fc2", lambda: moe.moe_expert_fc2(s, b["h"], W2, b2, b["fill"], b["capacity"], b["y"])),
-    ]
+    stage_fns.append(("route", lambda: moe.moe_route(s, lg, b["idx"], b["loc"], b["gates"], b["needed"], b["fill"],
+                                                     b["capacity"], b["slot_route"], b["ws"])))
+    if mxf is not None:
+        stage_fns += [
+            ("encode", lambda: moe.moe_encode_mx(s, x, b["idx"], b["loc"], b["fill"], b["capacity"], b["buf_codes"],
+                                                 b["buf_scales"])),
+            ("fc1", lambda: moe.moe_expert_fc1_mx(s, mxf, b["buf_codes"], b["buf_scales"], W1q, b1, b["fill"],
+                                                  b["capacity"], b["h_codes"], b["h_scales"])),
+            ("fc2", lambda: moe.moe_expert_fc2_mx(s, mxf, b["h_codes"], b["h_scales"], W2q, b2, b["fill"],
+                                                  b["capacity"], b["y"])),
+        ]
+    else:
+        stage_fns += [
+            ("encode", lambda: moe.moe_encode(s, x, b["idx"], b["loc"], b["fill"], b["capacity"], b["buf"])),
+            ("fc1", lambda: moe.moe_expert_fc1(s, b["buf"], W1, b1, b["fill"], b["capacity"], b["pre"], b["h"])),
+            ("fc2", lambda: moe.moe_expert_fc2(s, b["h"], W2, b2, b["fill"], b["capacity"], b["y"])),
+        ]
     if w.residual:
         stage_fns.append(("res_ffn", lambda: moe.moe_residual_ffn(s, x, res["W1r"], res["b1r"], res["W2r"], res["b2r"],
                                                                   b["h_r"], b["y_r"], b["ws"])))
@@ -316,7 +356,7 @@ def main():
     for n in names:
         ms = sum(e0.elapsed_time(e1) for e0, e1, r in ev[n]) / sum(r for _, _, r in ev[n])
         kind, amount = alg[n]
-        r = roofline_of(kind, amount, ms, w.dtype == W.DT_BF16)
+        r = roofline_of(kind, amount, ms, w.dtype == W.DT_BF16, mx=bool(w.mx) and n in ("fc1", "fc2"))
         r["ms"] = round(ms, 5)
         r["algorithmic_" + kind] = amount
         stages[n] = r
@@ -336,11 +376,11 @@ def main():
     line = dict(
         metric=METRIC, value=round(value, 1), unit="tokens/s", n_gpus=1, steps=args.steps, warmup=args.warmup,
         ms_per_step=round(ms_per_step, 5), higher_is_better=True, scaling="weak", vs_baseline=None,
-        dtype="bf16" if w.dtype == W.DT_BF16 else "f32", data="synthetic",
+        dtype=(w.mx + "/bf16") if w.mx else ("bf16" if w.dtype == W.DT_BF16 else "f32"), data="synthetic",
         config=dict(workload=w.name, S=w.S, M=w.M, E=w.E, k=w.k, H=w.H, capacity_factor=w.capacity_factor,
                     act="gelu" if w.act == W.ACT_GELU else "relu", biases=[w.has_fc1_bias, w.has_fc2_bias],
                     logits=w.logits, backward=w.backward, C=C, kept_routes=kept, parallelism="single-gpu",
-                    aux_coef=moe.AUX_COEF if w.backward else None, residual=w.residual),
+                    aux_coef=moe.AUX_COEF if w.backward else None, residual=w.residual, mx=w.mx or None),
         roofline=roofline, stages=stages, cpu_baseline=cpu,
     )
     print(json.dumps(line), flush=True)

@@ -738,9 +738,9 @@ __global__ __launch_bounds__(NTH, 1) void rows_gemm_big(const bf16_t *__restrict
 // lane l holds row l % 32; with 8-bit elements lane half h = l / 32 holds the
 // slice's bytes [16h, 16h+16) and [32+16h, 32+16h+16) (two 16-byte LDS reads),
 // with 4-bit elements bytes [16h, 16h+16) (32 values); the scale of k-block h of
-// the slice comes from lane half h. Each lane loads, one stage ahead, the four
-// scale bytes of a stage for each of its rows (one dword) and picks byte
-// 2 * slice + h. The hardware's fp8 accumulation drops low-order bits of products
+// the slice comes from lane half h. Each lane loads, a stage ahead of use, the
+// scale bytes of four stages (one 16-byte load) for each of its rows and picks
+// byte 2 * slice + h of the stage's dword. The hardware's fp8 accumulation drops low-order bits of products
 // far below the largest one in a group of eight (about 1e-4 of the sum of
 // magnitudes), so results match an exact sum within that, not bit for bit.
 // Epilogues: fc1 adds the bias, applies the activation and quantises h to MXFP8
@@ -847,12 +847,33 @@ __global__ __launch_bounds__(NTH, 1) void rows_gemm_mx(const uint8_t *__restrict
             const int c = min(lane * 8, cols_valid - 8);
             __builtin_amdgcn_global_load_lds(bias + wrow0 + c, (lds_void_t *)sbias, 16, 0, 0);
         }
-        // stage 0's scales, then the ring's first two stages (loads complete in order)
-        uint32_t sa_cur[TM], sb_cur[TN], sa_nxt[TM], sb_nxt[TN];
+        // Scales: four stages' worth (16 bytes) per row and load when the rows are 16-byte
+        // aligned (K a multiple of 512), else one stage (a dword) per load. Each lane's
+        // rows are all different, so every load instruction touches 32 cache lines; the
+        // wide form makes four times fewer of them. Stage 0's group first, then the ring's
+        // first two stages (loads complete in order).
+        const bool wide = (K % 512) == 0;
+        uint4 sa_g[TM], sb_g[TN];
+        auto load_group = [&](int g0, uint4 (&ga)[TM], uint4 (&gb)[TN]) {
+            if (wide) {
 #pragma unroll
-        for (int i = 0; i < TM; ++i) sa_cur[i] = sa_row[i][0];
+                for (int i = 0; i < TM; ++i) ga[i] = reinterpret_cast<const uint4 *>(sa_row[i])[g0 / 4];
 #pragma unroll
-        for (int j = 0; j < TN; ++j) sb_cur[j] = sb_row[j][0];
+                for (int j = 0; j < TN; ++j) gb[j] = reinterpret_cast<const uint4 *>(sb_row[j])[g0 / 4];
+            } else {
+#pragma unroll
+                for (int i = 0; i < TM; ++i) ga[i].x = sa_row[i][g0];
+#pragma unroll
+                for (int j = 0; j < TN; ++j) gb[j].x = sb_row[j][g0];
+            }
+        };
+        auto pick = [&](const uint4 &v, int t) -> uint32_t {
+            if (!wide) return v.x;
+            const int q = t & 3;
+            return q == 0 ? v.x : (q == 1 ? v.y : (q == 2 ? v.z : v.w));
+        };
+        load_group(0, sa_g, sb_g);
+        uint32_t sa_cur[TM], sb_cur[TN];
         dma_tile<BM, KA, NW>(Ab, ldA, rows_valid, 0, lds, wave, lane);
         dma_tile<BN, KW, NW>(Bb, ldB, cols_valid, 0, lds + BM * KA, wave, lane);
         if (nk > 1) {
@@ -863,29 +884,39 @@ __global__ __launch_bounds__(NTH, 1) void rows_gemm_mx(const uint8_t *__restrict
             wait_vmcnt<0>();
         }
         barrier_keep_loads();
+        // Ping-pong over the two 64-wide slices of a stage: slice 1's fragments are read
+        // while slice 0 multiplies; the barrier sits before slice 1's MFMAs, after which
+        // stage t+2's loads refill the buffer just read and stage t+1's first fragments are
+        // read while slice 1 multiplies.
+        mx_v8i fa0[TM], fb0[TN], fa1[TM], fb1[TN];
+#pragma unroll
+        for (int i = 0; i < TM; ++i) fa0[i] = mx_frag<RA, false>(lds, wr0 + i * 32 + (lane & 31), 0, h);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) fb0[j] = mx_frag<RBW, FP4>(lds + BM * KA, wc0 + j * 32 + (lane & 31), 0, h);
         for (int t = 0; t < nk; ++t) {
             const bf16_t *scur = lds + (t & 1) * STAGE;
-            if (t + 1 < nk) {  // next stage's scales, one dword (four blocks) per row
+            // this stage's scale dwords (four blocks per row); the next group is requested one
+            // stage ahead of its first use
 #pragma unroll
-                for (int i = 0; i < TM; ++i) sa_nxt[i] = sa_row[i][t + 1];
+            for (int i = 0; i < TM; ++i) sa_cur[i] = pick(sa_g[i], t);
 #pragma unroll
-                for (int j = 0; j < TN; ++j) sb_nxt[j] = sb_row[j][t + 1];
-            }
+            for (int j = 0; j < TN; ++j) sb_cur[j] = pick(sb_g[j], t);
+            // the group's last stage has taken its dwords: the registers take the next group,
+            // which lands before the end-of-stage wait
+            const int step = wide ? 4 : 1;
+            if ((t + 1) % step == 0 && t + 1 < nk) load_group(t + 1, sa_g, sb_g);
 #pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                mx_v8i fa[TM], fb[TN];
+            for (int i = 0; i < TM; ++i) fa1[i] = mx_frag<RA, false>(scur, wr0 + i * 32 + (lane & 31), 1, h);
 #pragma unroll
-                for (int i = 0; i < TM; ++i) fa[i] = mx_frag<RA, false>(scur, wr0 + i * 32 + (lane & 31), s, h);
-#pragma unroll
-                for (int j = 0; j < TN; ++j)
-                    fb[j] = mx_frag<RBW, FP4>(scur + BM * KA, wc0 + j * 32 + (lane & 31), s, h);
-                const int sh = 8 * (2 * s + h);
+            for (int j = 0; j < TN; ++j) fb1[j] = mx_frag<RBW, FP4>(scur + BM * KA, wc0 + j * 32 + (lane & 31), 1, h);
+            {
+                const int sh = 8 * h;  // slice 0: k-blocks 0 (half 0) and 1 (half 1) of the stage
 #pragma unroll
                 for (int i = 0; i < TM; ++i)
 #pragma unroll
                     for (int j = 0; j < TN; ++j)
                         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                            fb[j], fa[i], acc[i][j], WCODE, 0, 0, static_cast<int>((sb_cur[j] >> sh) & 0xFFu), 0,
+                            fb0[j], fa0[i], acc[i][j], WCODE, 0, 0, static_cast<int>((sb_cur[j] >> sh) & 0xFFu), 0,
                             static_cast<int>((sa_cur[i] >> sh) & 0xFFu));
             }
             wait_vmcnt<0>();  // stage t+1's ring loads and scales have landed
@@ -895,10 +926,22 @@ __global__ __launch_bounds__(NTH, 1) void rows_gemm_mx(const uint8_t *__restrict
                 dma_tile<BM, KA, NW>(Ab, ldA, rows_valid, (t + 2) * KA, sn, wave, lane);
                 dma_tile<BN, KW, NW>(Bb, ldB, cols_valid, (t + 2) * KW, sn + BM * KA, wave, lane);
             }
+            // at the last stage these reads are from the other buffer and unused
+            const bf16_t *snext = lds + ((t + 1) & 1) * STAGE;
 #pragma unroll
-            for (int i = 0; i < TM; ++i) sa_cur[i] = sa_nxt[i];
+            for (int i = 0; i < TM; ++i) fa0[i] = mx_frag<RA, false>(snext, wr0 + i * 32 + (lane & 31), 0, h);
 #pragma unroll
-            for (int j = 0; j < TN; ++j) sb_cur[j] = sb_nxt[j];
+            for (int j = 0; j < TN; ++j) fb0[j] = mx_frag<RBW, FP4>(snext + BM * KA, wc0 + j * 32 + (lane & 31), 0, h);
+            {
+                const int sh = 8 * (2 + h);  // slice 1: k-blocks 2 and 3
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+#pragma unroll
+                    for (int j = 0; j < TN; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                            fb1[j], fa1[i], acc[i][j], WCODE, 0, 0, static_cast<int>((sb_cur[j] >> sh) & 0xFFu), 0,
+                            static_cast<int>((sa_cur[i] >> sh) & 0xFFu));
+            }
         }
         wait_vmcnt<0>();
         barrier_keep_loads_lds();  // every wavefront is done with the ring

@@ -57,6 +57,7 @@ class Workload:
     logits: str = "normal"  # "normal" | "gate" (x @ Wg) | "zipf" (normal + Zipf(1.1) bias x2)
     backward: bool = False
     residual: bool = False  # Residual-MoE: a dense MLP branch added to the MoE output
+    mx: str = ""  # "mxfp8" / "mxfp4": experts with MX-quantised weights (tokens and h in MXFP8)
 
     def replace(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
@@ -88,8 +89,16 @@ FINE_BF16 = Workload("fine_bf16_S16384_M2048_E64_k6_H1408", S=16384, M=2048, E=6
 LARGE_BF16 = Workload("large_bf16_S32768_M4096_E128_k8_H1536", S=32768, M=4096, E=128, k=8, H=1536,
                       capacity_factor=-2.0, logits="zipf", backward=True)
 
+# the gated layer with MX low-precision experts (the weights quantised from the same bf16 draws)
+GATED_MXFP8 = GATED_BF16.replace(name="gated_mxfp8_S4096_M1024_E8_k2_H4096", mx="mxfp8")
+GATED_MXFP4 = GATED_BF16.replace(name="gated_mxfp4_S4096_M1024_E8_k2_H4096", mx="mxfp4")
+DSPR_MXFP8 = Workload("dspr_mxfp8_S8192_M2048_E16_k3_H8192", S=8192, M=2048, E=16, k=3, H=8192,
+                      capacity_factor=0.0, mx="mxfp8")
+
 WORKLOADS = [TINY_F32, GATED_BF16, GATED_TRAIN_BF16, RESIDUAL_BF16, DSPR_BF16, FINE_BF16, LARGE_BF16]
-BY_NAME = {w.name: w for w in WORKLOADS}
+# MX workloads are measured by bench.py and checked by the MX parity tests
+MX_WORKLOADS = [GATED_MXFP8, GATED_MXFP4, DSPR_MXFP8]
+BY_NAME = {w.name: w for w in WORKLOADS + MX_WORKLOADS}
 
 
 def _gen(seed: int, tensor: str, device) -> torch.Generator:
