@@ -51,6 +51,10 @@ def parse():
                     help="workload name (see workloads.py); default: the S=4096 gate-projected bf16 layer")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle FFN sample")
+    ap.add_argument("--pipeline-chunks", type=int, default=0, metavar="D",
+                    help="run the expert FFN in D capacity chunks on --pipeline-streams streams "
+                         "(bf16 forward workloads; 0 = the fused forward)")
+    ap.add_argument("--pipeline-streams", type=int, default=2)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 3 plain device copies of MIB MiB each (the reference kernel that scales the "
                          "FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -244,9 +248,20 @@ def main():
         W2q = moe.mx_quantize_weights(W2, mxf)
         torch.cuda.synchronize()
 
+    pipe = args.pipeline_chunks > 0
+    if pipe:
+        assert mxf is None and not w.residual and not w.backward and w.dtype == W.DT_BF16, \
+            "--pipeline-chunks applies to the bf16 forward workloads"
+        pstreams = [torch.cuda.Stream() for _ in range(args.pipeline_streams)]
+        pevents = [torch.cuda.Event() for _ in range(args.pipeline_streams + 1)]
+
     def step():
         if mxf is not None:
             moe.layer_forward_mx(s, mxf, x, W1q, b1, W2q, b2, logits=logits_in, Wg=Wg, bufs=bufs)
+            return
+        if pipe:
+            moe.layer_forward_pipelined(s, x, W1, b1, W2, b2, args.pipeline_chunks, pstreams, pevents,
+                                        logits=logits_in, Wg=Wg, bufs=bufs)
             return
         moe.layer_forward(s, x, W1, b1, W2, b2, logits=logits_in, Wg=Wg, bufs=bufs, residual=res)
         if w.backward:
@@ -380,7 +395,8 @@ def main():
         config=dict(workload=w.name, S=w.S, M=w.M, E=w.E, k=w.k, H=w.H, capacity_factor=w.capacity_factor,
                     act="gelu" if w.act == W.ACT_GELU else "relu", biases=[w.has_fc1_bias, w.has_fc2_bias],
                     logits=w.logits, backward=w.backward, C=C, kept_routes=kept, parallelism="single-gpu",
-                    aux_coef=moe.AUX_COEF if w.backward else None, residual=w.residual, mx=w.mx or None),
+                    aux_coef=moe.AUX_COEF if w.backward else None, residual=w.residual, mx=w.mx or None,
+                    pipeline=dict(chunks=args.pipeline_chunks, streams=args.pipeline_streams) if pipe else None),
         roofline=roofline, stages=stages, cpu_baseline=cpu,
     )
     print(json.dumps(line), flush=True)

@@ -82,6 +82,8 @@ _SIGS = {
     "moe_expert_ffn": [_SP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
     "moe_expert_fc1": [_SP, _P, _P, _P, _P, _P, _P, _P, _P],
     "moe_expert_fc2": [_SP, _P, _P, _P, _P, _P, _P, _P],
+    "moe_expert_ffn_window": [_SP] + [_P] * 7 + [ctypes.c_int32, ctypes.c_int32] + [_P] * 4,
+    "moe_layer_forward_pipelined": [_SP] + [_P] * 21 + [ctypes.c_size_t, ctypes.c_int32, _P, ctypes.c_int32, _P, _P],
     "moe_decode": [_SP, _P, _P, _P, _P, _P, _P, _P],
     "moe_layer_forward": [_SP] + [_P] * 21 + [ctypes.c_size_t, _P],
     "moe_mx_quantize": [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _P, _P, _P, _P],
@@ -177,6 +179,41 @@ def moe_expert_fc1(shape: Shape, buf, W1, b1, fill, capacity, pre, h, stream=Non
 def moe_expert_fc2(shape: Shape, h, W2, b2, fill, capacity, y, stream=None) -> None:
     _check(_lib.moe_expert_fc2(ctypes.byref(shape.c()), _ptr(h), _ptr(W2), _ptr(b2), _ptr(fill), _ptr(capacity),
                                _ptr(y), _stream(stream)))
+
+
+def moe_expert_ffn_window(shape: Shape, buf, W1, b1, W2, b2, fill, capacity, slot_begin: int, slot_end: int, pre,
+                          h, y, stream=None) -> None:
+    _check(_lib.moe_expert_ffn_window(ctypes.byref(shape.c()), _ptr(buf), _ptr(W1), _ptr(b1), _ptr(W2), _ptr(b2),
+                                      _ptr(fill), _ptr(capacity), int(slot_begin), int(slot_end), _ptr(pre), _ptr(h),
+                                      _ptr(y), _stream(stream)))
+
+
+def pipeline_windows(shape: Shape, d: int):
+    """The d slot windows [begin, end) that cut the host capacity bound into near-equal chunks."""
+    cmax = moe_capacity_bound(shape)
+    w = -(-cmax // d)
+    return [(i * w, min(cmax, (i + 1) * w)) for i in range(d) if i * w < cmax]
+
+
+def layer_forward_pipelined(shape: Shape, x, W1, b1, W2, b2, chunks: int, streams, events, logits=None, Wg=None,
+                            bufs=None, stream=None):
+    """moe_layer_forward_pipelined: the expert FFN in ``chunks`` capacity windows on the given torch
+    streams (``events``: len(streams) + 1 torch events, created with default flags)."""
+    if bufs is None:
+        bufs = alloc_forward(shape, x.device, gate_projection=Wg is not None)
+    for e_ in events:  # a torch event is created lazily, on its first record
+        if e_.cuda_event == 0:
+            e_.record()
+    sp = (ctypes.c_void_p * len(streams))(*[st.cuda_stream for st in streams])
+    ep = (ctypes.c_void_p * len(events))(*[e_.cuda_event for e_ in events])
+    lo = bufs["logits"] if Wg is not None else None
+    _check(_lib.moe_layer_forward_pipelined(
+        ctypes.byref(shape.c()), _ptr(x), _ptr(logits), _ptr(Wg), _ptr(lo), _ptr(W1), _ptr(b1), _ptr(W2), _ptr(b2),
+        _ptr(bufs["idx"]), _ptr(bufs["loc"]), _ptr(bufs["gates"]), _ptr(bufs["needed"]), _ptr(bufs["fill"]),
+        _ptr(bufs["capacity"]), _ptr(bufs["slot_route"]), _ptr(bufs["buf"]), _ptr(bufs["pre"]), _ptr(bufs["h"]),
+        _ptr(bufs["y"]), _ptr(bufs["out"]), *_ws_args(bufs["ws"]), int(chunks), sp, len(streams), ep,
+        _stream(stream)))
+    return bufs
 
 
 def moe_decode(shape: Shape, y, gates, idx, loc, capacity, out, stream=None) -> None:

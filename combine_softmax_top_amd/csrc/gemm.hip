@@ -464,15 +464,22 @@ struct TileSched {
     int end;      // end of this XCD's range
 };
 
+// Rows of expert e inside the slot window [s0, s1) of its capacity.
+__device__ __forceinline__ int window_rows(const int32_t *fill, int e, int s0, int s1) {
+    return max(0, min(fill[e], s1) - s0);
+}
+
 // prefix[e] = sum over e' < e of row tiles (LDS, E + 1 entries); returns the schedule.
+// Only the slots [s0, s1) of every expert are walked (the whole capacity by default).
 template <int NTH>
-__device__ __forceinline__ TileSched make_sched(const int32_t *fill, int E, int BMv, int nx, int *prefix) {
+__device__ __forceinline__ TileSched make_sched(const int32_t *fill, int E, int BMv, int nx, int *prefix, int s0 = 0,
+                                                int s1 = 0x7FFFFFFF) {
     __shared__ int wsum[NTH / 64];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     int base = 0;
     for (int e0 = 0; e0 < E; e0 += NTH) {
         const int e = e0 + tid;
-        const int rt = e < E ? (fill[e] + BMv - 1) / BMv : 0;
+        const int rt = e < E ? (window_rows(fill, e, s0, s1) + BMv - 1) / BMv : 0;
         int inc = rt;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
@@ -542,7 +549,7 @@ __global__ __launch_bounds__(NTH, 1) void rows_gemm_big(const bf16_t *__restrict
                                                       const int32_t *__restrict__ fill,
                                                       const int32_t *__restrict__ cap,
                                                       const bf16_t *__restrict__ bias, bf16_t *__restrict__ pre_out,
-                                                      const bf16_t *__restrict__ aux) {
+                                                      const bf16_t *__restrict__ aux, int s0, int s1) {
     extern __shared__ __align__(16) bf16_t lds[];
     constexpr int KB = kBigKB, S = KB / 16;
     // NW wavefronts in 2 rows x NW/2 columns, each owning a (BM/2) x (BN/(NW/2)) block
@@ -556,7 +563,7 @@ __global__ __launch_bounds__(NTH, 1) void rows_gemm_big(const bf16_t *__restrict
     int *prefix = reinterpret_cast<int *>(lds + 2 * STAGE);
     bf16_t *sbias = lds + 2 * STAGE + kBigPrefixBytes / 2;
     const int nx = (N + BN - 1) / BN;
-    const TileSched sc = make_sched<NTH>(fill, E, BM, nx, prefix);
+    const TileSched sc = make_sched<NTH>(fill, E, BM, nx, prefix, s0, s1);
     const int C = *cap;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wr0 = (wave / WGC) * (BM / 2), wc0 = (wave % WGC) * (BN / WGC);
@@ -565,9 +572,9 @@ __global__ __launch_bounds__(NTH, 1) void rows_gemm_big(const bf16_t *__restrict
         int g, rtile, ctile;
         decode_tile(L, prefix, E, nx, g, rtile, ctile);
         const int row0 = rtile * BM, col0 = ctile * BN;
-        const int rows_valid = min(BM, fill[g] - row0);
+        const int rows_valid = min(BM, window_rows(fill, g, s0, s1) - row0);
         const int cols_valid = min(BN, N - col0);
-        const int64_t grow0 = static_cast<int64_t>(g) * C + row0;
+        const int64_t grow0 = static_cast<int64_t>(g) * C + s0 + row0;
         const bf16_t *Ab = A + grow0 * K;
         const bf16_t *Bb = BMN ? B + static_cast<int64_t>(g) * K * N + col0
                                : B + static_cast<int64_t>(g) * N * K + static_cast<int64_t>(col0) * K;
@@ -1417,7 +1424,7 @@ static int resident_blocks(int per_cu) {
 template <int BM, int BN, int NTH, int EPI, bool BMN = false>
 hipError_t big_launch(int act, const void *A, const void *B, void *D, int N, int K, int E, const int32_t *fill,
                       const int32_t *cap, const void *bias, void *pre_out, hipStream_t st,
-                      const void *aux = nullptr) {
+                      const void *aux = nullptr, int s0 = 0, int s1 = 0x7FFFFFFF) {
     constexpr int lds = big_lds_bytes<BM, BN>();
     constexpr int per_cu = (160 * 1024) / lds >= 2 ? 2 : 1;
     const dim3 grid(resident_blocks(per_cu));
@@ -1432,13 +1439,13 @@ hipError_t big_launch(int act, const void *A, const void *B, void *D, int N, int
         static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(k),
                                                            hipFuncAttributeMaxDynamicSharedMemorySize, lds);
         if (attr != hipSuccess) return attr;
-        hipLaunchKernelGGL(k, grid, dim3(NTH), lds, st, a, b, d, N, K, E, fill, cap, bi, po, ax);
+        hipLaunchKernelGGL(k, grid, dim3(NTH), lds, st, a, b, d, N, K, E, fill, cap, bi, po, ax, s0, s1);
     } else {
         auto k = rows_gemm_big<BM, BN, NTH, EPI, MOE_ACT_RELU, BMN>;
         static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(k),
                                                            hipFuncAttributeMaxDynamicSharedMemorySize, lds);
         if (attr != hipSuccess) return attr;
-        hipLaunchKernelGGL(k, grid, dim3(NTH), lds, st, a, b, d, N, K, E, fill, cap, bi, po, ax);
+        hipLaunchKernelGGL(k, grid, dim3(NTH), lds, st, a, b, d, N, K, E, fill, cap, bi, po, ax, s0, s1);
     }
     return hipGetLastError();
 }
@@ -1484,13 +1491,15 @@ hipError_t bwd_data_launch(int act, const void *A, const void *B, void *D, int N
 
 template <int EPI>
 hipError_t fwd_launch(int act, const void *A, const void *B, void *D, int N, int K, int64_t rows_hint, int E,
-                      const int32_t *fill, const int32_t *cap, const void *bias, void *pre_out, hipStream_t st) {
+                      const int32_t *fill, const int32_t *cap, const void *bias, void *pre_out, hipStream_t st,
+                      int s0 = 0, int s1 = 0x7FFFFFFF) {
     int cfg = gemm_cfg_override();
     if (cfg < 1 || cfg > 3) cfg = default_cfg(N, K, rows_hint);
     switch (cfg) {
-    case 1: return big_launch<256, 256, 512, EPI>(act, A, B, D, N, K, E, fill, cap, bias, pre_out, st);
-    case 2: return big_launch<256, 128, 256, EPI>(act, A, B, D, N, K, E, fill, cap, bias, pre_out, st);
-    default: return big_launch<128, 128, 256, EPI>(act, A, B, D, N, K, E, fill, cap, bias, pre_out, st);
+    case 1: return big_launch<256, 256, 512, EPI>(act, A, B, D, N, K, E, fill, cap, bias, pre_out, st, nullptr, s0, s1);
+    case 2: return big_launch<256, 128, 256, EPI>(act, A, B, D, N, K, E, fill, cap, bias, pre_out, st, nullptr, s0, s1);
+    default:
+        return big_launch<128, 128, 256, EPI>(act, A, B, D, N, K, E, fill, cap, bias, pre_out, st, nullptr, s0, s1);
     }
 }
 
@@ -1535,6 +1544,18 @@ hipError_t launch_fc1(const moe_shape &s, const void *buf, const void *W1, const
     a.N = H; a.K = M; a.kgrouped = 0; a.fill = fill; a.cap = cap;
     a.bias = static_cast<const float *>(b1); a.pre_out = static_cast<float *>(pre);
     return simt_launch<EPI_FC1>(a, s.act, cmax, E, st);
+}
+
+// The expert FFN on the capacity slots [s0, s1) of every expert (bf16 data).
+hipError_t launch_ffn_window(const moe_shape &s, const void *buf, const void *W1, const void *b1, const void *W2,
+                             const void *b2, const int32_t *fill, const int32_t *cap, void *pre, void *h, void *y,
+                             int32_t cmax, int32_t s0, int32_t s1, hipStream_t st) {
+    const int M = s.M, H = s.H, E = s.E;
+    const int64_t win = std::max<int64_t>(0, std::min<int64_t>(s1, cmax) - s0);
+    const int64_t rh = std::min<int64_t>(static_cast<int64_t>(s.k) * s.S, static_cast<int64_t>(E) * win);
+    hipError_t err = fwd_launch<EPI_FC1>(s.act, buf, W1, h, H, M, rh, E, fill, cap, b1, pre, st, s0, s1);
+    if (err != hipSuccess) return err;
+    return fwd_launch<EPI_FC2>(s.act, h, W2, y, M, H, rh, E, fill, cap, b2, nullptr, st, s0, s1);
 }
 
 hipError_t launch_fc2(const moe_shape &s, const void *h, const void *W2, const void *b2, const int32_t *fill,

@@ -175,6 +175,24 @@ moe_status moe_expert_ffn(const moe_shape *shape, const void *buf, const void *W
     return e == hipSuccess ? MOE_OK : hip_fail(e, "expert fc2");
 }
 
+moe_status moe_expert_ffn_window(const moe_shape *shape, const void *buf, const void *W1, const void *b1,
+                                 const void *W2, const void *b2, const int32_t *fill, const int32_t *capacity,
+                                 int32_t slot_begin, int32_t slot_end, void *pre, void *h, void *y, void *stream) {
+    moe_status st = check_shape(shape);
+    if (st != MOE_OK) return st;
+    const moe_shape &s = *shape;
+    if (s.dtype != MOE_DT_BF16) return fail(MOE_EUNSUPPORTED, "the slot-window FFN takes bf16 data");
+    MOE_REQUIRE(slot_begin >= 0 && slot_end >= slot_begin, "bad slot window [%d, %d)", slot_begin, slot_end);
+    MOE_REQUIRE(buf && W1 && W2 && fill && capacity && h && y, "buf, W1, W2, fill, capacity, h and y must be non-NULL");
+    MOE_REQUIRE((b1 != nullptr) == (s.has_fc1_bias != 0), "b1 must be given iff has_fc1_bias");
+    MOE_REQUIRE((b2 != nullptr) == (s.has_fc2_bias != 0), "b2 must be given iff has_fc2_bias");
+    MOE_REQUIRE_ALIGNED(buf, W1, b1, W2, b2, fill, capacity, pre, h, y);
+    if (slot_end == slot_begin) return MOE_OK;
+    hipError_t e = moe::launch_ffn_window(s, buf, W1, b1, W2, b2, fill, capacity, pre, h, y,
+                                          static_cast<int32_t>(cap_bound(s)), slot_begin, slot_end, as_stream(stream));
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "expert ffn window");
+}
+
 moe_status moe_expert_fc1(const moe_shape *shape, const void *buf, const void *W1, const void *b1,
                           const int32_t *fill, const int32_t *capacity, void *pre, void *h, void *stream) {
     moe_status st = check_shape(shape);
@@ -512,6 +530,70 @@ moe_status moe_layer_forward(const moe_shape *shape, const void *x, const float 
                              void *out, void *ws, size_t ws_bytes, void *stream) {
     return layer_forward_impl(shape, x, logits_in, Wg, logits_out, W1, b1, W2, b2, idx, loc, gates, needed, fill,
                               capacity, slot_route, buf, pre, h, y, out, ws, ws_bytes, nullptr, stream);
+}
+
+moe_status moe_layer_forward_pipelined(const moe_shape *shape, const void *x, const float *logits_in,
+                                       const float *Wg, float *logits_out, const void *W1, const void *b1,
+                                       const void *W2, const void *b2, int32_t *idx, int32_t *loc, float *gates,
+                                       int32_t *needed, int32_t *fill, int32_t *capacity, int32_t *slot_route,
+                                       void *buf, void *pre, void *h, void *y, void *out, void *ws, size_t ws_bytes,
+                                       int32_t chunks, void *const *streams, int32_t nstreams, void *const *events,
+                                       void *stream) {
+    moe_status st = check_shape(shape);
+    if (st != MOE_OK) return st;
+    const moe_shape &s = *shape;
+    if (s.dtype != MOE_DT_BF16) return fail(MOE_EUNSUPPORTED, "the pipelined forward takes bf16 data");
+    MOE_REQUIRE(chunks >= 1 && chunks <= 64, "chunks must be in [1, 64]");
+    MOE_REQUIRE(nstreams >= 1 && nstreams <= 64 && streams != nullptr && events != nullptr,
+                "1..64 streams and nstreams + 1 events are required");
+    for (int i = 0; i < nstreams; ++i) MOE_REQUIRE(events[i] != nullptr, "events must be non-NULL");
+    MOE_REQUIRE(events[nstreams] != nullptr, "events must be non-NULL");
+    // everything before and after the expert FFN, checked and run by the fused forward's steps
+    MOE_REQUIRE(!(logits_in != nullptr && Wg != nullptr), "exactly one of logits_in and Wg must be given");
+    MOE_REQUIRE(s.S == 0 || logits_in != nullptr || Wg != nullptr, "exactly one of logits_in and Wg must be given");
+    MOE_REQUIRE(Wg == nullptr || logits_out != nullptr || s.S == 0, "logits_out is required with Wg");
+    MOE_REQUIRE(needed && fill && capacity && buf && W1 && W2 && h && y,
+                "needed, fill, capacity, buf, W1, W2, h and y must be non-NULL");
+    if (s.S > 0) MOE_REQUIRE(x && idx && loc && gates && out, "x, idx, loc, gates and out must be non-NULL");
+    MOE_REQUIRE((b1 != nullptr) == (s.has_fc1_bias != 0), "b1 must be given iff has_fc1_bias");
+    MOE_REQUIRE((b2 != nullptr) == (s.has_fc2_bias != 0), "b2 must be given iff has_fc2_bias");
+    if ((st = check_ws(s, ws, ws_bytes)) != MOE_OK) return st;
+    MOE_REQUIRE_ALIGNED(x, logits_in, Wg, logits_out, W1, b1, W2, b2, idx, loc, gates, needed, fill, capacity,
+                        slot_route, buf, pre, h, y, out, ws);
+    if (Wg != nullptr && !moe::gate_supported(s.M, s.E, s.dtype))
+        return fail(MOE_EUNSUPPORTED, "gate projection tiles for M=%d, E=%d do not fit in LDS", s.M, s.E);
+    hipStream_t strm = as_stream(stream);
+    const int32_t cmax = static_cast<int32_t>(cap_bound(s));
+    const float *logits = logits_in;
+    hipError_t e;
+    if (Wg != nullptr && s.S > 0) {
+        if ((e = moe::launch_gate_project(s, x, Wg, logits_out, strm)) != hipSuccess) return hip_fail(e, "gate projection");
+        logits = logits_out;
+    }
+    moe::RouteWs w{static_cast<int32_t *>(ws), num_tiles(s)};
+    if ((e = moe::launch_route(s, logits, idx, loc, gates, needed, fill, capacity, slot_route, w, by_factor(s), strm)) !=
+        hipSuccess)
+        return hip_fail(e, "route");
+    if ((e = moe::launch_encode(s, x, idx, loc, fill, capacity, buf, cmax, strm)) != hipSuccess)
+        return hip_fail(e, "encode");
+    auto ev = [&](int i) { return reinterpret_cast<hipEvent_t>(events[i]); };
+    if ((e = hipEventRecord(ev(0), strm)) != hipSuccess) return hip_fail(e, "event record");
+    for (int i = 0; i < nstreams; ++i)
+        if ((e = hipStreamWaitEvent(as_stream(streams[i]), ev(0), 0)) != hipSuccess) return hip_fail(e, "stream wait");
+    const int32_t width = (cmax + chunks - 1) / chunks;
+    for (int c = 0; c < chunks && c * width < cmax; ++c) {
+        const int32_t a = c * width, b = std::min(cmax, a + width);
+        if ((e = moe::launch_ffn_window(s, buf, W1, b1, W2, b2, fill, capacity, pre, h, y, cmax, a, b,
+                                        as_stream(streams[c % nstreams]))) != hipSuccess)
+            return hip_fail(e, "expert ffn window");
+    }
+    for (int i = 0; i < nstreams; ++i) {
+        if ((e = hipEventRecord(ev(i + 1), as_stream(streams[i]))) != hipSuccess) return hip_fail(e, "event record");
+        if ((e = hipStreamWaitEvent(strm, ev(i + 1), 0)) != hipSuccess) return hip_fail(e, "stream wait");
+    }
+    if ((e = moe::launch_decode(s, y, gates, idx, loc, capacity, out, false, strm)) != hipSuccess)
+        return hip_fail(e, "decode");
+    return MOE_OK;
 }
 
 moe_status moe_residual_layer_forward(const moe_shape *shape, const void *x, const float *logits_in,

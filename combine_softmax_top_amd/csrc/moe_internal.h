@@ -161,6 +161,10 @@ hipError_t launch_fc1(const moe_shape &s, const void *buf, const void *W1, const
                       const int32_t *cap, void *pre, void *h, int32_t cmax, hipStream_t st);
 hipError_t launch_fc2(const moe_shape &s, const void *h, const void *W2, const void *b2, const int32_t *fill,
                       const int32_t *cap, void *y, int32_t cmax, hipStream_t st);
+// fc1 and fc2 on the capacity slots [s0, s1) of every expert only (bf16 data).
+hipError_t launch_ffn_window(const moe_shape &s, const void *buf, const void *W1, const void *b1, const void *W2,
+                             const void *b2, const int32_t *fill, const int32_t *cap, void *pre, void *h, void *y,
+                             int32_t cmax, int32_t s0, int32_t s1, hipStream_t st);
 // Gate backward: dlogits (and, with needed, the auxiliary-loss partials in ws
 // and aux_loss if non-NULL); dWg = x^T dlogits; dx = kept dbuf rows + dlogits Wg^T.
 size_t gate_grad_ws_bytes(int S, int M, int E);

@@ -167,6 +167,18 @@ moe_status moe_expert_fc1(const moe_shape *shape, const void *buf, const void *W
 moe_status moe_expert_fc2(const moe_shape *shape, const void *h, const void *W2, const void *b2,
                           const int32_t *fill, const int32_t *capacity, void *y, void *stream);
 
+/* moe_expert_ffn restricted to the capacity slots [slot_begin, slot_end) of
+ * every expert: rows e*C + j with slot_begin <= j < min(fill[e], slot_end).
+ * The rows of pre, h and y outside the window are left as they are. For
+ * pipelining over the capacity dimension (MoE training blog, part 3 section
+ * 3.4, adaptive pipelining: the capacity is cut into d chunks whose expert
+ * computation runs as separate launches, here on caller streams; windows that
+ * partition [0, cmax) compute exactly moe_expert_ffn). bf16 data only. */
+moe_status moe_expert_ffn_window(const moe_shape *shape, const void *buf, const void *W1, const void *b1,
+                                 const void *W2, const void *b2, const int32_t *fill,
+                                 const int32_t *capacity, int32_t slot_begin, int32_t slot_end, void *pre,
+                                 void *h, void *y, void *stream);
+
 /* Fast decode (blog part 3 section 3.5, "Decode"; DeepSpeed PR #8195 section 3,
  * combine accumulated in fp32): out[s] = sum over kept routes r = 0..k-1, in
  * order, of gates[r][s] * y[idx*C + loc], accumulated in fp32 from +0 with
@@ -312,6 +324,23 @@ moe_status moe_residual_layer_forward(const moe_shape *shape, const void *x, con
                                       int32_t *slot_route, void *buf, void *pre, void *h, void *y,
                                       void *h_r, void *y_r, void *out, void *ws, size_t ws_bytes,
                                       void *stream);
+
+/* moe_layer_forward with the expert FFN pipelined over the capacity dimension
+ * (MoE training blog, part 3 section 3.4, adaptive pipelining, its single-GPU
+ * half): [gate projection], route and encode on `stream`; then the capacity
+ * bound cmax is cut into `chunks` windows of ceil(cmax / chunks) slots, window
+ * c computed by moe_expert_ffn_window on streams[c % nstreams]; decode on
+ * `stream` after every chunk. events: nstreams + 1 caller-created hipEvent_t
+ * (recorded and waited on, never destroyed). Same results as
+ * moe_layer_forward. bf16 data only; 1 <= chunks, nstreams <= 64. */
+moe_status moe_layer_forward_pipelined(const moe_shape *shape, const void *x, const float *logits_in,
+                                       const float *Wg, float *logits_out, const void *W1, const void *b1,
+                                       const void *W2, const void *b2, int32_t *idx, int32_t *loc,
+                                       float *gates, int32_t *needed, int32_t *fill, int32_t *capacity,
+                                       int32_t *slot_route, void *buf, void *pre, void *h, void *y,
+                                       void *out, void *ws, size_t ws_bytes, int32_t chunks,
+                                       void *const *streams, int32_t nstreams, void *const *events,
+                                       void *stream);
 
 /* The backward of decode, expert FFN and encode for upstream gradient dout
  * [S, M] (blog part 3 section 3.5: K1 is combine-backward, K2 the cross term,
