@@ -543,7 +543,7 @@ __device__ __forceinline__ void decode_tile(int L, const int *prefix, int E, int
 // them). Epilogues: fc1 (bias, optional pre-activation output, activation),
 // fc2 (bias), plain, and the activation gradient (D = acc * act'(aux), aux the
 // saved pre-activation, staged through LDS so that the product is rounded once).
-template <int BM, int BN, int NTH, int EPI, int ACT, bool BMN>
+template <int BM, int BN, int NTH, int EPI, int ACT, bool BMN, int WR = 2>
 __global__ __launch_bounds__(NTH, 1) void rows_gemm_big(const bf16_t *__restrict__ A, const bf16_t *__restrict__ B,
                                                       bf16_t *__restrict__ D, int N, int K, int E,
                                                       const int32_t *__restrict__ fill,
@@ -553,8 +553,8 @@ __global__ __launch_bounds__(NTH, 1) void rows_gemm_big(const bf16_t *__restrict
     extern __shared__ __align__(16) bf16_t lds[];
     constexpr int KB = kBigKB, S = KB / 16;
     // NW wavefronts in 2 rows x NW/2 columns, each owning a (BM/2) x (BN/(NW/2)) block
-    constexpr int NW = NTH / 64, WGC = NW / 2;
-    constexpr int TM = BM / 64, TN = BN / (32 * WGC);
+    constexpr int NW = NTH / 64, WGC = NW / WR;  // WR rows x WGC columns of wavefronts
+    constexpr int TM = BM / (32 * WR), TN = BN / (32 * WGC);
     static_assert(TN >= 1 && BN % (32 * WGC) == 0, "wavefront columns must be whole 32-wide blocks");
     constexpr int STAGE = (BM + BN) * KB;
     constexpr int LPS = (BM + BN) * KB / 8 / NTH;  // direct-load instructions per stage per thread
@@ -566,7 +566,7 @@ __global__ __launch_bounds__(NTH, 1) void rows_gemm_big(const bf16_t *__restrict
     const TileSched sc = make_sched<NTH>(fill, E, BM, nx, prefix, s0, s1);
     const int C = *cap;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wr0 = (wave / WGC) * (BM / 2), wc0 = (wave % WGC) * (BN / WGC);
+    const int wr0 = (wave / WGC) * (BM / WR), wc0 = (wave % WGC) * (BN / WGC);
     const int nk = K / KB;
     for (int L = sc.first; L < sc.end; L += sc.stride) {
         int g, rtile, ctile;
@@ -1421,7 +1421,7 @@ static int resident_blocks(int per_cu) {
     return ((cus[dev] * per_cu + kXcds - 1) / kXcds) * kXcds;
 }
 
-template <int BM, int BN, int NTH, int EPI, bool BMN = false>
+template <int BM, int BN, int NTH, int EPI, bool BMN = false, int WR = 2>
 hipError_t big_launch(int act, const void *A, const void *B, void *D, int N, int K, int E, const int32_t *fill,
                       const int32_t *cap, const void *bias, void *pre_out, hipStream_t st,
                       const void *aux = nullptr, int s0 = 0, int s1 = 0x7FFFFFFF) {
@@ -1435,13 +1435,13 @@ hipError_t big_launch(int act, const void *A, const void *B, void *D, int N, int
     auto po = static_cast<bf16_t *>(pre_out);
     auto ax = static_cast<const bf16_t *>(aux);
     if (act == MOE_ACT_GELU) {
-        auto k = rows_gemm_big<BM, BN, NTH, EPI, MOE_ACT_GELU, BMN>;
+        auto k = rows_gemm_big<BM, BN, NTH, EPI, MOE_ACT_GELU, BMN, WR>;
         static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(k),
                                                            hipFuncAttributeMaxDynamicSharedMemorySize, lds);
         if (attr != hipSuccess) return attr;
         hipLaunchKernelGGL(k, grid, dim3(NTH), lds, st, a, b, d, N, K, E, fill, cap, bi, po, ax, s0, s1);
     } else {
-        auto k = rows_gemm_big<BM, BN, NTH, EPI, MOE_ACT_RELU, BMN>;
+        auto k = rows_gemm_big<BM, BN, NTH, EPI, MOE_ACT_RELU, BMN, WR>;
         static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(k),
                                                            hipFuncAttributeMaxDynamicSharedMemorySize, lds);
         if (attr != hipSuccess) return attr;
@@ -1485,6 +1485,7 @@ hipError_t bwd_data_launch(int act, const void *A, const void *B, void *D, int N
     switch (cfg) {
     case 1: return big_launch<256, 256, 512, EPI, true>(act, A, B, D, N, K, E, fill, cap, nullptr, nullptr, st, aux);
     case 2: return big_launch<256, 128, 256, EPI, true>(act, A, B, D, N, K, E, fill, cap, nullptr, nullptr, st, aux);
+
     default: return big_launch<128, 128, 256, EPI, true>(act, A, B, D, N, K, E, fill, cap, nullptr, nullptr, st, aux);
     }
 }
@@ -1498,6 +1499,7 @@ hipError_t fwd_launch(int act, const void *A, const void *B, void *D, int N, int
     switch (cfg) {
     case 1: return big_launch<256, 256, 512, EPI>(act, A, B, D, N, K, E, fill, cap, bias, pre_out, st, nullptr, s0, s1);
     case 2: return big_launch<256, 128, 256, EPI>(act, A, B, D, N, K, E, fill, cap, bias, pre_out, st, nullptr, s0, s1);
+
     default:
         return big_launch<128, 128, 256, EPI>(act, A, B, D, N, K, E, fill, cap, bias, pre_out, st, nullptr, s0, s1);
     }
