@@ -1459,9 +1459,16 @@ hipError_t big_launch(int act, const void *A, const void *B, void *D, int N, int
 // products with fewer than 128 large tiles (half the CUs), where 128 x 128
 // tiles keep four times as many workgroups busy (measured: top-1 fc2 at S=4096,
 // M=1024, E=8, H=4096, 64 large tiles, 86 -> 55 us; the top-2 layer's 128 large
-// tiles still favour 256 x 256, 96 vs 105 us). rows_hint bounds the filled rows
-// over all experts (k*S, or S for a dense product). MOE_GEMM_CFG overrides the
-// choice for tuning (1 = 256 x 256, 2 = 256 x 128, 3 = 128 x 128).
+// tiles still favour 256 x 256, 96 vs 105 us). Between 256 x 256 and 192 x 256
+// tiles (eight wavefronts of 96 x 64) the choice counts the rounds of the
+// persistent grid each needs at an even fill per expert: a tile is computed for
+// all its rows, filled or not, and the last round runs on part of the CUs, so
+// where 192-row tiles take as many rounds they finish sooner (a round costs
+// about 192/256 of the time at ~8% lower throughput per flop; measured: fc2 of
+// the top-2 layer above, 144 large tiles or 192 of 192 rows, 95 -> 82 us).
+// rows_hint bounds the filled rows over all experts (k*S, or S for a dense
+// product). MOE_GEMM_CFG overrides the choice for tuning (1 = 256 x 256,
+// 2 = 256 x 128, 3 = 128 x 128, 4 = 192 x 256).
 static int gemm_cfg_override() {
     static const int v = [] {
         const char *e = getenv("MOE_GEMM_CFG");
@@ -1470,9 +1477,13 @@ static int gemm_cfg_override() {
     return v;
 }
 
-static int default_cfg(int N, int K, int64_t rows_hint) {
+static int default_cfg(int N, int K, int64_t rows_hint, int E) {
     const int64_t big_tiles = ((rows_hint + 255) / 256) * ((N + 255) / 256);
-    return (K <= 1024 || big_tiles < 128) ? 3 : 1;
+    if (K <= 1024 || big_tiles < 128) return 3;
+    const int64_t f = (rows_hint + E - 1) / E, nx = (N + 255) / 256, cus = resident_blocks(1);
+    const int64_t r256 = (E * ((f + 255) / 256) * nx + cus - 1) / cus;
+    const int64_t r192 = (E * ((f + 191) / 192) * nx + cus - 1) / cus;
+    return r192 * 192 * 100 < r256 * 256 * 92 ? 4 : 1;
 }
 
 // Backward data products, weights read n-contiguous: same tile choice as the
@@ -1481,10 +1492,11 @@ template <int EPI>
 hipError_t bwd_data_launch(int act, const void *A, const void *B, void *D, int N, int K, int E, const int32_t *fill,
                            const int32_t *cap, const void *aux, int64_t rows_hint, hipStream_t st) {
     int cfg = gemm_cfg_override();
-    if (cfg < 1 || cfg > 3) cfg = default_cfg(N, K, rows_hint);
+    if (cfg < 1 || cfg > 4) cfg = default_cfg(N, K, rows_hint, E);
     switch (cfg) {
     case 1: return big_launch<256, 256, 512, EPI, true>(act, A, B, D, N, K, E, fill, cap, nullptr, nullptr, st, aux);
     case 2: return big_launch<256, 128, 256, EPI, true>(act, A, B, D, N, K, E, fill, cap, nullptr, nullptr, st, aux);
+    case 4: return big_launch<192, 256, 512, EPI, true>(act, A, B, D, N, K, E, fill, cap, nullptr, nullptr, st, aux);
 
     default: return big_launch<128, 128, 256, EPI, true>(act, A, B, D, N, K, E, fill, cap, nullptr, nullptr, st, aux);
     }
@@ -1495,10 +1507,11 @@ hipError_t fwd_launch(int act, const void *A, const void *B, void *D, int N, int
                       const int32_t *fill, const int32_t *cap, const void *bias, void *pre_out, hipStream_t st,
                       int s0 = 0, int s1 = 0x7FFFFFFF) {
     int cfg = gemm_cfg_override();
-    if (cfg < 1 || cfg > 3) cfg = default_cfg(N, K, rows_hint);
+    if (cfg < 1 || cfg > 4) cfg = default_cfg(N, K, rows_hint, E);
     switch (cfg) {
     case 1: return big_launch<256, 256, 512, EPI>(act, A, B, D, N, K, E, fill, cap, bias, pre_out, st, nullptr, s0, s1);
     case 2: return big_launch<256, 128, 256, EPI>(act, A, B, D, N, K, E, fill, cap, bias, pre_out, st, nullptr, s0, s1);
+    case 4: return big_launch<192, 256, 512, EPI>(act, A, B, D, N, K, E, fill, cap, bias, pre_out, st, nullptr, s0, s1);
 
     default:
         return big_launch<128, 128, 256, EPI>(act, A, B, D, N, K, E, fill, cap, bias, pre_out, st, nullptr, s0, s1);
