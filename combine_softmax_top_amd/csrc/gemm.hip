@@ -613,6 +613,20 @@ __global__ __launch_bounds__(NTH, 1) void rows_gemm_big(const bf16_t *__restrict
             wait_vmcnt<0>();
         }
         barrier_keep_loads();
+        if (bias != nullptr) {
+            // the accumulators start at the bias: the epilogue then only applies the activation
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    float b4[4];
+                    load4_bf16(sbias + wc0 + j * 32 + 8 * q + 4 * (lane >> 5), b4);
+#pragma unroll
+                    for (int i = 0; i < TM; ++i)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) acc[i][j][4 * q + r] = b4[r];
+                }
+        }
         bf16x8 fa[2][TM], fb[2][TN];
         frag_load<TM, TN, KB, BMN, BN>(lds, lds + BM * KB, 0, fa[0], fb[0], wr0, wc0, lane);
         for (int t = 0; t < nk; ++t) {
@@ -640,8 +654,9 @@ __global__ __launch_bounds__(NTH, 1) void rows_gemm_big(const bf16_t *__restrict
         }
 
         // Epilogue through LDS. Per 32x32 block, lane l owns token row (l % 32)
-        // and, for q = 0..3, features 8q + 4(l / 32) .. +3: written (bias added,
-        // activation applied, rounded to bf16) into the free ring as a row-major
+        // and, for q = 0..3, features 8q + 4(l / 32) .. +3 (the bias is already in
+        // the accumulators): written (activation applied, rounded to bf16) into
+        // the free ring as a row-major
         // BM x BN tile whose 16-byte chunks are XOR-swizzled by row, then read
         // back a row at a time so that every global store is whole 16-byte
         // chunks of contiguous rows (full cache lines), not 32 rows x 16 bytes.
@@ -681,13 +696,6 @@ __global__ __launch_bounds__(NTH, 1) void rows_gemm_big(const bf16_t *__restrict
                         const int tcol = wc0 + j * 32 + 8 * q + 4 * (lane >> 5);
                         f32x2 lo = {acc[i][j][4 * q], acc[i][j][4 * q + 1]};
                         f32x2 hi = {acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-                        if (bias != nullptr) {
-                            const uint2 u2 = *reinterpret_cast<const uint2 *>(sbias + tcol);
-                            lo[0] += __uint_as_float(u2.x << 16);
-                            lo[1] += __uint_as_float(u2.x & 0xFFFF0000u);
-                            hi[0] += __uint_as_float(u2.y << 16);
-                            hi[1] += __uint_as_float(u2.y & 0xFFFF0000u);
-                        }
                         if (act) {
                             lo[0] = act_fast<ACT>(lo[0]);
                             lo[1] = act_fast<ACT>(lo[1]);

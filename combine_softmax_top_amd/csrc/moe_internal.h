@@ -46,8 +46,8 @@ __device__ __forceinline__ float gelu_grad_f(float v) {
 // erf by Abramowitz & Stegun, Handbook of Mathematical Functions, formula
 // 7.1.26: erf(x) = 1 - t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) exp(-x^2),
 // t = 1 / (1 + p x) for x >= 0, odd extension; absolute error <= 1.5e-7.
-// Used by the GEMM epilogue, where it costs about half the instructions of erff.
-// *ex receives exp(-x^2), which the formula computes anyway.
+// Used by the activation-gradient epilogue, where it costs about half the
+// instructions of erff. *ex receives exp(-x^2), which the formula computes anyway.
 __device__ __forceinline__ float erf_as(float x, float *ex = nullptr) {
     const float ax = fabsf(x);
     const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, ax, 1.0f));
@@ -61,8 +61,28 @@ __device__ __forceinline__ float erf_as(float x, float *ex = nullptr) {
     const float r = 1.0f - y * e;
     return copysignf(r, x);
 }
+// GELU for the GEMM epilogues, where it is VALU-bound (one evaluation per output):
+// gelu(v) = v Phi(v), and with a = min(|v|, 6) and q = Phi(-a) = 2^P(a), where P is
+// the degree-7 least-squares fit (Chebyshev basis on [0, 6], then expanded in a) of
+// log2 Phi(-a), gelu = v q for v < 0 and v - v q for v >= 0, i.e. max(v, 0) - |v| q.
+// One exp2, no reciprocal, and no cancellation on the negative side (1 + erf there
+// loses the small values):
+// |error| <= 5e-7, relative error <= 9e-6 where |gelu| > 1e-3; past |v| = 6 the
+// error is below 2e-8. combine_softmax_top_amd/gelu_fit.py recomputes the coefficients.
 __device__ __forceinline__ float gelu_fast(float v) {
-    return 0.5f * v * (1.0f + erf_as(v * 0.70710678118654752f));
+    const float a = fabsf(__builtin_amdgcn_fmed3f(v, -6.0f, 6.0f));
+    float p = -1.9449178e-06f;
+    p = fmaf(p, a, 6.3860469e-05f);
+    p = fmaf(p, a, -9.4887050e-04f);
+    p = fmaf(p, a, 8.5823713e-03f);
+    p = fmaf(p, a, -5.4118313e-02f);
+    p = fmaf(p, a, -4.5829743e-01f);
+    p = fmaf(p, a, -1.1513246e+00f);
+    p = fmaf(p, a, -9.9998695e-01f);
+    // max(v, 0) in one instruction: fmaxf would first canonicalize v (NaN quieting)
+    float m;
+    asm("v_max_f32 %0, 0, %1" : "=v"(m) : "v"(v));
+    return fmaf(-fabsf(v), __builtin_amdgcn_exp2f(p), m);
 }
 // d/dv of 0.5 v (1 + erf(v / sqrt 2)) = Phi(v) + v phi(v), phi(v) = exp(-v^2/2) / sqrt(2 pi);
 // exp(-v^2/2) is the exp(-x^2) of erf_as at x = v / sqrt 2.
