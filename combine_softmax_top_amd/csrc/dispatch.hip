@@ -85,6 +85,78 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const uint4 *__restric
     }
 }
 
+// Routing's phase 3 fused with encode. The wavefront of token s places each of
+// its routes r as the route assignment does: rank = the number of lower tokens
+// of its 64-token tile whose route r goes to the same expert (one ballot over
+// the tile), loc = the tile's scanned offset for (expert, r) + rank; then the
+// row is copied to the kept slots. Every block derives C from needed[]; fill is
+// min(needed, C), computed where the padding rows are cleared.
+__global__ __launch_bounds__(kThreads) void assign_encode_kernel(
+    const uint4 *__restrict__ x, const int32_t *__restrict__ idx, const int32_t *__restrict__ offsets,
+    const int32_t *__restrict__ needed, int S, int E, int k, int nblk, int mode, int64_t cap_by_factor,
+    int32_t *__restrict__ loc, int32_t *__restrict__ fill, int32_t *__restrict__ cap_out,
+    int32_t *__restrict__ slot_route, uint4 *__restrict__ buf, int V) {
+    __shared__ int sh[4];
+    const int C = block_capacity(needed, E, mode, cap_by_factor, sh);
+    const int lane = threadIdx.x & (kWave - 1);
+    if (blockIdx.x == 0) {
+        if (threadIdx.x == 0) cap_out[0] = C;
+        for (int e = threadIdx.x; e < E; e += kThreads) fill[e] = min(needed[e], C);
+    }
+    const int64_t nw = num_waves();
+    for (int64_t s = global_wave(); s < S; s += nw) {
+        const int tile = static_cast<int>(s / kRouteTile);
+        const int64_t t0 = static_cast<int64_t>(tile) * kRouteTile;
+        const int j = static_cast<int>(s - t0);
+        const uint64_t below = j == 0 ? 0ull : (~0ull >> (64 - j));
+        const bool in = t0 + lane < S;
+        int slot = -1;
+        for (int r = 0; r < k; ++r) {
+            const int64_t q = static_cast<int64_t>(r) * S + s;
+            const int e = idx[q];
+            const int te = in ? idx[static_cast<int64_t>(r) * S + t0 + lane] : -1;
+            const int rank = __popcll(__ballot(te == e) & below);
+            const int l = offsets[(static_cast<int64_t>(e) * k + r) * nblk + tile] + rank;
+            if (lane == 0) {
+                loc[q] = l;
+                if (slot_route != nullptr && l < C) slot_route[static_cast<int64_t>(e) * C + l] = static_cast<int32_t>(q);
+            }
+            if (lane == r) slot = l < C ? e * C + l : -1;
+        }
+        const uint4 *src = x + s * V;
+        int v = lane;
+        for (; v + 3 * kWave < V; v += 4 * kWave) {
+            uint4 a[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) a[u] = src[v + u * kWave];
+            for (int r = 0; r < k; ++r) {
+                const int sl = wave_read(slot, r);
+                if (sl < 0) continue;
+                uint4 *dst = buf + static_cast<int64_t>(sl) * V + v;
+#pragma unroll
+                for (int u = 0; u < 4; ++u) dst[u * kWave] = a[u];
+            }
+        }
+        for (; v < V; v += kWave) {
+            const uint4 a = src[v];
+            for (int r = 0; r < k; ++r) {
+                const int sl = wave_read(slot, r);
+                if (sl >= 0) buf[static_cast<int64_t>(sl) * V + v] = a;
+            }
+        }
+    }
+    // Padding rows j in [min(needed[e], C), C) of every expert are +0.
+    const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
+    const int64_t rows = static_cast<int64_t>(E) * C;
+    for (int64_t row = global_wave(); row < rows; row += nw) {
+        const int e = static_cast<int>(row / C);
+        const int j = static_cast<int>(row - static_cast<int64_t>(e) * C);
+        if (j < min(needed[e], C)) continue;
+        uint4 *dst = buf + row * V;
+        for (int v = lane; v < V; v += kWave) dst[v] = zero;
+    }
+}
+
 // ---------------------------------------------------------------- decode / gather-sum
 
 template <bool BF16>
@@ -497,6 +569,18 @@ hipError_t launch_encode(const moe_shape &s, const void *x, const int32_t *idx, 
     const int grid = grid_for(static_cast<int64_t>(s.S) + static_cast<int64_t>(s.E) * cmax);
     hipLaunchKernelGGL(encode_kernel, dim3(grid), dim3(kThreads), 0, st, static_cast<const uint4 *>(x), idx, loc, fill,
                        cap, static_cast<uint4 *>(buf), s.S, s.E, s.k, V);
+    return hipGetLastError();
+}
+
+hipError_t launch_assign_encode(const moe_shape &s, const void *x, const int32_t *idx, RouteWs ws,
+                                const int32_t *needed, int64_t cap_by_factor, int32_t *loc, int32_t *fill,
+                                int32_t *cap, int32_t *slot_route, void *buf, int32_t cmax, hipStream_t st) {
+    const int eb = s.dtype == MOE_DT_BF16 ? 2 : 4;
+    const int V = s.M * eb / 16;
+    const int grid = grid_for(static_cast<int64_t>(s.S) + static_cast<int64_t>(s.E) * cmax);
+    hipLaunchKernelGGL(assign_encode_kernel, dim3(grid), dim3(kThreads), 0, st, static_cast<const uint4 *>(x), idx,
+                       ws.counts, needed, s.S, s.E, s.k, ws.nblk, capacity_mode(s), cap_by_factor, loc, fill, cap,
+                       slot_route, static_cast<uint4 *>(buf), V);
     return hipGetLastError();
 }
 

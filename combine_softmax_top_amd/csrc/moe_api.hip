@@ -499,11 +499,11 @@ moe_status layer_forward_impl(const moe_shape *shape, const void *x, const float
         logits = logits_out;
     }
     moe::RouteWs w{static_cast<int32_t *>(ws), num_tiles(s)};
-    if ((e = moe::launch_route(s, logits, idx, loc, gates, needed, fill, capacity, slot_route, w, by_factor(s), strm)) !=
-        hipSuccess)
+    if ((e = moe::launch_route_counts(s, logits, idx, gates, needed, w, strm)) != hipSuccess)
         return hip_fail(e, "route");
-    if ((e = moe::launch_encode(s, x, idx, loc, fill, capacity, buf, cmax, strm)) != hipSuccess)
-        return hip_fail(e, "encode");
+    if ((e = moe::launch_assign_encode(s, x, idx, w, needed, by_factor(s), loc, fill, capacity, slot_route, buf, cmax,
+                                       strm)) != hipSuccess)
+        return hip_fail(e, "route assignment and encode");
     if ((e = moe::launch_fc1(s, buf, W1, b1, fill, capacity, pre, h, cmax, strm)) != hipSuccess)
         return hip_fail(e, "expert fc1");
     if ((e = moe::launch_fc2(s, h, W2, b2, fill, capacity, y, cmax, strm)) != hipSuccess)
@@ -571,11 +571,11 @@ moe_status moe_layer_forward_pipelined(const moe_shape *shape, const void *x, co
         logits = logits_out;
     }
     moe::RouteWs w{static_cast<int32_t *>(ws), num_tiles(s)};
-    if ((e = moe::launch_route(s, logits, idx, loc, gates, needed, fill, capacity, slot_route, w, by_factor(s), strm)) !=
-        hipSuccess)
+    if ((e = moe::launch_route_counts(s, logits, idx, gates, needed, w, strm)) != hipSuccess)
         return hip_fail(e, "route");
-    if ((e = moe::launch_encode(s, x, idx, loc, fill, capacity, buf, cmax, strm)) != hipSuccess)
-        return hip_fail(e, "encode");
+    if ((e = moe::launch_assign_encode(s, x, idx, w, needed, by_factor(s), loc, fill, capacity, slot_route, buf, cmax,
+                                       strm)) != hipSuccess)
+        return hip_fail(e, "route assignment and encode");
     auto ev = [&](int i) { return reinterpret_cast<hipEvent_t>(events[i]); };
     if ((e = hipEventRecord(ev(0), strm)) != hipSuccess) return hip_fail(e, "event record");
     for (int i = 0; i < nstreams; ++i)

@@ -158,6 +158,35 @@ hipError_t launch_gate_project(const moe_shape &s, const void *x, const float *W
                                hipStream_t st);
 // Whether the gate projection's LDS tiles fit for this model dim / expert count.
 bool gate_supported(int M, int E, int dtype);
+// Capacity C from the per-expert route counts, in every thread of a 256-thread
+// block: mode +1 the factor's bound (cap_by_factor), 0 the largest count, -1 the
+// smaller of the two; at least 1. sh: 4 ints of LDS.
+__device__ __forceinline__ int block_capacity(const int32_t *needed, int E, int mode, int64_t cap_by_factor,
+                                              int *sh) {
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    int mx = 0;
+    for (int e = tid; e < E; e += 256) mx = max(mx, needed[e]);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) mx = max(mx, __shfl_xor(mx, off, 64));
+    if (lane == 0) sh[wv] = mx;
+    __syncthreads();
+    mx = max(max(sh[0], sh[1]), max(sh[2], sh[3]));
+    const int64_t c = mode > 0 ? cap_by_factor : (mode == 0 ? mx : min<int64_t>(cap_by_factor, mx));
+    return static_cast<int>(c < 1 ? 1 : c);
+}
+inline int capacity_mode(const moe_shape &s) {
+    return s.capacity_factor > 0 ? 1 : (s.capacity_factor == 0 ? 0 : -1);
+}
+
+// Routing phases 1 and 2 only (top-k, gates, per-tile counts scanned to offsets,
+// needed); launch_assign_encode then places every route and encodes.
+hipError_t launch_route_counts(const moe_shape &s, const float *logits, int32_t *idx, float *gates,
+                               int32_t *needed, RouteWs ws, hipStream_t st);
+// Phase 3 of routing fused with encode: loc, fill, capacity and slot_route as
+// launch_route's, and buf as launch_encode's, in one launch.
+hipError_t launch_assign_encode(const moe_shape &s, const void *x, const int32_t *idx, RouteWs ws,
+                                const int32_t *needed, int64_t cap_by_factor, int32_t *loc, int32_t *fill,
+                                int32_t *cap, int32_t *slot_route, void *buf, int32_t cmax, hipStream_t st);
 hipError_t launch_route(const moe_shape &s, const float *logits, int32_t *idx, int32_t *loc,
                         float *gates, int32_t *needed, int32_t *fill, int32_t *cap, int32_t *slot_route,
                         RouteWs ws, int64_t cap_by_factor, hipStream_t st);

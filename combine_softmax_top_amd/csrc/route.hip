@@ -18,6 +18,9 @@
 //                     ballots (a match over the expert id's bits), adds the
 //                     tile's offset, and compares with C, which every
 //                     workgroup derives from needed[] and capacity_factor.
+// The fused layer forward runs phase 3 inside the encode launch instead
+// (assign_encode_kernel: the same ranks and offsets, one wavefront per token),
+// so routing and encode there take three launches, not four.
 #include "moe_internal.h"
 
 namespace moe {
@@ -168,15 +171,7 @@ __global__ __launch_bounds__(256) void route_assign_kernel(
     int32_t *__restrict__ fill, int32_t *__restrict__ cap_out, int32_t *__restrict__ slot_route) {
     __shared__ int sh[4];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    int mx = 0;
-    for (int e = tid; e < E; e += 256) mx = max(mx, needed[e]);
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) mx = max(mx, __shfl_xor(mx, off, 64));
-    if (lane == 0) sh[wv] = mx;
-    __syncthreads();
-    mx = max(max(sh[0], sh[1]), max(sh[2], sh[3]));
-    int64_t Cl = mode > 0 ? cap_by_factor : (mode == 0 ? mx : min<int64_t>(cap_by_factor, mx));
-    const int C = static_cast<int>(Cl < 1 ? 1 : Cl);
+    const int C = block_capacity(needed, E, mode, cap_by_factor, sh);
     if (blockIdx.x == 0) {
         if (tid == 0) cap_out[0] = C;
         for (int e = tid; e < E; e += 256) fill[e] = min(needed[e], C);
@@ -212,9 +207,8 @@ static hipError_t launch_topk(const float *logits, int S, int E, int k, int nblk
     return hipGetLastError();
 }
 
-hipError_t launch_route(const moe_shape &s, const float *logits, int32_t *idx, int32_t *loc, float *gates,
-                        int32_t *needed, int32_t *fill, int32_t *cap, int32_t *slot_route, RouteWs ws,
-                        int64_t cap_by_factor, hipStream_t st) {
+hipError_t launch_route_counts(const moe_shape &s, const float *logits, int32_t *idx, float *gates,
+                               int32_t *needed, RouteWs ws, hipStream_t st) {
     const int S = s.S, E = s.E, k = s.k, nblk = ws.nblk;
     hipError_t err = hipSuccess;
     if (nblk > 0) {
@@ -241,10 +235,19 @@ hipError_t launch_route(const moe_shape &s, const float *logits, int32_t *idx, i
     }
     const int L = k * nblk;
     hipLaunchKernelGGL(route_scan_kernel, dim3(E), dim3(256), 0, st, ws.counts, L, needed);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
+    return hipGetLastError();
+}
+
+hipError_t launch_route(const moe_shape &s, const float *logits, int32_t *idx, int32_t *loc, float *gates,
+                        int32_t *needed, int32_t *fill, int32_t *cap, int32_t *slot_route, RouteWs ws,
+                        int64_t cap_by_factor, hipStream_t st) {
+    const int S = s.S, E = s.E, k = s.k, nblk = ws.nblk;
+    hipError_t err = launch_route_counts(s, logits, idx, gates, needed, ws, st);
+    if (err != hipSuccess) return err;
+    const int L = k * nblk;
     int ebits = 0;
     while ((1 << ebits) < E) ++ebits;
-    const int mode = s.capacity_factor > 0 ? 1 : (s.capacity_factor == 0 ? 0 : -1);
+    const int mode = capacity_mode(s);
     const int blocks = L > 0 ? (L + 3) / 4 : 1;
     hipLaunchKernelGGL(route_assign_kernel, dim3(blocks), dim3(256), 0, st, idx, ws.counts, needed, S, E, k, nblk,
                        ebits, mode, cap_by_factor, loc, fill, cap, slot_route);
