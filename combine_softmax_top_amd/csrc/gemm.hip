@@ -438,12 +438,15 @@ __device__ __forceinline__ int epi_swz(int r, int c) {
 }
 
 constexpr int kBigKB = 64;  // k per ring stage of the large-tile GEMM
-// LDS of the large-tile GEMM: two ring stages, the tile prefix table
-// (kMaxE + 1 ints, padded to 16 bytes), then the tile's BN bias values.
+// LDS of the MX GEMM after its ring: the tile prefix table (kMaxE + 1 ints,
+// padded to 16 bytes), then the tile's BN bias values.
 constexpr int kBigPrefixBytes = ((kMaxE + 1) * 4 + 15) / 16 * 16;
+// LDS of the large-tile bf16 GEMM: the two ring stages only (its tile schedule
+// lives in registers and its bias is read from global memory), so a 192 x 128
+// tile (80 KiB) runs two workgroups per CU.
 template <int BM, int BN>
 constexpr int big_lds_bytes() {
-    return 2 * (BM + BN) * kBigKB * 2 + kBigPrefixBytes + BN * 2;
+    return 2 * (BM + BN) * kBigKB * 2;
 }
 
 // Tile schedule of a persistent rows-grouped GEMM. Expert e has
@@ -530,6 +533,67 @@ __device__ __forceinline__ void decode_tile(int L, const int *prefix, int E, int
     ctile = within / gm;
 }
 
+// The same tile schedule without LDS, computed by every wavefront for itself:
+// lane l of a 64-expert chunk holds expert e0 + l's row tiles, a wavefront scan
+// gives the prefix, and a ballot finds the tile's expert. Every lane returns
+// the same values.
+__device__ __forceinline__ int wave_row_tiles(const int32_t *fill, int e, int E, int BMv, int s0, int s1) {
+    return e < E ? (window_rows(fill, e, s0, s1) + BMv - 1) / BMv : 0;
+}
+
+__device__ __forceinline__ TileSched wave_sched(const int32_t *fill, int E, int BMv, int nx, int s0, int s1) {
+    const int lane = threadIdx.x & 63;
+    int total = 0;
+    for (int e0 = 0; e0 < E; e0 += 64) {
+        int v = wave_row_tiles(fill, e0 + lane, E, BMv, s0, s1);
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+        total += v;
+    }
+    TileSched sc;
+    sc.T = total * nx;
+    const int x = blockIdx.x % kXcds, nb = gridDim.x / kXcds;  // gridDim.x is a multiple of 8
+    const int per = (sc.T + kXcds - 1) / kXcds;
+    const int start = min(sc.T, x * per);
+    sc.end = min(sc.T, start + per);
+    sc.first = start + static_cast<int>(blockIdx.x) / kXcds;
+    sc.stride = nb;
+    return sc;
+}
+
+// tile number -> (expert, row tile, column tile), as decode_tile
+__device__ __forceinline__ void wave_decode_tile(int L, const int32_t *fill, int E, int BMv, int nx, int s0, int s1,
+                                                 int &e, int &rtile, int &ctile) {
+    const int lane = threadIdx.x & 63;
+    const int r = L / nx;  // global row-tile index
+    int base = 0, before = 0, rt_e = 1;
+    e = 0;
+    for (int e0 = 0; e0 < E; e0 += 64) {
+        const int rt = wave_row_tiles(fill, e0 + lane, E, BMv, s0, s1);
+        int inc = rt;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int o = __shfl_up(inc, off, 64);
+            if (lane >= off) inc += o;
+        }
+        const uint64_t hit = __ballot(base + inc > r);  // experts whose tiles end past r
+        if (hit != 0ull) {
+            const int l = __ffsll(static_cast<long long>(hit)) - 1;
+            e = e0 + l;
+            rt_e = __shfl(rt, l, 64);
+            before = base + __shfl(inc, l, 64) - rt_e;
+            break;
+        }
+        base += __shfl(inc, 63, 64);
+    }
+    const int u = L - before * nx;  // tile within the expert
+    const int g = u / (kGroupM * nx);
+    const int gm = min(kGroupM, rt_e - g * kGroupM);
+    const int within = u - g * kGroupM * nx;
+    rtile = g * kGroupM + within % gm;
+    ctile = within / gm;
+}
+
 // K loop ("ping-pong"): two LDS stages of 64 k. The workgroup barrier of stage
 // t sits before its last 16-wide slice: by then every wavefront has read all of
 // stage t's fragments (waited with lgkmcnt(0)) and has waited for its own loads
@@ -544,7 +608,7 @@ __device__ __forceinline__ void decode_tile(int L, const int *prefix, int E, int
 // fc2 (bias), plain, and the activation gradient (D = acc * act'(aux), aux the
 // saved pre-activation, staged through LDS so that the product is rounded once).
 template <int BM, int BN, int NTH, int EPI, int ACT, bool BMN, int WR = 2>
-__global__ __launch_bounds__(NTH, 1) void rows_gemm_big(const bf16_t *__restrict__ A, const bf16_t *__restrict__ B,
+__global__ __launch_bounds__(NTH, (big_lds_bytes<BM, BN>() * 2 <= 160 * 1024 ? 2 : 1)) void rows_gemm_big(const bf16_t *__restrict__ A, const bf16_t *__restrict__ B,
                                                       bf16_t *__restrict__ D, int N, int K, int E,
                                                       const int32_t *__restrict__ fill,
                                                       const int32_t *__restrict__ cap,
@@ -560,17 +624,15 @@ __global__ __launch_bounds__(NTH, 1) void rows_gemm_big(const bf16_t *__restrict
     constexpr int LPS = (BM + BN) * KB / 8 / NTH;  // direct-load instructions per stage per thread
     static_assert(BM * BN <= 2 * STAGE, "the epilogue tile must fit in the ring");
     static_assert(BM * (BN / 8) % NTH == 0, "epilogue chunks must split evenly over the threads");
-    int *prefix = reinterpret_cast<int *>(lds + 2 * STAGE);
-    bf16_t *sbias = lds + 2 * STAGE + kBigPrefixBytes / 2;
     const int nx = (N + BN - 1) / BN;
-    const TileSched sc = make_sched<NTH>(fill, E, BM, nx, prefix, s0, s1);
+    const TileSched sc = wave_sched(fill, E, BM, nx, s0, s1);
     const int C = *cap;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wr0 = (wave / WGC) * (BM / WR), wc0 = (wave % WGC) * (BN / WGC);
     const int nk = K / KB;
     for (int L = sc.first; L < sc.end; L += sc.stride) {
         int g, rtile, ctile;
-        decode_tile(L, prefix, E, nx, g, rtile, ctile);
+        wave_decode_tile(L, fill, E, BM, nx, s0, s1, g, rtile, ctile);
         const int row0 = rtile * BM, col0 = ctile * BN;
         const int rows_valid = min(BM, window_rows(fill, g, s0, s1) - row0);
         const int cols_valid = min(BN, N - col0);
@@ -594,15 +656,6 @@ __global__ __launch_bounds__(NTH, 1) void rows_gemm_big(const bf16_t *__restrict
         // The previous tile's LDS reads (epilogue) are complete in every
         // wavefront; its global stores may still be in flight.
         barrier_keep_loads_lds();
-        // The tile's BN bias values go to LDS by one direct load of wavefront 0,
-        // issued before the ring's loads: vector-memory loads complete in order,
-        // so the stage waits below (which count only the newest loads) cover it.
-        // Columns past the matrix read the last valid chunk and are never used.
-        if (bias != nullptr && wave == 0 && lane < BN / 8) {
-            const int c = min(lane * 8, cols_valid - 8);
-            __builtin_amdgcn_global_load_lds(bias + static_cast<int64_t>(g) * N + col0 + c, (lds_void_t *)sbias, 16,
-                                             0, 0);
-        }
         dma_tile<BM, KB, NW>(Ab, K, rows_valid, 0, lds, wave, lane);
         load_b(0, lds + BM * KB);
         if (nk > 1) {
@@ -614,13 +667,16 @@ __global__ __launch_bounds__(NTH, 1) void rows_gemm_big(const bf16_t *__restrict
         }
         barrier_keep_loads();
         if (bias != nullptr) {
-            // the accumulators start at the bias: the epilogue then only applies the activation
+            // the accumulators start at the bias (read from global memory, L2-resident;
+            // columns past the matrix read the last valid chunk and are never stored):
+            // the epilogue then only applies the activation
+            const bf16_t *bt = bias + static_cast<int64_t>(g) * N + col0;
 #pragma unroll
             for (int j = 0; j < TN; ++j)
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     float b4[4];
-                    load4_bf16(sbias + wc0 + j * 32 + 8 * q + 4 * (lane >> 5), b4);
+                    load4_bf16(bt + min(wc0 + j * 32 + 8 * q + 4 * (lane >> 5), cols_valid - 4), b4);
 #pragma unroll
                     for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -1434,7 +1490,7 @@ hipError_t big_launch(int act, const void *A, const void *B, void *D, int N, int
                       const int32_t *cap, const void *bias, void *pre_out, hipStream_t st,
                       const void *aux = nullptr, int s0 = 0, int s1 = 0x7FFFFFFF) {
     constexpr int lds = big_lds_bytes<BM, BN>();
-    constexpr int per_cu = (160 * 1024) / lds >= 2 ? 2 : 1;
+    constexpr int per_cu = (160 * 1024) / lds >= 2 ? 2 : 1;  // the kernel's launch bounds match
     const dim3 grid(resident_blocks(per_cu));
     auto a = static_cast<const bf16_t *>(A);
     auto b = static_cast<const bf16_t *>(B);
@@ -1485,12 +1541,26 @@ static int gemm_cfg_override() {
     return v;
 }
 
+// Rounds of a persistent grid of `slots` workgroups over E experts' row tiles of
+// BMv rows and nx column tiles, at an even fill f per expert; fills vary around
+// f, so an expert is taken to need f / BMv + 1/2 row tiles, rounded up.
+static int64_t tile_rounds(int64_t f, int BMv, int64_t nx, int E, int64_t slots) {
+    const int64_t rt = (2 * f + BMv + 2 * BMv - 1) / (2 * BMv);
+    return (E * rt * nx + slots - 1) / slots;
+}
+
 static int default_cfg(int N, int K, int64_t rows_hint, int E) {
     const int64_t big_tiles = ((rows_hint + 255) / 256) * ((N + 255) / 256);
-    if (K <= 1024 || big_tiles < 128) return 3;
-    const int64_t f = (rows_hint + E - 1) / E, nx = (N + 255) / 256, cus = resident_blocks(1);
-    const int64_t r256 = (E * ((f + 255) / 256) * nx + cus - 1) / cus;
-    const int64_t r192 = (E * ((f + 191) / 192) * nx + cus - 1) / cus;
+    const int64_t f = (rows_hint + E - 1) / E, cus = resident_blocks(1);
+    if (K <= 1024 || big_tiles < 128) {
+        // two workgroups per CU: 128 x 128 tiles, or 192 x 128 where they take
+        // fewer rounds (each costs about 1.5 of a 128-row round)
+        const int64_t n128 = (N + 127) / 128;
+        const int64_t r128 = tile_rounds(f, 128, n128, E, 2 * cus), r192 = tile_rounds(f, 192, n128, E, 2 * cus);
+        return r192 * 3 < r128 * 2 ? 5 : 3;
+    }
+    const int64_t nx = (N + 255) / 256;
+    const int64_t r256 = tile_rounds(f, 256, nx, E, cus), r192 = tile_rounds(f, 192, nx, E, cus);
     return r192 * 192 * 100 < r256 * 256 * 92 ? 4 : 1;
 }
 
@@ -1500,11 +1570,12 @@ template <int EPI>
 hipError_t bwd_data_launch(int act, const void *A, const void *B, void *D, int N, int K, int E, const int32_t *fill,
                            const int32_t *cap, const void *aux, int64_t rows_hint, hipStream_t st) {
     int cfg = gemm_cfg_override();
-    if (cfg < 1 || cfg > 4) cfg = default_cfg(N, K, rows_hint, E);
+    if (cfg < 1 || cfg > 5) cfg = default_cfg(N, K, rows_hint, E);
     switch (cfg) {
     case 1: return big_launch<256, 256, 512, EPI, true>(act, A, B, D, N, K, E, fill, cap, nullptr, nullptr, st, aux);
     case 2: return big_launch<256, 128, 256, EPI, true>(act, A, B, D, N, K, E, fill, cap, nullptr, nullptr, st, aux);
     case 4: return big_launch<192, 256, 512, EPI, true>(act, A, B, D, N, K, E, fill, cap, nullptr, nullptr, st, aux);
+    case 5: return big_launch<192, 128, 256, EPI, true>(act, A, B, D, N, K, E, fill, cap, nullptr, nullptr, st, aux);
 
     default: return big_launch<128, 128, 256, EPI, true>(act, A, B, D, N, K, E, fill, cap, nullptr, nullptr, st, aux);
     }
@@ -1515,11 +1586,12 @@ hipError_t fwd_launch(int act, const void *A, const void *B, void *D, int N, int
                       const int32_t *fill, const int32_t *cap, const void *bias, void *pre_out, hipStream_t st,
                       int s0 = 0, int s1 = 0x7FFFFFFF) {
     int cfg = gemm_cfg_override();
-    if (cfg < 1 || cfg > 4) cfg = default_cfg(N, K, rows_hint, E);
+    if (cfg < 1 || cfg > 5) cfg = default_cfg(N, K, rows_hint, E);
     switch (cfg) {
     case 1: return big_launch<256, 256, 512, EPI>(act, A, B, D, N, K, E, fill, cap, bias, pre_out, st, nullptr, s0, s1);
     case 2: return big_launch<256, 128, 256, EPI>(act, A, B, D, N, K, E, fill, cap, bias, pre_out, st, nullptr, s0, s1);
     case 4: return big_launch<192, 256, 512, EPI>(act, A, B, D, N, K, E, fill, cap, bias, pre_out, st, nullptr, s0, s1);
+    case 5: return big_launch<192, 128, 256, EPI>(act, A, B, D, N, K, E, fill, cap, bias, pre_out, st, nullptr, s0, s1);
 
     default:
         return big_launch<128, 128, 256, EPI>(act, A, B, D, N, K, E, fill, cap, bias, pre_out, st, nullptr, s0, s1);
