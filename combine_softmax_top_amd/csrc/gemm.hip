@@ -551,7 +551,7 @@ __device__ __forceinline__ TileSched wave_sched(const int32_t *fill, int E, int 
         total += v;
     }
     TileSched sc;
-    sc.T = total * nx;
+    sc.T = __builtin_amdgcn_readfirstlane(total) * nx;
     const int x = blockIdx.x % kXcds, nb = gridDim.x / kXcds;  // gridDim.x is a multiple of 8
     const int per = (sc.T + kXcds - 1) / kXcds;
     const int start = min(sc.T, x * per);
@@ -586,6 +586,10 @@ __device__ __forceinline__ void wave_decode_tile(int L, const int32_t *fill, int
         }
         base += __shfl(inc, 63, 64);
     }
+    // wavefront-uniform: kept in scalar registers (so are the addresses derived from them)
+    e = __builtin_amdgcn_readfirstlane(e);
+    before = __builtin_amdgcn_readfirstlane(before);
+    rt_e = __builtin_amdgcn_readfirstlane(rt_e);
     const int u = L - before * nx;  // tile within the expert
     const int g = u / (kGroupM * nx);
     const int gm = min(kGroupM, rt_e - g * kGroupM);
@@ -666,7 +670,7 @@ __global__ __launch_bounds__(NTH, (big_lds_bytes<BM, BN>() * 2 <= 160 * 1024 ? 2
             wait_vmcnt<0>();
         }
         barrier_keep_loads();
-        if (bias != nullptr) {
+        if (EPI <= EPI_FC2 && bias != nullptr) {  // only the forward products have a bias
             // the accumulators start at the bias (read from global memory, L2-resident;
             // columns past the matrix read the last valid chunk and are never stored):
             // the epilogue then only applies the activation
