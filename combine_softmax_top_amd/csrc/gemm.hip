@@ -523,9 +523,10 @@ __device__ __forceinline__ void decode_tile(int L, const int *prefix, int E, int
         if (prefix[mid] <= r) lo = mid;
         else hi = mid - 1;
     }
-    e = lo;
-    const int rt_e = prefix[e + 1] - prefix[e];
-    const int u = L - prefix[e] * nx;  // tile within the expert
+    e = __builtin_amdgcn_readfirstlane(lo);  // wavefront-uniform: scalar registers
+    const int pe = __builtin_amdgcn_readfirstlane(prefix[e]);
+    const int rt_e = __builtin_amdgcn_readfirstlane(prefix[e + 1]) - pe;
+    const int u = L - pe * nx;  // tile within the expert
     const int g = u / (kGroupM * nx);
     const int gm = min(kGroupM, rt_e - g * kGroupM);
     const int within = u - g * kGroupM * nx;
