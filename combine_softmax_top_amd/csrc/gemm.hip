@@ -1158,7 +1158,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const bf16_t *base, u
 }
 
 template <int BM, int BN, int NTH>
-__global__ __launch_bounds__(NTH, 1) void kgrad_gemm_big(const bf16_t *__restrict__ X, const bf16_t *__restrict__ Y,
+__global__ __launch_bounds__(NTH, (4 * (BM + BN) * kBigKB * 2 <= 160 * 1024 ? 2 : 1)) void kgrad_gemm_big(const bf16_t *__restrict__ X, const bf16_t *__restrict__ Y,
                                                        float *__restrict__ D, int P, int Q, int E,
                                                        const int32_t *__restrict__ fill,
                                                        const int32_t *__restrict__ cap,
@@ -1605,11 +1605,31 @@ hipError_t fwd_launch(int act, const void *A, const void *B, void *D, int N, int
 
 // Weight gradients: the large-tile kernel when one expert's rows of either
 // operand span less than 2 GiB (its raw-buffer offsets are 32-bit), else the
-// register-staged kernel below.
+// register-staged kernel below. The reduction runs over an expert's rows: up to
+// about 1024 of them (16 K steps) the fp32 tile's store is a large share of a
+// tile, and 128 x 128 tiles at two workgroups per CU overlap one's stores with
+// the other's MFMAs (the bench layer's backward: 500 -> 488 us); with more rows
+// 256 x 256 tiles win (S=32768, E=128, k=8: 19.5 vs 20.7 ms). MOE_KGRAD_CFG
+// (1 = 256 x 256, 2 = 128 x 128) overrides the choice for tuning.
 hipError_t kgroup_launch(const void *A, const void *B, float *D, int Mo, int No, int E, const int32_t *fill,
-                         const int32_t *cap, float *colsum, int32_t cmax, hipStream_t st) {
+                         const int32_t *cap, float *colsum, int32_t cmax, int64_t rows_hint, hipStream_t st) {
     // the last K step reads up to 63 rows past the expert's fill (they read as zero)
     if (static_cast<int64_t>(cmax + 64) * std::max(Mo, No) * 2 < (int64_t(1) << 31)) {
+        static const int kc = [] {
+            const char *v = getenv("MOE_KGRAD_CFG");
+            return v ? atoi(v) : 0;
+        }();
+        const bool small = kc == 2 || (kc != 1 && rows_hint <= 1024LL * E);
+        if (small) {
+            constexpr int lds = 2 * (128 + 128) * kBigKB * 2;
+            auto k = kgrad_gemm_big<128, 128, 256>;
+            static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(k),
+                                                               hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+            if (attr != hipSuccess) return attr;
+            hipLaunchKernelGGL(k, dim3(resident_blocks(2)), dim3(256), lds, st, static_cast<const bf16_t *>(A),
+                               static_cast<const bf16_t *>(B), D, Mo, No, E, fill, cap, colsum);
+            return hipGetLastError();
+        }
         constexpr int lds = 2 * (256 + 256) * kBigKB * 2;
         auto k = kgrad_gemm_big<256, 256, 512>;
         static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(k),
@@ -1757,13 +1777,14 @@ hipError_t launch_expert_ffn_bwd(const moe_shape &s, const void *buf, const void
             hipSuccess)
             return err;
         // dW2[e] = dy^T h (+ db2 = column sums of dy)
-        if ((err = kgroup_launch(dy, h, dW2, M, H, E, fill, cap, db2, cmax, st)) != hipSuccess) return err;
+        if ((err = kgroup_launch(dy, h, dW2, M, H, E, fill, cap, db2, cmax, rows_hint(s, cmax), st)) != hipSuccess)
+            return err;
         // dbuf = dpre . W1[e]: B = W1[e] read as [K=H][N=M]   (dbuf may alias dy: dy is consumed above)
         if ((err = bwd_data_launch<EPI_PLAIN>(s.act, dpre, W1, dbuf, M, H, E, fill, cap, nullptr, rows_hint(s, cmax),
                                               st)) != hipSuccess)
             return err;
         // dW1[e] = dpre^T buf (+ db1 = column sums of dpre)
-        return kgroup_launch(dpre, buf, dW1, H, M, E, fill, cap, db1, cmax, st);
+        return kgroup_launch(dpre, buf, dW1, H, M, E, fill, cap, db1, cmax, rows_hint(s, cmax), st);
     }
     SimtArgs a{};  // dpre = (dy . W2) * act'(pre); B(n=h, kk=m) = W2[e][m][h]
     a.A = static_cast<const float *>(dy); a.a_si = M; a.a_sk = 1; a.a_gfix = 0; a.a_gcap = M;
