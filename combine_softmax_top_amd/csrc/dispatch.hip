@@ -25,18 +25,32 @@ __device__ __forceinline__ int64_t global_wave() {
 }
 __device__ __forceinline__ int64_t num_waves() { return static_cast<int64_t>(gridDim.x) * kWavesPerBlock; }
 
-// Slot of route `lane` of token s (lanes < k), -1 when dropped or lane >= k.
-__device__ __forceinline__ int lane_slot(const int32_t *idx, const int32_t *loc, int64_t s, int S, int k, int C,
-                                         int lane) {
-    if (lane >= k) return -1;
-    const int64_t q = static_cast<int64_t>(lane) * S + s;
-    const int l = loc[q];
-    return l < C ? idx[q] * C + l : -1;
-}
-
 __device__ __forceinline__ int wave_read(int v, int lane) { return __builtin_amdgcn_readlane(v, lane); }
 __device__ __forceinline__ float wave_read(float v, int lane) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+// Lane r < k of a token's wavefront: the slot e * C + loc of route r (-1 when
+// the route was dropped) and, with gates given, its gate. The loads (loc, idx
+// and the gate, read whether or not the route was kept) all go out together and
+// are waited for once, here: the values pass through one empty asm statement.
+// Without it the compiler moves each read-only load into the branch that uses
+// it (one memory round trip after another), and its wait counting, which is
+// conservative where branches join, would wait for every load in flight
+// (vmcnt(0)) before each read of the slot or gate inside the per-route loops
+// that follow, one round trip per route row.
+__device__ __forceinline__ int lane_slot(const int32_t *idx, const int32_t *loc, const float *gates, int64_t s,
+                                         int S, int k, int C, int lane, float &g) {
+    int l = C, e = 0;
+    g = 0.f;
+    if (lane < k) {
+        const int64_t q = static_cast<int64_t>(lane) * S + s;
+        l = loc[q];
+        e = idx[q];
+        if (gates != nullptr) g = gates[q];
+    }
+    asm volatile("" : "+v"(l), "+v"(e), "+v"(g));
+    return l < C ? e * C + l : -1;
 }
 
 // ---------------------------------------------------------------- encode
@@ -51,7 +65,8 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const uint4 *__restric
     const int64_t nw = num_waves();
     const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
     for (int64_t s = global_wave(); s < S; s += nw) {
-        const int slot = lane_slot(idx, loc, s, S, k, C, lane);
+        float g_unused;
+        const int slot = lane_slot(idx, loc, nullptr, s, S, k, C, lane, g_unused);
         const uint4 *src = x + s * V;
         int v = lane;
         for (; v + 3 * kWave < V; v += 4 * kWave) {
@@ -211,9 +226,8 @@ __global__ __launch_bounds__(kThreads) void gather_sum_kernel(const uint4 *__res
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t nw = num_waves();
     for (int64_t s = global_wave(); s < S; s += nw) {
-        const int slot = lane_slot(idx, loc, s, S, k, C, lane);
-        float g = 0.f;
-        if (!UNIT && slot >= 0) g = gates[static_cast<int64_t>(lane) * S + s];
+        float g;
+        const int slot = lane_slot(idx, loc, UNIT ? nullptr : gates, s, S, k, C, lane, g);
         for (int v = lane; v < V; v += kWave) {
             float acc[N];
 #pragma unroll
@@ -269,9 +283,8 @@ __global__ __launch_bounds__(kThreads) void decode_bwd_kernel(const uint4 *__res
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t nw = num_waves();
     for (int64_t s = global_wave(); s < S; s += nw) {
-        const int slot = lane_slot(idx, loc, s, S, k, C, lane);
-        float g = 0.f;
-        if (slot >= 0) g = gates[static_cast<int64_t>(lane) * S + s];
+        float g;
+        const int slot = lane_slot(idx, loc, gates, s, S, k, C, lane, g);
         const uint4 *drow = dout + s * V;
         for (int r = 0; r < k; ++r) {
             const int sl = wave_read(slot, r);
@@ -380,6 +393,19 @@ __host__ GateTile gate_tile(int S, int M, int E, int esz) {
     return t;
 }
 
+// The eight loaded values of a staging batch pass through one empty asm
+// statement, so every load of the batch is issued (and waited for once) before
+// the first of the conditional LDS stores that consume them. Without it the
+// compiler sinks each load into its store's branch (the inputs are read-only,
+// so nothing pins the loads), and the batch costs one memory round trip per load.
+typedef float gate_f4 __attribute__((ext_vector_type(4)));
+typedef uint32_t gate_u4 __attribute__((ext_vector_type(4)));
+template <class V>
+__device__ __forceinline__ void issue_together(V (&r)[8]) {
+    asm volatile("" : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]), "+v"(r[4]), "+v"(r[5]), "+v"(r[6]),
+                 "+v"(r[7]));
+}
+
 template <bool BF16, int TPL>
 __global__ __launch_bounds__(kThreads) void gate_project_kernel(const void *__restrict__ xv,
                                                                 const float *__restrict__ Wg,
@@ -405,9 +431,9 @@ __global__ __launch_bounds__(kThreads) void gate_project_kernel(const void *__re
         // every expert: Wg is M*E contiguous floats; a chunk's L*E of them are
         // contiguous in LDS too (L*E is a multiple of 4)
         const int total4 = M * E / 4;
-        const float4 *w4 = reinterpret_cast<const float4 *>(Wg);
+        const gate_f4 *w4 = reinterpret_cast<const gate_f4 *>(Wg);
         for (int i0 = tid; i0 < total4; i0 += 8 * kThreads) {
-            float4 r[8];
+            gate_f4 r[8];
             int dst[8];
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
@@ -416,9 +442,10 @@ __global__ __launch_bounds__(kThreads) void gate_project_kernel(const void *__re
                 r[u] = w4[i];
                 dst[u] = c * tl.wpitch + (i - c * (L * E / 4)) * 4;
             }
+            issue_together(r);
 #pragma unroll
             for (int u = 0; u < 8; ++u)
-                if (i0 + u * kThreads < total4) *reinterpret_cast<float4 *>(wl + dst[u]) = r[u];
+                if (i0 + u * kThreads < total4) *reinterpret_cast<gate_f4 *>(wl + dst[u]) = r[u];
         }
     } else {
         const FastDiv dne = ne == ET ? tl.dne : FastDiv{static_cast<uint32_t>(ne), 0u, 0u};
@@ -434,6 +461,7 @@ __global__ __launch_bounds__(kThreads) void gate_project_kernel(const void *__re
                 r[u] = Wg[static_cast<int64_t>(m) * E + e0 + e];
                 dst[u] = c * tl.wpitch + (m - c * L) * ET + e;
             }
+            issue_together(r);
 #pragma unroll
             for (int u = 0; u < 8; ++u)
                 if (i0 + u * kThreads < total) wl[dst[u]] = r[u];
@@ -444,9 +472,9 @@ __global__ __launch_bounds__(kThreads) void gate_project_kernel(const void *__re
         const int vpr = M / EPV;  // vectors per row
         const int vpc = L / EPV;  // vectors per chunk
         const int total = nt * vpr;
-        const uint4 *xg = reinterpret_cast<const uint4 *>(xv);
+        const gate_u4 *xg = reinterpret_cast<const gate_u4 *>(xv);
         for (int i0 = tid; i0 < total; i0 += 8 * kThreads) {
-            uint4 r[8];
+            gate_u4 r[8];
             int dst[8];
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
@@ -455,9 +483,10 @@ __global__ __launch_bounds__(kThreads) void gate_project_kernel(const void *__re
                 r[u] = xg[(s0 + t) * vpr + v];
                 dst[u] = (t * n + c) * tl.xpitch + (v - c * vpc) * 16;
             }
+            issue_together(r);
 #pragma unroll
             for (int u = 0; u < 8; ++u)
-                if (i0 + u * kThreads < total) *reinterpret_cast<uint4 *>(xl + dst[u]) = r[u];
+                if (i0 + u * kThreads < total) *reinterpret_cast<gate_u4 *>(xl + dst[u]) = r[u];
         }
     }
     __syncthreads();

@@ -650,13 +650,36 @@ __global__ __launch_bounds__(NTH, (big_lds_bytes<BM, BN>() * 2 <= 160 * 1024 ? 2
             else dma_tile<BN, KB, NW>(Bb, K, cols_valid, k0, dst, wave, lane);
         };
 
-        f32x16 acc[TM][TN];
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
+        // Only the forward products have a bias: the accumulators start at it (read
+        // from global memory, L2-resident; columns past the matrix read the last
+        // valid chunk and are never stored), so the epilogue only applies the
+        // activation. Its loads go out ahead of the prologue's stage loads: loads
+        // complete in order, so the wait for stage 0 covers them as well, where
+        // loads issued after stage 1 would hold the first MFMA until stage 1 lands.
+        // Tiles with 128 accumulators per lane at eight wavefronts (256 x 256) have
+        // no registers to spare across the prologue and read it after the prologue.
+        constexpr bool kBias = EPI <= EPI_FC2;
+        constexpr bool kEarlyBias = kBias && TM * TN * 16 < 128;
+        const bool with_bias = kBias && bias != nullptr;
+        const bf16_t *bt = with_bias ? bias + static_cast<int64_t>(g) * N + col0 : nullptr;
+        uint2 bq[kEarlyBias ? TN : 1][4];
+        if (kEarlyBias && with_bias) {
 #pragma unroll
             for (int j = 0; j < TN; ++j)
 #pragma unroll
-                for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+                for (int q = 0; q < 4; ++q)
+                    bq[kEarlyBias ? j : 0][q] = *reinterpret_cast<const uint2 *>(
+                        bt + min(wc0 + j * 32 + 8 * q + 4 * (lane >> 5), cols_valid - 4));
+        }
+        f32x16 acc[TM][TN];
+        if constexpr (!kEarlyBias) {
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+        }
 
         // The previous tile's LDS reads (epilogue) are complete in every
         // wavefront; its global stores may still be in flight.
@@ -671,11 +694,25 @@ __global__ __launch_bounds__(NTH, (big_lds_bytes<BM, BN>() * 2 <= 160 * 1024 ? 2
             wait_vmcnt<0>();
         }
         barrier_keep_loads();
-        if (EPI <= EPI_FC2 && bias != nullptr) {  // only the forward products have a bias
-            // the accumulators start at the bias (read from global memory, L2-resident;
-            // columns past the matrix read the last valid chunk and are never stored):
-            // the epilogue then only applies the activation
-            const bf16_t *bt = bias + static_cast<int64_t>(g) * N + col0;
+        if constexpr (kEarlyBias) {
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    float b4[4] = {0.f, 0.f, 0.f, 0.f};
+                    if (with_bias) {
+                        const uint2 u = bq[kEarlyBias ? j : 0][q];
+                        b4[0] = __uint_as_float(u.x << 16);
+                        b4[1] = __uint_as_float(u.x & 0xFFFF0000u);
+                        b4[2] = __uint_as_float(u.y << 16);
+                        b4[3] = __uint_as_float(u.y & 0xFFFF0000u);
+                    }
+#pragma unroll
+                    for (int i = 0; i < TM; ++i)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) acc[i][j][4 * q + r] = b4[r];
+                }
+        } else if (kBias && with_bias) {
 #pragma unroll
             for (int j = 0; j < TN; ++j)
 #pragma unroll
