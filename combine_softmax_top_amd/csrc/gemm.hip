@@ -1809,14 +1809,15 @@ hipError_t launch_expert_ffn_bwd(const moe_shape &s, const void *buf, const void
     const int M = s.M, H = s.H, E = s.E;
     hipError_t err;
     if (s.dtype == MOE_DT_BF16) {
+        // dW2[e] = dy^T h (+ db2 = column sums of dy)
+        if ((err = kgroup_launch(dy, h, dW2, M, H, E, fill, cap, db2, cmax, rows_hint(s, cmax), st)) != hipSuccess)
+            return err;
         // dpre = (dy . W2[e]) * act'(pre): A = dy [rows][M], B = W2[e] read as [K=M][N=H]
         if ((err = bwd_data_launch<EPI_DACT>(s.act, dy, W2, dpre, H, M, E, fill, cap, pre, rows_hint(s, cmax), st)) !=
             hipSuccess)
             return err;
-        // dW2[e] = dy^T h (+ db2 = column sums of dy)
-        if ((err = kgroup_launch(dy, h, dW2, M, H, E, fill, cap, db2, cmax, rows_hint(s, cmax), st)) != hipSuccess)
-            return err;
-        // dbuf = dpre . W1[e]: B = W1[e] read as [K=H][N=M]   (dbuf may alias dy: dy is consumed above)
+        // dbuf = dpre . W1[e]: B = W1[e] read as [K=H][N=M]   (dbuf may alias dy: dy is consumed above;
+        // run right after dpre is written, dpre's rows are still in the last-level cache)
         if ((err = bwd_data_launch<EPI_PLAIN>(s.act, dpre, W1, dbuf, M, H, E, fill, cap, nullptr, rows_hint(s, cmax),
                                               st)) != hipSuccess)
             return err;
