@@ -8,7 +8,10 @@ capacity_factor 1.25) that is gate projection -> route -> encode -> fc1 -> fc2
 summed into decode); workloads with a backward add the backward of decode, FFN, encode
 and the gate (dlogits through the softmax, the 0.01 load-balance loss, and for
 a projected gate dWg and the projection's share of dx). The timed region is exactly --steps calls of the fused C-ABI entry
-points, bracketed by synchronisations.
+points, bracketed by synchronisations. Forward workloads run consecutive batches on two streams by
+default, each stream with its own buffers (--batch-streams): a batch's short routing, encode and
+decode launches then overlap the neighbouring batch's expert products, which leave CUs idle in their
+last round. The same steps run one after another on one stream are timed too (single_stream).
 
 A second timed loop records HIP events around each stage on the stream the
 library launches on, to report each stage against its roofline (bytes or flops
@@ -55,6 +58,11 @@ def parse():
                     help="run the expert FFN in D capacity chunks on --pipeline-streams streams "
                          "(bf16 forward workloads; 0 = the fused forward)")
     ap.add_argument("--pipeline-streams", type=int, default=2)
+    ap.add_argument("--batch-streams", type=int, default=0, metavar="N",
+                    help="consecutive batches alternate over N streams, each stream with its own buffers, so that "
+                         "one batch's routing, encode and decode overlap the neighbouring batches' expert products; "
+                         "0 (default): 2 for forward workloads, 1 for training and pipelined runs. With N > 1 the "
+                         "same steps are also timed on one stream and reported as single_stream")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 3 plain device copies of MIB MiB each (the reference kernel that scales the "
                          "FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -255,15 +263,28 @@ def main():
         pstreams = [torch.cuda.Stream() for _ in range(args.pipeline_streams)]
         pevents = [torch.cuda.Event() for _ in range(args.pipeline_streams + 1)]
 
-    def step():
+    nb = args.batch_streams if args.batch_streams > 0 else (1 if (w.backward or pipe) else 2)
+    bsets, bstreams = [bufs], [None]
+    if nb > 1:
+        assert not w.backward and not pipe, "--batch-streams applies to the forward workloads"
+        for _ in range(nb - 1):
+            bsets.append(moe.alloc_forward_mx(s, dev, gate_projection=gate) if mxf is not None else
+                         moe.alloc_forward(s, dev, gate_projection=gate, residual=w.residual))
+        bstreams = [torch.cuda.Stream() for _ in range(nb)]
+    counter = [0]
+
+    def step(one_stream=False):
+        i = 0 if one_stream else counter[0] % nb
+        counter[0] += 1
+        b, st = bsets[i], bstreams[i]
         if mxf is not None:
-            moe.layer_forward_mx(s, mxf, x, W1q, b1, W2q, b2, logits=logits_in, Wg=Wg, bufs=bufs)
+            moe.layer_forward_mx(s, mxf, x, W1q, b1, W2q, b2, logits=logits_in, Wg=Wg, bufs=b, stream=st)
             return
         if pipe:
             moe.layer_forward_pipelined(s, x, W1, b1, W2, b2, args.pipeline_chunks, pstreams, pevents,
                                         logits=logits_in, Wg=Wg, bufs=bufs)
             return
-        moe.layer_forward(s, x, W1, b1, W2, b2, logits=logits_in, Wg=Wg, bufs=bufs, residual=res)
+        moe.layer_forward(s, x, W1, b1, W2, b2, logits=logits_in, Wg=Wg, bufs=b, residual=res, stream=st)
         if w.backward:
             backward()
 
@@ -278,6 +299,20 @@ def main():
     elapsed = time.perf_counter() - t0
     ms_per_step = elapsed * 1e3 / max(1, args.steps)
     value = w.S * args.steps / elapsed
+    single = None
+    if nb > 1:
+        # the same steps, one after another on one stream
+        for _ in range(args.warmup):
+            step(one_stream=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            step(one_stream=True)
+        torch.cuda.synchronize()
+        e1 = time.perf_counter() - t0
+        single = dict(value=round(w.S * args.steps / e1, 1), ms_per_step=round(e1 * 1e3 / max(1, args.steps), 5))
+        log(f"[bench] {nb} streams: {ms_per_step:.4f} ms/step; one stream: {single['ms_per_step']:.4f} ms/step, "
+            f"{single['value']:.4g} tokens/s")
 
     C = int(bufs["capacity"].item())
     kept = int(bufs["fill"].sum().item())
@@ -396,8 +431,9 @@ def main():
                     act="gelu" if w.act == W.ACT_GELU else "relu", biases=[w.has_fc1_bias, w.has_fc2_bias],
                     logits=w.logits, backward=w.backward, C=C, kept_routes=kept, parallelism="single-gpu",
                     aux_coef=moe.AUX_COEF if w.backward else None, residual=w.residual, mx=w.mx or None,
-                    pipeline=dict(chunks=args.pipeline_chunks, streams=args.pipeline_streams) if pipe else None),
-        roofline=roofline, stages=stages, cpu_baseline=cpu,
+                    pipeline=dict(chunks=args.pipeline_chunks, streams=args.pipeline_streams) if pipe else None,
+                    batch_streams=nb if nb > 1 else None),
+        roofline=roofline, stages=stages, cpu_baseline=cpu, single_stream=single,
     )
     print(json.dumps(line), flush=True)
 
