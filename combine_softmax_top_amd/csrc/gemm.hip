@@ -1194,6 +1194,59 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const bf16_t *base, u
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t *>(base), 0, static_cast<int>(bytes), 0x00020000);
 }
 
+// First tile of the weight-gradient tile list (expert-major, per_e tiles per
+// expert) at which cumulative work reaches t. A tile of expert e costs
+// w_e = ceil(fill[e] / KB) + 1 units (its K steps and its store); cw_e is the
+// work of the experts before e. The list is cut at work t, so that the 8 XCDs
+// get equal work rather than equal tile counts: with uneven fills (a skewed
+// router) equal tile counts leave one XCD with half again the mean work.
+// Computed by every wavefront for itself; every lane returns the same value.
+__device__ __forceinline__ int kgrad_cut(const int32_t *fill, int E, int per_e, int KB, int64_t t) {
+    const int lane = threadIdx.x & 63;
+    int64_t base = 0;
+    for (int e0 = 0; e0 < E; e0 += 64) {
+        const int e = e0 + lane;
+        const int64_t w = e < E ? static_cast<int64_t>((fill[e] + KB - 1) / KB + 1) : 0;
+        int64_t inc = w * per_e;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int64_t o = __shfl_up(inc, off, 64);
+            if (lane >= off) inc += o;
+        }
+        // the expert whose work range [cw_e, cw_e + W_e) holds t
+        const uint64_t hit = __ballot(e < E && base + inc > t);
+        if (hit != 0ull) {
+            const int l = __ffsll(static_cast<long long>(hit)) - 1;
+            const int64_t we = __shfl(w, l, 64);
+            const int64_t cw = base + __shfl(inc, l, 64) - we * per_e;
+            const int u = static_cast<int>(min<int64_t>((t - cw + we - 1) / we, per_e));
+            // a cut within an eighth of an expert's tiles of the expert's first or last
+            // tile moves to that boundary: with even fills every XCD then keeps whole
+            // experts (their operands shared in its L2), as an equal count would
+            const int snap = u * 8 <= per_e ? 0 : ((per_e - u) * 8 <= per_e ? per_e : u);
+            return __builtin_amdgcn_readfirstlane((e0 + l) * per_e + snap);
+        }
+        base += __shfl(inc, 63, 64);
+    }
+    return E * per_e;  // t at or past the total work
+}
+
+// Total work of the weight-gradient tile list (units as kgrad_cut), in every lane.
+__device__ __forceinline__ int64_t kgrad_work(const int32_t *fill, int E, int per_e, int KB) {
+    const int lane = threadIdx.x & 63;
+    int64_t total = 0;
+    for (int e0 = 0; e0 < E; e0 += 64) {
+        const int e = e0 + lane;
+        int64_t v = e < E ? static_cast<int64_t>((fill[e] + KB - 1) / KB + 1) * per_e : 0;
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+        total += v;
+    }
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(total));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(total >> 32));
+    return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
 template <int BM, int BN, int NTH>
 __global__ __launch_bounds__(NTH, (4 * (BM + BN) * kBigKB * 2 <= 160 * 1024 ? 2 : 1)) void kgrad_gemm_big(const bf16_t *__restrict__ X, const bf16_t *__restrict__ Y,
                                                        float *__restrict__ D, int P, int Q, int E,
@@ -1208,10 +1261,11 @@ __global__ __launch_bounds__(NTH, (4 * (BM + BN) * kBigKB * 2 <= 160 * 1024 ? 2 
     constexpr int STAGE = (BM + BN) * KB;
     const int tp = (P + BM - 1) / BM, tq = (Q + BN - 1) / BN;
     const int per_e = tp * tq;
-    const int T = E * per_e;
     const int x = blockIdx.x % kXcds, nb = gridDim.x / kXcds;
-    const int per = (T + kXcds - 1) / kXcds;
-    const int start = min(T, x * per), end = min(T, start + per);
+    // XCD x takes the tiles of the x-th eighth of the work (see kgrad_cut)
+    const int64_t work = kgrad_work(fill, E, per_e, KB);
+    const int start = kgrad_cut(fill, E, per_e, KB, work * x / kXcds);
+    const int end = kgrad_cut(fill, E, per_e, KB, work * (x + 1) / kXcds);
     const int C = *cap;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wr0 = (wave / WGC) * (BM / 2), wc0 = (wave % WGC) * (BN / WGC);
