@@ -228,12 +228,18 @@ __global__ __launch_bounds__(kThreads) void gather_sum_kernel(const uint4 *__res
     for (int64_t s = global_wave(); s < S; s += nw) {
         float g;
         const int slot = lane_slot(idx, loc, UNIT ? nullptr : gates, s, S, k, C, lane, g);
-        for (int v = lane; v < V; v += kWave) {
-            float acc[N];
+        // two vectors per lane at a time (v and v + 64): the loads of every route
+        // for both are in flight together; each output still sums its routes in
+        // route order
+        for (int v = lane; v < V; v += 2 * kWave) {
+            const bool two = v + kWave < V;
+            float acc[2][N];
 #pragma unroll
-            for (int i = 0; i < N; ++i) acc[i] = 0.f;
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int i = 0; i < N; ++i) acc[h][i] = 0.f;
             for (int r0 = 0; r0 < k; r0 += RB) {
-                uint4 val[RB];
+                uint4 val[2][RB];
                 float gr[RB];
                 int sls[RB];
 #pragma unroll
@@ -241,25 +247,38 @@ __global__ __launch_bounds__(kThreads) void gather_sum_kernel(const uint4 *__res
                     const int r = r0 + u;
                     sls[u] = r < k ? wave_read(slot, r) : -1;
                     gr[u] = (UNIT || sls[u] < 0) ? 0.f : wave_read(g, r);
-                    val[u] = make_uint4(0u, 0u, 0u, 0u);
-                    if (sls[u] >= 0) val[u] = rows[static_cast<int64_t>(sls[u]) * V + v];
+                    val[0][u] = make_uint4(0u, 0u, 0u, 0u);
+                    val[1][u] = make_uint4(0u, 0u, 0u, 0u);
+                    if (sls[u] >= 0) {
+                        const uint4 *row = rows + static_cast<int64_t>(sls[u]) * V;
+                        val[0][u] = row[v];
+                        if (two) val[1][u] = row[v + kWave];
+                    }
                 }
 #pragma unroll
                 for (int u = 0; u < RB; ++u) {
                     if (sls[u] < 0) continue;
-                    float f[N];
-                    VT::unpack(val[u], f);
 #pragma unroll
-                    for (int i = 0; i < N; ++i) acc[i] = UNIT ? acc[i] + f[i] : acc[i] + gr[u] * f[i];
+                    for (int h = 0; h < 2; ++h) {
+                        float f[N];
+                        VT::unpack(val[h][u], f);
+#pragma unroll
+                        for (int i = 0; i < N; ++i) acc[h][i] = UNIT ? acc[h][i] + f[i] : acc[h][i] + gr[u] * f[i];
+                    }
                 }
             }
-            if constexpr (RES) {
-                float f[N];
-                VT::unpack(yres[s * V + v], f);
 #pragma unroll
-                for (int i = 0; i < N; ++i) acc[i] = acc[i] + f[i];
+            for (int h = 0; h < 2; ++h) {
+                if (h == 1 && !two) break;
+                const int vv = v + h * kWave;
+                if constexpr (RES) {
+                    float f[N];
+                    VT::unpack(yres[s * V + vv], f);
+#pragma unroll
+                    for (int i = 0; i < N; ++i) acc[h][i] = acc[h][i] + f[i];
+                }
+                out[s * V + vv] = VT::pack(acc[h]);
             }
-            out[s * V + v] = VT::pack(acc);
         }
     }
 }
