@@ -68,24 +68,20 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const uint4 *__restric
         float g_unused;
         const int slot = lane_slot(idx, loc, nullptr, s, S, k, C, lane, g_unused);
         const uint4 *src = x + s * V;
-        int v = lane;
-        for (; v + 3 * kWave < V; v += 4 * kWave) {
+        // four vectors per lane at a time, the last batch masked: all loads of a
+        // batch are in flight before its stores
+        for (int v = lane; v < V; v += 4 * kWave) {
             uint4 a[4];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) a[u] = src[v + u * kWave];
+            for (int u = 0; u < 4; ++u)
+                a[u] = v + u * kWave < V ? src[v + u * kWave] : make_uint4(0u, 0u, 0u, 0u);
             for (int r = 0; r < k; ++r) {
                 const int sl = wave_read(slot, r);
                 if (sl < 0) continue;
                 uint4 *dst = buf + static_cast<int64_t>(sl) * V + v;
 #pragma unroll
-                for (int u = 0; u < 4; ++u) dst[u * kWave] = a[u];
-            }
-        }
-        for (; v < V; v += kWave) {
-            const uint4 a = src[v];
-            for (int r = 0; r < k; ++r) {
-                const int sl = wave_read(slot, r);
-                if (sl >= 0) buf[static_cast<int64_t>(sl) * V + v] = a;
+                for (int u = 0; u < 4; ++u)
+                    if (v + u * kWave < V) dst[u * kWave] = a[u];
             }
         }
     }
@@ -139,24 +135,20 @@ __global__ __launch_bounds__(kThreads) void assign_encode_kernel(
             if (lane == r) slot = l < C ? e * C + l : -1;
         }
         const uint4 *src = x + s * V;
-        int v = lane;
-        for (; v + 3 * kWave < V; v += 4 * kWave) {
+        // four vectors per lane at a time, the last batch masked: all loads of a
+        // batch are in flight before its stores
+        for (int v = lane; v < V; v += 4 * kWave) {
             uint4 a[4];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) a[u] = src[v + u * kWave];
+            for (int u = 0; u < 4; ++u)
+                a[u] = v + u * kWave < V ? src[v + u * kWave] : make_uint4(0u, 0u, 0u, 0u);
             for (int r = 0; r < k; ++r) {
                 const int sl = wave_read(slot, r);
                 if (sl < 0) continue;
                 uint4 *dst = buf + static_cast<int64_t>(sl) * V + v;
 #pragma unroll
-                for (int u = 0; u < 4; ++u) dst[u * kWave] = a[u];
-            }
-        }
-        for (; v < V; v += kWave) {
-            const uint4 a = src[v];
-            for (int r = 0; r < k; ++r) {
-                const int sl = wave_read(slot, r);
-                if (sl >= 0) buf[static_cast<int64_t>(sl) * V + v] = a;
+                for (int u = 0; u < 4; ++u)
+                    if (v + u * kWave < V) dst[u * kWave] = a[u];
             }
         }
     }
