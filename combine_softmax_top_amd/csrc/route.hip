@@ -57,21 +57,29 @@ __device__ __forceinline__ double group_sum_f64(double v) {
     return v;
 }
 
-// Phase 1. Block = 256 threads, one 64-token tile; G lanes per token, EPL
-// experts per lane (expert e = lane_in_group + G * j). counts is [E][k][nblk].
+// Phase 1. Block = one 64-token tile, NT = 64 * G threads up to 1024 (every token's
+// group at once when G <= 16); G lanes per token, EPL experts per lane (expert
+// e = lane_in_group + G * j). counts is [E][k][nblk].
+template <int G>
+constexpr int topk_threads() {
+    return kRouteTile * G < 256 ? 256 : (kRouteTile * G > 1024 ? 1024 : kRouteTile * G);
+}
+
 template <int G, int EPL>
-__global__ __launch_bounds__(256) void route_topk_kernel(const float *__restrict__ logits, int S, int E,
-                                                         int k, int nblk, int32_t *__restrict__ idx,
-                                                         float *__restrict__ gates,
-                                                         int32_t *__restrict__ counts) {
+__global__ __launch_bounds__(topk_threads<G>()) void route_topk_kernel(const float *__restrict__ logits, int S,
+                                                                       int E, int k, int nblk,
+                                                                       int32_t *__restrict__ idx,
+                                                                       float *__restrict__ gates,
+                                                                       int32_t *__restrict__ counts) {
+    constexpr int NT = topk_threads<G>();
     extern __shared__ int32_t tile_count[];  // [k][E]
     const int tid = threadIdx.x;
     const int tile = blockIdx.x;
-    for (int i = tid; i < k * E; i += 256) tile_count[i] = 0;
+    for (int i = tid; i < k * E; i += NT) tile_count[i] = 0;
     __syncthreads();
 
     const int gl = tid % G;
-    constexpr int groups = 256 / G;
+    constexpr int groups = NT / G;
     for (int t = tid / G; t < kRouteTile; t += groups) {
         const int s = tile * kRouteTile + t;
         if (s >= S) break;  // uniform across the G lanes of a group
@@ -115,7 +123,7 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float *__restrict
         }
     }
     __syncthreads();
-    for (int i = tid; i < k * E; i += 256) {
+    for (int i = tid; i < k * E; i += NT) {
         const int r = i / E, e = i - r * E;
         counts[(static_cast<int64_t>(e) * k + r) * nblk + tile] = tile_count[i];
     }
@@ -202,8 +210,8 @@ template <int G, int EPL>
 static hipError_t launch_topk(const float *logits, int S, int E, int k, int nblk, int32_t *idx, float *gates,
                               int32_t *counts, hipStream_t st) {
     const size_t lds = sizeof(int32_t) * static_cast<size_t>(k) * E;
-    hipLaunchKernelGGL((route_topk_kernel<G, EPL>), dim3(nblk), dim3(256), lds, st, logits, S, E, k, nblk, idx,
-                       gates, counts);
+    hipLaunchKernelGGL((route_topk_kernel<G, EPL>), dim3(nblk), dim3(topk_threads<G>()), lds, st, logits, S, E, k,
+                       nblk, idx, gates, counts);
     return hipGetLastError();
 }
 
