@@ -218,7 +218,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU's share of the layer: --gpus {args.gpus} is not supported "
-              "(this build has no multi-GPU path; run with --gpus 1)", file=sys.stderr)
+              "(the layer here runs on one GPU, with no collectives; run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
