@@ -108,12 +108,11 @@ moe_status moe_capacity_bound(const moe_shape *shape, int32_t *cmax_host);
 moe_status moe_workspace_size(const moe_shape *shape, size_t *bytes_host);
 
 /* Gate projection (Tutel catalogue page, "key configuration": the top-k gate
- * scores each token against E experts): logits[s][e] = fp32(sum_m x[s][m] *
- * Wg[m][e]). The products are exact in fp64 and are summed in fp64 in a fixed
- * order, so the logits (on which routing decisions are taken) are reproducible
- * bit for bit: m is cut into chunks of 64 * ceil(M / 4096), each chunk summed in
- * increasing m, the chunk sums combined pairwise level by level (neighbours
- * added, an unpaired last one carried up), the result rounded once to fp32.
+ * scores each token against E experts): logits[s][e] = sum_m x[s][m] * Wg[m][e]
+ * in fp32, within the fp32 summation bound of the exact sum (gamma_M *
+ * sum_m |x[s][m] Wg[m][e]|, gamma_n = n 2^-24 / (1 - n 2^-24)). The summation
+ * order is fixed, so the logits (on which routing decisions are taken) are
+ * reproducible bit for bit from run to run; routing itself is exact given them.
  * x [S, M] data type, Wg [M, E] fp32 row-major, logits [S, E] fp32.
  * Supported for M <= 12288 with bf16 x and M <= 7680 with fp32 x (the LDS tiles
  * must fit; MOE_EUNSUPPORTED otherwise, also from moe_layer_forward with Wg). */
@@ -346,9 +345,10 @@ moe_status moe_layer_forward_pipelined(const moe_shape *shape, const void *x, co
  * [S, M] (blog part 3 section 3.5: K1 is combine-backward, K2 the cross term,
  * K0 encode-backward), given the forward's saved tensors (buf, pre, h, y and
  * the route tables):
- *   dy[slot]     = gates[r][s] * dout[s]            (rows of kept routes only)
+ *   dy[slot]     = gates[r][s] * dout[s] in fp32, stored (rows of kept routes only)
  *   dgates[r][s] = <dout[s], y[slot]> in fp32, 0 for dropped routes
- *   dpre = (dy . W2[e]) * act'(pre), stored;   dbuf = dpre . W1[e], stored
+ *   dpre = (dy . W2[e]) * act'(pre), stored, with pre the forward's stored
+ *          pre-activation (in the data type);   dbuf = dpre . W1[e], stored
  *   dW2[e] = sum_j dy_j^T h_j, db2[e] = sum_j dy_j,
  *   dW1[e] = sum_j dpre_j^T buf_j, db1[e] = sum_j dpre_j   (fp32, over j < fill[e])
  *   dx[s] = sum over kept routes of dbuf[slot] (fp32 accumulation), stored;

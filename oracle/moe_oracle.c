@@ -52,10 +52,13 @@
  *    type like an expert's, and decode adds y_r[s] in fp32 after the routes;
  *    the MoE branch is gate-weighted as usual (the pages say only that the two
  *    outputs are added);
- *  - backward: dy = g * dout (rounded to the data type), dgate = <dout, y>,
- *    dh = dy . W2[e], dpre = dh * act'(pre) rounded, dbuf = dpre . W1[e]
- *    rounded, dx = sum of dbuf over kept routes rounded; weight and bias
- *    gradients are fp32 sums over the expert's filled rows;
+ *  - backward: dy = g * dout computed in fp32 (the product rounded to fp32)
+ *    and then rounded to the data type, dgate = <dout, y>, dh = dy . W2[e],
+ *    dpre = dh * act'(pre) rounded, where pre is the pre-activation as the
+ *    forward stored it (rounded to the data type: the value a training step
+ *    keeps for its backward), dbuf = dpre . W1[e] rounded, dx = sum of dbuf
+ *    over kept routes rounded; weight and bias gradients are fp32 sums over
+ *    the expert's filled rows;
  *  - gate backward: the gates are softmax probabilities p of the logits, so
  *    the gradient reaching p is dgates at each route's expert (all k routes as
  *    given; the layer passes 0 for dropped ones) plus the gradient of an
@@ -129,6 +132,10 @@ static double round_to_dtype(double v, int dtype) {
     return bf16_value(f64_to_bf16(v));
 }
 
+/* The product of an fp32 gate and a data-type value as fp32 arithmetic gives it:
+ * the exact product (it fits in fp64) rounded once to fp32. */
+static double fp32_product(float g, double v) { return (double)(float)((double)g * v); }
+
 static double act_f(int act, double v) {
     if (act == ACT_RELU) return v > 0.0 ? v : 0.0;
     return 0.5 * v * (1.0 + erf(v / sqrt(2.0)));
@@ -156,35 +163,19 @@ double oracle_act_grad(int act, double v) { return act_grad(act, v); }
 
 /* ------------------------------------------------------------------ gating */
 
-/* Gate projection: logit[s][e] = fp32( sum_m x[s][m] * Wg[m][e] ). x is [S,M]
- * in the data type, Wg is [M,E] fp32; every product is exact in fp64. The pages
- * leave the summation order open; the reading taken here: m is cut into
- * consecutive chunks of L = 64 * ceil(M / 4096) (so there are at most 64; the
- * last may be shorter), each chunk is summed in fp64 from 0 in increasing m,
- * and the chunk sums are combined level by level, neighbours 2i and 2i+1
- * added (left + right), an unpaired last sum carried up unchanged; the root
- * is rounded once to fp32. */
-enum { GATE_MAX_CHUNKS = 64 };
-static int32_t gate_chunk_len(int32_t M) { return 64 * ((M + 4095) / 4096); }
-
+/* Gate projection: logit[s][e] = fp32( sum_m x[s][m] * Wg[m][e] ), the plain
+ * definition of the product of x (data type, [S,M]) and the fp32 gate matrix
+ * Wg [M,E] (Tutel catalogue page, key configuration: the gate scores each token
+ * against the E experts). Every product is exact in fp64; the sum runs in fp64
+ * from 0 in increasing m and is rounded once to fp32. */
 void oracle_gate_logits(int32_t S, int32_t M, int32_t E, int dtype, const void *x,
                         const float *Wg, float *logits) {
-    const int32_t L = gate_chunk_len(M);
-    const int32_t n = (M + L - 1) / L;
     for (int64_t s = 0; s < S; ++s)
         for (int32_t e = 0; e < E; ++e) {
-            double part[GATE_MAX_CHUNKS];
-            for (int32_t c = 0; c < n; ++c) {
-                double acc = 0.0;
-                for (int32_t m = c * L; m < M && m < (c + 1) * L; ++m)
-                    acc += load_elem(x, dtype, s * M + m) * (double)Wg[(int64_t)m * E + e];
-                part[c] = acc;
-            }
-            for (int32_t cnt = n; cnt > 1; cnt = (cnt + 1) / 2) {
-                for (int32_t i = 0; i < cnt / 2; ++i) part[i] = part[2 * i] + part[2 * i + 1];
-                if (cnt % 2) part[cnt / 2] = part[cnt - 1];
-            }
-            logits[s * E + e] = (float)part[0];
+            double acc = 0.0;
+            for (int32_t m = 0; m < M; ++m)
+                acc += load_elem(x, dtype, s * M + m) * (double)Wg[(int64_t)m * E + e];
+            logits[s * E + e] = (float)acc;
         }
 }
 
@@ -378,9 +369,10 @@ void oracle_decode(int32_t S, int32_t M, int32_t E, int32_t k, int32_t C, int dt
 /* ---------------------------------------------------------------- backward */
 
 /* Backward of one kept buffer row `row` = e*C + j that holds route q = r*S+s:
- *   dy[m]   = gates[q] * dout[s][m], rounded to the data type
+ *   dy[m]   = gates[q] * dout[s][m] rounded to fp32, then to the data type
  *   dh[h]   = sum_m dy[m] * W2[e][m][h]                      (fp64)
- *   dpre[h] = dh[h] * act'(pre_exact[h]), rounded
+ *   dpre[h] = dh[h] * act'(pre[h]), rounded, with pre[h] the stored
+ *             (rounded) pre-activation
  *   dbuf[m] = sum_h dpre[h] * W1[e][h][m], rounded
  * Outputs (compact, rows in the data type) may each be NULL. */
 void oracle_backward_rows(int32_t S, int32_t M, int32_t H, int32_t E, int32_t C, int dtype,
@@ -406,14 +398,14 @@ void oracle_backward_rows(int32_t S, int32_t M, int32_t H, int32_t E, int32_t C,
                 pre[h] = acc;
             }
             for (int32_t m = 0; m < M; ++m) {
-                dy[m] = round_to_dtype((double)gates[q] * load_elem(dout, dtype, s * M + m), dtype);
+                dy[m] = round_to_dtype(fp32_product(gates[q], load_elem(dout, dtype, s * M + m)), dtype);
                 if (dy_out) store_elem(dy_out, dtype, i * M + m, dy[m]);
             }
             for (int32_t h = 0; h < H; ++h) {
                 double acc = 0.0;
                 for (int32_t m = 0; m < M; ++m)
                     acc += dy[m] * load_elem(W2, dtype, (e * M + m) * H + h);
-                dpre[h] = round_to_dtype(acc * act_grad(act, pre[h]), dtype);
+                dpre[h] = round_to_dtype(acc * act_grad(act, round_to_dtype(pre[h], dtype)), dtype);
                 if (dpre_out) store_elem(dpre_out, dtype, i * H + h, dpre[h]);
             }
             if (dbuf_out)
@@ -431,8 +423,8 @@ void oracle_backward_rows(int32_t S, int32_t M, int32_t H, int32_t E, int32_t C,
 /* The same backward quantities for selected hidden columns only, for sampling
  * the weight gradients of large layers. For each listed kept row (rows[i] =
  * e*C + j holding route routes[i]) and each hidden column hcols[c]:
- *   hv[i][c]   = act(pre) rounded,  dpre[i][c] = (dy . W2[e][:, h]) * act'(pre) rounded,
- * and the full dy row dy[i][:] = gates * dout[s] rounded. Every element follows
+ *   hv[i][c]   = act(pre) rounded,  dpre[i][c] = (dy . W2[e][:, h]) * act'(stored pre) rounded,
+ * and the full dy row dy[i][:] = gates * dout[s] (fp32, then rounded). Every element follows
  * the same definitions as ffn_row / oracle_backward_rows. */
 void oracle_backward_cols(int32_t S, int32_t M, int32_t H, int32_t C, int dtype, int act, const void *buf,
                           const void *W1, const void *b1, const void *W2, const float *gates,
@@ -446,7 +438,7 @@ void oracle_backward_cols(int32_t S, int32_t M, int32_t H, int32_t C, int dtype,
             const int64_t row = rows[i], e = row / C;
             const int64_t q = routes[i], s = q % S;
             for (int32_t m = 0; m < M; ++m) {
-                dy[m] = round_to_dtype((double)gates[q] * load_elem(dout, dtype, s * M + m), dtype);
+                dy[m] = round_to_dtype(fp32_product(gates[q], load_elem(dout, dtype, s * M + m)), dtype);
                 store_elem(dy_out, dtype, i * M + m, dy[m]);
             }
             for (int32_t c = 0; c < ncols; ++c) {
@@ -458,7 +450,7 @@ void oracle_backward_cols(int32_t S, int32_t M, int32_t H, int32_t C, int dtype,
                 store_elem(hv_out, dtype, i * ncols + c, act_f(act, pre));
                 double dh = 0.0;
                 for (int32_t m = 0; m < M; ++m) dh += dy[m] * load_elem(W2, dtype, (e * M + m) * H + h);
-                store_elem(dpre_out, dtype, i * ncols + c, dh * act_grad(act, pre));
+                store_elem(dpre_out, dtype, i * ncols + c, dh * act_grad(act, round_to_dtype(pre, dtype)));
             }
         }
         free(dy);

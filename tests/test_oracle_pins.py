@@ -64,18 +64,14 @@ def _gate_case(x_vals, w_vals):
     return x, Wg
 
 
-def test_gate_logits_summation_order_is_chunked_tree():
-    # Reading of the unspecified summation order: chunks of 64 products summed
-    # in order in fp64, chunk sums combined pairwise (left + right, an odd one
-    # carried up). Products: +2^30 at m = 0, 2^-23 at m = 64..126 (63 terms),
-    # -2^30 at m = 128; all others 0. Chunk sums: 2^30, 63 * 2^-23 (exact),
-    # -2^30.
-    #   chunked tree ((c0 + c1) + c2): 63 * 2^-23 is 31.5 ulps of 2^30 (ulp
-    #     2^-22), a tie rounded to even: 2^30 + 2^-17; minus 2^30 gives 2^-17.
-    #   one sequential sum: each 2^-23 is half an ulp of 2^30 and rounds away
-    #     (to even), giving 0; chunks of 128 behave the same.
-    #   right-leaning tree (c0 + (c1 + c2)): 2^30 - 63 * 2^-23 is exact (ulp
-    #     2^-23 below 2^30), giving 63 * 2^-23.
+def test_gate_logits_sum_in_increasing_m():
+    # The plain definition: one fp64 sum over m from 0 upward, rounded once. The
+    # products are +2^30 at m = 0, 2^-23 at m = 64..126 (63 terms) and -2^30 at
+    # m = 128, all others 0; the exact sum is 63 * 2^-23. Summed upward, each
+    # 2^-23 is half an fp64 ulp of 2^30 and rounds away (ties to even), giving 0.
+    # Other orders give other values: downward, -2^30 + 63 * 2^-23 is exact
+    # (ulp 2^-23 just below 2^30 in magnitude), giving 63 * 2^-23; chunks of 64
+    # combined pairwise give 2^-17.
     M = 192
     xv = np.zeros(M, np.float32)
     wv = np.zeros(M, np.float32)
@@ -83,14 +79,17 @@ def test_gate_logits_summation_order_is_chunked_tree():
     xv[64:127], wv[64:127] = 2.0 ** -8, 2.0 ** -15
     xv[128], wv[128] = -(2.0 ** 15), 2.0 ** 15
     x, Wg = _gate_case(xv, wv)
-    got = oracle.gate_logits(x, Wg, W.DT_BF16)[0, 0]
-    assert got == np.float32(2.0 ** -17)
+    assert oracle.gate_logits(x, Wg, W.DT_BF16)[0, 0] == np.float32(0.0)
+    # the same terms with the two large ones swapped in position sum to the exact value
+    xv[0], xv[128] = -xv[0], -xv[128]
+    x, Wg = _gate_case(xv, wv)
+    assert oracle.gate_logits(x, Wg, W.DT_BF16)[0, 0] == np.float32(63 * 2.0 ** -23)
 
 
 def test_gate_logits_one_hot_weights_select_inputs():
     # Wg[m][e] = 1 iff m == e: every logit is one input element, whatever the order.
     rng = np.random.default_rng(7)
-    S, M, E = 6, 4160, 5  # M > 4096: chunks of 128, 33 of them, the last one short
+    S, M, E = 6, 4160, 5
     x = bf16_bits_of_f32(rng.standard_normal((S, M)).astype(np.float32))
     Wg = np.zeros((M, E), np.float32)
     for e in range(E):
@@ -100,7 +99,7 @@ def test_gate_logits_one_hot_weights_select_inputs():
 
 
 def test_gate_logits_within_error_bound_of_exact_sum():
-    # The fp64 tree sum differs from the exact sum by far less than half an fp32
+    # The fp64 sum differs from the exact sum by far less than half an fp32
     # ulp of typical logits, so the fp32 result is the exact sum rounded, except
     # (rarely) next to a rounding boundary: allow one fp32 ulp.
     import math
@@ -419,6 +418,156 @@ def test_backward_matches_autograd_of_dense_layer(act, k, f):
         assert np.abs(got - ref).max() / scale < 2e-6, n
     # dropped routes get no gate gradient
     assert (bw["dgates"][rt["loc"] >= rt["C"]] == 0).all()
+
+
+def _bf16_rne_f64(t: torch.Tensor) -> torch.Tensor:
+    """fp64 values rounded once to bf16 (to nearest, ties to even), as fp64: the 52-bit
+    significand is rounded at its 7th bit by integer arithmetic on the bit pattern
+    (values inside the bf16 normal range, and zero)."""
+    a = t.detach().contiguous().numpy().copy()
+    u = a.view(np.int64)
+    sign = u & np.int64(-0x8000000000000000)
+    mag = u & np.int64(0x7FFFFFFFFFFFFFFF)
+    lsb = (mag >> 45) & 1
+    mag = (mag + (np.int64(1) << 44) - 1 + lsb) & ~((np.int64(1) << 45) - 1)
+    return torch.from_numpy((sign | mag).view(np.float64).copy())
+
+
+class _RoundGradBF16(torch.autograd.Function):
+    """Identity forward; the gradient passing back is rounded to bf16 (a bf16 store)."""
+    @staticmethod
+    def forward(ctx, t):
+        return t.clone()
+
+    @staticmethod
+    def backward(ctx, g):
+        return _bf16_rne_f64(g)
+
+
+class _RoundGradF32BF16(torch.autograd.Function):
+    """Identity forward; the gradient passing back is rounded to fp32, then to bf16."""
+    @staticmethod
+    def forward(ctx, t):
+        return t.clone()
+
+    @staticmethod
+    def backward(ctx, g):
+        return _bf16_rne_f64(g.float().double())
+
+
+class _StoreBF16(torch.autograd.Function):
+    """Forward rounds to bf16 (a stored activation); the gradient passes unchanged."""
+    @staticmethod
+    def forward(ctx, t):
+        return _bf16_rne_f64(t)
+
+    @staticmethod
+    def backward(ctx, g):
+        return g
+
+
+class _ActAtStoredPre(torch.autograd.Function):
+    """act(pre) on the unrounded pre-activation; its derivative taken by torch at the
+    pre-activation as stored in bf16."""
+    @staticmethod
+    def forward(ctx, pre, act):
+        ctx.act = act
+        ctx.save_for_backward(_bf16_rne_f64(pre))
+        return torch.nn.functional.gelu(pre) if act == W.ACT_GELU else torch.relu(pre)
+
+    @staticmethod
+    def backward(ctx, g):
+        (ps,) = ctx.saved_tensors
+        with torch.enable_grad():
+            p = ps.clone().requires_grad_(True)
+            a = torch.nn.functional.gelu(p) if ctx.act == W.ACT_GELU else torch.relu(p)
+            (d,) = torch.autograd.grad(a, p, g)
+        return d, None
+
+
+@pytest.mark.parametrize("act,k,f", [(W.ACT_GELU, 2, 0.0), (W.ACT_GELU, 3, -0.75), (W.ACT_RELU, 2, 0.5)])
+def test_bf16_backward_rounding_points_match_autograd(act, k, f):
+    # fp64 autograd of the dense one-hot layer with bf16 stores inserted where the
+    # layer stores bf16: the forward's h and y (values), the pre-activation the
+    # backward reads, and the gradients dy (an fp32 product, then bf16), dpre and
+    # dbuf; dx is the fp64 sum of a token's dbuf rows rounded once. The oracle's
+    # dy, dpre and dbuf must equal these bit for bit, dx too, and its fp32 weight
+    # and bias gradients must be the fp64 sums rounded to fp32 (within one fp32
+    # ulp: only the fp64 summation order differs). A missing or doubled rounding
+    # at any of these points, or act' taken at the unrounded pre, changes a
+    # share of the bf16 values or the weight gradients by ~2^-9 relative.
+    S, M, E, H = 24, 16, 3, 24
+    w = W.Workload("bf16bwd", S=S, M=M, E=E, k=k, H=H, capacity_factor=f, act=act, backward=True)
+    inp = {n: np_of(v) for n, v in W.make_inputs(w, seed=5).items()}
+    # larger weights than the workloads' 0.02, so that pre-activations spread over GELU's curve
+    for n in ("W1", "W2", "b1", "b2"):
+        inp[n] = bf16_bits_of_f32(f32_of(inp[n]) * 15.0)
+    fw = oracle.layer_forward(inp, k, f, act, W.DT_BF16)
+    bw = oracle.layer_backward(fw, inp, act, W.DT_BF16)
+    rt = fw["route"]
+    C = rt["C"]
+    t = {n: torch.from_numpy(f32_of(v).astype(np.float64)) for n, v in inp.items()}
+    for n in ("x", "W1", "b1", "W2", "b2"):
+        t[n].requires_grad_(True)
+    mask = torch.from_numpy(onehot_mask(rt["idx"], rt["loc"], E, C)).double()
+    gates = torch.from_numpy(rt["gates"].astype(np.float64))
+    buf = torch.einsum("sec,sm->ecm", mask.sum(0), t["x"])
+    buf.retain_grad()
+    pre = torch.bmm(_RoundGradBF16.apply(buf), t["W1"].transpose(1, 2).contiguous()) + t["b1"][:, None, :]
+    pre.retain_grad()
+    h = _StoreBF16.apply(_ActAtStoredPre.apply(_RoundGradBF16.apply(pre), act))
+    y = _StoreBF16.apply(torch.bmm(h, t["W2"].transpose(1, 2).contiguous()) + t["b2"][:, None, :])
+    y.retain_grad()
+    yr = _RoundGradF32BF16.apply(y)
+    out = torch.zeros(S, M, dtype=torch.float64)
+    for r in range(k):
+        out = out + torch.einsum("sec,ecm->sm", gates[r][:, None, None] * mask[r], yr)
+    (out * t["dout"]).sum().backward()
+    rows = fw["rows"]
+    assert len(rows) > 20
+    # the oracle's [E*C] row numbering is the dense [E, C] flattening
+    flat = lambda g, n: g.reshape(E * C, n)[torch.from_numpy(rows)]  # noqa: E731
+    for name, want, got in (("dy", flat(y.grad, M), bw["dy"]), ("dpre", flat(pre.grad, H), bw["dpre"]),
+                            ("dbuf", flat(buf.grad, M), bw["dbuf"])):
+        assert np.array_equal(f32_of(got).astype(np.float64), want.numpy()), name
+    assert np.array_equal(f32_of(bw["dx"]).astype(np.float64), _bf16_rne_f64(t["x"].grad).numpy()), "dx"
+    for name, ref in (("dW1", t["W1"].grad), ("db1", t["b1"].grad), ("dW2", t["W2"].grad), ("db2", t["b2"].grad)):
+        ref32 = ref.numpy().astype(np.float32)
+        d = np.abs(bw[name].view(np.int32).astype(np.int64) - ref32.view(np.int32).astype(np.int64))
+        assert d.max() <= 1, (name, int(d.max()))
+
+
+def test_dy_is_the_fp32_product_rounded_to_bf16():
+    # dy = gate * dout is fp32 arithmetic whose result is stored in bf16: two roundings.
+    # Constructed case where they differ from one rounding of the exact product: the
+    # gate g (fp32) and dout d = 1 + 2^-7 (bf16) give g d just above the bf16 midpoint
+    # 1 + 2^-8 by less than half an fp32 ulp; fp32 rounds it onto the midpoint, which
+    # then goes to the even neighbour 1, where one rounding would give 1 + 2^-7.
+    from fractions import Fraction
+    d = 1.0 + 2.0 ** -7
+    g0 = np.float32((1.0 + 2.0 ** -8) / d)
+    g = None
+    for step in range(-8, 9):
+        c = np.nextafter(g0, np.float32(2.0 if step > 0 else 0.0), dtype=np.float32) if step else g0
+        for _ in range(abs(step) - 1):
+            c = np.nextafter(c, np.float32(2.0 if step > 0 else 0.0), dtype=np.float32)
+        p = Fraction(float(c)) * Fraction(d)
+        if np.float32(float(p)) == np.float32(1.0 + 2.0 ** -8) and p > Fraction(1) + Fraction(1, 256):
+            g = c
+            break
+    assert g is not None
+    S, M, E, H = 4, 8, 2, 8
+    w = W.Workload("dy", S=S, M=M, E=E, k=1, H=H, capacity_factor=0.0, backward=True)
+    inp = {n: np_of(v) for n, v in W.make_inputs(w, seed=1).items()}
+    dout = f32_of(inp["dout"]).copy()
+    dout[:, 0] = d
+    inp["dout"] = bf16_bits_of_f32(dout)
+    fw = oracle.layer_forward(inp, 1, 0.0, w.act, W.DT_BF16)
+    fw["route"]["gates"][:] = g
+    routes, dy, _, _ = oracle.backward_rows(fw, inp, fw["rows"], w.act, W.DT_BF16, want_dpre=False,
+                                            want_dbuf=False)
+    assert len(routes) == S
+    assert (f32_of(dy[:, 0]) == 1.0).all(), f32_of(dy[:, 0])
 
 
 def test_encode_decode_adjoint_identities():
