@@ -3,12 +3,13 @@ torch device tensors (HIP side), running the library's entry points, and the
 tolerance rules.
 
 Tolerances: routing indices, locations, needed, fill, C, slot map and the
-encode buffer are compared bit for bit; gates within one fp32 ulp (both sides
-compute the softmax in fp64 and round once; only the fp64 summation order
-differs); decode given the same expert output bit for bit. Everything
+encode buffer are compared bit for bit, given the same fp32 logits; gate
+logits within an fp32 summation bound (check_logits); gates within one fp32 ulp
+(both sides compute the softmax in fp64 and round once; only the fp64 summation
+order differs); decode given the same expert output bit for bit. Everything
 downstream of a GEMM is compared in fp32 with max |got - want| <= 1e-4 for fp32
-data, or max |got - want| <= 2e-2 RMS(want) for bf16 data, where each bf16
-element may also differ by one bf16 ulp of its value (see check_close).
+data, or max |got - want| <= 2e-2 RMS(want) for bf16 data; a result stored in
+bf16 may exceed that only by being the adjacent bf16 value (see check_close).
 """
 from __future__ import annotations
 
@@ -41,20 +42,27 @@ def inputs_np(inp: Dict[str, torch.Tensor]) -> Dict[str, np.ndarray]:
     return {k: np_of(v) for k, v in inp.items()}
 
 
-def check_close(got: np.ndarray, want: np.ndarray, dtype: int, what: str, mag: np.ndarray = None,
-                extra: np.ndarray = None) -> float:
-    """The tolerance rule; returns the largest error / bound ratio (<= 1 passes).
+def _bf16_key(a: np.ndarray) -> np.ndarray:
+    """Ordered integer key of bf16 bit patterns: adjacent values differ by 1 (+0 and -0 are both 0)."""
+    a = a.astype(np.int64)
+    return np.where(a & 0x8000, -(a & 0x7FFF), a)
+
+
+def check_close(got: np.ndarray, want: np.ndarray, dtype: int, what: str, extra: np.ndarray = None) -> float:
+    """The tolerance rule; returns the largest error / bound ratio over the elements held to
+    the bound (<= 1 passes).
 
     fp32 data: max |got - want| <= 1e-4.
-    bf16 data: |got - want| <= 2e-2 RMS(want) + 2^-7 mag elementwise, where mag
-    defaults to |want|. The first term is the max-abs-versus-RMS rule; the second
-    is one bf16 ulp of the element (an ulp is at most 2^-7 of the value): both
-    sides round their own fp32/fp64 result to bf16, and whenever the two
-    unrounded values straddle a rounding boundary the stored values differ by
-    one ulp, which at values several times the RMS exceeds 2e-2 RMS by itself.
-    Sums of separately rounded bf16 terms (dx) pass mag = |want| + sum |term|.
-    extra (elementwise, either dtype) widens the bound by the propagated effect of
-    an upstream input that the two sides computed within tolerance of each other.
+    bf16 data: max |got - want| <= 2e-2 RMS(want), every element. For results stored in
+    bf16 (got and want both bf16 bit patterns) an element may exceed that only if got and
+    want are adjacent bf16 values: the two sides round different unrounded values (their
+    summation orders differ) and a rounding boundary lay between them. Those elements are
+    counted and printed. Results stored in fp32 (weight and bias gradients, dgates) have no
+    such exception.
+    extra (elementwise, >= 0, either dtype): where an input of this result was computed by
+    the two sides within tolerance of each other rather than bit-identically (MX codes of
+    h, dlogits feeding dx's gate share), the bound is widened by that input's bound carried
+    through linearly: bound = rule + extra.
     """
     g = f32_of(got).astype(np.float64)
     w = f32_of(want).astype(np.float64)
@@ -63,24 +71,57 @@ def check_close(got: np.ndarray, want: np.ndarray, dtype: int, what: str, mag: n
         return 0.0
     assert np.isfinite(g).all(), f"{what}: non-finite values"
     d = np.abs(g - w)
-    diff = d.max()
     if dtype == W.DT_F32:
         if extra is not None:
             d = np.maximum(d - np.asarray(extra, np.float64), 0.0)
-            diff = d.max()
+        diff = d.max()
         assert diff <= TOL_F32_ABS, f"{what}: max abs err {diff:.3e} > {TOL_F32_ABS}"
         return float(diff / TOL_F32_ABS)
     rms = math.sqrt((w ** 2).mean())
-    if mag is None:
-        mag = np.abs(w)
-    bound = TOL_BF16_REL_RMS * rms + 2.0 ** -7 * np.asarray(mag, np.float64)
+    bound = np.full(d.shape, TOL_BF16_REL_RMS * rms)
     if extra is not None:
         bound = bound + np.asarray(extra, np.float64)
     ratio = d / np.maximum(bound, 1e-300)
+    over = ratio > 1.0
+    nflip = 0
+    if over.any() and got.dtype == np.uint16 and want.dtype == np.uint16:
+        flip = over & (np.abs(_bf16_key(got) - _bf16_key(want)) == 1)
+        nflip = int(flip.sum())
+        over &= ~flip
+        ratio = np.where(flip, 0.0, ratio)
     i = np.unravel_index(np.argmax(ratio), d.shape)
-    assert ratio[i] <= 1.0, (f"{what}: |err| {d[i]:.3e} exceeds 2e-2*rms + 2^-7*mag = {bound[i]:.3e} at {i} "
-                             f"(got {g[i]:.6e} want {w[i]:.6e}, rms {rms:.3e}; max err/rms {diff / rms:.3e})")
+    if nflip:
+        print(f"[tolerance] {what}: {nflip} of {d.size} elements beyond 2e-2 RMS are one-ulp bf16 rounding flips",
+              flush=True)
+    assert not over.any(), (f"{what}: {int(over.sum())} elements exceed 2e-2*rms{' + extra' if extra is not None else ''}"
+                            f"; worst |err| {d[i]:.3e} > {bound[i]:.3e} at {i} (got {g[i]:.6e} want {w[i]:.6e}, "
+                            f"rms {rms:.3e})")
     return float(ratio[i])
+
+
+def check_logits(got: np.ndarray, want: np.ndarray, x: np.ndarray, Wg: np.ndarray, what="logits") -> float:
+    """GPU gate logits (fp32 accumulation, any summation order) against the oracle's plain
+    fp64 sum rounded once. Bound per element: the fp32 summation bound gamma_M sum_m
+    |x_m Wg[m, e]| (gamma_n = n u / (1 - n u), u = 2^-24, any order of n - 1 additions)
+    plus half an fp32 ulp of the oracle's value and the fp64 sum's own error; and at most
+    1e-5 absolute. Returns max |got - want|. Routing is then checked on the GPU's logits."""
+    g = np.asarray(got, np.float64)
+    w = np.asarray(want, np.float64)
+    assert g.shape == w.shape, (what, g.shape, w.shape)
+    if g.size == 0:
+        return 0.0
+    assert np.isfinite(g).all(), f"{what}: non-finite values"
+    M = x.shape[1]
+    u = 2.0 ** -24
+    gam = M * u / (1.0 - M * u)
+    absum = np.abs(f32_of(x).astype(np.float64)) @ np.abs(np.asarray(Wg, np.float64))
+    bound = (gam + M * 2.0 ** -53) * absum + 0.5 * np.spacing(np.abs(want).astype(np.float32)).astype(np.float64)
+    d = np.abs(g - w)
+    ratio = d / np.maximum(bound, 1e-300)
+    i = np.unravel_index(np.argmax(ratio), d.shape)
+    assert ratio[i] <= 1.0, f"{what}: |err| {d[i]:.3e} > fp32 summation bound {bound[i]:.3e} at {i}"
+    assert d.max() <= 1e-5, f"{what}: max abs err {d.max():.3e} > 1e-5"
+    return float(d.max())
 
 
 def check_gates(got: np.ndarray, want: np.ndarray, what="gates"):
@@ -175,9 +216,9 @@ def check_dwg(got, want, x, dl, dtype, dl_err=None, what="dWg"):
 
 
 def dgates_err(dg_want, dtype):
-    """Elementwise bound of the dgates tolerance rule (check_close) for these values."""
+    """Elementwise bound of the dgates tolerance rule (check_close; dgates are stored in fp32)."""
     w = np.asarray(dg_want, np.float64)
     if dtype == W.DT_F32:
         return np.full(w.shape, TOL_F32_ABS)
     rms = math.sqrt((w ** 2).mean()) if w.size else 0.0
-    return TOL_BF16_REL_RMS * rms + 2.0 ** -7 * np.abs(w)
+    return np.full(w.shape, TOL_BF16_REL_RMS * rms)

@@ -17,7 +17,7 @@ import torch
 
 import oracle
 import workloads as W
-from tests.gpu_helpers import check_close, compare_route, dev, host, inputs_np, shape_of
+from tests.gpu_helpers import check_close, check_logits, compare_route, dev, host, inputs_np, shape_of
 
 pytestmark = pytest.mark.gpu
 
@@ -236,8 +236,8 @@ def test_mx_full_size_gated_layer(wfmt):
     b = moe.layer_forward_mx(s, wfmt, inp["x"], W1g, inp["b1"], W2g, inp["b2"], Wg=inp["Wg"])
     torch.cuda.synchronize()
     ni = {k_: host(v) for k_, v in inp.items()}
-    logits = oracle.gate_logits(ni["x"], ni["Wg"], w.dtype)
-    assert np.array_equal(host(b["logits"]), logits)
+    logits = host(b["logits"])
+    check_logits(logits, oracle.gate_logits(ni["x"], ni["Wg"], w.dtype), ni["x"], ni["Wg"])
     rt = oracle.route(logits, w.k, w.capacity_factor)
     C = rt["C"]
     W1q = (host(W1g[0]), host(W1g[1]))

@@ -12,7 +12,8 @@ import torch
 
 import oracle
 import workloads as W
-from tests.gpu_helpers import (check_close, check_gates, compare_route, dev, gpu_route, host, inputs_np, shape_of)
+from tests.gpu_helpers import (check_close, check_gates, check_logits, compare_route, dev, gpu_route, host, inputs_np,
+                               shape_of)
 from tests.helpers import f32_of
 
 pytestmark = pytest.mark.gpu
@@ -90,9 +91,8 @@ def test_route_empty_input():
     assert g["C"] == 1 and (g["needed"] == 0).all() and (g["fill"] == 0).all()
 
 
-# Gate projection shapes: one summation chunk (M = 64) up to 48 chunks and the
-# 128-wide chunks of M > 4096, chunk counts that are not powers of two, ragged
-# token groups, E from 3 to 512, both dtypes.
+# Gate projection shapes: M from 64 to 4160, ragged token groups, E from 3 to 512,
+# both dtypes.
 GATE_CASES = [
     MID[3],
     W.GATED_BF16.replace(S=1024),
@@ -109,14 +109,15 @@ GATE_CASES = [
 
 
 @pytest.mark.parametrize("w", GATE_CASES, ids=lambda w: w.name)
-def test_gate_projection_bit_exact(w):
+def test_gate_projection_within_fp32_bound(w):
     import combine_softmax_top_amd as moe
     inp = W.make_inputs(w, seed=3)
-    o = oracle.gate_logits(host(inp["x"]), host(inp["Wg"]), w.dtype)
+    x, Wg = host(inp["x"]), host(inp["Wg"])
+    o = oracle.gate_logits(x, Wg, w.dtype)
     logits = torch.empty(w.S, w.E, dtype=torch.float32, device="cuda")
     moe.moe_gate_project(shape_of(w), inp["x"].cuda(), inp["Wg"].cuda(), logits)
     torch.cuda.synchronize()
-    assert np.array_equal(host(logits), o)
+    check_logits(host(logits), o, x, Wg)
 
 
 # ------------------------------------------------------------------ stage by stage
@@ -198,7 +199,7 @@ def test_layer_forward_matches_oracle(w):
     logits = None
     if w.logits == "gate":
         logits = host(b["logits"])
-        assert np.array_equal(logits, oracle.gate_logits(ni["x"], ni["Wg"], w.dtype))
+        check_logits(logits, oracle.gate_logits(ni["x"], ni["Wg"], w.dtype), ni["x"], ni["Wg"])
     fw = _oracle_forward(w, ni, logits=logits)
     rt = fw["route"]
     C = int(b["capacity"].item())
@@ -278,11 +279,7 @@ def test_layer_backward_matches_oracle(w):
     ni = inputs_np(inp)
     fw = _oracle_forward(w, ni)
     bw = oracle.layer_backward(fw, ni, w.act, w.dtype)
-    # dx sums the token's rounded dbuf rows: each may differ by one ulp
-    terms = np.zeros(bw["dx"].shape)
-    for i, q in enumerate(bw["routes"]):
-        terms[int(q) % w.S] += np.abs(f32_of(bw["dbuf"][i]))
-    check_close(host(gr["dx"]), bw["dx"], w.dtype, "dx", mag=np.abs(f32_of(bw["dx"])) + terms)
+    check_close(host(gr["dx"]), bw["dx"], w.dtype, "dx")
     check_close(host(gr["dgates"]), bw["dgates"], w.dtype, "dgates")
     check_close(host(gr["dW1"]), bw["dW1"], w.dtype, "dW1")
     check_close(host(gr["dW2"]), bw["dW2"], w.dtype, "dW2")

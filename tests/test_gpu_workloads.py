@@ -1,9 +1,10 @@
 """GPU parity at the named workloads' full sizes, in the launch configuration the
 benchmark times (the fused C-ABI calls).
 
-Routing (and the gate projection) and the encode buffer are compared in full,
-bit for bit. GEMM-dependent outputs are compared on seeded samples that the
-oracle computes one by one from the original inputs: every expert's first and
+The gate projection is compared in full within its fp32 summation bound;
+routing (on the GPU's logits) and the encode buffer in full, bit for bit.
+GEMM-dependent outputs are compared on seeded samples that the oracle computes
+one by one from the original inputs: every expert's first and
 last filled rows plus random rows of h and y, a random set of tokens of the
 layer output, and, for the workloads with a backward, random gate gradients,
 random tokens of dx, and the weight/bias gradients of three experts (hottest,
@@ -24,7 +25,7 @@ import torch
 
 import oracle
 import workloads as W
-from tests.gpu_helpers import check_close, check_dlogits, check_dwg, compare_route, dgates_err, host
+from tests.gpu_helpers import check_close, check_dlogits, check_dwg, check_logits, compare_route, dgates_err, host
 from tests.helpers import f32_of
 
 pytestmark = pytest.mark.gpu
@@ -57,8 +58,10 @@ def test_full_size_workload(w):
 
     # ---- gate projection and routing, in full
     if gate:
-        logits = oracle.gate_logits(ni["x"], ni["Wg"], w.dtype)
-        assert np.array_equal(host(b["logits"]), logits), "gate projection"
+        # the projection within its fp32 bound; routing parity runs on the GPU's logits
+        logits = host(b["logits"])
+        err = check_logits(logits, oracle.gate_logits(ni["x"], ni["Wg"], w.dtype), ni["x"], ni["Wg"])
+        _say(f"[{w.name}] gate logits within the fp32 summation bound (max abs err {err:.2e})")
     else:
         logits = ni["logits"]
     rt = oracle.route(logits, w.k, w.capacity_factor)
@@ -159,16 +162,11 @@ def test_full_size_workload(w):
     q, _, _, dbuf_o = oracle.backward_rows(fw, ni, dx_rows, w.act, w.dtype, want_dy=False, want_dpre=False)
     dx_o = oracle.dx_tokens(q, dbuf_o, dx_toks, w.S, w.k, w.dtype, dlogits=dl_o if gate else None,
                             Wg=ni.get("Wg"))
-    terms = np.zeros(dx_o.shape)
-    for i, qq in enumerate(q):
-        terms[list(dx_toks).index(int(qq) % w.S)] += np.abs(f32_of(dbuf_o[i]))
     extra = None
     if gate:
-        wga = np.abs(ni["Wg"].astype(np.float64))
-        terms += np.abs(dl_o[dx_toks]) @ wga.T
-        extra = dl_err[dx_toks] @ wga.T
-    check_close(host(gr["dx"][torch.from_numpy(dx_toks).cuda()]), dx_o, w.dtype, "dx (sampled)",
-                mag=np.abs(f32_of(dx_o)) + terms, extra=extra)
+        # dx's gate share: the dlogits bound carried through |Wg|^T
+        extra = dl_err[dx_toks] @ np.abs(ni["Wg"].astype(np.float64)).T
+    check_close(host(gr["dx"][torch.from_numpy(dx_toks).cuda()]), dx_o, w.dtype, "dx (sampled)", extra=extra)
     _say(f"[{w.name}] dgates on {len(routes)} routes and dx on {len(dx_toks)} tokens within tolerance")
     order = np.argsort(fill)
     experts = sorted({int(order[-1]), int(order[len(order) // 2]), int(order[0])})
