@@ -1,22 +1,26 @@
 """Benchmark of the single-GPU MoE layer on MI355X.
 
 One step = one pass of the whole layer over one batch of synthetic input that is
-already resident in HBM: for the default workload (S=4096 tokens, M=1024, E=8
-experts, top-2, H=4096, bf16, logits projected from x by an fp32 gate matrix,
-capacity_factor 1.25) that is gate projection -> route -> encode -> fc1 -> fc2
--> decode (Residual-MoE workloads add the dense MLP branch over all tokens,
-summed into decode); workloads with a backward add the backward of decode, FFN, encode
-and the gate (dlogits through the softmax, the 0.01 load-balance loss, and for
-a projected gate dWg and the projection's share of dx). The timed region is exactly --steps calls of the fused C-ABI entry
-points, bracketed by synchronisations. Forward workloads run consecutive batches on two streams by
-default, each stream with its own buffers (--batch-streams): a batch's short routing, encode and
-decode launches then overlap the neighbouring batch's expert products, which leave CUs idle in their
-last round. The same steps run one after another on one stream are timed too (single_stream).
+already resident in HBM. The default workload is the largest one that fits one
+GPU: S=32768 tokens, M=4096, E=128 experts, top-8, H=1536, bf16, Zipf-skewed
+logits, capacity_factor -2.0, forward + backward. Its step is route -> encode ->
+fc1 -> fc2 -> decode, then the backward: decode backward (dy, dgates), the gate
+backward (dlogits through the softmax and the 0.01 load-balance loss), the four
+expert products (dpre with the activation gradient, dW2, dbuf, dW1) and the
+encode backward (dx). Gate-projected workloads add the projection (and dWg and
+dx's gate share in training); Residual-MoE workloads add the dense branch.
+The timed region is exactly --steps calls of the fused C-ABI entry points
+(moe_layer_forward, moe_layer_backward), bracketed by synchronisations; `value`
+is tokens per second of that one-stream loop.
 
-A second timed loop records HIP events around each stage on the stream the
-library launches on, to report each stage against its roofline (bytes or flops
-the method must move or compute per launch, over the stage's average time).
-The CPU oracle is timed on a bounded sample of the same workload as a baseline.
+A second loop times each stage through its own C-ABI entry point (one kernel
+each, except route and the gate backward) with HIP events on the stream the
+library launches on, and reports it against its roofline: the bytes or flops the
+method must move or compute per launch over the stage's average time. HBM-bound
+stages are timed one launch at a time after a 512 MiB buffer fill, so that
+their operands come from HBM, not from L2 or the Infinity Cache; MFMA-bound
+stages run in back-to-back batches. `roofline` is the slowest single-kernel
+stage. The CPU oracle is timed on a bounded sample of the same workload.
 
 Prints one JSON line on stdout; diagnostics go to stderr.
 """
@@ -25,6 +29,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import platform
 import re
 import sys
 import time
@@ -37,6 +42,8 @@ HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 MFMA_BF16_PEAK_TFS = 2500.0  # dense bf16 MFMA
 MFMA_FP8_PEAK_TFS = 5000.0   # dense fp8 MFMA (MX experts: the token operand is always MXFP8)
 FP32_VECTOR_PEAK_TFS = 157.3
+DEFAULT_WORKLOAD = "large_bf16_S32768_M4096_E128_k8_H1536"
+FLUSH_MIB = 512
 
 
 def log(*a):
@@ -46,23 +53,21 @@ def log(*a):
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    # a step of the default workload is ~0.25 ms: 1000 timed steps keep the GPU at
-    # its steady clocks for about a quarter second (20 steps measured the ramp)
-    ap.add_argument("--steps", type=int, default=1000)
-    ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--workload", default="gated_bf16_S4096_M1024_E8_k2_H4096",
-                    help="workload name (see workloads.py); default: the S=4096 gate-projected bf16 layer")
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD,
+                    help="workload name (see workloads.py); default: the S=32768 forward + backward layer")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle FFN sample")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle's sample")
+    ap.add_argument("--stage-reps", type=int, default=0,
+                    help="launches per stage in the stage timing (0: about 2 s of GPU time per stage, 3..50)")
     ap.add_argument("--pipeline-chunks", type=int, default=0, metavar="D",
                     help="run the expert FFN in D capacity chunks on --pipeline-streams streams "
                          "(bf16 forward workloads; 0 = the fused forward)")
     ap.add_argument("--pipeline-streams", type=int, default=2)
     ap.add_argument("--batch-streams", type=int, default=0, metavar="N",
-                    help="consecutive batches alternate over N streams, each stream with its own buffers, so that "
-                         "one batch's routing, encode and decode overlap the neighbouring batches' expert products; "
-                         "0 (default): 2 for forward workloads, 1 for training and pipelined runs. With N > 1 the "
-                         "same steps are also timed on one stream and reported as single_stream")
+                    help="forward workloads: also time consecutive batches alternating over N streams, each stream "
+                         "with its own buffers (reported as multi_stream; 0: 2 for forward workloads, off otherwise)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 3 plain device copies of MIB MiB each (the reference kernel that scales the "
                          "FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -73,7 +78,8 @@ def parse():
 # WRITE_SIZE) recorded in profiles/traffic_<stage>_<workload>.md together with the
 # sha256 of the kernel sources they were taken on; it is reported only while those
 # sources are unchanged.
-TRAFFIC_SOURCES = ("combine_softmax_top_amd/csrc/gemm.hip", "combine_softmax_top_amd/csrc/moe_internal.h")
+TRAFFIC_SOURCES = ("combine_softmax_top_amd/csrc/gemm.hip", "combine_softmax_top_amd/csrc/dispatch.hip",
+                   "combine_softmax_top_amd/csrc/moe_internal.h")
 
 
 def sources_sha256():
@@ -113,32 +119,41 @@ def copy_calibration(mib):
 
 
 def algorithmic(w, C, kept):
-    """Bytes (or flops) each stage must move (or compute), per launch."""
+    """Bytes (or flops) each stage must move (or compute), per launch, and its bound."""
     b = w.elem_bytes
     S, M, E, k, H = w.S, w.M, w.E, w.k, w.H
+    prod = 2 * M * H * kept  # one expert product over the filled rows
     st = {
         "route": ("bytes", 4 * S * E + 12 * k * S + 4 * kept + 8 * E),
         # MX encode writes one code byte per value plus a scale byte per 32
         "encode": ("bytes", S * M * b + (E * C * M * 33 // 32 if w.mx else E * C * M * b) + 8 * k * S),
-        "fc1": ("flops", 2 * M * H * kept),
-        "fc2": ("flops", 2 * M * H * kept),
+        "fc1": ("flops", prod),
+        "fc2": ("flops", prod),
         "decode": ("bytes", kept * M * b + S * M * b + 12 * k * S + (S * M * b if w.residual else 0)),
     }
     if w.residual:
-        # the dense branch: fc1 and fc2 over all S tokens
-        st["res_ffn"] = ("flops", 4 * M * H * S)
+        st["res_ffn"] = ("flops", 4 * M * H * S)  # the dense branch: fc1 and fc2 over all S tokens
     if w.logits == "gate":
         st["gate"] = ("bytes", S * M * b + 4 * M * E + 4 * S * E)
     if w.backward:
-        # dy/dgates: read dout and kept y rows, write kept dy rows; dx: read kept dbuf rows, write dx;
-        # GEMMs: dh, dW2, dbuf, dW1 (2*M*H*kept flops each)
-        st["backward"] = ("flops", 8 * M * H * kept)
+        # K1' and K2: read dout and the kept y rows, write the kept dy rows and dgates
+        st["decode_bwd"] = ("bytes", S * M * b + 2 * kept * M * b + 16 * k * S)
+        st["fc2_bwd_data"] = ("flops", prod)  # dpre = (dy W2) * act'(pre)
+        st["fc2_wgrad"] = ("flops", prod)     # dW2 = dy^T h
+        st["fc1_bwd_data"] = ("flops", prod)  # dbuf = dpre W1
+        st["fc1_wgrad"] = ("flops", prod)     # dW1 = dpre^T buf
+        # K0: read the kept dbuf rows, write dx
+        st["encode_bwd"] = ("bytes", kept * M * b + S * M * b + 8 * k * S)
         # gate backward: read logits, idx, dgates, needed; write dlogits
         st["gate_bwd"] = ("bytes", 8 * S * E + 8 * k * S + 4 * E)
         if w.logits == "gate":
-            # dWg = x^T dlogits: read x and dlogits, write dWg
-            st["gate_wgrad"] = ("bytes", S * M * b + 4 * S * E + 4 * M * E)
+            st["gate_wgrad"] = ("bytes", S * M * b + 4 * S * E + 4 * M * E)  # dWg = x^T dlogits
     return st
+
+
+# stages that are one kernel launch (candidates for the dominant kernel)
+SINGLE_KERNEL = {"gate", "encode", "fc1", "fc2", "decode", "decode_bwd", "fc2_bwd_data", "fc2_wgrad",
+                 "fc1_bwd_data", "fc1_wgrad", "encode_bwd"}
 
 
 def roofline_of(kind, amount, ms, dtype_bf16=True, mx=False):
@@ -152,30 +167,53 @@ def roofline_of(kind, amount, ms, dtype_bf16=True, mx=False):
                 frac=round(ach / peak, 4))
 
 
-def cpu_baseline(w, inp, C_gpu, budget_s):
-    """Time the CPU oracle on a bounded sample of the workload; returns the cpu_baseline object."""
+def host_info():
+    model = platform.processor() or ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return dict(cpu_model=model, nproc=os.cpu_count(), affinity_cores=len(os.sched_getaffinity(0)))
+
+
+def cpu_baseline(w, inp, budget_s):
+    """Time the CPU oracle on a bounded sample of the workload; returns the cpu_baseline object.
+
+    Routing, encode and decode run on every token. The expert FFN (and for training
+    workloads its backward: the per-row backward, dgates, the weight gradients and dx)
+    runs on the kept routes of a seeded sample of tokens, sized to about budget_s, and
+    each stage's time is scaled linearly to the whole workload (rows, or tokens for dx).
+    """
     import numpy as np
     import oracle
     from tests.helpers import np_of
     ni = {k: np_of(v) for k, v in inp.items()}
-    t = {}
+    t, scaled = {}, {}
     t0 = time.perf_counter()
-    if w.logits == "gate":
-        logits = oracle.gate_logits(ni["x"], ni["Wg"], w.dtype)
-    else:
-        logits = ni["logits"]
+    logits = oracle.gate_logits(ni["x"], ni["Wg"], w.dtype) if w.logits == "gate" else ni["logits"]
     t["gate"] = time.perf_counter() - t0
     t0 = time.perf_counter()
-    rt = oracle.route(logits, w.k, w.capacity_factor, with_slots=False)
+    rt = oracle.route(logits, w.k, w.capacity_factor)
     t["route"] = time.perf_counter() - t0
-    assert rt["C"] == C_gpu, (rt["C"], C_gpu)
     t0 = time.perf_counter()
     buf = oracle.encode(ni["x"], rt, w.E, w.dtype)
     t["encode"] = time.perf_counter() - t0
-    rows = oracle.filled_rows(rt)
-    kept = len(rows)
+    C = rt["C"]
+    kept_rows = oracle.filled_rows(rt)
+    kept = len(kept_rows)
+    rng = np.random.default_rng(0)
+    order = rng.permutation(w.S)
+
+    def rows_of(toks):
+        r = [int(rt["idx"][q, s]) * C + int(rt["loc"][q, s]) for s in toks for q in range(w.k)
+             if rt["loc"][q, s] < C]
+        return np.asarray(sorted(r), np.int64)
+
     if w.mx:
-        # MX experts: the token rows are quantised in the encode (timed with it), the weights offline
         wf = oracle.MX_FP8 if w.mx == "mxfp8" else oracle.MX_FP4
         t0 = time.perf_counter()
         bufq = oracle.mx_quantize(buf, oracle.MX_FP8, w.dtype)
@@ -184,41 +222,89 @@ def cpu_baseline(w, inp, C_gpu, budget_s):
         W2q = oracle.mx_quantize(ni["W2"], wf, w.dtype)
 
         def ffn(rs):
-            return None, None, oracle.expert_rows_mx(bufq, W1q, ni.get("b1"), W2q, ni.get("b2"), rs, rt["C"], w.act,
-                                                     wf)[1]
+            return None, oracle.expert_rows_mx(bufq, W1q, ni.get("b1"), W2q, ni.get("b2"), rs, C, w.act, wf)[1]
     else:
         def ffn(rs):
-            return oracle.expert_rows(buf, ni["W1"], ni.get("b1"), ni["W2"], ni.get("b2"), rs, rt["C"], w.act,
-                                      w.dtype)
-    # FFN on an evenly strided sample of the filled rows, sized to about budget_s
-    probe = rows[:: max(1, kept // 16)][:16]
-    t0 = time.perf_counter()
-    ffn(probe)
-    per_row = (time.perf_counter() - t0) / max(1, len(probe))
-    n = int(min(kept, max(16, budget_s / max(per_row, 1e-9))))
-    sample = rows[:: max(1, kept // n)][:n]
-    t0 = time.perf_counter()
-    _, _, ys = ffn(sample)
-    t_sample = time.perf_counter() - t0
-    t["ffn"] = t_sample / len(sample) * kept
-    y = np.zeros((w.E * rt["C"], w.M), ys.dtype)  # decode's cost does not depend on the values
-    y[sample] = ys
+            _, h, y = oracle.expert_rows(buf, ni["W1"], ni.get("b1"), ni["W2"], ni.get("b2"), rs, C, w.act, w.dtype,
+                                         want_h=True)
+            return h, y
+
+    def sample_pass(toks, timings):
+        rs = rows_of(toks)
+        t0 = time.perf_counter()
+        h, y = ffn(rs)
+        timings["ffn"] = time.perf_counter() - t0
+        if w.backward:
+            fw = dict(route=rt, buf=buf)
+            t0 = time.perf_counter()
+            q, dy, dpre, dbuf = oracle.backward_rows(fw, ni, rs, w.act, w.dtype)
+            timings["ffn_bwd_rows"] = time.perf_counter() - t0
+            t0 = time.perf_counter()
+            oracle.dgates(q, ni["dout"], y, w.S, w.dtype)
+            timings["dgates"] = time.perf_counter() - t0
+            t0 = time.perf_counter()
+            oracle.dx_tokens(q, dbuf, toks, w.S, w.k, w.dtype)
+            timings["dx"] = time.perf_counter() - t0
+        return len(rs), y
+
+    # probe on a few tokens, then a sample sized to the budget
+    probe = {}
+    n_probe = max(1, min(w.S, 4))
+    nr, _ = sample_pass(order[:n_probe], probe)
+    per_token = sum(probe.values()) / n_probe
+    # a tenth of the budget goes to the weight gradients below
+    ntok = int(min(w.S, max(n_probe, 0.9 * budget_s / max(per_token, 1e-9))))
+    toks = np.sort(order[:ntok])
+    samp = {}
+    nrows, ys = sample_pass(toks, samp)
+    row_scale = kept / max(1, nrows)
+    for name, v in samp.items():
+        scaled[name] = v * (w.S / ntok if name == "dx" else row_scale)
+    nw = 0
+    if w.backward and kept > 0:
+        # weight gradients: a fixed cost per expert (its M x H outputs) plus one per row, so
+        # they are timed on enough rows of one expert (the fullest) for the fixed part to be
+        # small, and scaled by rows: kept rows over all experts
+        e_w = int(np.argmax(rt["fill"]))
+        nw = int(min(48, rt["fill"][e_w]))
+        wr = e_w * C + np.arange(nw, dtype=np.int64)
+        _, dyw, dprew, _ = oracle.backward_rows(dict(route=rt, buf=buf), ni, wr, w.act, w.dtype, want_dbuf=False)
+        hw, _ = ffn(wr)
+        t0 = time.perf_counter()
+        oracle.weight_grads(dyw, hw, dprew, buf[wr], w.dtype)
+        samp["wgrad"] = time.perf_counter() - t0
+        scaled["wgrad"] = samp["wgrad"] * kept / nw
+    rs = rows_of(toks)
+    y = np.zeros((w.E * C, w.M), ys.dtype)  # decode's cost does not depend on the values
+    y[rs] = ys
     t0 = time.perf_counter()
     oracle.decode(y, rt, w.E, w.dtype)
     t["decode"] = time.perf_counter() - t0
-    total = sum(t.values())
+    if w.backward:
+        dg = np.zeros((w.k, w.S), np.float32)
+        t0 = time.perf_counter()
+        oracle.gate_backward(logits, rt["idx"], dg, rt["needed"], 0.01)
+        t["gate_bwd"] = time.perf_counter() - t0
+    total = sum(t.values()) + sum(scaled.values())
+    what = "forward + backward" if w.backward else "forward"
     return dict(value=round(w.S / total, 2), unit="tokens/s", cores=oracle.num_threads(), kind="oracle",
-                sample=(f"gate/route/encode/decode on all {w.S} tokens; expert FFN on {len(sample)} of the {kept} "
-                        f"filled rows (evenly strided, {t_sample:.1f}s), scaled linearly to all filled rows; "
-                        f"forward only"),
-                seconds={k: round(v, 3) for k, v in t.items()})
+                sample=(f"{what}; gate/route/encode/decode{'/gate backward' if w.backward else ''} on all {w.S} "
+                        f"tokens; expert FFN{' and its backward (rows, dgates, dx)' if w.backward else ''}"
+                        f" on the {nrows} kept routes of {ntok} seeded random tokens"
+                        + (f", weight gradients on {nw} rows of one expert" if w.backward else "")
+                        + f" ({sum(samp.values()):.1f} s), scaled linearly to all {kept} kept routes "
+                        f"({w.S} tokens for dx)"),
+                seconds={**{k: round(v, 3) for k, v in t.items()}, **{k: round(v, 2) for k, v in scaled.items()}},
+                sample_seconds={k: round(v, 3) for k, v in samp.items()},
+                host=host_info())
 
 
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU's share of the layer: --gpus {args.gpus} is not supported "
-              "(the layer here runs on one GPU, with no collectives; run with --gpus 1)", file=sys.stderr)
+        print(f"bench.py measures one GPU's share of the MoE layer (routing, encode, the experts' GEMMs, decode and "
+              f"their backward on one GPU, no collectives): --gpus {args.gpus} is not supported, run with --gpus 1",
+              file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
@@ -240,7 +326,10 @@ def main():
     else:
         bufs = moe.alloc_forward(s, dev, training=w.backward, gate_projection=gate, residual=w.residual)
     res = {n: inp.get(n) for n in ("W1r", "b1r", "W2r", "b2r")} if w.residual else None
-    grads = moe.alloc_backward(s, dev, gate=True, gate_projection=gate) if w.backward else None
+    grads = None
+    if w.backward:
+        grads = moe.alloc_backward(s, dev, gate=True, gate_projection=gate)
+        grads["dbuf"] = torch.empty_like(grads["dy"])  # its own memory, so each stage can be timed alone
     x, W1, W2, b1, b2 = inp["x"], inp["W1"], inp["W2"], inp.get("b1"), inp.get("b2")
     logits_in, Wg = (None, inp["Wg"]) if gate else (inp["logits"], None)
     # the training step's backward includes the gate: dlogits, the load-balance loss, and with a
@@ -273,10 +362,10 @@ def main():
         bstreams = [torch.cuda.Stream() for _ in range(nb)]
     counter = [0]
 
-    def step(one_stream=False):
-        i = 0 if one_stream else counter[0] % nb
+    def step(multi=False):
+        i = counter[0] % nb if multi else 0
         counter[0] += 1
-        b, st = bsets[i], bstreams[i]
+        b, st = bsets[i], bstreams[i] if multi else None
         if mxf is not None:
             moe.layer_forward_mx(s, mxf, x, W1q, b1, W2q, b2, logits=logits_in, Wg=Wg, bufs=b, stream=st)
             return
@@ -288,75 +377,38 @@ def main():
         if w.backward:
             backward()
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    log(f"[bench] warmup done ({args.warmup} steps); timing {args.steps} steps")
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    ms_per_step = elapsed * 1e3 / max(1, args.steps)
-    value = w.S * args.steps / elapsed
-    single = None
-    if nb > 1:
-        # the same steps, one after another on one stream
+    def timed_loop(multi):
         for _ in range(args.warmup):
-            step(one_stream=True)
+            step(multi)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for _ in range(args.steps):
-            step(one_stream=True)
+            step(multi)
         torch.cuda.synchronize()
-        e1 = time.perf_counter() - t0
-        single = dict(value=round(w.S * args.steps / e1, 1), ms_per_step=round(e1 * 1e3 / max(1, args.steps), 5))
-        log(f"[bench] {nb} streams: {ms_per_step:.4f} ms/step; one stream: {single['ms_per_step']:.4f} ms/step, "
-            f"{single['value']:.4g} tokens/s")
+        return time.perf_counter() - t0
+
+    # ---- the timed region: --steps fused steps on one stream
+    elapsed = timed_loop(False)
+    ms_per_step = elapsed * 1e3 / max(1, args.steps)
+    value = w.S * args.steps / elapsed
+    log(f"[bench] {args.steps} steps after {args.warmup} warm-up: {ms_per_step:.4f} ms/step, {value:.4g} tokens/s")
+    multi = None
+    if nb > 1:
+        e2 = timed_loop(True)
+        multi = dict(streams=nb, value=round(w.S * args.steps / e2, 1),
+                     ms_per_step=round(e2 * 1e3 / max(1, args.steps), 5))
+        log(f"[bench] the same steps alternating over {nb} streams: {multi['ms_per_step']:.4f} ms/step, "
+            f"{multi['value']:.4g} tokens/s")
 
     C = int(bufs["capacity"].item())
     kept = int(bufs["fill"].sum().item())
-    log(f"[bench] {ms_per_step:.4f} ms/step, {value:.4g} tokens/s; C={C}, kept={kept}")
+    log(f"[bench] C={C}, kept={kept}")
 
-    # ---- per-stage HIP-event timing on the library's stream
+    # ---- per-stage timing through each stage's own entry point, on the library's stream
     stream = torch.cuda.current_stream()
-    names = (["gate"] if gate else []) + ["route", "encode", "fc1", "fc2"] + (["res_ffn"] if w.residual else []) + [
-        "decode"] + (
-        ["backward", "gate_bwd"] + (["gate_wgrad"] if gate else []) if w.backward else [])
-    ev = {n: [] for n in names}
     lg = bufs["logits"] if gate else logits_in
     b = bufs
-
-    # Each stage is timed over a batch of back-to-back launches between two events.
-    # bf16 matmuls enqueued ahead of the first event keep the GPU busy while the
-    # host enqueues the batch, so the events bracket kernel time, not host gaps.
-    # Every stage is idempotent (same inputs, same outputs).
-    fa = torch.randn(4096, 4096, device="cuda", dtype=torch.bfloat16)
-    fb = torch.randn(4096, 4096, device="cuda", dtype=torch.bfloat16)
-    torch.mm(fa, fb)
-    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    c0.record(stream)
-    for _ in range(4):
-        torch.mm(fa, fb)
-    c1.record(stream)
-    torch.cuda.synchronize()
-    filler_ms = max(c0.elapsed_time(c1) / 4, 1e-3)
-
-    def stage_batch(name, fn, reps):
-        t0 = time.perf_counter()
-        fn()
-        torch.cuda.synchronize()
-        host_ms = (time.perf_counter() - t0) * 1e3  # bounds one call's host time
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        for _ in range(min(200, int((2.0 * host_ms * reps + 0.5) / filler_ms) + 1)):
-            torch.mm(fa, fb)
-        e0.record(stream)
-        for _ in range(reps):
-            fn()
-        e1.record(stream)
-        ev[name].append((e0, e1, reps))
-
+    alg = algorithmic(w, C, kept)
     stage_fns = []
     if gate:
         stage_fns.append(("gate", lambda: moe.moe_gate_project(s, x, Wg, lg)))
@@ -386,42 +438,90 @@ def main():
         stage_fns.append(("decode", lambda: moe.moe_decode(s, b["y"], b["gates"], b["idx"], b["loc"], b["capacity"],
                                                            b["out"])))
     if w.backward:
-        stage_fns.append(("backward", backward))
-        stage_fns.append(("gate_bwd", lambda: moe.moe_gate_backward(s, lg, b["idx"], grads["dgates"], b["needed"],
-                                                                    moe.AUX_COEF, grads["dlogits"],
-                                                                    grads["aux_loss"], b["ws"])))
+        g = grads
+        stage_fns += [
+            ("decode_bwd", lambda: moe.moe_decode_backward(s, inp["dout"], b["y"], b["gates"], b["idx"], b["loc"],
+                                                           b["capacity"], g["dy"], g["dgates"])),
+            ("gate_bwd", lambda: moe.moe_gate_backward(s, lg, b["idx"], g["dgates"], b["needed"], moe.AUX_COEF,
+                                                       g["dlogits"], g["aux_loss"], b["ws"])),
+            ("fc2_wgrad", lambda: moe.moe_expert_fc2_weight_grad(s, g["dy"], b["h"], b["fill"], b["capacity"],
+                                                                 g["dW2"], g["db2"])),
+            ("fc2_bwd_data", lambda: moe.moe_expert_fc2_backward_data(s, g["dy"], W2, b["pre"], b["fill"],
+                                                                      b["capacity"], g["dpre"])),
+            ("fc1_bwd_data", lambda: moe.moe_expert_fc1_backward_data(s, g["dpre"], W1, b["fill"], b["capacity"],
+                                                                      g["dbuf"])),
+            ("fc1_wgrad", lambda: moe.moe_expert_fc1_weight_grad(s, g["dpre"], b["buf"], b["fill"], b["capacity"],
+                                                                 g["dW1"], g["db1"])),
+            ("encode_bwd", lambda: moe.moe_encode_backward(s, g["dbuf"], b["idx"], b["loc"], b["capacity"], g["dx"])),
+        ]
         if gate:
-            stage_fns.append(("gate_wgrad", lambda: moe.moe_gate_weight_grad(s, x, grads["dlogits"], grads["dWg"],
-                                                                             b["ws"])))
-    reps = max(1, min(50, args.steps))
-    rounds = max(1, min(10, args.steps // reps))
-    for rd in range(rounds):
-        for name, fn in stage_fns:
-            stage_batch(name, fn, reps)
-        torch.cuda.synchronize()
-        log(f"[bench] stage timing round {rd + 1}/{rounds} done ({reps} launches per stage)")
+            stage_fns.append(("gate_wgrad", lambda: moe.moe_gate_weight_grad(s, x, g["dlogits"], g["dWg"], b["ws"])))
+
+    flush = torch.empty(FLUSH_MIB * 2 ** 20 // 4, dtype=torch.float32, device=dev)
+    # bf16 matmuls enqueued ahead of a batch keep the GPU busy while the host enqueues it,
+    # so the events bracket kernel time, not host gaps
+    fa = torch.randn(4096, 4096, device=dev, dtype=torch.bfloat16)
+    fb = torch.randn(4096, 4096, device=dev, dtype=torch.bfloat16)
+    torch.mm(fa, fb)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    for _ in range(4):
+        torch.mm(fa, fb)
+    c1.record(stream)
     torch.cuda.synchronize()
-    alg = algorithmic(w, C, kept)
+    filler_ms = max(c0.elapsed_time(c1) / 4, 1e-3)
+
     stages = {}
-    for n in names:
-        ms = sum(e0.elapsed_time(e1) for e0, e1, r in ev[n]) / sum(r for _, _, r in ev[n])
-        kind, amount = alg[n]
-        r = roofline_of(kind, amount, ms, w.dtype == W.DT_BF16, mx=bool(w.mx) and n in ("fc1", "fc2"))
+    for name, fn in stage_fns:
+        kind, amount = alg[name]
+        t0 = time.perf_counter()
+        fn()
+        torch.cuda.synchronize()
+        host_ms = (time.perf_counter() - t0) * 1e3  # bounds one call (host + device)
+        reps = args.stage_reps or max(3, min(50, int(2000.0 / max(host_ms, 1e-3))))
+        flushed = kind == "bytes"
+        pairs = []
+        if flushed:
+            # one launch at a time, after a fill that evicts L2 and the Infinity Cache
+            for _ in range(reps):
+                flush.fill_(1.0)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                fn()
+                e1.record(stream)
+                pairs.append((e0, e1, 1))
+        else:
+            for _ in range(min(200, int((2.0 * host_ms * reps + 0.5) / filler_ms) + 1)):
+                torch.mm(fa, fb)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                fn()
+            e1.record(stream)
+            pairs.append((e0, e1, reps))
+        torch.cuda.synchronize()
+        ms = sum(a.elapsed_time(z) for a, z, _ in pairs) / sum(r for _, _, r in pairs)
+        r = roofline_of(kind, amount, ms, w.dtype == W.DT_BF16, mx=bool(w.mx) and name in ("fc1", "fc2"))
         r["ms"] = round(ms, 5)
+        r["launches"] = reps
+        r["timing"] = "flushed single launches" if flushed else "back-to-back batch"
         r["algorithmic_" + kind] = amount
-        stages[n] = r
-        log(f"[bench] stage {n:9s} {ms:9.4f} ms  {r['achieved']:10.2f} {r['unit']}  ({100 * r['frac']:.1f}% of peak)")
-    # one-kernel stages only (the fused backward and the dense branch are several launches)
-    dominant = max((n for n in names if n not in ("backward", "res_ffn")), key=lambda n: stages[n]["ms"])
+        stages[name] = r
+        log(f"[bench] stage {name:13s} {ms:9.4f} ms  {r['achieved']:10.2f} {r['unit']}  "
+            f"({100 * r['frac']:.1f}% of peak; {r['timing']}, {reps} launches)")
+    del flush
+    dominant = max((n for n in stages if n in SINGLE_KERNEL), key=lambda n: stages[n]["ms"])
     d = stages[dominant]
     roofline = dict(kernel=dominant, bound=d["bound"], achieved=d["achieved"], peak=d["peak"], unit=d["unit"],
                     frac=d["frac"], traffic=recorded_traffic(dominant, w.name))
+    log(f"[bench] dominant kernel: {dominant} ({d['ms']:.4f} ms, {100 * d['frac']:.1f}% of peak)")
 
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
-        cpu = cpu_baseline(w, inp, C, args.cpu_seconds)
-        log(f"[bench] cpu baseline {cpu['value']} tokens/s on {cpu['cores']} threads: {cpu['sample']}")
+        cpu = cpu_baseline(w, inp, args.cpu_seconds)
+        log(f"[bench] cpu baseline {cpu['value']} tokens/s on {cpu['cores']} threads ({cpu['host']}): "
+            f"{cpu['sample']}")
 
     line = dict(
         metric=METRIC, value=round(value, 1), unit="tokens/s", n_gpus=1, steps=args.steps, warmup=args.warmup,
@@ -431,9 +531,8 @@ def main():
                     act="gelu" if w.act == W.ACT_GELU else "relu", biases=[w.has_fc1_bias, w.has_fc2_bias],
                     logits=w.logits, backward=w.backward, C=C, kept_routes=kept, parallelism="single-gpu",
                     aux_coef=moe.AUX_COEF if w.backward else None, residual=w.residual, mx=w.mx or None,
-                    pipeline=dict(chunks=args.pipeline_chunks, streams=args.pipeline_streams) if pipe else None,
-                    batch_streams=nb if nb > 1 else None),
-        roofline=roofline, stages=stages, cpu_baseline=cpu, single_stream=single,
+                    pipeline=dict(chunks=args.pipeline_chunks, streams=args.pipeline_streams) if pipe else None),
+        roofline=roofline, stages=stages, cpu_baseline=cpu, multi_stream=multi,
     )
     print(json.dumps(line), flush=True)
 

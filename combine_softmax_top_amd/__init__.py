@@ -98,6 +98,12 @@ _SIGS = {
     "moe_gate_backward": [_SP, _P, _P, _P, _P, ctypes.c_double, _P, _P, _P, ctypes.c_size_t, _P],
     "moe_gate_weight_grad": [_SP, _P, _P, _P, _P, ctypes.c_size_t, _P],
     "moe_layer_backward": [_SP] + [_P] * 23 + [ctypes.c_double] + [_P] * 6 + [ctypes.c_size_t, _P],
+    "moe_decode_backward": [_SP] + [_P] * 9,
+    "moe_expert_fc2_backward_data": [_SP] + [_P] * 7,
+    "moe_expert_fc2_weight_grad": [_SP] + [_P] * 7,
+    "moe_expert_fc1_backward_data": [_SP] + [_P] * 6,
+    "moe_expert_fc1_weight_grad": [_SP] + [_P] * 7,
+    "moe_encode_backward": [_SP] + [_P] * 6,
 }
 
 # coefficient of the auxiliary load-balance loss in the MoE training blog's runs
@@ -347,6 +353,36 @@ def moe_layer_backward(shape: Shape, dout, buf, pre, h, y, gates, idx, loc, fill
         _ptr(loc), _ptr(fill), _ptr(capacity), _ptr(W1), _ptr(W2), _ptr(dy), _ptr(dpre), _ptr(dbuf), _ptr(dx),
         _ptr(dW1), _ptr(db1), _ptr(dW2), _ptr(db2), _ptr(dgates), _ptr(logits), _ptr(needed), float(aux_coef),
         _ptr(x), _ptr(Wg), _ptr(dlogits), _ptr(dWg), _ptr(aux_loss), *_ws_args(ws), _stream(stream)))
+
+
+def moe_decode_backward(shape: Shape, dout, y, gates, idx, loc, capacity, dy, dgates, stream=None) -> None:
+    _check(_lib.moe_decode_backward(ctypes.byref(shape.c()), _ptr(dout), _ptr(y), _ptr(gates), _ptr(idx), _ptr(loc),
+                                    _ptr(capacity), _ptr(dy), _ptr(dgates), _stream(stream)))
+
+
+def moe_expert_fc2_backward_data(shape: Shape, dy, W2, pre, fill, capacity, dpre, stream=None) -> None:
+    _check(_lib.moe_expert_fc2_backward_data(ctypes.byref(shape.c()), _ptr(dy), _ptr(W2), _ptr(pre), _ptr(fill),
+                                             _ptr(capacity), _ptr(dpre), _stream(stream)))
+
+
+def moe_expert_fc2_weight_grad(shape: Shape, dy, h, fill, capacity, dW2, db2, stream=None) -> None:
+    _check(_lib.moe_expert_fc2_weight_grad(ctypes.byref(shape.c()), _ptr(dy), _ptr(h), _ptr(fill), _ptr(capacity),
+                                           _ptr(dW2), _ptr(db2), _stream(stream)))
+
+
+def moe_expert_fc1_backward_data(shape: Shape, dpre, W1, fill, capacity, dbuf, stream=None) -> None:
+    _check(_lib.moe_expert_fc1_backward_data(ctypes.byref(shape.c()), _ptr(dpre), _ptr(W1), _ptr(fill),
+                                             _ptr(capacity), _ptr(dbuf), _stream(stream)))
+
+
+def moe_expert_fc1_weight_grad(shape: Shape, dpre, buf, fill, capacity, dW1, db1, stream=None) -> None:
+    _check(_lib.moe_expert_fc1_weight_grad(ctypes.byref(shape.c()), _ptr(dpre), _ptr(buf), _ptr(fill),
+                                           _ptr(capacity), _ptr(dW1), _ptr(db1), _stream(stream)))
+
+
+def moe_encode_backward(shape: Shape, dbuf, idx, loc, capacity, dx, stream=None) -> None:
+    _check(_lib.moe_encode_backward(ctypes.byref(shape.c()), _ptr(dbuf), _ptr(idx), _ptr(loc), _ptr(capacity),
+                                    _ptr(dx), _stream(stream)))
 
 
 # ---------------------------------------------------------------- buffers

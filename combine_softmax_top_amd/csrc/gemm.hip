@@ -1856,52 +1856,74 @@ hipError_t launch_expert_ffn_mx(const moe_shape &s, int wfmt, const uint8_t *buf
     return launch_fc2_mx(s, wfmt, h_codes, h_scales, w2_codes, w2_scales, b2, fill, cap, y, cmax, st);
 }
 
-hipError_t launch_expert_ffn_bwd(const moe_shape &s, const void *buf, const void *pre, const void *h, const void *W1,
-                                 const void *W2, const int32_t *fill, const int32_t *cap, void *dy, void *dpre,
-                                 void *dbuf, float *dW1, float *db1, float *dW2, float *db2, int32_t cmax,
-                                 hipStream_t st) {
+// The four products of the FFN backward, one kernel each.
+// dpre = (dy . W2[e]) * act'(pre): A = dy [rows][M], B = W2[e] read as [K=M][N=H]
+hipError_t launch_fc2_bwd_data(const moe_shape &s, const void *dy, const void *W2, const void *pre,
+                               const int32_t *fill, const int32_t *cap, void *dpre, int32_t cmax, hipStream_t st) {
     const int M = s.M, H = s.H, E = s.E;
-    hipError_t err;
-    if (s.dtype == MOE_DT_BF16) {
-        // dW2[e] = dy^T h (+ db2 = column sums of dy)
-        if ((err = kgroup_launch(dy, h, dW2, M, H, E, fill, cap, db2, cmax, rows_hint(s, cmax), st)) != hipSuccess)
-            return err;
-        // dpre = (dy . W2[e]) * act'(pre): A = dy [rows][M], B = W2[e] read as [K=M][N=H]
-        if ((err = bwd_data_launch<EPI_DACT>(s.act, dy, W2, dpre, H, M, E, fill, cap, pre, rows_hint(s, cmax), st)) !=
-            hipSuccess)
-            return err;
-        // dbuf = dpre . W1[e]: B = W1[e] read as [K=H][N=M]   (dbuf may alias dy: dy is consumed above;
-        // run right after dpre is written, dpre's rows are still in the last-level cache)
-        if ((err = bwd_data_launch<EPI_PLAIN>(s.act, dpre, W1, dbuf, M, H, E, fill, cap, nullptr, rows_hint(s, cmax),
-                                              st)) != hipSuccess)
-            return err;
-        // dW1[e] = dpre^T buf (+ db1 = column sums of dpre)
-        return kgroup_launch(dpre, buf, dW1, H, M, E, fill, cap, db1, cmax, rows_hint(s, cmax), st);
-    }
-    SimtArgs a{};  // dpre = (dy . W2) * act'(pre); B(n=h, kk=m) = W2[e][m][h]
+    if (s.dtype == MOE_DT_BF16)
+        return bwd_data_launch<EPI_DACT>(s.act, dy, W2, dpre, H, M, E, fill, cap, pre, rows_hint(s, cmax), st);
+    SimtArgs a{};  // B(n=h, kk=m) = W2[e][m][h]
     a.A = static_cast<const float *>(dy); a.a_si = M; a.a_sk = 1; a.a_gfix = 0; a.a_gcap = M;
     a.B = static_cast<const float *>(W2); a.b_sn = 1; a.b_sk = H; a.b_gfix = static_cast<int64_t>(M) * H; a.b_gcap = 0;
     a.D = static_cast<float *>(dpre); a.d_si = H; a.d_gfix = 0; a.d_gcap = H;
     a.N = H; a.K = M; a.kgrouped = 0; a.fill = fill; a.cap = cap; a.aux = static_cast<const float *>(pre);
-    if ((err = simt_launch<EPI_DACT>(a, s.act, cmax, E, st)) != hipSuccess) return err;
+    return simt_launch<EPI_DACT>(a, s.act, cmax, E, st);
+}
+
+// dW2[e] = dy^T h (+ db2 = column sums of dy)
+hipError_t launch_fc2_wgrad(const moe_shape &s, const void *dy, const void *h, const int32_t *fill, const int32_t *cap,
+                            float *dW2, float *db2, int32_t cmax, hipStream_t st) {
+    const int M = s.M, H = s.H, E = s.E;
+    if (s.dtype == MOE_DT_BF16) return kgroup_launch(dy, h, dW2, M, H, E, fill, cap, db2, cmax, rows_hint(s, cmax), st);
     SimtArgs b{};  // dW2[e](m, h) = sum_j dy[j][m] h[j][h]
     b.A = static_cast<const float *>(dy); b.a_si = 1; b.a_sk = M; b.a_gfix = 0; b.a_gcap = M;
     b.B = static_cast<const float *>(h); b.b_sn = 1; b.b_sk = H; b.b_gfix = 0; b.b_gcap = H;
     b.D = dW2; b.d_si = H; b.d_gfix = static_cast<int64_t>(M) * H; b.d_gcap = 0;
     b.rows = M; b.N = H; b.kgrouped = 1; b.fill = fill; b.cap = cap; b.colsum = db2;
-    if ((err = simt_launch<EPI_PLAIN>(b, s.act, M, E, st)) != hipSuccess) return err;
-    SimtArgs c{};  // dbuf = dpre . W1; B(n=m, kk=h) = W1[e][h][m]
+    return simt_launch<EPI_PLAIN>(b, s.act, M, E, st);
+}
+
+// dbuf = dpre . W1[e]: B = W1[e] read as [K=H][N=M]
+hipError_t launch_fc1_bwd_data(const moe_shape &s, const void *dpre, const void *W1, const int32_t *fill,
+                               const int32_t *cap, void *dbuf, int32_t cmax, hipStream_t st) {
+    const int M = s.M, H = s.H, E = s.E;
+    if (s.dtype == MOE_DT_BF16)
+        return bwd_data_launch<EPI_PLAIN>(s.act, dpre, W1, dbuf, M, H, E, fill, cap, nullptr, rows_hint(s, cmax), st);
+    SimtArgs c{};  // B(n=m, kk=h) = W1[e][h][m]
     c.A = static_cast<const float *>(dpre); c.a_si = H; c.a_sk = 1; c.a_gfix = 0; c.a_gcap = H;
     c.B = static_cast<const float *>(W1); c.b_sn = 1; c.b_sk = M; c.b_gfix = static_cast<int64_t>(H) * M; c.b_gcap = 0;
     c.D = static_cast<float *>(dbuf); c.d_si = M; c.d_gfix = 0; c.d_gcap = M;
     c.N = M; c.K = H; c.kgrouped = 0; c.fill = fill; c.cap = cap;
-    if ((err = simt_launch<EPI_PLAIN>(c, s.act, cmax, E, st)) != hipSuccess) return err;
+    return simt_launch<EPI_PLAIN>(c, s.act, cmax, E, st);
+}
+
+// dW1[e] = dpre^T buf (+ db1 = column sums of dpre)
+hipError_t launch_fc1_wgrad(const moe_shape &s, const void *dpre, const void *buf, const int32_t *fill,
+                            const int32_t *cap, float *dW1, float *db1, int32_t cmax, hipStream_t st) {
+    const int M = s.M, H = s.H, E = s.E;
+    if (s.dtype == MOE_DT_BF16)
+        return kgroup_launch(dpre, buf, dW1, H, M, E, fill, cap, db1, cmax, rows_hint(s, cmax), st);
     SimtArgs d{};  // dW1[e](h, m) = sum_j dpre[j][h] buf[j][m]
     d.A = static_cast<const float *>(dpre); d.a_si = 1; d.a_sk = H; d.a_gfix = 0; d.a_gcap = H;
     d.B = static_cast<const float *>(buf); d.b_sn = 1; d.b_sk = M; d.b_gfix = 0; d.b_gcap = M;
     d.D = dW1; d.d_si = M; d.d_gfix = static_cast<int64_t>(H) * M; d.d_gcap = 0;
     d.rows = H; d.N = M; d.kgrouped = 1; d.fill = fill; d.cap = cap; d.colsum = db1;
     return simt_launch<EPI_PLAIN>(d, s.act, H, E, st);
+}
+
+// The FFN backward in the order that keeps operands cached: dW2 first, so that
+// dbuf runs right after dpre is written (dpre's rows are still in the last-level
+// cache); dbuf may alias dy, which is consumed by then.
+hipError_t launch_expert_ffn_bwd(const moe_shape &s, const void *buf, const void *pre, const void *h, const void *W1,
+                                 const void *W2, const int32_t *fill, const int32_t *cap, void *dy, void *dpre,
+                                 void *dbuf, float *dW1, float *db1, float *dW2, float *db2, int32_t cmax,
+                                 hipStream_t st) {
+    hipError_t err;
+    if ((err = launch_fc2_wgrad(s, dy, h, fill, cap, dW2, db2, cmax, st)) != hipSuccess) return err;
+    if ((err = launch_fc2_bwd_data(s, dy, W2, pre, fill, cap, dpre, cmax, st)) != hipSuccess) return err;
+    if ((err = launch_fc1_bwd_data(s, dpre, W1, fill, cap, dbuf, cmax, st)) != hipSuccess) return err;
+    return launch_fc1_wgrad(s, dpre, buf, fill, cap, dW1, db1, cmax, st);
 }
 
 }  // namespace moe

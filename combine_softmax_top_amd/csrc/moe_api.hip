@@ -608,6 +608,76 @@ moe_status moe_residual_layer_forward(const moe_shape *shape, const void *x, con
                               capacity, slot_route, buf, pre, h, y, out, ws, ws_bytes, &res, stream);
 }
 
+moe_status moe_decode_backward(const moe_shape *shape, const void *dout, const void *y, const float *gates,
+                               const int32_t *idx, const int32_t *loc, const int32_t *capacity, void *dy,
+                               float *dgates, void *stream) {
+    moe_status st = check_shape(shape);
+    if (st != MOE_OK) return st;
+    const moe_shape &s = *shape;
+    MOE_REQUIRE(capacity != nullptr, "capacity is NULL");
+    if (s.S > 0) MOE_REQUIRE(dout && y && gates && idx && loc && dy && dgates,
+                             "dout, y, gates, idx, loc, dy and dgates must be non-NULL");
+    MOE_REQUIRE_ALIGNED(dout, y, gates, idx, loc, capacity, dy, dgates);
+    hipError_t e = moe::launch_decode_bwd(s, dout, y, gates, idx, loc, capacity, dy, dgates, as_stream(stream));
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "decode backward");
+}
+
+moe_status moe_expert_fc2_backward_data(const moe_shape *shape, const void *dy, const void *W2, const void *pre,
+                                        const int32_t *fill, const int32_t *capacity, void *dpre, void *stream) {
+    moe_status st = check_shape(shape);
+    if (st != MOE_OK) return st;
+    MOE_REQUIRE(dy && W2 && pre && fill && capacity && dpre, "dy, W2, pre, fill, capacity and dpre must be non-NULL");
+    MOE_REQUIRE_ALIGNED(dy, W2, pre, fill, capacity, dpre);
+    hipError_t e = moe::launch_fc2_bwd_data(*shape, dy, W2, pre, fill, capacity, dpre,
+                                            static_cast<int32_t>(cap_bound(*shape)), as_stream(stream));
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "fc2 backward (data)");
+}
+
+moe_status moe_expert_fc2_weight_grad(const moe_shape *shape, const void *dy, const void *h, const int32_t *fill,
+                                      const int32_t *capacity, float *dW2, float *db2, void *stream) {
+    moe_status st = check_shape(shape);
+    if (st != MOE_OK) return st;
+    MOE_REQUIRE(dy && h && fill && capacity && dW2, "dy, h, fill, capacity and dW2 must be non-NULL");
+    MOE_REQUIRE_ALIGNED(dy, h, fill, capacity, dW2, db2);
+    hipError_t e = moe::launch_fc2_wgrad(*shape, dy, h, fill, capacity, dW2, db2,
+                                         static_cast<int32_t>(cap_bound(*shape)), as_stream(stream));
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "fc2 weight gradient");
+}
+
+moe_status moe_expert_fc1_backward_data(const moe_shape *shape, const void *dpre, const void *W1, const int32_t *fill,
+                                        const int32_t *capacity, void *dbuf, void *stream) {
+    moe_status st = check_shape(shape);
+    if (st != MOE_OK) return st;
+    MOE_REQUIRE(dpre && W1 && fill && capacity && dbuf, "dpre, W1, fill, capacity and dbuf must be non-NULL");
+    MOE_REQUIRE_ALIGNED(dpre, W1, fill, capacity, dbuf);
+    hipError_t e = moe::launch_fc1_bwd_data(*shape, dpre, W1, fill, capacity, dbuf,
+                                            static_cast<int32_t>(cap_bound(*shape)), as_stream(stream));
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "fc1 backward (data)");
+}
+
+moe_status moe_expert_fc1_weight_grad(const moe_shape *shape, const void *dpre, const void *buf, const int32_t *fill,
+                                      const int32_t *capacity, float *dW1, float *db1, void *stream) {
+    moe_status st = check_shape(shape);
+    if (st != MOE_OK) return st;
+    MOE_REQUIRE(dpre && buf && fill && capacity && dW1, "dpre, buf, fill, capacity and dW1 must be non-NULL");
+    MOE_REQUIRE_ALIGNED(dpre, buf, fill, capacity, dW1, db1);
+    hipError_t e = moe::launch_fc1_wgrad(*shape, dpre, buf, fill, capacity, dW1, db1,
+                                         static_cast<int32_t>(cap_bound(*shape)), as_stream(stream));
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "fc1 weight gradient");
+}
+
+moe_status moe_encode_backward(const moe_shape *shape, const void *dbuf, const int32_t *idx, const int32_t *loc,
+                               const int32_t *capacity, void *dx, void *stream) {
+    moe_status st = check_shape(shape);
+    if (st != MOE_OK) return st;
+    const moe_shape &s = *shape;
+    MOE_REQUIRE(capacity != nullptr, "capacity is NULL");
+    if (s.S > 0) MOE_REQUIRE(dbuf && idx && loc && dx, "dbuf, idx, loc and dx must be non-NULL");
+    MOE_REQUIRE_ALIGNED(dbuf, idx, loc, capacity, dx);
+    hipError_t e = moe::launch_decode(s, dbuf, nullptr, idx, loc, capacity, dx, true, as_stream(stream));
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "encode backward");
+}
+
 moe_status moe_layer_backward(const moe_shape *shape, const void *dout, const void *buf, const void *pre,
                               const void *h, const void *y, const float *gates, const int32_t *idx,
                               const int32_t *loc, const int32_t *fill, const int32_t *capacity, const void *W1,

@@ -242,6 +242,15 @@ hipError_t launch_expert_ffn_mx(const moe_shape &s, int wfmt, const uint8_t *buf
                                 const uint8_t *w2_codes, const uint8_t *w2_scales, const void *b2,
                                 const int32_t *fill, const int32_t *cap, uint8_t *h_codes, uint8_t *h_scales, void *y,
                                 int32_t cmax, hipStream_t st);
+// The FFN backward's four products (one kernel each), then all four in order.
+hipError_t launch_fc2_bwd_data(const moe_shape &s, const void *dy, const void *W2, const void *pre,
+                               const int32_t *fill, const int32_t *cap, void *dpre, int32_t cmax, hipStream_t st);
+hipError_t launch_fc2_wgrad(const moe_shape &s, const void *dy, const void *h, const int32_t *fill, const int32_t *cap,
+                            float *dW2, float *db2, int32_t cmax, hipStream_t st);
+hipError_t launch_fc1_bwd_data(const moe_shape &s, const void *dpre, const void *W1, const int32_t *fill,
+                               const int32_t *cap, void *dbuf, int32_t cmax, hipStream_t st);
+hipError_t launch_fc1_wgrad(const moe_shape &s, const void *dpre, const void *buf, const int32_t *fill,
+                            const int32_t *cap, float *dW1, float *db1, int32_t cmax, hipStream_t st);
 hipError_t launch_expert_ffn_bwd(const moe_shape &s, const void *buf, const void *pre, const void *h,
                                  const void *W1, const void *W2, const int32_t *fill,
                                  const int32_t *cap, void *dy, void *dpre, void *dbuf, float *dW1,

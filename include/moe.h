@@ -374,6 +374,32 @@ moe_status moe_layer_backward(const moe_shape *shape, const void *dout, const vo
                               double aux_coef, const void *x, const float *Wg, float *dlogits,
                               float *dWg, float *aux_loss, void *ws, size_t ws_bytes, void *stream);
 
+/* The stages of moe_layer_backward as calls of their own (same definitions,
+ * same buffers), for callers that schedule or time them separately:
+ *   moe_decode_backward           K1' and K2 (blog part 3 section 3.5): dy rows
+ *                                 of kept routes and dgates [k,S];
+ *   moe_expert_fc2_backward_data  dpre = (dy . W2[e]) * act'(pre), stored;
+ *   moe_expert_fc2_weight_grad    dW2[e] = sum_j dy_j^T h_j, db2 (may be NULL);
+ *   moe_expert_fc1_backward_data  dbuf = dpre . W1[e], stored;
+ *   moe_expert_fc1_weight_grad    dW1[e] = sum_j dpre_j^T buf_j, db1 (may be NULL);
+ *   moe_encode_backward           K0: dx[s] = sum of the token's kept dbuf rows
+ *                                 (fp32, route order), stored (no gate share).
+ * Every product covers the filled rows j < fill[e] of each expert. */
+moe_status moe_decode_backward(const moe_shape *shape, const void *dout, const void *y, const float *gates,
+                               const int32_t *idx, const int32_t *loc, const int32_t *capacity, void *dy,
+                               float *dgates, void *stream);
+moe_status moe_expert_fc2_backward_data(const moe_shape *shape, const void *dy, const void *W2, const void *pre,
+                                        const int32_t *fill, const int32_t *capacity, void *dpre, void *stream);
+moe_status moe_expert_fc2_weight_grad(const moe_shape *shape, const void *dy, const void *h, const int32_t *fill,
+                                      const int32_t *capacity, float *dW2, float *db2, void *stream);
+moe_status moe_expert_fc1_backward_data(const moe_shape *shape, const void *dpre, const void *W1,
+                                        const int32_t *fill, const int32_t *capacity, void *dbuf, void *stream);
+moe_status moe_expert_fc1_weight_grad(const moe_shape *shape, const void *dpre, const void *buf,
+                                      const int32_t *fill, const int32_t *capacity, float *dW1, float *db1,
+                                      void *stream);
+moe_status moe_encode_backward(const moe_shape *shape, const void *dbuf, const int32_t *idx, const int32_t *loc,
+                               const int32_t *capacity, void *dx, void *stream);
+
 /* Message of the last failing call on this thread ("" if none). */
 const char *moe_last_error(void);
 

@@ -15,8 +15,8 @@ import torch
 
 import oracle
 import workloads as W
-from tests.gpu_helpers import (check_close, check_dlogits, check_dwg, check_logits, dev, dgates_err, host, inputs_np,
-                               shape_of)
+from tests.gpu_helpers import (check_close, check_dlogits, check_dwg, check_logits, decode_extra, dev, dgates_err, host,
+                               inputs_np, shape_of)
 from tests.helpers import f32_of
 
 pytestmark = pytest.mark.gpu
@@ -159,11 +159,13 @@ def test_layer_backward_with_gate_matches_oracle(w):
                            w.S, moe.AUX_COEF, dg_err=dg_err)
     aux_g = float(host(gr["aux_loss"])[0])
     assert abs(aux_g - bw["aux_loss"]) <= AUX_REL * abs(bw["aux_loss"]), (aux_g, bw["aux_loss"])
-    extra = None
+    # dx sums the token's dbuf rows: the two sides' rows (each within tolerance) carried through
+    rows = fw["rows"]
+    extra = decode_extra(rt, rows, host(gr["dbuf"])[rows], bw["dbuf"], gated=False)
     if gate:
         check_dwg(host(gr["dWg"]), bw["dWg"], ni["x"], bw["dlogits"], w.dtype, dl_err=dl_err)
         # dx's gate share: the dlogits bound carried through |Wg|^T
-        extra = dl_err @ np.abs(ni["Wg"].astype(np.float64)).T
+        extra += dl_err @ np.abs(ni["Wg"].astype(np.float64)).T
     check_close(host(gr["dx"]), bw["dx"], w.dtype, "dx", extra=extra)
     check_close(host(gr["dW1"]), bw["dW1"], w.dtype, "dW1")
     check_close(host(gr["dW2"]), bw["dW2"], w.dtype, "dW2")

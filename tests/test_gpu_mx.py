@@ -17,7 +17,7 @@ import torch
 
 import oracle
 import workloads as W
-from tests.gpu_helpers import check_close, check_logits, compare_route, dev, host, inputs_np, shape_of
+from tests.gpu_helpers import check_close, check_logits, compare_route, decode_extra, dev, host, inputs_np, shape_of
 
 pytestmark = pytest.mark.gpu
 
@@ -138,21 +138,6 @@ def _y_extra(dh, rows, C, W2q, wfmt):
     return out
 
 
-def _out_extra(ey, rows, rt, S, M):
-    """The y bound carried through decode: sum over a token's kept routes of gate * bound."""
-    C = rt["C"]
-    pos = {int(r): i for i, r in enumerate(rows)}
-    out = np.zeros((S, M))
-    k = rt["idx"].shape[0]
-    for r in range(k):
-        for t in range(S):
-            if rt["loc"][r, t] < C:
-                i = pos.get(int(rt["idx"][r, t]) * C + int(rt["loc"][r, t]))
-                if i is not None:
-                    out[t] += abs(float(rt["gates"][r, t])) * ey[i]
-    return out
-
-
 @pytest.mark.parametrize("wfmt", FMTS)
 @pytest.mark.parametrize("w", MXW, ids=lambda w: w.name)
 def test_expert_ffn_mx_matches_oracle(w, wfmt):
@@ -215,11 +200,12 @@ def test_layer_forward_mx_matches_oracle(w, wfmt):
     dh = _check_h(host(b["h_codes"][ridx]), host(b["h_scales"][ridx]), hq_o, "h",
                   _pre_slack(bufq, W1q, rows, C, wfmt, w.act))
     ey = _y_extra(dh, rows, C, W2q, wfmt)
-    check_close(host(b["y"][ridx]), y_o, w.dtype, "y", extra=ey)
+    yg = host(b["y"][ridx])
+    check_close(yg, y_o, w.dtype, "y", extra=ey)
     y_full = np.zeros((w.E * C, w.M), np.uint16)
     y_full[rows] = y_o
     out_o = oracle.decode(y_full, rt, w.E, w.dtype)
-    check_close(host(b["out"]), out_o, w.dtype, "out", extra=_out_extra(ey, rows, rt, w.S, w.M))
+    check_close(host(b["out"]), out_o, w.dtype, "out", extra=decode_extra(rt, rows, yg, y_o))
 
 
 @pytest.mark.parametrize("wfmt", FMTS)
@@ -255,9 +241,10 @@ def test_mx_full_size_gated_layer(wfmt):
     dh = _check_h(host(b["h_codes"][ridx]), host(b["h_scales"][ridx]), hq_o, "h (sampled rows)",
                   _pre_slack(bufq, W1q, rows, C, wfmt, w.act))
     ey = _y_extra(dh, rows, C, W2q, wfmt)
-    check_close(host(b["y"][ridx]), y_o, w.dtype, "y (sampled rows)", extra=ey)
+    yg = host(b["y"][ridx])
+    check_close(yg, y_o, w.dtype, "y (sampled rows)", extra=ey)
     y_full = np.zeros((w.E * C, w.M), np.uint16)
     y_full[rows] = y_o
     out_o = oracle.decode(y_full, rt, w.E, w.dtype, tokens=toks)
-    eo = _out_extra(ey, rows, rt, w.S, w.M)[toks]
+    eo = decode_extra(rt, rows, yg, y_o, tokens=toks)
     check_close(host(b["out"][torch.from_numpy(toks).cuda()]), out_o, w.dtype, "out (sampled tokens)", extra=eo)

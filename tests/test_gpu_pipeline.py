@@ -11,7 +11,7 @@ import torch
 
 import oracle
 import workloads as W
-from tests.gpu_helpers import check_close, host, inputs_np, shape_of
+from tests.gpu_helpers import check_close, decode_extra, host, inputs_np, shape_of
 
 pytestmark = pytest.mark.gpu
 
@@ -76,4 +76,6 @@ def test_pipelined_forward_equals_fused(w, chunks, nstreams):
     assert np.array_equal(host(b["out"]).view(np.uint16), host(ref["out"]).view(np.uint16))
     ni = inputs_np(inp)
     fw = oracle.layer_forward(ni, w.k, w.capacity_factor, w.act, w.dtype)
-    check_close(host(b["out"]), fw["out"], w.dtype, "out")
+    rows = fw["rows"]
+    check_close(host(b["out"]), fw["out"], w.dtype, "out",
+                extra=decode_extra(fw["route"], rows, host(b["y"])[rows], fw["y"][rows]))

@@ -9,7 +9,8 @@ import torch
 
 import oracle
 import workloads as W
-from tests.gpu_helpers import check_close, dev, host, inputs_np, shape_of
+from tests.gpu_helpers import check_close, check_logits, decode_extra, dev, host, inputs_np, shape_of
+from tests.helpers import f32_of
 
 pytestmark = pytest.mark.gpu
 
@@ -88,12 +89,22 @@ def test_residual_layer_forward_matches_oracle(w):
                           Wg=d.get("Wg"), residual=res)
     torch.cuda.synchronize()
     ni = inputs_np(inp)
-    fw = oracle.layer_forward(ni, w.k, w.capacity_factor, w.act, w.dtype)
+    glog = None
+    if w.logits == "gate":
+        # the projection within its fp32 bound; the oracle routes on the GPU's logits
+        glog = host(b["logits"])
+        check_logits(glog, oracle.gate_logits(ni["x"], ni["Wg"], w.dtype), ni["x"], ni["Wg"])
+    fw = oracle.layer_forward(ni, w.k, w.capacity_factor, w.act, w.dtype, logits=glog)
     rt = fw["route"]
     assert int(b["capacity"].item()) == rt["C"]
     assert np.array_equal(host(b["idx"]), rt["idx"]) and np.array_equal(host(b["loc"]), rt["loc"])
-    check_close(host(b["y_r"]), fw["y_r"], w.dtype, "y_r")
-    check_close(host(b["out"]), fw["out"], w.dtype, "out")
+    yr_g = host(b["y_r"])
+    check_close(yr_g, fw["y_r"], w.dtype, "y_r")
+    # the end-to-end output: the two sides' y and y_r rows (each within tolerance) carried through decode
+    rows = fw["rows"]
+    extra = decode_extra(rt, rows, host(b["y"])[rows], fw["y"][rows])
+    extra += np.abs(f32_of(yr_g).astype(np.float64) - f32_of(fw["y_r"]).astype(np.float64))
+    check_close(host(b["out"]), fw["out"], w.dtype, "out", extra=extra)
     # given the GPU's own expert outputs and dense rows, the residual decode is exact
     want = oracle.decode(host(b["y"][: w.E * rt["C"]]), rt, w.E, w.dtype, yres=host(b["y_r"]))
     assert np.array_equal(host(b["out"]).view(np.uint8), want.view(np.uint8))

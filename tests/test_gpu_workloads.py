@@ -25,7 +25,8 @@ import torch
 
 import oracle
 import workloads as W
-from tests.gpu_helpers import check_close, check_dlogits, check_dwg, check_logits, compare_route, dgates_err, host
+from tests.gpu_helpers import (check_close, check_dlogits, check_dwg, check_logits, compare_route, decode_extra,
+                               dgates_err, host)
 from tests.helpers import f32_of
 
 pytestmark = pytest.mark.gpu
@@ -116,7 +117,12 @@ def test_full_size_workload(w):
         yres = np.zeros((w.S, w.M), yr_o.dtype)
         yres[toks] = yr_o
     out_o = oracle.decode(y_full, rt, w.E, w.dtype, tokens=toks, yres=yres)
-    check_close(host(b["out"][torch.from_numpy(toks).cuda()]), out_o, w.dtype, "out tokens")
+    # the end-to-end output: the two sides' y rows (each within tolerance) carried through decode
+    extra = decode_extra(rt, all_rows, gy, y_o, tokens=toks)
+    if w.residual:
+        extra += np.abs(f32_of(host(b["y_r"][torch.from_numpy(toks).cuda()])).astype(np.float64)
+                        - f32_of(yr_o).astype(np.float64))
+    check_close(host(b["out"][torch.from_numpy(toks).cuda()]), out_o, w.dtype, "out tokens", extra=extra)
     _say(f"[{w.name}] FFN rows and {ntok} output tokens within tolerance")
 
     if not w.backward:
@@ -162,10 +168,13 @@ def test_full_size_workload(w):
     q, _, _, dbuf_o = oracle.backward_rows(fw, ni, dx_rows, w.act, w.dtype, want_dy=False, want_dpre=False)
     dx_o = oracle.dx_tokens(q, dbuf_o, dx_toks, w.S, w.k, w.dtype, dlogits=dl_o if gate else None,
                             Wg=ni.get("Wg"))
-    extra = None
+    # dx sums the token's dbuf rows: the two sides' rows (each within tolerance) carried through
+    srt = np.argsort(dx_rows)
+    extra = decode_extra(rt, dx_rows[srt], host(gr["dbuf"][torch.from_numpy(dx_rows[srt]).cuda()]), dbuf_o[srt],
+                         tokens=dx_toks, gated=False)
     if gate:
         # dx's gate share: the dlogits bound carried through |Wg|^T
-        extra = dl_err[dx_toks] @ np.abs(ni["Wg"].astype(np.float64)).T
+        extra += dl_err[dx_toks] @ np.abs(ni["Wg"].astype(np.float64)).T
     check_close(host(gr["dx"][torch.from_numpy(dx_toks).cuda()]), dx_o, w.dtype, "dx (sampled)", extra=extra)
     _say(f"[{w.name}] dgates on {len(routes)} routes and dx on {len(dx_toks)} tokens within tolerance")
     order = np.argsort(fill)
