@@ -104,6 +104,7 @@ _SIGS = {
     "moe_expert_fc1_backward_data": [_SP] + [_P] * 6,
     "moe_expert_fc1_weight_grad": [_SP] + [_P] * 7,
     "moe_encode_backward": [_SP] + [_P] * 6,
+    "moe_layer_forward_noalloc": [_SP] + [_P] * 21,
 }
 
 # coefficient of the auxiliary load-balance loss in the MoE training blog's runs
@@ -343,6 +344,14 @@ def moe_layer_forward(shape: Shape, x, logits_in, Wg, logits_out, W1, b1, W2, b2
         _ptr(b2), _ptr(idx), _ptr(loc), _ptr(gates), _ptr(needed), _ptr(fill), _ptr(capacity), _ptr(slot_route),
         _ptr(buf), _ptr(pre), _ptr(h), _ptr(y), _ptr(out), _ptr(ws),
         0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def moe_layer_forward_noalloc(shape: Shape, x, logits_in, Wg, logits_out, W1, b1, W2, b2, idx, loc, gates, needed,
+                              fill, capacity, slot_route, buf, pre, h, y, out, stream=None) -> None:
+    _check(_lib.moe_layer_forward_noalloc(
+        ctypes.byref(shape.c()), _ptr(x), _ptr(logits_in), _ptr(Wg), _ptr(logits_out), _ptr(W1), _ptr(b1), _ptr(W2),
+        _ptr(b2), _ptr(idx), _ptr(loc), _ptr(gates), _ptr(needed), _ptr(fill), _ptr(capacity), _ptr(slot_route),
+        _ptr(buf), _ptr(pre), _ptr(h), _ptr(y), _ptr(out), _stream(stream)))
 
 
 def moe_layer_backward(shape: Shape, dout, buf, pre, h, y, gates, idx, loc, fill, capacity, W1, W2, dy, dpre, dbuf,

@@ -5,6 +5,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "moe_internal.h"
@@ -56,19 +57,31 @@ int64_t cap_bound(const moe_shape &s) {
 
 int32_t num_tiles(const moe_shape &s) { return (s.S + moe::kRouteTile - 1) / moe::kRouteTile; }
 
+// Workspace of routing and the forwards: routing's per-tile route counts; the
+// Residual-MoE branch reuses 8 bytes of it after routing.
+size_t forward_ws_bytes(const moe_shape &s) {
+    const size_t n = static_cast<size_t>(s.E) * s.k * num_tiles(s);
+    return std::max<size_t>(256, ((n * sizeof(int32_t)) + 255) & ~static_cast<size_t>(255));
+}
+
 // One workspace serves routing (per-tile route counts) and the gate backward
 // (auxiliary-loss partials and dWg slice partials); they are never live together.
 size_t ws_bytes_needed(const moe_shape &s) {
-    const size_t n = static_cast<size_t>(s.E) * s.k * num_tiles(s);
-    const size_t route = ((n * sizeof(int32_t)) + 255) & ~static_cast<size_t>(255);
-    return std::max(route, moe::gate_grad_ws_bytes(s.S, s.M, s.E));
+    return std::max(forward_ws_bytes(s), moe::gate_grad_ws_bytes(s.S, s.M, s.E));
 }
 
-moe_status check_ws(const moe_shape &s, const void *ws, size_t ws_bytes) {
-    const size_t need = ws_bytes_needed(s);
+moe_status check_ws_bytes(const void *ws, size_t ws_bytes, size_t need) {
     if (need > 0 && (ws == nullptr || ws_bytes < need))
         return fail(MOE_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws == nullptr ? 0 : ws_bytes);
     return MOE_OK;
+}
+
+moe_status check_forward_ws(const moe_shape &s, const void *ws, size_t ws_bytes) {
+    return check_ws_bytes(ws, ws_bytes, forward_ws_bytes(s));
+}
+
+moe_status check_ws(const moe_shape &s, const void *ws, size_t ws_bytes) {
+    return check_ws_bytes(ws, ws_bytes, ws_bytes_needed(s));
 }
 
 moe_status check_shape(const moe_shape *sp) {
@@ -485,7 +498,7 @@ moe_status layer_forward_impl(const moe_shape *shape, const void *x, const float
             return fail(MOE_EUNSUPPORTED, "S=%d too large for the dense branch's GEMM grid", s.S);
         MOE_REQUIRE_ALIGNED(res->W1r, res->b1r, res->W2r, res->b2r, res->h_r, res->y_r);
     }
-    if ((st = check_ws(s, ws, ws_bytes)) != MOE_OK) return st;
+    if ((st = check_forward_ws(s, ws, ws_bytes)) != MOE_OK) return st;
     MOE_REQUIRE_ALIGNED(x, logits_in, Wg, logits_out, W1, b1, W2, b2, idx, loc, gates, needed, fill, capacity,
                         slot_route, buf, pre, h, y, out, ws);
     if (Wg != nullptr && !moe::gate_supported(s.M, s.E, s.dtype))
@@ -729,5 +742,71 @@ moe_status moe_layer_backward(const moe_shape *shape, const void *dout, const vo
 }
 
 const char *moe_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"
+
+// ---------------------------------------------------------------- the forward without allocation
+// moe_layer_forward_noalloc keeps routing's workspace in this array instead of a
+// caller buffer. Each GPU the library runs on holds its own copy of it, at its own
+// address, until the process ends; every call on a GPU shares that GPU's copy.
+// Routing writes every count it later reads, so nothing in it has to start at zero.
+namespace {
+
+constexpr size_t kNoAllocScratchBytes = size_t(4) << 20;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_addr[kMaxDevices];  // device address of `scratch` per device, once looked up
+
+// The device address of `scratch` on the device of `stream` (the current device for
+// NULL), looked up once per device with that device current. Host code uses only
+// this address: the array's name is a host-side stand-in, not a device pointer.
+moe_status scratch_address(hipStream_t stream, void **addr) {
+    int dev = -1;
+    hipError_t e = stream != nullptr ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "device of the stream");
+    if (dev < 0 || dev >= kMaxDevices) return fail(MOE_EUNSUPPORTED, "device %d beyond the %d supported", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_addr[dev] == nullptr) {
+        int cur = -1;
+        if ((e = hipGetDevice(&cur)) != hipSuccess) return hip_fail(e, "current device");
+        if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return hip_fail(e, "set device");
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != dev) {
+            const hipError_t e2 = hipSetDevice(cur);
+            if (e == hipSuccess && e2 != hipSuccess) e = e2;
+        }
+        if (e != hipSuccess) return hip_fail(e, "address of the static scratch");
+        if (p == nullptr) return fail(MOE_EHIP, "address of the static scratch is NULL");
+        g_scratch_addr[dev] = p;
+    }
+    *addr = g_scratch_addr[dev];
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_layer_forward_noalloc(const moe_shape *shape, const void *x, const float *logits_in, const float *Wg,
+                                     float *logits_out, const void *W1, const void *b1, const void *W2,
+                                     const void *b2, int32_t *idx, int32_t *loc, float *gates, int32_t *needed,
+                                     int32_t *fill, int32_t *capacity, int32_t *slot_route, void *buf, void *pre,
+                                     void *h, void *y, void *out, void *stream) {
+    moe_status st = check_shape(shape);
+    if (st != MOE_OK) return st;
+    const size_t need = forward_ws_bytes(*shape);
+    if (need > kNoAllocScratchBytes)
+        return fail(MOE_EUNSUPPORTED,
+                    "routing needs %zu bytes of workspace (E*k*ceil(S/64) counts), above the %zu-byte static scratch "
+                    "of moe_layer_forward_noalloc: use moe_layer_forward with a workspace",
+                    need, kNoAllocScratchBytes);
+    void *ws = nullptr;
+    if ((st = scratch_address(as_stream(stream), &ws)) != MOE_OK) return st;
+    return layer_forward_impl(shape, x, logits_in, Wg, logits_out, W1, b1, W2, b2, idx, loc, gates, needed, fill,
+                              capacity, slot_route, buf, pre, h, y, out, ws, kNoAllocScratchBytes, nullptr, stream);
+}
 
 }  // extern "C"

@@ -312,6 +312,23 @@ moe_status moe_layer_forward(const moe_shape *shape, const void *x, const float 
                              int32_t *slot_route, void *buf, void *pre, void *h, void *y, void *out,
                              void *ws, size_t ws_bytes, void *stream);
 
+/* moe_layer_forward for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments, results and kernels without the workspace.
+ * Routing's counts go to a static scratch array of the library, 4 MiB per GPU
+ * (held until the process ends), so shapes with E * k * ceil(S / 64) above
+ * 1048576 counts return MOE_EUNSUPPORTED, enqueuing nothing. The call makes no
+ * allocation of any kind. Every call on one GPU shares that GPU's scratch:
+ * calls that may overlap on one GPU (different streams, or several host
+ * threads) race and must be ordered by the caller; moe_layer_forward with
+ * workspaces of their own does not have this limit. The first call on a
+ * device looks up the scratch's address (not an allocation). */
+moe_status moe_layer_forward_noalloc(const moe_shape *shape, const void *x, const float *logits_in,
+                                     const float *Wg, float *logits_out, const void *W1, const void *b1,
+                                     const void *W2, const void *b2, int32_t *idx, int32_t *loc, float *gates,
+                                     int32_t *needed, int32_t *fill, int32_t *capacity, int32_t *slot_route,
+                                     void *buf, void *pre, void *h, void *y, void *out, void *stream);
+
 /* moe_layer_forward of a Residual-MoE layer: the same steps, plus the dense
  * branch (moe_residual_ffn: W1r, b1r, W2r, b2r -> h_r, y_r) before decode,
  * and decode as moe_decode_residual. Forward only. */

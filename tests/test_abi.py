@@ -32,7 +32,7 @@ def odd_ptr():
 
 def test_every_declared_symbol_is_exported(moe):
     names = _declared()
-    assert len(names) == 32, names
+    assert len(names) == 33, names
     lib = ctypes.CDLL(moe.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -136,3 +136,14 @@ def test_entry_points_reject_before_enqueueing(moe):
     assert st == moe.MOE_EINVAL and "aligned" in moe.moe_last_error()
     st = lib.moe_expert_fc2(ctypes.byref(c), fake, fake, fake, fake, fake, odd, None)
     assert st == moe.MOE_EINVAL and "aligned" in moe.moe_last_error()
+
+
+def test_noalloc_forward_rejects_before_enqueueing(moe):
+    # beyond the static scratch (E*k*ceil(S/64) = 512*32*65 counts > 4 MiB): rejected on the
+    # host, before the device is touched
+    s = moe.Shape(S=64 * 65, M=64, E=512, k=32, H=64, capacity_factor=1.0)
+    fake = ctypes.c_void_p(0x1000)
+    st = moe._lib.moe_layer_forward_noalloc(ctypes.byref(s.c()), fake, fake, None, None, *([fake] * 16), None)
+    assert st == moe.MOE_EUNSUPPORTED and "static scratch" in moe.moe_last_error()
+    st = moe._lib.moe_layer_forward_noalloc(None, *([fake] * 20), None)
+    assert st == moe.MOE_EINVAL
