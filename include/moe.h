@@ -113,9 +113,7 @@ moe_status moe_workspace_size(const moe_shape *shape, size_t *bytes_host);
  * sum_m |x[s][m] Wg[m][e]|, gamma_n = n 2^-24 / (1 - n 2^-24)). The summation
  * order is fixed, so the logits (on which routing decisions are taken) are
  * reproducible bit for bit from run to run; routing itself is exact given them.
- * x [S, M] data type, Wg [M, E] fp32 row-major, logits [S, E] fp32.
- * Supported for M <= 12288 with bf16 x and M <= 7680 with fp32 x (the LDS tiles
- * must fit; MOE_EUNSUPPORTED otherwise, also from moe_layer_forward with Wg). */
+ * x [S, M] data type, Wg [M, E] fp32 row-major, logits [S, E] fp32. */
 moe_status moe_gate_project(const moe_shape *shape, const void *x, const float *Wg, float *logits,
                             void *stream);
 

@@ -60,8 +60,11 @@ MXW = [
 ]
 
 
-def _oracle_mx(w, ni, wfmt):
-    logits = ni["logits"] if "logits" in ni else oracle.gate_logits(ni["x"], ni["Wg"], w.dtype)
+def _oracle_mx(w, ni, wfmt, logits=None):
+    """The oracle's routing, encode and MX operands; a gate-projected workload routes on the given
+    (GPU-exported) logits."""
+    if logits is None:
+        logits = ni["logits"] if "logits" in ni else oracle.gate_logits(ni["x"], ni["Wg"], w.dtype)
     rt = oracle.route(logits, w.k, w.capacity_factor)
     buf = oracle.encode(ni["x"], rt, w.E, w.dtype)
     bufq = oracle.mx_quantize(buf, oracle.MX_FP8, w.dtype)
@@ -180,7 +183,6 @@ def test_layer_forward_mx_matches_oracle(w, wfmt):
     print(f"[mx layer] {w.name} wfmt={wfmt}", flush=True)
     inp = W.make_inputs(w, seed=0)
     ni = inputs_np(inp)
-    logits, rt, bufq, W1q, W2q = _oracle_mx(w, ni, wfmt)
     s = shape_of(w)
     d = {k_: v.cuda() for k_, v in inp.items()}
     W1g = moe.mx_quantize_weights(d["W1"], wfmt)
@@ -188,6 +190,11 @@ def test_layer_forward_mx_matches_oracle(w, wfmt):
     b = moe.layer_forward_mx(s, wfmt, d["x"], W1g, d.get("b1"), W2g, d.get("b2"), logits=d.get("logits"),
                              Wg=d.get("Wg"))
     torch.cuda.synchronize()
+    glog = None
+    if "Wg" in ni:  # the projection within its fp32 bound; the oracle routes on the GPU's logits
+        glog = host(b["logits"])
+        check_logits(glog, oracle.gate_logits(ni["x"], ni["Wg"], w.dtype), ni["x"], ni["Wg"])
+    logits, rt, bufq, W1q, W2q = _oracle_mx(w, ni, wfmt, logits=glog)
     assert np.array_equal(host(W1g[0]), W1q[0]) and np.array_equal(host(W1g[1]), W1q[1])
     C = rt["C"]
     g = dict(idx=host(b["idx"]), loc=host(b["loc"]), gates=host(b["gates"]), needed=host(b["needed"]),
