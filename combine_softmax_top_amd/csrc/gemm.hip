@@ -259,6 +259,40 @@ __global__ __launch_bounds__(NT) void rows_gemm_bf16(const bf16_t *__restrict__ 
 // or columns that are never stored.
 
 typedef __attribute__((address_space(3))) void lds_void_t;
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+
+// Direct global->LDS loads, 16 bytes per lane (lane l's chunk lands at LDS byte
+// M0 + 16 l), issued from inline asm rather than through the compiler's
+// builtins. After a builtin direct load the compiler cannot tell that a
+// transposing LDS read (ds_read_b64_tr_b16) does not touch the LDS being
+// filled, and makes that read wait for every outstanding vector-memory
+// operation: the loads of the next ring stage, meant to stay in flight for a
+// whole stage, were waited for at every K step of the products that read an
+// operand n-contiguous (plain 16-byte LDS reads get no such wait). The kernels
+// order every stage themselves (each wavefront waits for its own loads, then a
+// workgroup barrier, before a stage is read), so the compiler need not see
+// these loads. The LDS destination goes to M0; gfx9-family parts need one
+// wait state between an M0 write and a direct load reading it (s_nop 0).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"  // m0 is a reserved register; the clobber is declared anyway
+__device__ __forceinline__ uint32_t lds_m0(const void *lds_dst) {
+    return __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void_t *)lds_dst)));
+}
+// global_load_lds_dwordx4 from base (uniform) + voff_bytes (per lane)
+__device__ __forceinline__ void dma16(const void *base, uint32_t voff_bytes, const void *lds_dst) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :
+                 : "s"(lds_m0(lds_dst)), "v"(voff_bytes), "s"(base)
+                 : "memory", "m0");
+}
+// buffer_load_dwordx4 ... lds through a raw buffer resource (loads past its range return zero)
+__device__ __forceinline__ void dma16_buf(i32x4_t rsrc, uint32_t voff_bytes, const void *lds_dst) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(lds_m0(lds_dst)), "v"(voff_bytes), "s"(rsrc)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
 
 // 16-byte chunk slot of logical chunk c of row r in a tile whose rows hold KB
 // bf16 (KB/8 chunks). The LDS serves 16 lanes of a 16-byte read per cycle over
@@ -286,7 +320,7 @@ __device__ __forceinline__ void dma_tile(const bf16_t *base, int64_t ld, int row
         const int src_row = row < rows_valid ? row : rows_valid - 1;
         // uniform base + 32-bit lane offset (a tile spans well under 2^31 elements)
         const uint32_t off = static_cast<uint32_t>(src_row * static_cast<int>(ld) + kc * 8);
-        __builtin_amdgcn_global_load_lds(base + k0 + off, (lds_void_t *)(lds + rb * KB), 16, 0, 0);
+        dma16(base + k0, off * 2, lds + rb * KB);
     }
 }
 
@@ -307,8 +341,7 @@ __device__ __forceinline__ void dma_tile_mn(const bf16_t *base, int64_t ld, int 
         const int row = rb + lane / CPR;
         const int c = min((lane % CPR) ^ (4 * (row & 3)), cols_valid / 8 - 1);  // chunk stored at this slot
         const uint32_t off = static_cast<uint32_t>(row * static_cast<int>(ld) + c * 8);
-        __builtin_amdgcn_global_load_lds(base + static_cast<int64_t>(k0) * ld + off, (lds_void_t *)(lds + rb * BN),
-                                         16, 0, 0);
+        dma16(base + static_cast<int64_t>(k0) * ld, off * 2, lds + rb * BN);
     }
 }
 
@@ -638,7 +671,9 @@ __global__ __launch_bounds__(NTH, (big_lds_bytes<BM, BN>() * 2 <= 160 * 1024 ? 2
     const int nx = (N + BN - 1) / BN;
     const TileSched sc = wave_sched(fill, E, BM, nx, s0, s1);
     const int C = *cap;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // the wavefront index as a scalar: the tile offsets and LDS addresses derived
+    // from it stay in SGPRs rather than taking VGPRs from the accumulators
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wr0 = (wave / WGC) * (BM / WR), wc0 = (wave % WGC) * (BN / WGC);
     const int nk = K / KB;
     for (int L = sc.first; L < sc.end; L += sc.stride) {
@@ -777,8 +812,7 @@ __global__ __launch_bounds__(NTH, (big_lds_bytes<BM, BN>() * 2 <= 160 * 1024 ? 2
                 const int c = min(epi_swz<CH>(r, lane % CH), cols_valid / 8 - 1);  // chunk stored at this slot
                 const int rr = min(r, rows_valid - 1);
                 const uint32_t off = static_cast<uint32_t>(rr * N + c * 8);
-                __builtin_amdgcn_global_load_lds(aux + grow0 * N + col0 + off, (lds_void_t *)(lds + rb * BN), 16, 0,
-                                                 0);
+                dma16(aux + grow0 * N + col0, off * 2, lds + rb * BN);
             }
             wait_vmcnt<0>();
             barrier_keep_loads();
@@ -924,7 +958,7 @@ __global__ __launch_bounds__(NTH, 1) void rows_gemm_mx(const uint8_t *__restrict
     const int nx = (N + BN - 1) / BN;
     const TileSched sc = make_sched<NTH>(fill, E, BM, nx, prefix);
     const int C = *cap;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5;
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6), h = lane >> 5;
     const int wr0 = (wave / WGC) * (BM / 2), wc0 = (wave % WGC) * (BN / WGC);
     const int nk = K / kMxStageK, KS = K / 32;  // stages, scale bytes per row
     const int ldA = K / 2, ldB = FP4 ? K / 4 : K / 2;   // row length in bf16 units
@@ -1180,7 +1214,7 @@ __global__ __launch_bounds__(NTH, 1) void rows_gemm_mx(const uint8_t *__restrict
 // XCD-contiguous ranges. The bias gradient is summed from the X fragments of
 // the first column tile.
 template <int BN, int KB, int NW>
-__device__ __forceinline__ void buf_tile_mn(__amdgpu_buffer_rsrc_t rs, int ld, int cols_valid, int k0, bf16_t *lds,
+__device__ __forceinline__ void buf_tile_mn(i32x4_t rs, int ld, int cols_valid, int k0, bf16_t *lds,
                                             int wave, int lane) {
     constexpr int CPR = BN / 8;   // chunks per k row
     constexpr int RPI = 64 / CPR; // k rows per wavefront instruction
@@ -1191,13 +1225,17 @@ __device__ __forceinline__ void buf_tile_mn(__amdgpu_buffer_rsrc_t rs, int ld, i
         const int row = rb + lane / CPR;
         const int c = min((lane % CPR) ^ (4 * (row & 3)), cols_valid / 8 - 1);  // chunk stored at this slot
         const int voff = ((k0 + row) * ld + c * 8) * 2;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t *)(lds + rb * BN), 16, voff, 0, 0, 0);
+        dma16_buf(rs, static_cast<uint32_t>(voff), lds + rb * BN);
     }
 }
 
-// Raw buffer over [base, base + bytes): loads past the end return zero.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const bf16_t *base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t *>(base), 0, static_cast<int>(bytes), 0x00020000);
+// Raw buffer resource over [base, base + bytes): loads past the end return zero.
+// Words: base address (low 32 bits; high 16 bits with stride 0), the range in
+// bytes, and the flags word 0x00020000.
+__device__ __forceinline__ i32x4_t raw_rsrc(const bf16_t *base, uint32_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    return i32x4_t{static_cast<int>(static_cast<uint32_t>(a)), static_cast<int>(static_cast<uint32_t>(a >> 32) & 0xFFFFu),
+                   static_cast<int>(bytes), 0x00020000};
 }
 
 // First tile of the weight-gradient tile list (expert-major, per_e tiles per
@@ -1273,7 +1311,9 @@ __global__ __launch_bounds__(NTH, (4 * (BM + BN) * kBigKB * 2 <= 160 * 1024 ? 2 
     const int start = kgrad_cut(fill, E, per_e, KB, work * x / kXcds);
     const int end = kgrad_cut(fill, E, per_e, KB, work * (x + 1) / kXcds);
     const int C = *cap;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // the wavefront index as a scalar: the tile offsets and LDS addresses derived
+    // from it stay in SGPRs rather than taking VGPRs from the accumulators
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wr0 = (wave / WGC) * (BM / 2), wc0 = (wave % WGC) * (BN / WGC);
     for (int L = start + static_cast<int>(blockIdx.x) / kXcds; L < end; L += nb) {
         const int e = L / per_e, u = L - e * per_e;
@@ -1287,8 +1327,8 @@ __global__ __launch_bounds__(NTH, (4 * (BM + BN) * kBigKB * 2 <= 160 * 1024 ? 2 
         const int rows = fill[e];
         const int nk = (rows + KB - 1) / KB;
         const int64_t r0 = static_cast<int64_t>(e) * C;
-        const __amdgpu_buffer_rsrc_t rx = raw_rsrc(X + r0 * P + p0, static_cast<uint32_t>((rows * P - p0) * 2));
-        const __amdgpu_buffer_rsrc_t ry = raw_rsrc(Y + r0 * Q + q0, static_cast<uint32_t>((rows * Q - q0) * 2));
+        const i32x4_t rx = raw_rsrc(X + r0 * P + p0, static_cast<uint32_t>((rows * P - p0) * 2));
+        const i32x4_t ry = raw_rsrc(Y + r0 * Q + q0, static_cast<uint32_t>((rows * Q - q0) * 2));
         const bool col_sums = colsum != nullptr && qt == 0 && (wave % WGC) == 0;
 
         f32x16 acc[TM][TN];
