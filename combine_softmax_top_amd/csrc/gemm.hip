@@ -493,11 +493,13 @@ constexpr int big_lds_bytes() {
 constexpr int kXcds = 8;
 constexpr int kGroupM = 4;
 // Weight gradients with 256 x 256 tiles walk output tiles in groups of
-// kGroupKgrad row tiles (128 x 128 tiles keep kGroupM). Measured
-// at S=32768, M=4096, E=128, k=8 over group sizes 1..16 (256 x 256 tiles): dW2
-// (16 x 6 tiles per expert) 4.11 -> 3.89 ms and dW1 (6 x 16) 3.90 -> 3.69 ms
-// going from 4 to 6; the row-grouped products change by under 2% with any size.
-constexpr int kGroupKgrad = 6;
+// kGroupKgrad row tiles (128 x 128 tiles keep kGroupM). Measured at S=32768,
+// M=4096, E=128, k=8 (256 x 256 tiles, ms): dW2 (16 x 6 tiles per expert) 3.49 /
+// 3.51 / 3.41 / 3.50 / 3.64 / 3.55 / 3.63 for groups of 1 / 2 / 3 / 4 / 6 / 8 / 16,
+// dW1 (6 x 16) 3.98 / 3.99 / 3.18 / 3.36 / 3.14 / 3.11 / 3.10: a group of 3
+// keeps the first and splits the second's 6 row tiles evenly. The row-grouped
+// products change by under 2% with group sizes 2 to 8.
+constexpr int kGroupKgrad = 3;
 
 struct TileSched {
     int T;        // total tiles
