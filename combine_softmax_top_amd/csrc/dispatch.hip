@@ -368,7 +368,7 @@ __global__ __launch_bounds__(kThreads) void decode_bwd_kernel(const uint4 *__res
 // configuration": the gate scores each token against the E experts). An
 // HBM-bound product: x is read once; the small Wg is staged in LDS.
 // A workgroup takes 16 tokens (TPW per wavefront) and one chunk of 8 experts.
-// It stages Wg's rows for those experts, GM rows at a time, in LDS (every load
+// It stages Wg's rows for those experts, kGateRows rows at a time, in LDS (every load
 // of a pass issued together); lane l owns the 16-byte chunks c = l, l + 64, ...
 // of its tokens' rows (VE elements each) and keeps TPW * 8 fp32 sums, each taken
 // over its chunks in increasing m with fused multiply-adds; the wavefront then
