@@ -77,16 +77,17 @@ def parse():
 
 # HBM traffic of the dominant kernel comes from two counter runs (FETCH_SIZE, then
 # WRITE_SIZE) recorded in profiles/traffic_<stage>_<workload>.md together with the
-# sha256 of the kernel sources they were taken on; it is reported only while those
-# sources are unchanged.
-TRAFFIC_SOURCES = ("combine_softmax_top_amd/csrc/gemm.hip", "combine_softmax_top_amd/csrc/dispatch.hip",
-                   "combine_softmax_top_amd/csrc/moe_internal.h")
+# sha256 of the sources that define that stage's kernel; it is reported only while
+# those sources are unchanged.
+GEMM_STAGES = {"fc1", "fc2", "fc2_bwd_data", "fc2_wgrad", "fc1_bwd_data", "fc1_wgrad"}
+GEMM_SOURCES = ("combine_softmax_top_amd/csrc/gemm.hip", "combine_softmax_top_amd/csrc/moe_internal.h")
+ROW_SOURCES = ("combine_softmax_top_amd/csrc/dispatch.hip", "combine_softmax_top_amd/csrc/moe_internal.h")
 
 
-def sources_sha256():
+def sources_sha256(stage):
     import hashlib
     h = hashlib.sha256()
-    for rel in TRAFFIC_SOURCES:
+    for rel in (GEMM_SOURCES if stage in GEMM_STAGES else ROW_SOURCES):
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
@@ -103,7 +104,7 @@ def recorded_traffic(stage, workload):
             m = re.match(r"^- ([a-z_0-9]+): `?([^`\s]+)`?", line.strip())
             if m:
                 fields[m.group(1)] = m.group(2)
-    if fields.get("sources_sha256") != sources_sha256() or "traffic_bytes_per_launch" not in fields:
+    if fields.get("sources_sha256") != sources_sha256(stage) or "traffic_bytes_per_launch" not in fields:
         return None
     return int(fields["traffic_bytes_per_launch"])
 
