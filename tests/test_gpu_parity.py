@@ -301,6 +301,32 @@ def test_layer_backward_matches_oracle(w):
         assert (host(gr["dW1"][e]) == 0).all() and (host(gr["dW2"][e]) == 0).all()
 
 
+@pytest.mark.parametrize("w", BWD, ids=lambda w: w.name)
+def test_backward_intermediates_match_oracle(w):
+    # dy, dpre and dbuf on every filled row, through the stage entry points (the fused
+    # backward lets dbuf reuse dy's memory): dy = g * dout rounded to the data type,
+    # dpre = (dy W2) * act'(pre), dbuf = dpre W1
+    import combine_softmax_top_amd as moe
+    print(f"[backward intermediates] {w.name}", flush=True)
+    inp = W.make_inputs(w, seed=0)
+    b, d = _gpu_forward(w, inp, training=True)
+    s = shape_of(w)
+    g = moe.alloc_backward(s)
+    g["dbuf"] = torch.empty_like(g["dy"])
+    moe.moe_decode_backward(s, d["dout"], b["y"], b["gates"], b["idx"], b["loc"], b["capacity"], g["dy"], g["dgates"])
+    moe.moe_expert_fc2_backward_data(s, g["dy"], d["W2"], b["pre"], b["fill"], b["capacity"], g["dpre"])
+    moe.moe_expert_fc1_backward_data(s, g["dpre"], d["W1"], b["fill"], b["capacity"], g["dbuf"])
+    torch.cuda.synchronize()
+    ni = inputs_np(inp)
+    fw = _oracle_forward(w, ni)
+    bw = oracle.layer_backward(fw, ni, w.act, w.dtype)
+    rows = fw["rows"]
+    assert len(rows) > 0
+    check_close(host(g["dy"])[rows], bw["dy"], w.dtype, "dy rows")
+    check_close(host(g["dpre"])[rows], bw["dpre"], w.dtype, "dpre rows")
+    check_close(host(g["dbuf"])[rows], bw["dbuf"], w.dtype, "dbuf rows")
+
+
 @pytest.mark.parametrize("w", [BWD[0], BWD[2], BWD[4]], ids=lambda w: w.name)
 def test_backward_stages_equal_the_fused_backward(w):
     # the per-stage entry points run the fused backward's kernels: same bits

@@ -7,8 +7,9 @@ GEMM-dependent outputs are compared on seeded samples that the oracle computes
 one by one from the original inputs: every expert's first and
 last filled rows plus random rows of h and y, a random set of tokens of the
 layer output, and, for the workloads with a backward, random gate gradients,
-random tokens of dx, and the weight/bias gradients of three experts (hottest,
-median, coldest) on random hidden columns. Residual-MoE: the dense branch's
+random tokens of dx with the dpre and dbuf rows behind them, and the
+weight/bias gradients of three experts (hottest, median, coldest) on random
+hidden columns. Residual-MoE: the dense branch's
 output on the sampled tokens, and the layer output with it. The gate backward: the auxiliary
 loss in full; dlogits on the sampled tokens (the oracle's dgates of their
 routes upstream); with a projected gate (small enough for the oracle to run
@@ -165,7 +166,11 @@ def test_full_size_workload(w):
     dx_rows = np.asarray([rt["idx"][r, t] * C + rt["loc"][r, t] for r in range(w.k) for t in dx_toks
                           if rt["loc"][r, t] < C], np.int64)
     fw = dict(route=rt, buf=obuf)
-    q, _, _, dbuf_o = oracle.backward_rows(fw, ni, dx_rows, w.act, w.dtype, want_dy=False, want_dpre=False)
+    q, _, dpre_o, dbuf_o = oracle.backward_rows(fw, ni, dx_rows, w.act, w.dtype, want_dy=False)
+    # the rows behind the sampled tokens' dx: dpre and dbuf themselves
+    rows_t = torch.from_numpy(dx_rows).cuda()
+    check_close(host(gr["dpre"][rows_t]), dpre_o, w.dtype, "dpre (sampled rows)")
+    check_close(host(gr["dbuf"][rows_t]), dbuf_o, w.dtype, "dbuf (sampled rows)")
     dx_o = oracle.dx_tokens(q, dbuf_o, dx_toks, w.S, w.k, w.dtype, dlogits=dl_o if gate else None,
                             Wg=ni.get("Wg"))
     # dx sums the token's dbuf rows: the two sides' rows (each within tolerance) carried through
