@@ -72,6 +72,26 @@ __device__ __forceinline__ int lane_slot(const int32_t *idx, const int32_t *loc,
 
 // ---------------------------------------------------------------- encode
 
+// Padding rows j in [min(filled[e], C), C) of every expert are +0. A wavefront
+// takes rows in grid-stride order; the row index is scalar, so filled[e] is a
+// scalar load and no vector-memory wait sits between one row's stores and the
+// next's. At S=32768, M=4096, E=128, k=8 the clearing (2.3 GB) takes 0.43 ms on
+// its own, 5.3 TB/s, against 0.34 ms for a plain fill of as many bytes; neither
+// this form nor the whole grid clearing each expert's padding as one range
+// (0.46 ms) closes that gap.
+__device__ __forceinline__ void clear_padding(const int32_t *__restrict__ filled, uint4 *__restrict__ buf, int E,
+                                              int C, int V, int lane) {
+    const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
+    const int rows = E * C;  // the buffer's rows (its byte size is checked on the host)
+    const int nw = static_cast<int>(num_waves());
+    for (int row = __builtin_amdgcn_readfirstlane(static_cast<int>(global_wave())); row < rows; row += nw) {
+        const int e = row / C;
+        if (row - e * C < min(filled[e], C)) continue;
+        uint4 *dst = buf + static_cast<int64_t>(row) * V;
+        for (int v = lane; v < V; v += kWave) dst[v] = zero;
+    }
+}
+
 __global__ __launch_bounds__(kThreads) void encode_kernel(const uint4 *__restrict__ x, const int32_t *__restrict__ idx,
                                                           const int32_t *__restrict__ loc,
                                                           const int32_t *__restrict__ fill,
@@ -80,7 +100,6 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const uint4 *__restric
     const int C = *cap;
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t nw = num_waves();
-    const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
     for (int64_t s = global_wave(); s < S; s += nw) {
         float g_unused;
         const int slot = lane_slot(idx, loc, nullptr, s, S, k, C, lane, g_unused);
@@ -103,14 +122,7 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const uint4 *__restric
         }
     }
     // Padding rows j in [fill[e], C) of every expert are +0.
-    const int64_t rows = static_cast<int64_t>(E) * C;
-    for (int64_t row = global_wave(); row < rows; row += nw) {
-        const int e = static_cast<int>(row / C);
-        const int j = static_cast<int>(row - static_cast<int64_t>(e) * C);
-        if (j < fill[e]) continue;
-        uint4 *dst = buf + row * V;
-        for (int v = lane; v < V; v += kWave) dst[v] = zero;
-    }
+    clear_padding(fill, buf, E, C, V, lane);
 }
 
 // Routing's phase 3 fused with encode. The wavefront of token s places each of
@@ -170,15 +182,7 @@ __global__ __launch_bounds__(kThreads) void assign_encode_kernel(
         }
     }
     // Padding rows j in [min(needed[e], C), C) of every expert are +0.
-    const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
-    const int64_t rows = static_cast<int64_t>(E) * C;
-    for (int64_t row = global_wave(); row < rows; row += nw) {
-        const int e = static_cast<int>(row / C);
-        const int j = static_cast<int>(row - static_cast<int64_t>(e) * C);
-        if (j < min(needed[e], C)) continue;
-        uint4 *dst = buf + row * V;
-        for (int v = lane; v < V; v += kWave) dst[v] = zero;
-    }
+    clear_padding(needed, buf, E, C, V, lane);
 }
 
 // ---------------------------------------------------------------- decode / gather-sum
