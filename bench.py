@@ -18,9 +18,9 @@ each, except route and the gate backward) with HIP events on the stream the
 library launches on, and reports it against its roofline: the bytes or flops the
 method must move or compute per launch over the stage's average time. HBM-bound
 stages run each launch after a 512 MiB buffer fill, so that their operands come
-from HBM, not from L2 or the Infinity Cache (timed as batches of fill + launch
-minus batches of fills alone, so no launch latency is counted); MFMA-bound
-stages run in back-to-back batches. `roofline` is the slowest single-kernel
+from HBM, not from L2 or the Infinity Cache, each launch bracketed by events of
+its own (the interval includes its dispatch); MFMA-bound stages run in
+back-to-back batches. `roofline` is the slowest single-kernel
 stage. The CPU oracle is timed on a bounded sample of the same workload.
 
 Prints one JSON line on stdout; diagnostics go to stderr.
@@ -496,26 +496,35 @@ def main():
             return e0.elapsed_time(e1)
 
         if flushed:
-            # each launch after a fill that evicts L2 and the Infinity Cache: a batch of
-            # (fill, launch) pairs minus a batch of fills alone, alternated over rounds,
-            # so that the launches' operands come from HBM and no launch latency is counted
-            def flush_and_run():
-                flush.fill_(1.0)
-                fn()
+            # each launch after a fill that evicts L2 and the Infinity Cache, so that its
+            # operands come from HBM, bracketed by events of its own (the pairs are queued
+            # behind fillers, so no host gap falls between a fill and its launch; the
+            # interval includes the launch's dispatch). A batch of (fill, launch) pairs
+            # minus a batch of fills was tried first: for launches of a few microseconds it
+            # read up to 30x the kernel's traced duration.
+            def flushed_total(n):
+                for _ in range(min(200, int((2.0 * (host_ms + 0.1) * n + 0.5) / filler_ms) + 1)):
+                    torch.mm(fa, fb)
+                evs = []
+                for _ in range(n):
+                    flush.fill_(1.0)
+                    a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    a.record(stream)
+                    fn()
+                    z.record(stream)
+                    evs.append((a, z))
+                torch.cuda.synchronize()
+                return sum(a.elapsed_time(z) for a, z in evs)
 
             n = max(5, min(reps, 20))
-            tot = 0.0
-            for _ in range(3):
-                tot += batch(flush_and_run, n) - batch(lambda: flush.fill_(1.0), n)
-            ms = max(tot / (3 * n), 1e-6)
+            ms = max(sum(flushed_total(n) for _ in range(3)) / (3 * n), 1e-6)
             reps = 3 * n
         else:
             ms = batch(fn, reps) / reps
         r = roofline_of(kind, amount, ms, w.dtype == W.DT_BF16, mx=bool(w.mx) and name in ("fc1", "fc2"))
         r["ms"] = round(ms, 5)
         r["launches"] = reps
-        r["timing"] = "after a 512 MiB fill each (fill + launch batches minus fill batches)" if flushed else \
-            "back-to-back batch"
+        r["timing"] = "after a 512 MiB fill each, per-launch events" if flushed else "back-to-back batch"
         r["algorithmic_" + kind] = amount
         stages[name] = r
         log(f"[bench] stage {name:13s} {ms:9.4f} ms  {r['achieved']:10.2f} {r['unit']}  "
