@@ -272,7 +272,9 @@ typedef int i32x4_t __attribute__((ext_vector_type(4)));
 // order every stage themselves (each wavefront waits for its own loads, then a
 // workgroup barrier, before a stage is read), so the compiler need not see
 // these loads. The LDS destination goes to M0; gfx9-family parts need one
-// wait state between an M0 write and a direct load reading it (s_nop 0).
+// wait state between an M0 write and a direct load reading it (s_nop 0). Every
+// direct load in this file goes through these two helpers, so no M0 value the
+// compiler sets is live across them.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"  // m0 is a reserved register; the clobber is declared anyway
 __device__ __forceinline__ uint32_t lds_m0(const void *lds_dst) {
@@ -1000,7 +1002,7 @@ __global__ __launch_bounds__(NTH, 1) void rows_gemm_mx(const uint8_t *__restrict
         barrier_keep_loads_lds();  // the previous tile's epilogue reads of LDS are complete
         if (bias != nullptr && wave == 0 && lane < BN / 8) {
             const int c = min(lane * 8, cols_valid - 8);
-            __builtin_amdgcn_global_load_lds(bias + wrow0 + c, (lds_void_t *)sbias, 16, 0, 0);
+            dma16(bias + wrow0, static_cast<uint32_t>(c) * 2, sbias);
         }
         // Scales: four stages' worth (16 bytes) per row and load when the rows are 16-byte
         // aligned (K a multiple of 512), else one stage (a dword) per load. Each lane's
