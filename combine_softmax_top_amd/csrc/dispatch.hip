@@ -498,11 +498,15 @@ __global__ __launch_bounds__(kThreads) void gate_project_kernel(const uint4 *__r
     if ((lane & 1) == 0 && tok0 + t < S && e < ne) logits[(tok0 + t) * E + e0 + e] = v[0];
 }
 
-int grid_for(int64_t waves) {
-    // enough waves to cover the work, capped at 32 waves per CU on 256 CUs
+int grid_for(int64_t waves, int64_t max_blocks = 2048) {
+    // enough waves to cover the work, by default capped at 32 waves per CU on 256 CUs
     const int64_t blocks = (waves + kWavesPerBlock - 1) / kWavesPerBlock;
-    return static_cast<int>(blocks < 1 ? 1 : (blocks > 2048 ? 2048 : blocks));
+    return static_cast<int>(blocks < 1 ? 1 : (blocks > max_blocks ? max_blocks : blocks));
 }
+// Encode (row copies and the padding clear, almost all writes) runs its grid-stride
+// loops on up to 32768 workgroups: at S=32768, M=4096, E=128, k=8 the launch takes
+// 0.86 ms against 0.90 ms on 2048 and 0.88 ms with one wavefront per item.
+constexpr int64_t kEncodeMaxBlocks = 32768;
 
 }  // namespace
 
@@ -530,7 +534,7 @@ hipError_t launch_encode(const moe_shape &s, const void *x, const int32_t *idx, 
                          const int32_t *fill, const int32_t *cap, void *buf, int32_t cmax, hipStream_t st) {
     const int eb = s.dtype == MOE_DT_BF16 ? 2 : 4;
     const int V = s.M * eb / 16;
-    const int grid = grid_for(static_cast<int64_t>(s.S) + static_cast<int64_t>(s.E) * cmax);
+    const int grid = grid_for(static_cast<int64_t>(s.S) + static_cast<int64_t>(s.E) * cmax, kEncodeMaxBlocks);
     hipLaunchKernelGGL(encode_kernel, dim3(grid), dim3(kThreads), 0, st, static_cast<const uint4 *>(x), idx, loc, fill,
                        cap, static_cast<uint4 *>(buf), s.S, s.E, s.k, V);
     return hipGetLastError();
@@ -541,7 +545,7 @@ hipError_t launch_assign_encode(const moe_shape &s, const void *x, const int32_t
                                 int32_t *cap, int32_t *slot_route, void *buf, int32_t cmax, hipStream_t st) {
     const int eb = s.dtype == MOE_DT_BF16 ? 2 : 4;
     const int V = s.M * eb / 16;
-    const int grid = grid_for(static_cast<int64_t>(s.S) + static_cast<int64_t>(s.E) * cmax);
+    const int grid = grid_for(static_cast<int64_t>(s.S) + static_cast<int64_t>(s.E) * cmax, kEncodeMaxBlocks);
     hipLaunchKernelGGL(assign_encode_kernel, dim3(grid), dim3(kThreads), 0, st, static_cast<const uint4 *>(x), idx,
                        ws.counts, needed, s.S, s.E, s.k, ws.nblk, capacity_mode(s), cap_by_factor, loc, fill, cap,
                        slot_route, static_cast<uint4 *>(buf), V);
