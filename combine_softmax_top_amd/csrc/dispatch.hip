@@ -82,12 +82,13 @@ __device__ __forceinline__ int lane_slot(const int32_t *idx, const int32_t *loc,
 __device__ __forceinline__ void clear_padding(const int32_t *__restrict__ filled, uint4 *__restrict__ buf, int E,
                                               int C, int V, int lane) {
     const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
-    const int rows = E * C;  // the buffer's rows (its byte size is checked on the host)
-    const int nw = static_cast<int>(num_waves());
-    for (int row = __builtin_amdgcn_readfirstlane(static_cast<int>(global_wave())); row < rows; row += nw) {
-        const int e = row / C;
-        if (row - e * C < min(filled[e], C)) continue;
-        uint4 *dst = buf + static_cast<int64_t>(row) * V;
+    const int64_t rows = static_cast<int64_t>(E) * C;  // below 2^31 (checked on the host)
+    const int64_t nw = num_waves();
+    for (int64_t row = __builtin_amdgcn_readfirstlane(static_cast<int>(global_wave())); row < rows; row += nw) {
+        const int r = static_cast<int>(row);  // 32-bit division: row < rows < 2^31
+        const int e = r / C;
+        if (r - e * C < min(filled[e], C)) continue;
+        uint4 *dst = buf + row * V;
         for (int v = lane; v < V; v += kWave) dst[v] = zero;
     }
 }
