@@ -91,8 +91,9 @@ def test_route_empty_input():
     assert g["C"] == 1 and (g["needed"] == 0).all() and (g["fill"] == 0).all()
 
 
-# Gate projection shapes: M from 64 to 4160, ragged token groups, E from 3 to 512,
-# both dtypes.
+# Gate projection shapes: M from 64 to 4160 (one to three LDS passes of up to 2048
+# rows of Wg), ragged token groups, E from 3 to 512 (expert groups of 8, the last one
+# partial; E not a multiple of 4 stages Wg element by element), both dtypes.
 GATE_CASES = [
     MID[3],
     W.GATED_BF16.replace(S=1024),
@@ -103,8 +104,12 @@ GATE_CASES = [
                logits="gate"),
     W.Workload("gp_bf16_S37_M128_E512", S=37, M=128, E=512, k=2, H=64, capacity_factor=1.0, logits="gate"),
     W.Workload("gp_bf16_S5_M64_E200", S=5, M=64, E=200, k=4, H=64, capacity_factor=1.0, logits="gate"),
-    # M > 4096: chunks of 128, 33 of them, the last one 64 long
+    # three passes: 2048, 2048 and 64 rows
     W.Workload("gp_bf16_S19_M4160_E4", S=19, M=4160, E=4, k=2, H=64, capacity_factor=1.0, logits="gate"),
+    # E = 13: two expert groups (8 and 5), Wg staged element by element; two passes (2048 + 128)
+    W.Workload("gp_bf16_S77_M2176_E13", S=77, M=2176, E=13, k=3, H=64, capacity_factor=1.0, logits="gate"),
+    W.Workload("gp_f32_S29_M2112_E13", S=29, M=2112, E=13, k=2, H=64, capacity_factor=1.0, dtype=W.DT_F32,
+               logits="gate"),
 ]
 
 
