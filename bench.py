@@ -146,6 +146,8 @@ def algorithmic(w, C, kept):
         st["fc1_wgrad"] = ("flops", prod)     # dW1 = dpre^T buf
         # K0: read the kept dbuf rows, write dx
         st["encode_bwd"] = ("bytes", kept * M * b + S * M * b + 8 * k * S)
+        if w.residual:
+            st["res_bwd"] = ("flops", 8 * M * H * S)  # the dense branch's four backward products
         # gate backward: read logits, idx, dgates, needed; write dlogits
         st["gate_bwd"] = ("bytes", 8 * S * E + 8 * k * S + 4 * E)
         if w.logits == "gate":
@@ -247,6 +249,15 @@ def cpu_baseline(w, inp, budget_s):
             t0 = time.perf_counter()
             oracle.dx_tokens(q, dbuf, toks, w.S, w.k, w.dtype)
             timings["dx"] = time.perf_counter() - t0
+        if w.residual:
+            t0 = time.perf_counter()
+            oracle.residual_mlp(ni["x"], ni["W1r"], ni.get("b1r"), ni["W2r"], ni.get("b2r"), w.act, w.dtype,
+                                tokens=toks)
+            timings["res_ffn"] = time.perf_counter() - t0
+            if w.backward:
+                t0 = time.perf_counter()
+                oracle.residual_backward(ni, w.act, w.dtype, tokens=toks, want_wgrad=False)
+                timings["res_bwd_rows"] = time.perf_counter() - t0
         return len(rs), y
 
     # probe on a few tokens, then a sample sized to the budget
@@ -261,7 +272,7 @@ def cpu_baseline(w, inp, budget_s):
     nrows, ys = sample_pass(toks, samp)
     row_scale = kept / max(1, nrows)
     for name, v in samp.items():
-        scaled[name] = v * (w.S / ntok if name == "dx" else row_scale)
+        scaled[name] = v * (w.S / ntok if name in ("dx", "res_ffn", "res_bwd_rows") else row_scale)
     nw = 0
     if w.backward and kept > 0:
         # weight gradients: a fixed cost per expert (its M x H outputs) plus one per row, so
@@ -276,6 +287,15 @@ def cpu_baseline(w, inp, budget_s):
         oracle.weight_grads(dyw, hw, dprew, buf[wr], w.dtype)
         samp["wgrad"] = time.perf_counter() - t0
         scaled["wgrad"] = samp["wgrad"] * kept / nw
+        if w.residual:
+            # the dense branch's weight gradients: one row per token, timed on the first nw tokens
+            xs = {n: ni[n][:nw] for n in ("x", "dout")}
+            hr, _ = oracle.residual_mlp(xs["x"], ni["W1r"], ni.get("b1r"), ni["W2r"], ni.get("b2r"), w.act, w.dtype)
+            dpr = oracle.residual_backward(dict(ni, **xs), w.act, w.dtype, want_wgrad=False)["dpre_r"]
+            t0 = time.perf_counter()
+            oracle.weight_grads(xs["dout"], hr, dpr, xs["x"], w.dtype)
+            samp["res_wgrad"] = time.perf_counter() - t0
+            scaled["res_wgrad"] = samp["res_wgrad"] * w.S / nw
     rs = rows_of(toks)
     y = np.zeros((w.E * C, w.M), ys.dtype)  # decode's cost does not depend on the values
     y[rs] = ys
@@ -294,8 +314,11 @@ def cpu_baseline(w, inp, budget_s):
                         f"tokens; expert FFN{' and its backward (rows, dgates, dx)' if w.backward else ''}"
                         f" on the {nrows} kept routes of {ntok} seeded random tokens"
                         + (f", weight gradients on {nw} rows of one expert" if w.backward else "")
+                        + (f"; the Residual-MoE dense branch{' and its backward rows' if w.backward else ''} on the "
+                           f"same tokens" + (f", its weight gradients on {nw} tokens" if w.backward else "")
+                           if w.residual else "")
                         + f" ({sum(samp.values()):.1f} s), scaled linearly to all {kept} kept routes "
-                        f"({w.S} tokens for dx)"),
+                        f"({w.S} tokens for dx{' and the dense branch' if w.residual else ''})"),
                 seconds={**{k: round(v, 3) for k, v in t.items()}, **{k: round(v, 2) for k, v in scaled.items()}},
                 sample_seconds={k: round(v, 3) for k, v in samp.items()},
                 host=host_info())
@@ -330,7 +353,7 @@ def main():
     res = {n: inp.get(n) for n in ("W1r", "b1r", "W2r", "b2r")} if w.residual else None
     grads = None
     if w.backward:
-        grads = moe.alloc_backward(s, dev, gate=True, gate_projection=gate)
+        grads = moe.alloc_backward(s, dev, gate=True, gate_projection=gate, residual=w.residual)
         grads["dbuf"] = torch.empty_like(grads["dy"])  # its own memory, so each stage can be timed alone
     x, W1, W2, b1, b2 = inp["x"], inp["W1"], inp["W2"], inp.get("b1"), inp.get("b2")
     logits_in, Wg = (None, inp["Wg"]) if gate else (inp["logits"], None)
@@ -339,7 +362,7 @@ def main():
     logits_bwd = bufs["logits"] if gate else logits_in
 
     def backward():
-        moe.layer_backward(s, bufs, inp["dout"], W1, W2, grads=grads, logits=logits_bwd, x=x, Wg=Wg)
+        moe.layer_backward(s, bufs, inp["dout"], W1, W2, grads=grads, logits=logits_bwd, x=x, Wg=Wg, residual=res)
 
     if mxf is not None:
         # MX experts: the weights are quantised once, outside the timed region (offline)
@@ -433,7 +456,7 @@ def main():
         ]
     if w.residual:
         stage_fns.append(("res_ffn", lambda: moe.moe_residual_ffn(s, x, res["W1r"], res["b1r"], res["W2r"], res["b2r"],
-                                                                  b["h_r"], b["y_r"], b["ws"])))
+                                                                  b["pre_r"], b["h_r"], b["y_r"], b["ws"])))
         stage_fns.append(("decode", lambda: moe.moe_decode_residual(s, b["y"], b["gates"], b["idx"], b["loc"],
                                                                     b["capacity"], b["y_r"], b["out"])))
     else:
@@ -458,6 +481,10 @@ def main():
         ]
         if gate:
             stage_fns.append(("gate_wgrad", lambda: moe.moe_gate_weight_grad(s, x, g["dlogits"], g["dWg"], b["ws"])))
+        if w.residual:
+            stage_fns.append(("res_bwd", lambda: moe.moe_residual_backward(
+                s, inp["dout"], x, b["pre_r"], b["h_r"], res["W1r"], res["W2r"], g["dpre_r"], g["dx_r"], g["dW1r"],
+                g["db1r"], g["dW2r"], g["db2r"], b["ws"])))
 
     flush = torch.empty(FLUSH_MIB * 2 ** 20 // 4, dtype=torch.float32, device=dev)
     # bf16 matmuls enqueued ahead of a batch keep the GPU busy while the host enqueues it,

@@ -92,12 +92,14 @@ _SIGS = {
     "moe_layer_forward_mx": [_SP, ctypes.c_int32] + [_P] * 24 + [ctypes.c_size_t, _P],
     "moe_expert_fc1_mx": [_SP, ctypes.c_int32] + [_P] * 10,
     "moe_expert_fc2_mx": [_SP, ctypes.c_int32] + [_P] * 9,
-    "moe_residual_ffn": [_SP] + [_P] * 8 + [ctypes.c_size_t, _P],
+    "moe_residual_ffn": [_SP] + [_P] * 9 + [ctypes.c_size_t, _P],
+    "moe_residual_backward": [_SP] + [_P] * 13 + [ctypes.c_size_t, _P],
     "moe_decode_residual": [_SP] + [_P] * 8,
-    "moe_residual_layer_forward": [_SP] + [_P] * 27 + [ctypes.c_size_t, _P],
+    "moe_residual_layer_forward": [_SP] + [_P] * 28 + [ctypes.c_size_t, _P],
     "moe_gate_backward": [_SP, _P, _P, _P, _P, ctypes.c_double, _P, _P, _P, ctypes.c_size_t, _P],
     "moe_gate_weight_grad": [_SP, _P, _P, _P, _P, ctypes.c_size_t, _P],
     "moe_layer_backward": [_SP] + [_P] * 23 + [ctypes.c_double] + [_P] * 6 + [ctypes.c_size_t, _P],
+    "moe_residual_layer_backward": [_SP] + [_P] * 23 + [ctypes.c_double] + [_P] * 16 + [ctypes.c_size_t, _P],
     "moe_decode_backward": [_SP] + [_P] * 9,
     "moe_expert_fc2_backward_data": [_SP] + [_P] * 7,
     "moe_expert_fc2_weight_grad": [_SP] + [_P] * 7,
@@ -306,9 +308,16 @@ def layer_forward_mx(shape: Shape, wfmt: int, x, W1q, b1, W2q, b2, logits=None, 
     return bufs
 
 
-def moe_residual_ffn(shape: Shape, x, W1r, b1r, W2r, b2r, h_r, y_r, ws, stream=None) -> None:
+def moe_residual_ffn(shape: Shape, x, W1r, b1r, W2r, b2r, pre_r, h_r, y_r, ws, stream=None) -> None:
     _check(_lib.moe_residual_ffn(ctypes.byref(shape.c()), _ptr(x), _ptr(W1r), _ptr(b1r), _ptr(W2r), _ptr(b2r),
-                                 _ptr(h_r), _ptr(y_r), *_ws_args(ws), _stream(stream)))
+                                 _ptr(pre_r), _ptr(h_r), _ptr(y_r), *_ws_args(ws), _stream(stream)))
+
+
+def moe_residual_backward(shape: Shape, dout, x, pre_r, h_r, W1r, W2r, dpre_r, dx_r, dW1r, db1r, dW2r, db2r, ws,
+                          stream=None) -> None:
+    _check(_lib.moe_residual_backward(ctypes.byref(shape.c()), _ptr(dout), _ptr(x), _ptr(pre_r), _ptr(h_r),
+                                      _ptr(W1r), _ptr(W2r), _ptr(dpre_r), _ptr(dx_r), _ptr(dW1r), _ptr(db1r),
+                                      _ptr(dW2r), _ptr(db2r), *_ws_args(ws), _stream(stream)))
 
 
 def moe_decode_residual(shape: Shape, y, gates, idx, loc, capacity, y_r, out, stream=None) -> None:
@@ -317,13 +326,13 @@ def moe_decode_residual(shape: Shape, y, gates, idx, loc, capacity, y_r, out, st
 
 
 def moe_residual_layer_forward(shape: Shape, x, logits_in, Wg, logits_out, W1, b1, W2, b2, W1r, b1r, W2r, b2r,
-                               idx, loc, gates, needed, fill, capacity, slot_route, buf, pre, h, y, h_r, y_r, out, ws,
-                               stream=None) -> None:
+                               idx, loc, gates, needed, fill, capacity, slot_route, buf, pre, h, y, pre_r, h_r, y_r,
+                               out, ws, stream=None) -> None:
     _check(_lib.moe_residual_layer_forward(
         ctypes.byref(shape.c()), _ptr(x), _ptr(logits_in), _ptr(Wg), _ptr(logits_out), _ptr(W1), _ptr(b1), _ptr(W2),
         _ptr(b2), _ptr(W1r), _ptr(b1r), _ptr(W2r), _ptr(b2r), _ptr(idx), _ptr(loc), _ptr(gates), _ptr(needed),
-        _ptr(fill), _ptr(capacity), _ptr(slot_route), _ptr(buf), _ptr(pre), _ptr(h), _ptr(y), _ptr(h_r), _ptr(y_r),
-        _ptr(out), *_ws_args(ws), _stream(stream)))
+        _ptr(fill), _ptr(capacity), _ptr(slot_route), _ptr(buf), _ptr(pre), _ptr(h), _ptr(y), _ptr(pre_r), _ptr(h_r),
+        _ptr(y_r), _ptr(out), *_ws_args(ws), _stream(stream)))
 
 
 def moe_gate_backward(shape: Shape, logits, idx, dgates, needed, aux_coef, dlogits, aux_loss, ws,
@@ -364,6 +373,18 @@ def moe_layer_backward(shape: Shape, dout, buf, pre, h, y, gates, idx, loc, fill
         _ptr(x), _ptr(Wg), _ptr(dlogits), _ptr(dWg), _ptr(aux_loss), *_ws_args(ws), _stream(stream)))
 
 
+def moe_residual_layer_backward(shape: Shape, dout, buf, pre, h, y, gates, idx, loc, fill, capacity, W1, W2, dy, dpre,
+                                dbuf, dx, dW1, db1, dW2, db2, dgates, W1r, W2r, pre_r, h_r, dpre_r, dx_r, dW1r, db1r,
+                                dW2r, db2r, ws, logits=None, needed=None, aux_coef=0.0, x=None, Wg=None,
+                                dlogits=None, dWg=None, aux_loss=None, stream=None) -> None:
+    _check(_lib.moe_residual_layer_backward(
+        ctypes.byref(shape.c()), _ptr(dout), _ptr(buf), _ptr(pre), _ptr(h), _ptr(y), _ptr(gates), _ptr(idx),
+        _ptr(loc), _ptr(fill), _ptr(capacity), _ptr(W1), _ptr(W2), _ptr(dy), _ptr(dpre), _ptr(dbuf), _ptr(dx),
+        _ptr(dW1), _ptr(db1), _ptr(dW2), _ptr(db2), _ptr(dgates), _ptr(logits), _ptr(needed), float(aux_coef),
+        _ptr(x), _ptr(Wg), _ptr(dlogits), _ptr(dWg), _ptr(aux_loss), _ptr(W1r), _ptr(W2r), _ptr(pre_r), _ptr(h_r),
+        _ptr(dpre_r), _ptr(dx_r), _ptr(dW1r), _ptr(db1r), _ptr(dW2r), _ptr(db2r), *_ws_args(ws), _stream(stream)))
+
+
 def moe_decode_backward(shape: Shape, dout, y, gates, idx, loc, capacity, dy, dgates, stream=None) -> None:
     _check(_lib.moe_decode_backward(ctypes.byref(shape.c()), _ptr(dout), _ptr(y), _ptr(gates), _ptr(idx), _ptr(loc),
                                     _ptr(capacity), _ptr(dy), _ptr(dgates), _stream(stream)))
@@ -400,7 +421,7 @@ def alloc_forward(shape: Shape, device="cuda", training: bool = False,
                   gate_projection: bool = False, residual: bool = False) -> Dict[str, torch.Tensor]:
     """Allocate every output and scratch buffer the forward writes, sized with the host
     capacity bound (torch.empty: contents undefined until the library writes them);
-    residual adds the dense branch's h_r [S, H] and y_r [S, M]."""
+    residual adds the dense branch's h_r [S, H] and y_r [S, M] (and pre_r [S, H] when training)."""
     S, M, E, k, H = shape.S, shape.M, shape.E, shape.k, shape.H
     cmax = moe_capacity_bound(shape)
     dt = shape.torch_dtype
@@ -420,6 +441,7 @@ def alloc_forward(shape: Shape, device="cuda", training: bool = False,
     bufs["logits"] = torch.empty(S, E, dtype=torch.float32, device=device) if gate_projection else None
     bufs["h_r"] = torch.empty(S, H, dtype=dt, device=device) if residual else None
     bufs["y_r"] = torch.empty(S, M, dtype=dt, device=device) if residual else None
+    bufs["pre_r"] = torch.empty(S, H, dtype=dt, device=device) if residual and training else None
     return bufs
 
 
@@ -440,20 +462,27 @@ def layer_forward(shape: Shape, x, W1, b1, W2, b2, logits=None, Wg=None, bufs=No
         moe_residual_layer_forward(shape, x, logits, Wg, lo, W1, b1, W2, b2, residual["W1r"], residual.get("b1r"),
                                    residual["W2r"], residual.get("b2r"), bufs["idx"], bufs["loc"], bufs["gates"],
                                    bufs["needed"], bufs["fill"], bufs["capacity"], bufs["slot_route"], bufs["buf"],
-                                   bufs["pre"], bufs["h"], bufs["y"], bufs["h_r"], bufs["y_r"], bufs["out"],
-                                   bufs["ws"], stream)
+                                   bufs["pre"], bufs["h"], bufs["y"], bufs["pre_r"], bufs["h_r"], bufs["y_r"],
+                                   bufs["out"], bufs["ws"], stream)
     return bufs
 
 
 def alloc_backward(shape: Shape, device="cuda", gate: bool = False,
-                   gate_projection: bool = False) -> Dict[str, torch.Tensor]:
-    """Gradient buffers; gate adds dlogits and aux_loss, gate_projection also dWg."""
+                   gate_projection: bool = False, residual: bool = False) -> Dict[str, torch.Tensor]:
+    """Gradient buffers; gate adds dlogits and aux_loss, gate_projection also dWg; residual the
+    dense branch's dpre_r, dx_r and its weight and bias gradients."""
     S, M, E, k, H = shape.S, shape.M, shape.E, shape.k, shape.H
     cmax = moe_capacity_bound(shape)
     dt = shape.torch_dtype
     f32 = dict(dtype=torch.float32, device=device)
     dyb = torch.empty(E * cmax, M, dtype=dt, device=device)
-    return dict(
+    res = {}
+    if residual:
+        res = dict(dpre_r=torch.empty(S, H, dtype=dt, device=device), dx_r=torch.empty(S, M, dtype=dt, device=device),
+                   dW1r=torch.empty(H, M, **f32), dW2r=torch.empty(M, H, **f32),
+                   db1r=torch.empty(H, **f32) if shape.has_fc1_bias else None,
+                   db2r=torch.empty(M, **f32) if shape.has_fc2_bias else None)
+    return dict(**res,
         dlogits=torch.empty(S, E, **f32) if gate or gate_projection else None,
         aux_loss=torch.empty(1, **f32) if gate or gate_projection else None,
         dWg=torch.empty(M, E, **f32) if gate_projection else None,
@@ -468,14 +497,27 @@ def alloc_backward(shape: Shape, device="cuda", gate: bool = False,
 
 
 def layer_backward(shape: Shape, fw: Dict[str, torch.Tensor], dout, W1, W2, grads=None, logits=None, x=None,
-                   Wg=None, aux_coef=AUX_COEF, stream=None):
+                   Wg=None, aux_coef=AUX_COEF, residual=None, stream=None):
     """The fused backward into ``grads`` (allocated if None). With ``logits`` (the forward's;
     ``fw["logits"]`` for a projected gate) it includes the gate backward and the auxiliary
     load-balance loss of coefficient ``aux_coef``; with ``Wg`` and ``x`` also dWg and the gate
-    projection's share of dx."""
+    projection's share of dx. ``residual``: the Residual-MoE dense branch's weights (a dict with
+    W1r and W2r; ``fw`` from a training forward with the branch, ``x`` required): adds its
+    backward, and its dx_r to dx."""
     if grads is None:
-        grads = alloc_backward(shape, dout.device, gate=logits is not None, gate_projection=Wg is not None)
+        grads = alloc_backward(shape, dout.device, gate=logits is not None, gate_projection=Wg is not None,
+                               residual=residual is not None)
     gate = logits is not None
+    if residual is not None:
+        moe_residual_layer_backward(
+            shape, dout, fw["buf"], fw["pre"], fw["h"], fw["y"], fw["gates"], fw["idx"], fw["loc"], fw["fill"],
+            fw["capacity"], W1, W2, grads["dy"], grads["dpre"], grads["dbuf"], grads["dx"], grads["dW1"], grads["db1"],
+            grads["dW2"], grads["db2"], grads["dgates"], residual["W1r"], residual["W2r"], fw["pre_r"], fw["h_r"],
+            grads["dpre_r"], grads["dx_r"], grads["dW1r"], grads["db1r"], grads["dW2r"], grads["db2r"], fw["ws"],
+            logits=logits, needed=fw["needed"] if gate else None, aux_coef=aux_coef if gate else 0.0, x=x, Wg=Wg,
+            dlogits=grads["dlogits"] if gate else None, dWg=grads["dWg"] if Wg is not None else None,
+            aux_loss=grads["aux_loss"] if gate else None, stream=stream)
+        return grads
     moe_layer_backward(shape, dout, fw["buf"], fw["pre"], fw["h"], fw["y"], fw["gates"], fw["idx"], fw["loc"],
                        fw["fill"], fw["capacity"], W1, W2, grads["dy"], grads["dpre"], grads["dbuf"], grads["dx"],
                        grads["dW1"], grads["db1"], grads["dW2"], grads["db2"], grads["dgates"],

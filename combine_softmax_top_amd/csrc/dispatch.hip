@@ -557,7 +557,10 @@ template <bool BF16, int NV>
 static void decode_dispatch_nv(bool unit, bool res, int grid, hipStream_t st, const uint4 *Y, const float *gates,
                                const int32_t *idx, const int32_t *loc, const int32_t *cap, const uint4 *R, uint4 *O,
                                int S, int k, int V) {
-    if (unit)
+    if (unit && res)
+        hipLaunchKernelGGL((gather_sum_kernel<BF16, true, true, NV>), dim3(grid), dim3(kThreads), 0, st, Y, gates,
+                           idx, loc, cap, R, O, S, k, V);
+    else if (unit)
         hipLaunchKernelGGL((gather_sum_kernel<BF16, true, false, NV>), dim3(grid), dim3(kThreads), 0, st, Y, gates,
                            idx, loc, cap, R, O, S, k, V);
     else if (res)
@@ -598,25 +601,43 @@ hipError_t launch_decode(const moe_shape &s, const void *y, const float *gates, 
 // ---------------------------------------------------------------- Residual-MoE dense branch
 
 // The grouped GEMMs read an expert's row count and the capacity from device
-// memory; the dense branch is one "expert" whose rows are all S tokens.
+// memory; the dense branch is one "expert" whose rows are all S tokens (the
+// capacity, a row stride only, is kept at least 1).
 __global__ void set_dense_rows_kernel(int32_t *rows, int S) {
     if (threadIdx.x == 0) {
-        rows[0] = S;  // fill[0]
-        rows[1] = S;  // capacity
+        rows[0] = S;             // fill[0]
+        rows[1] = S > 0 ? S : 1;  // capacity
     }
 }
 
 hipError_t launch_residual_ffn(const moe_shape &s, const void *x, const void *W1r, const void *b1r, const void *W2r,
-                               const void *b2r, void *h_r, void *y_r, int32_t *dense_rows, hipStream_t st) {
+                               const void *b2r, void *pre_r, void *h_r, void *y_r, int32_t *dense_rows,
+                               hipStream_t st) {
     if (s.S == 0) return hipSuccess;
     hipLaunchKernelGGL(set_dense_rows_kernel, dim3(1), dim3(64), 0, st, dense_rows, s.S);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     moe_shape d = s;
     d.E = 1;
-    if ((err = launch_fc1(d, x, W1r, b1r, dense_rows, dense_rows + 1, nullptr, h_r, s.S, st)) != hipSuccess)
+    if ((err = launch_fc1(d, x, W1r, b1r, dense_rows, dense_rows + 1, pre_r, h_r, s.S, st)) != hipSuccess)
         return err;
     return launch_fc2(d, h_r, W2r, b2r, dense_rows, dense_rows + 1, y_r, s.S, st);
+}
+
+// The dense branch's backward: the expert FFN backward's four products with the
+// branch as one expert over all S rows (dy = dout, buf = x). With S = 0 the
+// weight-gradient products still run, over no rows, and write zeros.
+hipError_t launch_residual_bwd(const moe_shape &s, const void *dout, const void *x, const void *pre_r,
+                               const void *h_r, const void *W1r, const void *W2r, void *dpre_r, void *dx_r,
+                               float *dW1r, float *db1r, float *dW2r, float *db2r, int32_t *dense_rows,
+                               hipStream_t st) {
+    hipLaunchKernelGGL(set_dense_rows_kernel, dim3(1), dim3(64), 0, st, dense_rows, s.S);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    moe_shape d = s;
+    d.E = 1;
+    return launch_expert_ffn_bwd(d, x, pre_r, h_r, W1r, W2r, dense_rows, dense_rows + 1, const_cast<void *>(dout),
+                                 dpre_r, dx_r, dW1r, db1r, dW2r, db2r, s.S > 0 ? s.S : 1, st);
 }
 
 hipError_t launch_decode_bwd(const moe_shape &s, const void *dout, const void *y, const float *gates,

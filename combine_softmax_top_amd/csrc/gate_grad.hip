@@ -17,8 +17,8 @@
 //    more than one slice, each writes a partial [M, E] and wgrad_reduce_kernel
 //    adds them in a fixed order.
 //  - gate_dx_kernel: dx[s] = sum of the kept dbuf rows (route order, fp32) +
-//    dlogits[s] . Wg^T, rounded once to the data type: the encode backward with
-//    the gate projection's share fused in. A block takes 32 tokens x 256
+//    dlogits[s] . Wg^T (+ the Residual-MoE dense branch's dx_r[s]), rounded once
+//    to the data type: the encode backward with the gate projection's share fused in. A block takes 32 tokens x 256
 //    columns; the dlogits . Wg^T product runs over E in chunks of 16 staged in
 //    LDS (a small-K outer-product GEMM in fp32 FMA).
 #include <algorithm>
@@ -348,7 +348,7 @@ __global__ __launch_bounds__(256) void gate_dx_kernel(const void *__restrict__ d
                                                       const int32_t *__restrict__ cap,
                                                       const float *__restrict__ dlogits,
                                                       const float *__restrict__ Wg, int S, int M, int E, int k,
-                                                      void *__restrict__ dx) {
+                                                      const void *__restrict__ dxres, void *__restrict__ dx) {
 #pragma clang fp contract(off)
     __shared__ __align__(16) float swg[kDxEK][kDxCols];
     __shared__ float sdl[kDxTok][kDxEK + 1];
@@ -427,6 +427,27 @@ __global__ __launch_bounds__(256) void gate_dx_kernel(const void *__restrict__ d
         }
 #pragma unroll
         for (int c = 0; c < 8; ++c) sum[c] = sum[c] + acc[i][c];
+        if (dxres != nullptr) {
+            float f[8];
+            if constexpr (BF16) {
+                const uint4 u = *reinterpret_cast<const uint4 *>(static_cast<const bf16_t *>(dxres) +
+                                                                 static_cast<int64_t>(s) * M + m);
+                const uint32_t wv[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+                for (int h = 0; h < 4; ++h) {
+                    f[2 * h] = __uint_as_float(wv[h] << 16);
+                    f[2 * h + 1] = __uint_as_float(wv[h] & 0xFFFF0000u);
+                }
+            } else {
+                const float4 *p = reinterpret_cast<const float4 *>(static_cast<const float *>(dxres) +
+                                                                   static_cast<int64_t>(s) * M + m);
+                const float4 a = p[0], b = p[1];
+                f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
+                f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+            }
+#pragma unroll
+            for (int c = 0; c < 8; ++c) sum[c] = sum[c] + f[c];
+        }
         if constexpr (BF16) {
             uint4 o;
             o.x = pack_bf16x2(sum[0], sum[1]);
@@ -563,16 +584,17 @@ hipError_t launch_gate_weight_grad(const moe_shape &s, const void *x, const floa
 }
 
 hipError_t launch_gate_dx(const moe_shape &s, const void *dbuf, const int32_t *idx, const int32_t *loc,
-                          const int32_t *cap, const float *dlogits, const float *Wg, void *dx, hipStream_t st) {
+                          const int32_t *cap, const float *dlogits, const float *Wg, void *dx, hipStream_t st,
+                          const void *dxres) {
     const int S = s.S, M = s.M;
     if (S == 0) return hipSuccess;
     const dim3 grid((S + kDxTok - 1) / kDxTok, (M + kDxCols - 1) / kDxCols);
     if (s.dtype == MOE_DT_BF16)
         hipLaunchKernelGGL(gate_dx_kernel<true>, grid, dim3(256), 0, st, dbuf, idx, loc, cap, dlogits, Wg, S, M, s.E,
-                           s.k, dx);
+                           s.k, dxres, dx);
     else
         hipLaunchKernelGGL(gate_dx_kernel<false>, grid, dim3(256), 0, st, dbuf, idx, loc, cap, dlogits, Wg, S, M, s.E,
-                           s.k, dx);
+                           s.k, dxres, dx);
     return hipGetLastError();
 }
 

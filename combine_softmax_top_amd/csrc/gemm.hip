@@ -1751,8 +1751,10 @@ hipError_t fwd_launch(int act, const void *A, const void *B, void *D, int N, int
 // about 1024 of them (16 K steps) the fp32 tile's store is a large share of a
 // tile, and 128 x 128 tiles at two workgroups per CU overlap one's stores with
 // the other's MFMAs (the bench layer's backward: 500 -> 488 us); with more rows
-// 256 x 256 tiles win (S=32768, E=128, k=8: 19.5 vs 20.7 ms). MOE_KGRAD_CFG
-// (1 = 256 x 256, 2 = 128 x 128) overrides the choice for tuning.
+// 256 x 256 tiles win (S=32768, E=128, k=8: 19.5 vs 20.7 ms), unless there are
+// fewer of them than CUs (one expert's gradients, as Residual-MoE's dense
+// branch: four times as many 128 x 128 tiles). MOE_KGRAD_CFG (1 = 256 x 256,
+// 2 = 128 x 128) overrides the choice for tuning.
 hipError_t kgroup_launch(const void *A, const void *B, float *D, int Mo, int No, int E, const int32_t *fill,
                          const int32_t *cap, float *colsum, int32_t cmax, int64_t rows_hint, hipStream_t st) {
     // the last K step reads up to 63 rows past the expert's fill (they read as zero)
@@ -1761,7 +1763,8 @@ hipError_t kgroup_launch(const void *A, const void *B, float *D, int Mo, int No,
             const char *v = getenv("MOE_KGRAD_CFG");
             return v ? atoi(v) : 0;
         }();
-        const bool small = kc == 2 || (kc != 1 && rows_hint <= 1024LL * E);
+        const int64_t big_tiles = static_cast<int64_t>(E) * ((Mo + 255) / 256) * ((No + 255) / 256);
+        const bool small = kc == 2 || (kc != 1 && (rows_hint <= 1024LL * E || big_tiles < resident_blocks(1)));
         if (small) {
             constexpr int lds = 2 * (128 + 128) * kBigKB * 2;
             auto k = kgrad_gemm_big<128, 128, 256>;

@@ -433,8 +433,8 @@ moe_status moe_gate_weight_grad(const moe_shape *shape, const void *x, const flo
 }
 
 moe_status moe_residual_ffn(const moe_shape *shape, const void *x, const void *W1r, const void *b1r,
-                            const void *W2r, const void *b2r, void *h_r, void *y_r, void *ws, size_t ws_bytes,
-                            void *stream) {
+                            const void *W2r, const void *b2r, void *pre_r, void *h_r, void *y_r, void *ws,
+                            size_t ws_bytes, void *stream) {
     moe_status st = check_shape(shape);
     if (st != MOE_OK) return st;
     const moe_shape &s = *shape;
@@ -444,10 +444,28 @@ moe_status moe_residual_ffn(const moe_shape *shape, const void *x, const void *W
     MOE_REQUIRE((b2r != nullptr) == (s.has_fc2_bias != 0), "b2r must be given iff has_fc2_bias");
     if (s.S / 128 >= 65535) return fail(MOE_EUNSUPPORTED, "S=%d too large for the dense branch's GEMM grid", s.S);
     if ((st = check_ws(s, ws, ws_bytes)) != MOE_OK) return st;
-    MOE_REQUIRE_ALIGNED(x, W1r, b1r, W2r, b2r, h_r, y_r, ws);
-    hipError_t e = moe::launch_residual_ffn(s, x, W1r, b1r, W2r, b2r, h_r, y_r, static_cast<int32_t *>(ws),
+    MOE_REQUIRE_ALIGNED(x, W1r, b1r, W2r, b2r, pre_r, h_r, y_r, ws);
+    hipError_t e = moe::launch_residual_ffn(s, x, W1r, b1r, W2r, b2r, pre_r, h_r, y_r, static_cast<int32_t *>(ws),
                                             as_stream(stream));
     return e == hipSuccess ? MOE_OK : hip_fail(e, "residual dense branch");
+}
+
+moe_status moe_residual_backward(const moe_shape *shape, const void *dout, const void *x, const void *pre_r,
+                                 const void *h_r, const void *W1r, const void *W2r, void *dpre_r, void *dx_r,
+                                 float *dW1r, float *db1r, float *dW2r, float *db2r, void *ws, size_t ws_bytes,
+                                 void *stream) {
+    moe_status st = check_shape(shape);
+    if (st != MOE_OK) return st;
+    const moe_shape &s = *shape;
+    MOE_REQUIRE(W1r && W2r && dW1r && dW2r, "W1r, W2r, dW1r and dW2r must be non-NULL");
+    if (s.S > 0)
+        MOE_REQUIRE(dout && x && pre_r && h_r && dpre_r && dx_r, "dout, x, pre_r, h_r, dpre_r and dx_r must be non-NULL");
+    if (s.S / 128 >= 65535) return fail(MOE_EUNSUPPORTED, "S=%d too large for the dense branch's GEMM grid", s.S);
+    if ((st = check_ws(s, ws, ws_bytes)) != MOE_OK) return st;
+    MOE_REQUIRE_ALIGNED(dout, x, pre_r, h_r, W1r, W2r, dpre_r, dx_r, dW1r, db1r, dW2r, db2r, ws);
+    hipError_t e = moe::launch_residual_bwd(s, dout, x, pre_r, h_r, W1r, W2r, dpre_r, dx_r, dW1r, db1r, dW2r, db2r,
+                                            static_cast<int32_t *>(ws), as_stream(stream));
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "residual dense branch backward");
 }
 
 moe_status moe_decode_residual(const moe_shape *shape, const void *y, const float *gates, const int32_t *idx,
@@ -469,7 +487,7 @@ namespace {
 
 struct Residual {
     const void *W1r, *b1r, *W2r, *b2r;
-    void *h_r, *y_r;
+    void *pre_r, *h_r, *y_r;
 };
 
 moe_status layer_forward_impl(const moe_shape *shape, const void *x, const float *logits_in, const float *Wg,
@@ -496,7 +514,7 @@ moe_status layer_forward_impl(const moe_shape *shape, const void *x, const float
         MOE_REQUIRE((res->b2r != nullptr) == (s.has_fc2_bias != 0), "b2r must be given iff has_fc2_bias");
         if (s.S / 128 >= 65535)
             return fail(MOE_EUNSUPPORTED, "S=%d too large for the dense branch's GEMM grid", s.S);
-        MOE_REQUIRE_ALIGNED(res->W1r, res->b1r, res->W2r, res->b2r, res->h_r, res->y_r);
+        MOE_REQUIRE_ALIGNED(res->W1r, res->b1r, res->W2r, res->b2r, res->pre_r, res->h_r, res->y_r);
     }
     if ((st = check_forward_ws(s, ws, ws_bytes)) != MOE_OK) return st;
     MOE_REQUIRE_ALIGNED(x, logits_in, Wg, logits_out, W1, b1, W2, b2, idx, loc, gates, needed, fill, capacity,
@@ -523,7 +541,7 @@ moe_status layer_forward_impl(const moe_shape *shape, const void *x, const float
         return hip_fail(e, "expert fc2");
     // the dense branch uses the workspace after routing is done with it
     if (res != nullptr &&
-        (e = moe::launch_residual_ffn(s, x, res->W1r, res->b1r, res->W2r, res->b2r, res->h_r, res->y_r,
+        (e = moe::launch_residual_ffn(s, x, res->W1r, res->b1r, res->W2r, res->b2r, res->pre_r, res->h_r, res->y_r,
                                       static_cast<int32_t *>(ws), strm)) != hipSuccess)
         return hip_fail(e, "residual dense branch");
     if ((e = moe::launch_decode(s, y, gates, idx, loc, capacity, out, false, strm,
@@ -614,9 +632,9 @@ moe_status moe_residual_layer_forward(const moe_shape *shape, const void *x, con
                                       const void *W2, const void *b2, const void *W1r, const void *b1r,
                                       const void *W2r, const void *b2r, int32_t *idx, int32_t *loc, float *gates,
                                       int32_t *needed, int32_t *fill, int32_t *capacity, int32_t *slot_route,
-                                      void *buf, void *pre, void *h, void *y, void *h_r, void *y_r, void *out,
-                                      void *ws, size_t ws_bytes, void *stream) {
-    const Residual res{W1r, b1r, W2r, b2r, h_r, y_r};
+                                      void *buf, void *pre, void *h, void *y, void *pre_r, void *h_r, void *y_r,
+                                      void *out, void *ws, size_t ws_bytes, void *stream) {
+    const Residual res{W1r, b1r, W2r, b2r, pre_r, h_r, y_r};
     return layer_forward_impl(shape, x, logits_in, Wg, logits_out, W1, b1, W2, b2, idx, loc, gates, needed, fill,
                               capacity, slot_route, buf, pre, h, y, out, ws, ws_bytes, &res, stream);
 }
@@ -691,13 +709,27 @@ moe_status moe_encode_backward(const moe_shape *shape, const void *dbuf, const i
     return e == hipSuccess ? MOE_OK : hip_fail(e, "encode backward");
 }
 
-moe_status moe_layer_backward(const moe_shape *shape, const void *dout, const void *buf, const void *pre,
-                              const void *h, const void *y, const float *gates, const int32_t *idx,
-                              const int32_t *loc, const int32_t *fill, const int32_t *capacity, const void *W1,
-                              const void *W2, void *dy, void *dpre, void *dbuf, void *dx, float *dW1, float *db1,
-                              float *dW2, float *db2, float *dgates, const float *logits, const int32_t *needed,
-                              double aux_coef, const void *x, const float *Wg, float *dlogits, float *dWg,
-                              float *aux_loss, void *ws, size_t ws_bytes, void *stream) {
+const char *moe_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"
+
+namespace {
+
+// Residual-MoE's dense branch in the layer backward: its forward tensors, weights and
+// gradient outputs.
+struct ResidualGrad {
+    const void *W1r, *W2r, *pre_r, *h_r;
+    void *dpre_r, *dx_r;
+    float *dW1r, *db1r, *dW2r, *db2r;
+};
+
+moe_status layer_backward_impl(const moe_shape *shape, const void *dout, const void *buf, const void *pre,
+                               const void *h, const void *y, const float *gates, const int32_t *idx,
+                               const int32_t *loc, const int32_t *fill, const int32_t *capacity, const void *W1,
+                               const void *W2, void *dy, void *dpre, void *dbuf, void *dx, float *dW1, float *db1,
+                               float *dW2, float *db2, float *dgates, const float *logits, const int32_t *needed,
+                               double aux_coef, const void *x, const float *Wg, float *dlogits, float *dWg,
+                               float *aux_loss, void *ws, size_t ws_bytes, const ResidualGrad *res, void *stream) {
     moe_status st = check_shape(shape);
     if (st != MOE_OK) return st;
     const moe_shape &s = *shape;
@@ -712,15 +744,34 @@ moe_status moe_layer_backward(const moe_shape *shape, const void *dout, const vo
         if (s.S > 0) MOE_REQUIRE(logits && dlogits, "the gate backward needs logits and dlogits");
         MOE_REQUIRE((Wg != nullptr) == (dWg != nullptr), "Wg and dWg go together");
         if (s.S > 0 && Wg != nullptr) MOE_REQUIRE(x != nullptr, "x is required with Wg");
-        if ((st = check_ws(s, ws, ws_bytes)) != MOE_OK) return st;
     } else {
         MOE_REQUIRE(Wg == nullptr, "Wg needs the gate backward (logits, dlogits, dWg)");
     }
+    if (res != nullptr) {
+        MOE_REQUIRE(res->W1r && res->W2r && res->dW1r && res->dW2r, "W1r, W2r, dW1r and dW2r must be non-NULL");
+        if (s.S > 0)
+            MOE_REQUIRE(x && res->pre_r && res->h_r && res->dpre_r && res->dx_r,
+                        "x, pre_r, h_r, dpre_r and dx_r must be non-NULL");
+        MOE_REQUIRE(res->dx_r != dx || s.S == 0, "dx_r and dx must be different buffers");
+        if (s.S / 128 >= 65535)
+            return fail(MOE_EUNSUPPORTED, "S=%d too large for the dense branch's GEMM grid", s.S);
+        MOE_REQUIRE_ALIGNED(res->W1r, res->W2r, res->pre_r, res->h_r, res->dpre_r, res->dx_r, res->dW1r, res->db1r,
+                            res->dW2r, res->db2r);
+    }
+    if (gate || res != nullptr)
+        if ((st = check_ws(s, ws, ws_bytes)) != MOE_OK) return st;
     MOE_REQUIRE_ALIGNED(dout, buf, pre, h, y, gates, idx, loc, fill, capacity, W1, W2, dy, dpre, dbuf, dx, dW1, db1,
                         dW2, db2, dgates, logits, needed, x, Wg, dlogits, dWg, aux_loss, ws);
     hipStream_t strm = as_stream(stream);
     const int32_t cmax = static_cast<int32_t>(cap_bound(s));
     hipError_t e;
+    // the dense branch first: its two row counts in the workspace are read before the
+    // gate backward reuses the workspace (stream order)
+    if (res != nullptr &&
+        (e = moe::launch_residual_bwd(s, dout, x, res->pre_r, res->h_r, res->W1r, res->W2r, res->dpre_r, res->dx_r,
+                                      res->dW1r, res->db1r, res->dW2r, res->db2r, static_cast<int32_t *>(ws),
+                                      strm)) != hipSuccess)
+        return hip_fail(e, "residual dense branch backward");
     if ((e = moe::launch_decode_bwd(s, dout, y, gates, idx, loc, capacity, dy, dgates, strm)) != hipSuccess)
         return hip_fail(e, "decode backward");
     if (gate) {
@@ -733,15 +784,46 @@ moe_status moe_layer_backward(const moe_shape *shape, const void *dout, const vo
     if ((e = moe::launch_expert_ffn_bwd(s, buf, pre, h, W1, W2, fill, capacity, dy, dpre, dbuf, dW1, db1, dW2, db2,
                                         cmax, strm)) != hipSuccess)
         return hip_fail(e, "expert ffn backward");
+    const void *dxres = res != nullptr ? res->dx_r : nullptr;
     if (gate && Wg != nullptr)
-        e = moe::launch_gate_dx(s, dbuf, idx, loc, capacity, dlogits, Wg, dx, strm);
+        e = moe::launch_gate_dx(s, dbuf, idx, loc, capacity, dlogits, Wg, dx, strm, dxres);
     else
-        e = moe::launch_decode(s, dbuf, nullptr, idx, loc, capacity, dx, true, strm);
+        e = moe::launch_decode(s, dbuf, nullptr, idx, loc, capacity, dx, true, strm, dxres);
     if (e != hipSuccess) return hip_fail(e, "encode backward");
     return MOE_OK;
 }
 
-const char *moe_last_error(void) { return g_last_error.c_str(); }
+}  // namespace
+
+extern "C" {
+
+moe_status moe_layer_backward(const moe_shape *shape, const void *dout, const void *buf, const void *pre,
+                              const void *h, const void *y, const float *gates, const int32_t *idx,
+                              const int32_t *loc, const int32_t *fill, const int32_t *capacity, const void *W1,
+                              const void *W2, void *dy, void *dpre, void *dbuf, void *dx, float *dW1, float *db1,
+                              float *dW2, float *db2, float *dgates, const float *logits, const int32_t *needed,
+                              double aux_coef, const void *x, const float *Wg, float *dlogits, float *dWg,
+                              float *aux_loss, void *ws, size_t ws_bytes, void *stream) {
+    return layer_backward_impl(shape, dout, buf, pre, h, y, gates, idx, loc, fill, capacity, W1, W2, dy, dpre, dbuf,
+                               dx, dW1, db1, dW2, db2, dgates, logits, needed, aux_coef, x, Wg, dlogits, dWg, aux_loss,
+                               ws, ws_bytes, nullptr, stream);
+}
+
+moe_status moe_residual_layer_backward(const moe_shape *shape, const void *dout, const void *buf, const void *pre,
+                                       const void *h, const void *y, const float *gates, const int32_t *idx,
+                                       const int32_t *loc, const int32_t *fill, const int32_t *capacity,
+                                       const void *W1, const void *W2, void *dy, void *dpre, void *dbuf, void *dx,
+                                       float *dW1, float *db1, float *dW2, float *db2, float *dgates,
+                                       const float *logits, const int32_t *needed, double aux_coef, const void *x,
+                                       const float *Wg, float *dlogits, float *dWg, float *aux_loss,
+                                       const void *W1r, const void *W2r, const void *pre_r, const void *h_r,
+                                       void *dpre_r, void *dx_r, float *dW1r, float *db1r, float *dW2r, float *db2r,
+                                       void *ws, size_t ws_bytes, void *stream) {
+    const ResidualGrad res{W1r, W2r, pre_r, h_r, dpre_r, dx_r, dW1r, db1r, dW2r, db2r};
+    return layer_backward_impl(shape, dout, buf, pre, h, y, gates, idx, loc, fill, capacity, W1, W2, dy, dpre, dbuf,
+                               dx, dW1, db1, dW2, db2, dgates, logits, needed, aux_coef, x, Wg, dlogits, dWg, aux_loss,
+                               ws, ws_bytes, &res, stream);
+}
 
 }  // extern "C"
 

@@ -194,14 +194,22 @@ hipError_t launch_encode(const moe_shape &s, const void *x, const int32_t *idx, 
                          const int32_t *fill, const int32_t *cap, void *buf, int32_t cmax,
                          hipStream_t st);
 // Gate-weighted combine (unit_gates = false) or plain gather-sum (gates ignored);
-// yres (gate-weighted combine only): Residual-MoE's dense-branch rows, added before the rounding.
+// yres: Residual-MoE's dense-branch rows (y_r, or dx_r in the encode backward),
+// added after the routes, before the rounding.
 hipError_t launch_decode(const moe_shape &s, const void *y, const float *gates, const int32_t *idx,
                          const int32_t *loc, const int32_t *cap, void *out, bool unit_gates,
                          hipStream_t st, const void *yres = nullptr);
-// Residual-MoE dense branch: h_r = act(x W1r^T + b1r), y_r = h_r W2r^T + b2r over all S
-// tokens; dense_rows is 2 int32 of device scratch (the branch's row count and "capacity").
+// Residual-MoE dense branch: pre_r = x W1r^T + b1r (stored when pre_r is non-NULL),
+// h_r = act(pre_r), y_r = h_r W2r^T + b2r over all S tokens; dense_rows is 2 int32 of
+// device scratch (the branch's row count and "capacity").
 hipError_t launch_residual_ffn(const moe_shape &s, const void *x, const void *W1r, const void *b1r,
-                               const void *W2r, const void *b2r, void *h_r, void *y_r, int32_t *dense_rows,
+                               const void *W2r, const void *b2r, void *pre_r, void *h_r, void *y_r,
+                               int32_t *dense_rows, hipStream_t st);
+// Its backward for upstream gradient dout [S, M]: dpre_r, dx_r = dpre_r W1r (stored),
+// dW1r, db1r, dW2r, db2r (fp32; the bias gradients may be NULL).
+hipError_t launch_residual_bwd(const moe_shape &s, const void *dout, const void *x, const void *pre_r,
+                               const void *h_r, const void *W1r, const void *W2r, void *dpre_r, void *dx_r,
+                               float *dW1r, float *db1r, float *dW2r, float *db2r, int32_t *dense_rows,
                                hipStream_t st);
 hipError_t launch_decode_bwd(const moe_shape &s, const void *dout, const void *y, const float *gates,
                              const int32_t *idx, const int32_t *loc, const int32_t *cap, void *dy,
@@ -222,8 +230,10 @@ hipError_t launch_gate_backward(const moe_shape &s, const float *logits, const i
                                 hipStream_t st);
 hipError_t launch_gate_weight_grad(const moe_shape &s, const void *x, const float *dlogits, float *dWg, void *ws,
                                    hipStream_t st);
+// dxres (may be NULL): Residual-MoE's dense-branch dx_r rows, added last before the rounding.
 hipError_t launch_gate_dx(const moe_shape &s, const void *dbuf, const int32_t *idx, const int32_t *loc,
-                          const int32_t *cap, const float *dlogits, const float *Wg, void *dx, hipStream_t st);
+                          const int32_t *cap, const float *dlogits, const float *Wg, void *dx, hipStream_t st,
+                          const void *dxres = nullptr);
 // MX: quantise a row-major [rows, K] matrix (K a multiple of 32) of the data type;
 // encode with the token rows quantised to MXFP8; the expert FFN on MX operands.
 hipError_t launch_mx_quantize(int fmt, int64_t rows, int32_t K, int dtype, const void *src, uint8_t *codes,

@@ -251,15 +251,33 @@ moe_status moe_layer_forward_mx(const moe_shape *shape, int32_t wfmt, const void
  * PR-MoE): every token also passes through one fixed dense MLP, and its output
  * is added to the MoE output. The dense branch has the experts' form with its
  * own weights over all S tokens:
- *   h_r = act(x . W1r^T + b1r)   stored in the data type
- *   y_r = h_r . W2r^T + b2r       (fp32 accumulation), stored
+ *   pre_r = x . W1r^T + b1r       (fp32 accumulation), stored if pre_r != NULL
+ *   h_r   = act(pre_r)            stored in the data type
+ *   y_r   = h_r . W2r^T + b2r      (fp32 accumulation), stored
  * W1r [H, M], b1r [H] (NULL iff !has_fc1_bias), W2r [M, H], b2r [M] (NULL iff
- * !has_fc2_bias); x, y_r [S, M]; h_r [S, H]; ws: moe_workspace_size() bytes (8
- * bytes of it hold the branch's row count for the grouped GEMMs). Supported
- * for S < 128 * 65535. */
+ * !has_fc2_bias); x, y_r [S, M]; pre_r, h_r [S, H] (pre_r is kept for the
+ * backward; NULL for inference); ws: moe_workspace_size() bytes (8 bytes of it
+ * hold the branch's row count for the grouped GEMMs). Supported for
+ * S < 128 * 65535. */
 moe_status moe_residual_ffn(const moe_shape *shape, const void *x, const void *W1r, const void *b1r,
-                            const void *W2r, const void *b2r, void *h_r, void *y_r, void *ws,
+                            const void *W2r, const void *b2r, void *pre_r, void *h_r, void *y_r, void *ws,
                             size_t ws_bytes, void *stream);
+
+/* Backward of the dense branch for the layer's upstream gradient dout [S, M]
+ * (the branch's output is added to the layer output, so its output gradient
+ * is dout itself), the same definitions as the experts' backward with the
+ * branch as one expert over all S rows:
+ *   dpre_r = (dout . W2r) * act'(pre_r), stored, with pre_r the forward's
+ *            stored pre-activation;       dx_r = dpre_r . W1r, stored
+ *   dW2r = sum_s dout_s^T h_r,s, db2r = sum_s dout_s,
+ *   dW1r = sum_s dpre_r,s^T x_s, db1r = sum_s dpre_r,s     (fp32)
+ * dpre_r [S, H] and dx_r [S, M] are caller buffers in the data type; dW1r
+ * [H, M], dW2r [M, H] fp32 (overwritten; zeros when S == 0); db1r [H], db2r
+ * [M] fp32 or NULL (not computed). ws: moe_workspace_size() bytes. */
+moe_status moe_residual_backward(const moe_shape *shape, const void *dout, const void *x, const void *pre_r,
+                                 const void *h_r, const void *W1r, const void *W2r, void *dpre_r, void *dx_r,
+                                 float *dW1r, float *db1r, float *dW2r, float *db2r, void *ws, size_t ws_bytes,
+                                 void *stream);
 
 /* moe_decode with the Residual-MoE add fused in: the fp32 sum over the kept
  * routes (as in moe_decode) gains y_r[s] after the last route, then is rounded
@@ -328,15 +346,15 @@ moe_status moe_layer_forward_noalloc(const moe_shape *shape, const void *x, cons
                                      void *buf, void *pre, void *h, void *y, void *out, void *stream);
 
 /* moe_layer_forward of a Residual-MoE layer: the same steps, plus the dense
- * branch (moe_residual_ffn: W1r, b1r, W2r, b2r -> h_r, y_r) before decode,
- * and decode as moe_decode_residual. Forward only. */
+ * branch (moe_residual_ffn: W1r, b1r, W2r, b2r -> pre_r, h_r, y_r; pre_r may
+ * be NULL for inference) before decode, and decode as moe_decode_residual. */
 moe_status moe_residual_layer_forward(const moe_shape *shape, const void *x, const float *logits_in,
                                       const float *Wg, float *logits_out, const void *W1, const void *b1,
                                       const void *W2, const void *b2, const void *W1r, const void *b1r,
                                       const void *W2r, const void *b2r, int32_t *idx, int32_t *loc,
                                       float *gates, int32_t *needed, int32_t *fill, int32_t *capacity,
                                       int32_t *slot_route, void *buf, void *pre, void *h, void *y,
-                                      void *h_r, void *y_r, void *out, void *ws, size_t ws_bytes,
+                                      void *pre_r, void *h_r, void *y_r, void *out, void *ws, size_t ws_bytes,
                                       void *stream);
 
 /* moe_layer_forward with the expert FFN pipelined over the capacity dimension
@@ -388,6 +406,25 @@ moe_status moe_layer_backward(const moe_shape *shape, const void *dout, const vo
                               float *db2, float *dgates, const float *logits, const int32_t *needed,
                               double aux_coef, const void *x, const float *Wg, float *dlogits,
                               float *dWg, float *aux_loss, void *ws, size_t ws_bytes, void *stream);
+
+/* moe_layer_backward of a Residual-MoE layer (MoE training blog, part 1
+ * section 1.2: out = MoE output + the dense branch's y_r): the same arguments
+ * and results, plus the dense branch's backward (moe_residual_backward: W1r,
+ * W2r, the forward's pre_r and h_r -> dpre_r, dx_r, dW1r, db1r, dW2r, db2r),
+ * and dx[s] = the kept dbuf rows (+ the gate projection's share) + dx_r[s],
+ * added in fp32 after the other terms, rounded once to the data type. x is
+ * required; dx_r must not be dx. ws: moe_workspace_size() bytes (always). */
+moe_status moe_residual_layer_backward(const moe_shape *shape, const void *dout, const void *buf,
+                                       const void *pre, const void *h, const void *y, const float *gates,
+                                       const int32_t *idx, const int32_t *loc, const int32_t *fill,
+                                       const int32_t *capacity, const void *W1, const void *W2, void *dy,
+                                       void *dpre, void *dbuf, void *dx, float *dW1, float *db1, float *dW2,
+                                       float *db2, float *dgates, const float *logits, const int32_t *needed,
+                                       double aux_coef, const void *x, const float *Wg, float *dlogits,
+                                       float *dWg, float *aux_loss, const void *W1r, const void *W2r,
+                                       const void *pre_r, const void *h_r, void *dpre_r, void *dx_r,
+                                       float *dW1r, float *db1r, float *dW2r, float *db2r, void *ws,
+                                       size_t ws_bytes, void *stream);
 
 /* The stages of moe_layer_backward as calls of their own (same definitions,
  * same buffers), for callers that schedule or time them separately:

@@ -84,7 +84,7 @@ def lib():
         L.oracle_weight_grads.restype = None
         L.oracle_dgates.argtypes = [i32, i32, ctypes.c_int, i64, _c_i32p, vp, vp, _c_f32p]
         L.oracle_dgates.restype = None
-        L.oracle_dx.argtypes = [i32, i32, ctypes.c_int, vp, i64, _c_i64p, i32, vp, vp, vp]
+        L.oracle_dx.argtypes = [i32, i32, ctypes.c_int, vp, i64, _c_i64p, i32, vp, vp, vp, vp]
         L.oracle_dx.restype = None
         u8p = np.ctypeslib.ndpointer(dtype=np.uint8, flags="C_CONTIGUOUS")
         L.oracle_e4m3_value.argtypes = [ctypes.c_int]; L.oracle_e4m3_value.restype = d
@@ -265,21 +265,71 @@ def decode(y: np.ndarray, rt: Dict, E: int, dtype: int, tokens: Optional[Sequenc
     return out
 
 
-def residual_mlp(x: np.ndarray, W1r, b1r, W2r, b2r, act_kind: int, dtype: int, tokens=None):
+def residual_mlp(x: np.ndarray, W1r, b1r, W2r, b2r, act_kind: int, dtype: int, tokens=None, want_pre=False):
     """Residual-MoE's dense branch: the FFN of the experts' form, with its own weights
-    (W1r [H, M], W2r [M, H]), over the listed tokens (all by default). Returns (h, y) compact."""
+    (W1r [H, M], W2r [M, H]), over the listed tokens (all by default). Returns (h, y) compact,
+    or (pre, h, y) with want_pre (the stored pre-activation the backward reads)."""
     S = x.shape[0]
     tok = np.arange(S, dtype=np.int64) if tokens is None else np.asarray(tokens, np.int64)
-    _, h, y = expert_rows(x, W1r[None], None if b1r is None else b1r[None], W2r[None],
-                          None if b2r is None else b2r[None], tok, S, act_kind, dtype, want_h=True)
-    return h, y
+    pre, h, y = expert_rows(x, W1r[None], None if b1r is None else b1r[None], W2r[None],
+                            None if b2r is None else b2r[None], tok, S, act_kind, dtype, want_pre=want_pre,
+                            want_h=True)
+    return (pre, h, y) if want_pre else (h, y)
+
+
+def residual_backward(inp: Dict[str, np.ndarray], act_kind: int, dtype: int, h_r: Optional[np.ndarray] = None,
+                      tokens=None, want_wgrad: bool = True) -> Dict[str, np.ndarray]:
+    """Backward of Residual-MoE's dense branch for the layer's upstream gradient inp["dout"]
+    (the branch's output adds to the layer output, so its output gradient is dout): the
+    experts' per-row backward with the branch as one expert over the S token rows and every
+    gate 1, so dy = dout; dpre_r and dx_r (= the row backward's dbuf) for the listed tokens
+    (all by default), compact. With want_wgrad (all tokens) also dW1r, db1r, dW2r, db2r (fp32)
+    from h_r (the forward's; recomputed when not given)."""
+    x = _check(inp["x"], dtype)
+    S, M = x.shape
+    dout = _check(inp["dout"], dtype, (S, M))
+    W1r, W2r = inp["W1r"], inp["W2r"]
+    H = W1r.shape[0]
+    b1r = inp.get("b1r")
+    tok = np.arange(S, dtype=np.int64) if tokens is None else np.ascontiguousarray(np.asarray(tokens, np.int64))
+    n = tok.shape[0]
+    et = elem_dtype(dtype)
+    dpre = np.empty((n, H), et)
+    dxr = np.empty((n, M), et)
+    ones = np.ones((S,), np.float32)
+    lib().oracle_backward_rows(S, M, H, 1, max(S, 1), dtype, act_kind, _ptr(x), _ptr(_check(W1r[None], dtype)),
+                               _ptr(None if b1r is None else _check(b1r[None], dtype)),
+                               _ptr(_check(W2r[None], dtype)), ones, _ptr(dout), n, tok,
+                               np.ascontiguousarray(tok.astype(np.int32)), None, _ptr(dpre), _ptr(dxr))
+    out = dict(dpre_r=dpre, dx_r=dxr)
+    if want_wgrad:
+        assert tokens is None, "the weight gradients sum over every token"
+        if h_r is None:
+            h_r, _ = residual_mlp(x, W1r, b1r, W2r, inp.get("b2r"), act_kind, dtype)
+        out["dW1r"], out["db1r"], out["dW2r"], out["db2r"] = weight_grads(dout, h_r, dpre, x, dtype)
+    return out
+
+
+def residual_backward_cols(inp: Dict[str, np.ndarray], hcols, act_kind: int, dtype: int):
+    """The dense branch's weight and bias gradients on the listed hidden columns, summed over
+    every token (for sampling large layers): (dW1r[hcols], db1r[hcols], dW2r[:, hcols], db2r),
+    fp32. The branch is one expert over the S token rows with every gate 1 (dy = dout)."""
+    x = inp["x"]
+    S = x.shape[0]
+    rt = dict(C=max(S, 1), idx=np.zeros((1, S), np.int32), gates=np.ones((1, S), np.float32),
+              slot_route=np.arange(S, dtype=np.int32))
+    one = dict(W1=inp["W1r"][None], W2=inp["W2r"][None], dout=inp["dout"])
+    if inp.get("b1r") is not None:
+        one["b1"] = inp["b1r"][None]
+    _, dy, hv, dpre = backward_cols(rt, x, one, np.arange(S), hcols, act_kind, dtype)
+    return weight_grads(dy, hv, dpre, x, dtype)
 
 
 def layer_forward(inp: Dict[str, np.ndarray], k: int, f: float, act_kind: int, dtype: int,
                   logits: Optional[np.ndarray] = None) -> Dict:
     """The whole forward for small shapes: returns route tables, buf, pre, h, y (full E*C rows,
     padding rows of pre/h/y left zero) and out. With the Residual-MoE weights in inp (W1r, W2r,
-    and b1r/b2r when the biases are on) also h_r, y_r and out = MoE output + y_r."""
+    and b1r/b2r when the biases are on) also pre_r, h_r, y_r and out = MoE output + y_r."""
     x = inp["x"]
     if logits is None:
         logits = inp["logits"] if "logits" in inp else gate_logits(x, inp["Wg"], dtype)
@@ -297,8 +347,8 @@ def layer_forward(inp: Dict[str, np.ndarray], k: int, f: float, act_kind: int, d
     y = np.zeros((E * rt["C"], M), et); y[rows] = y_r
     res = {}
     if "W1r" in inp:
-        res["h_r"], res["y_r"] = residual_mlp(x, inp["W1r"], inp.get("b1r"), inp["W2r"], inp.get("b2r"), act_kind,
-                                              dtype)
+        res["pre_r"], res["h_r"], res["y_r"] = residual_mlp(x, inp["W1r"], inp.get("b1r"), inp["W2r"], inp.get("b2r"),
+                                                            act_kind, dtype, want_pre=True)
     out = decode(y, rt, E, dtype, yres=res.get("y_r"))
     return dict(logits=logits, route=rt, buf=buf, pre=pre, h=h, y=y, out=out, rows=rows, **res)
 
@@ -372,9 +422,11 @@ def dgates(routes: np.ndarray, dout: np.ndarray, yrows: np.ndarray, S: int, dtyp
 
 
 def dx_tokens(routes: np.ndarray, dbufrows: np.ndarray, tokens: Sequence[int], S: int, k: int,
-              dtype: int, dlogits: Optional[np.ndarray] = None, Wg: Optional[np.ndarray] = None) -> np.ndarray:
+              dtype: int, dlogits: Optional[np.ndarray] = None, Wg: Optional[np.ndarray] = None,
+              res: Optional[np.ndarray] = None) -> np.ndarray:
     """dx of the listed tokens from the dbuf rows of kept routes (routes[i] = r*S + s), plus
-    dlogits[token] . Wg^T when the gate projection's gradient (fp64 dlogits [S,E]) is given."""
+    dlogits[token] . Wg^T when the gate projection's gradient (fp64 dlogits [S,E]) is given,
+    plus the Residual-MoE dense branch's dx_r rows (res, [S, M] in the data type) when given."""
     routes = np.asarray(routes, dtype=np.int64)
     tok = np.asarray(tokens, dtype=np.int64)
     pos = {int(t): i for i, t in enumerate(tok)}
@@ -391,8 +443,9 @@ def dx_tokens(routes: np.ndarray, dbufrows: np.ndarray, tokens: Sequence[int], S
         dl = np.ascontiguousarray(np.asarray(dlogits, np.float64)[tok])
         wg = np.ascontiguousarray(Wg, dtype=np.float32)
         assert wg.shape == (M, E)
+    rr = None if res is None else np.ascontiguousarray(_check(res, dtype, (S, M))[tok])
     lib().oracle_dx(M, k, dtype, _ptr(np.ascontiguousarray(dbufrows)), tok.shape[0],
-                    np.ascontiguousarray(table), E, _ptr(dl), _ptr(wg), _ptr(out))
+                    np.ascontiguousarray(table), E, _ptr(dl), _ptr(wg), _ptr(rr), _ptr(out))
     return out
 
 
@@ -430,7 +483,9 @@ def layer_backward(fw: Dict, inp: Dict, act_kind: int, dtype: int, aux_coef: Opt
     """The whole backward for small shapes: dx, dW1, db1, dW2, db2 (fp32) and dgates [k,S]
     (0 for dropped routes). With aux_coef given, also the gate backward: dlogits (fp64) and
     aux_loss from the forward's logits, and, when the logits were projected (inp has Wg),
-    dWg (fp64) and the gate projection's share of dx."""
+    dWg (fp64) and the gate projection's share of dx. With the Residual-MoE weights in inp
+    (W1r, W2r), also the dense branch's dpre_r, dx_r, dW1r, db1r, dW2r, db2r, and dx_r is
+    added to dx."""
     rt = fw["route"]
     C = rt["C"]
     k, S = rt["idx"].shape
@@ -459,7 +514,12 @@ def layer_backward(fw: Dict, inp: Dict, act_kind: int, dtype: int, aux_coef: Opt
             out["dWg"] = gate_weight_grad(inp["x"], dl, dtype)
         else:
             dl = None
-    out["dx"] = dx_tokens(routes, dbuf, np.arange(S), S, k, dtype, dlogits=dl, Wg=Wg)
+    dxr = None
+    if "W1r" in inp:
+        rb = residual_backward(inp, act_kind, dtype, h_r=fw.get("h_r"))
+        out.update(rb)
+        dxr = rb["dx_r"]
+    out["dx"] = dx_tokens(routes, dbuf, np.arange(S), S, k, dtype, dlogits=dl, Wg=Wg, res=dxr)
     return out
 
 

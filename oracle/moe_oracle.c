@@ -507,10 +507,13 @@ void oracle_dgates(int32_t S, int32_t M, int dtype, int64_t n, const int32_t *ro
 /* dx[s][m] = sum over the token's kept routes of dbuf[slot][m] in route order
  * (fp64), rounded to the data type. dbufrows [n, M] holds dbuf rows; for token
  * t, route_rows[t*k + r] is the dbuf row of its route r, or -1 when that route
- * was dropped. dx is [ntok, M]. */
+ * was dropped. dx is [ntok, M]. With dlog_rows, the gate projection's share
+ * dlogits[t] . Wg^T is added; with res_rows ([ntok, M] in the data type), the
+ * Residual-MoE dense branch's dx_r row (the branch's output is added to the
+ * layer output, so its input gradient adds to dx), after the other terms. */
 void oracle_dx(int32_t M, int32_t k, int dtype, const void *dbufrows, int64_t ntok,
                const int64_t *route_rows, int32_t E, const double *dlog_rows, const float *Wg,
-               void *dx) {
+               const void *res_rows, void *dx) {
     for (int64_t t = 0; t < ntok; ++t)
         for (int32_t m = 0; m < M; ++m) {
             double acc = 0.0;
@@ -520,6 +523,7 @@ void oracle_dx(int32_t M, int32_t k, int dtype, const void *dbufrows, int64_t nt
             }
             if (dlog_rows != NULL) /* the gate projection's share: dlogits[t] . Wg[m]^T */
                 for (int32_t e = 0; e < E; ++e) acc += dlog_rows[t * E + e] * (double)Wg[(int64_t)m * E + e];
+            if (res_rows != NULL) acc += load_elem(res_rows, dtype, t * M + m);
             store_elem(dx, dtype, t * M + m, acc);
         }
 }

@@ -32,7 +32,7 @@ def odd_ptr():
 
 def test_every_declared_symbol_is_exported(moe):
     names = _declared()
-    assert len(names) == 33, names
+    assert len(names) == 35, names
     lib = ctypes.CDLL(moe.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -129,6 +129,26 @@ def test_entry_points_reject_before_enqueueing(moe):
     st = lib.moe_layer_backward(ctypes.byref(c), *full[:21], None, None, 0.0, None, None, fake, None, None,
                                 None, 0, None)
     assert st == moe.MOE_EINVAL and "logits" in moe.moe_last_error()
+    # Residual-MoE backward: the dense branch alone, and inside the layer backward
+    st = lib.moe_residual_backward(ctypes.byref(c), fake, fake, fake, fake, None, fake, fake, fake, fake, None, fake,
+                                   None, fake, 1 << 20, None)
+    assert st == moe.MOE_EINVAL and "W1r" in moe.moe_last_error()
+    st = lib.moe_residual_backward(ctypes.byref(c), fake, fake, fake, fake, fake, fake, fake, fake, fake, None, fake,
+                                   None, fake, 1, None)
+    assert st == moe.MOE_EWORKSPACE
+    other = ctypes.c_void_p(0x2000)
+    res = [fake, fake, fake, fake, fake, other, fake, None, fake, None]  # W1r .. db2r (dx_r distinct from dx)
+    st = lib.moe_residual_layer_backward(ctypes.byref(c), *full[:21], None, None, 0.0, fake, None, None, None, None,
+                                         *res, None, 0, None)
+    assert st == moe.MOE_EWORKSPACE  # the dense branch always needs the workspace
+    dx = full[15]
+    same = res[:5] + [dx] + res[6:]  # dx_r aliasing dx
+    st = lib.moe_residual_layer_backward(ctypes.byref(c), *full[:21], None, None, 0.0, fake, None, None, None, None,
+                                         *same, fake, 1 << 20, None)
+    assert st == moe.MOE_EINVAL and "dx_r" in moe.moe_last_error()
+    st = lib.moe_residual_layer_backward(ctypes.byref(c), *full[:21], None, None, 0.0, None, None, None, None, None,
+                                         *res, fake, 1 << 20, None)
+    assert st == moe.MOE_EINVAL and "x" in moe.moe_last_error()  # the dense branch reads x
     with pytest.raises(moe.MoeError):
         moe._check(lib.moe_decode(ctypes.byref(c), None, None, None, None, None, None, None))
     odd = odd_ptr()

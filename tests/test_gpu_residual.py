@@ -1,6 +1,7 @@
 """GPU parity of Residual-MoE (a dense MLP branch every token passes through, added to
 the MoE output in the decode's fp32 sum) against the CPU oracle: the dense branch on
-its own, the residual decode bit for bit given the same inputs, and the fused layer."""
+its own, forward and backward, the residual decode bit for bit given the same inputs,
+and the fused layer, forward and backward."""
 from __future__ import annotations
 
 import numpy as np
@@ -9,8 +10,9 @@ import torch
 
 import oracle
 import workloads as W
-from tests.gpu_helpers import check_close, check_logits, decode_extra, dev, host, inputs_np, shape_of
-from tests.helpers import f32_of
+from tests.gpu_helpers import (check_close, check_dlogits, check_logits, decode_extra, dev, dgates_err, host,
+                               inputs_np, shape_of)
+from tests.helpers import bf16_bits_of_f32, f32_of
 
 pytestmark = pytest.mark.gpu
 
@@ -32,14 +34,63 @@ def test_residual_ffn_matches_oracle(S, M, H, dtype, act, bias):
     s = shape_of(w)
     d = {k_: v.cuda() for k_, v in inp.items()}
     ws = torch.empty(max(1, moe.moe_workspace_size(s)), dtype=torch.uint8, device="cuda")
+    pre_r = torch.empty(S, H, dtype=w.torch_dtype, device="cuda")
     h_r = torch.empty(S, H, dtype=w.torch_dtype, device="cuda")
     y_r = torch.empty(S, M, dtype=w.torch_dtype, device="cuda")
-    moe.moe_residual_ffn(s, d["x"], d["W1r"], d.get("b1r"), d["W2r"], d.get("b2r"), h_r, y_r, ws)
+    moe.moe_residual_ffn(s, d["x"], d["W1r"], d.get("b1r"), d["W2r"], d.get("b2r"), pre_r, h_r, y_r, ws)
     torch.cuda.synchronize()
     ni = inputs_np(inp)
-    h_o, y_o = oracle.residual_mlp(ni["x"], ni["W1r"], ni.get("b1r"), ni["W2r"], ni.get("b2r"), act, dtype)
+    p_o, h_o, y_o = oracle.residual_mlp(ni["x"], ni["W1r"], ni.get("b1r"), ni["W2r"], ni.get("b2r"), act, dtype,
+                                        want_pre=True)
+    check_close(host(pre_r), p_o, dtype, "pre_r")
     check_close(host(h_r), h_o, dtype, "h_r")
     check_close(host(y_r), y_o, dtype, "y_r")
+    # without pre_r (inference) the branch's outputs are the same bits
+    h2, y2 = torch.empty_like(h_r), torch.empty_like(y_r)
+    moe.moe_residual_ffn(s, d["x"], d["W1r"], d.get("b1r"), d["W2r"], d.get("b2r"), None, h2, y2, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(h2.view(torch.uint8), h_r.view(torch.uint8)) and torch.equal(y2.view(torch.uint8),
+                                                                                    y_r.view(torch.uint8))
+
+
+@pytest.mark.parametrize("S,M,H,dtype,act,bias", FFN_CASES, ids=lambda v: str(v))
+def test_residual_backward_matches_oracle(S, M, H, dtype, act, bias):
+    # the dense branch's backward on its own: dpre_r, dx_r (stored) and the fp32 weight and
+    # bias gradients summed over every token
+    import combine_softmax_top_amd as moe
+    print(f"[residual backward] S={S} M={M} H={H} dtype={dtype} act={act} bias={bias}", flush=True)
+    w = W.Workload("resb", S=S, M=M, E=2, k=1, H=H, capacity_factor=1.0, dtype=dtype, act=act, has_fc1_bias=bias,
+                   has_fc2_bias=bias, residual=True)
+    inp = W.make_inputs(w, seed=1, with_dout=True)
+    s = shape_of(w)
+    d = {k_: v.cuda() for k_, v in inp.items()}
+    dt = w.torch_dtype
+    f32 = dict(dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(1, moe.moe_workspace_size(s)), dtype=torch.uint8, device="cuda")
+    pre_r, h_r = torch.empty(S, H, dtype=dt, device="cuda"), torch.empty(S, H, dtype=dt, device="cuda")
+    y_r = torch.empty(S, M, dtype=dt, device="cuda")
+    moe.moe_residual_ffn(s, d["x"], d["W1r"], d.get("b1r"), d["W2r"], d.get("b2r"), pre_r, h_r, y_r, ws)
+    dpre_r, dx_r = torch.empty(S, H, dtype=dt, device="cuda"), torch.empty(S, M, dtype=dt, device="cuda")
+    # gradients start as NaN: the call must overwrite every element
+    dW1r, dW2r = torch.full((H, M), float("nan"), **f32), torch.full((M, H), float("nan"), **f32)
+    db1r = torch.full((H,), float("nan"), **f32) if bias else None
+    db2r = torch.full((M,), float("nan"), **f32) if bias else None
+    moe.moe_residual_backward(s, d["dout"], d["x"], pre_r, h_r, d["W1r"], d["W2r"], dpre_r, dx_r, dW1r, db1r, dW2r,
+                              db2r, ws)
+    torch.cuda.synchronize()
+    if S == 0:
+        for t in (dW1r, dW2r) + ((db1r, db2r) if bias else ()):
+            assert (host(t) == 0).all()
+        return
+    ni = inputs_np(inp)
+    rb = oracle.residual_backward(ni, act, dtype)
+    check_close(host(dpre_r), rb["dpre_r"], dtype, "dpre_r")
+    check_close(host(dx_r), rb["dx_r"], dtype, "dx_r")
+    check_close(host(dW1r), rb["dW1r"], dtype, "dW1r")
+    check_close(host(dW2r), rb["dW2r"], dtype, "dW2r")
+    if bias:
+        check_close(host(db1r), rb["db1r"], dtype, "db1r")
+        check_close(host(db2r), rb["db2r"], dtype, "db2r")
 
 
 @pytest.mark.parametrize("dtype", [W.DT_BF16, W.DT_F32])
@@ -111,3 +162,59 @@ def test_residual_layer_forward_matches_oracle(w):
     dropped = np.nonzero((rt["loc"] >= rt["C"]).all(axis=0))[0]
     if len(dropped):
         assert np.array_equal(host(b["out"])[dropped].view(np.uint8), host(b["y_r"])[dropped].view(np.uint8))
+
+
+@pytest.mark.parametrize("w", RES, ids=lambda w: w.name)
+def test_residual_layer_backward_matches_oracle(w):
+    # the fused training step of a Residual-MoE layer: the MoE backward, the dense branch's
+    # backward, and dx = the kept dbuf rows (+ the gate share) + dx_r, rounded once
+    import combine_softmax_top_amd as moe
+    print(f"[residual layer backward] {w.name}", flush=True)
+    inp = W.make_inputs(w, seed=2, with_dout=True)
+    s = shape_of(w)
+    d = {k_: v.cuda() for k_, v in inp.items()}
+    gate = w.logits == "gate"
+    res = {n: d.get(n) for n in ("W1r", "b1r", "W2r", "b2r")}
+    b = moe.layer_forward(s, d["x"], d["W1"], d.get("b1"), d["W2"], d.get("b2"), logits=d.get("logits"),
+                          Wg=d.get("Wg"), training=True, residual=res)
+    gr = moe.layer_backward(s, b, d["dout"], d["W1"], d["W2"], logits=b["logits"] if gate else None, x=d["x"],
+                            Wg=d.get("Wg"), residual=res)
+    torch.cuda.synchronize()
+    ni = inputs_np(inp)
+    glog = None
+    if gate:
+        glog = host(b["logits"])
+        check_logits(glog, oracle.gate_logits(ni["x"], ni["Wg"], w.dtype), ni["x"], ni["Wg"])
+    fw = oracle.layer_forward(ni, w.k, w.capacity_factor, w.act, w.dtype, logits=glog)
+    bw = oracle.layer_backward(fw, ni, w.act, w.dtype, aux_coef=moe.AUX_COEF if gate else None)
+    rt = fw["route"]
+    check_close(host(b["pre_r"]), fw["pre_r"], w.dtype, "pre_r")
+    for n in ("dpre_r", "dx_r", "dW1r", "dW2r") + (("db1r", "db2r") if w.has_fc1_bias else ()):
+        check_close(host(gr[n]), bw[n], w.dtype, n)
+    check_close(host(gr["dW1"]), bw["dW1"], w.dtype, "dW1")
+    check_close(host(gr["dW2"]), bw["dW2"], w.dtype, "dW2")
+    # dx: both sides' dbuf rows and dx_r rows (each within tolerance) carried through the sum
+    rows = fw["rows"]
+    extra = decode_extra(rt, rows, host(gr["dbuf"])[rows], bw["dbuf"], gated=False)
+    extra += np.abs(f32_of(host(gr["dx_r"])).astype(np.float64) - f32_of(bw["dx_r"]).astype(np.float64))
+    if gate:
+        dg_err = dgates_err(bw["dgates"], w.dtype)
+        dg_err[rt["loc"] >= rt["C"]] = 0.0
+        dl_err = check_dlogits(host(gr["dlogits"]), bw["dlogits"], fw["logits"], rt["idx"], bw["dgates"],
+                               rt["needed"], w.k, w.S, moe.AUX_COEF, dg_err=dg_err)
+        extra += dl_err @ np.abs(ni["Wg"].astype(np.float64)).T
+    check_close(host(gr["dx"]), bw["dx"], w.dtype, "dx", extra=extra)
+    # given the GPU's own dbuf and dx_r rows (and no gate share), dx is their fp32 sum rounded once
+    if not gate:
+        dbuf = f32_of(host(gr["dbuf"])).astype(np.float32)
+        want = np.zeros((w.S, w.M), np.float32)
+        for r in range(w.k):
+            kept = rt["loc"][r] < rt["C"]
+            slot = rt["idx"][r].astype(np.int64) * rt["C"] + rt["loc"][r]
+            want[kept] = want[kept] + dbuf[slot[kept]]
+        want = want + f32_of(host(gr["dx_r"])).astype(np.float32)
+        got = f32_of(host(gr["dx"]))
+        if w.dtype == W.DT_F32:
+            assert np.array_equal(got, want)
+        else:
+            assert np.array_equal(host(gr["dx"]).view(np.uint16), bf16_bits_of_f32(want))

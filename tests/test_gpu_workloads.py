@@ -10,7 +10,9 @@ layer output, and, for the workloads with a backward, random gate gradients,
 random tokens of dx with the dpre and dbuf rows behind them, and the
 weight/bias gradients of three experts (hottest, median, coldest) on random
 hidden columns. Residual-MoE: the dense branch's
-output on the sampled tokens, and the layer output with it. The gate backward: the auxiliary
+output on the sampled tokens, and the layer output with it; trained, its dpre_r and
+dx_r on the sampled dx tokens (dx with it) and its weight and bias gradients on random
+hidden columns. The gate backward: the auxiliary
 loss in full; dlogits on the sampled tokens (the oracle's dgates of their
 routes upstream); with a projected gate (small enough for the oracle to run
 every expert row) dgates, dlogits and dWg in full and dx's gate share on the
@@ -52,7 +54,8 @@ def test_full_size_workload(w):
     gr = None
     if w.backward:
         gr = moe.layer_backward(s, b, inp["dout"], inp["W1"], inp["W2"],
-                                logits=b["logits"] if gate else inp["logits"], x=inp["x"], Wg=inp.get("Wg"))
+                                logits=b["logits"] if gate else inp["logits"], x=inp["x"], Wg=inp.get("Wg"),
+                                residual=res)
     torch.cuda.synchronize()
     _say(f"[{w.name}] GPU forward{'+backward' if w.backward else ''} done in {time.time() - t0:.1f}s")
     ni = {k: host(v) for k, v in inp.items()}
@@ -171,8 +174,17 @@ def test_full_size_workload(w):
     rows_t = torch.from_numpy(dx_rows).cuda()
     check_close(host(gr["dpre"][rows_t]), dpre_o, w.dtype, "dpre (sampled rows)")
     check_close(host(gr["dbuf"][rows_t]), dbuf_o, w.dtype, "dbuf (sampled rows)")
+    dxr_full = None
+    if w.residual:
+        # the dense branch's dpre_r and dx_r rows of the sampled tokens, added to their dx
+        rb = oracle.residual_backward(ni, w.act, w.dtype, tokens=dx_toks, want_wgrad=False)
+        tt = torch.from_numpy(dx_toks).cuda()
+        check_close(host(gr["dpre_r"][tt]), rb["dpre_r"], w.dtype, "dpre_r (sampled tokens)")
+        check_close(host(gr["dx_r"][tt]), rb["dx_r"], w.dtype, "dx_r (sampled tokens)")
+        dxr_full = np.zeros((w.S, w.M), rb["dx_r"].dtype)
+        dxr_full[dx_toks] = rb["dx_r"]
     dx_o = oracle.dx_tokens(q, dbuf_o, dx_toks, w.S, w.k, w.dtype, dlogits=dl_o if gate else None,
-                            Wg=ni.get("Wg"))
+                            Wg=ni.get("Wg"), res=dxr_full)
     # dx sums the token's dbuf rows: the two sides' rows (each within tolerance) carried through
     srt = np.argsort(dx_rows)
     extra = decode_extra(rt, dx_rows[srt], host(gr["dbuf"][torch.from_numpy(dx_rows[srt]).cuda()]), dbuf_o[srt],
@@ -180,6 +192,9 @@ def test_full_size_workload(w):
     if gate:
         # dx's gate share: the dlogits bound carried through |Wg|^T
         extra += dl_err[dx_toks] @ np.abs(ni["Wg"].astype(np.float64)).T
+    if w.residual:
+        extra += np.abs(f32_of(host(gr["dx_r"][torch.from_numpy(dx_toks).cuda()])).astype(np.float64)
+                        - f32_of(dxr_full[dx_toks]).astype(np.float64))
     check_close(host(gr["dx"][torch.from_numpy(dx_toks).cuda()]), dx_o, w.dtype, "dx (sampled)", extra=extra)
     _say(f"[{w.name}] dgates on {len(routes)} routes and dx on {len(dx_toks)} tokens within tolerance")
     order = np.argsort(fill)
@@ -203,3 +218,14 @@ def test_full_size_workload(w):
             check_close(host(gr["db2"][e]), db2_o, w.dtype, f"db2[{e}]")
         _say(f"[{w.name}] expert {e} ({len(erows)} rows) weight gradients within tolerance "
              f"({time.time() - t1:.1f}s)")
+    if w.residual:
+        t1 = time.time()
+        dW1r_o, db1r_o, dW2r_o, db2r_o = oracle.residual_backward_cols(ni, hcols, w.act, w.dtype)
+        hc = torch.from_numpy(hcols.astype(np.int64)).cuda()
+        check_close(host(gr["dW1r"][hc]), dW1r_o, w.dtype, f"dW1r (columns {hcols.tolist()})")
+        check_close(host(gr["dW2r"][:, hc]), dW2r_o, w.dtype, f"dW2r (columns {hcols.tolist()})")
+        if w.has_fc1_bias:
+            check_close(host(gr["db1r"][hc]), db1r_o, w.dtype, "db1r")
+        if w.has_fc2_bias:
+            check_close(host(gr["db2r"]), db2r_o, w.dtype, "db2r")
+        _say(f"[{w.name}] dense branch weight gradients within tolerance ({time.time() - t1:.1f}s)")

@@ -836,6 +836,97 @@ def test_residual_branch_ignores_routing():
     assert np.abs(f32_of(a["y_r"]) - r).max() <= 2 ** -6 * np.abs(r).max()
 
 
+@pytest.mark.parametrize("act,k,f,bias", [(W.ACT_GELU, 1, 1.0, True), (W.ACT_RELU, 2, 0.5, False),
+                                          (W.ACT_GELU, 2, 0.0, True)])
+def test_residual_backward_matches_autograd_of_the_two_branches(act, k, f, bias):
+    # fp32 data: out = (one-hot MoE layer) + (dense MLP) in fp64 torch; autograd gives every
+    # gradient, the dense branch's own and dx through both branches
+    S, M, E, H = 20, 8, 3, 12
+    rng = np.random.default_rng(11 + k)
+    r = lambda *shape: (rng.standard_normal(shape) * 0.4).astype(np.float32)  # noqa: E731
+    inp = dict(x=r(S, M) * 2.5, W1=r(E, H, M), W2=r(E, M, H), W1r=r(H, M), W2r=r(M, H), dout=r(S, M) * 2.5)
+    if bias:
+        inp.update(b1=r(E, H), b2=r(E, M), b1r=r(H), b2r=r(M))
+    logits = rng.standard_normal((S, E)).astype(np.float32)
+    fw = oracle.layer_forward(inp, k, f, act, W.DT_F32, logits=logits)
+    bw = oracle.layer_backward(fw, inp, act, W.DT_F32)
+    rt = fw["route"]
+    tt = {n: torch.from_numpy(v).double().requires_grad_(True) for n, v in inp.items() if n != "dout"}
+    zero = lambda shape: torch.zeros(shape, dtype=torch.float64)  # noqa: E731
+    g = torch.from_numpy(rt["gates"]).double()
+    moe_out = _dense_layer_torch(tt["x"], logits, tt["W1"], tt.get("b1", zero((E, H))), tt["W2"],
+                                 tt.get("b2", zero((E, M))), act, E, rt["C"], rt["idx"], rt["loc"], g)
+    dense = _torch_mlp(tt["x"], tt["W1r"], tt.get("b1r"), tt["W2r"], tt.get("b2r"), act)
+    out = moe_out + dense
+    assert np.allclose(fw["out"], out.detach().numpy(), rtol=1e-5, atol=1e-6)
+    names = ["x", "W1r", "W2r"] + (["b1r", "b2r"] if bias else [])
+    grads = torch.autograd.grad((out * torch.from_numpy(inp["dout"]).double()).sum(), [tt[n] for n in names])
+    for n, ref in zip(names, grads):
+        ref = ref.numpy()
+        got = bw["dx" if n == "x" else "d" + n].astype(np.float64)
+        assert np.abs(got - ref).max() / max(np.abs(ref).max(), 1e-30) < 2e-6, n
+    # the dense branch's input gradient on its own: dpre_r W1r
+    xd = tt["x"].detach().clone().requires_grad_(True)
+    d_only = _torch_mlp(xd, *(tt[n].detach() if n in tt else None for n in ("W1r", "b1r", "W2r", "b2r")), act)
+    (ref,) = torch.autograd.grad((d_only * torch.from_numpy(inp["dout"]).double()).sum(), [xd])
+    assert np.abs(bw["dx_r"] - ref.numpy()).max() / np.abs(ref.numpy()).max() < 2e-6
+
+
+@pytest.mark.parametrize("act", [W.ACT_GELU, W.ACT_RELU])
+def test_residual_bf16_backward_rounding_points_match_autograd(act):
+    # bf16 data: fp64 autograd of the dense branch with bf16 stores where the branch stores
+    # bf16 (pre_r as read by the backward, h_r, y_r; the gradients dpre_r and dx_r), and dx
+    # as the fp64 sum of the token's dbuf rows and its dx_r row rounded once. The oracle's
+    # dpre_r and dx_r must equal these bit for bit, dx too, and its fp32 weight and bias
+    # gradients the fp64 sums rounded to fp32 (within one ulp: the summation order differs).
+    S, M, E, H = 24, 16, 3, 24
+    w = W.Workload("resbwd", S=S, M=M, E=E, k=2, H=H, capacity_factor=1.0, act=act, residual=True, backward=True)
+    inp = {n: np_of(v) for n, v in W.make_inputs(w, seed=8).items()}
+    for n in ("W1", "W2", "b1", "b2", "W1r", "W2r", "b1r", "b2r"):
+        inp[n] = bf16_bits_of_f32(f32_of(inp[n]) * 15.0)
+    fw = oracle.layer_forward(inp, 2, 1.0, act, W.DT_BF16)
+    bw = oracle.layer_backward(fw, inp, act, W.DT_BF16)
+    t = {n: torch.from_numpy(f32_of(v).astype(np.float64)) for n, v in inp.items()}
+    for n in ("x", "W1r", "b1r", "W2r", "b2r"):
+        t[n].requires_grad_(True)
+    xr = _RoundGradBF16.apply(t["x"])
+    pre = xr @ t["W1r"].T + t["b1r"]
+    pre.retain_grad()
+    h = _StoreBF16.apply(_ActAtStoredPre.apply(_RoundGradBF16.apply(pre), act))
+    y = _StoreBF16.apply(h @ t["W2r"].T + t["b2r"])
+    (y * t["dout"]).sum().backward()
+    assert np.array_equal(f32_of(bw["dpre_r"]).astype(np.float64), _bf16_rne_f64(pre.grad).numpy()), "dpre_r"
+    assert np.array_equal(f32_of(bw["dx_r"]).astype(np.float64), _bf16_rne_f64(t["x"].grad).numpy()), "dx_r"
+    for name, ref in (("dW1r", t["W1r"].grad), ("db1r", t["b1r"].grad), ("dW2r", t["W2r"].grad),
+                      ("db2r", t["b2r"].grad)):
+        ref32 = ref.numpy().astype(np.float32)
+        d = np.abs(bw[name].view(np.int32).astype(np.int64) - ref32.view(np.int32).astype(np.int64))
+        assert d.max() <= 1, (name, int(d.max()))
+    # dx: the MoE branch's dbuf rows (fp64 sum) plus dx_r, rounded once
+    rt = fw["route"]
+    want = np.zeros((S, M))
+    for i, q in enumerate(bw["routes"]):
+        want[int(q) % S] += f32_of(bw["dbuf"][i])
+    want += f32_of(bw["dx_r"])
+    assert np.array_equal(f32_of(bw["dx"]).astype(np.float64), _bf16_rne_f64(torch.from_numpy(want)).numpy())
+    assert (rt["loc"] >= rt["C"]).any()  # some routes dropped: those tokens' dx has the dense share only
+
+
+def test_residual_backward_columns_equal_backward_rows():
+    # the column-sampled weight gradients of the dense branch (for large layers) are the full
+    # ones restricted to those columns, bit for bit: the same per-element definitions
+    S, M, H = 37, 16, 40
+    for dtype in (W.DT_F32, W.DT_BF16):
+        w = W.Workload("rescols", S=S, M=M, E=2, k=1, H=H, capacity_factor=1.0, dtype=dtype, residual=True,
+                       backward=True)
+        inp = {n: np_of(v) for n, v in W.make_inputs(w, seed=4).items()}
+        full = oracle.residual_backward(inp, W.ACT_GELU, dtype)
+        hcols = np.array([0, 7, 21, 39], np.int32)
+        dW1c, db1c, dW2c, db2c = oracle.residual_backward_cols(inp, hcols, W.ACT_GELU, dtype)
+        assert np.array_equal(dW1c, full["dW1r"][hcols]) and np.array_equal(db1c, full["db1r"][hcols])
+        assert np.array_equal(dW2c, full["dW2r"][:, hcols]) and np.array_equal(db2c, full["db2r"])
+
+
 # ---------------------------------------------------------------- MX (microscaling) experts
 
 def test_e4m3_decode_matches_torch():

@@ -82,6 +82,8 @@ GATED_TRAIN_BF16 = GATED_BF16.replace(name="gated_train_bf16_S4096_M1024_E8_k2_H
 # blog's PR-MoE layers use top-1 gating with the residual branch)
 RESIDUAL_BF16 = Workload("residual_bf16_S4096_M1024_E8_k1_H4096", S=4096, M=1024, E=8, k=1, H=4096,
                          capacity_factor=1.25, logits="gate", residual=True)
+# ... trained: forward + backward of both branches, gate backward included
+RESIDUAL_TRAIN_BF16 = RESIDUAL_BF16.replace(name="residual_train_bf16_S4096_M1024_E8_k1_H4096", backward=True)
 DSPR_BF16 = Workload("dspr_bf16_S8192_M2048_E16_k3_H8192", S=8192, M=2048, E=16, k=3, H=8192,
                      capacity_factor=0.0)
 FINE_BF16 = Workload("fine_bf16_S16384_M2048_E64_k6_H1408", S=16384, M=2048, E=64, k=6, H=1408,
@@ -95,7 +97,8 @@ GATED_MXFP4 = GATED_BF16.replace(name="gated_mxfp4_S4096_M1024_E8_k2_H4096", mx=
 DSPR_MXFP8 = Workload("dspr_mxfp8_S8192_M2048_E16_k3_H8192", S=8192, M=2048, E=16, k=3, H=8192,
                       capacity_factor=0.0, mx="mxfp8")
 
-WORKLOADS = [TINY_F32, GATED_BF16, GATED_TRAIN_BF16, RESIDUAL_BF16, DSPR_BF16, FINE_BF16, LARGE_BF16]
+WORKLOADS = [TINY_F32, GATED_BF16, GATED_TRAIN_BF16, RESIDUAL_BF16, RESIDUAL_TRAIN_BF16, DSPR_BF16, FINE_BF16,
+             LARGE_BF16]
 # MX workloads are measured by bench.py and checked by the MX parity tests
 MX_WORKLOADS = [GATED_MXFP8, GATED_MXFP4, DSPR_MXFP8]
 BY_NAME = {w.name: w for w in WORKLOADS + MX_WORKLOADS}
