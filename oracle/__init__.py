@@ -96,6 +96,13 @@ def lib():
         L.oracle_expert_rows_mx.argtypes = [i32, i32, i32, ctypes.c_int, ctypes.c_int, u8p, u8p, u8p, u8p, vp, u8p,
                                             u8p, vp, i64, _c_i64p, vp, vp, vp]
         L.oracle_expert_rows_mx.restype = None
+        L.oracle_blockfp8_quantize.argtypes = [i64, i32, i32, ctypes.c_int, vp, u8p, _c_f32p]
+        L.oracle_blockfp8_quantize.restype = None
+        L.oracle_blockfp8_dequantize.argtypes = [i64, i32, i32, u8p, _c_f32p, _c_f64p]
+        L.oracle_blockfp8_dequantize.restype = None
+        L.oracle_expert_rows_blockfp8.argtypes = [i32, i32, i32, ctypes.c_int, u8p, _c_f32p, u8p, _c_f32p, vp, u8p,
+                                                  _c_f32p, vp, i64, _c_i64p, vp, vp, vp]
+        L.oracle_expert_rows_blockfp8.restype = None
         L.oracle_gate_backward.argtypes = [i32, i32, i32, d, _c_f32p, _c_i32p, _c_f32p, vp, _c_f64p, _c_f64p]
         L.oracle_gate_backward.restype = None
         L.oracle_gate_weight_grad.argtypes = [i32, i32, i32, ctypes.c_int, vp, _c_f64p, _c_f64p]
@@ -581,4 +588,60 @@ def expert_rows_mx(bufq, W1q, b1, W2q, b2, rows: Sequence[int], C: int, act_kind
     b2 = None if b2 is None else _check(b2, DT_BF16, (E, M))
     lib().oracle_expert_rows_mx(M, H, C, act_kind, wfmt, bc, bs, w1c, w1s, _ptr(b1), w2c, w2s, _ptr(b2), n, rows,
                                 _ptr(hc), _ptr(hs), _ptr(y))
+    return ((hc, hs) if want_hq else None), y
+
+
+# ------------------------------------------------------------------ block-wise FP8 experts
+
+BLOCK = 128  # block edge: 128 x 128 weight blocks, 1 x 128 activation blocks
+
+
+def blockfp8_quantize(a: np.ndarray, brows: int, dtype: int):
+    """Block-wise FP8 quantisation of a data-type array along its last dimension (a multiple of
+    128) in blocks of brows (1 or 128) rows x 128: returns (codes uint8, same shape as a; scales
+    fp32 [..., rows / brows, K / 128] over the last two dimensions, or [..., K / 128] for
+    brows = 1)."""
+    a = _check(a, dtype)
+    K = a.shape[-1]
+    assert K % BLOCK == 0 and brows in (1, BLOCK)
+    rows = int(np.prod(a.shape[:-1], dtype=np.int64))
+    assert rows % brows == 0
+    codes = np.zeros(a.shape, np.uint8)
+    if brows == 1:
+        sshape = a.shape[:-1] + (K // BLOCK,)
+    else:
+        assert a.shape[-2] % brows == 0
+        sshape = a.shape[:-2] + (a.shape[-2] // brows, K // BLOCK)
+    scales = np.zeros(sshape, np.float32)
+    lib().oracle_blockfp8_quantize(rows, K, brows, dtype, _ptr(a), codes, scales)
+    return codes, scales
+
+
+def blockfp8_dequantize(codes: np.ndarray, scales: np.ndarray, brows: int) -> np.ndarray:
+    """Exact values (fp64, the shape of codes) of a block-FP8 array."""
+    K = codes.shape[-1]
+    rows = int(np.prod(codes.shape[:-1], dtype=np.int64))
+    out = np.empty(codes.shape, np.float64)
+    lib().oracle_blockfp8_dequantize(rows, K, brows, np.ascontiguousarray(codes),
+                                     np.ascontiguousarray(scales, dtype=np.float32), out)
+    return out
+
+
+def expert_rows_blockfp8(bufq, W1q, b1, W2q, b2, rows: Sequence[int], C: int, act_kind: int, want_hq: bool = False):
+    """Block-FP8 expert FFN for the listed buffer rows: bufq = (codes [E*C, M], scales [E*C, M/128]);
+    W1q = (codes [E, H, M], scales [E, H/128, M/128]) and W2q likewise [E, M, H]; biases bf16 or None.
+    Returns (h codes, h scales) when asked and y (bf16, compact [n, M])."""
+    bc, bs = np.ascontiguousarray(bufq[0]), np.ascontiguousarray(bufq[1], dtype=np.float32)
+    w1c, w1s = np.ascontiguousarray(W1q[0]), np.ascontiguousarray(W1q[1], dtype=np.float32)
+    w2c, w2s = np.ascontiguousarray(W2q[0]), np.ascontiguousarray(W2q[1], dtype=np.float32)
+    E, H, M = w1c.shape
+    rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    n = rows.shape[0]
+    hc = np.empty((n, H), np.uint8) if want_hq else None
+    hs = np.empty((n, H // BLOCK), np.float32) if want_hq else None
+    y = np.empty((n, M), np.uint16)
+    b1 = None if b1 is None else _check(b1, DT_BF16, (E, H))
+    b2 = None if b2 is None else _check(b2, DT_BF16, (E, M))
+    lib().oracle_expert_rows_blockfp8(M, H, C, act_kind, bc, bs, w1c, w1s, _ptr(b1), w2c, w2s, _ptr(b2), n, rows,
+                                      _ptr(hc), _ptr(hs), _ptr(y))
     return ((hc, hs) if want_hq else None), y

@@ -715,3 +715,104 @@ void oracle_expert_rows_mx(int32_t M, int32_t H, int32_t C, int act, int wfmt, c
         free(xv); free(hv); free(hc); free(hs);
     }
 }
+
+/* ------------------------------------------------------------------ block-wise FP8 experts */
+
+/* Block-wise FP8 (the Tutel pages list it beside FP8, NVFP4 and MXFP4 without
+ * defining it; the reading is the fine-grained scheme published with DeepSeek-V3,
+ * one of the model families the Tutel project summary names): E4M3 elements and
+ * one fp32 scale per block of brows x 128 values, 128 x 128 for weights (128
+ * output features by 128 steps of the reduction dimension) and 1 x 128 for
+ * activations (128 consecutive features of one token). A block is quantised as
+ *   amax = max |v|,  s = amax / 448  (fp32 division; 448 is E4M3's largest value),
+ *   code = v / s (fp32 division) rounded to the nearest E4M3 value, ties to the
+ *          even code, magnitudes beyond 448 clamped to it, the sign kept;
+ * an all-zero block has s = 0 and codes 0. A code c of a block of scale s stands
+ * for e4m3(c) * s. Scales are laid out [rows / brows][K / 128], row-major. */
+static void blk_quantize(const float *v, int64_t rows, int32_t K, int32_t brows, uint8_t *codes, float *scales) {
+    const int32_t KB = K / 128;
+    for (int64_t rb = 0; rb < rows / brows; ++rb)
+        for (int32_t kb = 0; kb < KB; ++kb) {
+            float amax = 0.0f;
+            for (int32_t i = 0; i < brows; ++i)
+                for (int32_t j = 0; j < 128; ++j) amax = fmaxf(amax, fabsf(v[(rb * brows + i) * K + kb * 128 + j]));
+            const float s = amax / 448.0f;
+            scales[rb * KB + kb] = s;
+            for (int32_t i = 0; i < brows; ++i)
+                for (int32_t j = 0; j < 128; ++j) {
+                    const int64_t at = (rb * brows + i) * K + kb * 128 + j;
+                    int c = 0;
+                    if (s > 0.0f) {
+                        const float q = v[at] / s;
+                        c = nearest_code(fabs((double)q), 0) | (signbit(q) ? 0x80 : 0);
+                    }
+                    codes[at] = (uint8_t)c;
+                }
+        }
+}
+
+static double blk_value(const uint8_t *codes, const float *scales, int32_t K, int32_t brows, int64_t row, int32_t k) {
+    return oracle_e4m3_value(codes[row * K + k]) * (double)scales[(row / brows) * (K / 128) + k / 128];
+}
+
+/* Quantise a row-major [rows, K] matrix of the data type (rows a multiple of
+ * brows, K of 128): codes [rows, K], scales [rows / brows, K / 128]. */
+void oracle_blockfp8_quantize(int64_t rows, int32_t K, int32_t brows, int dtype, const void *src, uint8_t *codes,
+                              float *scales) {
+    float *v = (float *)malloc(sizeof(float) * (size_t)(rows * K > 0 ? rows * K : 1));
+    for (int64_t i = 0; i < rows * K; ++i) v[i] = (float)load_elem(src, dtype, i);
+    blk_quantize(v, rows, K, brows, codes, scales);
+    free(v);
+}
+
+/* Exact values of a block-FP8 matrix, fp64 [rows, K]. */
+void oracle_blockfp8_dequantize(int64_t rows, int32_t K, int32_t brows, const uint8_t *codes, const float *scales,
+                                double *out) {
+    for (int64_t r = 0; r < rows; ++r)
+        for (int32_t k = 0; k < K; ++k) out[r * K + k] = blk_value(codes, scales, K, brows, r, k);
+}
+
+/* Expert FFN on block-FP8 operands, for the listed buffer rows (row = e*C + j):
+ *   pre = sum_m buf[row][m] W1[e][h][m] + b1[e][h]   (dequantised values, fp64 sums)
+ *   h   = act(pre), rounded to fp32, then quantised in 1 x 128 blocks along H
+ *   y   = sum_h hq[h] W2[e][m][h] + b2[e][m], rounded to bf16
+ * buf: codes [E*C, M], scales [E*C, M/128] (1 x 128 blocks); W1 [E*H, M] and W2
+ * [E*M, H] codes with 128 x 128 block scales [E*H/128, M/128] and [E*M/128, H/128];
+ * biases bf16 (may be NULL). Outputs compact per listed row: h codes [n, H], h
+ * scales [n, H/128] (either may be NULL), y bf16 [n, M]. */
+void oracle_expert_rows_blockfp8(int32_t M, int32_t H, int32_t C, int act, const uint8_t *buf_codes,
+                                 const float *buf_scales, const uint8_t *w1_codes, const float *w1_scales,
+                                 const void *b1, const uint8_t *w2_codes, const float *w2_scales, const void *b2,
+                                 int64_t nrows, const int64_t *rows, uint8_t *h_codes, float *h_scales, void *y_out) {
+#pragma omp parallel
+    {
+        double *xv = (double *)malloc(sizeof(double) * (size_t)M);
+        float *hf = (float *)malloc(sizeof(float) * (size_t)H);
+        double *hv = (double *)malloc(sizeof(double) * (size_t)H);
+        uint8_t *hc = (uint8_t *)malloc((size_t)H);
+        float *hs = (float *)malloc(sizeof(float) * (size_t)(H / 128));
+#pragma omp for schedule(dynamic, 4)
+        for (int64_t i = 0; i < nrows; ++i) {
+            const int64_t row = rows[i];
+            const int64_t e = row / C;
+            for (int32_t m = 0; m < M; ++m) xv[m] = blk_value(buf_codes, buf_scales, M, 1, row, m);
+            for (int32_t h = 0; h < H; ++h) {
+                double acc = 0.0;
+                for (int32_t m = 0; m < M; ++m) acc += xv[m] * blk_value(w1_codes, w1_scales, M, 128, e * H + h, m);
+                if (b1) acc += load_elem(b1, DT_BF16, e * H + h);
+                hf[h] = (float)act_f(act, acc);
+            }
+            blk_quantize(hf, 1, H, 1, hc, hs);
+            if (h_codes) memcpy(h_codes + i * H, hc, (size_t)H);
+            if (h_scales) memcpy(h_scales + i * (H / 128), hs, sizeof(float) * (size_t)(H / 128));
+            for (int32_t h = 0; h < H; ++h) hv[h] = blk_value(hc, hs, H, 1, 0, h);
+            for (int32_t m = 0; m < M; ++m) {
+                double acc = 0.0;
+                for (int32_t h = 0; h < H; ++h) acc += hv[h] * blk_value(w2_codes, w2_scales, H, 128, e * M + m, h);
+                if (b2) acc += load_elem(b2, DT_BF16, e * M + m);
+                store_elem(y_out, DT_BF16, i * M + m, acc);
+            }
+        }
+        free(xv); free(hf); free(hv); free(hc); free(hs);
+    }
+}

@@ -1057,3 +1057,105 @@ def test_mx_ffn_on_exact_operands_matches_torch(wfmt):
         yr = torch.from_numpy(hd) @ torch.from_numpy(W2[e]).T + torch.from_numpy(f32_of(b2[e]).astype(np.float64))
         assert np.array_equal(y[r], bf16_bits_of_f32(yr.numpy().astype(np.float32))) or \
             np.abs(f32_of(y[r]) - yr.numpy()).max() <= 2 ** -8 * np.abs(yr.numpy()).max()
+
+
+# ---------------------------------------------------------------- block-wise FP8 experts
+
+@pytest.mark.parametrize("brows", [1, 128])
+@pytest.mark.parametrize("dtype", [W.DT_F32, W.DT_BF16])
+def test_blockfp8_quantize_against_brute_force(brows, dtype):
+    # per block of brows x 128: s = amax / 448 in fp32, codes = the E4M3 value nearest to v / s
+    # (fp32 quotient; ties to the even code; only finite codes, so beyond 448 saturates), sign
+    # kept; an all-zero block has s = 0 and codes 0
+    rng = np.random.default_rng(60 + brows)
+    rows, K = 256, 384
+    a = rng.standard_normal((rows, K)) * np.exp(rng.uniform(-10, 10, (rows, 1)))
+    a[:, :128] *= np.exp(rng.uniform(-6, 6, (rows, 1)))  # blocks of very different ranges
+    if brows == 1:
+        a[0, :128] = 0.0                        # an all-zero block
+        a[1, :128] = 0.0; a[1, 5] = -0.0        # and one with a negative zero
+        a[2, 128:256] = 3.0; a[2, 130] = -3.0   # every element at amax: codes +-448
+        a[3, :128] = 1e-3; a[3, 0] = 50.0       # small elements: subnormal E4M3 codes
+    else:
+        a[:128, :128] = 0.0; a[7, 9] = -0.0
+        a[128:, 256:] = 1e-2; a[200, 300] = -9.0
+    a = to_dtype_bits(a.astype(np.float32), dtype)
+    v = f32_of(a).astype(np.float32)
+    codes, scales = oracle.blockfp8_quantize(a, brows, dtype)
+    assert codes.shape == (rows, K) and scales.shape == (rows // brows, K // 128)
+    mags = np.array([oracle.e4m3_value(c) for c in range(127)])
+    blk = v.reshape(rows // brows, brows, K // 128, 128)
+    amax = np.abs(blk).max(axis=(1, 3)).astype(np.float32)
+    s = amax / np.float32(448.0)
+    assert s.dtype == np.float32 and np.array_equal(scales, s)
+    sfull = np.repeat(np.repeat(s, brows, axis=0), 128, axis=1)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q = np.where(sfull > 0, v / np.where(sfull > 0, sfull, 1), 0).astype(np.float32)
+    d = np.abs(mags[None, :] - np.abs(q).reshape(-1, 1).astype(np.float64))
+    best = d.min(axis=1)
+    c = codes.reshape(-1).astype(np.int64)
+    mag = c & 0x7F
+    assert np.array_equal(d[np.arange(len(c)), mag], best)
+    ties = (d == best[:, None]).sum(axis=1) > 1
+    assert (mag[ties] % 2 == 0).all()
+    zero_blk = (sfull == 0).reshape(-1)
+    assert (c[zero_blk] == 0).all() and zero_blk.any()
+    assert np.array_equal((c[~zero_blk] & 0x80) != 0, np.signbit(q.reshape(-1)[~zero_blk]))
+    if brows == 1:
+        assert set(np.unique(codes[2, 128:256])) == {0x7E, 0xFE}  # +-448
+        assert (codes[3, 1:128] < 8).all() and (codes[3, 1:128] > 0).all()  # subnormal codes
+    deq = oracle.blockfp8_dequantize(codes, scales, brows)
+    assert np.array_equal(deq, np.array([oracle.e4m3_value(x) for x in range(256)])[codes] * sfull.astype(np.float64))
+
+
+def test_blockfp8_elements_match_torch_cast():
+    # the element codes equal torch's round-to-nearest fp32 -> e4m3 cast of the fp32 quotient
+    rng = np.random.default_rng(61)
+    a = (rng.standard_normal((64, 256)) * 5).astype(np.float32)
+    codes, scales = oracle.blockfp8_quantize(a, 1, W.DT_F32)
+    q = (a / np.repeat(scales, 128, axis=1)).astype(np.float32)
+    ok = np.abs(q) <= 448
+    ref = torch.from_numpy(q).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert ok.mean() > 0.99 and np.array_equal(codes[ok], ref[ok])
+
+
+def _blk_representable(rng, shape, brows):
+    """Values whose block-FP8 quantisation is exact: integers -14..14 (all E4M3 values) times 2^j
+    per block, with one element of each block +-448 * 2^j, so that s = 2^j exactly."""
+    v = rng.integers(-14, 15, size=shape).astype(np.float64)
+    R, K = shape[-2], shape[-1]
+    lead = v.reshape(-1, R // brows, brows, K // 128, 128)
+    nb = lead.shape[0] * lead.shape[1] * lead.shape[3]
+    j = rng.integers(-4, 3, size=(lead.shape[0], lead.shape[1], 1, lead.shape[3], 1)).astype(np.float64)
+    lead[:, :, 0, :, 0] = rng.choice([448.0, -448.0], size=(lead.shape[0], lead.shape[1], lead.shape[3]))
+    assert nb > 0
+    return (lead * 2.0 ** j).reshape(shape)
+
+
+def test_blockfp8_ffn_on_exact_operands_matches_torch():
+    # operands that quantise exactly: fc1's pre-activation is the exact product sum, h is
+    # act(pre) rounded to fp32 and block-quantised (1 x 128), y = deq(hq) . W2^T + b2 in bf16
+    rng = np.random.default_rng(62)
+    E, C, M, H = 2, 3, 128, 256
+    x = _blk_representable(rng, (E * C, M), 1)
+    W1 = _blk_representable(rng, (E, H, M), 128) * 2.0 ** -12
+    W2 = _blk_representable(rng, (E, M, H), 128) * 2.0 ** -12
+    b1 = bf16_bits_of_f32(rng.standard_normal((E, H)).astype(np.float32))
+    b2 = bf16_bits_of_f32(rng.standard_normal((E, M)).astype(np.float32))
+    bufq = oracle.blockfp8_quantize(x.astype(np.float32), 1, W.DT_F32)
+    W1q = oracle.blockfp8_quantize(W1.astype(np.float32), 128, W.DT_F32)
+    W2q = oracle.blockfp8_quantize(W2.astype(np.float32), 128, W.DT_F32)
+    assert np.array_equal(oracle.blockfp8_dequantize(*bufq, 1), x)
+    assert np.array_equal(oracle.blockfp8_dequantize(*W1q, 128), W1)
+    assert np.array_equal(oracle.blockfp8_dequantize(*W2q, 128), W2)
+    rows = np.arange(E * C)
+    hq, y = oracle.expert_rows_blockfp8(bufq, W1q, b1, W2q, b2, rows, C, W.ACT_GELU, want_hq=True)
+    for r in rows:
+        e = r // C
+        pre = torch.from_numpy(x[r]) @ torch.from_numpy(W1[e]).T + torch.from_numpy(f32_of(b1[e]).astype(np.float64))
+        h32 = torch.nn.functional.gelu(pre).to(torch.float32).numpy()
+        hc, hs = oracle.blockfp8_quantize(h32[None], 1, W.DT_F32)
+        assert np.array_equal(hc[0], hq[0][r]) and np.array_equal(hs[0], hq[1][r])
+        hd = oracle.blockfp8_dequantize(hc, hs, 1)[0]
+        yr = torch.from_numpy(hd) @ torch.from_numpy(W2[e]).T + torch.from_numpy(f32_of(b2[e]).astype(np.float64))
+        assert np.abs(f32_of(y[r]) - yr.numpy()).max() <= 2 ** -8 * np.abs(yr.numpy()).max()
