@@ -127,7 +127,7 @@ def algorithmic(w, C, kept):
     prod = 2 * M * H * kept  # one expert product over the filled rows
     st = {
         "route": ("bytes", 4 * S * E + 12 * k * S + 4 * kept + 8 * E),
-        # MX encode writes one code byte per value plus a scale byte per 32
+        # MX encode writes one code byte per value plus a scale byte per 32 (block FP8: 4 bytes per 128)
         "encode": ("bytes", S * M * b + (E * C * M * 33 // 32 if w.mx else E * C * M * b) + 8 * k * S),
         "fc1": ("flops", prod),
         "fc2": ("flops", prod),
@@ -217,7 +217,16 @@ def cpu_baseline(w, inp, budget_s):
              if rt["loc"][q, s] < C]
         return np.asarray(sorted(r), np.int64)
 
-    if w.mx:
+    if w.mx == "blockfp8":
+        t0 = time.perf_counter()
+        bufq = oracle.blockfp8_quantize(buf, 1, w.dtype)
+        t["encode"] += time.perf_counter() - t0
+        W1q = oracle.blockfp8_quantize(ni["W1"], oracle.BLOCK, w.dtype)
+        W2q = oracle.blockfp8_quantize(ni["W2"], oracle.BLOCK, w.dtype)
+
+        def ffn(rs):
+            return None, oracle.expert_rows_blockfp8(bufq, W1q, ni.get("b1"), W2q, ni.get("b2"), rs, C, w.act)[1]
+    elif w.mx:
         wf = oracle.MX_FP8 if w.mx == "mxfp8" else oracle.MX_FP4
         t0 = time.perf_counter()
         bufq = oracle.mx_quantize(buf, oracle.MX_FP8, w.dtype)
@@ -346,8 +355,14 @@ def main():
     s = moe.Shape.of(w)
     gate = w.logits == "gate"
     mxf = {"mxfp8": moe.MOE_MX_FP8, "mxfp4": moe.MOE_MX_FP4}.get(w.mx)
-    if mxf is not None:
-        bufs = moe.alloc_forward_mx(s, dev, gate_projection=gate)
+    blk = w.mx == "blockfp8"
+
+    def alloc_lowp():
+        return (moe.alloc_forward_blockfp8(s, dev, gate_projection=gate) if blk else
+                moe.alloc_forward_mx(s, dev, gate_projection=gate))
+
+    if mxf is not None or blk:
+        bufs = alloc_lowp()
     else:
         bufs = moe.alloc_forward(s, dev, training=w.backward, gate_projection=gate, residual=w.residual)
     res = {n: inp.get(n) for n in ("W1r", "b1r", "W2r", "b2r")} if w.residual else None
@@ -364,15 +379,15 @@ def main():
     def backward():
         moe.layer_backward(s, bufs, inp["dout"], W1, W2, grads=grads, logits=logits_bwd, x=x, Wg=Wg, residual=res)
 
-    if mxf is not None:
-        # MX experts: the weights are quantised once, outside the timed region (offline)
-        W1q = moe.mx_quantize_weights(W1, mxf)
-        W2q = moe.mx_quantize_weights(W2, mxf)
+    if mxf is not None or blk:
+        # low-precision experts: the weights are quantised once, outside the timed region (offline)
+        W1q = moe.blockfp8_quantize_weights(W1) if blk else moe.mx_quantize_weights(W1, mxf)
+        W2q = moe.blockfp8_quantize_weights(W2) if blk else moe.mx_quantize_weights(W2, mxf)
         torch.cuda.synchronize()
 
     pipe = args.pipeline_chunks > 0
     if pipe:
-        assert mxf is None and not w.residual and not w.backward and w.dtype == W.DT_BF16, \
+        assert not w.mx and not w.residual and not w.backward and w.dtype == W.DT_BF16, \
             "--pipeline-chunks applies to the bf16 forward workloads"
         pstreams = [torch.cuda.Stream() for _ in range(args.pipeline_streams)]
         pevents = [torch.cuda.Event() for _ in range(args.pipeline_streams + 1)]
@@ -382,7 +397,7 @@ def main():
     if nb > 1:
         assert not w.backward and not pipe, "--batch-streams applies to the forward workloads"
         for _ in range(nb - 1):
-            bsets.append(moe.alloc_forward_mx(s, dev, gate_projection=gate) if mxf is not None else
+            bsets.append(alloc_lowp() if w.mx else
                          moe.alloc_forward(s, dev, gate_projection=gate, residual=w.residual))
         bstreams = [torch.cuda.Stream() for _ in range(nb)]
     counter = [0]
@@ -391,6 +406,9 @@ def main():
         i = counter[0] % nb if multi else 0
         counter[0] += 1
         b, st = bsets[i], bstreams[i] if multi else None
+        if blk:
+            moe.layer_forward_blockfp8(s, x, W1q, b1, W2q, b2, logits=logits_in, Wg=Wg, bufs=b, stream=st)
+            return
         if mxf is not None:
             moe.layer_forward_mx(s, mxf, x, W1q, b1, W2q, b2, logits=logits_in, Wg=Wg, bufs=b, stream=st)
             return
@@ -439,7 +457,16 @@ def main():
         stage_fns.append(("gate", lambda: moe.moe_gate_project(s, x, Wg, lg)))
     stage_fns.append(("route", lambda: moe.moe_route(s, lg, b["idx"], b["loc"], b["gates"], b["needed"], b["fill"],
                                                      b["capacity"], b["slot_route"], b["ws"])))
-    if mxf is not None:
+    if blk:
+        stage_fns += [
+            ("encode", lambda: moe.moe_encode_blockfp8(s, x, b["idx"], b["loc"], b["fill"], b["capacity"],
+                                                       b["buf_codes"], b["buf_scales"])),
+            ("fc1", lambda: moe.moe_expert_fc1_blockfp8(s, b["buf_codes"], b["buf_scales"], W1q, b1, b["fill"],
+                                                        b["capacity"], b["h_codes"], b["h_scales"])),
+            ("fc2", lambda: moe.moe_expert_fc2_blockfp8(s, b["h_codes"], b["h_scales"], W2q, b2, b["fill"],
+                                                        b["capacity"], b["y"])),
+        ]
+    elif mxf is not None:
         stage_fns += [
             ("encode", lambda: moe.moe_encode_mx(s, x, b["idx"], b["loc"], b["fill"], b["capacity"], b["buf_codes"],
                                                  b["buf_scales"])),

@@ -92,6 +92,12 @@ _SIGS = {
     "moe_layer_forward_mx": [_SP, ctypes.c_int32] + [_P] * 24 + [ctypes.c_size_t, _P],
     "moe_expert_fc1_mx": [_SP, ctypes.c_int32] + [_P] * 10,
     "moe_expert_fc2_mx": [_SP, ctypes.c_int32] + [_P] * 9,
+    "moe_blockfp8_quantize": [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, _P, _P, _P],
+    "moe_encode_blockfp8": [_SP] + [_P] * 8,
+    "moe_expert_ffn_blockfp8": [_SP] + [_P] * 14,
+    "moe_layer_forward_blockfp8": [_SP] + [_P] * 24 + [ctypes.c_size_t, _P],
+    "moe_expert_fc1_blockfp8": [_SP] + [_P] * 10,
+    "moe_expert_fc2_blockfp8": [_SP] + [_P] * 9,
     "moe_residual_ffn": [_SP] + [_P] * 9 + [ctypes.c_size_t, _P],
     "moe_residual_backward": [_SP] + [_P] * 13 + [ctypes.c_size_t, _P],
     "moe_decode_residual": [_SP] + [_P] * 8,
@@ -301,6 +307,86 @@ def layer_forward_mx(shape: Shape, wfmt: int, x, W1q, b1, W2q, b2, logits=None, 
     lo = bufs["logits"] if Wg is not None else None
     _check(_lib.moe_layer_forward_mx(
         ctypes.byref(shape.c()), wfmt, _ptr(x), _ptr(logits), _ptr(Wg), _ptr(lo), _ptr(W1q[0]), _ptr(W1q[1]),
+        _ptr(b1), _ptr(W2q[0]), _ptr(W2q[1]), _ptr(b2), _ptr(bufs["idx"]), _ptr(bufs["loc"]), _ptr(bufs["gates"]),
+        _ptr(bufs["needed"]), _ptr(bufs["fill"]), _ptr(bufs["capacity"]), _ptr(bufs["slot_route"]),
+        _ptr(bufs["buf_codes"]), _ptr(bufs["buf_scales"]), _ptr(bufs["h_codes"]), _ptr(bufs["h_scales"]),
+        _ptr(bufs["y"]), _ptr(bufs["out"]), *_ws_args(bufs["ws"]), _stream(stream)))
+    return bufs
+
+
+# ---------------------------------------------------------------- block-wise FP8 experts
+
+BLOCK = 128  # block edge: 128 x 128 weight blocks, 1 x 128 token blocks
+
+
+def moe_blockfp8_quantize(src, brows: int, codes, scales, dtype: int = None, stream=None) -> None:
+    """Block-FP8-quantise ``src`` ([..., K], fp32 or bf16, rows a multiple of brows) into codes
+    (uint8, same shape) and scales (fp32, [rows / brows, K / 128])."""
+    K = src.shape[-1]
+    rows = src.numel() // K if K else 0
+    if dtype is None:
+        dtype = MOE_DT_F32 if src.dtype == torch.float32 else MOE_DT_BF16
+    _check(_lib.moe_blockfp8_quantize(rows, K, brows, dtype, _ptr(src), _ptr(codes), _ptr(scales), _stream(stream)))
+
+
+def blockfp8_alloc(shape_rows_k, brows: int, device="cuda"):
+    """Empty (codes, scales) for a block-FP8 matrix of the given [..., R, K] shape: scales
+    [..., R / brows, K / 128]."""
+    *lead, R, K = shape_rows_k
+    return (torch.empty(*lead, R, K, dtype=torch.uint8, device=device),
+            torch.empty(*lead, R // brows, K // BLOCK, dtype=torch.float32, device=device))
+
+
+def blockfp8_quantize_weights(W):
+    """(codes, scales) of expert weights [E, N, K] in 128 x 128 blocks along the input dimension."""
+    codes, scales = blockfp8_alloc(tuple(W.shape), BLOCK, W.device)
+    moe_blockfp8_quantize(W, BLOCK, codes, scales)
+    return codes, scales
+
+
+def moe_encode_blockfp8(shape: Shape, x, idx, loc, fill, capacity, buf_codes, buf_scales, stream=None) -> None:
+    _check(_lib.moe_encode_blockfp8(ctypes.byref(shape.c()), _ptr(x), _ptr(idx), _ptr(loc), _ptr(fill),
+                                    _ptr(capacity), _ptr(buf_codes), _ptr(buf_scales), _stream(stream)))
+
+
+def moe_expert_ffn_blockfp8(shape: Shape, buf_codes, buf_scales, W1q, b1, W2q, b2, fill, capacity, h_codes, h_scales,
+                            y, stream=None) -> None:
+    _check(_lib.moe_expert_ffn_blockfp8(ctypes.byref(shape.c()), _ptr(buf_codes), _ptr(buf_scales), _ptr(W1q[0]),
+                                        _ptr(W1q[1]), _ptr(b1), _ptr(W2q[0]), _ptr(W2q[1]), _ptr(b2), _ptr(fill),
+                                        _ptr(capacity), _ptr(h_codes), _ptr(h_scales), _ptr(y), _stream(stream)))
+
+
+def moe_expert_fc1_blockfp8(shape: Shape, buf_codes, buf_scales, W1q, b1, fill, capacity, h_codes, h_scales,
+                            stream=None) -> None:
+    _check(_lib.moe_expert_fc1_blockfp8(ctypes.byref(shape.c()), _ptr(buf_codes), _ptr(buf_scales), _ptr(W1q[0]),
+                                        _ptr(W1q[1]), _ptr(b1), _ptr(fill), _ptr(capacity), _ptr(h_codes),
+                                        _ptr(h_scales), _stream(stream)))
+
+
+def moe_expert_fc2_blockfp8(shape: Shape, h_codes, h_scales, W2q, b2, fill, capacity, y, stream=None) -> None:
+    _check(_lib.moe_expert_fc2_blockfp8(ctypes.byref(shape.c()), _ptr(h_codes), _ptr(h_scales), _ptr(W2q[0]),
+                                        _ptr(W2q[1]), _ptr(b2), _ptr(fill), _ptr(capacity), _ptr(y), _stream(stream)))
+
+
+def alloc_forward_blockfp8(shape: Shape, device="cuda", gate_projection: bool = False) -> Dict[str, torch.Tensor]:
+    """Buffers of the block-FP8 forward: the bf16 forward's route tables, out, y and workspace,
+    with the expert buffer and h as E4M3 codes and fp32 scales per 128 features."""
+    b = alloc_forward(shape, device, gate_projection=gate_projection)
+    cmax = moe_capacity_bound(shape)
+    M, E, H = shape.M, shape.E, shape.H
+    b["buf_codes"], b["buf_scales"] = blockfp8_alloc((E * cmax, M), 1, device)
+    b["h_codes"], b["h_scales"] = blockfp8_alloc((E * cmax, H), 1, device)
+    del b["buf"], b["h"]
+    return b
+
+
+def layer_forward_blockfp8(shape: Shape, x, W1q, b1, W2q, b2, logits=None, Wg=None, bufs=None, stream=None):
+    """The fused block-FP8 forward (W1q, W2q = (codes, scales) from blockfp8_quantize_weights)."""
+    if bufs is None:
+        bufs = alloc_forward_blockfp8(shape, x.device, gate_projection=Wg is not None)
+    lo = bufs["logits"] if Wg is not None else None
+    _check(_lib.moe_layer_forward_blockfp8(
+        ctypes.byref(shape.c()), _ptr(x), _ptr(logits), _ptr(Wg), _ptr(lo), _ptr(W1q[0]), _ptr(W1q[1]),
         _ptr(b1), _ptr(W2q[0]), _ptr(W2q[1]), _ptr(b2), _ptr(bufs["idx"]), _ptr(bufs["loc"]), _ptr(bufs["gates"]),
         _ptr(bufs["needed"]), _ptr(bufs["fill"]), _ptr(bufs["capacity"]), _ptr(bufs["slot_route"]),
         _ptr(bufs["buf_codes"]), _ptr(bufs["buf_scales"]), _ptr(bufs["h_codes"]), _ptr(bufs["h_scales"]),

@@ -904,21 +904,35 @@ __global__ __launch_bounds__(NTH, (big_lds_bytes<BM, BN>() * 2 <= 160 * 1024 ? 2
 // per (token, 32 features): the two lanes l, l ^ 32 holding a token's 32
 // features of a block exchange their amax, codes and scales go through LDS to
 // whole-row stores; fc2 adds the bias and stores bf16 as the bf16 kernel does.
+//
+// BLK: block-wise FP8 instead (E4M3 codes; one fp32 scale per 1 x 128 block of a
+// token row, s = amax / 448, and per 128 x 128 block of the weights). A ring stage
+// is exactly one 128-deep block of both operands, so its two MFMAs run with unit
+// scales into a fresh partial P, and acc += P * (s_token * s_weight): the token's
+// scale is per lane (its row), the weight's per 32-column MFMA block (uniform).
+// The scale words have the MX layout's stride (one 32-bit word per row and stage),
+// so they load the same way. fc1 quantises h per (token, 128 features): a
+// wavefront holds 64 of a block's features, so the two wavefronts of a block
+// exchange their amax through LDS before dividing by s.
 typedef int mx_v8i __attribute__((ext_vector_type(8)));
 
 constexpr int kMxStageK = 128;  // k per ring stage
 
 // Bytes of the LDS region shared by the two ring stages and the epilogue tile
 // (bf16 y of fc2, or fc1's h codes and scales), then the tile prefix and bias.
-template <int BM, int BN, int WFMT, int EPI>
+template <int BM, int BN, int WFMT, int EPI, bool BLK = false>
 constexpr int mx_region_bytes() {
     constexpr int ring = 2 * (BM * kMxStageK + BN * (WFMT == kMxFp8 ? kMxStageK : kMxStageK / 2));
-    constexpr int epi = EPI == EPI_FC1 ? BM * BN + BM * BN / 32 : BM * BN * 2;
+    // fc1's h tile: codes, then the scales (BLK: fp32 per 128 features, and each wavefront's
+    // per-row amax, BN / 64 of them per row)
+    constexpr int epi = EPI == EPI_FC1 ? (BLK ? BM * BN + BM * (BN / 128) * 4 + BM * (BN / 64) * 4
+                                              : BM * BN + BM * BN / 32)
+                                       : BM * BN * 2;
     return ring > epi ? ring : epi;
 }
-template <int BM, int BN, int WFMT, int EPI>
+template <int BM, int BN, int WFMT, int EPI, bool BLK = false>
 constexpr int mx_lds_bytes() {
-    return mx_region_bytes<BM, BN, WFMT, EPI>() + kBigPrefixBytes + BN * 2;
+    return mx_region_bytes<BM, BN, WFMT, EPI, BLK>() + kBigPrefixBytes + BN * 2;
 }
 
 // MFMA operand of one row (the lane's) for slice s from an LDS tile of rows of
@@ -941,7 +955,7 @@ __device__ __forceinline__ mx_v8i mx_frag(const bf16_t *tile, int row, int s, in
     return v;
 }
 
-template <int BM, int BN, int NTH, int EPI, int ACT, int WFMT>
+template <int BM, int BN, int NTH, int EPI, int ACT, int WFMT, bool BLK = false>
 __global__ __launch_bounds__(NTH, 1) void rows_gemm_mx(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
                                                      const uint8_t *__restrict__ B, const uint8_t *__restrict__ Bs,
                                                      void *__restrict__ D, uint8_t *__restrict__ Dsc, int N, int K,
@@ -955,8 +969,9 @@ __global__ __launch_bounds__(NTH, 1) void rows_gemm_mx(const uint8_t *__restrict
     constexpr int NW = NTH / 64, WGC = NW / 2;
     constexpr int TM = BM / 64, TN = BN / (32 * WGC);
     static_assert(TN >= 1 && BN % (32 * WGC) == 0, "wavefront columns must be whole 32-wide blocks");
+    static_assert(!BLK || (WFMT == kMxFp8 && BN / WGC == 64), "block FP8: E4M3 weights, 64 columns a wavefront");
     constexpr int STAGE = BM * KA + BN * KW;  // bf16 units
-    constexpr int REGION = mx_region_bytes<BM, BN, WFMT, EPI>() / 2;
+    constexpr int REGION = mx_region_bytes<BM, BN, WFMT, EPI, BLK>() / 2;
     int *prefix = reinterpret_cast<int *>(lds + REGION);
     bf16_t *sbias = lds + REGION + kBigPrefixBytes / 2;
     const int nx = (N + BN - 1) / BN;
@@ -987,17 +1002,23 @@ __global__ __launch_bounds__(NTH, 1) void rows_gemm_mx(const uint8_t *__restrict
         }
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
-            const int c = min(wc0 + j * 32 + (lane & 31), cols_valid - 1);
-            sb_row[j] = reinterpret_cast<const uint32_t *>(Bs + (wrow0 + c) * KS);
+            if constexpr (BLK) {  // the 128-row weight block of the MFMA block's columns
+                const int c = min(wc0 + j * 32, cols_valid - 1);
+                sb_row[j] = reinterpret_cast<const uint32_t *>(Bs + ((wrow0 + c) / 128) * KS);
+            } else {
+                const int c = min(wc0 + j * 32 + (lane & 31), cols_valid - 1);
+                sb_row[j] = reinterpret_cast<const uint32_t *>(Bs + (wrow0 + c) * KS);
+            }
         }
 
-        f32x16 acc[TM][TN];
+        f32x16 acc[TM][TN], part[TM][TN];  // part: BLK's per-stage partial sums
+        f32x16 zero;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) zero[v] = 0.f;
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
-            for (int j = 0; j < TN; ++j)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+            for (int j = 0; j < TN; ++j) acc[i][j] = zero;
 
         barrier_keep_loads_lds();  // the previous tile's epilogue reads of LDS are complete
         if (bias != nullptr && wave == 0 && lane < BN / 8) {
@@ -1071,10 +1092,15 @@ __global__ __launch_bounds__(NTH, 1) void rows_gemm_mx(const uint8_t *__restrict
 #pragma unroll
                 for (int i = 0; i < TM; ++i)
 #pragma unroll
-                    for (int j = 0; j < TN; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                            fb0[j], fa0[i], acc[i][j], WCODE, 0, 0, static_cast<int>((sb_cur[j] >> sh) & 0xFFu), 0,
-                            static_cast<int>((sa_cur[i] >> sh) & 0xFFu));
+                    for (int j = 0; j < TN; ++j) {
+                        if constexpr (BLK)
+                            part[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb0[j], fa0[i], zero, 0, 0,
+                                                                                         0, 127, 0, 127);
+                        else
+                            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                                fb0[j], fa0[i], acc[i][j], WCODE, 0, 0, static_cast<int>((sb_cur[j] >> sh) & 0xFFu),
+                                0, static_cast<int>((sa_cur[i] >> sh) & 0xFFu));
+                    }
             }
             wait_vmcnt<0>();  // stage t+1's ring loads and scales have landed
             barrier_keep_loads_lds();
@@ -1094,16 +1120,101 @@ __global__ __launch_bounds__(NTH, 1) void rows_gemm_mx(const uint8_t *__restrict
 #pragma unroll
                 for (int i = 0; i < TM; ++i)
 #pragma unroll
-                    for (int j = 0; j < TN; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                            fb1[j], fa1[i], acc[i][j], WCODE, 0, 0, static_cast<int>((sb_cur[j] >> sh) & 0xFFu), 0,
-                            static_cast<int>((sa_cur[i] >> sh) & 0xFFu));
+                    for (int j = 0; j < TN; ++j) {
+                        if constexpr (BLK)
+                            part[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb1[j], fa1[i], part[i][j],
+                                                                                         0, 0, 0, 127, 0, 127);
+                        else
+                            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                                fb1[j], fa1[i], acc[i][j], WCODE, 0, 0, static_cast<int>((sb_cur[j] >> sh) & 0xFFu),
+                                0, static_cast<int>((sa_cur[i] >> sh) & 0xFFu));
+                    }
+                if constexpr (BLK) {
+                    // the stage's partial sums times the token's and the weight block's scales
+#pragma unroll
+                    for (int i = 0; i < TM; ++i)
+#pragma unroll
+                        for (int j = 0; j < TN; ++j) {
+                            const float f = __uint_as_float(sa_cur[i]) * __uint_as_float(sb_cur[j]);
+#pragma unroll
+                            for (int v = 0; v < 16; ++v) acc[i][j][v] = fmaf(part[i][j][v], f, acc[i][j][v]);
+                        }
+                }
             }
         }
         wait_vmcnt<0>();
         barrier_keep_loads_lds();  // every wavefront is done with the ring
 
-        if constexpr (EPI == EPI_FC1) {
+        if constexpr (EPI == EPI_FC1 && BLK) {
+            // h = act(acc + b1) quantised per (token, 128 features): codes staged as below, the
+            // fp32 scales as [BM][BN/128]; each wavefront first posts its rows' amax over its 64
+            // columns ([BM][BN/64]), and a block's two wavefronts combine them
+            constexpr int CH = BN / 16, NB = BN / 128, WPR = BN / 64;
+            uint8_t *scodes = reinterpret_cast<uint8_t *>(lds);
+            float *sscale = reinterpret_cast<float *>(scodes + BM * BN);
+            float *samax = sscale + BM * NB;
+            const int wq = wave % WGC;  // the wavefront's 64-column slab; block wq / 2
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+                const int trow = wr0 + i * 32 + (lane & 31);
+                float am = 0.f;
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int tcol = wc0 + j * 32 + 8 * q + 4 * h;
+                        float b4[4] = {0.f, 0.f, 0.f, 0.f};
+                        if (bias != nullptr) {
+                            const uint2 u2 = *reinterpret_cast<const uint2 *>(sbias + tcol);
+                            b4[0] = __uint_as_float(u2.x << 16);
+                            b4[1] = __uint_as_float(u2.x & 0xFFFF0000u);
+                            b4[2] = __uint_as_float(u2.y << 16);
+                            b4[3] = __uint_as_float(u2.y & 0xFFFF0000u);
+                        }
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const float v = act_fast<ACT>(acc[i][j][4 * q + r] + b4[r]);
+                            acc[i][j][4 * q + r] = v;
+                            am = fmaxf(am, fabsf(v));
+                        }
+                    }
+                am = fmaxf(am, __shfl_xor(am, 32, 64));
+                if (h == 0) samax[trow * WPR + wq] = am;
+            }
+            barrier_keep_loads_lds();
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+                const int trow = wr0 + i * 32 + (lane & 31);
+                const float sc = fmaxf(samax[trow * WPR + (wq & ~1)], samax[trow * WPR + (wq | 1)]) / 448.f;
+#pragma unroll
+                for (int j = 0; j < TN; ++j) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const uint32_t lo = blk_fp8x2(acc[i][j][4 * q], acc[i][j][4 * q + 1], sc);
+                        const uint32_t hi = blk_fp8x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3], sc);
+                        const int tcol = wc0 + j * 32 + 8 * q + 4 * h;
+                        *reinterpret_cast<uint32_t *>(scodes + trow * BN + (epi_swz<CH>(trow, tcol >> 4) << 4) +
+                                                      (tcol & 15)) = lo | (hi << 16);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                if (h == 0 && (wq & 1) == 0) sscale[trow * NB + wq / 2] = sc;
+            }
+            barrier_keep_loads_lds();
+            uint8_t *Dc = static_cast<uint8_t *>(D);
+#pragma unroll 4
+            for (int u = 0; u < BM * CH / NTH; ++u) {
+                const int idx = tid + u * NTH, r = idx / CH, c = idx % CH;
+                const uint4 v = *reinterpret_cast<const uint4 *>(scodes + r * BN + (epi_swz<CH>(r, c) << 4));
+                if (r < rows_valid && c * 16 < cols_valid)
+                    *reinterpret_cast<uint4 *>(Dc + (grow0 + r) * N + col0 + c * 16) = v;
+            }
+            float *Ds = reinterpret_cast<float *>(Dsc);
+            for (int idx = tid; idx < BM * NB; idx += NTH) {
+                const int r = idx / NB, c = idx % NB;
+                if (r < rows_valid && c * 128 < cols_valid) Ds[(grow0 + r) * (N / 128) + col0 / 128 + c] = sscale[idx];
+            }
+        } else if constexpr (EPI == EPI_FC1) {
             // h = act(acc + b1) quantised to MXFP8 per (token, 32-feature block); codes staged as a
             // row-major BM x BN byte tile (16-byte chunks XOR-swizzled by row), scales as [BM][BN/32]
             constexpr int CH = BN / 16;
@@ -1837,22 +1948,24 @@ hipError_t launch_fc2(const moe_shape &s, const void *h, const void *W2, const v
     return simt_launch<EPI_FC2>(b, s.act, cmax, E, st);
 }
 
-template <int BM, int BN, int NTH, int EPI, int WFMT>
+template <int BM, int BN, int NTH, int EPI, int WFMT, bool BLK = false>
 hipError_t mx_launch(int act, const uint8_t *A, const uint8_t *As, const uint8_t *B, const uint8_t *Bs, void *D,
                      uint8_t *Dsc, int N, int K, int E, const int32_t *fill, const int32_t *cap, const void *bias,
                      hipStream_t st) {
-    constexpr int lds = mx_lds_bytes<BM, BN, WFMT, EPI>();
-    constexpr int per_cu = (160 * 1024) / lds >= 2 ? 2 : 1;
+    constexpr int lds = mx_lds_bytes<BM, BN, WFMT, EPI, BLK>();
+    // BLK's per-stage partial sums take the registers of a second workgroup per CU (at two
+    // waves per SIMD the compiler spills)
+    constexpr int per_cu = (!BLK && (160 * 1024) / lds >= 2) ? 2 : 1;
     const dim3 grid(resident_blocks(per_cu));
     auto bi = static_cast<const bf16_t *>(bias);
     if (act == MOE_ACT_GELU) {
-        auto k = rows_gemm_mx<BM, BN, NTH, EPI, MOE_ACT_GELU, WFMT>;
+        auto k = rows_gemm_mx<BM, BN, NTH, EPI, MOE_ACT_GELU, WFMT, BLK>;
         static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(k),
                                                            hipFuncAttributeMaxDynamicSharedMemorySize, lds);
         if (attr != hipSuccess) return attr;
         hipLaunchKernelGGL(k, grid, dim3(NTH), lds, st, A, As, B, Bs, D, Dsc, N, K, E, fill, cap, bi);
     } else {
-        auto k = rows_gemm_mx<BM, BN, NTH, EPI, MOE_ACT_RELU, WFMT>;
+        auto k = rows_gemm_mx<BM, BN, NTH, EPI, MOE_ACT_RELU, WFMT, BLK>;
         static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(k),
                                                            hipFuncAttributeMaxDynamicSharedMemorySize, lds);
         if (attr != hipSuccess) return attr;
@@ -1861,7 +1974,7 @@ hipError_t mx_launch(int act, const uint8_t *A, const uint8_t *As, const uint8_t
     return hipGetLastError();
 }
 
-template <int EPI, int WFMT>
+template <int EPI, int WFMT, bool BLK = false>
 hipError_t mx_product(int act, const uint8_t *A, const uint8_t *As, const uint8_t *B, const uint8_t *Bs, void *D,
                       uint8_t *Dsc, int N, int K, int E, const int32_t *fill, const int32_t *cap, const void *bias,
                       int64_t rows_hint, hipStream_t st) {
@@ -1871,9 +1984,9 @@ hipError_t mx_product(int act, const uint8_t *A, const uint8_t *As, const uint8_
     (void)rows_hint;
     const int cfg = gemm_cfg_override();
     switch (cfg) {
-    case 1: return mx_launch<256, 256, 512, EPI, WFMT>(act, A, As, B, Bs, D, Dsc, N, K, E, fill, cap, bias, st);
-    case 2: return mx_launch<256, 128, 256, EPI, WFMT>(act, A, As, B, Bs, D, Dsc, N, K, E, fill, cap, bias, st);
-    default: return mx_launch<128, 128, 256, EPI, WFMT>(act, A, As, B, Bs, D, Dsc, N, K, E, fill, cap, bias, st);
+    case 1: return mx_launch<256, 256, 512, EPI, WFMT, BLK>(act, A, As, B, Bs, D, Dsc, N, K, E, fill, cap, bias, st);
+    case 2: return mx_launch<256, 128, 256, EPI, WFMT, BLK>(act, A, As, B, Bs, D, Dsc, N, K, E, fill, cap, bias, st);
+    default: return mx_launch<128, 128, 256, EPI, WFMT, BLK>(act, A, As, B, Bs, D, Dsc, N, K, E, fill, cap, bias, st);
     }
 }
 
@@ -1881,6 +1994,9 @@ hipError_t launch_fc1_mx(const moe_shape &s, int wfmt, const uint8_t *buf_codes,
                          const uint8_t *w1_codes, const uint8_t *w1_scales, const void *b1, const int32_t *fill,
                          const int32_t *cap, uint8_t *h_codes, uint8_t *h_scales, int32_t cmax, hipStream_t st) {
     const int64_t rh = rows_hint(s, cmax);
+    if (wfmt == kBlkFp8)
+        return mx_product<EPI_FC1, kMxFp8, true>(s.act, buf_codes, buf_scales, w1_codes, w1_scales, h_codes, h_scales,
+                                                 s.H, s.M, s.E, fill, cap, b1, rh, st);
     if (wfmt == kMxFp8)
         return mx_product<EPI_FC1, kMxFp8>(s.act, buf_codes, buf_scales, w1_codes, w1_scales, h_codes, h_scales, s.H,
                                            s.M, s.E, fill, cap, b1, rh, st);
@@ -1892,6 +2008,9 @@ hipError_t launch_fc2_mx(const moe_shape &s, int wfmt, const uint8_t *h_codes, c
                          const uint8_t *w2_codes, const uint8_t *w2_scales, const void *b2, const int32_t *fill,
                          const int32_t *cap, void *y, int32_t cmax, hipStream_t st) {
     const int64_t rh = rows_hint(s, cmax);
+    if (wfmt == kBlkFp8)
+        return mx_product<EPI_FC2, kMxFp8, true>(s.act, h_codes, h_scales, w2_codes, w2_scales, y, nullptr, s.M, s.H,
+                                                 s.E, fill, cap, b2, rh, st);
     if (wfmt == kMxFp8)
         return mx_product<EPI_FC2, kMxFp8>(s.act, h_codes, h_scales, w2_codes, w2_scales, y, nullptr, s.M, s.H, s.E,
                                            fill, cap, b2, rh, st);

@@ -350,17 +350,27 @@ moe_status moe_expert_fc2_mx(const moe_shape *shape, int32_t wfmt, const void *h
     return e == hipSuccess ? MOE_OK : hip_fail(e, "MX expert fc2");
 }
 
-moe_status moe_layer_forward_mx(const moe_shape *shape, int32_t wfmt, const void *x, const float *logits_in,
-                                const float *Wg, float *logits_out, const void *W1_codes, const void *W1_scales,
-                                const void *b1, const void *W2_codes, const void *W2_scales, const void *b2,
-                                int32_t *idx, int32_t *loc, float *gates, int32_t *needed, int32_t *fill,
-                                int32_t *capacity, int32_t *slot_route, void *buf_codes, void *buf_scales,
-                                void *h_codes, void *h_scales, void *y, void *out, void *ws, size_t ws_bytes,
-                                void *stream) {
-    moe_status st = check_shape(shape);
-    if (st != MOE_OK) return st;
-    const moe_shape &s = *shape;
-    if ((st = check_mx_shape(s, wfmt)) != MOE_OK) return st;
+}  // extern "C"
+
+namespace {
+
+moe_status check_blk_shape(const moe_shape &s) {
+    if (s.dtype != MOE_DT_BF16) return fail(MOE_EUNSUPPORTED, "block-FP8 experts take bf16 tokens and outputs");
+    if (s.M % 128 != 0 || s.H % 128 != 0)
+        return fail(MOE_EUNSUPPORTED, "block-FP8 experts need M and H multiples of 128 (M=%d, H=%d)", s.M, s.H);
+    return MOE_OK;
+}
+
+// The forward with low-precision experts: wfmt is an MX weight format (tokens and h
+// MXFP8) or kBlkFp8 (block-wise FP8 throughout); the shape was checked for it.
+moe_status layer_forward_lp_impl(const moe_shape &s, int wfmt, const void *x, const float *logits_in,
+                                 const float *Wg, float *logits_out, const void *W1_codes, const void *W1_scales,
+                                 const void *b1, const void *W2_codes, const void *W2_scales, const void *b2,
+                                 int32_t *idx, int32_t *loc, float *gates, int32_t *needed, int32_t *fill,
+                                 int32_t *capacity, int32_t *slot_route, void *buf_codes, void *buf_scales,
+                                 void *h_codes, void *h_scales, void *y, void *out, void *ws, size_t ws_bytes,
+                                 void *stream) {
+    moe_status st;
     MOE_REQUIRE(!(logits_in != nullptr && Wg != nullptr), "exactly one of logits_in and Wg must be given");
     MOE_REQUIRE(s.S == 0 || logits_in != nullptr || Wg != nullptr, "exactly one of logits_in and Wg must be given");
     MOE_REQUIRE(Wg == nullptr || logits_out != nullptr || s.S == 0, "logits_out is required with Wg");
@@ -390,17 +400,145 @@ moe_status moe_layer_forward_mx(const moe_shape *shape, int32_t wfmt, const void
         return hip_fail(e, "route");
     auto *bc = static_cast<uint8_t *>(buf_codes);
     auto *bs = static_cast<uint8_t *>(buf_scales);
-    if ((e = moe::launch_encode_mx(s, x, idx, loc, fill, capacity, bc, bs, cmax, strm)) != hipSuccess)
-        return hip_fail(e, "MX encode");
+    e = wfmt == moe::kBlkFp8
+            ? moe::launch_encode_blk(s, x, idx, loc, fill, capacity, bc, static_cast<float *>(buf_scales), cmax, strm)
+            : moe::launch_encode_mx(s, x, idx, loc, fill, capacity, bc, bs, cmax, strm);
+    if (e != hipSuccess) return hip_fail(e, "low-precision encode");
     if ((e = moe::launch_expert_ffn_mx(s, wfmt, bc, bs, static_cast<const uint8_t *>(W1_codes),
                                        static_cast<const uint8_t *>(W1_scales), b1,
                                        static_cast<const uint8_t *>(W2_codes), static_cast<const uint8_t *>(W2_scales),
                                        b2, fill, capacity, static_cast<uint8_t *>(h_codes),
                                        static_cast<uint8_t *>(h_scales), y, cmax, strm)) != hipSuccess)
-        return hip_fail(e, "MX expert ffn");
+        return hip_fail(e, "low-precision expert ffn");
     if ((e = moe::launch_decode(s, y, gates, idx, loc, capacity, out, false, strm)) != hipSuccess)
         return hip_fail(e, "decode");
     return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_layer_forward_mx(const moe_shape *shape, int32_t wfmt, const void *x, const float *logits_in,
+                                const float *Wg, float *logits_out, const void *W1_codes, const void *W1_scales,
+                                const void *b1, const void *W2_codes, const void *W2_scales, const void *b2,
+                                int32_t *idx, int32_t *loc, float *gates, int32_t *needed, int32_t *fill,
+                                int32_t *capacity, int32_t *slot_route, void *buf_codes, void *buf_scales,
+                                void *h_codes, void *h_scales, void *y, void *out, void *ws, size_t ws_bytes,
+                                void *stream) {
+    moe_status st = check_shape(shape);
+    if (st != MOE_OK) return st;
+    if ((st = check_mx_shape(*shape, wfmt)) != MOE_OK) return st;
+    return layer_forward_lp_impl(*shape, wfmt, x, logits_in, Wg, logits_out, W1_codes, W1_scales, b1, W2_codes,
+                                 W2_scales, b2, idx, loc, gates, needed, fill, capacity, slot_route, buf_codes,
+                                 buf_scales, h_codes, h_scales, y, out, ws, ws_bytes, stream);
+}
+
+moe_status moe_layer_forward_blockfp8(const moe_shape *shape, const void *x, const float *logits_in,
+                                      const float *Wg, float *logits_out, const void *W1_codes,
+                                      const float *W1_scales, const void *b1, const void *W2_codes,
+                                      const float *W2_scales, const void *b2, int32_t *idx, int32_t *loc,
+                                      float *gates, int32_t *needed, int32_t *fill, int32_t *capacity,
+                                      int32_t *slot_route, void *buf_codes, float *buf_scales, void *h_codes,
+                                      float *h_scales, void *y, void *out, void *ws, size_t ws_bytes, void *stream) {
+    moe_status st = check_shape(shape);
+    if (st != MOE_OK) return st;
+    if ((st = check_blk_shape(*shape)) != MOE_OK) return st;
+    return layer_forward_lp_impl(*shape, moe::kBlkFp8, x, logits_in, Wg, logits_out, W1_codes, W1_scales, b1,
+                                 W2_codes, W2_scales, b2, idx, loc, gates, needed, fill, capacity, slot_route,
+                                 buf_codes, buf_scales, h_codes, h_scales, y, out, ws, ws_bytes, stream);
+}
+
+moe_status moe_blockfp8_quantize(int64_t rows, int32_t K, int32_t brows, int32_t dtype, const void *src, void *codes,
+                                 float *scales, void *stream) {
+    MOE_REQUIRE(brows == 1 || brows == 128, "brows must be 1 or 128, not %d", brows);
+    MOE_REQUIRE(dtype == MOE_DT_F32 || dtype == MOE_DT_BF16, "unknown dtype %d", dtype);
+    MOE_REQUIRE(rows >= 0 && K > 0 && K % 128 == 0, "rows must be >= 0 and K a positive multiple of 128");
+    MOE_REQUIRE(rows % brows == 0, "rows=%lld must be a multiple of brows=%d", (long long)rows, brows);
+    MOE_REQUIRE(rows * (K / 128) < (int64_t(1) << 40), "matrix too large");
+    if (rows > 0) MOE_REQUIRE(src && codes && scales, "src, codes and scales must be non-NULL");
+    MOE_REQUIRE_ALIGNED(src, codes, scales);
+    hipError_t e = moe::launch_blk_quantize(brows, rows, K, dtype, src, static_cast<uint8_t *>(codes), scales,
+                                            as_stream(stream));
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "block-FP8 quantisation");
+}
+
+moe_status moe_encode_blockfp8(const moe_shape *shape, const void *x, const int32_t *idx, const int32_t *loc,
+                               const int32_t *fill, const int32_t *capacity, void *buf_codes, float *buf_scales,
+                               void *stream) {
+    moe_status st = check_shape(shape);
+    if (st != MOE_OK) return st;
+    const moe_shape &s = *shape;
+    if ((st = check_blk_shape(s)) != MOE_OK) return st;
+    MOE_REQUIRE(fill && capacity && buf_codes && buf_scales, "fill, capacity, buf_codes and buf_scales must be non-NULL");
+    if (s.S > 0) MOE_REQUIRE(x && idx && loc, "x, idx and loc must be non-NULL");
+    MOE_REQUIRE_ALIGNED(x, idx, loc, fill, capacity, buf_codes, buf_scales);
+    hipError_t e = moe::launch_encode_blk(s, x, idx, loc, fill, capacity, static_cast<uint8_t *>(buf_codes),
+                                          buf_scales, static_cast<int32_t>(cap_bound(s)), as_stream(stream));
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "block-FP8 encode");
+}
+
+moe_status moe_expert_ffn_blockfp8(const moe_shape *shape, const void *buf_codes, const float *buf_scales,
+                                   const void *W1_codes, const float *W1_scales, const void *b1, const void *W2_codes,
+                                   const float *W2_scales, const void *b2, const int32_t *fill,
+                                   const int32_t *capacity, void *h_codes, float *h_scales, void *y, void *stream) {
+    moe_status st = check_shape(shape);
+    if (st != MOE_OK) return st;
+    const moe_shape &s = *shape;
+    if ((st = check_blk_shape(s)) != MOE_OK) return st;
+    MOE_REQUIRE(buf_codes && buf_scales && W1_codes && W1_scales && W2_codes && W2_scales && fill && capacity &&
+                    h_codes && h_scales && y,
+                "buffers, weights, fill, capacity, h and y must be non-NULL");
+    MOE_REQUIRE((b1 != nullptr) == (s.has_fc1_bias != 0), "b1 must be given iff has_fc1_bias");
+    MOE_REQUIRE((b2 != nullptr) == (s.has_fc2_bias != 0), "b2 must be given iff has_fc2_bias");
+    MOE_REQUIRE_ALIGNED(buf_codes, buf_scales, W1_codes, W1_scales, b1, W2_codes, W2_scales, b2, fill, capacity,
+                        h_codes, h_scales, y);
+    hipError_t e = moe::launch_expert_ffn_mx(
+        s, moe::kBlkFp8, static_cast<const uint8_t *>(buf_codes), reinterpret_cast<const uint8_t *>(buf_scales),
+        static_cast<const uint8_t *>(W1_codes), reinterpret_cast<const uint8_t *>(W1_scales), b1,
+        static_cast<const uint8_t *>(W2_codes), reinterpret_cast<const uint8_t *>(W2_scales), b2, fill, capacity,
+        static_cast<uint8_t *>(h_codes), reinterpret_cast<uint8_t *>(h_scales), y, static_cast<int32_t>(cap_bound(s)),
+        as_stream(stream));
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "block-FP8 expert ffn");
+}
+
+moe_status moe_expert_fc1_blockfp8(const moe_shape *shape, const void *buf_codes, const float *buf_scales,
+                                   const void *W1_codes, const float *W1_scales, const void *b1, const int32_t *fill,
+                                   const int32_t *capacity, void *h_codes, float *h_scales, void *stream) {
+    moe_status st = check_shape(shape);
+    if (st != MOE_OK) return st;
+    const moe_shape &s = *shape;
+    if ((st = check_blk_shape(s)) != MOE_OK) return st;
+    MOE_REQUIRE(buf_codes && buf_scales && W1_codes && W1_scales && fill && capacity && h_codes && h_scales,
+                "buffers, weights, fill, capacity and h must be non-NULL");
+    MOE_REQUIRE((b1 != nullptr) == (s.has_fc1_bias != 0), "b1 must be given iff has_fc1_bias");
+    MOE_REQUIRE_ALIGNED(buf_codes, buf_scales, W1_codes, W1_scales, b1, fill, capacity, h_codes, h_scales);
+    hipError_t e = moe::launch_fc1_mx(s, moe::kBlkFp8, static_cast<const uint8_t *>(buf_codes),
+                                      reinterpret_cast<const uint8_t *>(buf_scales),
+                                      static_cast<const uint8_t *>(W1_codes),
+                                      reinterpret_cast<const uint8_t *>(W1_scales), b1, fill, capacity,
+                                      static_cast<uint8_t *>(h_codes), reinterpret_cast<uint8_t *>(h_scales),
+                                      static_cast<int32_t>(cap_bound(s)), as_stream(stream));
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "block-FP8 expert fc1");
+}
+
+moe_status moe_expert_fc2_blockfp8(const moe_shape *shape, const void *h_codes, const float *h_scales,
+                                   const void *W2_codes, const float *W2_scales, const void *b2, const int32_t *fill,
+                                   const int32_t *capacity, void *y, void *stream) {
+    moe_status st = check_shape(shape);
+    if (st != MOE_OK) return st;
+    const moe_shape &s = *shape;
+    if ((st = check_blk_shape(s)) != MOE_OK) return st;
+    MOE_REQUIRE(h_codes && h_scales && W2_codes && W2_scales && fill && capacity && y,
+                "h, weights, fill, capacity and y must be non-NULL");
+    MOE_REQUIRE((b2 != nullptr) == (s.has_fc2_bias != 0), "b2 must be given iff has_fc2_bias");
+    MOE_REQUIRE_ALIGNED(h_codes, h_scales, W2_codes, W2_scales, b2, fill, capacity, y);
+    hipError_t e = moe::launch_fc2_mx(s, moe::kBlkFp8, static_cast<const uint8_t *>(h_codes),
+                                      reinterpret_cast<const uint8_t *>(h_scales),
+                                      static_cast<const uint8_t *>(W2_codes),
+                                      reinterpret_cast<const uint8_t *>(W2_scales), b2, fill, capacity, y,
+                                      static_cast<int32_t>(cap_bound(s)), as_stream(stream));
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "block-FP8 expert fc2");
 }
 
 moe_status moe_gate_backward(const moe_shape *shape, const float *logits, const int32_t *idx, const float *dgates,

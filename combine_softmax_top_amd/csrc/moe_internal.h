@@ -121,6 +121,9 @@ __device__ __forceinline__ float act_grad_f(float v) {
 // index in the low nibble). A block's shared exponent is floor(log2 amax) - emax_elem
 // (8 for E4M3, 2 for E2M1), clamped to [-127, 127], and -127 for an all-zero block.
 constexpr int kMxFp8 = 0, kMxFp4 = 1;
+// The expert GEMMs' third operand scheme: block-wise FP8 (E4M3, fp32 scales per 1 x 128
+// token block and 128 x 128 weight block), passed where the MX weight format goes.
+constexpr int kBlkFp8 = 2;
 
 __device__ __forceinline__ int mx_shared_exp(float amax, int emax) {
     if (!(amax > 0.f)) return -127;
@@ -136,6 +139,11 @@ __device__ __forceinline__ uint32_t mx_fp8x2(float a, float b) {
     a = fminf(fmaxf(a, -448.f), 448.f);
     b = fminf(fmaxf(b, -448.f), 448.f);
     return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false)) & 0xFFFFu;
+}
+// Block-wise FP8: two values of a block with fp32 scale s -> two E4M3 codes of v / s
+// (fp32 division), both 0 when s is 0 (an all-zero block).
+__device__ __forceinline__ uint32_t blk_fp8x2(float a, float b, float s) {
+    return s > 0.f ? mx_fp8x2(a / s, b / s) : 0u;
 }
 // One value (already divided by the block scale) -> E2M1 code: nearest of 0, 0.5, 1,
 // 1.5, 2, 3, 4, 6, ties to the even code, saturating at 6, sign bit 8.
@@ -241,6 +249,14 @@ hipError_t launch_mx_quantize(int fmt, int64_t rows, int32_t K, int dtype, const
 hipError_t launch_encode_mx(const moe_shape &s, const void *x, const int32_t *idx, const int32_t *loc,
                             const int32_t *fill, const int32_t *cap, uint8_t *buf_codes, uint8_t *buf_scales,
                             int32_t cmax, hipStream_t st);
+// Block-wise FP8: quantise a row-major [rows, K] matrix (K a multiple of 128) in blocks of
+// brows (1 or 128; rows a multiple of it) x 128; encode with the token rows quantised in
+// 1 x 128 blocks. The FFN launchers below take wfmt = kBlkFp8 for this scheme (scales fp32).
+hipError_t launch_blk_quantize(int brows, int64_t rows, int32_t K, int dtype, const void *src, uint8_t *codes,
+                               float *scales, hipStream_t st);
+hipError_t launch_encode_blk(const moe_shape &s, const void *x, const int32_t *idx, const int32_t *loc,
+                             const int32_t *fill, const int32_t *cap, uint8_t *buf_codes, float *buf_scales,
+                             int32_t cmax, hipStream_t st);
 hipError_t launch_fc1_mx(const moe_shape &s, int wfmt, const uint8_t *buf_codes, const uint8_t *buf_scales,
                          const uint8_t *w1_codes, const uint8_t *w1_scales, const void *b1, const int32_t *fill,
                          const int32_t *cap, uint8_t *h_codes, uint8_t *h_scales, int32_t cmax, hipStream_t st);

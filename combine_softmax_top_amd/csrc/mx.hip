@@ -1,10 +1,12 @@
-// MX (OCP microscaling) quantisation on gfx950: whole matrices (the experts'
-// weights, offline) and the encode step's token rows (MXFP8, fused into the
-// copy into the flat expert buffer). Four lanes take a 32-value block, eight
-// values each: the block's amax is a two-step shuffle max, the shared exponent
-// comes from frexp, values are scaled by an exact power of two and converted
-// (E4M3 by the hardware conversion, which rounds to nearest even; E2M1 by
-// comparison with the rounding midpoints).
+// MX (OCP microscaling) and block-wise FP8 quantisation on gfx950: whole
+// matrices (the experts' weights, offline) and the encode step's token rows
+// (fused into the copy into the flat expert buffer). MX: four lanes take a
+// 32-value block, eight values each: the block's amax is a two-step shuffle max,
+// the shared exponent comes from frexp, values are scaled by an exact power of
+// two and converted (E4M3 by the hardware conversion, which rounds to nearest
+// even; E2M1 by comparison with the rounding midpoints). Block-wise FP8: sixteen
+// lanes take a 1 x 128 block, a workgroup a 128 x 128 one, and the values are
+// divided by the block's fp32 scale before the same E4M3 conversion.
 #include "moe_internal.h"
 
 namespace moe {
@@ -129,6 +131,131 @@ __global__ __launch_bounds__(kThreads) void encode_mx_kernel(const bf16_t *__res
     }
 }
 
+// ---------------------------------------------------------------- block-wise FP8
+// E4M3 codes with one fp32 scale s = amax / 448 per block (1 x 128 for activations,
+// 128 x 128 for weights); code = v / s (fp32 division) converted to nearest even and
+// saturated like the MX elements; an all-zero block has s = 0 and codes 0.
+
+// Eight values of a block with scale s -> eight E4M3 codes.
+__device__ __forceinline__ uint2 blk_codes8(const float *f, float s) {
+    return make_uint2(blk_fp8x2(f[0], f[1], s) | (blk_fp8x2(f[2], f[3], s) << 16),
+                      blk_fp8x2(f[4], f[5], s) | (blk_fp8x2(f[6], f[7], s) << 16));
+}
+
+// Amax of a 128-value block held by 16 consecutive lanes, eight values each.
+__device__ __forceinline__ float blk_amax16(const float *f) {
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 16));
+    return amax;
+}
+
+// 1 x 128 blocks: sixteen lanes per block, grid-stride over the rows * K/128 blocks.
+__global__ __launch_bounds__(kThreads) void blk_quantize_rows_kernel(const void *__restrict__ src, int dtype,
+                                                                     int64_t rows, int32_t K,
+                                                                     uint8_t *__restrict__ codes,
+                                                                     float *__restrict__ scales) {
+    const int KB = K / 128;
+    const int64_t nblk = rows * KB;
+    const int sub = threadIdx.x & 15;
+    for (int64_t b = (static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x) / 16; b < nblk;
+         b += static_cast<int64_t>(gridDim.x) * (kThreads / 16)) {
+        const int64_t r = b / KB, kb = b - r * KB;
+        const int64_t at = r * K + kb * 128 + sub * 8;
+        float f[8];
+        load8(src, dtype, at, f);
+        const float sc = blk_amax16(f) / 448.f;
+        *reinterpret_cast<uint2 *>(codes + at) = blk_codes8(f, sc);
+        if (sub == 0) scales[b] = sc;
+    }
+}
+
+// 128 x 128 blocks: a workgroup per block, each thread 64 values of one row (two per row).
+__global__ __launch_bounds__(kThreads) void blk_quantize_tiles_kernel(const void *__restrict__ src, int dtype,
+                                                                      int64_t rows, int32_t K,
+                                                                      uint8_t *__restrict__ codes,
+                                                                      float *__restrict__ scales) {
+    static_assert(kThreads == 256, "two threads per row of a 128-row block");
+    __shared__ float wmax[kThreads / 64];
+    const int KB = K / 128;
+    const int64_t nblk = (rows / 128) * KB;
+    const int row = threadIdx.x >> 1, half = threadIdx.x & 1, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    for (int64_t b = blockIdx.x; b < nblk; b += gridDim.x) {
+        const int64_t rb = b / KB, kb = b - rb * KB;
+        const int64_t at = (rb * 128 + row) * K + kb * 128 + half * 64;
+        float f[64];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) load8(src, dtype, at + 8 * u, f + 8 * u);
+        float amax = 0.f;
+#pragma unroll
+        for (int i = 0; i < 64; ++i) amax = fmaxf(amax, fabsf(f[i]));
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+        if (lane == 0) wmax[wave] = amax;
+        __syncthreads();
+        amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+        const float sc = amax / 448.f;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const uint2 lo = blk_codes8(f + 16 * u, sc), hi = blk_codes8(f + 16 * u + 8, sc);
+            *reinterpret_cast<uint4 *>(codes + at + 16 * u) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+        }
+        if (threadIdx.x == 0) scales[b] = sc;
+        __syncthreads();  // wmax is read before the next block overwrites it
+    }
+}
+
+// One wavefront per token, as encode_mx_kernel: the row is quantised once in 1 x 128 blocks
+// (four per pass of 512 values) and its codes and scales go to every kept slot; then the
+// padding rows of every expert get codes 0 and scale 0.
+__global__ __launch_bounds__(kThreads) void encode_blk_kernel(const bf16_t *__restrict__ x,
+                                                              const int32_t *__restrict__ idx,
+                                                              const int32_t *__restrict__ loc,
+                                                              const int32_t *__restrict__ fill,
+                                                              const int32_t *__restrict__ cap,
+                                                              uint8_t *__restrict__ codes, float *__restrict__ scales,
+                                                              int S, int M, int E, int k) {
+    const int C = *cap;
+    const int lane = threadIdx.x & 63;
+    const int64_t nw = static_cast<int64_t>(gridDim.x) * (kThreads / 64);
+    const int64_t w0 = (static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x) / 64;
+    for (int64_t s = w0; s < S; s += nw) {
+        int slot = -1;
+        if (lane < k) {
+            const int64_t q = static_cast<int64_t>(lane) * S + s;
+            const int l = loc[q];
+            if (l < C) slot = idx[q] * C + l;
+        }
+        for (int m0 = 0; m0 < M; m0 += 512) {
+            const bool in = m0 + lane * 8 < M;  // M is a multiple of 128: whole blocks of 16 lanes
+            float f[8];
+            if (in) load8(x, MOE_DT_BF16, s * M + m0 + lane * 8, f);
+            else
+#pragma unroll
+                for (int i = 0; i < 8; ++i) f[i] = 0.f;
+            const float sc = blk_amax16(f) / 448.f;
+            const uint2 c = blk_codes8(f, sc);
+            for (int r = 0; r < k; ++r) {
+                const int sl = __builtin_amdgcn_readlane(slot, r);
+                if (sl < 0 || !in) continue;
+                *reinterpret_cast<uint2 *>(codes + static_cast<int64_t>(sl) * M + m0 + lane * 8) = c;
+                if ((lane & 15) == 0) scales[static_cast<int64_t>(sl) * (M / 128) + (m0 + lane * 8) / 128] = sc;
+            }
+        }
+    }
+    const int64_t rows = static_cast<int64_t>(E) * C;
+    for (int64_t row = w0; row < rows; row += nw) {
+        const int e = static_cast<int>(row / C);
+        const int j = static_cast<int>(row - static_cast<int64_t>(e) * C);
+        if (j < fill[e]) continue;
+        for (int m = lane * 16; m < M; m += 64 * 16)
+            *reinterpret_cast<uint4 *>(codes + row * M + m) = make_uint4(0u, 0u, 0u, 0u);
+        for (int b = lane; b < M / 128; b += 64) scales[row * (M / 128) + b] = 0.f;
+    }
+}
+
 int grid_blocks(int64_t threads) {
     const int64_t b = (threads + kThreads - 1) / kThreads;
     return static_cast<int>(b < 1 ? 1 : (b > 4096 ? 4096 : b));
@@ -146,6 +273,30 @@ hipError_t launch_mx_quantize(int fmt, int64_t rows, int32_t K, int dtype, const
     else
         hipLaunchKernelGGL(mx_quantize_kernel<kMxFp4>, dim3(grid), dim3(kThreads), 0, st, src, dtype, rows, K, codes,
                            scales);
+    return hipGetLastError();
+}
+
+hipError_t launch_blk_quantize(int brows, int64_t rows, int32_t K, int dtype, const void *src, uint8_t *codes,
+                               float *scales, hipStream_t st) {
+    if (rows == 0) return hipSuccess;
+    if (brows == 1) {
+        hipLaunchKernelGGL(blk_quantize_rows_kernel, dim3(grid_blocks(rows * (K / 128) * 16)), dim3(kThreads), 0, st,
+                           src, dtype, rows, K, codes, scales);
+    } else {
+        const int64_t nblk = (rows / 128) * (K / 128);
+        const int grid = static_cast<int>(nblk < 8192 ? nblk : 8192);
+        hipLaunchKernelGGL(blk_quantize_tiles_kernel, dim3(grid), dim3(kThreads), 0, st, src, dtype, rows, K, codes,
+                           scales);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_encode_blk(const moe_shape &s, const void *x, const int32_t *idx, const int32_t *loc,
+                             const int32_t *fill, const int32_t *cap, uint8_t *buf_codes, float *buf_scales,
+                             int32_t cmax, hipStream_t st) {
+    const int grid = grid_blocks((static_cast<int64_t>(s.S) + static_cast<int64_t>(s.E) * cmax) * 64);
+    hipLaunchKernelGGL(encode_blk_kernel, dim3(grid), dim3(kThreads), 0, st, static_cast<const bf16_t *>(x), idx, loc,
+                       fill, cap, buf_codes, buf_scales, s.S, s.M, s.E, s.k);
     return hipGetLastError();
 }
 

@@ -185,7 +185,7 @@ moe_status moe_decode(const moe_shape *shape, const void *y, const float *gates,
                       const int32_t *loc, const int32_t *capacity, void *out, void *stream);
 
 /* MX low-precision experts (Tutel catalogue page and its project summaries:
- * FP8 / MXFP4 / block-wise FP8 quantised inference). Format: OCP Microscaling
+ * FP8 / MXFP4 quantised inference). Format: OCP Microscaling
  * (MX) -- 32 consecutive values along a row share one E8M0 scale byte b
  * (2^(b - 127)); elements are E4M3 (MOE_MX_FP8: one byte each, max 448) or
  * E2M1 (MOE_MX_FP4: two per byte, the even index in the low nibble, max 6).
@@ -246,6 +246,77 @@ moe_status moe_layer_forward_mx(const moe_shape *shape, int32_t wfmt, const void
                                 float *gates, int32_t *needed, int32_t *fill, int32_t *capacity,
                                 int32_t *slot_route, void *buf_codes, void *buf_scales, void *h_codes,
                                 void *h_scales, void *y, void *out, void *ws, size_t ws_bytes, void *stream);
+
+/* Block-wise FP8 experts (Tutel catalogue page and its project summaries:
+ * BlockwiseFP8 quantised inference, named there without a definition; the
+ * reading is the fine-grained scheme published with DeepSeek-V3, a model family
+ * the project summary names). E4M3 elements (one byte each) with one fp32 scale
+ * per block: 128 x 128 for the experts' weights (128 output features by 128
+ * steps of the reduction dimension), 1 x 128 for token rows and h (128
+ * consecutive features). A block is quantised as s = amax / 448 (fp32 division;
+ * 448 is E4M3's largest value) and code = v / s (fp32 division) rounded to the
+ * nearest E4M3 value, ties to the even code, saturating at +-448, the sign kept;
+ * an all-zero block has s = 0 and codes 0. A code c of a block with scale s
+ * stands for e4m3(c) * s. Scale arrays are fp32 [rows / brows][K / 128],
+ * row-major.
+ *
+ * moe_blockfp8_quantize: a row-major [rows, K] matrix of dtype (fp32 or bf16),
+ * K a multiple of 128, in blocks of brows x 128 (brows 1 or 128, rows a multiple
+ * of brows) -> codes [rows, K] bytes, scales fp32 [rows / brows, K / 128]. For
+ * the experts' weights (brows = 128): W1 [E*H, M] and W2 [E*M, H] rows,
+ * quantised along their input dimension (H and M multiples of 128, so no block
+ * straddles two experts). */
+moe_status moe_blockfp8_quantize(int64_t rows, int32_t K, int32_t brows, int32_t dtype, const void *src,
+                                 void *codes, float *scales, void *stream);
+
+/* moe_encode with the token rows quantised to block-wise FP8 (1 x 128 blocks) on
+ * the way: buf_codes [E*cmax, M] bytes and buf_scales fp32 [E*cmax, M/128], the
+ * rows of moe_encode (a token row quantised once, copied to each kept slot;
+ * padding rows have codes 0 and scale 0). bf16 x; M a multiple of 128. */
+moe_status moe_encode_blockfp8(const moe_shape *shape, const void *x, const int32_t *idx, const int32_t *loc,
+                               const int32_t *fill, const int32_t *capacity, void *buf_codes, float *buf_scales,
+                               void *stream);
+
+/* Expert FFN on block-wise FP8 operands with gfx950's fp8 MFMA, for the filled
+ * rows j < fill[e] (padding rows are not written):
+ *   pre = buf . W1[e]^T + b1[e]  (products of the dequantised values, fp32
+ *         accumulation: each 128-deep block's partial sum times its two scales)
+ *   h   = act(pre) in fp32, quantised in 1 x 128 blocks along H: h_codes
+ *         [E*cmax, H], h_scales fp32 [E*cmax, H/128]
+ *   y   = h . W2[e]^T + b2[e]    (fp32 accumulation), stored bf16 [E*cmax, M]
+ * W1 codes/scales from moe_blockfp8_quantize(brows = 128) of [E*H, M], W2 of
+ * [E*M, H]; b1 [E, H], b2 [E, M] bf16 (NULL iff the bias is off). dtype must be
+ * bf16; M and H multiples of 128. The hardware's fp8 accumulation within a
+ * block drops low-order bits of products far below the largest (about 1e-4 of
+ * the sum of magnitudes). */
+moe_status moe_expert_ffn_blockfp8(const moe_shape *shape, const void *buf_codes, const float *buf_scales,
+                                   const void *W1_codes, const float *W1_scales, const void *b1,
+                                   const void *W2_codes, const float *W2_scales, const void *b2,
+                                   const int32_t *fill, const int32_t *capacity, void *h_codes, float *h_scales,
+                                   void *y, void *stream);
+
+/* The two halves of moe_expert_ffn_blockfp8 (same definitions and row rules):
+ *   moe_expert_fc1_blockfp8: h = blockFP8(act(buf . W1[e]^T + b1[e]))
+ *   moe_expert_fc2_blockfp8: y = h . W2[e]^T + b2[e]                 */
+moe_status moe_expert_fc1_blockfp8(const moe_shape *shape, const void *buf_codes, const float *buf_scales,
+                                   const void *W1_codes, const float *W1_scales, const void *b1,
+                                   const int32_t *fill, const int32_t *capacity, void *h_codes, float *h_scales,
+                                   void *stream);
+moe_status moe_expert_fc2_blockfp8(const moe_shape *shape, const void *h_codes, const float *h_scales,
+                                   const void *W2_codes, const float *W2_scales, const void *b2,
+                                   const int32_t *fill, const int32_t *capacity, void *y, void *stream);
+
+/* The whole forward with block-wise FP8 experts: [gate projection] -> route ->
+ * moe_encode_blockfp8 -> moe_expert_ffn_blockfp8 -> moe_decode (bf16 out),
+ * arguments as in moe_layer_forward and the calls above. */
+moe_status moe_layer_forward_blockfp8(const moe_shape *shape, const void *x, const float *logits_in,
+                                      const float *Wg, float *logits_out, const void *W1_codes,
+                                      const float *W1_scales, const void *b1, const void *W2_codes,
+                                      const float *W2_scales, const void *b2, int32_t *idx, int32_t *loc,
+                                      float *gates, int32_t *needed, int32_t *fill, int32_t *capacity,
+                                      int32_t *slot_route, void *buf_codes, float *buf_scales, void *h_codes,
+                                      float *h_scales, void *y, void *out, void *ws, size_t ws_bytes,
+                                      void *stream);
 
 /* Residual-MoE (MoE training blog, part 1 section 1.2, the residual half of
  * PR-MoE): every token also passes through one fixed dense MLP, and its output

@@ -32,7 +32,7 @@ def odd_ptr():
 
 def test_every_declared_symbol_is_exported(moe):
     names = _declared()
-    assert len(names) == 35, names
+    assert len(names) == 41, names
     lib = ctypes.CDLL(moe.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n

@@ -57,7 +57,8 @@ class Workload:
     logits: str = "normal"  # "normal" | "gate" (x @ Wg) | "zipf" (normal + Zipf(1.1) bias x2)
     backward: bool = False
     residual: bool = False  # Residual-MoE: a dense MLP branch added to the MoE output
-    mx: str = ""  # "mxfp8" / "mxfp4": experts with MX-quantised weights (tokens and h in MXFP8)
+    mx: str = ""  # "mxfp8" / "mxfp4": experts with MX-quantised weights (tokens and h in MXFP8);
+    #               "blockfp8": block-wise FP8 experts (weights, tokens and h)
 
     def replace(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
@@ -96,11 +97,14 @@ GATED_MXFP8 = GATED_BF16.replace(name="gated_mxfp8_S4096_M1024_E8_k2_H4096", mx=
 GATED_MXFP4 = GATED_BF16.replace(name="gated_mxfp4_S4096_M1024_E8_k2_H4096", mx="mxfp4")
 DSPR_MXFP8 = Workload("dspr_mxfp8_S8192_M2048_E16_k3_H8192", S=8192, M=2048, E=16, k=3, H=8192,
                       capacity_factor=0.0, mx="mxfp8")
+# ... and with block-wise FP8 experts (fp32 scales per 128 x 128 weight block, 1 x 128 token block)
+GATED_BLOCKFP8 = GATED_BF16.replace(name="gated_blockfp8_S4096_M1024_E8_k2_H4096", mx="blockfp8")
+DSPR_BLOCKFP8 = DSPR_MXFP8.replace(name="dspr_blockfp8_S8192_M2048_E16_k3_H8192", mx="blockfp8")
 
 WORKLOADS = [TINY_F32, GATED_BF16, GATED_TRAIN_BF16, RESIDUAL_BF16, RESIDUAL_TRAIN_BF16, DSPR_BF16, FINE_BF16,
              LARGE_BF16]
 # MX workloads are measured by bench.py and checked by the MX parity tests
-MX_WORKLOADS = [GATED_MXFP8, GATED_MXFP4, DSPR_MXFP8]
+MX_WORKLOADS = [GATED_MXFP8, GATED_MXFP4, DSPR_MXFP8, GATED_BLOCKFP8, DSPR_BLOCKFP8]
 BY_NAME = {w.name: w for w in WORKLOADS + MX_WORKLOADS}
 
 
