@@ -956,7 +956,7 @@ __device__ __forceinline__ mx_v8i mx_frag(const bf16_t *tile, int row, int s, in
 }
 
 template <int BM, int BN, int NTH, int EPI, int ACT, int WFMT, bool BLK = false>
-__global__ __launch_bounds__(NTH, 1) void rows_gemm_mx(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
+__global__ __launch_bounds__(NTH, (BLK && BM * BN <= 128 * 128) ? 2 : 1) void rows_gemm_mx(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
                                                      const uint8_t *__restrict__ B, const uint8_t *__restrict__ Bs,
                                                      void *__restrict__ D, uint8_t *__restrict__ Dsc, int N, int K,
                                                      int E, const int32_t *__restrict__ fill,
@@ -1062,83 +1062,111 @@ __global__ __launch_bounds__(NTH, 1) void rows_gemm_mx(const uint8_t *__restrict
             wait_vmcnt<0>();
         }
         barrier_keep_loads();
-        // Ping-pong over the two 64-wide slices of a stage: slice 1's fragments are read
-        // while slice 0 multiplies; the barrier sits before slice 1's MFMAs, after which
-        // stage t+2's loads refill the buffer just read and stage t+1's first fragments are
-        // read while slice 1 multiplies.
-        mx_v8i fa0[TM], fb0[TN], fa1[TM], fb1[TN];
+        if constexpr (BLK) {
+            // One set of fragments: a stage's slice 0 is read and multiplied, then slice 1,
+            // into the partial P; then acc += P * (s_token * s_weight) and the end-of-stage
+            // barrier, after which stage t+2's loads refill the buffer just read. Without the
+            // ping-pong's second set of fragments the kernel fits two workgroups per CU, whose
+            // MFMAs cover each other's LDS reads.
+            for (int t = 0; t < nk; ++t) {
+                const bf16_t *scur = lds + (t & 1) * STAGE;
 #pragma unroll
-        for (int i = 0; i < TM; ++i) fa0[i] = mx_frag<RA, false>(lds, wr0 + i * 32 + (lane & 31), 0, h);
+                for (int i = 0; i < TM; ++i) sa_cur[i] = pick(sa_g[i], t);
 #pragma unroll
-        for (int j = 0; j < TN; ++j) fb0[j] = mx_frag<RBW, FP4>(lds + BM * KA, wc0 + j * 32 + (lane & 31), 0, h);
-        for (int t = 0; t < nk; ++t) {
-            const bf16_t *scur = lds + (t & 1) * STAGE;
-            // this stage's scale dwords (four blocks per row); the next group is requested one
-            // stage ahead of its first use
+                for (int j = 0; j < TN; ++j) sb_cur[j] = pick(sb_g[j], t);
+                const int step = wide ? 4 : 1;
+                if ((t + 1) % step == 0 && t + 1 < nk) load_group(t + 1, sa_g, sb_g);
 #pragma unroll
-            for (int i = 0; i < TM; ++i) sa_cur[i] = pick(sa_g[i], t);
+                for (int sl = 0; sl < 2; ++sl) {
+                    mx_v8i fa[TM], fb[TN];
 #pragma unroll
-            for (int j = 0; j < TN; ++j) sb_cur[j] = pick(sb_g[j], t);
-            // the group's last stage has taken its dwords: the registers take the next group,
-            // which lands before the end-of-stage wait
-            const int step = wide ? 4 : 1;
-            if ((t + 1) % step == 0 && t + 1 < nk) load_group(t + 1, sa_g, sb_g);
+                    for (int i = 0; i < TM; ++i) fa[i] = mx_frag<RA, false>(scur, wr0 + i * 32 + (lane & 31), sl, h);
 #pragma unroll
-            for (int i = 0; i < TM; ++i) fa1[i] = mx_frag<RA, false>(scur, wr0 + i * 32 + (lane & 31), 1, h);
-#pragma unroll
-            for (int j = 0; j < TN; ++j) fb1[j] = mx_frag<RBW, FP4>(scur + BM * KA, wc0 + j * 32 + (lane & 31), 1, h);
-            {
-                const int sh = 8 * h;  // slice 0: k-blocks 0 (half 0) and 1 (half 1) of the stage
-#pragma unroll
-                for (int i = 0; i < TM; ++i)
-#pragma unroll
-                    for (int j = 0; j < TN; ++j) {
-                        if constexpr (BLK)
-                            part[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb0[j], fa0[i], zero, 0, 0,
-                                                                                         0, 127, 0, 127);
-                        else
-                            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                                fb0[j], fa0[i], acc[i][j], WCODE, 0, 0, static_cast<int>((sb_cur[j] >> sh) & 0xFFu),
-                                0, static_cast<int>((sa_cur[i] >> sh) & 0xFFu));
-                    }
-            }
-            wait_vmcnt<0>();  // stage t+1's ring loads and scales have landed
-            barrier_keep_loads_lds();
-            if (t + 2 < nk) {
-                bf16_t *sn = lds + (t & 1) * STAGE;
-                dma_tile<BM, KA, NW>(Ab, ldA, rows_valid, (t + 2) * KA, sn, wave, lane);
-                dma_tile<BN, KW, NW>(Bb, ldB, cols_valid, (t + 2) * KW, sn + BM * KA, wave, lane);
-            }
-            // at the last stage these reads are from the other buffer and unused
-            const bf16_t *snext = lds + ((t + 1) & 1) * STAGE;
-#pragma unroll
-            for (int i = 0; i < TM; ++i) fa0[i] = mx_frag<RA, false>(snext, wr0 + i * 32 + (lane & 31), 0, h);
-#pragma unroll
-            for (int j = 0; j < TN; ++j) fb0[j] = mx_frag<RBW, FP4>(snext + BM * KA, wc0 + j * 32 + (lane & 31), 0, h);
-            {
-                const int sh = 8 * (2 + h);  // slice 1: k-blocks 2 and 3
-#pragma unroll
-                for (int i = 0; i < TM; ++i)
-#pragma unroll
-                    for (int j = 0; j < TN; ++j) {
-                        if constexpr (BLK)
-                            part[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb1[j], fa1[i], part[i][j],
-                                                                                         0, 0, 0, 127, 0, 127);
-                        else
-                            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                                fb1[j], fa1[i], acc[i][j], WCODE, 0, 0, static_cast<int>((sb_cur[j] >> sh) & 0xFFu),
-                                0, static_cast<int>((sa_cur[i] >> sh) & 0xFFu));
-                    }
-                if constexpr (BLK) {
-                    // the stage's partial sums times the token's and the weight block's scales
+                    for (int j = 0; j < TN; ++j)
+                        fb[j] = mx_frag<RBW, false>(scur + BM * KA, wc0 + j * 32 + (lane & 31), sl, h);
 #pragma unroll
                     for (int i = 0; i < TM; ++i)
 #pragma unroll
-                        for (int j = 0; j < TN; ++j) {
-                            const float f = __uint_as_float(sa_cur[i]) * __uint_as_float(sb_cur[j]);
+                        for (int j = 0; j < TN; ++j)
+                            part[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                                fb[j], fa[i], sl == 0 ? zero : part[i][j], 0, 0, 0, 127, 0, 127);
+                }
 #pragma unroll
-                            for (int v = 0; v < 16; ++v) acc[i][j][v] = fmaf(part[i][j][v], f, acc[i][j][v]);
-                        }
+                for (int i = 0; i < TM; ++i)
+#pragma unroll
+                    for (int j = 0; j < TN; ++j) {
+                        const float f = __uint_as_float(sa_cur[i]) * __uint_as_float(sb_cur[j]);
+#pragma unroll
+                        for (int v = 0; v < 16; ++v) acc[i][j][v] = fmaf(part[i][j][v], f, acc[i][j][v]);
+                    }
+                wait_vmcnt<0>();  // stage t+1's ring loads and the scales have landed
+                barrier_keep_loads_lds();
+                if (t + 2 < nk) {
+                    bf16_t *sn = lds + (t & 1) * STAGE;
+                    dma_tile<BM, KA, NW>(Ab, ldA, rows_valid, (t + 2) * KA, sn, wave, lane);
+                    dma_tile<BN, KW, NW>(Bb, ldB, cols_valid, (t + 2) * KW, sn + BM * KA, wave, lane);
+                }
+            }
+        } else {
+            // Ping-pong over the two 64-wide slices of a stage: slice 1's fragments are read
+            // while slice 0 multiplies; the barrier sits before slice 1's MFMAs, after which
+            // stage t+2's loads refill the buffer just read and stage t+1's first fragments are
+            // read while slice 1 multiplies.
+            mx_v8i fa0[TM], fb0[TN], fa1[TM], fb1[TN];
+#pragma unroll
+            for (int i = 0; i < TM; ++i) fa0[i] = mx_frag<RA, false>(lds, wr0 + i * 32 + (lane & 31), 0, h);
+#pragma unroll
+            for (int j = 0; j < TN; ++j) fb0[j] = mx_frag<RBW, FP4>(lds + BM * KA, wc0 + j * 32 + (lane & 31), 0, h);
+            for (int t = 0; t < nk; ++t) {
+                const bf16_t *scur = lds + (t & 1) * STAGE;
+                // this stage's scale dwords (four blocks per row); the next group is requested one
+                // stage ahead of its first use
+#pragma unroll
+                for (int i = 0; i < TM; ++i) sa_cur[i] = pick(sa_g[i], t);
+#pragma unroll
+                for (int j = 0; j < TN; ++j) sb_cur[j] = pick(sb_g[j], t);
+                // the group's last stage has taken its dwords: the registers take the next group,
+                // which lands before the end-of-stage wait
+                const int step = wide ? 4 : 1;
+                if ((t + 1) % step == 0 && t + 1 < nk) load_group(t + 1, sa_g, sb_g);
+#pragma unroll
+                for (int i = 0; i < TM; ++i) fa1[i] = mx_frag<RA, false>(scur, wr0 + i * 32 + (lane & 31), 1, h);
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+                    fb1[j] = mx_frag<RBW, FP4>(scur + BM * KA, wc0 + j * 32 + (lane & 31), 1, h);
+                {
+                    const int sh = 8 * h;  // slice 0: k-blocks 0 (half 0) and 1 (half 1) of the stage
+#pragma unroll
+                    for (int i = 0; i < TM; ++i)
+#pragma unroll
+                        for (int j = 0; j < TN; ++j)
+                            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                                fb0[j], fa0[i], acc[i][j], WCODE, 0, 0, static_cast<int>((sb_cur[j] >> sh) & 0xFFu), 0,
+                                static_cast<int>((sa_cur[i] >> sh) & 0xFFu));
+                }
+                wait_vmcnt<0>();  // stage t+1's ring loads and scales have landed
+                barrier_keep_loads_lds();
+                if (t + 2 < nk) {
+                    bf16_t *sn = lds + (t & 1) * STAGE;
+                    dma_tile<BM, KA, NW>(Ab, ldA, rows_valid, (t + 2) * KA, sn, wave, lane);
+                    dma_tile<BN, KW, NW>(Bb, ldB, cols_valid, (t + 2) * KW, sn + BM * KA, wave, lane);
+                }
+                // at the last stage these reads are from the other buffer and unused
+                const bf16_t *snext = lds + ((t + 1) & 1) * STAGE;
+#pragma unroll
+                for (int i = 0; i < TM; ++i) fa0[i] = mx_frag<RA, false>(snext, wr0 + i * 32 + (lane & 31), 0, h);
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+                    fb0[j] = mx_frag<RBW, FP4>(snext + BM * KA, wc0 + j * 32 + (lane & 31), 0, h);
+                {
+                    const int sh = 8 * (2 + h);  // slice 1: k-blocks 2 and 3
+#pragma unroll
+                    for (int i = 0; i < TM; ++i)
+#pragma unroll
+                        for (int j = 0; j < TN; ++j)
+                            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                                fb1[j], fa1[i], acc[i][j], WCODE, 0, 0, static_cast<int>((sb_cur[j] >> sh) & 0xFFu), 0,
+                                static_cast<int>((sa_cur[i] >> sh) & 0xFFu));
                 }
             }
         }
@@ -1953,9 +1981,9 @@ hipError_t mx_launch(int act, const uint8_t *A, const uint8_t *As, const uint8_t
                      uint8_t *Dsc, int N, int K, int E, const int32_t *fill, const int32_t *cap, const void *bias,
                      hipStream_t st) {
     constexpr int lds = mx_lds_bytes<BM, BN, WFMT, EPI, BLK>();
-    // BLK's per-stage partial sums take the registers of a second workgroup per CU (at two
-    // waves per SIMD the compiler spills)
-    constexpr int per_cu = (!BLK && (160 * 1024) / lds >= 2) ? 2 : 1;
+    // BLK's 256-row tiles need every register of a SIMD for one wavefront (their per-stage
+    // partial sums); the 128 x 128 tiles fit two workgroups per CU
+    constexpr int per_cu = ((!BLK || BM * BN <= 128 * 128) && (160 * 1024) / lds >= 2) ? 2 : 1;
     const dim3 grid(resident_blocks(per_cu));
     auto bi = static_cast<const bf16_t *>(bias);
     if (act == MOE_ACT_GELU) {
