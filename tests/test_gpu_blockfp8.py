@@ -257,3 +257,21 @@ def test_blockfp8_full_size_gated_layer():
     out_o = oracle.decode(y_full, rt, w.E, w.dtype, tokens=toks)
     eo = decode_extra(rt, rows, yg, y_o, tokens=toks)
     check_close(host(b["out"][torch.from_numpy(toks).cuda()]), out_o, w.dtype, "out (sampled tokens)", extra=eo)
+
+
+def test_layer_forward_blockfp8_empty_input():
+    # S = 0: every expert buffer row is padding (codes 0, scale 0) and nothing else is written
+    import combine_softmax_top_amd as moe
+    w = W.Workload("blk_empty", S=0, M=256, E=3, k=2, H=128, capacity_factor=1.0)
+    inp = W.make_inputs(w, seed=0)
+    s = shape_of(w)
+    d = {k_: v.cuda() for k_, v in inp.items()}
+    W1g = moe.blockfp8_quantize_weights(d["W1"])
+    W2g = moe.blockfp8_quantize_weights(d["W2"])
+    bufs = moe.alloc_forward_blockfp8(s)
+    bufs["buf_codes"].fill_(0xAB)
+    bufs["buf_scales"].fill_(1.0)
+    b = moe.layer_forward_blockfp8(s, d["x"], W1g, d.get("b1"), W2g, d.get("b2"), logits=d["logits"], bufs=bufs)
+    torch.cuda.synchronize()
+    assert int(b["capacity"].item()) == 1 and b["out"].numel() == 0
+    assert (host(b["buf_codes"][:3]) == 0).all() and (host(b["buf_scales"][:3]) == 0).all()

@@ -218,3 +218,48 @@ def test_residual_layer_backward_matches_oracle(w):
             assert np.array_equal(got, want)
         else:
             assert np.array_equal(host(gr["dx"]).view(np.uint16), bf16_bits_of_f32(want))
+
+
+def test_residual_layer_empty_input():
+    # S = 0: the training step runs and overwrites every weight and bias gradient with zeros
+    import combine_softmax_top_amd as moe
+    w = W.Workload("res_empty", S=0, M=64, E=3, k=1, H=128, capacity_factor=1.0, residual=True)
+    inp = W.make_inputs(w, seed=0, with_dout=True)
+    s = shape_of(w)
+    d = {k_: v.cuda() for k_, v in inp.items()}
+    res = {n: d.get(n) for n in ("W1r", "b1r", "W2r", "b2r")}
+    b = moe.layer_forward(s, d["x"], d["W1"], d.get("b1"), d["W2"], d.get("b2"), logits=d["logits"], training=True,
+                          residual=res)
+    g = moe.alloc_backward(s, residual=True)
+    for n in ("dW1", "dW2", "db1", "db2", "dW1r", "dW2r", "db1r", "db2r"):
+        g[n].fill_(float("nan"))
+    moe.layer_backward(s, b, d["dout"], d["W1"], d["W2"], grads=g, x=d["x"], residual=res)
+    torch.cuda.synchronize()
+    assert b["out"].numel() == 0 and g["dx"].numel() == 0
+    for n in ("dW1", "dW2", "db1", "db2", "dW1r", "dW2r", "db1r", "db2r"):
+        assert (host(g[n]) == 0).all(), n
+
+
+def test_residual_backward_of_fully_dropped_tokens_is_the_dense_branch():
+    # all logits tie, so every token picks expert 0 (ties go to the lower index) and capacity keeps
+    # C of them; a token with no kept route gets dx = dx_r exactly (0 + dx_r rounds to dx_r), the
+    # kept ones gain their dbuf rows
+    import combine_softmax_top_amd as moe
+    w = W.Workload("res_ties", S=256, M=128, E=4, k=1, H=128, capacity_factor=0.25, residual=True)
+    inp = W.make_inputs(w, seed=3, with_dout=True)
+    inp["logits"] = torch.zeros(w.S, w.E)
+    s = shape_of(w)
+    d = {k_: v.cuda() for k_, v in inp.items()}
+    res = {n: d.get(n) for n in ("W1r", "b1r", "W2r", "b2r")}
+    b = moe.layer_forward(s, d["x"], d["W1"], d.get("b1"), d["W2"], d.get("b2"), logits=d["logits"], training=True,
+                          residual=res)
+    g = moe.layer_backward(s, b, d["dout"], d["W1"], d["W2"], x=d["x"], residual=res)
+    torch.cuda.synchronize()
+    loc = host(b["loc"])[0]
+    C = int(b["capacity"].item())
+    dropped = np.nonzero(loc >= C)[0]
+    kept = np.nonzero(loc < C)[0]
+    assert len(dropped) == w.S - C > 0
+    dx, dxr = host(g["dx"]).view(np.uint16), host(g["dx_r"]).view(np.uint16)
+    assert np.array_equal(dx[dropped], dxr[dropped])
+    assert not np.array_equal(dx[kept], dxr[kept])
