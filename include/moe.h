@@ -33,10 +33,11 @@
  *  - Every device pointer is 16-byte aligned (checked: MOE_EINVAL); the
  *    kernels move rows as 16-byte vectors.
  *  - Data-type tensors (x, W1, b1, W2, b2, buf, pre, h, y, out, dout, dx, dy,
- *    dpre, dbuf, and Residual-MoE's W1r, b1r, W2r, b2r, h_r, y_r) are fp32 or
- *    bf16 as moe_shape.dtype says. logits, Wg, gates,
- *    dgates, dlogits, the auxiliary loss and the weight/bias gradients are
- *    fp32. Index tables are int32.
+ *    dpre, dbuf, and Residual-MoE's W1r, b1r, W2r, b2r, pre_r, h_r, y_r,
+ *    dpre_r, dx_r) are fp32 or bf16 as moe_shape.dtype says. logits, Wg,
+ *    gates, dgates, dlogits, the auxiliary loss, the weight/bias gradients and
+ *    the block-FP8 scales are fp32; MX and block-FP8 codes and MX scales are
+ *    bytes. Index tables are int32.
  *  - Route tables are route-major [k, S]: entry r*S + s is route r of token s,
  *    r = 0 the largest gate.
  *  - The capacity C is computed on the device and written to capacity[0];
