@@ -69,6 +69,8 @@ def parse():
     ap.add_argument("--batch-streams", type=int, default=0, metavar="N",
                     help="forward workloads: also time consecutive batches alternating over N streams, each stream "
                          "with its own buffers (reported as multi_stream; 0: 2 for forward workloads, off otherwise)")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step captured once in a HIP graph and replayed (reported as 'graph')")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 3 plain device copies of MIB MiB each (the reference kernel that scales the "
                          "FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -443,6 +445,24 @@ def main():
         log(f"[bench] the same steps alternating over {nb} streams: {multi['ms_per_step']:.4f} ms/step, "
             f"{multi['value']:.4g} tokens/s")
 
+    graph = None
+    if args.graph and not pipe:
+        # the same one-stream step captured once (after the eager steps above) and replayed
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(False)
+        for _ in range(args.warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            g.replay()
+        torch.cuda.synchronize()
+        eg = time.perf_counter() - t0
+        graph = dict(value=round(w.S * args.steps / eg, 1), ms_per_step=round(eg * 1e3 / max(1, args.steps), 5))
+        log(f"[bench] the same step replayed from a HIP graph: {graph['ms_per_step']:.4f} ms/step, "
+            f"{graph['value']:.4g} tokens/s")
+
     C = int(bufs["capacity"].item())
     kept = int(bufs["fill"].sum().item())
     log(f"[bench] C={C}, kept={kept}")
@@ -606,7 +626,7 @@ def main():
                     logits=w.logits, backward=w.backward, C=C, kept_routes=kept, parallelism="single-gpu",
                     aux_coef=moe.AUX_COEF if w.backward else None, residual=w.residual, mx=w.mx or None,
                     pipeline=dict(chunks=args.pipeline_chunks, streams=args.pipeline_streams) if pipe else None),
-        roofline=roofline, stages=stages, cpu_baseline=cpu, multi_stream=multi,
+        roofline=roofline, stages=stages, cpu_baseline=cpu, multi_stream=multi, graph=graph,
     )
     print(json.dumps(line), flush=True)
 
