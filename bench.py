@@ -8,10 +8,14 @@ fc1 -> fc2 -> decode, then the backward: decode backward (dy, dgates), the gate
 backward (dlogits through the softmax and the 0.01 load-balance loss), the four
 expert products (dpre with the activation gradient, dW2, dbuf, dW1) and the
 encode backward (dx). Gate-projected workloads add the projection (and dWg and
-dx's gate share in training); Residual-MoE workloads add the dense branch.
-The timed region is exactly --steps calls of the fused C-ABI entry points
-(moe_layer_forward, moe_layer_backward), bracketed by synchronisations; `value`
-is tokens per second of that one-stream loop.
+dx's gate share in training); Residual-MoE workloads add the dense branch (and
+its backward in training); MX and block-FP8 workloads run their experts on the
+fp8 MFMA. The timed region is exactly --steps calls of the fused C-ABI entry
+points (moe_layer_forward, moe_layer_backward, or their variants), bracketed by
+synchronisations; `value` is tokens per second of that one-stream loop. Forward
+workloads also report consecutive batches alternating over two streams
+(`multi_stream`), and --graph the step captured in a HIP graph and replayed
+(`graph`); neither is `value`.
 
 A second loop times each stage through its own C-ABI entry point (one kernel
 each, except route and the gate backward) with HIP events on the stream the
