@@ -636,7 +636,7 @@ hipError_t launch_residual_bwd(const moe_shape &s, const void *dout, const void 
     if (err != hipSuccess) return err;
     moe_shape d = s;
     d.E = 1;
-    return launch_expert_ffn_bwd(d, x, pre_r, h_r, W1r, W2r, dense_rows, dense_rows + 1, const_cast<void *>(dout),
+    return launch_expert_ffn_bwd(d, x, pre_r, h_r, W1r, W2r, dense_rows, dense_rows + 1, dout,
                                  dpre_r, dx_r, dW1r, db1r, dW2r, db2r, s.S > 0 ? s.S : 1, st);
 }
 

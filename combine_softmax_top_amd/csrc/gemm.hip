@@ -2117,7 +2117,7 @@ hipError_t launch_fc1_wgrad(const moe_shape &s, const void *dpre, const void *bu
 // dbuf runs right after dpre is written (dpre's rows are still in the last-level
 // cache); dbuf may alias dy, which is consumed by then.
 hipError_t launch_expert_ffn_bwd(const moe_shape &s, const void *buf, const void *pre, const void *h, const void *W1,
-                                 const void *W2, const int32_t *fill, const int32_t *cap, void *dy, void *dpre,
+                                 const void *W2, const int32_t *fill, const int32_t *cap, const void *dy, void *dpre,
                                  void *dbuf, float *dW1, float *db1, float *dW2, float *db2, int32_t cmax,
                                  hipStream_t st) {
     hipError_t err;

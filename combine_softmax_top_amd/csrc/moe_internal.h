@@ -279,7 +279,7 @@ hipError_t launch_fc1_wgrad(const moe_shape &s, const void *dpre, const void *bu
                             const int32_t *cap, float *dW1, float *db1, int32_t cmax, hipStream_t st);
 hipError_t launch_expert_ffn_bwd(const moe_shape &s, const void *buf, const void *pre, const void *h,
                                  const void *W1, const void *W2, const int32_t *fill,
-                                 const int32_t *cap, void *dy, void *dpre, void *dbuf, float *dW1,
+                                 const int32_t *cap, const void *dy, void *dpre, void *dbuf, float *dW1,
                                  float *db1, float *dW2, float *db2, int32_t cmax, hipStream_t st);
 
 }  // namespace moe
