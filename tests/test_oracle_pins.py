@@ -48,6 +48,7 @@ def test_activation_matches_library():
     t = torch.from_numpy(v).requires_grad_(True)
     g = torch.nn.functional.gelu(t)  # exact erf form
     (dg,) = torch.autograd.grad(g.sum(), t)
+    g = g.detach()
     for i, a in enumerate(v):
         assert oracle.act(W.ACT_GELU, a) == pytest.approx(float(g[i]), abs=1e-15)
         assert oracle.act_grad(W.ACT_GELU, a) == pytest.approx(float(dg[i]), abs=1e-14)
