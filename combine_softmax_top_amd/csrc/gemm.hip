@@ -287,6 +287,13 @@ __device__ __forceinline__ void dma16(const void *base, uint32_t voff_bytes, con
                  : "s"(lds_m0(lds_dst)), "v"(voff_bytes), "s"(base)
                  : "memory", "m0");
 }
+// global_load_lds_dword: 4 bytes per lane, lane l's word at LDS byte M0 + 4 l
+__device__ __forceinline__ void dma4(const void *base, uint32_t voff_bytes, const void *lds_dst) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
+                 :
+                 : "s"(lds_m0(lds_dst)), "v"(voff_bytes), "s"(base)
+                 : "memory", "m0");
+}
 // buffer_load_dwordx4 ... lds through a raw buffer resource (loads past its range return zero)
 __device__ __forceinline__ void dma16_buf(i32x4_t rsrc, uint32_t voff_bytes, const void *lds_dst) {
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
@@ -895,9 +902,14 @@ __global__ __launch_bounds__(NTH, (big_lds_bytes<BM, BN>() * 2 <= 160 * 1024 ? 2
 // lane l holds row l % 32; with 8-bit elements lane half h = l / 32 holds the
 // slice's bytes [16h, 16h+16) and [32+16h, 32+16h+16) (two 16-byte LDS reads),
 // with 4-bit elements bytes [16h, 16h+16) (32 values); the scale of k-block h of
-// the slice comes from lane half h. Each lane loads, a stage ahead of use, the
-// scale bytes of four stages (one 16-byte load) for each of its rows and picks
-// byte 2 * slice + h of the stage's dword. The hardware's fp8 accumulation drops low-order bits of products
+// the slice comes from lane half h, byte 2 * slice + h of the row's dword for the
+// stage. The scale dwords travel through LDS with the ring: the stage that opens a
+// group of four stages (one stage when K is not a multiple of 512) also loads the
+// group's dwords of every tile row, 16 (or 4) bytes per row, into one of two group
+// buffers, and each wavefront reads its rows' dwords after the end-of-stage barrier.
+// Loading them into registers instead would make the compiler, which does not see
+// the ring's direct loads, wait at their first use for every load in flight, the
+// next ring stage included. The hardware's fp8 accumulation drops low-order bits of products
 // far below the largest one in a group of eight (about 1e-4 of the sum of
 // magnitudes), so results match an exact sum within that, not bit for bit.
 // Epilogues: fc1 adds the bias, applies the activation and quantises h to MXFP8
@@ -911,7 +923,7 @@ __global__ __launch_bounds__(NTH, (big_lds_bytes<BM, BN>() * 2 <= 160 * 1024 ? 2
 // scales into a fresh partial P, and acc += P * (s_token * s_weight): the token's
 // scale is per lane (its row), the weight's per 32-column MFMA block (uniform).
 // The scale words have the MX layout's stride (one 32-bit word per row and stage),
-// so they load the same way. fc1 quantises h per (token, 128 features): a
+// so they travel the same way. fc1 quantises h per (token, 128 features): a
 // wavefront holds 64 of a block's features, so the two wavefronts of a block
 // exchange their amax through LDS before dividing by s.
 typedef int mx_v8i __attribute__((ext_vector_type(8)));
@@ -930,9 +942,14 @@ constexpr int mx_region_bytes() {
                                        : BM * BN * 2;
     return ring > epi ? ring : epi;
 }
+// Bytes of one scale group buffer: four stages' dwords of every tile row.
+template <int BM, int BN>
+constexpr int mx_scale_buf_bytes() {
+    return (BM + BN) * 16;
+}
 template <int BM, int BN, int WFMT, int EPI, bool BLK = false>
 constexpr int mx_lds_bytes() {
-    return mx_region_bytes<BM, BN, WFMT, EPI, BLK>() + kBigPrefixBytes + BN * 2;
+    return mx_region_bytes<BM, BN, WFMT, EPI, BLK>() + kBigPrefixBytes + BN * 2 + 2 * mx_scale_buf_bytes<BM, BN>();
 }
 
 // MFMA operand of one row (the lane's) for slice s from an LDS tile of rows of
@@ -974,6 +991,9 @@ __global__ __launch_bounds__(NTH, (BLK && BM * BN <= 128 * 128) ? 2 : 1) void ro
     constexpr int REGION = mx_region_bytes<BM, BN, WFMT, EPI, BLK>() / 2;
     int *prefix = reinterpret_cast<int *>(lds + REGION);
     bf16_t *sbias = lds + REGION + kBigPrefixBytes / 2;
+    // two scale group buffers, each [BM][GS] token dwords then [BN][GS] weight dwords
+    uint32_t *ssc = reinterpret_cast<uint32_t *>(sbias + BN);
+    constexpr int SCB = mx_scale_buf_bytes<BM, BN>() / 4;  // dwords per buffer
     const int nx = (N + BN - 1) / BN;
     const TileSched sc = make_sched<NTH>(fill, E, BM, nx, prefix);
     const int C = *cap;
@@ -992,24 +1012,10 @@ __global__ __launch_bounds__(NTH, (BLK && BM * BN <= 128 * 128) ? 2 : 1) void ro
         const bf16_t *Ab = reinterpret_cast<const bf16_t *>(A + grow0 * K);
         const int64_t wrow0 = static_cast<int64_t>(g) * N + col0;  // first weight row of the tile
         const bf16_t *Bb = reinterpret_cast<const bf16_t *>(B + wrow0 * (FP4 ? K / 2 : K));
-        // the lane's scale rows (clamped into the valid range; clamped rows are never stored)
-        const uint32_t *sa_row[TM];
-        const uint32_t *sb_row[TN];
-#pragma unroll
-        for (int i = 0; i < TM; ++i) {
-            const int r = min(wr0 + i * 32 + (lane & 31), rows_valid - 1);
-            sa_row[i] = reinterpret_cast<const uint32_t *>(As + (grow0 + r) * KS);
-        }
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            if constexpr (BLK) {  // the 128-row weight block of the MFMA block's columns
-                const int c = min(wc0 + j * 32, cols_valid - 1);
-                sb_row[j] = reinterpret_cast<const uint32_t *>(Bs + ((wrow0 + c) / 128) * KS);
-            } else {
-                const int c = min(wc0 + j * 32 + (lane & 31), cols_valid - 1);
-                sb_row[j] = reinterpret_cast<const uint32_t *>(Bs + (wrow0 + c) * KS);
-            }
-        }
+        // scale rows: the tile's tokens; the weights' rows (BLK: their 128-row blocks, the
+        // tile's first one at wrow0 / 128 as N is a multiple of 128)
+        const uint8_t *sa_base = As + grow0 * KS;
+        const uint8_t *sb_base = Bs + (BLK ? wrow0 / 128 : wrow0) * KS;
 
         f32x16 acc[TM][TN], part[TM][TN];  // part: BLK's per-stage partial sums
         f32x16 zero;
@@ -1025,43 +1031,62 @@ __global__ __launch_bounds__(NTH, (BLK && BM * BN <= 128 * 128) ? 2 : 1) void ro
             const int c = min(lane * 8, cols_valid - 8);
             dma16(bias + wrow0, static_cast<uint32_t>(c) * 2, sbias);
         }
-        // Scales: four stages' worth (16 bytes) per row and load when the rows are 16-byte
-        // aligned (K a multiple of 512), else one stage (a dword) per load. Each lane's
-        // rows are all different, so every load instruction touches 32 cache lines; the
-        // wide form makes four times fewer of them. Stage 0's group first, then the ring's
-        // first two stages (loads complete in order).
-        const bool wide = (K % 512) == 0;
-        uint4 sa_g[TM], sb_g[TN];
-        auto load_group = [&](int g0, uint4 (&ga)[TM], uint4 (&gb)[TN]) {
-            if (wide) {
-#pragma unroll
-                for (int i = 0; i < TM; ++i) ga[i] = reinterpret_cast<const uint4 *>(sa_row[i])[g0 / 4];
-#pragma unroll
-                for (int j = 0; j < TN; ++j) gb[j] = reinterpret_cast<const uint4 *>(sb_row[j])[g0 / 4];
-            } else {
-#pragma unroll
-                for (int i = 0; i < TM; ++i) ga[i].x = sa_row[i][g0];
-#pragma unroll
-                for (int j = 0; j < TN; ++j) gb[j].x = sb_row[j][g0];
+        // Scale groups of GS stages: 16-byte loads of four stages' dwords when the rows are
+        // 16-byte aligned (K a multiple of 512), else one stage's dword. Each wavefront loads
+        // 64 rows per instruction (rows clamped into the valid range, as for the ring), the
+        // group of stages [s, s + GS) going to buffer (s / GS) & 1.
+        const int GS = (K % 512) == 0 ? 4 : 1;
+        auto dma_scales = [&](int s) {
+            uint32_t *buf = ssc + ((s / GS) & 1) * SCB;
+            for (int q = wave; q < (BM + BN) / 64; q += NW) {
+                const bool tok = q < BM / 64;
+                const int r0 = (tok ? q : q - BM / 64) * 64;
+                uint32_t off;
+                if (tok) {
+                    off = static_cast<uint32_t>(min(r0 + lane, rows_valid - 1) * KS + s * 4);
+                } else {
+                    const int c = min(r0 + lane, cols_valid - 1);
+                    off = static_cast<uint32_t>((BLK ? c / 128 : c) * KS + s * 4);
+                }
+                uint32_t *dst = buf + (tok ? 0 : BM * 4) + r0 * GS;
+                if (GS == 4)
+                    dma16(tok ? sa_base : sb_base, off, dst);
+                else
+                    dma4(tok ? sa_base : sb_base, off, dst);
             }
         };
-        auto pick = [&](const uint4 &v, int t) -> uint32_t {
-            if (!wide) return v.x;
-            const int q = t & 3;
-            return q == 0 ? v.x : (q == 1 ? v.y : (q == 2 ? v.z : v.w));
+        // stage s's dwords of the wavefront's rows (the group was loaded with stage s - s % GS,
+        // which has passed an end-of-stage barrier)
+        auto read_scales = [&](int s, uint32_t(&ca)[TM], uint32_t(&cb)[TN]) {
+            const uint32_t *buf = ssc + ((s / GS) & 1) * SCB;
+            const int slot = s & (GS - 1);
+#pragma unroll
+            for (int i = 0; i < TM; ++i) ca[i] = buf[(wr0 + i * 32 + (lane & 31)) * GS + slot];
+#pragma unroll
+            for (int j = 0; j < TN; ++j) cb[j] = buf[BM * 4 + (wc0 + j * 32 + (lane & 31)) * GS + slot];
         };
-        load_group(0, sa_g, sb_g);
+        // stage t's ring loads, after its scale group when t opens one
+        auto dma_stage = [&](int t) {
+            if (t % GS == 0) dma_scales(t);
+            bf16_t *sn = lds + (t & 1) * STAGE;
+            dma_tile<BM, KA, NW>(Ab, ldA, rows_valid, t * KA, sn, wave, lane);
+            dma_tile<BN, KW, NW>(Bb, ldB, cols_valid, t * KW, sn + BM * KA, wave, lane);
+        };
         uint32_t sa_cur[TM], sb_cur[TN];
-        dma_tile<BM, KA, NW>(Ab, ldA, rows_valid, 0, lds, wave, lane);
-        dma_tile<BN, KW, NW>(Bb, ldB, cols_valid, 0, lds + BM * KA, wave, lane);
+        dma_stage(0);
         if (nk > 1) {
-            dma_tile<BM, KA, NW>(Ab, ldA, rows_valid, KA, lds + STAGE, wave, lane);
-            dma_tile<BN, KW, NW>(Bb, ldB, cols_valid, KW, lds + STAGE + BM * KA, wave, lane);
+            // stage 1's scale dwords (GS = 1) are requested before its ring loads, so this count
+            // of stage 1's ring loads still covers them
+            if (GS == 1) dma_scales(1);
+            bf16_t *sn = lds + STAGE;
+            dma_tile<BM, KA, NW>(Ab, ldA, rows_valid, KA, sn, wave, lane);
+            dma_tile<BN, KW, NW>(Bb, ldB, cols_valid, KW, sn + BM * KA, wave, lane);
             wait_vmcnt<(BM * KA + BN * KW) / 8 / NTH>();
         } else {
             wait_vmcnt<0>();
         }
         barrier_keep_loads();
+        read_scales(0, sa_cur, sb_cur);
         if constexpr (BLK) {
             // One set of fragments: a stage's slice 0 is read and multiplied, then slice 1,
             // into the partial P; then acc += P * (s_token * s_weight) and the end-of-stage
@@ -1070,12 +1095,6 @@ __global__ __launch_bounds__(NTH, (BLK && BM * BN <= 128 * 128) ? 2 : 1) void ro
             // MFMAs cover each other's LDS reads.
             for (int t = 0; t < nk; ++t) {
                 const bf16_t *scur = lds + (t & 1) * STAGE;
-#pragma unroll
-                for (int i = 0; i < TM; ++i) sa_cur[i] = pick(sa_g[i], t);
-#pragma unroll
-                for (int j = 0; j < TN; ++j) sb_cur[j] = pick(sb_g[j], t);
-                const int step = wide ? 4 : 1;
-                if ((t + 1) % step == 0 && t + 1 < nk) load_group(t + 1, sa_g, sb_g);
 #pragma unroll
                 for (int sl = 0; sl < 2; ++sl) {
                     mx_v8i fa[TM], fb[TN];
@@ -1099,13 +1118,10 @@ __global__ __launch_bounds__(NTH, (BLK && BM * BN <= 128 * 128) ? 2 : 1) void ro
 #pragma unroll
                         for (int v = 0; v < 16; ++v) acc[i][j][v] = fmaf(part[i][j][v], f, acc[i][j][v]);
                     }
-                wait_vmcnt<0>();  // stage t+1's ring loads and the scales have landed
+                wait_vmcnt<0>();  // stage t+1's ring loads and scales have landed
                 barrier_keep_loads_lds();
-                if (t + 2 < nk) {
-                    bf16_t *sn = lds + (t & 1) * STAGE;
-                    dma_tile<BM, KA, NW>(Ab, ldA, rows_valid, (t + 2) * KA, sn, wave, lane);
-                    dma_tile<BN, KW, NW>(Bb, ldB, cols_valid, (t + 2) * KW, sn + BM * KA, wave, lane);
-                }
+                if (t + 1 < nk) read_scales(t + 1, sa_cur, sb_cur);
+                if (t + 2 < nk) dma_stage(t + 2);
             }
         } else {
             // Ping-pong over the two 64-wide slices of a stage: slice 1's fragments are read
@@ -1119,16 +1135,6 @@ __global__ __launch_bounds__(NTH, (BLK && BM * BN <= 128 * 128) ? 2 : 1) void ro
             for (int j = 0; j < TN; ++j) fb0[j] = mx_frag<RBW, FP4>(lds + BM * KA, wc0 + j * 32 + (lane & 31), 0, h);
             for (int t = 0; t < nk; ++t) {
                 const bf16_t *scur = lds + (t & 1) * STAGE;
-                // this stage's scale dwords (four blocks per row); the next group is requested one
-                // stage ahead of its first use
-#pragma unroll
-                for (int i = 0; i < TM; ++i) sa_cur[i] = pick(sa_g[i], t);
-#pragma unroll
-                for (int j = 0; j < TN; ++j) sb_cur[j] = pick(sb_g[j], t);
-                // the group's last stage has taken its dwords: the registers take the next group,
-                // which lands before the end-of-stage wait
-                const int step = wide ? 4 : 1;
-                if ((t + 1) % step == 0 && t + 1 < nk) load_group(t + 1, sa_g, sb_g);
 #pragma unroll
                 for (int i = 0; i < TM; ++i) fa1[i] = mx_frag<RA, false>(scur, wr0 + i * 32 + (lane & 31), 1, h);
 #pragma unroll
@@ -1146,11 +1152,9 @@ __global__ __launch_bounds__(NTH, (BLK && BM * BN <= 128 * 128) ? 2 : 1) void ro
                 }
                 wait_vmcnt<0>();  // stage t+1's ring loads and scales have landed
                 barrier_keep_loads_lds();
-                if (t + 2 < nk) {
-                    bf16_t *sn = lds + (t & 1) * STAGE;
-                    dma_tile<BM, KA, NW>(Ab, ldA, rows_valid, (t + 2) * KA, sn, wave, lane);
-                    dma_tile<BN, KW, NW>(Bb, ldB, cols_valid, (t + 2) * KW, sn + BM * KA, wave, lane);
-                }
+                uint32_t sa_nxt[TM], sb_nxt[TN];
+                if (t + 1 < nk) read_scales(t + 1, sa_nxt, sb_nxt);
+                if (t + 2 < nk) dma_stage(t + 2);
                 // at the last stage these reads are from the other buffer and unused
                 const bf16_t *snext = lds + ((t + 1) & 1) * STAGE;
 #pragma unroll
@@ -1167,6 +1171,12 @@ __global__ __launch_bounds__(NTH, (BLK && BM * BN <= 128 * 128) ? 2 : 1) void ro
                             acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
                                 fb1[j], fa1[i], acc[i][j], WCODE, 0, 0, static_cast<int>((sb_cur[j] >> sh) & 0xFFu), 0,
                                 static_cast<int>((sa_cur[i] >> sh) & 0xFFu));
+                }
+                if (t + 1 < nk) {
+#pragma unroll
+                    for (int i = 0; i < TM; ++i) sa_cur[i] = sa_nxt[i];
+#pragma unroll
+                    for (int j = 0; j < TN; ++j) sb_cur[j] = sb_nxt[j];
                 }
             }
         }
