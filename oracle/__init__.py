@@ -103,6 +103,13 @@ def lib():
         L.oracle_expert_rows_blockfp8.argtypes = [i32, i32, i32, ctypes.c_int, u8p, _c_f32p, u8p, _c_f32p, vp, u8p,
                                                   _c_f32p, vp, i64, _c_i64p, vp, vp, vp]
         L.oracle_expert_rows_blockfp8.restype = None
+        L.oracle_nvfp4_quantize.argtypes = [i64, i32, i32, ctypes.c_int, vp, u8p, u8p, _c_f32p]
+        L.oracle_nvfp4_quantize.restype = None
+        L.oracle_nvfp4_dequantize.argtypes = [i64, i32, i32, u8p, u8p, _c_f32p, _c_f64p]
+        L.oracle_nvfp4_dequantize.restype = None
+        L.oracle_expert_rows_nvfp4.argtypes = [i32, i32, i32, ctypes.c_int, vp, u8p, u8p, _c_f32p, vp, u8p, u8p,
+                                               _c_f32p, vp, i64, _c_i64p, vp, vp, vp]
+        L.oracle_expert_rows_nvfp4.restype = None
         L.oracle_gate_backward.argtypes = [i32, i32, i32, d, _c_f32p, _c_i32p, _c_f32p, vp, _c_f64p, _c_f64p]
         L.oracle_gate_backward.restype = None
         L.oracle_gate_weight_grad.argtypes = [i32, i32, i32, ctypes.c_int, vp, _c_f64p, _c_f64p]
@@ -645,3 +652,62 @@ def expert_rows_blockfp8(bufq, W1q, b1, W2q, b2, rows: Sequence[int], C: int, ac
     lib().oracle_expert_rows_blockfp8(M, H, C, act_kind, bc, bs, w1c, w1s, _ptr(b1), w2c, w2s, _ptr(b2), n, rows,
                                       _ptr(hc), _ptr(hs), _ptr(y))
     return ((hc, hs) if want_hq else None), y
+
+
+# ------------------------------------------------------------------ NVFP4 experts (weights)
+
+NVFP4_BLOCK = 16  # values per E4M3-scaled block along the reduction dimension
+
+
+def nvfp4_quantize(a: np.ndarray, dtype: int):
+    """NVFP4 quantisation of a data-type array [..., rows, K] (K a multiple of 16), each matrix
+    over the last two dimensions one tensor with its own fp32 scale: returns (codes uint8
+    [..., rows, K/2], block scales uint8 (E4M3) [..., rows, K/16], g fp32 [...])."""
+    a = _check(a, dtype)
+    assert a.ndim >= 2
+    K = a.shape[-1]
+    assert K % NVFP4_BLOCK == 0
+    lead = a.shape[:-2]
+    nt = int(np.prod(lead, dtype=np.int64)) if lead else 1
+    rows = nt * a.shape[-2]
+    codes = np.zeros(a.shape[:-1] + (K // 2,), np.uint8)
+    scales = np.zeros(a.shape[:-1] + (K // NVFP4_BLOCK,), np.uint8)
+    g = np.zeros(lead if lead else (1,), np.float32)
+    lib().oracle_nvfp4_quantize(rows, K, nt, dtype, _ptr(a), codes, scales, g)
+    return codes, scales, (g if lead else g.reshape(()))
+
+
+def nvfp4_dequantize(codes: np.ndarray, scales: np.ndarray, g: np.ndarray) -> np.ndarray:
+    """Exact values (fp64 [..., rows, K]) of an NVFP4 array from nvfp4_quantize."""
+    K = scales.shape[-1] * NVFP4_BLOCK
+    lead = scales.shape[:-2]
+    nt = int(np.prod(lead, dtype=np.int64)) if lead else 1
+    rows = nt * scales.shape[-2]
+    out = np.empty(scales.shape[:-1] + (K,), np.float64)
+    lib().oracle_nvfp4_dequantize(rows, K, nt, np.ascontiguousarray(codes), np.ascontiguousarray(scales),
+                                  np.ascontiguousarray(np.asarray(g, np.float32).reshape(-1)), out)
+    return out
+
+
+def expert_rows_nvfp4(buf, W1q, b1, W2q, b2, rows: Sequence[int], C: int, act_kind: int):
+    """Expert FFN with NVFP4 weights for the listed buffer rows: buf bf16 [E*C, M]; W1q = (codes
+    [E, H, M/2], scales [E, H, M/16], g [E]) and W2q likewise [E, M, H]; biases bf16 or None.
+    Returns pre, h (bf16 [n, H]) and y (bf16 [n, M]), compact per listed row."""
+    w1c, w1s = np.ascontiguousarray(W1q[0]), np.ascontiguousarray(W1q[1])
+    w2c, w2s = np.ascontiguousarray(W2q[0]), np.ascontiguousarray(W2q[1])
+    g1 = np.ascontiguousarray(np.asarray(W1q[2], np.float32).reshape(-1))
+    g2 = np.ascontiguousarray(np.asarray(W2q[2], np.float32).reshape(-1))
+    E, H = w1s.shape[0], w1s.shape[1]
+    M = w2s.shape[1]
+    buf = _check(buf, DT_BF16)
+    assert buf.shape[-1] == M
+    rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    n = rows.shape[0]
+    pre = np.empty((n, H), np.uint16)
+    h = np.empty((n, H), np.uint16)
+    y = np.empty((n, M), np.uint16)
+    b1 = None if b1 is None else _check(b1, DT_BF16, (E, H))
+    b2 = None if b2 is None else _check(b2, DT_BF16, (E, M))
+    lib().oracle_expert_rows_nvfp4(M, H, C, act_kind, _ptr(buf), w1c, w1s, g1, _ptr(b1), w2c, w2s, g2, _ptr(b2), n,
+                                   rows, _ptr(pre), _ptr(h), _ptr(y))
+    return pre, h, y

@@ -816,3 +816,126 @@ void oracle_expert_rows_blockfp8(int32_t M, int32_t H, int32_t C, int act, const
         free(xv); free(hf); free(hv); free(hc); free(hs);
     }
 }
+
+/* ------------------------------------------------------------------ NVFP4 experts (weights) */
+
+/* NVFP4 (the Tutel pages name it beside FP8, MXFP4 and block-wise FP8 without
+ * defining it; the reading is NVIDIA's published two-level 4-bit format): E2M1
+ * elements in blocks of 16 consecutive values along the reduction dimension,
+ * each block with an E4M3 scale, and one fp32 scale g per tensor (here each
+ * expert's weight matrix). The pages list these formats for A100/A800/H100/MI300,
+ * which have no 4-bit matrix arithmetic, so the reading is weight-only: the
+ * experts' weights are stored NVFP4 and multiplied by bf16 tokens at their exact
+ * values. Quantisation of one tensor, fp32 arithmetic in this order:
+ *   amax_t = max |v|;  g = amax_t / 2688   (448 * 6: E4M3's and E2M1's largest)
+ *   per block of 16: amax_b = max |v|;  d = (amax_b / 6) / g;
+ *     q = the E4M3 code nearest d (ties to the even code, saturating at 448);
+ *     sd = e4m3(q);  each element: c = the E2M1 code nearest v / (sd * g) (the
+ *     product rounded to fp32, then the division), ties to the even code,
+ *     saturating at 6, the sign bit the input's;
+ *   g == 0 (an all-zero tensor) or sd == 0: the block's scale code and element
+ *   codes are 0.
+ * Element c of a block with scale code q in a tensor of scale g stands for
+ * e2m1(c) * e4m3(q) * g. Layout: codes [rows, K/2] (two per byte, the even index
+ * in the low nibble), scales [rows, K/16] E4M3 bytes, g [ntensor] fp32. */
+static void nvfp4_quantize_tensor(const float *v, int64_t rows, int32_t K, uint8_t *codes, uint8_t *scales,
+                                  float *g_out) {
+    float amax_t = 0.0f;
+    for (int64_t i = 0; i < rows * K; ++i) amax_t = fmaxf(amax_t, fabsf(v[i]));
+    const float g = amax_t / 2688.0f;
+    *g_out = g;
+    for (int64_t r = 0; r < rows; ++r)
+        for (int32_t b = 0; b < K / 16; ++b) {
+            const float *blk = v + r * K + 16 * b;
+            float amax_b = 0.0f;
+            for (int i = 0; i < 16; ++i) amax_b = fmaxf(amax_b, fabsf(blk[i]));
+            int q = 0;
+            if (g > 0.0f) {
+                const float d = (amax_b / 6.0f) / g;
+                q = nearest_code((double)d, 0);
+            }
+            const float sd = (float)oracle_e4m3_value(q);
+            scales[r * (K / 16) + b] = (uint8_t)q;
+            for (int i = 0; i < 16; ++i) {
+                int c = 0;
+                if (sd > 0.0f) {
+                    const float den = sd * g;
+                    const float x = blk[i] / den;
+                    c = nearest_code(fabs((double)x), 1) | (signbit(x) ? 0x8 : 0);
+                }
+                const int64_t k = 16 * b + i;
+                uint8_t *byte = codes + r * (K / 2) + k / 2;
+                if (k % 2 == 0) *byte = (uint8_t)c;
+                else *byte |= (uint8_t)(c << 4);
+            }
+        }
+}
+
+static double nvfp4_value(const uint8_t *codes, const uint8_t *scales, double g, int32_t K, int64_t row, int32_t k) {
+    const uint8_t byte = codes[row * (K / 2) + k / 2];
+    const int c = (k & 1) ? (byte >> 4) : (byte & 15);
+    return oracle_e2m1_value(c) * oracle_e4m3_value(scales[row * (K / 16) + k / 16]) * g;
+}
+
+/* Quantise a row-major [rows, K] matrix of the data type (K a multiple of 16) as
+ * ntensor tensors of rows / ntensor consecutive rows each (an expert's matrix). */
+void oracle_nvfp4_quantize(int64_t rows, int32_t K, int32_t ntensor, int dtype, const void *src, uint8_t *codes,
+                           uint8_t *scales, float *g) {
+    const int64_t per = rows / ntensor;
+    float *v = (float *)malloc(sizeof(float) * (size_t)(per * K > 0 ? per * K : 1));
+    for (int32_t t = 0; t < ntensor; ++t) {
+        for (int64_t i = 0; i < per * K; ++i) v[i] = (float)load_elem(src, dtype, t * per * K + i);
+        nvfp4_quantize_tensor(v, per, K, codes + t * per * (K / 2), scales + t * per * (K / 16), g + t);
+    }
+    free(v);
+}
+
+/* Exact values of an NVFP4 matrix of ntensor tensors, fp64 [rows, K]. */
+void oracle_nvfp4_dequantize(int64_t rows, int32_t K, int32_t ntensor, const uint8_t *codes, const uint8_t *scales,
+                             const float *g, double *out) {
+    const int64_t per = rows / ntensor;
+    for (int64_t r = 0; r < rows; ++r)
+        for (int32_t k = 0; k < K; ++k) out[r * K + k] = nvfp4_value(codes, scales, (double)g[r / per], K, r, k);
+}
+
+/* Expert FFN with NVFP4 weights and bf16 tokens, for the listed buffer rows
+ * (row = e*C + j), the bf16 expert FFN's definitions on the weights' values:
+ *   pre = sum_m buf[row][m] W1[e][h][m] + b1[e][h]   (fp64 sums)
+ *   h   = act(pre), rounded to bf16
+ *   y   = sum_h h[h] W2[e][m][h] + b2[e][m], rounded to bf16
+ * buf bf16 [E*C, M]; W1 codes [E*H, M/2], scales [E*H, M/16], g1 [E]; W2 codes
+ * [E*M, H/2], scales [E*M, H/16], g2 [E]; biases bf16 (may be NULL). Outputs
+ * compact per listed row: pre and h bf16 [n, H] (either may be NULL), y bf16 [n, M]. */
+void oracle_expert_rows_nvfp4(int32_t M, int32_t H, int32_t C, int act, const void *buf, const uint8_t *w1_codes,
+                              const uint8_t *w1_scales, const float *g1, const void *b1, const uint8_t *w2_codes,
+                              const uint8_t *w2_scales, const float *g2, const void *b2, int64_t nrows,
+                              const int64_t *rows, void *pre_out, void *h_out, void *y_out) {
+#pragma omp parallel
+    {
+        double *xv = (double *)malloc(sizeof(double) * (size_t)M);
+        double *hv = (double *)malloc(sizeof(double) * (size_t)H);
+#pragma omp for schedule(dynamic, 4)
+        for (int64_t i = 0; i < nrows; ++i) {
+            const int64_t row = rows[i];
+            const int64_t e = row / C;
+            for (int32_t m = 0; m < M; ++m) xv[m] = load_elem(buf, DT_BF16, row * M + m);
+            for (int32_t h = 0; h < H; ++h) {
+                double acc = 0.0;
+                for (int32_t m = 0; m < M; ++m)
+                    acc += xv[m] * nvfp4_value(w1_codes, w1_scales, (double)g1[e], M, e * H + h, m);
+                if (b1) acc += load_elem(b1, DT_BF16, e * H + h);
+                if (pre_out) store_elem(pre_out, DT_BF16, i * H + h, acc);
+                hv[h] = round_to_dtype(act_f(act, acc), DT_BF16);  /* h as stored feeds fc2 */
+                if (h_out) store_elem(h_out, DT_BF16, i * H + h, hv[h]);
+            }
+            for (int32_t m = 0; m < M; ++m) {
+                double acc = 0.0;
+                for (int32_t h = 0; h < H; ++h)
+                    acc += hv[h] * nvfp4_value(w2_codes, w2_scales, (double)g2[e], H, e * M + m, h);
+                if (b2) acc += load_elem(b2, DT_BF16, e * M + m);
+                store_elem(y_out, DT_BF16, i * M + m, acc);
+            }
+        }
+        free(xv); free(hv);
+    }
+}

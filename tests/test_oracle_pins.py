@@ -1160,3 +1160,135 @@ def test_blockfp8_ffn_on_exact_operands_matches_torch():
         hd = oracle.blockfp8_dequantize(hc, hs, 1)[0]
         yr = torch.from_numpy(hd) @ torch.from_numpy(W2[e]).T + torch.from_numpy(f32_of(b2[e]).astype(np.float64))
         assert np.abs(f32_of(y[r]) - yr.numpy()).max() <= 2 ** -8 * np.abs(yr.numpy()).max()
+
+
+# ---------------------------------------------------------------- NVFP4 experts (weights)
+
+_E2M1 = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def _nvfp4_codes_of(codes, K):
+    lo, hi = (codes & 15).astype(np.int64), (codes >> 4).astype(np.int64)
+    return np.stack([lo, hi], axis=-1).reshape(codes.shape[:-1] + (K,))
+
+
+def test_nvfp4_worked_codes():
+    # One tensor of four 16-value blocks, g fixed at 2^-4 by a block whose amax is 2688 g
+    # (scale code 448 = 0x7E). Hand-derived codes (E2M1 magnitudes 0,.5,1,1.5,2,3,4,6 = codes
+    # 0..7, ties to the even code; E4M3 1.0 = 0x38, 1.125 = 0x39, 448 = 0x7E):
+    g = 2.0 ** -4
+    t = np.zeros((1, 64))
+    t[0, :16] = 0.0; t[0, 0] = 2688 * g; t[0, 1] = -6 * 448 * g          # block 0: sd = 448
+    # block 1: sd = 1 (amax 6 g); x = v / g hits every E2M1 midpoint
+    x1 = [6.0, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, -0.75, -5.0, 0.2, 0.3, 4.9, 5.1, -0.0, 1.0]
+    t[0, 16:32] = np.array(x1) * g
+    want1 = [7, 0, 2, 2, 4, 4, 6, 6, 8 | 2, 8 | 6, 0, 1, 6, 7, 8, 2]
+    # block 2: amax = 6.375 g, d = 1.0625 (a tie between 1.0 and 1.125 -> the even code 0x38),
+    # so v / g = 6.375 saturates to 6 and 3.1875 rounds to 3
+    t[0, 32:48] = np.array([6.375, 3.1875] + [0.0] * 14) * g
+    want2 = [7, 5] + [0] * 14
+    # block 3: amax = 6.1875 g, d = 1.03125 -> E4M3 1.0 (0x38); 6.1875 saturates to 6
+    t[0, 48:64] = np.array([-6.1875, 1.5] + [0.0] * 14) * g
+    want3 = [8 | 7, 3] + [0] * 14
+    codes, scales, gq = oracle.nvfp4_quantize(t.astype(np.float32)[None], W.DT_F32)
+    assert float(gq[0]) == g
+    assert scales[0, 0].tolist() == [0x7E, 0x38, 0x38, 0x38]
+    c = _nvfp4_codes_of(codes[0], 64)[0]
+    assert c[:2].tolist() == [7, 8 | 7]
+    assert c[16:32].tolist() == want1 and c[32:48].tolist() == want2 and c[48:64].tolist() == want3
+    deq = oracle.nvfp4_dequantize(codes, scales, gq)[0, 0]
+    assert deq[17] == 0.0 and deq[18] == g and deq[32] == 6 * g and deq[48] == -6 * g
+    assert np.signbit(deq[30])  # -0 keeps its sign
+
+
+def test_nvfp4_zero_tensor_and_zero_block():
+    a = np.zeros((2, 4, 32), np.float32)
+    a[1, 0, :16] = 1.0; a[1, 2, 16:] = -0.0
+    codes, scales, g = oracle.nvfp4_quantize(a, W.DT_F32)
+    assert g[0] == 0.0 and not codes[0].any() and not scales[0].any()
+    assert g[1] == np.float32(1.0) / np.float32(2688.0)
+    assert not codes[1, 2].any() and not scales[1, 2].any()  # an all-zero block: scale 0, codes 0
+    # every element at amax: scale code 448 (0x7E), codes 6 (7); value 6 * 448 * g, g = fl(1 / 2688)
+    assert (scales[1, 0, 0] == 0x7E) and (_nvfp4_codes_of(codes[1, 0], 32)[:16] == 7).all()
+    assert (oracle.nvfp4_dequantize(codes, scales, g)[1, 0, :16] == 2688.0 * np.float64(g[1])).all()
+
+
+@pytest.mark.parametrize("dtype", [W.DT_F32, W.DT_BF16])
+def test_nvfp4_quantize_against_brute_force(dtype):
+    # g = amax_t / 2688 (fp32); per block d = (amax_b / 6) / g rounded to the nearest E4M3 value
+    # (ties even); elements: the E2M1 value nearest to v / (sd * g) (fp32 product and quotient)
+    rng = np.random.default_rng(70)
+    T, R, K = 3, 16, 64
+    a = rng.standard_normal((T, R, K)) * np.exp(rng.uniform(-6, 6, (T, R, 1)))
+    a[0, 3, :16] = 0.0
+    a[1] *= 1e-3
+    a = to_dtype_bits(a.astype(np.float32), dtype)
+    v = f32_of(a).astype(np.float32)
+    codes, scales, g = oracle.nvfp4_quantize(a, dtype)
+    amax_t = np.abs(v).reshape(T, -1).max(axis=1)
+    assert np.array_equal(g, (amax_t / np.float32(2688.0)).astype(np.float32))
+    e4 = np.array([oracle.e4m3_value(c) for c in range(127)])
+    blk = v.reshape(T, R, K // 16, 16)
+    amax_b = np.abs(blk).max(axis=3)
+    d = ((amax_b / np.float32(6.0)).astype(np.float32) / g[:, None, None]).astype(np.float32)
+    dist = np.abs(e4[None, :] - d.reshape(-1, 1).astype(np.float64))
+    q = scales.reshape(-1).astype(np.int64)
+    assert np.array_equal(dist[np.arange(len(q)), q], dist.min(axis=1))
+    tie = (dist == dist.min(axis=1)[:, None]).sum(axis=1) > 1
+    assert (q[tie] % 2 == 0).all()
+    sd = e4[q].reshape(T, R, K // 16).astype(np.float32)
+    den = (sd * g[:, None, None]).astype(np.float32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        x = np.where(den[..., None] > 0, blk / np.where(den > 0, den, 1)[..., None], 0).astype(np.float32)
+    c = _nvfp4_codes_of(codes, K).reshape(T, R, K // 16, 16)
+    dd = np.abs(_E2M1[None, :] - np.abs(x).reshape(-1, 1).astype(np.float64))
+    mag = (c & 7).reshape(-1)
+    assert np.array_equal(dd[np.arange(len(mag)), mag], dd.min(axis=1))
+    tie = (dd == dd.min(axis=1)[:, None]).sum(axis=1) > 1
+    assert (mag[tie] % 2 == 0).all()
+    nz = (den > 0)[..., None].repeat(16, axis=-1).reshape(-1)
+    assert (c.reshape(-1)[~nz] == 0).all() and (~nz).any()
+    assert np.array_equal((c.reshape(-1)[nz] & 8) != 0, np.signbit(x.reshape(-1)[nz]))
+    deq = oracle.nvfp4_dequantize(codes, scales, g)
+    sgn = np.where((c & 8) != 0, -1.0, 1.0)
+    want = sgn * _E2M1[c & 7] * sd[..., None].astype(np.float64) * g[:, None, None, None].astype(np.float64)
+    assert np.array_equal(deq, want.reshape(T, R, K))
+
+
+def _nvfp4_representable(rng, shape, lg):
+    """Values whose NVFP4 quantisation is exact, per tensor of the leading dimension: g = 2^lg,
+    16-blocks of E2M1 values times an E4M3 scale sd, each block holding +-6 sd (so d = sd
+    exactly), and the tensor's first block sd = 448 (so g = amax_t / 2688)."""
+    T, R, K = shape
+    pool = np.concatenate([_E2M1, -_E2M1[1:]])
+    v = rng.choice(pool, size=(T, R, K // 16, 16))
+    v[..., 0] = rng.choice([6.0, -6.0], size=v.shape[:-1])
+    sd = rng.choice([0.25, 0.375, 0.5, 0.75, 1.0, 1.25, 1.875, 2.0, 3.5, 8.0], size=(T, R, K // 16, 1))
+    sd[:, 0, 0, 0] = 448.0
+    return (v * sd * 2.0 ** lg).reshape(shape)
+
+
+def test_nvfp4_ffn_matches_torch_and_the_bf16_ffn():
+    # W4A16: the weights' exact values against bf16 tokens; where those values are themselves
+    # bf16 numbers the FFN must be the bf16 expert FFN's, and both match a torch fp64 reference
+    rng = np.random.default_rng(71)
+    E, C, M, H = 2, 3, 64, 96
+    W1 = _nvfp4_representable(rng, (E, H, M), -12)
+    W2 = _nvfp4_representable(rng, (E, M, H), -11)
+    W1q = oracle.nvfp4_quantize(W1.astype(np.float32), W.DT_F32)
+    W2q = oracle.nvfp4_quantize(W2.astype(np.float32), W.DT_F32)
+    assert np.array_equal(oracle.nvfp4_dequantize(*W1q), W1) and np.array_equal(oracle.nvfp4_dequantize(*W2q), W2)
+    x = bf16_bits_of_f32(rng.standard_normal((E * C, M)).astype(np.float32))
+    b1 = bf16_bits_of_f32(rng.standard_normal((E, H)).astype(np.float32))
+    b2 = bf16_bits_of_f32(rng.standard_normal((E, M)).astype(np.float32))
+    rows = np.arange(E * C)
+    pre, h, y = oracle.expert_rows_nvfp4(x, W1q, b1, W2q, b2, rows, C, W.ACT_GELU)
+    W1b, W2b = bf16_bits_of_f32(W1.astype(np.float32)), bf16_bits_of_f32(W2.astype(np.float32))
+    assert np.array_equal(f32_of(W1b).astype(np.float64), W1)
+    ref = oracle.expert_rows(x, W1b, b1, W2b, b2, rows, C, W.ACT_GELU, W.DT_BF16, want_pre=True, want_h=True)
+    assert np.array_equal(pre, ref[0]) and np.array_equal(h, ref[1]) and np.array_equal(y, ref[2])
+    for r in rows:
+        e = r // C
+        p64 = torch.from_numpy(f32_of(x[r]).astype(np.float64)) @ torch.from_numpy(W1[e]).T \
+            + torch.from_numpy(f32_of(b1[e]).astype(np.float64))
+        assert np.abs(f32_of(pre[r]) - p64.numpy()).max() <= 2 ** -8 * np.abs(p64.numpy()).max()
