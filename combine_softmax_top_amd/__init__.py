@@ -93,6 +93,7 @@ _SIGS = {
     "moe_expert_fc1_mx": [_SP, ctypes.c_int32] + [_P] * 10,
     "moe_expert_fc2_mx": [_SP, ctypes.c_int32] + [_P] * 9,
     "moe_blockfp8_quantize": [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, _P, _P, _P],
+    "moe_nvfp4_quantize": [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, _P, _P, _P, _P],
     "moe_encode_blockfp8": [_SP] + [_P] * 8,
     "moe_expert_ffn_blockfp8": [_SP] + [_P] * 14,
     "moe_layer_forward_blockfp8": [_SP] + [_P] * 24 + [ctypes.c_size_t, _P],
@@ -612,3 +613,31 @@ def layer_backward(shape: Shape, fw: Dict[str, torch.Tensor], dout, W1, W2, grad
                        dlogits=grads["dlogits"] if gate else None, dWg=grads["dWg"] if Wg is not None else None,
                        aux_loss=grads["aux_loss"] if gate else None, ws=fw["ws"] if gate else None, stream=stream)
     return grads
+
+
+# ---------------------------------------------------------------- NVFP4 experts (weights)
+
+NVFP4_BLOCK = 16  # values per E4M3-scaled block along the reduction dimension
+
+
+def moe_nvfp4_quantize(src, ntensor: int, codes, scales, g, dtype: int = None, stream=None) -> None:
+    """NVFP4-quantise ``src`` ([..., K], fp32 or bf16, K a multiple of 16) as ntensor tensors of
+    consecutive rows into codes (uint8 [rows, K/2]), scales (uint8 E4M3 [rows, K/16]) and g (fp32
+    [ntensor])."""
+    K = src.shape[-1]
+    rows = src.numel() // K if K else 0
+    if dtype is None:
+        dtype = MOE_DT_F32 if src.dtype == torch.float32 else MOE_DT_BF16
+    _check(_lib.moe_nvfp4_quantize(rows, K, ntensor, dtype, _ptr(src), _ptr(codes), _ptr(scales), _ptr(g),
+                                   _stream(stream)))
+
+
+def nvfp4_quantize_weights(W):
+    """(codes [E, N, K/2], scales [E, N, K/16], g [E]) of expert weights W [E, N, K], one tensor
+    (one fp32 scale) per expert."""
+    E, N, K = W.shape
+    codes = torch.empty(E, N, K // 2, dtype=torch.uint8, device=W.device)
+    scales = torch.empty(E, N, K // NVFP4_BLOCK, dtype=torch.uint8, device=W.device)
+    g = torch.empty(E, dtype=torch.float32, device=W.device)
+    moe_nvfp4_quantize(W, E, codes, scales, g)
+    return codes, scales, g

@@ -463,6 +463,20 @@ moe_status moe_blockfp8_quantize(int64_t rows, int32_t K, int32_t brows, int32_t
     return e == hipSuccess ? MOE_OK : hip_fail(e, "block-FP8 quantisation");
 }
 
+moe_status moe_nvfp4_quantize(int64_t rows, int32_t K, int32_t ntensor, int32_t dtype, const void *src, void *codes,
+                              void *scales, float *g, void *stream) {
+    MOE_REQUIRE(dtype == MOE_DT_F32 || dtype == MOE_DT_BF16, "unknown dtype %d", dtype);
+    MOE_REQUIRE(rows >= 0 && K > 0 && K % 16 == 0, "rows must be >= 0 and K a positive multiple of 16");
+    MOE_REQUIRE(ntensor >= 1 && ntensor <= 65535 && rows % ntensor == 0,
+                "ntensor must be in [1, 65535] and divide rows=%lld", (long long)rows);
+    MOE_REQUIRE(rows * (K / 16) < (int64_t(1) << 40), "matrix too large");
+    if (rows > 0) MOE_REQUIRE(src && codes && scales && g, "src, codes, scales and g must be non-NULL");
+    MOE_REQUIRE_ALIGNED(src, codes, scales, g);
+    hipError_t e = moe::launch_nvfp4_quantize(rows, K, ntensor, dtype, src, static_cast<uint8_t *>(codes),
+                                              static_cast<uint8_t *>(scales), g, as_stream(stream));
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "NVFP4 quantisation");
+}
+
 moe_status moe_encode_blockfp8(const moe_shape *shape, const void *x, const int32_t *idx, const int32_t *loc,
                                const int32_t *fill, const int32_t *capacity, void *buf_codes, float *buf_scales,
                                void *stream) {

@@ -254,6 +254,9 @@ hipError_t launch_encode_mx(const moe_shape &s, const void *x, const int32_t *id
 // 1 x 128 blocks. The FFN launchers below take wfmt = kBlkFp8 for this scheme (scales fp32).
 hipError_t launch_blk_quantize(int brows, int64_t rows, int32_t K, int dtype, const void *src, uint8_t *codes,
                                float *scales, hipStream_t st);
+// NVFP4 weights: rows / ntensor rows per tensor, K a multiple of 16; g [ntensor].
+hipError_t launch_nvfp4_quantize(int64_t rows, int32_t K, int32_t ntensor, int dtype, const void *src,
+                                 uint8_t *codes, uint8_t *scales, float *g, hipStream_t st);
 hipError_t launch_encode_blk(const moe_shape &s, const void *x, const int32_t *idx, const int32_t *loc,
                              const int32_t *fill, const int32_t *cap, uint8_t *buf_codes, float *buf_scales,
                              int32_t cmax, hipStream_t st);

@@ -7,6 +7,8 @@
 // even; E2M1 by comparison with the rounding midpoints). Block-wise FP8: sixteen
 // lanes take a 1 x 128 block, a workgroup a 128 x 128 one, and the values are
 // divided by the block's fp32 scale before the same E4M3 conversion.
+// NVFP4 (weights only): a workgroup per tensor finds its amax, then two lanes per
+// 16-value block round the block scale to E4M3 and the values to E2M1.
 #include "moe_internal.h"
 
 namespace moe {
@@ -207,6 +209,63 @@ __global__ __launch_bounds__(kThreads) void blk_quantize_tiles_kernel(const void
     }
 }
 
+// NVFP4 weights: E2M1 codes in 16-value blocks along K with E4M3 block scales and one
+// fp32 scale g per tensor (rows / ntensor consecutive rows). g = amax / 2688 needs the
+// whole tensor's amax first: one workgroup per tensor (offline weight preparation).
+__global__ __launch_bounds__(kThreads) void nvfp4_amax_kernel(const void *__restrict__ src, int dtype,
+                                                              int64_t per_elems, float *__restrict__ g) {
+    __shared__ float wmax[kThreads / 64];
+    const int64_t base = static_cast<int64_t>(blockIdx.x) * per_elems;
+    float amax = 0.f;
+    for (int64_t i = static_cast<int64_t>(threadIdx.x) * 8; i < per_elems; i += kThreads * 8) {
+        float f[8];
+        load8(src, dtype, base + i, f);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(f[j]));
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+    if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = amax;
+    __syncthreads();
+    if (threadIdx.x == 0) g[blockIdx.x] = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3])) / 2688.f;
+}
+
+// Two lanes per 16-value block, eight values each: d = (amax_b / 6) / g rounded to the
+// E4M3 code q (the hardware conversion: nearest even, clamped to 448), then each value
+// divided by the fp32 product e4m3(q) * g and rounded to E2M1 (codes 0 when that
+// product is 0, as for an all-zero tensor).
+__global__ __launch_bounds__(kThreads) void nvfp4_quantize_kernel(const void *__restrict__ src, int dtype,
+                                                                  int64_t rows, int32_t K, int64_t per,
+                                                                  const float *__restrict__ g,
+                                                                  uint8_t *__restrict__ codes,
+                                                                  uint8_t *__restrict__ scales) {
+    const int KB = K / 16;
+    const int64_t nblk = rows * KB;
+    const int sub = threadIdx.x & 1;
+    for (int64_t b = (static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x) / 2; b < nblk;
+         b += static_cast<int64_t>(gridDim.x) * (kThreads / 2)) {
+        const int64_t r = b / KB;
+        const int64_t at = b * 16 + sub * 8;  // = r * K + (b - r * KB) * 16 + sub * 8
+        float f[8];
+        load8(src, dtype, at, f);
+        float amax = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+        amax = fmaxf(amax, __shfl_xor(amax, 1, 2));
+        const float gt = g[r / per];
+        uint32_t q = 0u;
+        if (gt > 0.f) q = mx_fp8x2((amax / 6.f) / gt, 0.f) & 0xFFu;
+        const float den = __builtin_amdgcn_cvt_f32_fp8(static_cast<int>(q), 0) * gt;
+        uint32_t c = 0u;
+        if (den > 0.f) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) c |= mx_fp4(f[i] / den) << (4 * i);
+        }
+        *reinterpret_cast<uint32_t *>(codes + at / 2) = c;
+        if (sub == 0) scales[b] = static_cast<uint8_t>(q);
+    }
+}
+
 // One wavefront per token, as encode_mx_kernel: the row is quantised once in 1 x 128 blocks
 // (four per pass of 512 values) and its codes and scales go to every kept slot; then the
 // padding rows of every expert get codes 0 and scale 0.
@@ -288,6 +347,16 @@ hipError_t launch_blk_quantize(int brows, int64_t rows, int32_t K, int dtype, co
         hipLaunchKernelGGL(blk_quantize_tiles_kernel, dim3(grid), dim3(kThreads), 0, st, src, dtype, rows, K, codes,
                            scales);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_nvfp4_quantize(int64_t rows, int32_t K, int32_t ntensor, int dtype, const void *src,
+                                 uint8_t *codes, uint8_t *scales, float *g, hipStream_t st) {
+    if (rows == 0) return hipSuccess;
+    const int64_t per = rows / ntensor;
+    hipLaunchKernelGGL(nvfp4_amax_kernel, dim3(ntensor), dim3(kThreads), 0, st, src, dtype, per * K, g);
+    hipLaunchKernelGGL(nvfp4_quantize_kernel, dim3(grid_blocks(rows * (K / 16) * 2)), dim3(kThreads), 0, st, src,
+                       dtype, rows, K, per, g, codes, scales);
     return hipGetLastError();
 }
 

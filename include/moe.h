@@ -319,6 +319,31 @@ moe_status moe_layer_forward_blockfp8(const moe_shape *shape, const void *x, con
                                       float *h_scales, void *y, void *out, void *ws, size_t ws_bytes,
                                       void *stream);
 
+/* NVFP4 experts (Tutel catalogue page: the low-precision inference formats,
+ * NVFP4 among them, listed for A100/A800/H100/MI300 hardware). NVFP4 is named,
+ * not defined, there; the reading is NVIDIA's two-level 4-bit format: E2M1
+ * elements (values 0, 0.5, 1, 1.5, 2, 3, 4, 6 and their negatives) in blocks of
+ * 16 consecutive values along the reduction dimension, each block with an E4M3
+ * scale, and one fp32 scale g per tensor (here one expert's weight matrix). None
+ * of the listed GPUs multiplies 4-bit values, so the format is read as
+ * weight-only: the experts' weights are stored NVFP4 and multiplied at their
+ * exact values by bf16 tokens. Element c of a block with scale code q in a
+ * tensor of scale g stands for e2m1(c) * e4m3(q) * g.
+ *
+ * moe_nvfp4_quantize: a row-major [rows, K] matrix of dtype (fp32 or bf16), K a
+ * multiple of 16, taken as ntensor tensors of rows / ntensor consecutive rows
+ * (the experts' weights: W1 [E*H, M] or W2 [E*M, H] with ntensor = E). Per
+ * tensor, in fp32 arithmetic: g = amax / 2688 (448 * 6); per block of 16 values
+ * d = (amax_b / 6) / g, q = the E4M3 code nearest d (ties to the even code,
+ * saturating at 448); each value v -> the E2M1 code nearest v / (e4m3(q) * g)
+ * (that product rounded to fp32, then the division; ties to the even code,
+ * saturating at 6; the sign bit v's); codes 0 where e4m3(q) * g is 0. Outputs:
+ * codes [rows, K/2] bytes (two per byte, the even index in the low nibble),
+ * scales [rows, K/16] E4M3 bytes, g [ntensor] fp32. Two launches (the tensors'
+ * amax first). */
+moe_status moe_nvfp4_quantize(int64_t rows, int32_t K, int32_t ntensor, int32_t dtype, const void *src, void *codes,
+                              void *scales, float *g, void *stream);
+
 /* Residual-MoE (MoE training blog, part 1 section 1.2, the residual half of
  * PR-MoE): every token also passes through one fixed dense MLP, and its output
  * is added to the MoE output. The dense branch has the experts' form with its

@@ -833,8 +833,8 @@ void oracle_expert_rows_blockfp8(int32_t M, int32_t H, int32_t C, int act, const
  *     sd = e4m3(q);  each element: c = the E2M1 code nearest v / (sd * g) (the
  *     product rounded to fp32, then the division), ties to the even code,
  *     saturating at 6, the sign bit the input's;
- *   g == 0 (an all-zero tensor) or sd == 0: the block's scale code and element
- *   codes are 0.
+ *   g == 0 (an all-zero tensor): scale codes 0; a block whose sd * g is 0 in fp32
+ *   (sd == 0, or an underflowing product): element codes 0.
  * Element c of a block with scale code q in a tensor of scale g stands for
  * e2m1(c) * e4m3(q) * g. Layout: codes [rows, K/2] (two per byte, the even index
  * in the low nibble), scales [rows, K/16] E4M3 bytes, g [ntensor] fp32. */
@@ -858,8 +858,8 @@ static void nvfp4_quantize_tensor(const float *v, int64_t rows, int32_t K, uint8
             scales[r * (K / 16) + b] = (uint8_t)q;
             for (int i = 0; i < 16; ++i) {
                 int c = 0;
-                if (sd > 0.0f) {
-                    const float den = sd * g;
+                const float den = sd * g;
+                if (den > 0.0f) {
                     const float x = blk[i] / den;
                     c = nearest_code(fabs((double)x), 1) | (signbit(x) ? 0x8 : 0);
                 }

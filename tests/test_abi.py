@@ -32,7 +32,7 @@ def odd_ptr():
 
 def test_every_declared_symbol_is_exported(moe):
     names = _declared()
-    assert len(names) == 41, names
+    assert len(names) == 42, names
     lib = ctypes.CDLL(moe.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -136,6 +136,13 @@ def test_entry_points_reject_before_enqueueing(moe):
     st = lib.moe_residual_backward(ctypes.byref(c), fake, fake, fake, fake, fake, fake, fake, fake, fake, None, fake,
                                    None, fake, 1, None)
     assert st == moe.MOE_EWORKSPACE
+    # NVFP4 quantisation: K a multiple of 16, ntensor dividing rows, 16-byte aligned buffers
+    st = lib.moe_nvfp4_quantize(64, 24, 1, moe.MOE_DT_BF16, fake, fake, fake, fake, None)
+    assert st == moe.MOE_EINVAL and "16" in moe.moe_last_error()
+    st = lib.moe_nvfp4_quantize(64, 32, 3, moe.MOE_DT_BF16, fake, fake, fake, fake, None)
+    assert st == moe.MOE_EINVAL and "ntensor" in moe.moe_last_error()
+    st = lib.moe_nvfp4_quantize(64, 32, 2, moe.MOE_DT_BF16, fake, fake, odd_ptr(), fake, None)
+    assert st == moe.MOE_EINVAL and "aligned" in moe.moe_last_error()
     other = ctypes.c_void_p(0x2000)
     res = [fake, fake, fake, fake, fake, other, fake, None, fake, None]  # W1r .. db2r (dx_r distinct from dx)
     st = lib.moe_residual_layer_backward(ctypes.byref(c), *full[:21], None, None, 0.0, fake, None, None, None, None,
