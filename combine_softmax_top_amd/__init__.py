@@ -94,6 +94,10 @@ _SIGS = {
     "moe_expert_fc2_mx": [_SP, ctypes.c_int32] + [_P] * 9,
     "moe_blockfp8_quantize": [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, _P, _P, _P],
     "moe_nvfp4_quantize": [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, _P, _P, _P, _P],
+    "moe_expert_ffn_nvfp4": [_SP] + [_P] * 15,
+    "moe_expert_fc1_nvfp4": [_SP] + [_P] * 10,
+    "moe_expert_fc2_nvfp4": [_SP] + [_P] * 9,
+    "moe_layer_forward_nvfp4": [_SP] + [_P] * 24 + [ctypes.c_size_t, _P],
     "moe_encode_blockfp8": [_SP] + [_P] * 8,
     "moe_expert_ffn_blockfp8": [_SP] + [_P] * 14,
     "moe_layer_forward_blockfp8": [_SP] + [_P] * 24 + [ctypes.c_size_t, _P],
@@ -641,3 +645,35 @@ def nvfp4_quantize_weights(W):
     g = torch.empty(E, dtype=torch.float32, device=W.device)
     moe_nvfp4_quantize(W, E, codes, scales, g)
     return codes, scales, g
+
+
+def moe_expert_ffn_nvfp4(shape: Shape, buf, W1q, b1, W2q, b2, fill, capacity, pre, h, y, stream=None) -> None:
+    """Expert FFN with NVFP4 weights W1q, W2q = (codes, scales, g) from nvfp4_quantize_weights."""
+    _check(_lib.moe_expert_ffn_nvfp4(ctypes.byref(shape.c()), _ptr(buf), _ptr(W1q[0]), _ptr(W1q[1]), _ptr(W1q[2]),
+                                     _ptr(b1), _ptr(W2q[0]), _ptr(W2q[1]), _ptr(W2q[2]), _ptr(b2), _ptr(fill),
+                                     _ptr(capacity), _ptr(pre), _ptr(h), _ptr(y), _stream(stream)))
+
+
+def moe_expert_fc1_nvfp4(shape: Shape, buf, W1q, b1, fill, capacity, pre, h, stream=None) -> None:
+    _check(_lib.moe_expert_fc1_nvfp4(ctypes.byref(shape.c()), _ptr(buf), _ptr(W1q[0]), _ptr(W1q[1]), _ptr(W1q[2]),
+                                     _ptr(b1), _ptr(fill), _ptr(capacity), _ptr(pre), _ptr(h), _stream(stream)))
+
+
+def moe_expert_fc2_nvfp4(shape: Shape, h, W2q, b2, fill, capacity, y, stream=None) -> None:
+    _check(_lib.moe_expert_fc2_nvfp4(ctypes.byref(shape.c()), _ptr(h), _ptr(W2q[0]), _ptr(W2q[1]), _ptr(W2q[2]),
+                                     _ptr(b2), _ptr(fill), _ptr(capacity), _ptr(y), _stream(stream)))
+
+
+def layer_forward_nvfp4(shape: Shape, x, W1q, b1, W2q, b2, logits=None, Wg=None, bufs=None, stream=None):
+    """The fused forward (inference) with NVFP4 experts into ``bufs`` (alloc_forward's, allocated
+    if None)."""
+    if bufs is None:
+        bufs = alloc_forward(shape, x.device, gate_projection=Wg is not None)
+    lo = bufs["logits"] if Wg is not None else None
+    _check(_lib.moe_layer_forward_nvfp4(
+        ctypes.byref(shape.c()), _ptr(x), _ptr(logits), _ptr(Wg), _ptr(lo), _ptr(W1q[0]), _ptr(W1q[1]), _ptr(W1q[2]),
+        _ptr(b1), _ptr(W2q[0]), _ptr(W2q[1]), _ptr(W2q[2]), _ptr(b2), _ptr(bufs["idx"]), _ptr(bufs["loc"]),
+        _ptr(bufs["gates"]), _ptr(bufs["needed"]), _ptr(bufs["fill"]), _ptr(bufs["capacity"]),
+        _ptr(bufs["slot_route"]), _ptr(bufs["buf"]), _ptr(bufs["h"]), _ptr(bufs["y"]), _ptr(bufs["out"]),
+        *_ws_args(bufs["ws"]), _stream(stream)))
+    return bufs

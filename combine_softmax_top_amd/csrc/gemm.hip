@@ -36,6 +36,8 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int BM = 128, BN = 128, BK = 64, NT = 256;
 constexpr int kTileElems = 128 * BK;  // one operand tile, bf16 elements
@@ -456,6 +458,45 @@ __device__ __forceinline__ void slice_schedule() {
     __builtin_amdgcn_sched_group_barrier(0x008, MF - FR, 0);
 }
 
+// The same order for FR fragment reads (LDS instructions) and MF MFMAs in any ratio:
+// pairs while both last, then the rest of either.
+template <int FR, int MF>
+__device__ __forceinline__ void slice_schedule_n() {
+    constexpr int P = FR < MF ? FR : MF;
+#pragma unroll
+    for (int f = 0; f < P; ++f) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    if constexpr (MF > P) __builtin_amdgcn_sched_group_barrier(0x008, MF - P, 0);
+    if constexpr (FR > P) __builtin_amdgcn_sched_group_barrier(0x100, FR - P, 0);
+}
+
+// NVFP4 weights in the bf16 kernel: eight E2M1 codes (one dword, element i in nibble
+// i) of a 16-value block with E4M3 scale byte sb -> their exact values as bf16 (an
+// E2M1 value has two significant bits and an E4M3 scale four, so each product is a
+// bf16 number). The codes' magnitudes index a byte table of the E4M3 encodings of
+// 0, 0.5, 1, 1.5, 2, 3, 4, 6 (v_perm_b32 picks four bytes at once), the sign bits
+// move to bit 7, and the hardware's E4M3 -> fp32 conversion gives the values.
+__device__ __forceinline__ bf16x8 nvfp4_expand(uint32_t w, uint32_t sb) {
+    constexpr uint32_t kLo = 0x3C383000u, kHi = 0x4C484440u;  // E4M3 of 0, .5, 1, 1.5 | 2, 3, 4, 6
+    const float s = __builtin_amdgcn_cvt_f32_fp8(static_cast<int>(sb), 0);
+    const uint32_t even = __builtin_amdgcn_perm(kHi, kLo, w & 0x07070707u) | ((w & 0x08080808u) << 4);
+    const uint32_t odd = __builtin_amdgcn_perm(kHi, kLo, (w >> 4) & 0x07070707u) | (w & 0x80808080u);
+    const f32x2 e02 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(even), false);  // elements 0, 2
+    const f32x2 e46 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(even), true);   // 4, 6
+    const f32x2 e13 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(odd), false);   // 1, 3
+    const f32x2 e57 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(odd), true);    // 5, 7
+    const f32x2 p0 = {e02[0] * s, e13[0] * s}, p1 = {e02[1] * s, e13[1] * s};
+    const f32x2 p2 = {e46[0] * s, e57[0] * s}, p3 = {e46[1] * s, e57[1] * s};
+    const bf16x2 b0 = __builtin_convertvector(p0, bf16x2), b1 = __builtin_convertvector(p1, bf16x2);
+    const bf16x2 b2 = __builtin_convertvector(p2, bf16x2), b3 = __builtin_convertvector(p3, bf16x2);
+    return bf16x8{b0[0], b0[1], b1[0], b1[1], b2[0], b2[1], b3[0], b3[1]};
+}
+
+// Bytes per weight row of an NVFP4 ring stage (64 k): 32 of codes, then 4 E4M3 scales.
+constexpr int kNvRowCodes = 32, kNvRowBytes = 36;
+
 __device__ __forceinline__ void load4_bf16(const bf16_t *p, float *f) {
     const uint2 u = *reinterpret_cast<const uint2 *>(p);
     f[0] = __uint_as_float(u.x << 16);
@@ -467,8 +508,6 @@ __device__ __forceinline__ void store4_bf16(bf16_t *p, const float *f) {
     *reinterpret_cast<uint2 *>(p) = make_uint2(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]));
 }
 
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 // 16-byte chunk slot of chunk c of row r in the epilogue tile (CH chunks per
 // row, a power of two): XOR with the row spreads the 32 rows that one
@@ -486,9 +525,16 @@ constexpr int kBigPrefixBytes = ((kMaxE + 1) * 4 + 15) / 16 * 16;
 // LDS of the large-tile bf16 GEMM: the two ring stages only (its tile schedule
 // lives in registers and its bias is read from global memory), so a 192 x 128
 // tile (80 KiB) runs two workgroups per CU.
-template <int BM, int BN>
+// With NVFP4 weights (WQ) a stage holds the bf16 token tile and the weights' codes and
+// scales (kNvRowBytes per row); the bf16 epilogue tile then outgrows the ring.
+template <int BM, int BN, bool WQ = false>
 constexpr int big_lds_bytes() {
-    return 2 * (BM + BN) * kBigKB * 2;
+    if constexpr (!WQ) {
+        return 2 * (BM + BN) * kBigKB * 2;
+    } else {
+        constexpr int ring = 2 * (BM * kBigKB * 2 + BN * kNvRowBytes), epi = BM * BN * 2;
+        return ring > epi ? ring : epi;
+    }
 }
 
 // Tile schedule of a persistent rows-grouped GEMM. Expert e has
@@ -662,22 +708,33 @@ __device__ __forceinline__ void wave_decode_tile(int L, const int32_t *fill, int
 // them). Epilogues: fc1 (bias, optional pre-activation output, activation),
 // fc2 (bias), plain, and the activation gradient (D = acc * act'(aux), aux the
 // saved pre-activation, staged through LDS so that the product is rounded once).
-template <int BM, int BN, int NTH, int EPI, int ACT, bool BMN, int WR = 2>
-__global__ __launch_bounds__(NTH, (big_lds_bytes<BM, BN>() * 2 <= 160 * 1024 ? 2 : 1)) void rows_gemm_big(const bf16_t *__restrict__ A, const bf16_t *__restrict__ B,
+//
+// WQ: NVFP4 weights (B = their codes [E*N][K/2], Bsc the E4M3 block scales
+// [E*N][K/16], Bg the fp32 scale per expert). A stage's weight part is the rows'
+// 32 bytes of codes ([BN][32]) and then their 4 scale bytes ([BN][4]); each weight
+// fragment is one dword of codes and one scale byte, expanded to exact bf16 values
+// (nvfp4_expand) for the same bf16 MFMAs. The accumulators start at 0; the epilogue
+// multiplies them by the expert's g and then adds the bias.
+template <int BM, int BN, int NTH, int EPI, int ACT, bool BMN, int WR = 2, bool WQ = false>
+__global__ __launch_bounds__(NTH, (big_lds_bytes<BM, BN, WQ>() * 2 <= 160 * 1024 ? 2 : 1)) void rows_gemm_big(const bf16_t *__restrict__ A, const bf16_t *__restrict__ B,
                                                       bf16_t *__restrict__ D, int N, int K, int E,
                                                       const int32_t *__restrict__ fill,
                                                       const int32_t *__restrict__ cap,
                                                       const bf16_t *__restrict__ bias, bf16_t *__restrict__ pre_out,
-                                                      const bf16_t *__restrict__ aux, int s0, int s1) {
+                                                      const bf16_t *__restrict__ aux, int s0, int s1,
+                                                      const uint8_t *__restrict__ Bsc, const float *__restrict__ Bg) {
     extern __shared__ __align__(16) bf16_t lds[];
     constexpr int KB = kBigKB, S = KB / 16;
     // NW wavefronts in 2 rows x NW/2 columns, each owning a (BM/2) x (BN/(NW/2)) block
     constexpr int NW = NTH / 64, WGC = NW / WR;  // WR rows x WGC columns of wavefronts
     constexpr int TM = BM / (32 * WR), TN = BN / (32 * WGC);
     static_assert(TN >= 1 && BN % (32 * WGC) == 0, "wavefront columns must be whole 32-wide blocks");
-    constexpr int STAGE = (BM + BN) * KB;
-    constexpr int LPS = (BM + BN) * KB / 8 / NTH;  // direct-load instructions per stage per thread
-    static_assert(BM * BN <= 2 * STAGE, "the epilogue tile must fit in the ring");
+    static_assert(!WQ || (!BMN && EPI <= EPI_FC2 && BN % (32 * NW) == 0), "NVFP4 weights: forward products");
+    constexpr int STAGE = BM * KB + (WQ ? BN * kNvRowBytes / 2 : BN * KB);  // bf16 units
+    // direct-load instructions per stage per thread (NVFP4: the tokens' and the codes'; the
+    // wavefronts that load scale words issue one more, so waits on this count are conservative)
+    constexpr int LPS = WQ ? BM * KB / 8 / NTH + BN / (32 * NW) : (BM + BN) * KB / 8 / NTH;
+    static_assert(WQ || BM * BN <= 2 * STAGE, "the epilogue tile must fit in the ring");
     static_assert(BM * (BN / 8) % NTH == 0, "epilogue chunks must split evenly over the threads");
     const int nx = (N + BN - 1) / BN;
     const TileSched sc = wave_sched(fill, E, BM, nx, s0, s1);
@@ -697,9 +754,54 @@ __global__ __launch_bounds__(NTH, (big_lds_bytes<BM, BN>() * 2 <= 160 * 1024 ? 2
         const bf16_t *Ab = A + grow0 * K;
         const bf16_t *Bb = BMN ? B + static_cast<int64_t>(g) * K * N + col0
                                : B + static_cast<int64_t>(g) * N * K + static_cast<int64_t>(col0) * K;
+        const uint8_t *Bq = WQ ? reinterpret_cast<const uint8_t *>(B) + (static_cast<int64_t>(g) * N + col0) * (K / 2)
+                               : nullptr;
+        const uint8_t *Bsq = WQ ? Bsc + (static_cast<int64_t>(g) * N + col0) * (K / 16) : nullptr;
         auto load_b = [&](int k0, bf16_t *dst) {
-            if constexpr (BMN) dma_tile_mn<BN, KB, NW>(Bb, N, cols_valid, k0, dst, wave, lane);
-            else dma_tile<BN, KB, NW>(Bb, K, cols_valid, k0, dst, wave, lane);
+            if constexpr (WQ) {
+                // scale words first (BN / 64 wavefronts, a dword per row), then the codes: 32
+                // rows of 32 bytes per wavefront instruction; rows past the matrix clamped
+                uint8_t *dq = reinterpret_cast<uint8_t *>(dst);
+                if (wave < BN / 64) {
+                    const int row = min(wave * 64 + lane, cols_valid - 1);
+                    dma4(Bsq, static_cast<uint32_t>(row * (K / 16) + k0 / 16), dq + BN * kNvRowCodes + wave * 256);
+                }
+#pragma unroll
+                for (int j = 0; j < BN / (32 * NW); ++j) {
+                    const int rb = (j * NW + wave) * 32;
+                    const int row = min(rb + (lane >> 1), cols_valid - 1);
+                    dma16(Bq, static_cast<uint32_t>(row * (K / 2) + k0 / 2 + (lane & 1) * 16), dq + rb * kNvRowCodes);
+                }
+            } else if constexpr (BMN) {
+                dma_tile_mn<BN, KB, NW>(Bb, N, cols_valid, k0, dst, wave, lane);
+            } else {
+                dma_tile<BN, KB, NW>(Bb, K, cols_valid, k0, dst, wave, lane);
+            }
+        };
+        // one slice's fragments (and, NVFP4, the weights' expansion to bf16)
+        auto load_frags = [&](const bf16_t *st, int kk, bf16x8(&ax)[TM], bf16x8(&bx)[TN]) {
+            if constexpr (WQ) {
+                const int chunk = kk * 2 + (lane >> 5);
+#pragma unroll
+                for (int i = 0; i < TM; ++i) {
+                    const int row = wr0 + i * 32 + (lane & 31);
+                    ax[i] = *reinterpret_cast<const bf16x8 *>(st + row * KB + (swz_chunk<KB>(row, chunk) << 3));
+                }
+                const uint8_t *sq = reinterpret_cast<const uint8_t *>(st + BM * KB);
+#pragma unroll
+                for (int j = 0; j < TN; ++j) {
+                    const int col = wc0 + j * 32 + (lane & 31);
+                    const uint32_t w =
+                        *reinterpret_cast<const uint32_t *>(sq + col * kNvRowCodes + kk * 8 + 4 * (lane >> 5));
+                    bx[j] = nvfp4_expand(w, sq[BN * kNvRowCodes + col * 4 + kk]);
+                }
+            } else {
+                frag_load<TM, TN, KB, BMN, BN>(st, st + BM * KB, kk, ax, bx, wr0, wc0, lane);
+            }
+        };
+        auto schedule = [&]() {
+            if constexpr (WQ) slice_schedule_n<TM + 2 * TN, TM * TN>();
+            else slice_schedule<TM, TN>();
         };
 
         // Only the forward products have a bias: the accumulators start at it (read
@@ -711,7 +813,7 @@ __global__ __launch_bounds__(NTH, (big_lds_bytes<BM, BN>() * 2 <= 160 * 1024 ? 2
         // Tiles with 128 accumulators per lane at eight wavefronts (256 x 256) have
         // no registers to spare across the prologue and read it after the prologue.
         constexpr bool kBias = EPI <= EPI_FC2;
-        constexpr bool kEarlyBias = kBias && TM * TN * 16 < 128;
+        constexpr bool kEarlyBias = !WQ && kBias && TM * TN * 16 < 128;
         const bool with_bias = kBias && bias != nullptr;
         const bf16_t *bt = with_bias ? bias + static_cast<int64_t>(g) * N + col0 : nullptr;
         uint2 bq[kEarlyBias ? TN : 1][4];
@@ -764,7 +866,7 @@ __global__ __launch_bounds__(NTH, (big_lds_bytes<BM, BN>() * 2 <= 160 * 1024 ? 2
 #pragma unroll
                         for (int r = 0; r < 4; ++r) acc[i][j][4 * q + r] = b4[r];
                 }
-        } else if (kBias && with_bias) {
+        } else if (!WQ && kBias && with_bias) {
 #pragma unroll
             for (int j = 0; j < TN; ++j)
 #pragma unroll
@@ -778,15 +880,14 @@ __global__ __launch_bounds__(NTH, (big_lds_bytes<BM, BN>() * 2 <= 160 * 1024 ? 2
                 }
         }
         bf16x8 fa[2][TM], fb[2][TN];
-        frag_load<TM, TN, KB, BMN, BN>(lds, lds + BM * KB, 0, fa[0], fb[0], wr0, wc0, lane);
+        load_frags(lds, 0, fa[0], fb[0]);
         for (int t = 0; t < nk; ++t) {
             const bf16_t *scur = lds + (t & 1) * STAGE;
 #pragma unroll
             for (int kk = 0; kk < S - 1; ++kk) {
-                frag_load<TM, TN, KB, BMN, BN>(scur, scur + BM * KB, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1],
-                                               wr0, wc0, lane);
+                load_frags(scur, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
                 mfma_slice<TM, TN>(fa[kk & 1], fb[kk & 1], acc);
-                slice_schedule<TM, TN>();
+                schedule();
             }
             // At the last step this also runs, uniformly: there is no load to wait
             // for, and the fragments read from the other buffer are not used.
@@ -798,9 +899,24 @@ __global__ __launch_bounds__(NTH, (big_lds_bytes<BM, BN>() * 2 <= 160 * 1024 ? 2
                 load_b((t + 2) * KB, sn + BM * KB);
             }
             const bf16_t *snext = lds + ((t + 1) & 1) * STAGE;
-            frag_load<TM, TN, KB, BMN, BN>(snext, snext + BM * KB, 0, fa[S & 1], fb[S & 1], wr0, wc0, lane);
+            load_frags(snext, 0, fa[S & 1], fb[S & 1]);
             mfma_slice<TM, TN>(fa[(S - 1) & 1], fb[(S - 1) & 1], acc);
-            slice_schedule<TM, TN>();
+            schedule();
+        }
+        if constexpr (WQ) {
+            // the expert's fp32 scale, then the bias: acc = g * acc + b
+            const float gs = Bg[g];
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    float b4[4] = {0.f, 0.f, 0.f, 0.f};
+                    if (with_bias) load4_bf16(bt + min(wc0 + j * 32 + 8 * q + 4 * (lane >> 5), cols_valid - 4), b4);
+#pragma unroll
+                    for (int i = 0; i < TM; ++i)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) acc[i][j][4 * q + r] = fmaf(acc[i][j][4 * q + r], gs, b4[r]);
+                }
         }
 
         // Epilogue through LDS. Per 32x32 block, lane l owns token row (l % 32)
@@ -1781,11 +1897,12 @@ static int resident_blocks(int per_cu) {
     return ((cus[dev] * per_cu + kXcds - 1) / kXcds) * kXcds;
 }
 
-template <int BM, int BN, int NTH, int EPI, bool BMN = false, int WR = 2>
+template <int BM, int BN, int NTH, int EPI, bool BMN = false, int WR = 2, bool WQ = false>
 hipError_t big_launch(int act, const void *A, const void *B, void *D, int N, int K, int E, const int32_t *fill,
                       const int32_t *cap, const void *bias, void *pre_out, hipStream_t st,
-                      const void *aux = nullptr, int s0 = 0, int s1 = 0x7FFFFFFF) {
-    constexpr int lds = big_lds_bytes<BM, BN>();
+                      const void *aux = nullptr, int s0 = 0, int s1 = 0x7FFFFFFF, const uint8_t *Bsc = nullptr,
+                      const float *Bg = nullptr) {
+    constexpr int lds = big_lds_bytes<BM, BN, WQ>();
     constexpr int per_cu = (160 * 1024) / lds >= 2 ? 2 : 1;  // the kernel's launch bounds match
     const dim3 grid(resident_blocks(per_cu));
     auto a = static_cast<const bf16_t *>(A);
@@ -1795,17 +1912,17 @@ hipError_t big_launch(int act, const void *A, const void *B, void *D, int N, int
     auto po = static_cast<bf16_t *>(pre_out);
     auto ax = static_cast<const bf16_t *>(aux);
     if (act == MOE_ACT_GELU) {
-        auto k = rows_gemm_big<BM, BN, NTH, EPI, MOE_ACT_GELU, BMN, WR>;
+        auto k = rows_gemm_big<BM, BN, NTH, EPI, MOE_ACT_GELU, BMN, WR, WQ>;
         static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(k),
                                                            hipFuncAttributeMaxDynamicSharedMemorySize, lds);
         if (attr != hipSuccess) return attr;
-        hipLaunchKernelGGL(k, grid, dim3(NTH), lds, st, a, b, d, N, K, E, fill, cap, bi, po, ax, s0, s1);
+        hipLaunchKernelGGL(k, grid, dim3(NTH), lds, st, a, b, d, N, K, E, fill, cap, bi, po, ax, s0, s1, Bsc, Bg);
     } else {
-        auto k = rows_gemm_big<BM, BN, NTH, EPI, MOE_ACT_RELU, BMN, WR>;
+        auto k = rows_gemm_big<BM, BN, NTH, EPI, MOE_ACT_RELU, BMN, WR, WQ>;
         static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(k),
                                                            hipFuncAttributeMaxDynamicSharedMemorySize, lds);
         if (attr != hipSuccess) return attr;
-        hipLaunchKernelGGL(k, grid, dim3(NTH), lds, st, a, b, d, N, K, E, fill, cap, bi, po, ax, s0, s1);
+        hipLaunchKernelGGL(k, grid, dim3(NTH), lds, st, a, b, d, N, K, E, fill, cap, bi, po, ax, s0, s1, Bsc, Bg);
     }
     return hipGetLastError();
 }
@@ -1891,6 +2008,33 @@ hipError_t fwd_launch(int act, const void *A, const void *B, void *D, int N, int
 
     default:
         return big_launch<128, 128, 256, EPI>(act, A, B, D, N, K, E, fill, cap, bias, pre_out, st, nullptr, s0, s1);
+    }
+}
+
+// Forward products with NVFP4 weights: the bf16 products' tile choice.
+template <int EPI>
+hipError_t fwd_launch_nvfp4(int act, const void *A, const uint8_t *Bcodes, const uint8_t *Bsc, const float *Bg,
+                            void *D, int N, int K, int64_t rows_hint, int E, const int32_t *fill, const int32_t *cap,
+                            const void *bias, void *pre_out, hipStream_t st) {
+    int cfg = gemm_cfg_override();
+    if (cfg < 1 || cfg > 5) cfg = default_cfg(N, K, rows_hint, E);
+    const int s0 = 0, s1 = 0x7FFFFFFF;
+    switch (cfg) {
+    case 1:
+        return big_launch<256, 256, 512, EPI, false, 2, true>(act, A, Bcodes, D, N, K, E, fill, cap, bias, pre_out, st,
+                                                              nullptr, s0, s1, Bsc, Bg);
+    case 2:
+        return big_launch<256, 128, 256, EPI, false, 2, true>(act, A, Bcodes, D, N, K, E, fill, cap, bias, pre_out, st,
+                                                              nullptr, s0, s1, Bsc, Bg);
+    case 4:
+        return big_launch<192, 256, 512, EPI, false, 2, true>(act, A, Bcodes, D, N, K, E, fill, cap, bias, pre_out, st,
+                                                              nullptr, s0, s1, Bsc, Bg);
+    case 5:
+        return big_launch<192, 128, 256, EPI, false, 2, true>(act, A, Bcodes, D, N, K, E, fill, cap, bias, pre_out, st,
+                                                              nullptr, s0, s1, Bsc, Bg);
+    default:
+        return big_launch<128, 128, 256, EPI, false, 2, true>(act, A, Bcodes, D, N, K, E, fill, cap, bias, pre_out, st,
+                                                              nullptr, s0, s1, Bsc, Bg);
     }
 }
 
@@ -1984,6 +2128,20 @@ hipError_t launch_fc2(const moe_shape &s, const void *h, const void *W2, const v
     b.N = M; b.K = H; b.kgrouped = 0; b.fill = fill; b.cap = cap;
     b.bias = static_cast<const float *>(b2);
     return simt_launch<EPI_FC2>(b, s.act, cmax, E, st);
+}
+
+hipError_t launch_fc1_nvfp4(const moe_shape &s, const void *buf, const uint8_t *w1_codes, const uint8_t *w1_scales,
+                            const float *w1_g, const void *b1, const int32_t *fill, const int32_t *cap, void *pre,
+                            void *h, int32_t cmax, hipStream_t st) {
+    return fwd_launch_nvfp4<EPI_FC1>(s.act, buf, w1_codes, w1_scales, w1_g, h, s.H, s.M, rows_hint(s, cmax), s.E, fill,
+                                     cap, b1, pre, st);
+}
+
+hipError_t launch_fc2_nvfp4(const moe_shape &s, const void *h, const uint8_t *w2_codes, const uint8_t *w2_scales,
+                            const float *w2_g, const void *b2, const int32_t *fill, const int32_t *cap, void *y,
+                            int32_t cmax, hipStream_t st) {
+    return fwd_launch_nvfp4<EPI_FC2>(s.act, h, w2_codes, w2_scales, w2_g, y, s.M, s.H, rows_hint(s, cmax), s.E, fill,
+                                     cap, b2, nullptr, st);
 }
 
 template <int BM, int BN, int NTH, int EPI, int WFMT, bool BLK = false>

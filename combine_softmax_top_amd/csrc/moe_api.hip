@@ -188,6 +188,68 @@ moe_status moe_expert_ffn(const moe_shape *shape, const void *buf, const void *W
     return e == hipSuccess ? MOE_OK : hip_fail(e, "expert fc2");
 }
 
+static moe_status check_nvfp4_ffn(const moe_shape &s) {
+    if (s.dtype != MOE_DT_BF16) return fail(MOE_EUNSUPPORTED, "NVFP4 experts take bf16 tokens");
+    return MOE_OK;
+}
+
+moe_status moe_expert_ffn_nvfp4(const moe_shape *shape, const void *buf, const void *W1_codes, const void *W1_scales,
+                                const float *W1_g, const void *b1, const void *W2_codes, const void *W2_scales,
+                                const float *W2_g, const void *b2, const int32_t *fill, const int32_t *capacity,
+                                void *pre, void *h, void *y, void *stream) {
+    moe_status st = check_shape(shape);
+    if (st != MOE_OK) return st;
+    const moe_shape &s = *shape;
+    if ((st = check_nvfp4_ffn(s)) != MOE_OK) return st;
+    MOE_REQUIRE(buf && W1_codes && W1_scales && W1_g && W2_codes && W2_scales && W2_g && fill && capacity && h && y,
+                "buf, the weights' codes, scales and g, fill, capacity, h and y must be non-NULL");
+    MOE_REQUIRE((b1 != nullptr) == (s.has_fc1_bias != 0), "b1 must be given iff has_fc1_bias");
+    MOE_REQUIRE((b2 != nullptr) == (s.has_fc2_bias != 0), "b2 must be given iff has_fc2_bias");
+    MOE_REQUIRE_ALIGNED(buf, W1_codes, W1_scales, W1_g, b1, W2_codes, W2_scales, W2_g, b2, fill, capacity, pre, h, y);
+    const int32_t cmax = static_cast<int32_t>(cap_bound(s));
+    hipError_t e = moe::launch_fc1_nvfp4(s, buf, static_cast<const uint8_t *>(W1_codes),
+                                         static_cast<const uint8_t *>(W1_scales), W1_g, b1, fill, capacity, pre, h,
+                                         cmax, as_stream(stream));
+    if (e != hipSuccess) return hip_fail(e, "expert fc1 (NVFP4)");
+    e = moe::launch_fc2_nvfp4(s, h, static_cast<const uint8_t *>(W2_codes), static_cast<const uint8_t *>(W2_scales),
+                              W2_g, b2, fill, capacity, y, cmax, as_stream(stream));
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "expert fc2 (NVFP4)");
+}
+
+moe_status moe_expert_fc1_nvfp4(const moe_shape *shape, const void *buf, const void *W1_codes, const void *W1_scales,
+                                const float *W1_g, const void *b1, const int32_t *fill, const int32_t *capacity,
+                                void *pre, void *h, void *stream) {
+    moe_status st = check_shape(shape);
+    if (st != MOE_OK) return st;
+    const moe_shape &s = *shape;
+    if ((st = check_nvfp4_ffn(s)) != MOE_OK) return st;
+    MOE_REQUIRE(buf && W1_codes && W1_scales && W1_g && fill && capacity && h,
+                "buf, W1's codes, scales and g, fill, capacity and h must be non-NULL");
+    MOE_REQUIRE((b1 != nullptr) == (s.has_fc1_bias != 0), "b1 must be given iff has_fc1_bias");
+    MOE_REQUIRE_ALIGNED(buf, W1_codes, W1_scales, W1_g, b1, fill, capacity, pre, h);
+    hipError_t e = moe::launch_fc1_nvfp4(s, buf, static_cast<const uint8_t *>(W1_codes),
+                                         static_cast<const uint8_t *>(W1_scales), W1_g, b1, fill, capacity, pre, h,
+                                         static_cast<int32_t>(cap_bound(s)), as_stream(stream));
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "expert fc1 (NVFP4)");
+}
+
+moe_status moe_expert_fc2_nvfp4(const moe_shape *shape, const void *h, const void *W2_codes, const void *W2_scales,
+                                const float *W2_g, const void *b2, const int32_t *fill, const int32_t *capacity,
+                                void *y, void *stream) {
+    moe_status st = check_shape(shape);
+    if (st != MOE_OK) return st;
+    const moe_shape &s = *shape;
+    if ((st = check_nvfp4_ffn(s)) != MOE_OK) return st;
+    MOE_REQUIRE(h && W2_codes && W2_scales && W2_g && fill && capacity && y,
+                "h, W2's codes, scales and g, fill, capacity and y must be non-NULL");
+    MOE_REQUIRE((b2 != nullptr) == (s.has_fc2_bias != 0), "b2 must be given iff has_fc2_bias");
+    MOE_REQUIRE_ALIGNED(h, W2_codes, W2_scales, W2_g, b2, fill, capacity, y);
+    hipError_t e = moe::launch_fc2_nvfp4(s, h, static_cast<const uint8_t *>(W2_codes),
+                                         static_cast<const uint8_t *>(W2_scales), W2_g, b2, fill, capacity, y,
+                                         static_cast<int32_t>(cap_bound(s)), as_stream(stream));
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "expert fc2 (NVFP4)");
+}
+
 moe_status moe_expert_ffn_window(const moe_shape *shape, const void *buf, const void *W1, const void *b1,
                                  const void *W2, const void *b2, const int32_t *fill, const int32_t *capacity,
                                  int32_t slot_begin, int32_t slot_end, void *pre, void *h, void *y, void *stream) {
@@ -641,15 +703,28 @@ struct Residual {
     const void *W1r, *b1r, *W2r, *b2r;
     void *pre_r, *h_r, *y_r;
 };
+// NVFP4 experts: the weights' block scales and fp32 scales (W1 and W2 are their codes).
+struct Nvfp4Scales {
+    const void *W1s;
+    const float *W1g;
+    const void *W2s;
+    const float *W2g;
+};
 
 moe_status layer_forward_impl(const moe_shape *shape, const void *x, const float *logits_in, const float *Wg,
                               float *logits_out, const void *W1, const void *b1, const void *W2, const void *b2,
                               int32_t *idx, int32_t *loc, float *gates, int32_t *needed, int32_t *fill,
                               int32_t *capacity, int32_t *slot_route, void *buf, void *pre, void *h, void *y,
-                              void *out, void *ws, size_t ws_bytes, const Residual *res, void *stream) {
+                              void *out, void *ws, size_t ws_bytes, const Residual *res, void *stream,
+                              const Nvfp4Scales *nv = nullptr) {
     moe_status st = check_shape(shape);
     if (st != MOE_OK) return st;
     const moe_shape &s = *shape;
+    if (nv != nullptr) {
+        if (s.dtype != MOE_DT_BF16) return fail(MOE_EUNSUPPORTED, "NVFP4 experts take bf16 tokens");
+        MOE_REQUIRE(nv->W1s && nv->W1g && nv->W2s && nv->W2g, "the weights' scales and g must be non-NULL");
+        MOE_REQUIRE_ALIGNED(nv->W1s, nv->W1g, nv->W2s, nv->W2g);
+    }
     // with no token, empty logits may arrive as NULL
     MOE_REQUIRE(!(logits_in != nullptr && Wg != nullptr), "exactly one of logits_in and Wg must be given");
     MOE_REQUIRE(s.S == 0 || logits_in != nullptr || Wg != nullptr, "exactly one of logits_in and Wg must be given");
@@ -687,10 +762,19 @@ moe_status layer_forward_impl(const moe_shape *shape, const void *x, const float
     if ((e = moe::launch_assign_encode(s, x, idx, w, needed, by_factor(s), loc, fill, capacity, slot_route, buf, cmax,
                                        strm)) != hipSuccess)
         return hip_fail(e, "route assignment and encode");
-    if ((e = moe::launch_fc1(s, buf, W1, b1, fill, capacity, pre, h, cmax, strm)) != hipSuccess)
-        return hip_fail(e, "expert fc1");
-    if ((e = moe::launch_fc2(s, h, W2, b2, fill, capacity, y, cmax, strm)) != hipSuccess)
-        return hip_fail(e, "expert fc2");
+    if (nv != nullptr) {
+        e = moe::launch_fc1_nvfp4(s, buf, static_cast<const uint8_t *>(W1), static_cast<const uint8_t *>(nv->W1s),
+                                  nv->W1g, b1, fill, capacity, pre, h, cmax, strm);
+        if (e != hipSuccess) return hip_fail(e, "expert fc1 (NVFP4)");
+        e = moe::launch_fc2_nvfp4(s, h, static_cast<const uint8_t *>(W2), static_cast<const uint8_t *>(nv->W2s),
+                                  nv->W2g, b2, fill, capacity, y, cmax, strm);
+        if (e != hipSuccess) return hip_fail(e, "expert fc2 (NVFP4)");
+    } else {
+        if ((e = moe::launch_fc1(s, buf, W1, b1, fill, capacity, pre, h, cmax, strm)) != hipSuccess)
+            return hip_fail(e, "expert fc1");
+        if ((e = moe::launch_fc2(s, h, W2, b2, fill, capacity, y, cmax, strm)) != hipSuccess)
+            return hip_fail(e, "expert fc2");
+    }
     // the dense branch uses the workspace after routing is done with it
     if (res != nullptr &&
         (e = moe::launch_residual_ffn(s, x, res->W1r, res->b1r, res->W2r, res->b2r, res->pre_r, res->h_r, res->y_r,
@@ -713,6 +797,18 @@ moe_status moe_layer_forward(const moe_shape *shape, const void *x, const float 
                              void *out, void *ws, size_t ws_bytes, void *stream) {
     return layer_forward_impl(shape, x, logits_in, Wg, logits_out, W1, b1, W2, b2, idx, loc, gates, needed, fill,
                               capacity, slot_route, buf, pre, h, y, out, ws, ws_bytes, nullptr, stream);
+}
+
+moe_status moe_layer_forward_nvfp4(const moe_shape *shape, const void *x, const float *logits_in, const float *Wg,
+                                   float *logits_out, const void *W1_codes, const void *W1_scales, const float *W1_g,
+                                   const void *b1, const void *W2_codes, const void *W2_scales, const float *W2_g,
+                                   const void *b2, int32_t *idx, int32_t *loc, float *gates, int32_t *needed,
+                                   int32_t *fill, int32_t *capacity, int32_t *slot_route, void *buf, void *h, void *y,
+                                   void *out, void *ws, size_t ws_bytes, void *stream) {
+    const Nvfp4Scales nv{W1_scales, W1_g, W2_scales, W2_g};
+    return layer_forward_impl(shape, x, logits_in, Wg, logits_out, W1_codes, b1, W2_codes, b2, idx, loc, gates,
+                              needed, fill, capacity, slot_route, buf, nullptr, h, y, out, ws, ws_bytes, nullptr,
+                              stream, &nv);
 }
 
 moe_status moe_layer_forward_pipelined(const moe_shape *shape, const void *x, const float *logits_in,

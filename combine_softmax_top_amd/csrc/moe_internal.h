@@ -254,6 +254,14 @@ hipError_t launch_encode_mx(const moe_shape &s, const void *x, const int32_t *id
 // 1 x 128 blocks. The FFN launchers below take wfmt = kBlkFp8 for this scheme (scales fp32).
 hipError_t launch_blk_quantize(int brows, int64_t rows, int32_t K, int dtype, const void *src, uint8_t *codes,
                                float *scales, hipStream_t st);
+// Expert fc1 / fc2 with NVFP4 weights (codes [E*N][K/2], E4M3 block scales [E*N][K/16],
+// fp32 g [E]) and bf16 tokens: the bf16 products' definitions on the weights' values.
+hipError_t launch_fc1_nvfp4(const moe_shape &s, const void *buf, const uint8_t *w1_codes, const uint8_t *w1_scales,
+                            const float *w1_g, const void *b1, const int32_t *fill, const int32_t *cap, void *pre,
+                            void *h, int32_t cmax, hipStream_t st);
+hipError_t launch_fc2_nvfp4(const moe_shape &s, const void *h, const uint8_t *w2_codes, const uint8_t *w2_scales,
+                            const float *w2_g, const void *b2, const int32_t *fill, const int32_t *cap, void *y,
+                            int32_t cmax, hipStream_t st);
 // NVFP4 weights: rows / ntensor rows per tensor, K a multiple of 16; g [ntensor].
 hipError_t launch_nvfp4_quantize(int64_t rows, int32_t K, int32_t ntensor, int dtype, const void *src,
                                  uint8_t *codes, uint8_t *scales, float *g, hipStream_t st);

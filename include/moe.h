@@ -344,6 +344,42 @@ moe_status moe_layer_forward_blockfp8(const moe_shape *shape, const void *x, con
 moe_status moe_nvfp4_quantize(int64_t rows, int32_t K, int32_t ntensor, int32_t dtype, const void *src, void *codes,
                               void *scales, float *g, void *stream);
 
+/* Expert FFN with NVFP4 weights and bf16 tokens, for the filled rows
+ * j < fill[e] (padding rows are not written), the bf16 FFN's definitions on
+ * the weights' values w = e2m1(c) * e4m3(q) * g:
+ *   pre = buf . W1[e]^T + b1[e]   (fp32 accumulation), stored bf16 if pre != NULL
+ *   h   = act(pre), stored bf16 [E*cmax, H]
+ *   y   = h . W2[e]^T + b2[e]     (fp32 accumulation), stored bf16 [E*cmax, M]
+ * W1 from moe_nvfp4_quantize of [E*H, M] with ntensor = E (codes [E*H, M/2],
+ * scales [E*H, M/16], g [E]), W2 likewise of [E*M, H]; b1 [E, H], b2 [E, M]
+ * bf16 (NULL iff the bias is off). Each weight value is a bf16 number, so the
+ * products are exact and the sums run in fp32 as in the bf16 FFN; the expert's
+ * g multiplies the fp32 sum before the bias is added. dtype must be bf16. */
+moe_status moe_expert_ffn_nvfp4(const moe_shape *shape, const void *buf, const void *W1_codes, const void *W1_scales,
+                                const float *W1_g, const void *b1, const void *W2_codes, const void *W2_scales,
+                                const float *W2_g, const void *b2, const int32_t *fill, const int32_t *capacity,
+                                void *pre, void *h, void *y, void *stream);
+
+/* The two halves of moe_expert_ffn_nvfp4 (same definitions and row rules):
+ *   moe_expert_fc1_nvfp4: pre (optional), h = act(buf . W1[e]^T + b1[e])
+ *   moe_expert_fc2_nvfp4: y = h . W2[e]^T + b2[e]                     */
+moe_status moe_expert_fc1_nvfp4(const moe_shape *shape, const void *buf, const void *W1_codes, const void *W1_scales,
+                                const float *W1_g, const void *b1, const int32_t *fill, const int32_t *capacity,
+                                void *pre, void *h, void *stream);
+moe_status moe_expert_fc2_nvfp4(const moe_shape *shape, const void *h, const void *W2_codes, const void *W2_scales,
+                                const float *W2_g, const void *b2, const int32_t *fill, const int32_t *capacity,
+                                void *y, void *stream);
+
+/* The whole forward (inference) with NVFP4 experts: [gate projection] -> route
+ * -> encode -> moe_expert_ffn_nvfp4 -> moe_decode, arguments as in
+ * moe_layer_forward (no pre-activation output) with the weights as above. */
+moe_status moe_layer_forward_nvfp4(const moe_shape *shape, const void *x, const float *logits_in, const float *Wg,
+                                   float *logits_out, const void *W1_codes, const void *W1_scales, const float *W1_g,
+                                   const void *b1, const void *W2_codes, const void *W2_scales, const float *W2_g,
+                                   const void *b2, int32_t *idx, int32_t *loc, float *gates, int32_t *needed,
+                                   int32_t *fill, int32_t *capacity, int32_t *slot_route, void *buf, void *h, void *y,
+                                   void *out, void *ws, size_t ws_bytes, void *stream);
+
 /* Residual-MoE (MoE training blog, part 1 section 1.2, the residual half of
  * PR-MoE): every token also passes through one fixed dense MLP, and its output
  * is added to the MoE output. The dense branch has the experts' form with its

@@ -32,7 +32,7 @@ def odd_ptr():
 
 def test_every_declared_symbol_is_exported(moe):
     names = _declared()
-    assert len(names) == 42, names
+    assert len(names) == 46, names
     lib = ctypes.CDLL(moe.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -136,6 +136,15 @@ def test_entry_points_reject_before_enqueueing(moe):
     st = lib.moe_residual_backward(ctypes.byref(c), fake, fake, fake, fake, fake, fake, fake, fake, fake, None, fake,
                                    None, fake, 1, None)
     assert st == moe.MOE_EWORKSPACE
+    # NVFP4 experts take bf16 tokens and every weight part
+    c32 = moe.Shape(S=64, M=64, E=4, k=2, H=64, capacity_factor=1.0, dtype=moe.MOE_DT_F32).c()
+    st = lib.moe_expert_ffn_nvfp4(ctypes.byref(c32), *([fake] * 14), None)
+    assert st == moe.MOE_EUNSUPPORTED and "bf16" in moe.moe_last_error()
+    st = lib.moe_expert_fc1_nvfp4(ctypes.byref(c), fake, fake, None, fake, fake, fake, fake, None, fake, None)
+    assert st == moe.MOE_EINVAL and "W1" in moe.moe_last_error()
+    st = lib.moe_layer_forward_nvfp4(ctypes.byref(c), fake, fake, None, None, fake, fake, None, *([fake] * 17),
+                                     1 << 20, None)
+    assert st == moe.MOE_EINVAL and "scales" in moe.moe_last_error()
     # NVFP4 quantisation: K a multiple of 16, ntensor dividing rows, 16-byte aligned buffers
     st = lib.moe_nvfp4_quantize(64, 24, 1, moe.MOE_DT_BF16, fake, fake, fake, fake, None)
     assert st == moe.MOE_EINVAL and "16" in moe.moe_last_error()
