@@ -126,6 +126,12 @@ def copy_calibration(mib):
     print(json.dumps(dict(copy_bytes_read=a.numel() * 4, copy_bytes_written=a.numel() * 4, launches=3)))
 
 
+def fp8_tokens(w):
+    """Whether the workload's experts quantise the tokens and run 8-bit products (MX, block FP8);
+    NVFP4 experts are weight-only, on bf16 products."""
+    return w.mx in ("mxfp8", "mxfp4", "blockfp8")
+
+
 def algorithmic(w, C, kept):
     """Bytes (or flops) each stage must move (or compute), per launch, and its bound."""
     b = w.elem_bytes
@@ -134,7 +140,7 @@ def algorithmic(w, C, kept):
     st = {
         "route": ("bytes", 4 * S * E + 12 * k * S + 4 * kept + 8 * E),
         # MX encode writes one code byte per value plus a scale byte per 32 (block FP8: 4 bytes per 128)
-        "encode": ("bytes", S * M * b + (E * C * M * 33 // 32 if w.mx else E * C * M * b) + 8 * k * S),
+        "encode": ("bytes", S * M * b + (E * C * M * 33 // 32 if fp8_tokens(w) else E * C * M * b) + 8 * k * S),
         "fc1": ("flops", prod),
         "fc2": ("flops", prod),
         "decode": ("bytes", kept * M * b + S * M * b + 12 * k * S + (S * M * b if w.residual else 0)),
@@ -232,6 +238,13 @@ def cpu_baseline(w, inp, budget_s):
 
         def ffn(rs):
             return None, oracle.expert_rows_blockfp8(bufq, W1q, ni.get("b1"), W2q, ni.get("b2"), rs, C, w.act)[1]
+    elif w.mx == "nvfp4":
+        W1q = oracle.nvfp4_quantize(ni["W1"], w.dtype)
+        W2q = oracle.nvfp4_quantize(ni["W2"], w.dtype)
+
+        def ffn(rs):
+            _, h, y = oracle.expert_rows_nvfp4(buf, W1q, ni.get("b1"), W2q, ni.get("b2"), rs, C, w.act)
+            return h, y
     elif w.mx:
         wf = oracle.MX_FP8 if w.mx == "mxfp8" else oracle.MX_FP4
         t0 = time.perf_counter()
@@ -362,12 +375,15 @@ def main():
     gate = w.logits == "gate"
     mxf = {"mxfp8": moe.MOE_MX_FP8, "mxfp4": moe.MOE_MX_FP4}.get(w.mx)
     blk = w.mx == "blockfp8"
+    nv = w.mx == "nvfp4"
 
     def alloc_lowp():
+        if nv:
+            return moe.alloc_forward(s, dev, gate_projection=gate)
         return (moe.alloc_forward_blockfp8(s, dev, gate_projection=gate) if blk else
                 moe.alloc_forward_mx(s, dev, gate_projection=gate))
 
-    if mxf is not None or blk:
+    if mxf is not None or blk or nv:
         bufs = alloc_lowp()
     else:
         bufs = moe.alloc_forward(s, dev, training=w.backward, gate_projection=gate, residual=w.residual)
@@ -385,10 +401,14 @@ def main():
     def backward():
         moe.layer_backward(s, bufs, inp["dout"], W1, W2, grads=grads, logits=logits_bwd, x=x, Wg=Wg, residual=res)
 
-    if mxf is not None or blk:
+    if mxf is not None or blk or nv:
         # low-precision experts: the weights are quantised once, outside the timed region (offline)
-        W1q = moe.blockfp8_quantize_weights(W1) if blk else moe.mx_quantize_weights(W1, mxf)
-        W2q = moe.blockfp8_quantize_weights(W2) if blk else moe.mx_quantize_weights(W2, mxf)
+        if nv:
+            W1q, W2q = moe.nvfp4_quantize_weights(W1), moe.nvfp4_quantize_weights(W2)
+        elif blk:
+            W1q, W2q = moe.blockfp8_quantize_weights(W1), moe.blockfp8_quantize_weights(W2)
+        else:
+            W1q, W2q = moe.mx_quantize_weights(W1, mxf), moe.mx_quantize_weights(W2, mxf)
         torch.cuda.synchronize()
 
     pipe = args.pipeline_chunks > 0
@@ -412,6 +432,9 @@ def main():
         i = counter[0] % nb if multi else 0
         counter[0] += 1
         b, st = bsets[i], bstreams[i] if multi else None
+        if nv:
+            moe.layer_forward_nvfp4(s, x, W1q, b1, W2q, b2, logits=logits_in, Wg=Wg, bufs=b, stream=st)
+            return
         if blk:
             moe.layer_forward_blockfp8(s, x, W1q, b1, W2q, b2, logits=logits_in, Wg=Wg, bufs=b, stream=st)
             return
@@ -481,7 +504,13 @@ def main():
         stage_fns.append(("gate", lambda: moe.moe_gate_project(s, x, Wg, lg)))
     stage_fns.append(("route", lambda: moe.moe_route(s, lg, b["idx"], b["loc"], b["gates"], b["needed"], b["fill"],
                                                      b["capacity"], b["slot_route"], b["ws"])))
-    if blk:
+    if nv:
+        stage_fns += [
+            ("encode", lambda: moe.moe_encode(s, x, b["idx"], b["loc"], b["fill"], b["capacity"], b["buf"])),
+            ("fc1", lambda: moe.moe_expert_fc1_nvfp4(s, b["buf"], W1q, b1, b["fill"], b["capacity"], None, b["h"])),
+            ("fc2", lambda: moe.moe_expert_fc2_nvfp4(s, b["h"], W2q, b2, b["fill"], b["capacity"], b["y"])),
+        ]
+    elif blk:
         stage_fns += [
             ("encode", lambda: moe.moe_encode_blockfp8(s, x, b["idx"], b["loc"], b["fill"], b["capacity"],
                                                        b["buf_codes"], b["buf_scales"])),
@@ -599,7 +628,7 @@ def main():
             reps = 3 * n
         else:
             ms = batch(fn, reps) / reps
-        r = roofline_of(kind, amount, ms, w.dtype == W.DT_BF16, mx=bool(w.mx) and name in ("fc1", "fc2"))
+        r = roofline_of(kind, amount, ms, w.dtype == W.DT_BF16, mx=fp8_tokens(w) and name in ("fc1", "fc2"))
         r["ms"] = round(ms, 5)
         r["launches"] = reps
         r["timing"] = "after a 512 MiB fill each, per-launch events" if flushed else "back-to-back batch"

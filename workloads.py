@@ -58,7 +58,8 @@ class Workload:
     backward: bool = False
     residual: bool = False  # Residual-MoE: a dense MLP branch added to the MoE output
     mx: str = ""  # "mxfp8" / "mxfp4": experts with MX-quantised weights (tokens and h in MXFP8);
-    #               "blockfp8": block-wise FP8 experts (weights, tokens and h)
+    #               "blockfp8": block-wise FP8 experts (weights, tokens and h);
+    #               "nvfp4": NVFP4 weights only (tokens and h bf16)
 
     def replace(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
@@ -100,11 +101,14 @@ DSPR_MXFP8 = Workload("dspr_mxfp8_S8192_M2048_E16_k3_H8192", S=8192, M=2048, E=1
 # ... and with block-wise FP8 experts (fp32 scales per 128 x 128 weight block, 1 x 128 token block)
 GATED_BLOCKFP8 = GATED_BF16.replace(name="gated_blockfp8_S4096_M1024_E8_k2_H4096", mx="blockfp8")
 DSPR_BLOCKFP8 = DSPR_MXFP8.replace(name="dspr_blockfp8_S8192_M2048_E16_k3_H8192", mx="blockfp8")
+# ... and with NVFP4 weights (weight-only: E2M1 in 16-value blocks with E4M3 scales, bf16 tokens)
+GATED_NVFP4 = GATED_BF16.replace(name="gated_nvfp4_S4096_M1024_E8_k2_H4096", mx="nvfp4")
+DSPR_NVFP4 = DSPR_MXFP8.replace(name="dspr_nvfp4_S8192_M2048_E16_k3_H8192", mx="nvfp4")
 
 WORKLOADS = [TINY_F32, GATED_BF16, GATED_TRAIN_BF16, RESIDUAL_BF16, RESIDUAL_TRAIN_BF16, DSPR_BF16, FINE_BF16,
              LARGE_BF16]
 # MX workloads are measured by bench.py and checked by the MX parity tests
-MX_WORKLOADS = [GATED_MXFP8, GATED_MXFP4, DSPR_MXFP8, GATED_BLOCKFP8, DSPR_BLOCKFP8]
+MX_WORKLOADS = [GATED_MXFP8, GATED_MXFP4, DSPR_MXFP8, GATED_BLOCKFP8, DSPR_BLOCKFP8, GATED_NVFP4, DSPR_NVFP4]
 BY_NAME = {w.name: w for w in WORKLOADS + MX_WORKLOADS}
 
 
