@@ -188,3 +188,48 @@ def test_nvfp4_full_size_gated_layer():
     out_o = oracle.decode(y_full, rt, w.E, w.dtype, tokens=toks)
     eo = decode_extra(rt, rows, yg, y_o, tokens=toks)
     check_close(host(b["out"][torch.from_numpy(toks).cuda()]), out_o, w.dtype, "out (sampled tokens)", extra=eo)
+
+
+def test_layer_forward_nvfp4_empty_input():
+    # S = 0: every expert buffer row is padding (zeros) and nothing else is written
+    import combine_softmax_top_amd as moe
+    w = W.Workload("nv_empty", S=0, M=256, E=3, k=2, H=128, capacity_factor=1.0)
+    inp = W.make_inputs(w, seed=0)
+    s = shape_of(w)
+    d = {k_: v.cuda() for k_, v in inp.items()}
+    W1g = moe.nvfp4_quantize_weights(d["W1"])
+    W2g = moe.nvfp4_quantize_weights(d["W2"])
+    bufs = moe.alloc_forward(s)
+    bufs["buf"].fill_(7.0)
+    b = moe.layer_forward_nvfp4(s, d["x"], W1g, d.get("b1"), W2g, d.get("b2"), logits=d["logits"], bufs=bufs)
+    torch.cuda.synchronize()
+    assert int(b["capacity"].item()) == 1 and b["out"].numel() == 0
+    assert (host(b["buf"][:3]).view(np.uint16) == 0).all()
+
+
+def test_layer_forward_nvfp4_idle_experts():
+    # 16 experts for 24 top-1 tokens: most experts get no row, the others a partial tile
+    import combine_softmax_top_amd as moe
+    w = W.Workload("nv_idle_S24_M64_E16_k1_H128", S=24, M=64, E=16, k=1, H=128, capacity_factor=1.0)
+    print(f"[nvfp4 idle experts] {w.name}", flush=True)
+    inp = W.make_inputs(w, seed=3)
+    ni = inputs_np(inp)
+    s = shape_of(w)
+    d = {k_: v.cuda() for k_, v in inp.items()}
+    W1g = moe.nvfp4_quantize_weights(d["W1"])
+    W2g = moe.nvfp4_quantize_weights(d["W2"])
+    b = moe.layer_forward_nvfp4(s, d["x"], W1g, d.get("b1"), W2g, d.get("b2"), logits=d["logits"])
+    torch.cuda.synchronize()
+    _, rt, buf_o, W1q, W2q = _oracle_nv(w, ni)
+    assert (rt["fill"] == 0).sum() >= 4
+    C = rt["C"]
+    rows = oracle.filled_rows(rt)
+    _, h_o, y_o = oracle.expert_rows_nvfp4(buf_o, W1q, ni.get("b1"), W2q, ni.get("b2"), rows, C, w.act)
+    ridx = torch.from_numpy(rows).cuda()
+    check_close(host(b["h"][ridx]), h_o, w.dtype, "h")
+    yg = host(b["y"][ridx])
+    check_close(yg, y_o, w.dtype, "y")
+    y_full = np.zeros((w.E * C, w.M), np.uint16)
+    y_full[rows] = y_o
+    out_o = oracle.decode(y_full, rt, w.E, w.dtype)
+    check_close(host(b["out"]), out_o, w.dtype, "out", extra=decode_extra(rt, rows, yg, y_o))
