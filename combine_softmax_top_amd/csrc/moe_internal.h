@@ -166,6 +166,55 @@ hipError_t launch_gate_project(const moe_shape &s, const void *x, const float *W
                                hipStream_t st);
 // Whether the gate projection's LDS tiles fit for this model dim / expert count.
 bool gate_supported(int M, int E, int dtype);
+// Routing phase 2 inside the assignment launch of moe_route when the per-tile count
+// table is small (E * k * nblk <= kScanInBlock, 8 KiB): each of its few workgroups
+// (one per four routing tiles) reads the raw counts [E][k][nblk] and scans them itself,
+// which saves the scan's own launch (S = 4096, E = 8, k = 2: 13.2 -> 10.7 us). Not in
+// the fused forward's encode launch, whose many workgroups would each re-read the table
+// (measured: slower, and 15% slower at S = 8192, E = 16, k = 3).
+constexpr int kScanInBlock = 2048;
+inline bool scan_in_assign(int E, int k, int nblk) {
+    return static_cast<int64_t>(E) * k * nblk <= kScanInBlock;
+}
+// The scan: off[] (same layout as counts) gets each expert's exclusive prefix in (route,
+// tile) order, need[e] the expert's total. The table is first copied into off[] with
+// every thread's loads in flight together (the loads are independent; a loop-carried
+// scan over global memory would wait for one load latency per 64 counts), then one
+// wavefront per expert scans its counts in place, 64 a step.
+__device__ __forceinline__ void block_scan_counts(const int32_t *__restrict__ counts, int E, int L,
+                                                  int32_t *off, int32_t *need) {
+    const int T = E * L, nt = blockDim.x;
+    constexpr int U = 8;
+    for (int b = threadIdx.x; b < T; b += nt * U) {
+        int v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) v[u] = b + u * nt < T ? counts[b + u * nt] : 0;
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (b + u * nt < T) off[b + u * nt] = v[u];
+    }
+    __syncthreads();
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = nt >> 6;
+    for (int e = w; e < E; e += nw) {
+        int run = 0;
+        for (int b = 0; b < L; b += 64) {
+            const int i = e * L + b + lane;
+            const bool in = b + lane < L;
+            const int v = in ? off[i] : 0;
+            int inc = v;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const int t = __shfl_up(inc, o, 64);
+                if (lane >= o) inc += t;
+            }
+            if (in) off[i] = run + inc - v;
+            run += __shfl(inc, 63, 64);
+        }
+        if (lane == 0) need[e] = run;
+    }
+    __syncthreads();
+}
+
 // Capacity C from the per-expert route counts, in every thread of a 256-thread
 // block: mode +1 the factor's bound (cap_by_factor), 0 the largest count, -1 the
 // smaller of the two; at least 1. sh: 4 ints of LDS.
@@ -186,10 +235,11 @@ inline int capacity_mode(const moe_shape &s) {
     return s.capacity_factor > 0 ? 1 : (s.capacity_factor == 0 ? 0 : -1);
 }
 
-// Routing phases 1 and 2 only (top-k, gates, per-tile counts scanned to offsets,
-// needed); launch_assign_encode then places every route and encodes.
+// Routing phases 1 and 2 (top-k, gates, per-tile counts scanned to offsets, needed;
+// with scan = false phase 1 only, the counts left raw); launch_assign_encode then
+// places every route and encodes.
 hipError_t launch_route_counts(const moe_shape &s, const float *logits, int32_t *idx, float *gates,
-                               int32_t *needed, RouteWs ws, hipStream_t st);
+                               int32_t *needed, RouteWs ws, hipStream_t st, bool scan = true);
 // Phase 3 of routing fused with encode: loc, fill, capacity and slot_route as
 // launch_route's, and buf as launch_encode's, in one launch.
 hipError_t launch_assign_encode(const moe_shape &s, const void *x, const int32_t *idx, RouteWs ws,

@@ -20,7 +20,10 @@
 //                     workgroup derives from needed[] and capacity_factor.
 // The fused layer forward runs phase 3 inside the encode launch instead
 // (assign_encode_kernel: the same ranks and offsets, one wavefront per token),
-// so routing and encode there take three launches, not four.
+// so routing and encode there take three launches, not four. In moe_route, when
+// the count table is small (E * k * tiles <= kScanInBlock) phase 2 moves into
+// phase 3's launch: each of its workgroups scans the raw counts in LDS
+// (block_scan_counts), and routing takes two launches.
 #include "moe_internal.h"
 
 namespace moe {
@@ -172,17 +175,29 @@ __global__ __launch_bounds__(256) void route_scan_kernel(int32_t *__restrict__ c
 
 // Phase 3. Four (route rank, tile) wavefronts per block. mode: +1 fixed factor,
 // 0 max needed, -1 min(factor bound, max needed); cap_by_factor is
-// ceil(k*S*|f|/E) computed on the host.
+// ceil(k*S*|f|/E) computed on the host. SCAN: offsets holds phase 1's raw counts,
+// which every block scans in LDS (phase 2 folded in); block 0 writes needed.
+template <bool SCAN>
 __global__ __launch_bounds__(256) void route_assign_kernel(
-    const int32_t *__restrict__ idx, const int32_t *__restrict__ offsets, const int32_t *__restrict__ needed,
+    const int32_t *__restrict__ idx, const int32_t *__restrict__ offsets, int32_t *__restrict__ needed,
     int S, int E, int k, int nblk, int ebits, int mode, int64_t cap_by_factor, int32_t *__restrict__ loc,
     int32_t *__restrict__ fill, int32_t *__restrict__ cap_out, int32_t *__restrict__ slot_route) {
     __shared__ int sh[4];
+    extern __shared__ int32_t scan_lds[];  // SCAN: offsets [E*k*nblk], then needed [E]
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int C = block_capacity(needed, E, mode, cap_by_factor, sh);
+    const int32_t *offs = offsets, *need = needed;
+    if constexpr (SCAN) {
+        int32_t *o = scan_lds, *nd = scan_lds + E * k * nblk;
+        block_scan_counts(offsets, E, k * nblk, o, nd);
+        if (blockIdx.x == 0)
+            for (int e = tid; e < E; e += 256) needed[e] = nd[e];
+        offs = o;
+        need = nd;
+    }
+    const int C = block_capacity(need, E, mode, cap_by_factor, sh);
     if (blockIdx.x == 0) {
         if (tid == 0) cap_out[0] = C;
-        for (int e = tid; e < E; e += 256) fill[e] = min(needed[e], C);
+        for (int e = tid; e < E; e += 256) fill[e] = min(need[e], C);
     }
     const int w = blockIdx.x * 4 + wv;
     if (w >= k * nblk) return;
@@ -200,7 +215,7 @@ __global__ __launch_bounds__(256) void route_assign_kernel(
     const int rank = __popcll(same & below);
     if (active) {
         const int64_t q = static_cast<int64_t>(r) * S + s;
-        const int l = offsets[(static_cast<int64_t>(e) * k + r) * nblk + b] + rank;
+        const int l = offs[(static_cast<int64_t>(e) * k + r) * nblk + b] + rank;
         loc[q] = l;
         if (slot_route != nullptr && l < C) slot_route[static_cast<int64_t>(e) * C + l] = static_cast<int32_t>(q);
     }
@@ -216,7 +231,7 @@ static hipError_t launch_topk(const float *logits, int S, int E, int k, int nblk
 }
 
 hipError_t launch_route_counts(const moe_shape &s, const float *logits, int32_t *idx, float *gates,
-                               int32_t *needed, RouteWs ws, hipStream_t st) {
+                               int32_t *needed, RouteWs ws, hipStream_t st, bool scan) {
     const int S = s.S, E = s.E, k = s.k, nblk = ws.nblk;
     hipError_t err = hipSuccess;
     if (nblk > 0) {
@@ -242,7 +257,7 @@ hipError_t launch_route_counts(const moe_shape &s, const float *logits, int32_t 
         if (err != hipSuccess) return err;
     }
     const int L = k * nblk;
-    hipLaunchKernelGGL(route_scan_kernel, dim3(E), dim3(256), 0, st, ws.counts, L, needed);
+    if (scan) hipLaunchKernelGGL(route_scan_kernel, dim3(E), dim3(256), 0, st, ws.counts, L, needed);
     return hipGetLastError();
 }
 
@@ -250,15 +265,22 @@ hipError_t launch_route(const moe_shape &s, const float *logits, int32_t *idx, i
                         int32_t *needed, int32_t *fill, int32_t *cap, int32_t *slot_route, RouteWs ws,
                         int64_t cap_by_factor, hipStream_t st) {
     const int S = s.S, E = s.E, k = s.k, nblk = ws.nblk;
-    hipError_t err = launch_route_counts(s, logits, idx, gates, needed, ws, st);
+    const bool fold = scan_in_assign(E, k, nblk);  // the assignment scans the counts itself
+    hipError_t err = launch_route_counts(s, logits, idx, gates, needed, ws, st, !fold);
     if (err != hipSuccess) return err;
     const int L = k * nblk;
     int ebits = 0;
     while ((1 << ebits) < E) ++ebits;
     const int mode = capacity_mode(s);
     const int blocks = L > 0 ? (L + 3) / 4 : 1;
-    hipLaunchKernelGGL(route_assign_kernel, dim3(blocks), dim3(256), 0, st, idx, ws.counts, needed, S, E, k, nblk,
-                       ebits, mode, cap_by_factor, loc, fill, cap, slot_route);
+    if (fold) {
+        const size_t lds = sizeof(int32_t) * (static_cast<size_t>(E) * L + E);
+        hipLaunchKernelGGL(route_assign_kernel<true>, dim3(blocks), dim3(256), lds, st, idx, ws.counts, needed, S, E,
+                           k, nblk, ebits, mode, cap_by_factor, loc, fill, cap, slot_route);
+    } else {
+        hipLaunchKernelGGL(route_assign_kernel<false>, dim3(blocks), dim3(256), 0, st, idx, ws.counts, needed, S, E,
+                           k, nblk, ebits, mode, cap_by_factor, loc, fill, cap, slot_route);
+    }
     return hipGetLastError();
 }
 
