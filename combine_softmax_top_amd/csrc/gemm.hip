@@ -525,16 +525,11 @@ constexpr int kBigPrefixBytes = ((kMaxE + 1) * 4 + 15) / 16 * 16;
 // LDS of the large-tile bf16 GEMM: the two ring stages only (its tile schedule
 // lives in registers and its bias is read from global memory), so a 192 x 128
 // tile (80 KiB) runs two workgroups per CU.
-// With NVFP4 weights (WQ) a stage holds the bf16 token tile and the weights' codes and
-// scales (kNvRowBytes per row); the bf16 epilogue tile then outgrows the ring.
+// With NVFP4 weights (WQ) the ring is followed by two slots of the weights' codes and
+// scales (kNvRowBytes per row), which the ring's bf16 weight tiles are expanded from.
 template <int BM, int BN, bool WQ = false>
 constexpr int big_lds_bytes() {
-    if constexpr (!WQ) {
-        return 2 * (BM + BN) * kBigKB * 2;
-    } else {
-        constexpr int ring = 2 * (BM * kBigKB * 2 + BN * kNvRowBytes), epi = BM * BN * 2;
-        return ring > epi ? ring : epi;
-    }
+    return 2 * (BM + BN) * kBigKB * 2 + (WQ ? 2 * BN * kNvRowBytes : 0);
 }
 
 // Tile schedule of a persistent rows-grouped GEMM. Expert e has
@@ -710,11 +705,16 @@ __device__ __forceinline__ void wave_decode_tile(int L, const int32_t *fill, int
 // saved pre-activation, staged through LDS so that the product is rounded once).
 //
 // WQ: NVFP4 weights (B = their codes [E*N][K/2], Bsc the E4M3 block scales
-// [E*N][K/16], Bg the fp32 scale per expert). A stage's weight part is the rows'
-// 32 bytes of codes ([BN][32]) and then their 4 scale bytes ([BN][4]); each weight
-// fragment is one dword of codes and one scale byte, expanded to exact bf16 values
-// (nvfp4_expand) for the same bf16 MFMAs. The accumulators start at 0; the epilogue
-// multiplies them by the expert's g and then adds the bias.
+// [E*N][K/16], Bg the fp32 scale per expert). The direct loads bring a stage's
+// codes ([BN][32] bytes, then the scales [BN][4]) into one of two slots behind the
+// ring, one stage earlier than its tokens; the workgroup expands them once
+// (nvfp4_expand: a dword of codes and its block's scale byte -> one 16-byte chunk of
+// exact bf16 values) into the ring's weight tile, in the layout the bf16 loads give,
+// one chunk per thread per slice: stage t+2's expansion starts after stage t's
+// barrier, in the buffer that barrier releases, and runs beside stage t+1's MFMAs
+// until stage t+1's barrier publishes it. Fragments are then read as for bf16
+// weights. The accumulators start at 0; the epilogue multiplies them by the expert's
+// g and then adds the bias.
 template <int BM, int BN, int NTH, int EPI, int ACT, bool BMN, int WR = 2, bool WQ = false>
 __global__ __launch_bounds__(NTH, (big_lds_bytes<BM, BN, WQ>() * 2 <= 160 * 1024 ? 2 : 1)) void rows_gemm_big(const bf16_t *__restrict__ A, const bf16_t *__restrict__ B,
                                                       bf16_t *__restrict__ D, int N, int K, int E,
@@ -730,11 +730,11 @@ __global__ __launch_bounds__(NTH, (big_lds_bytes<BM, BN, WQ>() * 2 <= 160 * 1024
     constexpr int TM = BM / (32 * WR), TN = BN / (32 * WGC);
     static_assert(TN >= 1 && BN % (32 * WGC) == 0, "wavefront columns must be whole 32-wide blocks");
     static_assert(!WQ || (!BMN && EPI <= EPI_FC2 && BN % (32 * NW) == 0), "NVFP4 weights: forward products");
-    constexpr int STAGE = BM * KB + (WQ ? BN * kNvRowBytes / 2 : BN * KB);  // bf16 units
-    // direct-load instructions per stage per thread (NVFP4: the tokens' and the codes'; the
-    // wavefronts that load scale words issue one more, so waits on this count are conservative)
-    constexpr int LPS = WQ ? BM * KB / 8 / NTH + BN / (32 * NW) : (BM + BN) * KB / 8 / NTH;
-    static_assert(WQ || BM * BN <= 2 * STAGE, "the epilogue tile must fit in the ring");
+    constexpr int STAGE = (BM + BN) * KB;                // bf16 units
+    constexpr int LPS = (BM + BN) * KB / 8 / NTH;        // direct-load instructions per stage per thread
+    constexpr int SLOT = BN * kNvRowBytes;               // bytes of an NVFP4 code slot
+    static_assert(BM * BN <= 2 * STAGE, "the epilogue tile must fit in the ring");
+    static_assert(!WQ || BN * KB / 8 == S * NTH, "NVFP4: one weight chunk per thread per slice");
     static_assert(BM * (BN / 8) % NTH == 0, "epilogue chunks must split evenly over the threads");
     const int nx = (N + BN - 1) / BN;
     const TileSched sc = wave_sched(fill, E, BM, nx, s0, s1);
@@ -758,49 +758,42 @@ __global__ __launch_bounds__(NTH, (big_lds_bytes<BM, BN, WQ>() * 2 <= 160 * 1024
                                : nullptr;
         const uint8_t *Bsq = WQ ? Bsc + (static_cast<int64_t>(g) * N + col0) * (K / 16) : nullptr;
         auto load_b = [&](int k0, bf16_t *dst) {
-            if constexpr (WQ) {
-                // scale words first (BN / 64 wavefronts, a dword per row), then the codes: 32
-                // rows of 32 bytes per wavefront instruction; rows past the matrix clamped
-                uint8_t *dq = reinterpret_cast<uint8_t *>(dst);
-                if (wave < BN / 64) {
-                    const int row = min(wave * 64 + lane, cols_valid - 1);
-                    dma4(Bsq, static_cast<uint32_t>(row * (K / 16) + k0 / 16), dq + BN * kNvRowCodes + wave * 256);
-                }
-#pragma unroll
-                for (int j = 0; j < BN / (32 * NW); ++j) {
-                    const int rb = (j * NW + wave) * 32;
-                    const int row = min(rb + (lane >> 1), cols_valid - 1);
-                    dma16(Bq, static_cast<uint32_t>(row * (K / 2) + k0 / 2 + (lane & 1) * 16), dq + rb * kNvRowCodes);
-                }
-            } else if constexpr (BMN) {
+            if constexpr (BMN) {
                 dma_tile_mn<BN, KB, NW>(Bb, N, cols_valid, k0, dst, wave, lane);
             } else {
                 dma_tile<BN, KB, NW>(Bb, K, cols_valid, k0, dst, wave, lane);
             }
         };
-        // one slice's fragments (and, NVFP4, the weights' expansion to bf16)
-        auto load_frags = [&](const bf16_t *st, int kk, bf16x8(&ax)[TM], bf16x8(&bx)[TN]) {
-            if constexpr (WQ) {
-                const int chunk = kk * 2 + (lane >> 5);
+        uint8_t *const cslot = reinterpret_cast<uint8_t *>(lds + 2 * STAGE);
+        // NVFP4: a stage's codes into a slot: the scale words first (BN / 64 wavefronts,
+        // a dword per row), then the codes, 32 rows of 32 bytes per wavefront
+        // instruction; rows past the matrix clamped (their columns are never stored)
+        auto load_codes = [&](int k0, uint8_t *dq) {
+            if (wave < BN / 64) {
+                const int row = min(wave * 64 + lane, cols_valid - 1);
+                dma4(Bsq, static_cast<uint32_t>(row * (K / 16) + k0 / 16), dq + BN * kNvRowCodes + wave * 256);
+            }
 #pragma unroll
-                for (int i = 0; i < TM; ++i) {
-                    const int row = wr0 + i * 32 + (lane & 31);
-                    ax[i] = *reinterpret_cast<const bf16x8 *>(st + row * KB + (swz_chunk<KB>(row, chunk) << 3));
-                }
-                const uint8_t *sq = reinterpret_cast<const uint8_t *>(st + BM * KB);
-#pragma unroll
-                for (int j = 0; j < TN; ++j) {
-                    const int col = wc0 + j * 32 + (lane & 31);
-                    const uint32_t w =
-                        *reinterpret_cast<const uint32_t *>(sq + col * kNvRowCodes + kk * 8 + 4 * (lane >> 5));
-                    bx[j] = nvfp4_expand(w, sq[BN * kNvRowCodes + col * 4 + kk]);
-                }
-            } else {
-                frag_load<TM, TN, KB, BMN, BN>(st, st + BM * KB, kk, ax, bx, wr0, wc0, lane);
+            for (int j = 0; j < BN / (32 * NW); ++j) {
+                const int rb = (j * NW + wave) * 32;
+                const int row = min(rb + (lane >> 1), cols_valid - 1);
+                dma16(Bq, static_cast<uint32_t>(row * (K / 2) + k0 / 2 + (lane & 1) * 16), dq + rb * kNvRowCodes);
             }
         };
+        // NVFP4: chunk j of a slot (row n, eight k from 8c) to the weight tile's bf16 chunk;
+        // a wavefront covers eight whole rows, so its code reads are one contiguous block
+        auto expand_chunk = [&](const uint8_t *sq, bf16_t *dB, int j) {
+            const int idx = j * NTH + tid, n = idx >> 3, c = idx & 7;
+            const uint32_t w = *reinterpret_cast<const uint32_t *>(sq + n * kNvRowCodes + c * 4);
+            const uint32_t sb = sq[BN * kNvRowCodes + n * 4 + (c >> 1)];
+            *reinterpret_cast<bf16x8 *>(dB + n * KB + (swz_chunk<KB>(n, c) << 3)) = nvfp4_expand(w, sb);
+        };
+        auto load_frags = [&](const bf16_t *st, int kk, bf16x8(&ax)[TM], bf16x8(&bx)[TN]) {
+            frag_load<TM, TN, KB, BMN, BN>(st, st + BM * KB, kk, ax, bx, wr0, wc0, lane);
+        };
         auto schedule = [&]() {
-            if constexpr (WQ) slice_schedule_n<TM + 2 * TN, TM * TN>();
+            // NVFP4: the expansion's two LDS reads go with the fragment reads
+            if constexpr (WQ) slice_schedule_n<TM + TN + 2, TM * TN>();
             else slice_schedule<TM, TN>();
         };
 
@@ -838,16 +831,37 @@ __global__ __launch_bounds__(NTH, (big_lds_bytes<BM, BN, WQ>() * 2 <= 160 * 1024
         // The previous tile's LDS reads (epilogue) are complete in every
         // wavefront; its global stores may still be in flight.
         barrier_keep_loads_lds();
-        dma_tile<BM, KB, NW>(Ab, K, rows_valid, 0, lds, wave, lane);
-        load_b(0, lds + BM * KB);
-        if (nk > 1) {
-            dma_tile<BM, KB, NW>(Ab, K, rows_valid, KB, lds + STAGE, wave, lane);
-            load_b(KB, lds + STAGE + BM * KB);
-            wait_vmcnt<LPS>();
+        if constexpr (WQ) {
+            // stage 0's weights expanded whole, stage 1's first chunk (the rest during
+            // stage 0); stage 2's codes go out once every wavefront has read slot 0
+            // (stage 1's tokens go last, so that the expansion need not wait for them)
+            dma_tile<BM, KB, NW>(Ab, K, rows_valid, 0, lds, wave, lane);
+            load_codes(0, cslot);
+            if (nk > 1) {
+                load_codes(KB, cslot + SLOT);
+                dma_tile<BM, KB, NW>(Ab, K, rows_valid, KB, lds + STAGE, wave, lane);
+                wait_vmcnt<BM * KB / 8 / NTH>();
+            } else {
+                wait_vmcnt<0>();
+            }
+            barrier_keep_loads();
+#pragma unroll
+            for (int j = 0; j < S; ++j) expand_chunk(cslot, lds + BM * KB, j);
+            expand_chunk(cslot + SLOT, lds + STAGE + BM * KB, 0);
+            barrier_keep_loads_lds();
+            if (nk > 2) load_codes(2 * KB, cslot);
         } else {
-            wait_vmcnt<0>();
+            dma_tile<BM, KB, NW>(Ab, K, rows_valid, 0, lds, wave, lane);
+            load_b(0, lds + BM * KB);
+            if (nk > 1) {
+                dma_tile<BM, KB, NW>(Ab, K, rows_valid, KB, lds + STAGE, wave, lane);
+                load_b(KB, lds + STAGE + BM * KB);
+                wait_vmcnt<LPS>();
+            } else {
+                wait_vmcnt<0>();
+            }
+            barrier_keep_loads();
         }
-        barrier_keep_loads();
         if constexpr (kEarlyBias) {
 #pragma unroll
             for (int j = 0; j < TN; ++j)
@@ -883,9 +897,13 @@ __global__ __launch_bounds__(NTH, (big_lds_bytes<BM, BN, WQ>() * 2 <= 160 * 1024
         load_frags(lds, 0, fa[0], fb[0]);
         for (int t = 0; t < nk; ++t) {
             const bf16_t *scur = lds + (t & 1) * STAGE;
+            bf16_t *const onext = lds + ((t + 1) & 1) * STAGE;
 #pragma unroll
             for (int kk = 0; kk < S - 1; ++kk) {
                 load_frags(scur, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
+                // NVFP4: the rest of stage t+1's weights. Branch-free: at the last step it
+                // rewrites the other buffer's weight tile, which nothing reads any more.
+                if constexpr (WQ) expand_chunk(cslot + ((t + 1) & 1) * SLOT, onext + BM * KB, kk + 1);
                 mfma_slice<TM, TN>(fa[kk & 1], fb[kk & 1], acc);
                 schedule();
             }
@@ -893,13 +911,19 @@ __global__ __launch_bounds__(NTH, (big_lds_bytes<BM, BN, WQ>() * 2 <= 160 * 1024
             // for, and the fragments read from the other buffer are not used.
             wait_vmcnt<0>();  // this wavefront's loads of stage t+1 have landed
             barrier_keep_loads_lds();
+            bf16_t *const sn = lds + (t & 1) * STAGE;
             if (t + 2 < nk) {
-                bf16_t *sn = lds + (t & 1) * STAGE;
                 dma_tile<BM, KB, NW>(Ab, K, rows_valid, (t + 2) * KB, sn, wave, lane);
-                load_b((t + 2) * KB, sn + BM * KB);
+                if constexpr (WQ) {
+                    if (t + 3 < nk) load_codes((t + 3) * KB, cslot + ((t + 1) & 1) * SLOT);
+                } else {
+                    load_b((t + 2) * KB, sn + BM * KB);
+                }
             }
-            const bf16_t *snext = lds + ((t + 1) & 1) * STAGE;
-            load_frags(snext, 0, fa[S & 1], fb[S & 1]);
+            load_frags(onext, 0, fa[S & 1], fb[S & 1]);
+            // NVFP4: the first chunk of stage t+2's weights (from the last two steps on,
+            // into a buffer that nothing reads any more)
+            if constexpr (WQ) expand_chunk(cslot + (t & 1) * SLOT, sn + BM * KB, 0);
             mfma_slice<TM, TN>(fa[(S - 1) & 1], fb[(S - 1) & 1], acc);
             schedule();
         }
@@ -1962,6 +1986,14 @@ static int64_t tile_rounds(int64_t f, int BMv, int64_t nx, int E, int64_t slots)
     return (E * rt * nx + slots - 1) / slots;
 }
 
+// one workgroup per CU: 256 x 256 tiles, or 192 x 256 where their rounds cost less
+static int wide_cfg(int N, int64_t rows_hint, int E) {
+    const int64_t f = (rows_hint + E - 1) / E, cus = resident_blocks(1);
+    const int64_t nx = (N + 255) / 256;
+    const int64_t r256 = tile_rounds(f, 256, nx, E, cus), r192 = tile_rounds(f, 192, nx, E, cus);
+    return r192 * 192 * 100 < r256 * 256 * 92 ? 4 : 1;
+}
+
 static int default_cfg(int N, int K, int64_t rows_hint, int E) {
     const int64_t big_tiles = ((rows_hint + 255) / 256) * ((N + 255) / 256);
     const int64_t f = (rows_hint + E - 1) / E, cus = resident_blocks(1);
@@ -1972,9 +2004,7 @@ static int default_cfg(int N, int K, int64_t rows_hint, int E) {
         const int64_t r128 = tile_rounds(f, 128, n128, E, 2 * cus), r192 = tile_rounds(f, 192, n128, E, 2 * cus);
         return r192 * 3 < r128 * 2 ? 5 : 3;
     }
-    const int64_t nx = (N + 255) / 256;
-    const int64_t r256 = tile_rounds(f, 256, nx, E, cus), r192 = tile_rounds(f, 192, nx, E, cus);
-    return r192 * 192 * 100 < r256 * 256 * 92 ? 4 : 1;
+    return wide_cfg(N, rows_hint, E);
 }
 
 // Backward data products, weights read n-contiguous: same tile choice as the
@@ -2011,31 +2041,23 @@ hipError_t fwd_launch(int act, const void *A, const void *B, void *D, int N, int
     }
 }
 
-// Forward products with NVFP4 weights: the bf16 products' tile choice.
+// Forward products with NVFP4 weights: eight-wavefront tiles 256 wide at every
+// size. Their code slots keep the smaller tiles to one workgroup per CU, and the
+// expansion (one chunk per thread per slice) costs least per MFMA on the wide
+// tiles (gated S=4096 fc1 / fc2: 192 x 256 106 / 95 us, 128 x 128 118 / 131,
+// 192 x 128 139 / 131). Of MOE_GEMM_CFG, 1 and 4 are honoured.
 template <int EPI>
 hipError_t fwd_launch_nvfp4(int act, const void *A, const uint8_t *Bcodes, const uint8_t *Bsc, const float *Bg,
                             void *D, int N, int K, int64_t rows_hint, int E, const int32_t *fill, const int32_t *cap,
                             const void *bias, void *pre_out, hipStream_t st) {
     int cfg = gemm_cfg_override();
-    if (cfg < 1 || cfg > 5) cfg = default_cfg(N, K, rows_hint, E);
+    if (cfg != 1 && cfg != 4) cfg = wide_cfg(N, rows_hint, E);
     const int s0 = 0, s1 = 0x7FFFFFFF;
-    switch (cfg) {
-    case 1:
-        return big_launch<256, 256, 512, EPI, false, 2, true>(act, A, Bcodes, D, N, K, E, fill, cap, bias, pre_out, st,
-                                                              nullptr, s0, s1, Bsc, Bg);
-    case 2:
-        return big_launch<256, 128, 256, EPI, false, 2, true>(act, A, Bcodes, D, N, K, E, fill, cap, bias, pre_out, st,
-                                                              nullptr, s0, s1, Bsc, Bg);
-    case 4:
+    if (cfg == 4)
         return big_launch<192, 256, 512, EPI, false, 2, true>(act, A, Bcodes, D, N, K, E, fill, cap, bias, pre_out, st,
                                                               nullptr, s0, s1, Bsc, Bg);
-    case 5:
-        return big_launch<192, 128, 256, EPI, false, 2, true>(act, A, Bcodes, D, N, K, E, fill, cap, bias, pre_out, st,
-                                                              nullptr, s0, s1, Bsc, Bg);
-    default:
-        return big_launch<128, 128, 256, EPI, false, 2, true>(act, A, Bcodes, D, N, K, E, fill, cap, bias, pre_out, st,
-                                                              nullptr, s0, s1, Bsc, Bg);
-    }
+    return big_launch<256, 256, 512, EPI, false, 2, true>(act, A, Bcodes, D, N, K, E, fill, cap, bias, pre_out, st,
+                                                          nullptr, s0, s1, Bsc, Bg);
 }
 
 // Weight gradients: the large-tile kernel when one expert's rows of either

@@ -150,11 +150,16 @@ def test_layer_forward_nvfp4_matches_oracle(w):
     check_close(host(b["out"]), out_o, w.dtype, "out", extra=decode_extra(rt, rows, yg, y_o))
 
 
-def test_nvfp4_full_size_gated_layer():
-    # the gated workload's layer (S=4096, M=1024, E=8, k=2, H=4096) with NVFP4 experts: sampled
-    # rows and tokens
+# The gated workload's layer (S=4096, M=1024, E=8, k=2, H=4096) with NVFP4 experts, and the
+# same layer with H=1536: the products' tile choice takes 192 x 256 tiles for the first
+# (fc1 and fc2) and 256 x 256 tiles for the second's fc1.
+FULL = [W.GATED_BF16, W.GATED_BF16.replace(name="gated_bf16_S4096_M1024_E8_k2_H1536", H=1536)]
+
+
+@pytest.mark.parametrize("w", FULL, ids=lambda w: w.name)
+def test_nvfp4_full_size_gated_layer(w):
+    # sampled rows and tokens
     import combine_softmax_top_amd as moe
-    w = W.GATED_BF16
     print(f"[nvfp4 full size] {w.name}", flush=True)
     rng = np.random.default_rng(79)
     inp = W.make_inputs(w, seed=0, device="cuda")
