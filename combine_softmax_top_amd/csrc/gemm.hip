@@ -781,13 +781,23 @@ __global__ __launch_bounds__(NTH, (big_lds_bytes<BM, BN, WQ>() * 2 <= 160 * 1024
             }
         };
         // NVFP4: chunk j of a slot (row n, eight k from 8c) to the weight tile's bf16 chunk;
-        // a wavefront covers eight whole rows, so its code reads are one contiguous block
-        auto expand_chunk = [&](const uint8_t *sq, bf16_t *dB, int j) {
+        // a wavefront covers eight whole rows, so its code reads are one contiguous block.
+        // A chunk's codes are read one slice before its expansion where they can be.
+        auto read_chunk = [&](const uint8_t *sq, int j, uint32_t &w, uint32_t &sb) {
             const int idx = j * NTH + tid, n = idx >> 3, c = idx & 7;
-            const uint32_t w = *reinterpret_cast<const uint32_t *>(sq + n * kNvRowCodes + c * 4);
-            const uint32_t sb = sq[BN * kNvRowCodes + n * 4 + (c >> 1)];
+            w = *reinterpret_cast<const uint32_t *>(sq + n * kNvRowCodes + c * 4);
+            sb = sq[BN * kNvRowCodes + n * 4 + (c >> 1)];
+        };
+        auto write_chunk = [&](bf16_t *dB, int j, uint32_t w, uint32_t sb) {
+            const int idx = j * NTH + tid, n = idx >> 3, c = idx & 7;
             *reinterpret_cast<bf16x8 *>(dB + n * KB + (swz_chunk<KB>(n, c) << 3)) = nvfp4_expand(w, sb);
         };
+        auto expand_chunk = [&](const uint8_t *sq, bf16_t *dB, int j) {
+            uint32_t w, sb;
+            read_chunk(sq, j, w, sb);
+            write_chunk(dB, j, w, sb);
+        };
+        uint32_t pw = 0, psb = 0;  // NVFP4: the codes of the next chunk to expand
         auto load_frags = [&](const bf16_t *st, int kk, bf16x8(&ax)[TM], bf16x8(&bx)[TN]) {
             frag_load<TM, TN, KB, BMN, BN>(st, st + BM * KB, kk, ax, bx, wr0, wc0, lane);
         };
@@ -848,6 +858,7 @@ __global__ __launch_bounds__(NTH, (big_lds_bytes<BM, BN, WQ>() * 2 <= 160 * 1024
 #pragma unroll
             for (int j = 0; j < S; ++j) expand_chunk(cslot, lds + BM * KB, j);
             expand_chunk(cslot + SLOT, lds + STAGE + BM * KB, 0);
+            read_chunk(cslot + SLOT, 1, pw, psb);
             barrier_keep_loads_lds();
             if (nk > 2) load_codes(2 * KB, cslot);
         } else {
@@ -903,7 +914,13 @@ __global__ __launch_bounds__(NTH, (big_lds_bytes<BM, BN, WQ>() * 2 <= 160 * 1024
                 load_frags(scur, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
                 // NVFP4: the rest of stage t+1's weights. Branch-free: at the last step it
                 // rewrites the other buffer's weight tile, which nothing reads any more.
-                if constexpr (WQ) expand_chunk(cslot + ((t + 1) & 1) * SLOT, onext + BM * KB, kk + 1);
+                if constexpr (WQ) {
+                    uint32_t nw = 0, nsb = 0;
+                    if (kk + 2 < S) read_chunk(cslot + ((t + 1) & 1) * SLOT, kk + 2, nw, nsb);
+                    write_chunk(onext + BM * KB, kk + 1, pw, psb);
+                    pw = nw;
+                    psb = nsb;
+                }
                 mfma_slice<TM, TN>(fa[kk & 1], fb[kk & 1], acc);
                 schedule();
             }
@@ -923,7 +940,10 @@ __global__ __launch_bounds__(NTH, (big_lds_bytes<BM, BN, WQ>() * 2 <= 160 * 1024
             load_frags(onext, 0, fa[S & 1], fb[S & 1]);
             // NVFP4: the first chunk of stage t+2's weights (from the last two steps on,
             // into a buffer that nothing reads any more)
-            if constexpr (WQ) expand_chunk(cslot + (t & 1) * SLOT, sn + BM * KB, 0);
+            if constexpr (WQ) {
+                expand_chunk(cslot + (t & 1) * SLOT, sn + BM * KB, 0);
+                read_chunk(cslot + (t & 1) * SLOT, 1, pw, psb);
+            }
             mfma_slice<TM, TN>(fa[(S - 1) & 1], fb[(S - 1) & 1], acc);
             schedule();
         }
