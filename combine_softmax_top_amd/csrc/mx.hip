@@ -7,8 +7,9 @@
 // even; E2M1 by comparison with the rounding midpoints). Block-wise FP8: sixteen
 // lanes take a 1 x 128 block, a workgroup a 128 x 128 one, and the values are
 // divided by the block's fp32 scale before the same E4M3 conversion.
-// NVFP4 (weights only): a workgroup per tensor finds its amax, then two lanes per
-// 16-value block round the block scale to E4M3 and the values to E2M1.
+// NVFP4 (weights only): workgroups over stretches of each tensor combine its amax by
+// an atomic max, then two lanes per 16-value block round the block scale to E4M3 and
+// the values to E2M1.
 #include "moe_internal.h"
 
 namespace moe {
@@ -213,11 +214,14 @@ __global__ __launch_bounds__(kThreads) void blk_quantize_tiles_kernel(const void
 // fp32 scale g per tensor (rows / ntensor consecutive rows). g = amax / 2688 needs the
 // whole tensor's amax first: one workgroup per tensor (offline weight preparation).
 __global__ __launch_bounds__(kThreads) void nvfp4_amax_kernel(const void *__restrict__ src, int dtype,
-                                                              int64_t per_elems, float *__restrict__ g) {
+                                                              int64_t per_elems, int64_t span,
+                                                              uint32_t *__restrict__ amax_bits) {
+    // blockIdx.y: the tensor; blockIdx.x: its span-th stretch of elements (span a multiple of 8)
     __shared__ float wmax[kThreads / 64];
-    const int64_t base = static_cast<int64_t>(blockIdx.x) * per_elems;
+    const int64_t base = static_cast<int64_t>(blockIdx.y) * per_elems;
+    const int64_t lo = static_cast<int64_t>(blockIdx.x) * span, hi = min(per_elems, lo + span);
     float amax = 0.f;
-    for (int64_t i = static_cast<int64_t>(threadIdx.x) * 8; i < per_elems; i += kThreads * 8) {
+    for (int64_t i = lo + static_cast<int64_t>(threadIdx.x) * 8; i < hi; i += kThreads * 8) {
         float f[8];
         load8(src, dtype, base + i, f);
 #pragma unroll
@@ -227,7 +231,20 @@ __global__ __launch_bounds__(kThreads) void nvfp4_amax_kernel(const void *__rest
     for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
     if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = amax;
     __syncthreads();
-    if (threadIdx.x == 0) g[blockIdx.x] = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3])) / 2688.f;
+    // non-negative floats order as their bit patterns
+    if (threadIdx.x == 0)
+        atomicMax(amax_bits + blockIdx.y, __float_as_uint(fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]))));
+}
+
+__global__ void nvfp4_amax_zero_kernel(uint32_t *__restrict__ amax_bits, int n) {
+    const int t = blockIdx.x * blockDim.x + threadIdx.x;
+    if (t < n) amax_bits[t] = 0u;
+}
+
+// g = amax / 2688 (448 * 6), in place, once the quantiser has read the maxima
+__global__ void nvfp4_g_kernel(float *__restrict__ g, int n) {
+    const int t = blockIdx.x * blockDim.x + threadIdx.x;
+    if (t < n) g[t] = g[t] / 2688.f;
 }
 
 // Two lanes per 16-value block, eight values each: d = (amax_b / 6) / g rounded to the
@@ -236,7 +253,7 @@ __global__ __launch_bounds__(kThreads) void nvfp4_amax_kernel(const void *__rest
 // product is 0, as for an all-zero tensor).
 __global__ __launch_bounds__(kThreads) void nvfp4_quantize_kernel(const void *__restrict__ src, int dtype,
                                                                   int64_t rows, int32_t K, int64_t per,
-                                                                  const float *__restrict__ g,
+                                                                  const float *__restrict__ amax_t,
                                                                   uint8_t *__restrict__ codes,
                                                                   uint8_t *__restrict__ scales) {
     const int KB = K / 16;
@@ -252,7 +269,7 @@ __global__ __launch_bounds__(kThreads) void nvfp4_quantize_kernel(const void *__
 #pragma unroll
         for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
         amax = fmaxf(amax, __shfl_xor(amax, 1, 2));
-        const float gt = g[r / per];
+        const float gt = amax_t[r / per] / 2688.f;  // the tensor's g, as nvfp4_g_kernel computes it
         uint32_t q = 0u;
         if (gt > 0.f) q = mx_fp8x2((amax / 6.f) / gt, 0.f) & 0xFFu;
         const float den = __builtin_amdgcn_cvt_f32_fp8(static_cast<int>(q), 0) * gt;
@@ -353,10 +370,21 @@ hipError_t launch_blk_quantize(int brows, int64_t rows, int32_t K, int dtype, co
 hipError_t launch_nvfp4_quantize(int64_t rows, int32_t K, int32_t ntensor, int dtype, const void *src,
                                  uint8_t *codes, uint8_t *scales, float *g, hipStream_t st) {
     if (rows == 0) return hipSuccess;
-    const int64_t per = rows / ntensor;
-    hipLaunchKernelGGL(nvfp4_amax_kernel, dim3(ntensor), dim3(kThreads), 0, st, src, dtype, per * K, g);
+    // g holds each tensor's amax (as bits) until the codes are written: a fill, the
+    // maxima over stretches of 32 K values (one atomic max per workgroup), the
+    // quantiser, then g = amax / 2688 in place
+    const int64_t per = rows / ntensor, per_elems = per * K;
+    const int64_t span = static_cast<int64_t>(kThreads) * 8 * 16;
+    const int64_t nspan = (per_elems + span - 1) / span;
+    if (nspan > 0x7FFFFFFF) return hipErrorInvalidValue;
+    uint32_t *bits = reinterpret_cast<uint32_t *>(g);
+    const int small = (ntensor + kThreads - 1) / kThreads;
+    hipLaunchKernelGGL(nvfp4_amax_zero_kernel, dim3(small), dim3(kThreads), 0, st, bits, ntensor);
+    hipLaunchKernelGGL(nvfp4_amax_kernel, dim3(static_cast<uint32_t>(nspan), ntensor), dim3(kThreads), 0, st, src,
+                       dtype, per_elems, span, bits);
     hipLaunchKernelGGL(nvfp4_quantize_kernel, dim3(grid_blocks(rows * (K / 16) * 2)), dim3(kThreads), 0, st, src,
-                       dtype, rows, K, per, g, codes, scales);
+                       dtype, rows, K, per, static_cast<const float *>(g), codes, scales);
+    hipLaunchKernelGGL(nvfp4_g_kernel, dim3(small), dim3(kThreads), 0, st, g, ntensor);
     return hipGetLastError();
 }
 
