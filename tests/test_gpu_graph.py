@@ -25,7 +25,11 @@ CASES = [
                             capacity_factor=1.25, logits="gate")),
     ("mxfp8", W.Workload("graph_mx_S600_M256_E8_k2_H384", S=600, M=256, E=8, k=2, H=384,
                          capacity_factor=1.25, logits="gate")),
+    # the NVFP4 weights' quantisation (fill, amax, codes, g) is captured with the forward
+    ("nvfp4", W.Workload("graph_nv_S600_M256_E8_k2_H384", S=600, M=256, E=8, k=2, H=384,
+                         capacity_factor=1.25, logits="gate")),
 ]
+NV = ("W1c", "W1s", "W1g", "W2c", "W2s", "W2g")
 
 
 def _outputs(kind, b, g):
@@ -36,7 +40,8 @@ def _outputs(kind, b, g):
              "blockfp8": ["logits", "idx", "loc", "fill", "capacity", "buf_codes", "buf_scales", "h_codes",
                           "h_scales", "y", "out"],
              "mxfp8": ["logits", "idx", "loc", "fill", "capacity", "buf_codes", "buf_scales", "h_codes", "h_scales",
-                       "y", "out"]}[kind]
+                       "y", "out"],
+             "nvfp4": ["logits", "idx", "loc", "fill", "capacity", "buf", "h", "y", "out", *NV]}[kind]
     out = {n: b[n] for n in names}
     if g is not None:
         for n in ("dx", "dW1", "db1", "dW2", "db2", "dgates", "dlogits", "dWg", "aux_loss", "dW1r", "dW2r", "db1r",
@@ -65,6 +70,13 @@ def test_graph_replays_equal_eager(kind, w):
             return moe.alloc_forward_blockfp8(s, gate_projection=gate), None
         if kind == "mxfp8":
             return moe.alloc_forward_mx(s, gate_projection=gate), None
+        if kind == "nvfp4":
+            b = moe.alloc_forward(s, gate_projection=gate)
+            for n, (Wt, N, K) in zip(("W1", "W2"), ((d["W1"], w.H, w.M), (d["W2"], w.M, w.H))):
+                b[n + "c"] = torch.empty(w.E, N, K // 2, dtype=torch.uint8, device="cuda")
+                b[n + "s"] = torch.empty(w.E, N, K // 16, dtype=torch.uint8, device="cuda")
+                b[n + "g"] = torch.empty(w.E, dtype=torch.float32, device="cuda")
+            return b, None
         b = moe.alloc_forward(s, training=w.backward, gate_projection=gate, residual=w.residual)
         g = moe.alloc_backward(s, gate=True, gate_projection=gate, residual=w.residual) if w.backward else None
         return b, g
@@ -77,6 +89,12 @@ def test_graph_replays_equal_eager(kind, w):
         if kind == "mxfp8":
             moe.layer_forward_mx(s, moe.MOE_MX_FP8, x, W1q, d.get("b1"), W2q, d.get("b2"), logits=d.get("logits"),
                                  Wg=d.get("Wg"), bufs=b)
+            return
+        if kind == "nvfp4":
+            for n in ("W1", "W2"):
+                moe.moe_nvfp4_quantize(d[n], w.E, b[n + "c"], b[n + "s"], b[n + "g"])
+            moe.layer_forward_nvfp4(s, x, (b["W1c"], b["W1s"], b["W1g"]), d.get("b1"), (b["W2c"], b["W2s"], b["W2g"]),
+                                    d.get("b2"), logits=d.get("logits"), Wg=d.get("Wg"), bufs=b)
             return
         moe.layer_forward(s, x, d["W1"], d.get("b1"), d["W2"], d.get("b2"), logits=d.get("logits"), Wg=d.get("Wg"),
                           bufs=b, training=w.backward, residual=res)
