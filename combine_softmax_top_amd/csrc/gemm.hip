@@ -937,13 +937,16 @@ __global__ __launch_bounds__(NTH, (big_lds_bytes<BM, BN, WQ>() * 2 <= 160 * 1024
                     load_b((t + 2) * KB, sn + BM * KB);
                 }
             }
-            load_frags(onext, 0, fa[S & 1], fb[S & 1]);
             // NVFP4: the first chunk of stage t+2's weights (from the last two steps on,
-            // into a buffer that nothing reads any more)
+            // into a buffer that nothing reads any more); its codes are read ahead of the
+            // fragments, so that their wait does not take in the fragment reads
+            uint32_t w0 = 0, s0b = 0;
             if constexpr (WQ) {
-                expand_chunk(cslot + (t & 1) * SLOT, sn + BM * KB, 0);
+                read_chunk(cslot + (t & 1) * SLOT, 0, w0, s0b);
                 read_chunk(cslot + (t & 1) * SLOT, 1, pw, psb);
             }
+            load_frags(onext, 0, fa[S & 1], fb[S & 1]);
+            if constexpr (WQ) write_chunk(sn + BM * KB, 0, w0, s0b);
             mfma_slice<TM, TN>(fa[(S - 1) & 1], fb[(S - 1) & 1], acc);
             schedule();
         }
